@@ -1,0 +1,155 @@
+"""CPU oracle for RMSNorm / fused residual-Add + RMSNorm (forward, backward).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s CPU-baseline leg may import this module.  The GPU library never
+loads it.
+
+The arithmetic lives in ``addrms_oracle.c`` (plain C, binary64, one rounding
+per output); this module only marshals torch CPU tensors into it.  The
+definitions it follows are stated in that file's header: the operations are
+the RMSNorm op of the "Machete" README ("Built-In Areas") and the fused
+Add + RMSNorm of KernelAgent-Oink (KernelAgent repository digest, opening
+summary), with the textbook RMSNorm formula.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "addrms_oracle.c")
+# A test may point the wrapper at another build of the oracle source (the
+# mutation test builds deliberately broken copies to show the pins catch them).
+_LIB_PATH = os.environ.get("ADDRMS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.float64: F64}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc: no fast-math, no FMA contraction, so that
+    every operation is the IEEE operation written in the source."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+            "-fno-fast-math", "-Wall", "-Werror", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_bf16_round.restype = ctypes.c_uint16
+        lib.oracle_bf16_round.argtypes = [dbl]
+        lib.oracle_bf16_round_array.restype = None
+        lib.oracle_bf16_round_array.argtypes = [vp, vp, i64]
+        lib.oracle_rmsnorm_fwd.restype = i32
+        lib.oracle_rmsnorm_fwd.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, i64, i64, dbl]
+        lib.oracle_add_rmsnorm_fwd.restype = i32
+        lib.oracle_add_rmsnorm_fwd.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32,
+                                               i64, i64, dbl]
+        lib.oracle_rmsnorm_bwd.restype = i32
+        lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp,
+                                           i64, i64]
+        _lib = lib
+    return _lib
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype not in _CODES:
+        raise TypeError(f"oracle: unsupported dtype {t.dtype}")
+    return _CODES[t.dtype]
+
+
+def _cpu(t: torch.Tensor) -> torch.Tensor:
+    if t.device.type != "cpu":
+        raise ValueError("oracle: CPU tensors only")
+    return t.contiguous()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def eps_as_float32(eps: float) -> float:
+    """The eps value the GPU library sees: the binary32 nearest to eps."""
+    return float(np.float32(eps))
+
+
+def bf16_round(v) -> np.ndarray:
+    """binary64 values -> bfloat16 bit patterns (uint16), one RNE rounding."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_bf16_round_array(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float, *, y_dtype=None,
+                rstd_dtype=torch.float32, eps_exact: bool = False):
+    """y = x * rstd * w over the last dim; returns (y, rstd).  By default eps is
+    first rounded to binary32, as the library's float argument is."""
+    x, w = _cpu(x), _cpu(w)
+    N = x.shape[-1]
+    M = x.numel() // N
+    y = torch.empty(x.shape, dtype=y_dtype or x.dtype)
+    rstd = torch.empty(x.shape[:-1], dtype=rstd_dtype)
+    e = float(eps) if eps_exact else eps_as_float32(eps)
+    _check(_load().oracle_rmsnorm_fwd(_ptr(x), _code(x), _ptr(w), _code(w), _ptr(y), _code(y),
+                                      _ptr(rstd), _code(rstd), M, N, e), "rmsnorm_fwd")
+    return y, rstd
+
+
+def add_rmsnorm_fwd(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float, *,
+                    y_dtype=None, res_dtype=None, rstd_dtype=torch.float32,
+                    eps_exact: bool = False):
+    """residual_out = stored(x + r); y = RMSNorm(residual_out) * w.
+    Returns (y, residual_out, rstd)."""
+    x, r, w = _cpu(x), _cpu(r), _cpu(w)
+    if x.dtype != r.dtype or x.shape != r.shape:
+        raise ValueError("oracle: x and r must share dtype and shape")
+    N = x.shape[-1]
+    M = x.numel() // N
+    y = torch.empty(x.shape, dtype=y_dtype or x.dtype)
+    res = torch.empty(x.shape, dtype=res_dtype or x.dtype)
+    rstd = torch.empty(x.shape[:-1], dtype=rstd_dtype)
+    e = float(eps) if eps_exact else eps_as_float32(eps)
+    _check(_load().oracle_add_rmsnorm_fwd(_ptr(x), _ptr(r), _code(x), _ptr(w), _code(w),
+                                          _ptr(y), _code(y), _ptr(res), _code(res),
+                                          _ptr(rstd), _code(rstd), M, N, e), "add_rmsnorm_fwd")
+    return y, res, rstd
+
+
+def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor, *,
+                dx_dtype=None, dw_dtype=torch.float32):
+    """dx, dw from the saved rstd.  Returns (dx, dw, dw_abs) where dw_abs[j] is
+    sum_i |dy_ij * x_ij * rstd_i| in binary64."""
+    dy, x, w, rstd = _cpu(dy), _cpu(x), _cpu(w), _cpu(rstd)
+    if dy.dtype != x.dtype or dy.shape != x.shape:
+        raise ValueError("oracle: dy and x must share dtype and shape")
+    N = x.shape[-1]
+    M = x.numel() // N
+    dx = torch.empty(x.shape, dtype=dx_dtype or x.dtype)
+    dw = torch.empty((N,), dtype=dw_dtype)
+    dw_abs = torch.empty((N,), dtype=torch.float64)
+    _check(_load().oracle_rmsnorm_bwd(_ptr(dy), _ptr(x), _code(x), _ptr(w), _code(w),
+                                      _ptr(rstd), _code(rstd), _ptr(dx), _code(dx), _ptr(dw),
+                                      _code(dw), _ptr(dw_abs), M, N), "rmsnorm_bwd")
+    return dx, dw, dw_abs

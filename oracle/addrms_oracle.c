@@ -1,0 +1,265 @@
+/*
+ * CPU oracle for row-wise RMSNorm and fused residual-Add + RMSNorm,
+ * forward and backward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg load it; the GPU
+ * library never includes, links or calls it, and it shares no code with it.
+ *
+ * What it computes.  The pages name the operations but print no formula:
+ *   - "Machete" README, section "Built-In Areas": an RMSNorm op, plus
+ *     autograd helpers (so a backward exists);
+ *   - KernelAgent repository digest, opening summary: KernelAgent-Oink's
+ *     RMSNorm and fused Add + RMSNorm custom operators;
+ *   - "CuTe DSL" skill page, Workflow 0: RMSNorm is a float32 row reduction.
+ * The formula is the textbook one (Zhang & Sennrich 2019, "Root Mean Square
+ * Layer Normalization"), eps inside the square root:
+ *
+ *   h      = x                       (plain)
+ *   h      = stored(fp32(x) + fp32(r))  (fused; the residual as stored)
+ *   rstd_i = 1 / sqrt( (1/N) * sum_j h_ij^2 + eps )
+ *   y_ij   = h_ij * rstd_i * w_j
+ *
+ * and its exact derivative for the backward, given the saved rstd:
+ *
+ *   g_ij  = dy_ij * w_j,   xh_ij = x_ij * rstd_i
+ *   c_i   = (1/N) * sum_j g_ij * xh_ij
+ *   dx_ij = rstd_i * (g_ij - xh_ij * c_i)
+ *   dw_j  = sum_i dy_ij * xh_ij
+ *
+ * Every sum and product is in IEEE binary64, left to right.  Each output is
+ * rounded once, from binary64, to its storage type with round-to-nearest,
+ * ties-to-even.  The one deliberate exception is the residual add of the
+ * fused op for float32/bfloat16 inputs: it is a binary32 add (both operands
+ * widened exactly to float32, one RNE rounding), and the residual is then
+ * rounded to its storage type; the normalised value h is that stored
+ * residual.  For binary64 inputs the add is a binary64 add.
+ *
+ * Element types (codes): 0 = float32, 1 = bfloat16 (raw uint16 bits),
+ * 2 = float64.  All arrays are row-major and contiguous, row stride N.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_F64 2
+
+#define OR_OK 0
+#define OR_ERR_ARG -1
+#define OR_ERR_NOMEM -2
+
+/* ---- bfloat16 <-> binary64 ---------------------------------------------- */
+
+/* A bfloat16 pattern is the upper half of a binary32 pattern; the value is
+ * exact in binary64. */
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a binary64 value to bfloat16 (8 significant bits, binary32's
+ * exponent range, subnormals kept), round-to-nearest ties-to-even, written
+ * out from the definition: find the two neighbouring bfloat16 values lo <= |v|
+ * < hi on the grid of spacing ulp, and pick by comparing with their midpoint.
+ * NaN gives a quiet NaN with the sign kept; overflow gives +-Inf. */
+uint16_t oracle_bf16_round(double v)
+{
+    const double bf16_max = 0x1.FEp127; /* largest finite bfloat16 */
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a, ulp, lo, hi, mid, q;
+    float f;
+    uint32_t u;
+
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    a = fabs(v);
+    if (isinf(v) || a >= 0x1p128)
+        return (uint16_t)(sign | 0x7F80u);
+
+    if (a < 0x1p-126) {
+        ulp = 0x1p-133; /* subnormal spacing: 2^-126 / 2^7 */
+    } else {
+        int e;
+        frexp(a, &e); /* a in [2^(e-1), 2^e) */
+        ulp = ldexp(1.0, e - 8);
+    }
+    lo = floor(a / ulp) * ulp; /* exact: scaling by a power of two */
+    hi = lo + ulp;
+    mid = lo + 0.5 * ulp; /* exact: at most 10 significant bits */
+    if (a < mid)
+        q = lo;
+    else if (a > mid)
+        q = hi;
+    else
+        q = (fmod(lo / ulp, 2.0) == 0.0) ? lo : hi; /* tie: even significand */
+
+    if (q > bf16_max)
+        return (uint16_t)(sign | 0x7F80u);
+    f = (float)q; /* exact: q is a bfloat16 value */
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+/* binary32 pattern -> bfloat16 pattern, through the same single rounding. */
+uint16_t oracle_bf16_from_f32_bits(uint32_t bits)
+{
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return oracle_bf16_round((double)f);
+}
+
+/* Bulk form of oracle_bf16_round, for the converter's own checks. */
+void oracle_bf16_round_array(const double *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_bf16_round(v[i]);
+}
+
+static int dtype_ok(int dt) { return dt == OR_F32 || dt == OR_BF16 || dt == OR_F64; }
+
+static double load_elem(const void *p, int dt, int64_t i)
+{
+    switch (dt) {
+    case OR_F32:
+        return (double)((const float *)p)[i];
+    case OR_BF16:
+        return bf16_bits_to_double(((const uint16_t *)p)[i]);
+    default:
+        return ((const double *)p)[i];
+    }
+}
+
+/* One rounding from binary64 to the storage type (C's double->float
+ * conversion is round-to-nearest-even in the default rounding mode). */
+static void store_elem(void *p, int dt, int64_t i, double v)
+{
+    switch (dt) {
+    case OR_F32:
+        ((float *)p)[i] = (float)v;
+        break;
+    case OR_BF16:
+        ((uint16_t *)p)[i] = oracle_bf16_round(v);
+        break;
+    default:
+        ((double *)p)[i] = v;
+        break;
+    }
+}
+
+/* ---- forward ------------------------------------------------------------ */
+
+/* RMSNorm forward.  y = x * rstd * w row by row; rstd (nullable) receives
+ * 1/sqrt(mean(x^2) + eps) per row, rounded to rstd_dt. */
+int oracle_rmsnorm_fwd(const void *x, int x_dt, const void *w, int w_dt, void *y, int y_dt,
+                       void *rstd, int rstd_dt, int64_t M, int64_t N, double eps)
+{
+    if (!x || !w || !y || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || !dtype_ok(y_dt) || (rstd && !dtype_ok(rstd_dt)))
+        return OR_ERR_ARG;
+
+    for (int64_t i = 0; i < M; i++) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < N; j++) {
+            double h = load_elem(x, x_dt, i * N + j);
+            ss += h * h;
+        }
+        double ms = ss / (double)N;
+        double rs = 1.0 / sqrt(ms + eps);
+        if (rstd)
+            store_elem(rstd, rstd_dt, i, rs);
+        for (int64_t j = 0; j < N; j++) {
+            double h = load_elem(x, x_dt, i * N + j);
+            store_elem(y, y_dt, i * N + j, h * rs * load_elem(w, w_dt, j));
+        }
+    }
+    return OR_OK;
+}
+
+/* Fused residual-Add + RMSNorm forward.  residual_out = stored(x + r), with
+ * the add in binary32 for float32/bfloat16 inputs; then y is RMSNorm of the
+ * stored residual (the residual as written is what gets normalised). */
+int oracle_add_rmsnorm_fwd(const void *x, const void *r, int in_dt, const void *w, int w_dt,
+                           void *y, int y_dt, void *res, int res_dt, void *rstd, int rstd_dt,
+                           int64_t M, int64_t N, double eps)
+{
+    if (!x || !r || !w || !y || !res || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
+        return OR_ERR_ARG;
+
+    for (int64_t k = 0; k < M * N; k++) {
+        double s;
+        if (in_dt == OR_F64) {
+            s = load_elem(x, in_dt, k) + load_elem(r, in_dt, k);
+        } else {
+            float xs = (float)load_elem(x, in_dt, k); /* exact widening */
+            float rs = (float)load_elem(r, in_dt, k);
+            float s32 = xs + rs; /* one binary32 RNE rounding */
+            s = (double)s32;
+        }
+        store_elem(res, res_dt, k, s);
+    }
+    return oracle_rmsnorm_fwd(res, res_dt, w, w_dt, y, y_dt, rstd, rstd_dt, M, N, eps);
+}
+
+/* ---- backward ----------------------------------------------------------- */
+
+/* RMSNorm backward from the saved rstd.  dx per row; dw = sum over rows of
+ * dy * x * rstd, overwritten (not accumulated).  dw_abs (nullable, binary64)
+ * receives sum over rows of |dy * x * rstd| per column, the magnitude that
+ * bounds the rounding error of any summation order of dw. */
+int oracle_rmsnorm_bwd(const void *dy, const void *x, int in_dt, const void *w, int w_dt,
+                       const void *rstd, int rstd_dt, void *dx, int dx_dt, void *dw, int dw_dt,
+                       double *dw_abs, int64_t M, int64_t N)
+{
+    double *acc, *acc_abs;
+
+    if (!dy || !x || !w || !rstd || !dx || !dw || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(in_dt) || !dtype_ok(w_dt) || !dtype_ok(rstd_dt) || !dtype_ok(dx_dt) ||
+        !dtype_ok(dw_dt))
+        return OR_ERR_ARG;
+
+    acc = (double *)calloc((size_t)N, sizeof(double));
+    acc_abs = (double *)calloc((size_t)N, sizeof(double));
+    if (!acc || !acc_abs) {
+        free(acc);
+        free(acc_abs);
+        return OR_ERR_NOMEM;
+    }
+
+    for (int64_t i = 0; i < M; i++) {
+        double rs = load_elem(rstd, rstd_dt, i);
+        double c = 0.0;
+        for (int64_t j = 0; j < N; j++) {
+            double g = load_elem(dy, in_dt, i * N + j) * load_elem(w, w_dt, j);
+            double xh = load_elem(x, in_dt, i * N + j) * rs;
+            c += g * xh;
+        }
+        c /= (double)N;
+        for (int64_t j = 0; j < N; j++) {
+            double d = load_elem(dy, in_dt, i * N + j);
+            double g = d * load_elem(w, w_dt, j);
+            double xh = load_elem(x, in_dt, i * N + j) * rs;
+            store_elem(dx, dx_dt, i * N + j, rs * (g - xh * c));
+            acc[j] += d * xh;
+            acc_abs[j] += fabs(d * xh);
+        }
+    }
+    for (int64_t j = 0; j < N; j++) {
+        store_elem(dw, dw_dt, j, acc[j]);
+        if (dw_abs)
+            dw_abs[j] = acc_abs[j];
+    }
+    free(acc);
+    free(acc_abs);
+    return OR_OK;
+}

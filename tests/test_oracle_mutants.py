@@ -1,0 +1,57 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case below plants one mistake in a copy of the oracle's C source, builds
+it, and runs the oracle pin suite against that build in a subprocess: the
+suite must fail.  Mistakes cover every step of the definition: the eps
+placement, the mean's divisor, the square, the weight, the bfloat16 rounding
+rule, the fused op's choice of normalised value, the saved rstd, and each term
+of the backward."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "addrms_oracle.c")
+PINS = ["tests/test_oracle_bf16.py", "tests/test_oracle_fwd.py", "tests/test_oracle_bwd.py"]
+
+MUTANTS = {
+    "eps_outside_root": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms) + eps"),
+    "eps_dropped": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms)"),
+    "divisor_n_minus_1": ("ss / (double)N", "ss / (double)(N > 1 ? N - 1 : 1)"),
+    "abs_not_square": ("ss += h * h;", "ss += fabs(h);"),
+    "weight_dropped": ("h * rs * load_elem(w, w_dt, j)", "h * rs"),
+    "weight_wrong_index": ("h * rs * load_elem(w, w_dt, j)", "h * rs * load_elem(w, w_dt, N - 1 - j)"),
+    "rstd_saved_inverted": ("store_elem(rstd, rstd_dt, i, rs);", "store_elem(rstd, rstd_dt, i, 1.0 / rs);"),
+    "ties_away_from_zero": ("(fmod(lo / ulp, 2.0) == 0.0) ? lo : hi", "hi"),
+    "truncating_round": ("if (a < mid)", "if (a < hi)"),
+    "subnormal_spacing": ("ulp = 0x1p-133;", "ulp = 0x1p-134;"),
+    "overflow_saturates": ("return (uint16_t)(sign | 0x7F80u);\n    f = (float)q;",
+                           "q = bf16_max;\n    f = (float)q;"),
+    "fused_normalises_x": ("return oracle_rmsnorm_fwd(res, res_dt,", "return oracle_rmsnorm_fwd(x, in_dt,"),
+    "residual_subtracts": ("float s32 = xs + rs;", "float s32 = xs - rs;"),
+    "bwd_sign_of_projection": ("rs * (g - xh * c)", "rs * (g + xh * c)"),
+    "bwd_projection_not_averaged": ("c /= (double)N;", "c /= 1.0;"),
+    "bwd_g_without_weight": ("double g = load_elem(dy, in_dt, i * N + j) * load_elem(w, w_dt, j);",
+                             "double g = load_elem(dy, in_dt, i * N + j);"),
+    "bwd_dx_without_weight": ("double g = d * load_elem(w, w_dt, j);", "double g = d;"),
+    "bwd_dw_without_rstd": ("acc[j] += d * xh;", "acc[j] += d * load_elem(x, in_dt, i * N + j);"),
+    "bwd_dx_missing_outer_rstd": ("rs * (g - xh * c)", "(g - xh * c)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_fail_on_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique for {name}"
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-o", str(lib), str(mutant), "-lm"])
+    env = dict(os.environ, ADDRMS_ORACLE_LIB=str(lib))
+    run = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                          *PINS], cwd=ROOT, env=env, capture_output=True, text=True)
+    assert run.returncode == 1, f"pins did not catch {name}:\n{run.stdout[-2000:]}"
