@@ -1,0 +1,186 @@
+"""RMSNorm and fused residual-Add + RMSNorm on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/addrms.h`` (library
+``libaddrms.so`` next to this file).  It only marshals arguments: torch
+supplies device memory and the current stream; every step of the computation
+runs in the library's HIP kernels.  There is no fallback: if the library is
+missing, importing this package raises.
+
+Operations (same names as the C ABI):
+    rmsnorm_fwd(x, w, eps)            -> y (and rstd)
+    add_rmsnorm_fwd(x, r, w, eps)     -> y, residual_out (and rstd)
+    rmsnorm_bwd(dy, x, w, rstd)       -> dx, dw
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
+           "AddRmsError", "LIB_PATH", "lib"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
+
+F32, BF16 = 0, 1
+_CODES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class AddRmsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _lib.addrms_status_str(status).decode()
+        if status == -7:
+            msg += f" (hipError {_lib.addrms_last_hip_error()})"
+        super().__init__(f"{what}: {msg} [{status}]")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m add_rmsnorm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.rmsnorm_fwd.restype = i32
+    lib.rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd.restype = i32
+    lib.add_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.rmsnorm_bwd_workspace_bytes.restype = sz
+    lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
+    lib.rmsnorm_bwd.restype = i32
+    lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.addrms_status_str.restype = ctypes.c_char_p
+    lib.addrms_status_str.argtypes = [i32]
+    lib.addrms_last_hip_error.restype = i32
+    lib.addrms_last_hip_error.argtypes = []
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def _code(t: torch.Tensor, what: str) -> int:
+    if t.dtype not in _CODES:
+        raise TypeError(f"{what}: dtype {t.dtype} not supported (float32, bfloat16)")
+    return _CODES[t.dtype]
+
+
+def _dev(t: torch.Tensor, what: str, dtype=None, shape=None) -> torch.Tensor:
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _rows(x: torch.Tensor):
+    if x.dim() < 1 or x.shape[-1] == 0:
+        raise ValueError("input must have a non-empty last dimension")
+    N = x.shape[-1]
+    return x.numel() // N, N
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, y=None, rstd=None,
+                return_rstd: bool = False):
+    """y = x / sqrt(mean(x^2, -1) + eps) * w, normalising the last dimension.
+    `y` may be `x` (in place).  Returns y, or (y, rstd) with float32 rstd."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(w, "w", shape=(N,))
+    y = torch.empty_like(x) if y is None else _dev(y, "y", x.dtype, x.shape)
+    if rstd is None and return_rstd:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    elif rstd is not None:
+        _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    with torch.cuda.device(x.device):
+        st = _lib.rmsnorm_fwd(_p(x), _p(w), _p(y), _p(rstd), M, N, float(eps),
+                              _code(x, "x"), _code(w, "w"), _stream(x))
+    if st != 0:
+        raise AddRmsError(st, "rmsnorm_fwd")
+    return (y, rstd) if (return_rstd or rstd is not None) else y
+
+
+def add_rmsnorm_fwd(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *,
+                    y=None, residual_out=None, rstd=None, return_rstd: bool = False):
+    """residual_out = x + r (float32 add, stored in x's dtype);
+    y = residual_out / sqrt(mean(residual_out^2, -1) + eps) * w.
+    `residual_out` may be `r` or `x` (in-place residual update), `y` may be
+    `x` or `r`.  Returns (y, residual_out) or (y, residual_out, rstd)."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(r, "r", x.dtype, x.shape)
+    _dev(w, "w", shape=(N,))
+    y = torch.empty_like(x) if y is None else _dev(y, "y", x.dtype, x.shape)
+    residual_out = (torch.empty_like(x) if residual_out is None
+                    else _dev(residual_out, "residual_out", x.dtype, x.shape))
+    if rstd is None and return_rstd:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    elif rstd is not None:
+        _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    with torch.cuda.device(x.device):
+        st = _lib.add_rmsnorm_fwd(_p(x), _p(r), _p(w), _p(y), _p(residual_out), _p(rstd), M, N,
+                                  float(eps), _code(x, "x"), _code(w, "w"), _stream(x))
+    if st != 0:
+        raise AddRmsError(st, "add_rmsnorm_fwd")
+    if return_rstd or rstd is not None:
+        return y, residual_out, rstd
+    return y, residual_out
+
+
+def rmsnorm_bwd_workspace_bytes(M: int, N: int) -> int:
+    """Device scratch bytes rmsnorm_bwd needs for M rows of N."""
+    return int(_lib.rmsnorm_bwd_workspace_bytes(M, N))
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A per-device scratch buffer, grown on demand and reused across calls on
+    the current stream (calls on other streams must pass their own)."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor, *,
+                dx=None, dw=None, workspace: torch.Tensor | None = None):
+    """Gradients of y = x * rstd * w given dy and the forward's saved float32
+    rstd: returns (dx, dw) with dw float32.  `dx` may be `dy` or `x`."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(dy, "dy", x.dtype, x.shape)
+    _dev(w, "w", shape=(N,))
+    _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    dx = torch.empty_like(x) if dx is None else _dev(dx, "dx", x.dtype, x.shape)
+    dw = (torch.empty(N, dtype=torch.float32, device=x.device) if dw is None
+          else _dev(dw, "dw", torch.float32, (N,)))
+    need = rmsnorm_bwd_workspace_bytes(M, N)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    else:
+        _dev(workspace, "workspace")
+    with torch.cuda.device(x.device):
+        st = _lib.rmsnorm_bwd(_p(dy), _p(x), _p(w), _p(rstd), _p(dx), _p(dw), _p(workspace),
+                              workspace.numel() * workspace.element_size(), M, N,
+                              _code(x, "x"), _code(w, "w"), _stream(x))
+    if st != 0:
+        raise AddRmsError(st, "rmsnorm_bwd")
+    return dx, dw

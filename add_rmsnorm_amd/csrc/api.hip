@@ -1,0 +1,485 @@
+// C ABI of the library (declared in include/addrms.h): argument validation,
+// variant choice, grid sizing and launch on the caller's stream.
+//
+// Validation happens before any HIP call.  The library allocates nothing; the
+// only state is a per-device cache of CU counts and kernel occupancies.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "addrms.h"
+#include "internal.hpp"
+
+namespace addrms {
+
+const FwdTable &fwd_table_0();
+const FwdTable &fwd_table_1();
+const FwdTable &fwd_table_2();
+const FwdTable &fwd_table_3();
+const BwdTable &bwd_table_0();
+const BwdTable &bwd_table_1();
+const BwdTable &bwd_table_2();
+const BwdTable &bwd_table_3();
+
+const FwdTable &fwd_table(int c)
+{
+    switch (c) {
+    case 0: return fwd_table_0();
+    case 1: return fwd_table_1();
+    case 2: return fwd_table_2();
+    default: return fwd_table_3();
+    }
+}
+
+const BwdTable &bwd_table(int c)
+{
+    switch (c) {
+    case 0: return bwd_table_0();
+    case 1: return bwd_table_1();
+    case 2: return bwd_table_2();
+    default: return bwd_table_3();
+    }
+}
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxPartials = 1024; // dw partial rows (workspace rows)
+constexpr size_t kMaxDynLds = 65536;
+
+int fail_hip(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return ADDRMS_ERR_HIP;
+}
+
+bool dtype_ok(int d) { return d == ADDRMS_F32 || d == ADDRMS_BF16; }
+size_t esize(int d) { return d == ADDRMS_F32 ? 4 : 2; }
+int vec_elems(int d) { return d == ADDRMS_F32 ? 4 : 8; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Integer knob from the environment (0 when unset or not a number).  Read on
+// every call so that tests can switch variants inside one process.
+int env_int(const char *name)
+{
+    const char *s = std::getenv(name);
+    return s ? std::atoi(s) : 0;
+}
+
+// Byte range of a buffer.
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+};
+Span span(const void *p, size_t bytes)
+{
+    Span s;
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + bytes;
+    return s;
+}
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+// An output may be the very same buffer as an input of its shape, or disjoint.
+bool bad_alias(Span out, Span in, bool same_ok)
+{
+    if (!overlaps(out, in))
+        return false;
+    return !(same_ok && out.lo == in.lo && out.hi == in.hi);
+}
+
+// Shape check shared by every entry point: M >= 0, N >= 1, N and the element
+// count in range.
+int check_shape(int64_t M, int64_t N, int dtype)
+{
+    if (M < 0 || N <= 0 || N > INT_MAX)
+        return ADDRMS_ERR_SHAPE;
+    if (M > 0 && (uint64_t)M > ((uint64_t)1 << 62) / ((uint64_t)N * esize(dtype)))
+        return ADDRMS_ERR_SHAPE;
+    return ADDRMS_OK;
+}
+
+// ---- device facts (cached) --------------------------------------------------
+
+std::mutex g_mu;
+std::map<int, int> g_cus;
+std::map<std::tuple<int, const void *, size_t>, int> g_occ;
+
+int device_cus(int dev, int *cus)
+{
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_cus.find(dev);
+        if (it != g_cus.end()) {
+            *cus = it->second;
+            return ADDRMS_OK;
+        }
+    }
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_cus[dev] = n;
+    *cus = n;
+    return ADDRMS_OK;
+}
+
+// Resident blocks per CU of a kernel (ADDRMS_BLOCKS_PER_CU overrides).
+int blocks_per_cu(int dev, const KernelRef &k, size_t smem, int *out)
+{
+    const int forced = env_int("ADDRMS_BLOCKS_PER_CU");
+    if (forced > 0) {
+        *out = forced;
+        return ADDRMS_OK;
+    }
+    auto key = std::make_tuple(dev, k.fn, smem);
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_occ.find(key);
+        if (it != g_occ.end()) {
+            *out = it->second;
+            return ADDRMS_OK;
+        }
+    }
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k.fn, k.block, smem);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    if (n < 1)
+        n = 1;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_occ[key] = n;
+    *out = n;
+    return ADDRMS_OK;
+}
+
+// Persistent grid: no more blocks than the device holds at once, and no more
+// than there is work for.
+int persistent_grid(const KernelRef &k, size_t smem, int64_t blocks_needed, int64_t cap,
+                    int *grid)
+{
+    int dev = 0, cus = 0, per_cu = 0, rc;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    if ((rc = device_cus(dev, &cus)) != ADDRMS_OK)
+        return rc;
+    if ((rc = blocks_per_cu(dev, k, smem, &per_cu)) != ADDRMS_OK)
+        return rc;
+    int64_t g = (int64_t)cus * per_cu;
+    if (g > blocks_needed)
+        g = blocks_needed;
+    if (g > cap)
+        g = cap;
+    if (g < 1)
+        g = 1;
+    *grid = (int)g;
+    return ADDRMS_OK;
+}
+
+int launch(const KernelRef &k, dim3 grid, size_t smem, void *args, hipStream_t s)
+{
+    void *argv[] = {args};
+    hipError_t e = hipLaunchKernel(k.fn, grid, dim3(k.block), argv, smem, s);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    return ADDRMS_OK;
+}
+
+int device_cus_current(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    return device_cus(dev, cus);
+}
+
+// Index of the smallest supported VPL >= need, or -1.
+int vpl_index(int need)
+{
+    for (int i = 0; i < kNumVpl; ++i)
+        if (kVplList[i] >= need)
+            return i;
+    return -1;
+}
+
+// Forward variant: the fewest waves per row that still give every SIMD a wave
+// (M * WPR >= 4 * CUs), so wide rows or few rows spread over more waves.
+// ADDRMS_FWD_WPR forces a WPR when it fits.
+bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
+{
+    const int forced = env_int("ADDRMS_FWD_WPR");
+    int fallback_wi = -1, fallback_vi = -1;
+    for (int wi = 0; wi < kNumWpr; ++wi) {
+        const int wpr = kWprList[wi];
+        const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
+        const int vi = vpl_index(need);
+        if (vi < 0 || !fwd_built(wpr, kVplList[vi]))
+            continue;
+        if (forced > 0) {
+            if (wpr == forced) {
+                *wi_out = wi;
+                *vi_out = vi;
+                return true;
+            }
+            if (fallback_wi < 0) {
+                fallback_wi = wi;
+                fallback_vi = vi;
+            }
+            continue;
+        }
+        if (M * wpr >= 4LL * cus || wpr == kWprList[kNumWpr - 1] || need == 1) {
+            *wi_out = wi;
+            *vi_out = vi;
+            return true;
+        }
+    }
+    if (fallback_wi >= 0) {
+        *wi_out = fallback_wi;
+        *vi_out = fallback_vi;
+        return true;
+    }
+    return false;
+}
+
+// Backward variant: WPR in {1, 2, 4}; prefer at most 8 vectors per lane (the
+// dw accumulators live in registers), enough waves to fill the device, and a
+// dw exchange that fits in 64 KiB of LDS.  ADDRMS_BWD_WPR forces a WPR.
+bool pick_bwd(int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
+{
+    const int forced = env_int("ADDRMS_BWD_WPR");
+    int best_wi = -1, best_vi = -1;
+    for (int pass = 0; pass < 2 && best_wi < 0; ++pass) {
+        const int max_vpl = pass == 0 ? 8 : kMaxVpl;
+        for (int wi = 0; wi < kBwdNumWpr; ++wi) {
+            const int wpr = kWprList[wi];
+            const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
+            const int vi = vpl_index(need);
+            const int rpb = 4 / wpr;
+            if (vi < 0 || kVplList[vi] > max_vpl)
+                continue;
+            if ((size_t)(rpb / 2) * (size_t)N * 4u > kMaxDynLds)
+                continue;
+            if (forced > 0 && wpr != forced)
+                continue;
+            if (forced > 0 || M * wpr >= 4LL * cus || wi == kBwdNumWpr - 1) {
+                best_wi = wi;
+                best_vi = vi;
+                break;
+            }
+            if (best_wi < 0) { // remember the first fit in case none fills the device
+                best_wi = wi;
+                best_vi = vi;
+            }
+        }
+    }
+    if (best_wi < 0)
+        return false;
+    *wi_out = best_wi;
+    *vi_out = best_vi;
+    return true;
+}
+
+// dw[c] = sum over P partial rows of ws[:, c] (P = 0 writes zeros; ws unread).
+int colreduce(const void *workspace, int P, int N, float *dw, hipStream_t s)
+{
+    const float *ws = static_cast<const float *>(workspace);
+    const KernelRef k = colreduce_kernel();
+    void *argv[] = {(void *)&ws, (void *)&P, (void *)&N, (void *)&dw};
+    hipError_t e = hipLaunchKernel(k.fn, dim3((unsigned)((N + kColReduceCols - 1) / kColReduceCols)),
+                                   dim3(k.block), argv, 0, s);
+    return e == hipSuccess ? ADDRMS_OK : fail_hip(e);
+}
+
+int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, float *rstd,
+               int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream, bool fused)
+{
+    // ---- validation (no HIP call) ----
+    // With M == 0 the matrices are empty and may be NULL.
+    if (!w || (M != 0 && (!x || !y || (fused && (!r || !res)))))
+        return ADDRMS_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
+        return ADDRMS_ERR_DTYPE;
+    int rc = check_shape(M, N, dtype);
+    if (rc != ADDRMS_OK)
+        return rc;
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return ADDRMS_ERR_EPS;
+    const size_t mat = (size_t)M * (size_t)N * esize(dtype);
+    const Span sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype)), sy = span(y, mat);
+    const Span sr = fused ? span(r, mat) : Span{}, sres = fused ? span(res, mat) : Span{};
+    const Span srs = rstd ? span(rstd, (size_t)M * 4u) : Span{};
+    if (bad_alias(sy, sx, true) || bad_alias(sy, sw, false) || bad_alias(sy, srs, false))
+        return ADDRMS_ERR_ALIAS;
+    if (fused && (bad_alias(sy, sr, true) || bad_alias(sres, sx, true) ||
+                  bad_alias(sres, sr, true) || bad_alias(sres, sw, false) ||
+                  bad_alias(sres, srs, false) || bad_alias(sres, sy, false)))
+        return ADDRMS_ERR_ALIAS;
+    if (rstd && (bad_alias(srs, sx, false) || bad_alias(srs, sw, false) ||
+                 (fused && bad_alias(srs, sr, false))))
+        return ADDRMS_ERR_ALIAS;
+    if (M == 0)
+        return ADDRMS_OK;
+
+    // ---- variant and launch ----
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int c = combo(dtype, w_dtype);
+    const FwdTable &tab = fwd_table(c);
+    FwdArgs a{x, fused ? r : x, w, y, fused ? res : y, rstd, M, (int)N, 0, eps};
+
+    const int nv = vec_elems(dtype);
+    const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(x) &&
+                        aligned16(w) && aligned16(y) &&
+                        (!fused || (aligned16(r) && aligned16(res)));
+    int cus = 0;
+    if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
+        return rc;
+    int wi = 0, vi = 0;
+    if (vec_ok && pick_fwd(M, (int)(N / nv), cus, &wi, &vi)) {
+        a.nvec = (int)(N / nv);
+        const KernelRef &k = tab.vec[fused ? 1 : 0][wi][vi];
+        const int rpb = kWprList[wi] == 1 ? 4 : 1;
+        int grid = 0;
+        if ((rc = persistent_grid(k, 0, (M + rpb - 1) / rpb, INT_MAX, &grid)) != ADDRMS_OK)
+            return rc;
+        return launch(k, dim3(grid), 0, &a, s);
+    }
+    const KernelRef &k = tab.elem[fused ? 1 : 0];
+    int grid = 0;
+    if ((rc = persistent_grid(k, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
+        return rc;
+    return launch(k, dim3(grid), 0, &a, s);
+}
+
+} // namespace
+} // namespace addrms
+
+using namespace addrms;
+
+extern "C" {
+
+int rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int64_t M, int64_t N,
+                float eps, int dtype, int w_dtype, void *stream)
+{
+    return fwd_common(x, nullptr, w, y, nullptr, rstd, M, N, eps, dtype, w_dtype, stream, false);
+}
+
+int add_rmsnorm_fwd(const void *x, const void *r, const void *w, void *y, void *residual_out,
+                    float *rstd, int64_t M, int64_t N, float eps, int dtype, int w_dtype,
+                    void *stream)
+{
+    return fwd_common(x, r, w, y, residual_out, rstd, M, N, eps, dtype, w_dtype, stream, true);
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N)
+{
+    if (M <= 0 || N <= 0)
+        return 0;
+    const uint64_t rows = (uint64_t)(M < kMaxPartials ? M : kMaxPartials);
+    if ((uint64_t)N > (uint64_t)SIZE_MAX / 4u / rows)
+        return 0;
+    return (size_t)(rows * (uint64_t)N * 4u);
+}
+
+int rmsnorm_bwd(const void *dy, const void *x, const void *w, const float *rstd, void *dx,
+                float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                int dtype, int w_dtype, void *stream)
+{
+    // ---- validation (no HIP call) ----
+    // With M == 0 the row data is empty and may be NULL; dw is still written.
+    if (!w || !dw || (M != 0 && (!dy || !x || !rstd || !dx)))
+        return ADDRMS_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
+        return ADDRMS_ERR_DTYPE;
+    int rc = check_shape(M, N, dtype);
+    if (rc != ADDRMS_OK)
+        return rc;
+    const size_t need = rmsnorm_bwd_workspace_bytes(M, N);
+    if (M > 0 && (!workspace || workspace_bytes < need || need == 0))
+        return ADDRMS_ERR_WORKSPACE;
+    const size_t mat = (size_t)M * (size_t)N * esize(dtype);
+    const Span sdy = span(dy, mat), sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype));
+    const Span srs = span(rstd, (size_t)M * 4u), sdx = span(dx, mat), sdw = span(dw, (size_t)N * 4u);
+    const Span sws = workspace ? span(workspace, need) : Span{};
+    if (bad_alias(sdx, sdy, true) || bad_alias(sdx, sx, true) || bad_alias(sdx, sw, false) ||
+        bad_alias(sdx, srs, false) || bad_alias(sdx, sdw, false) || bad_alias(sdx, sws, false))
+        return ADDRMS_ERR_ALIAS;
+    if (bad_alias(sdw, sdy, false) || bad_alias(sdw, sx, false) || bad_alias(sdw, sw, false) ||
+        bad_alias(sdw, srs, false) || bad_alias(sdw, sws, false))
+        return ADDRMS_ERR_ALIAS;
+    if (bad_alias(sws, sdy, false) || bad_alias(sws, sx, false) || bad_alias(sws, sw, false) ||
+        bad_alias(sws, srs, false))
+        return ADDRMS_ERR_ALIAS;
+
+    // ---- variant and launch ----
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (M == 0) // dw of an empty batch is zero: the column reduce over P = 0 rows writes it
+        return colreduce(workspace, 0, (int)N, dw, s);
+    const BwdTable &tab = bwd_table(combo(dtype, w_dtype));
+    const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u));
+    const int64_t pmax = ws_rows < kMaxPartials ? ws_rows : kMaxPartials;
+    BwdArgs a{dy, x, w, rstd, dx, static_cast<float *>(workspace), M, (int)N, 0, 0, 0};
+
+    const int nv = vec_elems(dtype);
+    const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(dy) &&
+                        aligned16(x) && aligned16(w) && aligned16(dx) && aligned16(workspace);
+    int cus = 0;
+    if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
+        return rc;
+    int wi = 0, vi = 0;
+    if (vec_ok && pick_bwd(M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
+        a.nvec = (int)(N / nv);
+        const KernelRef &k = tab.vec[wi][vi];
+        const int rpb = 4 / kWprList[wi];
+        const size_t smem = (size_t)(rpb / 2) * (size_t)N * 4u;
+        int grid = 0;
+        if ((rc = persistent_grid(k, smem, (M + rpb - 1) / rpb, pmax, &grid)) != ADDRMS_OK)
+            return rc;
+        a.P = grid;
+        if ((rc = launch(k, dim3(grid), smem, &a, s)) != ADDRMS_OK)
+            return rc;
+    } else {
+        // element-wise: dw partials over row chunks first (reads dy, x intact),
+        // then dx (which may overwrite dy or x)
+        int64_t chunk = (M + pmax - 1) / pmax;
+        const int64_t P = (M + chunk - 1) / chunk;
+        a.P = (int)P;
+        a.chunk = chunk;
+        if ((rc = launch(tab.elem_dw, dim3((unsigned)((N + 63) / 64), (unsigned)P), 0, &a, s)) !=
+            ADDRMS_OK)
+            return rc;
+        int grid = 0;
+        if ((rc = persistent_grid(tab.elem_dx, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
+            return rc;
+        if ((rc = launch(tab.elem_dx, dim3(grid), 0, &a, s)) != ADDRMS_OK)
+            return rc;
+    }
+    // dw = column sums of the partials, same stream (ordered after stage 1)
+    return colreduce(workspace, a.P, (int)N, dw, s);
+}
+
+const char *addrms_status_str(int status)
+{
+    switch (status) {
+    case ADDRMS_OK: return "ok";
+    case ADDRMS_ERR_NULL: return "a required pointer is NULL";
+    case ADDRMS_ERR_SHAPE: return "invalid shape (M < 0, N <= 0, or too large)";
+    case ADDRMS_ERR_DTYPE: return "unknown element type";
+    case ADDRMS_ERR_EPS: return "eps must be finite and >= 0";
+    case ADDRMS_ERR_ALIAS: return "output overlaps another argument";
+    case ADDRMS_ERR_WORKSPACE: return "workspace missing or too small";
+    case ADDRMS_ERR_HIP: return "HIP call failed";
+    default: return "unknown status";
+    }
+}
+
+int addrms_last_hip_error(void) { return g_last_hip_error; }
+
+} // extern "C"

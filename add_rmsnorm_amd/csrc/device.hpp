@@ -1,0 +1,217 @@
+// Device-side building blocks for the gfx950 RMSNorm kernels: 128-bit vector
+// element access, bfloat16 packing, and the wave64 / workgroup float sums.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace addrms {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Storage tag for bfloat16 (the upper half of a binary32); never computed on.
+struct bf16_t {
+    uint16_t bits;
+};
+
+// Elements of T in one 16-byte vector.
+template <typename T> struct Vec;
+template <> struct Vec<float> { static constexpr int n = 4; };
+template <> struct Vec<bf16_t> { static constexpr int n = 8; };
+
+// ---- bfloat16 <-> float ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two floats -> two bfloat16 in one dword (a in the low half), each rounded to
+// nearest-even by the hardware converter v_cvt_pk_bf16_f32 (NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float a) { return (uint16_t)pack_bf16x2(a, 0.0f); }
+
+// ---- one 16-byte vector <-> floats -------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[Vec<T>::n]);
+
+template <>
+__device__ __forceinline__ void unpack<float>(const u32x4 &v, float (&f)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        f[i] = __uint_as_float(v[i]);
+}
+
+template <>
+__device__ __forceinline__ void unpack<bf16_t>(const u32x4 &v, float (&f)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(v[i]);
+        f[2 * i + 1] = bf16_hi(v[i]);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 pack(const float (&f)[Vec<T>::n]);
+
+template <>
+__device__ __forceinline__ u32x4 pack<float>(const float (&f)[4])
+{
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        v[i] = __float_as_uint(f[i]);
+    return v;
+}
+
+template <>
+__device__ __forceinline__ u32x4 pack<bf16_t>(const float (&f)[8])
+{
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return v;
+}
+
+// ---- global memory -----------------------------------------------------------
+
+// Streaming loads/stores of row data.  Policy bits: 1 = non-temporal loads,
+// 2 = non-temporal stores (the data is touched once; keep it out of the way
+// of the weight vector in the caches).
+template <int POL>
+__device__ __forceinline__ u32x4 ld_stream(const u32x4 *p)
+{
+    if constexpr (POL & 1)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <int POL>
+__device__ __forceinline__ void st_stream(u32x4 *p, const u32x4 &v)
+{
+    if constexpr (POL & 2)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+// The weights matching vector index v of a row of T: Vec<T>::n consecutive
+// elements of w (stored as WT), as floats.  w is 16-byte aligned.
+template <typename T, typename WT>
+__device__ __forceinline__ void load_w(const void *w, int v, float (&f)[Vec<T>::n])
+{
+    constexpr int n = Vec<T>::n;
+    if constexpr (sizeof(WT) == 4 && n == 4) { // float weights, float rows
+        u32x4 a = reinterpret_cast<const u32x4 *>(w)[v];
+        unpack<float>(a, f);
+    } else if constexpr (sizeof(WT) == 4 && n == 8) { // float weights, bf16 rows
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(w) + 2 * v;
+        u32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = __uint_as_float(a[i]);
+            f[4 + i] = __uint_as_float(b[i]);
+        }
+    } else if constexpr (sizeof(WT) == 2 && n == 8) { // bf16 weights, bf16 rows
+        u32x4 a = reinterpret_cast<const u32x4 *>(w)[v];
+        unpack<bf16_t>(a, f);
+    } else { // bf16 weights, float rows
+        u32x2 a = reinterpret_cast<const u32x2 *>(w)[v];
+        f[0] = bf16_lo(a[0]);
+        f[1] = bf16_hi(a[0]);
+        f[2] = bf16_lo(a[1]);
+        f[3] = bf16_hi(a[1]);
+    }
+}
+
+// Scalar element access for the unaligned/element-wise path.
+template <typename T> __device__ __forceinline__ float ld_elem(const void *p, int64_t i);
+template <> __device__ __forceinline__ float ld_elem<float>(const void *p, int64_t i)
+{
+    return reinterpret_cast<const float *>(p)[i];
+}
+template <> __device__ __forceinline__ float ld_elem<bf16_t>(const void *p, int64_t i)
+{
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
+}
+template <typename T> __device__ __forceinline__ void st_elem(void *p, int64_t i, float v);
+template <> __device__ __forceinline__ void st_elem<float>(void *p, int64_t i, float v)
+{
+    reinterpret_cast<float *>(p)[i] = v;
+}
+template <> __device__ __forceinline__ void st_elem<bf16_t>(void *p, int64_t i, float v)
+{
+    reinterpret_cast<uint16_t *>(p)[i] = to_bf16(v);
+}
+// The value an element has once stored as T (the rounding a store applies).
+template <typename T> __device__ __forceinline__ float as_stored(float v);
+template <> __device__ __forceinline__ float as_stored<float>(float v) { return v; }
+template <> __device__ __forceinline__ float as_stored<bf16_t>(float v)
+{
+    return __uint_as_float((uint32_t)to_bf16(v) << 16);
+}
+
+// ---- reductions --------------------------------------------------------------
+
+#define ADDRMS_DPP(v, ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
+
+// Sum over the 64 lanes of a wave, result in every lane (a wave-uniform value).
+// Within each 16-lane row: DPP quad_perm [1,0,3,2] and [2,3,0,1] give quad
+// sums, row_half_mirror pairs quads into 8-lane sums, row_mirror pairs halves
+// into 16-lane sums.  The four row sums are then read with v_readlane.  Every
+// lane must be active.  The order is fixed, so results are deterministic.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += ADDRMS_DPP(v, 0xB1);  // quad_perm [1,0,3,2]
+    v += ADDRMS_DPP(v, 0x4E);  // quad_perm [2,3,0,1]
+    v += ADDRMS_DPP(v, 0x141); // row_half_mirror
+    v += ADDRMS_DPP(v, 0x140); // row_mirror
+    const int b = __builtin_bit_cast(int, v);
+    float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// The same sum for doubles (each DPP step moves both 32-bit halves).
+template <int CTRL> __device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+#undef ADDRMS_DPP
+
+} // namespace addrms

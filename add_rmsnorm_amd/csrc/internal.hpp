@@ -1,0 +1,90 @@
+// Internal interface between the C-ABI dispatcher and the kernel translation
+// units: argument blocks and the per-dtype kernel tables.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace addrms {
+
+// Forward arguments (plain op: r and residual_out are unused).
+struct FwdArgs {
+    const void *x;
+    const void *r;
+    const void *w;
+    void *y;
+    void *res;
+    float *rstd; // may be null
+    int64_t M;
+    int N;
+    int nvec; // 16-byte vectors per row (vector path)
+    float eps;
+};
+
+// Backward arguments.
+struct BwdArgs {
+    const void *dy;
+    const void *x;
+    const void *w;
+    const float *rstd;
+    void *dx;
+    float *ws; // [P, N] float partial sums of dw
+    int64_t M;
+    int N;
+    int nvec;
+    int P;          // partial rows (element-wise path: row chunks)
+    int64_t chunk;  // rows per chunk (element-wise dw path)
+};
+
+// Supported shapes of the vector kernels: waves per row and 16-byte vectors per
+// lane.  A row of nvec vectors needs WPR * 64 * VPL >= nvec.
+constexpr int kWprList[] = {1, 2, 4, 8, 16};
+constexpr int kNumWpr = 5;
+constexpr int kVplList[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
+constexpr int kNumVpl = 12;
+constexpr int kMaxVpl = 16;
+
+// Backward vector kernels use 256-thread blocks and WPR in {1, 2, 4}.
+constexpr int kBwdNumWpr = 3;
+
+constexpr int kBlockFwd(int wpr) { return wpr == 1 ? 256 : 64 * wpr; }
+
+// Forward (WPR, VPL) pairs that are built: 512- and 1024-thread blocks get at
+// most 256 / 128 VGPRs per lane, so they only take rows short enough per lane
+// to stay in registers.
+constexpr bool fwd_built(int wpr, int vpl)
+{
+    return wpr <= 4 || (wpr == 8 && vpl <= 8) || (wpr == 16 && vpl <= 4);
+}
+constexpr int kBwdBlock = 256;
+constexpr int kColReduceCols = 64; // dw columns per column-reduce block
+
+// A kernel entry: function, block size, dynamic LDS bytes (backward: per
+// column of N), and whether it is an element-wise fallback.
+struct KernelRef {
+    const void *fn;
+    int block;
+};
+
+// Dtype combination index: (row dtype, weight dtype) -> 0..3, with
+// dtype codes ADDRMS_F32 = 0, ADDRMS_BF16 = 1.
+inline int combo(int dtype, int w_dtype) { return dtype * 2 + w_dtype; }
+
+// Kernel tables, one translation unit per dtype combination.
+// fwd_vec: [fused][wpr_idx][vpl_idx]; fwd_elem: [fused].
+struct FwdTable {
+    KernelRef vec[2][kNumWpr][kNumVpl];
+    KernelRef elem[2];
+};
+struct BwdTable {
+    KernelRef vec[kBwdNumWpr][kNumVpl];
+    KernelRef elem_dx;
+    KernelRef elem_dw;
+};
+
+const FwdTable &fwd_table(int combo_idx);
+const BwdTable &bwd_table(int combo_idx);
+KernelRef colreduce_kernel();
+
+} // namespace addrms

@@ -1,0 +1,503 @@
+// HIP kernels for gfx950 (CDNA4): RMSNorm and fused residual-Add + RMSNorm,
+// forward and backward.
+//
+// The operations are the RMSNorm and fused Add + RMSNorm ops named by the
+// "Machete" README ("Built-In Areas") and the KernelAgent digest (the
+// KernelAgent-Oink summary); the row reduction follows the "CuTe DSL" skill
+// page's float32 pattern for RMSNorm (Workflow 0: per-thread loops, a
+// butterfly within the warp, then a cross-warp step through shared memory),
+// which here becomes per-lane FMAs, a DPP wave64 sum, and an LDS step only when
+// several waves share a row.
+//
+// Memory traffic is the whole cost (a few VALU ops per 2-4 bytes moved), so
+// the design is about HBM streaming, not arithmetic:
+//   * each row is read once into registers with 128-bit loads (one wave64
+//     covers 1 KiB per load instruction, fully coalesced), normalised from
+//     registers, and written once: x, r read once; y, residual_out written
+//     once;
+//   * a persistent grid walks rows with a grid stride; the host sizes it to
+//     the resident capacity of the device;
+//   * one wave per row needs no barrier at all; wide rows or few rows use
+//     several waves per row and one LDS exchange per row.
+#pragma once
+
+#include <utility>
+
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace addrms {
+
+// Cache policy of the streamed row data (see ld_stream / st_stream).
+#ifndef ADDRMS_STREAM_POLICY
+#define ADDRMS_STREAM_POLICY 0
+#endif
+constexpr int kPol = ADDRMS_STREAM_POLICY;
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Arithmetic type of the backward's row reduction and dx.  float32 tensors use
+// binary64: dx = rstd * (g - xh * c) cancels when xh * c is close to g (always
+// so for very short rows), and the float32 products and sum would then leave
+// too few correct bits for a float32 result.  bfloat16 tensors use float32.
+template <typename T> struct BwdCompute { using type = float; };
+template <> struct BwdCompute<float> { using type = double; };
+
+// 1/N in the compute type.
+template <typename CT> __device__ __forceinline__ CT inv_n_ct(int N) { return (CT)1 / (CT)N; }
+
+__device__ __forceinline__ float fma_ct(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_ct(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
+// ---------------------------------------------------------------------------
+// Forward, vector path.  WPR waves per row, VPL 16-byte vectors per lane:
+// lane `l` of wave `q` (of the row's WPR waves) owns vectors
+// v = q*64 + l + k*64*WPR, k < VPL.  Requires 16-byte aligned rows.
+// ---------------------------------------------------------------------------
+template <typename T, typename WT, bool FUSED, int WPR, int VPL>
+__global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
+{
+    constexpr int NV = Vec<T>::n;
+    constexpr int VSTRIDE = 64 * WPR;
+    constexpr int RPB = kBlockFwd(WPR) / (64 * WPR); // rows per block step
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int rib = (WPR == 1) ? wave : 0;
+    const int wir = (WPR == 1) ? 0 : wave;
+    const int vbase = wir * 64 + lane;
+    const int nvec = a.nvec;
+    const float inv_n = 1.0f / (float)a.N;
+
+    __shared__ float part[2][16];
+
+    const int64_t step = (int64_t)gridDim.x * RPB;
+    int it = 0;
+    for (int64_t row = (int64_t)blockIdx.x * RPB + rib; row < a.M; row += step, ++it) {
+        const size_t base = (size_t)row * (size_t)a.N;
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.x) + base);
+        const u32x4 *rp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.r) + base);
+        u32x4 *yp = reinterpret_cast<u32x4 *>(static_cast<T *>(a.y) + base);
+        u32x4 *resp = reinterpret_cast<u32x4 *>(static_cast<T *>(a.res) + base);
+
+        // 1. issue every load of the row before any use
+        u32x4 hv[VPL];
+        u32x4 rv[FUSED ? VPL : 1];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            if (v < nvec) {
+                hv[k] = ld_stream<kPol>(xp + v);
+                if constexpr (FUSED)
+                    rv[k] = ld_stream<kPol>(rp + v);
+            } else {
+                hv[k] = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (FUSED)
+                    rv[k] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+
+        // 2. residual add (float32), store the residual as T, and sum squares
+        //    of the stored residual
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float h[NV];
+            unpack<T>(hv[k], h);
+            if constexpr (FUSED) {
+                float rr[NV];
+                unpack<T>(rv[k], rr);
+#pragma unroll
+                for (int e = 0; e < NV; ++e)
+                    h[e] = h[e] + rr[e];
+                hv[k] = pack<T>(h); // rounds to T (bf16: RNE)
+                unpack<T>(hv[k], h);
+                const int v = vbase + k * VSTRIDE;
+                if (v < nvec)
+                    st_stream<kPol>(resp + v, hv[k]);
+            }
+#pragma unroll
+            for (int e = 0; e < NV; ++e)
+                ss = __builtin_fmaf(h[e], h[e], ss);
+        }
+
+        // 3. row sum -> rstd
+        float tot = wave_sum(ss);
+        if constexpr (WPR > 1) {
+            if (lane == 0)
+                part[it & 1][wir] = tot;
+            __syncthreads();
+            tot = 0.0f;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i)
+                tot += part[it & 1][i];
+        }
+        const float rs = 1.0f / __builtin_sqrtf(tot * inv_n + a.eps);
+        if (a.rstd != nullptr && wir == 0 && lane == 0)
+            a.rstd[row] = rs;
+
+        // 4. y = h * rstd * w, rounded once to T
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            if (v < nvec) {
+                float h[NV], wf[NV], o[NV];
+                unpack<T>(hv[k], h);
+                load_w<T, WT>(a.w, v, wf);
+#pragma unroll
+                for (int e = 0; e < NV; ++e)
+                    o[e] = (h[e] * rs) * wf[e];
+                st_stream<kPol>(yp + v, pack<T>(o));
+            }
+        }
+    }
+}
+
+// Block-wide sum for 256-thread blocks; `slot` alternates between calls so one
+// barrier per call suffices.
+template <typename S>
+__device__ __forceinline__ S block256_sum(S v, S (&part)[2][4], int slot)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    S t = wave_sum(v);
+    if (lane == 0)
+        part[slot][wave] = t;
+    __syncthreads();
+    return (part[slot][0] + part[slot][1]) + (part[slot][2] + part[slot][3]);
+}
+
+// ---------------------------------------------------------------------------
+// Forward, element-wise path: any N, any alignment.  One 256-thread block per
+// row, two passes over the row (the second re-reads the stored residual).
+// ---------------------------------------------------------------------------
+template <typename T, typename WT, bool FUSED>
+__global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
+{
+    __shared__ float part[2][4];
+    const int tid = threadIdx.x;
+    const int N = a.N;
+    const float inv_n = 1.0f / (float)N;
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x, ++it) {
+        const int64_t base = row * (int64_t)N;
+        float ss = 0.0f;
+        for (int j = tid; j < N; j += 256) {
+            float h;
+            if constexpr (FUSED) {
+                const float s = ld_elem<T>(a.x, base + j) + ld_elem<T>(a.r, base + j);
+                st_elem<T>(a.res, base + j, s);
+                h = as_stored<T>(s);
+            } else {
+                h = ld_elem<T>(a.x, base + j);
+            }
+            ss = __builtin_fmaf(h, h, ss);
+        }
+        const float tot = block256_sum(ss, part, it & 1);
+        const float rs = 1.0f / __builtin_sqrtf(tot * inv_n + a.eps);
+        if (a.rstd != nullptr && tid == 0)
+            a.rstd[row] = rs;
+        for (int j = tid; j < N; j += 256) {
+            const float h = FUSED ? ld_elem<T>(a.res, base + j) : ld_elem<T>(a.x, base + j);
+            st_elem<T>(a.y, base + j, (h * rs) * ld_elem<WT>(a.w, j));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, vector path, 256-thread blocks, WPR in {1, 2, 4}: RPB = 4 / WPR
+// rows per block step.  Each lane keeps its columns' dw partial sums in
+// registers across all rows it visits; at the end the block's row groups are
+// summed through LDS (pairwise, fixed order) and written as one row of the
+// workspace: ws[blockIdx.x, :].  Dynamic LDS: (RPB / 2) * N floats.
+// ---------------------------------------------------------------------------
+template <typename T, typename WT, int WPR, int VPL>
+__global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
+{
+    constexpr int NV = Vec<T>::n;
+    constexpr int VSTRIDE = 64 * WPR;
+    constexpr int RPB = 4 / WPR;
+    using CT = typename BwdCompute<T>::type;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    __shared__ CT part[2][4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int rib = wave / WPR;
+    const int wir = wave % WPR;
+    const int vbase = wir * 64 + lane;
+    const int nvec = a.nvec;
+    const int N = a.N;
+
+    float acc[VPL][NV];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+#pragma unroll
+        for (int e = 0; e < NV; ++e)
+            acc[k][e] = 0.0f;
+
+    const int64_t step = (int64_t)gridDim.x * RPB;
+    int it = 0;
+    for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < a.M; row0 += step, ++it) {
+        const int64_t row = row0 + rib;
+        const bool active = row < a.M; // uniform per wave
+        const size_t base = (size_t)(active ? row : 0) * (size_t)N;
+        const u32x4 *dyp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dy) + base);
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.x) + base);
+        u32x4 *dxp = reinterpret_cast<u32x4 *>(static_cast<T *>(a.dx) + base);
+
+        u32x4 dyv[VPL], xv[VPL];
+        float rs = 0.0f;
+        if (active) {
+            rs = a.rstd[row];
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int v = vbase + k * VSTRIDE;
+                if (v < nvec) {
+                    dyv[k] = ld_stream<kPol>(dyp + v);
+                    xv[k] = ld_stream<kPol>(xp + v);
+                } else {
+                    dyv[k] = u32x4{0u, 0u, 0u, 0u};
+                    xv[k] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                dyv[k] = u32x4{0u, 0u, 0u, 0u};
+                xv[k] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+
+        // sum_j dy_j w_j x_j over the row
+        CT p = 0;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            if (v < nvec) {
+                float d[NV], xx[NV], wf[NV];
+                unpack<T>(dyv[k], d);
+                unpack<T>(xv[k], xx);
+                load_w<T, WT>(a.w, v, wf);
+#pragma unroll
+                for (int e = 0; e < NV; ++e)
+                    p = fma_ct((CT)d[e] * (CT)wf[e], (CT)xx[e], p);
+            }
+        }
+        p = wave_sum(p);
+        if constexpr (WPR > 1) {
+            if (lane == 0)
+                part[it & 1][wave] = p;
+            __syncthreads();
+            p = 0;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i)
+                p += part[it & 1][rib * WPR + i];
+        }
+        // c = mean_j(g_j * xh_j) = rstd * mean_j(dy_j w_j x_j)
+        const CT c = (p * (CT)rs) * (CT)inv_n_ct<CT>(N);
+
+        if (active) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int v = vbase + k * VSTRIDE;
+                if (v < nvec) {
+                    float d[NV], xx[NV], wf[NV], o[NV];
+                    unpack<T>(dyv[k], d);
+                    unpack<T>(xv[k], xx);
+                    load_w<T, WT>(a.w, v, wf);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) {
+                        const CT xh = (CT)xx[e] * (CT)rs;
+                        const CT g = (CT)d[e] * (CT)wf[e];
+                        o[e] = (float)((CT)rs * (g - xh * c));
+                        acc[k][e] = __builtin_fmaf(d[e], (float)xh, acc[k][e]);
+                    }
+                    st_stream<kPol>(dxp + v, pack<T>(o));
+                }
+            }
+        }
+    }
+
+    // dw: sum the block's RPB row groups (same columns) and write one row.
+    auto put = [&](float *dst) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            if (v < nvec) {
+                u32x4 *q = reinterpret_cast<u32x4 *>(dst + (size_t)v * NV);
+#pragma unroll
+                for (int h = 0; h < NV / 4; ++h)
+                    q[h] = u32x4{__float_as_uint(acc[k][4 * h]), __float_as_uint(acc[k][4 * h + 1]),
+                                 __float_as_uint(acc[k][4 * h + 2]), __float_as_uint(acc[k][4 * h + 3])};
+            }
+        }
+    };
+    auto add = [&](const float *src) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            if (v < nvec) {
+                const u32x4 *q = reinterpret_cast<const u32x4 *>(src + (size_t)v * NV);
+#pragma unroll
+                for (int h = 0; h < NV / 4; ++h) {
+                    const u32x4 t = q[h];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[k][4 * h + i] += __uint_as_float(t[i]);
+                }
+            }
+        }
+    };
+    float *out = a.ws + (size_t)blockIdx.x * (size_t)N;
+    if constexpr (RPB == 4) {
+        if (rib >= 2)
+            put(lds + (size_t)(rib - 2) * N);
+        __syncthreads();
+        if (rib < 2)
+            add(lds + (size_t)rib * N);
+        __syncthreads();
+        if (rib == 1)
+            put(lds);
+        __syncthreads();
+        if (rib == 0) {
+            add(lds);
+            put(out);
+        }
+    } else if constexpr (RPB == 2) {
+        if (rib == 1)
+            put(lds);
+        __syncthreads();
+        if (rib == 0) {
+            add(lds);
+            put(out);
+        }
+    } else {
+        put(out);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, element-wise path (any N, any alignment): dx one block per row in
+// two passes; dw partials per (column block, row chunk).  dw runs first, so dx
+// may overwrite dy or x.
+// ---------------------------------------------------------------------------
+template <typename T, typename WT>
+__global__ void __launch_bounds__(256) bwd_elem_dx_kernel(BwdArgs a)
+{
+    using CT = typename BwdCompute<T>::type;
+    __shared__ CT part[2][4];
+    const int tid = threadIdx.x;
+    const int N = a.N;
+    const CT inv_n = inv_n_ct<CT>(N);
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x, ++it) {
+        const int64_t base = row * (int64_t)N;
+        const CT rs = (CT)a.rstd[row];
+        CT p = 0;
+        for (int j = tid; j < N; j += 256)
+            p = fma_ct((CT)ld_elem<T>(a.dy, base + j) * (CT)ld_elem<WT>(a.w, j),
+                       (CT)ld_elem<T>(a.x, base + j), p);
+        const CT c = (block256_sum(p, part, it & 1) * rs) * inv_n;
+        for (int j = tid; j < N; j += 256) {
+            const CT xh = (CT)ld_elem<T>(a.x, base + j) * rs;
+            const CT g = (CT)ld_elem<T>(a.dy, base + j) * (CT)ld_elem<WT>(a.w, j);
+            st_elem<T>(a.dx, base + j, (float)(rs * (g - xh * c)));
+        }
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_elem_dw_kernel(BwdArgs a)
+{
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63;
+    const int s = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
+    const int64_t r0 = (int64_t)blockIdx.y * a.chunk;
+    const int64_t r1 = r0 + a.chunk < a.M ? r0 + a.chunk : a.M;
+    float acc = 0.0f;
+    if (c < a.N)
+        for (int64_t i = r0 + s; i < r1; i += 4) {
+            const int64_t idx = i * (int64_t)a.N + c;
+            acc = __builtin_fmaf(ld_elem<T>(a.dy, idx), ld_elem<T>(a.x, idx) * a.rstd[i], acc);
+        }
+    red[s][lane] = acc;
+    __syncthreads();
+    if (s == 0 && c < a.N)
+        a.ws[(size_t)blockIdx.y * a.N + c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+}
+
+// dw[c] = sum_p ws[p, c]: 64 columns x 4 row slices per block, fixed order.
+// (A template only so that each translation unit's copy is a weak symbol.)
+template <int Unused = 0>
+__global__ void __launch_bounds__(256) dw_colreduce_kernel(const float *ws, int P, int N, float *dw)
+{
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63;
+    const int s = threadIdx.x >> 6;
+    const int c = blockIdx.x * kColReduceCols + lane;
+    float acc = 0.0f;
+    if (c < N)
+        for (int p = s; p < P; p += 4)
+            acc += ws[(size_t)p * N + c];
+    red[s][lane] = acc;
+    __syncthreads();
+    if (s == 0 && c < N)
+        dw[c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel tables for one (row dtype, weight dtype) combination.
+// ---------------------------------------------------------------------------
+template <typename T, typename WT> struct TableBuilder {
+    template <bool F, int WPR, int VPL> static KernelRef fwd_ref()
+    {
+        if constexpr (fwd_built(WPR, VPL))
+            return KernelRef{reinterpret_cast<const void *>(&fwd_vec_kernel<T, WT, F, WPR, VPL>),
+                             kBlockFwd(WPR)};
+        else
+            return KernelRef{nullptr, 0};
+    }
+    template <bool F, int WI, int... VI>
+    static void fwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
+    {
+        ((row[VI] = fwd_ref<F, kWprList[WI], kVplList[VI]>()), ...);
+    }
+    template <bool F, int... WI>
+    static void fwd_all(FwdTable &t, std::integer_sequence<int, WI...>)
+    {
+        (fwd_row<F, WI>(t.vec[F ? 1 : 0][WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
+    }
+    static FwdTable fwd()
+    {
+        FwdTable t{};
+        fwd_all<false>(t, std::make_integer_sequence<int, kNumWpr>{});
+        fwd_all<true>(t, std::make_integer_sequence<int, kNumWpr>{});
+        t.elem[0] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, false>), 256};
+        t.elem[1] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, true>), 256};
+        return t;
+    }
+
+    template <int WI, int... VI>
+    static void bwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
+    {
+        ((row[VI] = KernelRef{reinterpret_cast<const void *>(
+                                  &bwd_vec_kernel<T, WT, kWprList[WI], kVplList[VI]>),
+                              kBwdBlock}),
+         ...);
+    }
+    template <int... WI> static void bwd_all(BwdTable &t, std::integer_sequence<int, WI...>)
+    {
+        (bwd_row<WI>(t.vec[WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
+    }
+    static BwdTable bwd()
+    {
+        BwdTable t{};
+        bwd_all(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        t.elem_dx = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT>), 256};
+        t.elem_dw = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dw_kernel<T>), 256};
+        return t;
+    }
+};
+
+} // namespace addrms

@@ -1,0 +1,133 @@
+/*
+ * addrms.h -- C ABI of the RMSNorm / fused residual-Add + RMSNorm library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (the pages name them; the formula is the textbook RMSNorm,
+ * Zhang & Sennrich 2019, with eps inside the square root):
+ *   - RMSNorm, an op of the "Machete" README ("Built-In Areas"), and the
+ *     fused residual Add + RMSNorm of KernelAgent-Oink (KernelAgent
+ *     repository digest, opening summary):
+ *         h      = x                                    (rmsnorm_fwd)
+ *         h      = residual_out = round(fp32(x) + fp32(r))   (add_rmsnorm_fwd)
+ *         rstd_i = 1 / sqrt(mean_j(h_ij^2) + eps)
+ *         y_ij   = round(h_ij * rstd_i * w_j)
+ *     The fused op normalises the residual exactly as it is stored, so its y
+ *     equals rmsnorm_fwd applied to residual_out, bit for bit.
+ *   - The backward the Machete README's autograd helpers ("Built-In Areas")
+ *     imply, the exact derivative given the saved rstd:
+ *         g = dy * w,  xh = x * rstd_i,  c_i = mean_j(g_ij * xh_ij)
+ *         dx_ij = round(rstd_i * (g_ij - xh_ij * c_i))
+ *         dw_j  = sum_i dy_ij * xh_ij                    (overwritten)
+ *
+ * Arithmetic: float32 throughout on the GPU; each output is rounded once to
+ * its storage type, round-to-nearest-even.  The residual add is a float32 add.
+ *
+ * Layout: every matrix is row-major and contiguous, M rows of N elements
+ * (row stride N).  w, dw have N elements; rstd has M.
+ *
+ * Memory and streams: every pointer argument is a DEVICE pointer.  The
+ * caller owns every buffer, including the backward's workspace; the library
+ * allocates nothing and keeps no per-call state.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL is the null stream) and the call returns
+ * without synchronising.  A device fault surfaces at the caller's next
+ * synchronisation, not in the return code.
+ *
+ * Alignment: any.  When every matrix pointer and w are 16-byte aligned and a
+ * row is a multiple of 16 bytes, 128-bit vector loads/stores are used;
+ * otherwise an element-wise path gives the same results.
+ *
+ * Aliasing: an output may be exactly the same buffer as an input of the same
+ * shape (y == x; residual_out == r or x; dx == dy or x).  Any other overlap
+ * between an output and any other argument is ADDRMS_ERR_ALIAS.
+ *
+ * Errors: arguments are validated before any HIP call; on error nothing is
+ * launched.  M == 0 is valid: the matrices and rstd may then be NULL, the
+ * forward launches nothing, and the backward only writes dw = 0.  Calls are
+ * thread-safe.
+ */
+#ifndef ADDRMS_H
+#define ADDRMS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+#define ADDRMS_F32 0  /* IEEE binary32 */
+#define ADDRMS_BF16 1 /* bfloat16: the upper 16 bits of a binary32 */
+
+/* Status codes: 0 on success, negative on error. */
+#define ADDRMS_OK 0
+#define ADDRMS_ERR_NULL -1      /* a required pointer is NULL */
+#define ADDRMS_ERR_SHAPE -2     /* M < 0, N <= 0, or M*N too large */
+#define ADDRMS_ERR_DTYPE -3     /* unknown element type code */
+#define ADDRMS_ERR_EPS -4       /* eps negative, NaN or infinite */
+#define ADDRMS_ERR_ALIAS -5     /* forbidden overlap between buffers */
+#define ADDRMS_ERR_WORKSPACE -6 /* workspace NULL or smaller than required */
+#define ADDRMS_ERR_HIP -7       /* a HIP call failed; see addrms_last_hip_error() */
+
+/*
+ * RMSNorm forward.
+ *   x     [M, N] dtype        input
+ *   w     [N]    w_dtype      per-column scale, multiplied as stored
+ *   y     [M, N] dtype        output; may be x itself
+ *   rstd  [M]    float32      optional output (NULL: not written); the
+ *                             rstd_i used, for the backward
+ *   eps   >= 0, finite
+ */
+int rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int64_t M, int64_t N,
+                float eps, int dtype, int w_dtype, void *stream);
+
+/*
+ * Fused residual-Add + RMSNorm forward (KernelAgent-Oink's fused op).
+ *   x, r          [M, N] dtype  inputs (x may equal r)
+ *   w             [N]    w_dtype
+ *   y             [M, N] dtype  output RMSNorm(residual_out) * w; may be x or r
+ *   residual_out  [M, N] dtype  output round(fp32(x) + fp32(r)); may be x or r
+ *                               (in-place residual update); must not be y
+ *   rstd          [M]    float32 optional output (NULL: not written)
+ */
+int add_rmsnorm_fwd(const void *x, const void *r, const void *w, void *y, void *residual_out,
+                    float *rstd, int64_t M, int64_t N, float eps, int dtype, int w_dtype,
+                    void *stream);
+
+/*
+ * Workspace, in bytes, that rmsnorm_bwd needs for these sizes: the float32
+ * per-workgroup partial sums of dw, min(M, 1024) rows of N.  Pure arithmetic,
+ * no HIP call.  Returns 0 for M <= 0 or N <= 0 (and for sizes whose byte count
+ * does not fit in size_t).
+ */
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N);
+
+/*
+ * RMSNorm backward from the saved rstd.
+ *   dy    [M, N] dtype     upstream gradient
+ *   x     [M, N] dtype     forward input
+ *   w     [N]    w_dtype
+ *   rstd  [M]    float32   saved by the forward (required)
+ *   dx    [M, N] dtype     output; may be dy or x
+ *   dw    [N]    float32   output, overwritten (not accumulated)
+ *   workspace              device scratch of >= rmsnorm_bwd_workspace_bytes(M, N)
+ *                          bytes, any contents; clobbered; must not overlap
+ *                          any other argument
+ * dw's summation order is fixed by (M, N, device): repeated calls give
+ * identical bits.
+ */
+int rmsnorm_bwd(const void *dy, const void *x, const void *w, const float *rstd, void *dx,
+                float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                int dtype, int w_dtype, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *addrms_status_str(int status);
+
+/* The hipError_t of the last ADDRMS_ERR_HIP returned on this thread (0 if none). */
+int addrms_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADDRMS_H */

@@ -1,0 +1,152 @@
+"""The C ABI on the host (CPU only): the library loads, exports every entry
+point include/addrms.h declares, sizes the backward workspace, and rejects bad
+arguments before making any HIP call (fake, never-dereferenced addresses are
+passed; on a validation error nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "addrms.h")
+LIB = os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms.so")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_EPS, E_ALIAS, E_WS = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libaddrms.so is not built (python -m add_rmsnorm_amd.build)")
+    lib = ctypes.CDLL(LIB)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.rmsnorm_bwd_workspace_bytes.restype = sz
+    lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
+    lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.addrms_status_str.restype = ctypes.c_char_p
+    lib.addrms_status_str.argtypes = [i32]
+    return lib
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd",
+                                  "rmsnorm_bwd_workspace_bytes", "addrms_status_str",
+                                  "addrms_last_hip_error"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_EPS, E_ALIAS, E_WS, -7):
+        assert lib.addrms_status_str(st)
+    assert lib.addrms_status_str(12345) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.rmsnorm_bwd_workspace_bytes
+    assert f(0, 4096) == 0 and f(5, 0) == 0 and f(-1, 8) == 0
+    assert f(1, 7) == 28
+    assert f(32768, 4096) == 1024 * 4096 * 4
+    assert f(100, 10) == 100 * 10 * 4
+    assert f(1 << 40, 1 << 40) == 1024 * (1 << 40) * 4
+    assert f(1 << 40, 1 << 62) == 0  # does not fit in size_t
+
+
+# fake device addresses, 4 KiB apart blocks; never dereferenced
+A, B, C, D, E, W = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
+
+
+def fwd(lib, x=A, w=W, y=B, rstd=None, M=4, N=64, eps=1e-6, dt=BF16, wdt=BF16):
+    return lib.rmsnorm_fwd(x, w, y, rstd, M, N, eps, dt, wdt, None)
+
+
+def add(lib, x=A, r=C, w=W, y=B, res=D, rstd=None, M=4, N=64, eps=1e-6, dt=BF16, wdt=BF16):
+    return lib.add_rmsnorm_fwd(x, r, w, y, res, rstd, M, N, eps, dt, wdt, None)
+
+
+def bwd(lib, dy=A, x=C, w=W, rstd=E, dx=B, dw=D, ws=0x70000000, wsb=None, M=4, N=64,
+        dt=BF16, wdt=BF16):
+    if wsb is None:
+        wsb = lib.rmsnorm_bwd_workspace_bytes(M, N)
+    return lib.rmsnorm_bwd(dy, x, w, rstd, dx, dw, ws, wsb, M, N, dt, wdt, None)
+
+
+def test_null_pointers(lib):
+    assert fwd(lib, x=None) == E_NULL
+    assert fwd(lib, w=None) == E_NULL
+    assert fwd(lib, y=None) == E_NULL
+    for k in ("x", "r", "w", "y", "res"):
+        assert add(lib, **{k: None}) == E_NULL, k
+    for k in ("dy", "x", "w", "rstd", "dx", "dw"):
+        assert bwd(lib, **{k: None}) == E_NULL, k
+
+
+def test_shapes(lib):
+    assert fwd(lib, M=-1) == E_SHAPE
+    assert fwd(lib, N=0) == E_SHAPE
+    assert fwd(lib, N=-3) == E_SHAPE
+    assert fwd(lib, N=1 << 31) == E_SHAPE
+    assert fwd(lib, M=1 << 62, N=1 << 20) == E_SHAPE
+    assert add(lib, N=0) == E_SHAPE
+    assert bwd(lib, M=-2) == E_SHAPE
+
+
+def test_dtypes(lib):
+    assert fwd(lib, dt=2) == E_DTYPE
+    assert fwd(lib, wdt=-1) == E_DTYPE
+    assert add(lib, dt=7) == E_DTYPE
+    assert bwd(lib, wdt=3) == E_DTYPE
+
+
+def test_eps(lib):
+    assert fwd(lib, eps=-1e-6) == E_EPS
+    assert fwd(lib, eps=float("nan")) == E_EPS
+    assert add(lib, eps=float("inf")) == E_EPS
+
+
+def test_workspace_errors(lib):
+    assert bwd(lib, ws=None) == E_WS
+    assert bwd(lib, wsb=10) == E_WS
+
+
+def test_aliasing(lib):
+    mat = 4 * 64 * 2
+    # partial overlap of an output with an input
+    assert fwd(lib, y=A + 16) == E_ALIAS
+    assert fwd(lib, y=W - 8) == E_ALIAS  # y tail overlaps w
+    assert fwd(lib, rstd=A + 32) == E_ALIAS
+    assert add(lib, y=D) == E_ALIAS  # y == residual_out
+    assert add(lib, res=C + 2) == E_ALIAS
+    assert add(lib, rstd=D + mat - 4) == E_ALIAS
+    assert bwd(lib, dx=A + 2) == E_ALIAS
+    assert bwd(lib, dw=A) == E_ALIAS
+    assert bwd(lib, ws=C + mat - 16) == E_ALIAS
+    assert bwd(lib, dw=E) == E_ALIAS  # dw overlaps rstd
+
+
+def test_empty_batch_is_a_noop_without_device(lib):
+    # M == 0 is valid and the forward returns before touching HIP; exact
+    # aliasing of an output with its input is allowed.
+    assert fwd(lib, M=0) == OK
+    assert add(lib, M=0) == OK
+    assert fwd(lib, M=0, y=A) == OK
+    assert add(lib, M=0, res=C, y=A) == OK
+    # empty matrices may be NULL; w may not
+    assert fwd(lib, M=0, x=None, y=None) == OK
+    assert add(lib, M=0, x=None, r=None, y=None, res=None) == OK
+    assert fwd(lib, M=0, w=None) == E_NULL
+    assert bwd(lib, M=0, dw=None) == E_NULL

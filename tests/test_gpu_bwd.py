@@ -1,0 +1,153 @@
+"""GPU parity of the backward (HIP library through the C ABI) against the CPU
+oracle on seeded inputs: dx element by element, dw per column, with the same
+saved float32 rstd (from the oracle's forward) fed to both sides; the named
+workload at full size, every kernel variant, ragged shapes, aliasing, an
+empty batch, determinism, and forward->backward chained on the GPU."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import add_rmsnorm_amd as ar
+import oracle
+import synth
+from parity import assert_close, assert_dw_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def oracle_rstd(x, w, eps):
+    return oracle.rmsnorm_fwd(x, w, eps)[1]
+
+
+def check_bwd(dy, x, w, eps, what="", rstd=None):
+    rstd = oracle_rstd(x, w, eps) if rstd is None else rstd
+    dx, dw = ar.rmsnorm_bwd(dy.to(DEV), x.to(DEV), w.to(DEV), rstd.to(DEV))
+    torch.cuda.synchronize()
+    rdx, rdw, mag = oracle.rmsnorm_bwd(dy, x, w, rstd)
+    assert_close(dx.cpu(), rdx, f"dx {what}")
+    assert_dw_close(dw.cpu(), rdw, mag, f"dw {what}")
+    return dx.cpu(), dw.cpu()
+
+
+def test_rmsnorm_bwd_bf16_32768x4096():
+    inp = synth.workload_inputs("rmsnorm_bwd_bf16_32768x4096")
+    check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6)
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4])
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.float32),
+                                          (torch.float32, torch.bfloat16)])
+def test_forced_waves_per_row(monkeypatch, wpr, dtype, wdtype):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", str(wpr))
+    for M, N in [(1000, 4096), (7, 1032), (3001, 256)]:
+        inp = synth.rmsnorm_bwd_inputs(M, N, dtype, wdtype, seed=M + N)
+        check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"wpr={wpr} {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,N", [(5, 4096), (2000, 7168), (3, 8), (1025, 1000)])
+def test_elementwise_path(monkeypatch, dtype, M, N):
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    inp = synth.rmsnorm_bwd_inputs(M, N, dtype, seed=5)
+    check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, "elem")
+
+
+BWD_N = [1, 7, 8, 64, 65, 520, 4095, 4096, 7168, 8192, 8200, 16384, 16392, 65536]
+
+
+@pytest.mark.parametrize("N", BWD_N)
+@pytest.mark.parametrize("M", [1, 3, 2049])
+def test_edge_shapes_bf16(M, N):
+    if M * N > 1 << 24:
+        M = max(1, (1 << 24) // N)
+    inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=N)
+    check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"{M}x{N}")
+
+
+@pytest.mark.parametrize("N", [1, 5, 4096, 4100, 8192])
+@pytest.mark.parametrize("M", [2, 700])
+def test_edge_shapes_f32(M, N):
+    inp = synth.rmsnorm_bwd_inputs(M, N, torch.float32, seed=N)
+    check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"{M}x{N}")
+
+
+def test_many_rows_exceed_partial_rows():
+    """More blocks' worth of rows than partial rows (1024): the grid is capped
+    and each block accumulates many rows."""
+    inp = synth.rmsnorm_bwd_inputs(70000, 256, torch.bfloat16, seed=23)
+    check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, "70000x256")
+
+
+@pytest.mark.parametrize("force_elem", ["0", "1"])
+def test_dx_in_place(monkeypatch, force_elem):
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", force_elem)
+    M, N = 300, 4096
+    inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=29)
+    rstd = oracle_rstd(inp["x"], inp["w"], 1e-6)
+    rdx, rdw, mag = oracle.rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], rstd)
+    for target in ("dy", "x"):
+        dy, x = inp["dy"].to(DEV), inp["x"].to(DEV)
+        out = dy if target == "dy" else x
+        dx, dw = ar.rmsnorm_bwd(dy, x, inp["w"].to(DEV), rstd.to(DEV), dx=out)
+        assert dx.data_ptr() == out.data_ptr()
+        assert_close(out.cpu(), rdx, f"dx over {target}")
+        assert_dw_close(dw.cpu(), rdw, mag, f"dw (dx over {target})")
+
+
+def test_empty_batch_zeroes_dw():
+    N = 4096
+    w = torch.ones(N, dtype=torch.bfloat16, device=DEV)
+    x = torch.empty(0, N, dtype=torch.bfloat16, device=DEV)
+    rstd = torch.empty(0, dtype=torch.float32, device=DEV)
+    dw = torch.full((N,), 7.0, device=DEV)
+    ar.rmsnorm_bwd(x, x, w, rstd, dw=dw)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+
+
+def test_deterministic():
+    inp = synth.rmsnorm_bwd_inputs(4096, 4096, torch.bfloat16, seed=31)
+    rstd = oracle_rstd(inp["x"], inp["w"], 1e-6).to(DEV)
+    args = [inp["dy"].to(DEV), inp["x"].to(DEV), inp["w"].to(DEV), rstd]
+    a = ar.rmsnorm_bwd(*args)
+    b = ar.rmsnorm_bwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+
+
+def test_forward_then_backward_on_gpu():
+    """GPU forward's rstd feeding the GPU backward, against the oracle chain."""
+    M, N = 2048, 4096
+    inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=37)
+    x, w, dy = inp["x"].to(DEV), inp["w"].to(DEV), inp["dy"].to(DEV)
+    _, rstd = ar.rmsnorm_fwd(x, w, 1e-6, return_rstd=True)
+    dx, dw = ar.rmsnorm_bwd(dy, x, w, rstd)
+    torch.cuda.synchronize()
+    rrstd = oracle_rstd(inp["x"], inp["w"], 1e-6)
+    assert_close(rstd.cpu(), rrstd, "rstd", atol=0, rtol=1e-5)
+    rdx, rdw, mag = oracle.rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], rrstd)
+    assert_close(dx.cpu(), rdx, "dx")
+    assert_dw_close(dw.cpu(), rdw, mag)
+
+
+def test_workspace_too_small_is_an_error():
+    M, N = 64, 512
+    inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=41)
+    rstd = oracle_rstd(inp["x"], inp["w"], 1e-6).to(DEV)
+    ws = torch.empty(ar.rmsnorm_bwd_workspace_bytes(M, N) - 4, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ar.AddRmsError, match="workspace"):
+        ar.rmsnorm_bwd(inp["dy"].to(DEV), inp["x"].to(DEV), inp["w"].to(DEV), rstd, workspace=ws)
