@@ -210,54 +210,55 @@ int vpl_index(int need)
     return -1;
 }
 
-// Forward variant: the fewest waves per row that still give every SIMD a wave
-// (M * WPR >= 4 * CUs), so wide rows or few rows spread over more waves.
-// ADDRMS_FWD_WPR forces a WPR when it fits.
+// Forward variant.  A row is spread over enough waves that each lane holds
+// about ADDRMS_FWD_VPL (default 2) 16-byte vectors per tensor: measured on
+// MI355X, short per-lane chains in many small row-blocks keep more rows in
+// flight and stream fastest (fused bf16 16384 x 7168: 8 waves per row reach
+// 6.2 TB/s, one wave per row 5.5 TB/s).  When there are too few rows to give
+// every SIMD a wave, rows get more waves still.  ADDRMS_FWD_WPR forces a WPR
+// when it is built.
 bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
 {
     const int forced = env_int("ADDRMS_FWD_WPR");
-    int fallback_wi = -1, fallback_vi = -1;
-    for (int wi = 0; wi < kNumWpr; ++wi) {
-        const int wpr = kWprList[wi];
-        const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
-        const int vi = vpl_index(need);
-        if (vi < 0 || !fwd_built(wpr, kVplList[vi]))
-            continue;
-        if (forced > 0) {
-            if (wpr == forced) {
+    const int env_vpl = env_int("ADDRMS_FWD_VPL");
+    const int target = env_vpl > 0 ? env_vpl : 2;
+    auto need_of = [&](int wi) { return (nvec + 64 * kWprList[wi] - 1) / (64 * kWprList[wi]); };
+    auto ok = [&](int wi) {
+        const int vi = vpl_index(need_of(wi));
+        return vi >= 0 && fwd_built(kWprList[wi], kVplList[vi]);
+    };
+    if (forced > 0)
+        for (int wi = 0; wi < kNumWpr; ++wi)
+            if (kWprList[wi] == forced && ok(wi)) {
                 *wi_out = wi;
-                *vi_out = vi;
+                *vi_out = vpl_index(need_of(wi));
                 return true;
             }
-            if (fallback_wi < 0) {
-                fallback_wi = wi;
-                fallback_vi = vi;
-            }
-            continue;
-        }
-        if (M * wpr >= 4LL * cus || wpr == kWprList[kNumWpr - 1] || need == 1) {
-            *wi_out = wi;
-            *vi_out = vi;
-            return true;
-        }
-    }
-    if (fallback_wi >= 0) {
-        *wi_out = fallback_wi;
-        *vi_out = fallback_vi;
-        return true;
-    }
-    return false;
+    int wi = 0;
+    while (wi < kNumWpr - 1 && need_of(wi) > target)
+        ++wi;
+    while (wi < kNumWpr - 1 && M * kWprList[wi] < 4LL * cus && need_of(wi) > 1)
+        ++wi;
+    while (wi < kNumWpr && !ok(wi)) // a built variant with at least as many waves
+        ++wi;
+    if (wi >= kNumWpr)
+        return false;
+    *wi_out = wi;
+    *vi_out = vpl_index(need_of(wi));
+    return true;
 }
 
-// Backward variant: WPR in {1, 2, 4}; prefer at most 8 vectors per lane (the
-// dw accumulators live in registers), enough waves to fill the device, and a
-// dw exchange that fits in 64 KiB of LDS.  ADDRMS_BWD_WPR forces a WPR.
+// Backward variant: WPR in {1, 2, 4}; prefer at most 4 vectors per lane (the
+// dw accumulators live in registers, and short per-lane rows stream best:
+// bf16 32768 x 4096 measured 5.4 TB/s with 2 waves per row, 5.1 with one),
+// then 8, then 16; enough waves to fill the device; and a dw exchange that
+// fits in 64 KiB of LDS.  ADDRMS_BWD_WPR forces a WPR.
 bool pick_bwd(int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
 {
     const int forced = env_int("ADDRMS_BWD_WPR");
     int best_wi = -1, best_vi = -1;
-    for (int pass = 0; pass < 2 && best_wi < 0; ++pass) {
-        const int max_vpl = pass == 0 ? 8 : kMaxVpl;
+    for (int pass = 0; pass < 3 && best_wi < 0; ++pass) {
+        const int max_vpl = pass == 0 ? 4 : pass == 1 ? 8 : kMaxVpl;
         for (int wi = 0; wi < kBwdNumWpr; ++wi) {
             const int wpr = kWprList[wi];
             const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
@@ -291,7 +292,8 @@ bool pick_bwd(int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
 int colreduce(const void *workspace, int P, int N, float *dw, hipStream_t s)
 {
     const float *ws = static_cast<const float *>(workspace);
-    const KernelRef k = colreduce_kernel();
+    const bool vec = (N % 4) == 0 && aligned16(dw) && (P == 0 || aligned16(ws));
+    const KernelRef k = colreduce_kernel(vec);
     void *argv[] = {(void *)&ws, (void *)&P, (void *)&N, (void *)&dw};
     hipError_t e = hipLaunchKernel(k.fn, dim3((unsigned)((N + kColReduceCols - 1) / kColReduceCols)),
                                    dim3(k.block), argv, 0, s);
@@ -346,8 +348,12 @@ int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, 
         a.nvec = (int)(N / nv);
         const KernelRef &k = tab.vec[fused ? 1 : 0][wi][vi];
         const int rpb = kWprList[wi] == 1 ? 4 : 1;
-        int grid = 0;
-        if ((rc = persistent_grid(k, 0, (M + rpb - 1) / rpb, INT_MAX, &grid)) != ADDRMS_OK)
+        const int64_t blocks = (M + rpb - 1) / rpb;
+        // One block per row group (the hardware dispatcher balances the
+        // tail); ADDRMS_BLOCKS_PER_CU > 0 selects a persistent grid instead.
+        int grid = (int)(blocks < INT_MAX ? blocks : INT_MAX);
+        if (env_int("ADDRMS_BLOCKS_PER_CU") > 0 &&
+            (rc = persistent_grid(k, 0, blocks, INT_MAX, &grid)) != ADDRMS_OK)
             return rc;
         return launch(k, dim3(grid), 0, &a, s);
     }

@@ -58,7 +58,7 @@ constexpr bool fwd_built(int wpr, int vpl)
     return wpr <= 4 || (wpr == 8 && vpl <= 8) || (wpr == 16 && vpl <= 4);
 }
 constexpr int kBwdBlock = 256;
-constexpr int kColReduceCols = 64; // dw columns per column-reduce block
+constexpr int kColReduceCols = 16; // dw columns per column-reduce block
 
 // A kernel entry: function, block size, dynamic LDS bytes (backward: per
 // column of N), and whether it is an element-wise fallback.
@@ -85,6 +85,6 @@ struct BwdTable {
 
 const FwdTable &fwd_table(int combo_idx);
 const BwdTable &bwd_table(int combo_idx);
-KernelRef colreduce_kernel();
+KernelRef colreduce_kernel(bool vec);
 
 } // namespace addrms

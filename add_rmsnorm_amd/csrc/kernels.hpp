@@ -15,10 +15,14 @@
 //     covers 1 KiB per load instruction, fully coalesced), normalised from
 //     registers, and written once: x, r read once; y, residual_out written
 //     once;
-//   * a persistent grid walks rows with a grid stride; the host sizes it to
-//     the resident capacity of the device;
-//   * one wave per row needs no barrier at all; wide rows or few rows use
-//     several waves per row and one LDS exchange per row.
+//   * rows are spread over enough waves that each lane holds about two
+//     16-byte vectors per tensor: many short, independent row-blocks keep the
+//     most rows in flight (one LDS exchange per row when a row has several
+//     waves; none when it has one);
+//   * every kernel walks rows with a grid stride, so the same code serves a
+//     one-block-per-row grid (the forward's default) and a persistent grid
+//     sized to the device (the backward, whose blocks keep dw partial sums
+//     in registers across the rows they visit).
 #pragma once
 
 #include <utility>
@@ -28,9 +32,12 @@
 
 namespace addrms {
 
-// Cache policy of the streamed row data (see ld_stream / st_stream).
+// Cache policy of the streamed row data (see ld_stream / st_stream): rows are
+// touched once, so loads and stores are non-temporal by default (measured on
+// MI355X: a 2-read/2-write stream moves ~6.3 TB/s with both non-temporal
+// versus ~5.5 TB/s with the default policy).
 #ifndef ADDRMS_STREAM_POLICY
-#define ADDRMS_STREAM_POLICY 0
+#define ADDRMS_STREAM_POLICY 3
 #endif
 constexpr int kPol = ADDRMS_STREAM_POLICY;
 
@@ -427,23 +434,87 @@ __global__ void __launch_bounds__(256) bwd_elem_dw_kernel(BwdArgs a)
         a.ws[(size_t)blockIdx.y * a.N + c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
-// dw[c] = sum_p ws[p, c]: 64 columns x 4 row slices per block, fixed order.
-// (A template only so that each translation unit's copy is a weak symbol.)
+// dw[c] = sum_p ws[p, c], the second stage of the dw reduction.  The partial
+// rows are few (P <= 1024) and the columns many, so a block takes a narrow
+// column strip and splits the rows over slices of threads; the slices are then
+// merged in LDS by a fixed-order tree, so the result is deterministic.
+// Vector form: 16-column strips read as 4 x 16-byte lanes, 64 row slices;
+// requires N % 4 == 0 and 16-byte aligned ws and dw.  (Templates only so that
+// each translation unit's copy is a weak symbol.)
+template <int Unused = 0>
+__global__ void __launch_bounds__(256) dw_colreduce_vec_kernel(const float *ws, int P, int N, float *dw)
+{
+    constexpr int Q = kColReduceCols / 4; // 16-byte lanes per strip row
+    constexpr int S = 256 / Q;            // row slices
+    __shared__ u32x4 red[S][Q];
+    const int q = threadIdx.x % Q;
+    const int sl = threadIdx.x / Q;
+    const int n4 = N / 4;
+    const int c4 = blockIdx.x * Q + q;
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c4 < n4) {
+        const u32x4 *base = reinterpret_cast<const u32x4 *>(ws) + c4;
+        int p = sl;
+        for (; p + 3 * S < P; p += 4 * S) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = base[(size_t)(p + u * S) * n4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a[i] += __uint_as_float(v[u][i]);
+        }
+        for (; p < P; p += S) {
+            const u32x4 v = base[(size_t)p * n4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] += __uint_as_float(v[i]);
+        }
+    }
+    red[sl][q] = u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                       __float_as_uint(a[3])};
+    __syncthreads();
+#pragma unroll
+    for (int h = S / 2; h >= 1; h >>= 1) {
+        if (sl < h) {
+            const u32x4 o = red[sl + h][q];
+            u32x4 m = red[sl][q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m[i] = __float_as_uint(__uint_as_float(m[i]) + __uint_as_float(o[i]));
+            red[sl][q] = m;
+        }
+        __syncthreads();
+    }
+    if (sl == 0 && c4 < n4)
+        reinterpret_cast<u32x4 *>(dw)[c4] = red[0][q];
+}
+
+// Element form for any N / alignment: 16-column strips, 16 row slices.
 template <int Unused = 0>
 __global__ void __launch_bounds__(256) dw_colreduce_kernel(const float *ws, int P, int N, float *dw)
 {
-    __shared__ float red[4][64];
-    const int lane = threadIdx.x & 63;
-    const int s = threadIdx.x >> 6;
-    const int c = blockIdx.x * kColReduceCols + lane;
+    constexpr int W = 16, S = 256 / W;
+    __shared__ float red[S][W];
+    const int q = threadIdx.x % W;
+    const int sl = threadIdx.x / W;
+    const int c = blockIdx.x * W + q;
     float acc = 0.0f;
     if (c < N)
-        for (int p = s; p < P; p += 4)
+        for (int p = sl; p < P; p += S)
             acc += ws[(size_t)p * N + c];
-    red[s][lane] = acc;
+    red[sl][q] = acc;
     __syncthreads();
-    if (s == 0 && c < N)
-        dw[c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+#pragma unroll
+    for (int h = S / 2; h >= 1; h >>= 1) {
+        if (sl < h)
+            red[sl][q] += red[sl + h][q];
+        __syncthreads();
+    }
+    if (sl == 0 && c < N)
+        dw[c] = red[0][q];
 }
 
 // ---------------------------------------------------------------------------

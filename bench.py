@@ -1,0 +1,399 @@
+"""Throughput of fused residual-Add + RMSNorm on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline] [--no-cpu-baseline]
+
+A step is one fused Add+RMSNorm forward over the whole batch: bf16 x, r
+[16384, 7168], bf16 w, eps 1e-6, writing y and residual_out (bf16).  Inputs
+are seeded synthetic data (the shared generator), resident in HBM before the
+timed region; two input/output sets alternate so that no step reads data the
+previous step left in the 256 MB last-level cache.
+
+Prints ONE JSON line on stdout: achieved GB/s over the algorithmic bytes
+(every tensor read or written once: 8*M*N + 2*N bytes), its fraction of the
+8 TB/s HBM peak, rows/s, the copy-kernel ceiling measured in the same run, the
+roofline of the dominant kernel, the CPU oracle's throughput on a bounded
+sample, and secondary figures (backward, decode latency) unless
+--only-headline.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) + rows/s, bf16 fused Add+RMSNorm M=16384 N=7168"
+WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
+HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, true, 8, 2>"
+KERNEL_SOURCES = ["add_rmsnorm_amd/csrc/kernels.hpp", "add_rmsnorm_amd/csrc/device.hpp",
+                  "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp"]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def timed(fn, steps: int, warmup: int):
+    """Run fn() warmup times, then time `steps` calls bracketed by device
+    synchronisation.  Returns (wall seconds, event seconds) for the K calls;
+    the events are recorded on the current stream, where fn launches."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / 1e3
+
+
+def graph_time(call, per_graph: int = 50, replays: int = 10) -> float:
+    """Device seconds per call: `per_graph` calls captured in one graph,
+    replayed; launch gaps between kernels in a graph are those of the device,
+    not of the Python host loop."""
+    import torch
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            call()
+    best = None
+    for _ in range(3):
+        _, ev = timed(g.replay, replays, 2)
+        best = ev if best is None else min(best, ev)
+    return best / per_graph
+
+
+def copy_ceiling(nbytes: int, steps: int = 20):
+    """GB/s of torch's device copy moving nbytes/2 read + nbytes/2 written."""
+    import torch
+    n = nbytes // 2
+    a = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    b = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for t in a:
+        t.fill_(1)
+    i = [0]
+
+    def step():
+        k = i[0] & 1
+        b[k].copy_(a[k])
+        i[0] += 1
+
+    _, ev = timed(step, steps, 3)
+    return 2 * n * steps / ev / 1e9
+
+
+def headline(steps: int, warmup: int):
+    import torch
+    import add_rmsnorm_amd as ar
+    import synth
+
+    cfg = synth.WORKLOADS[WORKLOAD]
+    M, N, eps = cfg["M"], cfg["N"], cfg["eps"]
+    log(f"generating {WORKLOAD} inputs")
+    inp = synth.workload_inputs(WORKLOAD)
+    sets = []
+    for k in range(2):
+        x = inp["x"].to("cuda")
+        r = inp["r"].to("cuda")
+        sets.append((x, r, torch.empty_like(x), torch.empty_like(x)))
+    w = inp["w"].to("cuda")
+    nbytes = 8 * M * N + 2 * N
+    i = [0]
+
+    def step():
+        x, r, y, res = sets[i[0] & 1]
+        ar.add_rmsnorm_fwd(x, r, w, eps, y=y, residual_out=res)
+        i[0] += 1
+
+    log(f"timing {steps} steps after {warmup} warmup")
+    wall, ev = timed(step, steps, warmup)
+    return dict(M=M, N=N, eps=eps, nbytes=nbytes, wall=wall, ev=ev, inputs=inp)
+
+
+def traffic_from_profile(nbytes_alg: int):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        if ln.startswith("- ") and ": " in ln:
+            k, v = ln[2:].split(": ", 1)
+            kv[k.strip("`")] = v.strip("`")
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    newest = max(files, key=os.path.getmtime)
+    with open(newest) as f:
+        return list(csv.DictReader(f)), newest
+
+
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands: dict):
+    """Write the committed profile summaries from rocprofv3 CSV output:
+    kernel-trace statistics of the bench command, and the headline kernel's
+    FETCH_SIZE / WRITE_SIZE scaled by the same counters of a device copy of
+    known size."""
+    stats, _ = _csv_rows(trace_dir, "kernel_stats.csv")
+    fetch, _ = _csv_rows(fetch_dir, "counter_collection.csv")
+    write, _ = _csv_rows(write_dir, "counter_collection.csv")
+
+    def counter(rows, name_part, min_kib=0.0):
+        return [float(r["Counter_Value"]) for r in rows
+                if name_part in r["Kernel_Name"] and float(r["Counter_Value"]) > min_kib]
+
+    # calibration: the device copies of nb/2 bytes that copy_ceiling() runs
+    nb = 8 * 16384 * 7168 + 2 * 7168
+    copy_kib = (nb // 2) / 1024.0
+    cf = counter(fetch, "copyBuffer", copy_kib / 4)
+    cw = counter(write, "copyBuffer", copy_kib / 4)
+    f_scale = copy_kib / (sum(cf) / len(cf))
+    w_scale = copy_kib / (sum(cw) / len(cw))
+    kf = counter(fetch, HEADLINE_KERNEL)
+    kw = counter(write, HEADLINE_KERNEL)
+    fetch_b = sum(kf) / len(kf) * f_scale * 1024
+    write_b = sum(kw) / len(kw) * w_scale * 1024
+    alg_read, alg_write = 4 * 16384 * 7168 + 2 * 7168, 4 * 16384 * 7168
+    st = [r for r in stats if HEADLINE_KERNEL in r["Name"]][0]
+    avg_us = float(st["AverageNs"]) / 1e3
+
+    out = [f"# {HEADLINE_KERNEL}: fused Add+RMSNorm, bf16, M=16384 N=7168", "",
+           "Kernel trace (rocprofv3 --kernel-trace --stats) of the default bench command:", "",
+           f"    {commands['trace']}", "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+        out.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f} |")
+    out += ["", "HBM traffic of the headline kernel (two counter runs, one counter each):", "",
+            f"    {commands['fetch']}", f"    {commands['write']}", "",
+            f"Calibration: a device copy of {nb // 2} bytes reads FETCH_SIZE "
+            f"{sum(cf) / len(cf):.1f} KiB and WRITE_SIZE {sum(cw) / len(cw):.1f} KiB per "
+            f"dispatch, so FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by "
+            f"{w_scale:.4f} to bytes moved.", "",
+            f"| | counter KiB/dispatch | scaled bytes | algorithmic bytes | ratio |",
+            f"|---|---|---|---|---|",
+            f"| read | {sum(kf) / len(kf):.1f} | {fetch_b:.0f} | {alg_read} | {fetch_b / alg_read:.4f} |",
+            f"| write | {sum(kw) / len(kw):.1f} | {write_b:.0f} | {alg_write} | {write_b / alg_write:.4f} |",
+            "", "Values read by bench.py:", "",
+            f"- kernel_source_digest: {kernel_source_digest()}",
+            f"- traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
+            f"- kernel_avg_us_rocprof: {avg_us:.3f}",
+            f"- achieved_GBps_rocprof: {nb / avg_us / 1e3:.1f}", ""]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out))
+    log(f"wrote {TRAFFIC_FILE}")
+
+
+def cpu_baseline(inp, M: int, N: int, eps: float, target_s: float = 12.0):
+    """The CPU oracle (single-threaded plain C, binary64) on the first rows of
+    the same inputs; the row count is sized for about target_s seconds."""
+    import oracle
+    x, r, w = inp["x"], inp["r"], inp["w"]
+    probe = 256
+    t0 = time.perf_counter()
+    oracle.add_rmsnorm_fwd(x[:probe], r[:probe], w, eps)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(min(M, max(probe, target_s / max(per_row, 1e-9))))
+    log(f"cpu baseline: oracle on {rows} rows (~{rows * per_row:.1f} s)")
+    t0 = time.perf_counter()
+    oracle.add_rmsnorm_fwd(x[:rows], r[:rows], w, eps)
+    dt = time.perf_counter() - t0
+    nbytes = 8 * rows * N + 2 * N
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {M} rows of the same inputs, one pass, "
+                      f"{dt:.1f} s; rows/s {rows / dt:.0f}"}
+
+
+def secondary(steps: int):
+    """Backward, smaller forward shapes and decode latency, same protocol."""
+    import torch
+    import add_rmsnorm_amd as ar
+    import synth
+
+    out = {}
+    # backward, bf16 32768 x 4096, rstd from the GPU forward
+    cfg = synth.WORKLOADS["rmsnorm_bwd_bf16_32768x4096"]
+    M, N = cfg["M"], cfg["N"]
+    inp = synth.workload_inputs("rmsnorm_bwd_bf16_32768x4096")
+    w = inp["w"].cuda()
+    sets = []
+    for _ in range(2):
+        x, dy = inp["x"].cuda(), inp["dy"].cuda()
+        _, rstd = ar.rmsnorm_fwd(x, w, cfg["eps"], return_rstd=True)
+        sets.append((dy, x, rstd, torch.empty_like(x), torch.empty(N, device="cuda")))
+    ws = torch.empty(ar.rmsnorm_bwd_workspace_bytes(M, N), dtype=torch.uint8, device="cuda")
+    i = [0]
+
+    def bstep():
+        dy, x, rstd, dx, dw = sets[i[0] & 1]
+        ar.rmsnorm_bwd(dy, x, w, rstd, dx=dx, dw=dw, workspace=ws)
+        i[0] += 1
+
+    _, ev = timed(bstep, steps, 5)
+    nb = 6 * M * N + 4 * M + 2 * N + 4 * N
+    out["rmsnorm_bwd_bf16_32768x4096"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
+                                                                       HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb}
+    del sets, ws
+    # fused forward, 4096 x 4096 bf16 (134 MB: fits in the last-level cache; rotate 4 sets)
+    inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_4096x4096")
+    M, N = 4096, 4096
+    w = inp["w"].cuda()
+    sets = [(inp["x"].cuda(), inp["r"].cuda()) for _ in range(4)]
+    sets = [(x, r, torch.empty_like(x), torch.empty_like(x)) for x, r in sets]
+
+    def fstep():
+        x, r, y, res = sets[i[0] & 3]
+        ar.add_rmsnorm_fwd(x, r, w, 1e-6, y=y, residual_out=res)
+        i[0] += 1
+
+    _, ev = timed(fstep, steps, 5)
+    nb = 8 * M * N + 2 * N
+    out["add_rmsnorm_fwd_bf16_4096x4096"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "us_per_call": round(ev / steps * 1e6, 2),
+        "bytes": nb, "note": "4 rotating buffer sets (537 MB)"}
+    del sets
+    # plain fp32 forward 256 x 4096 (8 MB: cache-resident, launch-bound)
+    inp = synth.workload_inputs("rmsnorm_fwd_f32_256x4096")
+    x, w = inp["x"].cuda(), inp["w"].cuda()
+    y = torch.empty_like(x)
+    dev_s = graph_time(lambda: ar.rmsnorm_fwd(x, w, 1e-6, y=y))
+    nb = 8 * 256 * 4096 + 4 * 4096
+    out["rmsnorm_fwd_f32_256x4096"] = {"GBps": round(nb / dev_s / 1e9, 1),
+                                       "us_per_call_device": round(dev_s * 1e6, 2), "bytes": nb,
+                                       "note": "cache-resident; device time from graph replay"}
+    # decode: N = 8192, fp32 w, M in {1, 8, 32, 128, 512}: device time per call
+    # (replay of a captured graph of calls) and host wall time per eager call
+    dec = {}
+    for M in synth.WORKLOADS["add_rmsnorm_fwd_bf16_decode_n8192"]["M_list"]:
+        inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_decode_n8192", M=M)
+        x, r, w = inp["x"].cuda(), inp["r"].cuda(), inp["w"].cuda()
+        y, res = torch.empty_like(x), torch.empty_like(x)
+        call = lambda: ar.add_rmsnorm_fwd(x, r, w, 1e-5, y=y, residual_out=res)
+        dev_s = graph_time(call)
+        n = max(steps, 200)
+        wall, _ = timed(call, n, 20)
+        nb = 8 * M * 8192 + 4 * 8192
+        dec[str(M)] = {"us_per_call_device": round(dev_s * 1e6, 2),
+                       "us_per_call_host": round(wall / n * 1e6, 2),
+                       "GBps_device": round(nb / dev_s / 1e9, 1), "bytes": nb}
+    out["add_rmsnorm_fwd_bf16_decode_n8192"] = dec
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true",
+                    help="skip the secondary figures (for profiler runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summary from rocprofv3 CSV output and exit")
+    ap.add_argument("--profile-commands", default="{}",
+                    help="JSON {trace, fetch, write}: the commands that made the CSVs")
+    args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, commands=json.loads(args.profile_commands))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the op is row-local, and this build runs on a "
+              "single MI355X (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    h = headline(args.steps, args.warmup)
+    M, N, nb = h["M"], h["N"], h["nbytes"]
+    gbps = nb * args.steps / h["wall"] / 1e9
+    achieved = nb * args.steps / h["ev"] / 1e9  # per-launch average from the events
+    log(f"fused fwd: {achieved:.1f} GB/s ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s), "
+        f"{h['ev'] / args.steps * 1e6:.2f} us per launch")
+    log("copy-kernel ceiling")
+    copy = copy_ceiling(nb)
+    traffic = traffic_from_profile(nb)
+    rec = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["wall"] / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "M": M, "N": N, "storage_dtype": "bf16",
+                   "w_dtype": "bf16", "eps": h["eps"], "bytes_per_step": nb,
+                   "outputs": "y, residual_out (bf16)", "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "rows_per_s": round(M * args.steps / h["wall"], 0),
+        "copy_ceiling_GBps": round(copy, 1),
+        "pct_of_copy_ceiling": round(100 * gbps / copy, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "fwd_vec_kernel<bf16_t, bf16_t, true, 8, 2> (fused, 8 waves/row, "
+                               "2 x 16 B per lane and tensor, one row per block)",
+                     "avg_launch_us": round(h["ev"] / args.steps * 1e6, 3)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(h["inputs"], M, N, h["eps"])
+    del h
+    if not args.only_headline:
+        log("secondary figures")
+        rec["secondary"] = secondary(min(args.steps, 100))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
