@@ -34,7 +34,8 @@ WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
 HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, true, 8, 2>"
 KERNEL_SOURCES = ["add_rmsnorm_amd/csrc/kernels.hpp", "add_rmsnorm_amd/csrc/device.hpp",
-                  "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp"]
+                  "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp",
+                  "add_rmsnorm_amd/csrc/api.hip"]
 
 
 def log(msg: str):
