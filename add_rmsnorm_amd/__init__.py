@@ -62,19 +62,20 @@ lib = _lib
 
 
 def _code(t: torch.Tensor, what: str) -> int:
-    if t.dtype not in _CODES:
+    c = _CODES.get(t.dtype)
+    if c is None:
         raise TypeError(f"{what}: dtype {t.dtype} not supported (float32, bfloat16)")
-    return _CODES[t.dtype]
+    return c
 
 
 def _dev(t: torch.Tensor, what: str, dtype=None, shape=None) -> torch.Tensor:
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{what} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
 
@@ -86,12 +87,37 @@ def _rows(x: torch.Tensor):
     return x.numel() // N, N
 
 
-def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+# The raw handle of the current stream (cheap internal accessor when present).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(dev: int) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+class _OnDevice:
+    """Make `dev` current for the call only when it is not already."""
+    __slots__ = ("dev", "prev")
+
+    def __init__(self, dev: int):
+        self.dev = dev
+        self.prev = -1
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.dev:
+            self.prev = cur
+            torch.cuda.set_device(self.dev)
+
+    def __exit__(self, *exc):
+        if self.prev >= 0:
+            torch.cuda.set_device(self.prev)
 
 
 def _p(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    return t.data_ptr() if t is not None else None
 
 
 def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, y=None, rstd=None,
@@ -106,9 +132,10 @@ def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, y=None, 
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     elif rstd is not None:
         _dev(rstd, "rstd", torch.float32, x.shape[:-1])
-    with torch.cuda.device(x.device):
+    dev = x.get_device()
+    with _OnDevice(dev):
         st = _lib.rmsnorm_fwd(_p(x), _p(w), _p(y), _p(rstd), M, N, float(eps),
-                              _code(x, "x"), _code(w, "w"), _stream(x))
+                              _code(x, "x"), _code(w, "w"), _stream(dev))
     if st != 0:
         raise AddRmsError(st, "rmsnorm_fwd")
     return (y, rstd) if (return_rstd or rstd is not None) else y
@@ -131,9 +158,10 @@ def add_rmsnorm_fwd(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: floa
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     elif rstd is not None:
         _dev(rstd, "rstd", torch.float32, x.shape[:-1])
-    with torch.cuda.device(x.device):
+    dev = x.get_device()
+    with _OnDevice(dev):
         st = _lib.add_rmsnorm_fwd(_p(x), _p(r), _p(w), _p(y), _p(residual_out), _p(rstd), M, N,
-                                  float(eps), _code(x, "x"), _code(w, "w"), _stream(x))
+                                  float(eps), _code(x, "x"), _code(w, "w"), _stream(dev))
     if st != 0:
         raise AddRmsError(st, "add_rmsnorm_fwd")
     if return_rstd or rstd is not None:
@@ -152,7 +180,7 @@ _ws_cache: dict = {}
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     """A per-device scratch buffer, grown on demand and reused across calls on
     the current stream (calls on other streams must pass their own)."""
-    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    key = (device.index, _stream(device.index))
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
@@ -177,10 +205,11 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
         workspace = _workspace(x.device, need)
     else:
         _dev(workspace, "workspace")
-    with torch.cuda.device(x.device):
+    dev = x.get_device()
+    with _OnDevice(dev):
         st = _lib.rmsnorm_bwd(_p(dy), _p(x), _p(w), _p(rstd), _p(dx), _p(dw), _p(workspace),
                               workspace.numel() * workspace.element_size(), M, N,
-                              _code(x, "x"), _code(w, "w"), _stream(x))
+                              _code(x, "x"), _code(w, "w"), _stream(dev))
     if st != 0:
         raise AddRmsError(st, "rmsnorm_bwd")
     return dx, dw

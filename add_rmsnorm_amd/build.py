@@ -17,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libaddrms.so")
+PROBE_LIB = os.path.join(PKG, "libaddrms_probe.so")
 
 ARCH = os.environ.get("ADDRMS_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -52,8 +53,18 @@ def build(verbose: bool = False, extra_defines=()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the benchmark's stream-ceiling probe: a separate library, never linked
+    # into libaddrms.so
+    _compile(os.path.join(CSRC, "stream_probe.hip"), os.path.join(BUILD, "stream_probe.o"))
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+           os.path.join(BUILD, "stream_probe.o")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

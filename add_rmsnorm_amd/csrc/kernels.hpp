@@ -39,6 +39,7 @@ namespace addrms {
 #ifndef ADDRMS_STREAM_POLICY
 #define ADDRMS_STREAM_POLICY 3
 #endif
+
 constexpr int kPol = ADDRMS_STREAM_POLICY;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -78,8 +79,12 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
     __shared__ float part[2][16];
 
     const int64_t step = (int64_t)gridDim.x * RPB;
+    // Blocks are dealt to the 8 XCDs round-robin, so the rows in flight form
+    // one compact window of memory; giving each XCD a contiguous range of rows
+    // instead measured 8 % slower.
+    const unsigned bid = blockIdx.x;
     int it = 0;
-    for (int64_t row = (int64_t)blockIdx.x * RPB + rib; row < a.M; row += step, ++it) {
+    for (int64_t row = (int64_t)bid * RPB + rib; row < a.M; row += step, ++it) {
         const size_t base = (size_t)row * (size_t)a.N;
         const u32x4 *xp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.x) + base);
         const u32x4 *rp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.r) + base);
@@ -243,37 +248,32 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
             acc[k][e] = 0.0f;
 
     const int64_t step = (int64_t)gridDim.x * RPB;
+    // Loads of one row group into registers.  Vector indices past the row are
+    // clamped to its last vector (in bounds) and masked out at use, so the
+    // loads need no branches; a row past M reads row 0 and is not used.
+    auto load_row = [&](int64_t row, u32x4 (&dyv)[VPL], u32x4 (&xv)[VPL], float &rs) {
+        const bool act = row < a.M;
+        const size_t base = (size_t)(act ? row : 0) * (size_t)N;
+        const u32x4 *dyp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dy) + base);
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.x) + base);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            const int vc = v < nvec ? v : nvec - 1;
+            dyv[k] = ld_stream<kPol>(dyp + vc);
+            xv[k] = ld_stream<kPol>(xp + vc);
+        }
+        rs = act ? a.rstd[row] : 0.0f;
+    };
+    u32x4 dyv[VPL], xv[VPL];
+    float rs = 0.0f;
     int it = 0;
     for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < a.M; row0 += step, ++it) {
         const int64_t row = row0 + rib;
         const bool active = row < a.M; // uniform per wave
         const size_t base = (size_t)(active ? row : 0) * (size_t)N;
-        const u32x4 *dyp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dy) + base);
-        const u32x4 *xp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.x) + base);
         u32x4 *dxp = reinterpret_cast<u32x4 *>(static_cast<T *>(a.dx) + base);
-
-        u32x4 dyv[VPL], xv[VPL];
-        float rs = 0.0f;
-        if (active) {
-            rs = a.rstd[row];
-#pragma unroll
-            for (int k = 0; k < VPL; ++k) {
-                const int v = vbase + k * VSTRIDE;
-                if (v < nvec) {
-                    dyv[k] = ld_stream<kPol>(dyp + v);
-                    xv[k] = ld_stream<kPol>(xp + v);
-                } else {
-                    dyv[k] = u32x4{0u, 0u, 0u, 0u};
-                    xv[k] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < VPL; ++k) {
-                dyv[k] = u32x4{0u, 0u, 0u, 0u};
-                xv[k] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
+        load_row(row, dyv, xv, rs);
 
         // sum_j dy_j w_j x_j over the row
         CT p = 0;

@@ -88,7 +88,7 @@ def graph_time(call, per_graph: int = 50, replays: int = 10) -> float:
     for _ in range(3):
         _, ev = timed(g.replay, replays, 2)
         best = ev if best is None else min(best, ev)
-    return best / per_graph
+    return best / (replays * per_graph)
 
 
 def copy_ceiling(nbytes: int, steps: int = 20):
@@ -108,6 +108,39 @@ def copy_ceiling(nbytes: int, steps: int = 20):
 
     _, ev = timed(step, steps, 3)
     return 2 * n * steps / ev / 1e9
+
+
+def stream_ceiling(nbytes: int, steps: int = 20):
+    """GB/s of the probe kernel that only streams two reads and two writes of
+    nbytes/4 each (libaddrms_probe.so): the practical ceiling of the fused
+    forward's access mix, measured in the same run."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.addrms_probe_stream_2r2w.restype = ctypes.c_int
+    lib.addrms_probe_stream_2r2w.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_size_t,
+                                                                      ctypes.c_void_p]
+    each = (nbytes // 4) // 16 * 16
+    sets = [[torch.empty(each, dtype=torch.uint8, device="cuda") for _ in range(4)]
+            for _ in range(2)]
+    for st in sets:
+        st[0].fill_(1)
+        st[1].fill_(2)
+    i = [0]
+
+    def step():
+        a, b, c, d = sets[i[0] & 1]
+        rc = lib.addrms_probe_stream_2r2w(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
+                                          each, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"stream probe failed: hipError {rc}")
+        i[0] += 1
+
+    _, ev = timed(step, steps, 3)
+    return 4 * each * steps / ev / 1e9
 
 
 def headline(steps: int, warmup: int):
@@ -357,8 +390,9 @@ def main():
     achieved = nb * args.steps / h["ev"] / 1e9  # per-launch average from the events
     log(f"fused fwd: {achieved:.1f} GB/s ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s), "
         f"{h['ev'] / args.steps * 1e6:.2f} us per launch")
-    log("copy-kernel ceiling")
+    log("copy-kernel and stream ceilings")
     copy = copy_ceiling(nb)
+    stream = stream_ceiling(nb)
     traffic = traffic_from_profile(nb)
     rec = {
         "metric": METRIC,
@@ -380,6 +414,8 @@ def main():
         "rows_per_s": round(M * args.steps / h["wall"], 0),
         "copy_ceiling_GBps": round(copy, 1),
         "pct_of_copy_ceiling": round(100 * gbps / copy, 1),
+        "stream_2r2w_ceiling_GBps": round(stream, 1) if stream else None,
+        "pct_of_stream_ceiling": round(100 * gbps / stream, 1) if stream else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,

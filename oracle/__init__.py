@@ -64,6 +64,9 @@ def _load():
         lib.oracle_rmsnorm_bwd.restype = i32
         lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp,
                                            i64, i64]
+        lib.oracle_add_rmsnorm_bwd.restype = i32
+        lib.oracle_add_rmsnorm_bwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, vp, i32, vp,
+                                               i32, vp, i64, i64]
         _lib = lib
     return _lib
 
@@ -153,3 +156,27 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
                                       _ptr(rstd), _code(rstd), _ptr(dx), _code(dx), _ptr(dw),
                                       _code(dw), _ptr(dw_abs), M, N), "rmsnorm_bwd")
     return dx, dw, dw_abs
+
+
+def add_rmsnorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
+                    rstd: torch.Tensor, *, dh_dtype=None, dw_dtype=torch.float32):
+    """Backward of the fused op: dh (the gradient of x and of r) and dw, from
+    the gradients of y (dy) and of residual_out (dres, None for zero), the
+    saved residual h and rstd.  Returns (dh, dw, dw_abs)."""
+    dy, h, w, rstd = _cpu(dy), _cpu(h), _cpu(w), _cpu(rstd)
+    if dres is not None:
+        dres = _cpu(dres)
+        if dres.dtype != h.dtype or dres.shape != h.shape:
+            raise ValueError("oracle: dres must match h")
+    if dy.dtype != h.dtype or dy.shape != h.shape:
+        raise ValueError("oracle: dy and h must share dtype and shape")
+    N = h.shape[-1]
+    M = h.numel() // N
+    dh = torch.empty(h.shape, dtype=dh_dtype or h.dtype)
+    dw = torch.empty((N,), dtype=dw_dtype)
+    dw_abs = torch.empty((N,), dtype=torch.float64)
+    _check(_load().oracle_add_rmsnorm_bwd(_ptr(dy), _ptr(dres), _ptr(h), _code(h), _ptr(w),
+                                          _code(w), _ptr(rstd), _code(rstd), _ptr(dh), _code(dh),
+                                          _ptr(dw), _code(dw), _ptr(dw_abs), M, N),
+           "add_rmsnorm_bwd")
+    return dh, dw, dw_abs

@@ -212,19 +212,24 @@ int oracle_add_rmsnorm_fwd(const void *x, const void *r, int in_dt, const void *
 
 /* ---- backward ----------------------------------------------------------- */
 
-/* RMSNorm backward from the saved rstd.  dx per row; dw = sum over rows of
- * dy * x * rstd, overwritten (not accumulated).  dw_abs (nullable, binary64)
- * receives sum over rows of |dy * x * rstd| per column, the magnitude that
- * bounds the rounding error of any summation order of dw. */
-int oracle_rmsnorm_bwd(const void *dy, const void *x, int in_dt, const void *w, int w_dt,
-                       const void *rstd, int rstd_dt, void *dx, int dx_dt, void *dw, int dw_dt,
-                       double *dw_abs, int64_t M, int64_t N)
+/* Backward of the fused op.  The forward's normalised input is the stored
+ * residual h = x + r, and the residual itself is also an output, so the
+ * gradient reaching h is the RMSNorm backward of dy plus the gradient of the
+ * residual output, dres (NULL: zero).  Because h = x + r, that one tensor
+ * dh is the gradient of both x and r:
+ *   dh_ij = rstd_i * (g_ij - xh_ij * c_i) + dres_ij,   one rounding,
+ * with g, xh, c as for RMSNorm (x replaced by h); dw as for RMSNorm.
+ * (The rounding of the stored residual is treated as the identity, as
+ * autograd through a bf16 add does.) */
+int oracle_add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, int in_dt,
+                           const void *w, int w_dt, const void *rstd, int rstd_dt, void *dh,
+                           int dh_dt, void *dw, int dw_dt, double *dw_abs, int64_t M, int64_t N)
 {
     double *acc, *acc_abs;
 
-    if (!dy || !x || !w || !rstd || !dx || !dw || M < 0 || N <= 0)
+    if (!dy || !h || !w || !rstd || !dh || !dw || M < 0 || N <= 0)
         return OR_ERR_ARG;
-    if (!dtype_ok(in_dt) || !dtype_ok(w_dt) || !dtype_ok(rstd_dt) || !dtype_ok(dx_dt) ||
+    if (!dtype_ok(in_dt) || !dtype_ok(w_dt) || !dtype_ok(rstd_dt) || !dtype_ok(dh_dt) ||
         !dtype_ok(dw_dt))
         return OR_ERR_ARG;
 
@@ -241,15 +246,16 @@ int oracle_rmsnorm_bwd(const void *dy, const void *x, int in_dt, const void *w, 
         double c = 0.0;
         for (int64_t j = 0; j < N; j++) {
             double g = load_elem(dy, in_dt, i * N + j) * load_elem(w, w_dt, j);
-            double xh = load_elem(x, in_dt, i * N + j) * rs;
+            double xh = load_elem(h, in_dt, i * N + j) * rs;
             c += g * xh;
         }
         c /= (double)N;
         for (int64_t j = 0; j < N; j++) {
             double d = load_elem(dy, in_dt, i * N + j);
             double g = d * load_elem(w, w_dt, j);
-            double xh = load_elem(x, in_dt, i * N + j) * rs;
-            store_elem(dx, dx_dt, i * N + j, rs * (g - xh * c));
+            double xh = load_elem(h, in_dt, i * N + j) * rs;
+            double extra = dres ? load_elem(dres, in_dt, i * N + j) : 0.0;
+            store_elem(dh, dh_dt, i * N + j, rs * (g - xh * c) + extra);
             acc[j] += d * xh;
             acc_abs[j] += fabs(d * xh);
         }
@@ -262,4 +268,17 @@ int oracle_rmsnorm_bwd(const void *dy, const void *x, int in_dt, const void *w, 
     free(acc);
     free(acc_abs);
     return OR_OK;
+}
+
+/* RMSNorm backward from the saved rstd.  dx per row; dw = sum over rows of
+ * dy * x * rstd, overwritten (not accumulated).  dw_abs (nullable, binary64)
+ * receives sum over rows of |dy * x * rstd| per column, the magnitude that
+ * bounds the rounding error of any summation order of dw.  It is the fused
+ * op's backward with no residual gradient. */
+int oracle_rmsnorm_bwd(const void *dy, const void *x, int in_dt, const void *w, int w_dt,
+                       const void *rstd, int rstd_dt, void *dx, int dx_dt, void *dw, int dw_dt,
+                       double *dw_abs, int64_t M, int64_t N)
+{
+    return oracle_add_rmsnorm_bwd(dy, NULL, x, in_dt, w, w_dt, rstd, rstd_dt, dx, dx_dt, dw, dw_dt,
+                                  dw_abs, M, N);
 }

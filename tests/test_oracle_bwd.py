@@ -126,3 +126,61 @@ def test_bf16_storage_uses_saved_fp32_rstd():
     F.rms_norm(xr, (N,), wr, oracle.eps_as_float32(1e-6)).backward(dy.double())
     torch.testing.assert_close(dx64, xr.grad, rtol=1e-6, atol=1e-6)
     torch.testing.assert_close(dw64, wr.grad, rtol=1e-6, atol=1e-6)
+
+
+# ---- backward of the fused op ------------------------------------------------
+
+@pytest.mark.parametrize("M,N", [(1, 1), (3, 17), (9, 64), (4, 300)])
+@pytest.mark.parametrize("eps", [1e-6, 0.3])
+def test_fused_matches_torch_autograd_float64(M, N, eps):
+    """dh is the gradient of both x and r of L = sum(dy * y) + sum(dres * res)
+    with res = x + r, y = rms_norm(res) * w."""
+    x, dy, w = _case(M, N, 61)
+    r = synth.store(synth.normal(61, "r", (M, N)), torch.float64)
+    dres = synth.store(synth.normal(62, "dy", (M, N)), torch.float64)
+    _, res, rstd = oracle.add_rmsnorm_fwd(x, r, w, eps, eps_exact=True, rstd_dtype=torch.float64)
+    dh, dw, _ = oracle.add_rmsnorm_bwd(dy, dres, res, w, rstd, dw_dtype=torch.float64)
+    xr, rr, wr = (t.clone().requires_grad_(True) for t in (x, r, w))
+    s = xr + rr
+    (F.rms_norm(s, (N,), wr, eps) * dy).sum().add((s * dres).sum()).backward()
+    torch.testing.assert_close(dh, xr.grad, rtol=1e-11, atol=1e-13)
+    torch.testing.assert_close(dh, rr.grad, rtol=1e-11, atol=1e-13)
+    torch.testing.assert_close(dw, wr.grad, rtol=1e-11, atol=1e-13)
+
+
+def test_fused_special_cases():
+    M, N = 5, 40
+    x, dy, w = _case(M, N, 67)
+    dres = synth.store(synth.normal(68, "dy", (M, N)), torch.float64)
+    _, rstd = oracle.rmsnorm_fwd(x, w, 1e-6, eps_exact=True, rstd_dtype=torch.float64)
+    # no residual gradient: the plain backward
+    dh0, dw0, _ = oracle.add_rmsnorm_bwd(dy, None, x, w, rstd, dw_dtype=torch.float64)
+    dx, dw, _ = oracle.rmsnorm_bwd(dy, x, w, rstd, dw_dtype=torch.float64)
+    assert torch.equal(dh0, dx) and torch.equal(dw0, dw)
+    # no gradient of y: dh is the residual gradient exactly, dw = 0
+    dh1, dw1, _ = oracle.add_rmsnorm_bwd(torch.zeros_like(dy), dres, x, w, rstd,
+                                         dw_dtype=torch.float64)
+    assert torch.equal(dh1, dres) and torch.all(dw1 == 0)
+
+
+@pytest.mark.parametrize("M,N", [(1, 2), (3, 5)])
+def test_fused_finite_differences(M, N):
+    eps, h = 1e-3, 1e-6
+    x, dy, w = _case(M, N, 71)
+    r = synth.store(synth.normal(71, "r", (M, N)), torch.float64)
+    dres = synth.store(synth.normal(72, "dy", (M, N)), torch.float64)
+
+    def loss(xx):
+        y, res, _ = oracle.add_rmsnorm_fwd(xx, r, w, eps, eps_exact=True)
+        return float((y * dy).sum() + (res * dres).sum())
+
+    _, res, rstd = oracle.add_rmsnorm_fwd(x, r, w, eps, eps_exact=True, rstd_dtype=torch.float64)
+    dh, _, _ = oracle.add_rmsnorm_bwd(dy, dres, res, w, rstd, dw_dtype=torch.float64)
+    fd = torch.empty_like(x)
+    for i in range(M):
+        for j in range(N):
+            xp, xm = x.clone(), x.clone()
+            xp[i, j] += h
+            xm[i, j] -= h
+            fd[i, j] = (loss(xp) - loss(xm)) / (2 * h)
+    assert float((fd - dh).abs().max()) < 1e-7 * max(1.0, float(dh.abs().max()))

@@ -5,7 +5,7 @@ it, and runs the oracle pin suite against that build in a subprocess: the
 suite must fail.  Mistakes cover every step of the definition: the eps
 placement, the mean's divisor, the square, the weight, the bfloat16 rounding
 rule, the fused op's choice of normalised value, the saved rstd, and each term
-of the backward."""
+of the backward, including the residual gradient of the fused op."""
 import os
 import subprocess
 import sys
@@ -36,7 +36,9 @@ MUTANTS = {
     "bwd_g_without_weight": ("double g = load_elem(dy, in_dt, i * N + j) * load_elem(w, w_dt, j);",
                              "double g = load_elem(dy, in_dt, i * N + j);"),
     "bwd_dx_without_weight": ("double g = d * load_elem(w, w_dt, j);", "double g = d;"),
-    "bwd_dw_without_rstd": ("acc[j] += d * xh;", "acc[j] += d * load_elem(x, in_dt, i * N + j);"),
+    "bwd_dw_without_rstd": ("acc[j] += d * xh;", "acc[j] += d * load_elem(h, in_dt, i * N + j);"),
+    "fused_bwd_drops_dres": ("rs * (g - xh * c) + extra);", "rs * (g - xh * c));"),
+    "fused_bwd_subtracts_dres": ("rs * (g - xh * c) + extra);", "rs * (g - xh * c) - extra);"),
     "bwd_dx_missing_outer_rstd": ("rs * (g - xh * c)", "(g - xh * c)"),
 }
 
