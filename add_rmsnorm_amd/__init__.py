@@ -10,6 +10,7 @@ Operations (same names as the C ABI):
     rmsnorm_fwd(x, w, eps)            -> y (and rstd)
     add_rmsnorm_fwd(x, r, w, eps)     -> y, residual_out (and rstd)
     rmsnorm_bwd(dy, x, w, rstd)       -> dx, dw
+    add_rmsnorm_bwd(dy, dres, h, w, rstd) -> dh (gradient of x and of r), dw
 """
 from __future__ import annotations
 
@@ -18,8 +19,8 @@ import os
 
 import torch
 
-__all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
-           "AddRmsError", "LIB_PATH", "lib"]
+__all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_bwd",
+           "rmsnorm_bwd_workspace_bytes", "AddRmsError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -50,6 +51,8 @@ def _load():
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.rmsnorm_bwd.restype = i32
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.add_rmsnorm_bwd.restype = i32
+    lib.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     lib.addrms_last_hip_error.restype = i32
@@ -213,3 +216,35 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
     if st != 0:
         raise AddRmsError(st, "rmsnorm_bwd")
     return dx, dw
+
+
+def add_rmsnorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
+                    rstd: torch.Tensor, *, dh=None, dw=None,
+                    workspace: torch.Tensor | None = None):
+    """Backward of add_rmsnorm_fwd: from the gradients of y (dy) and of
+    residual_out (dres, or None for zero), the saved residual_out h and rstd,
+    returns (dh, dw): dh is the gradient of both x and r.  `dh` may be `dy`,
+    `dres` or `h`."""
+    _dev(h, "h")
+    M, N = _rows(h)
+    _dev(dy, "dy", h.dtype, h.shape)
+    if dres is not None:
+        _dev(dres, "dres", h.dtype, h.shape)
+    _dev(w, "w", shape=(N,))
+    _dev(rstd, "rstd", torch.float32, h.shape[:-1])
+    dh = torch.empty_like(h) if dh is None else _dev(dh, "dh", h.dtype, h.shape)
+    dw = (torch.empty(N, dtype=torch.float32, device=h.device) if dw is None
+          else _dev(dw, "dw", torch.float32, (N,)))
+    need = rmsnorm_bwd_workspace_bytes(M, N)
+    if workspace is None:
+        workspace = _workspace(h.device, need)
+    else:
+        _dev(workspace, "workspace")
+    dev = h.get_device()
+    with _OnDevice(dev):
+        st = _lib.add_rmsnorm_bwd(_p(dy), _p(dres), _p(h), _p(w), _p(rstd), _p(dh), _p(dw),
+                                  _p(workspace), workspace.numel() * workspace.element_size(),
+                                  M, N, _code(h, "h"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "add_rmsnorm_bwd")
+    return dh, dw

@@ -1,0 +1,150 @@
+"""PyTorch custom ops with autograd for RMSNorm and fused Add + RMSNorm.
+
+The KernelAgent digest describes KernelAgent-Oink's RMSNorm and fused
+Add + RMSNorm as PyTorch custom operators, and the Machete README ("Built-In
+Areas") lists autograd helpers for composing kernel-backed modules.  This
+module registers the library's calls as ``torch.library`` custom ops
+(``addrms::*``) with fake (shape) implementations and autograd formulas, so
+they work in eager mode and under graph capture.  Every numeric step runs in
+the HIP library; these functions only allocate outputs and marshal.
+
+    y = rms_norm(x, w, eps)                    # differentiable in x and w
+    y, residual = add_rms_norm(x, r, w, eps)   # differentiable in x, r and w
+    RMSNorm(hidden, eps), AddRMSNorm(hidden, eps)   # nn.Module forms
+
+Gradients: dx (and dr, equal to it for the fused op) in x's dtype; dw is
+computed in float32 and returned in w's dtype.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+from torch import Tensor
+
+from . import add_rmsnorm_bwd, add_rmsnorm_fwd, rmsnorm_bwd, rmsnorm_fwd
+
+__all__ = ["rms_norm", "add_rms_norm", "RMSNorm", "AddRMSNorm"]
+
+
+# ---- forward / backward ops -------------------------------------------------
+
+@torch.library.custom_op("addrms::rms_norm_fwd", mutates_args=())
+def _rms_norm_fwd(x: Tensor, w: Tensor, eps: float) -> Tuple[Tensor, Tensor]:
+    return rmsnorm_fwd(x.contiguous(), w.contiguous(), eps, return_rstd=True)
+
+
+@_rms_norm_fwd.register_fake
+def _(x, w, eps):
+    return torch.empty_like(x), x.new_empty(x.shape[:-1], dtype=torch.float32)
+
+
+@torch.library.custom_op("addrms::rms_norm_bwd", mutates_args=())
+def _rms_norm_bwd(dy: Tensor, x: Tensor, w: Tensor, rstd: Tensor) -> Tuple[Tensor, Tensor]:
+    return rmsnorm_bwd(dy.contiguous(), x, w, rstd)
+
+
+@_rms_norm_bwd.register_fake
+def _(dy, x, w, rstd):
+    return torch.empty_like(x), w.new_empty(w.shape, dtype=torch.float32)
+
+
+@torch.library.custom_op("addrms::add_rms_norm_fwd", mutates_args=())
+def _add_rms_norm_fwd(x: Tensor, r: Tensor, w: Tensor, eps: float) -> Tuple[Tensor, Tensor, Tensor]:
+    return add_rmsnorm_fwd(x.contiguous(), r.contiguous(), w.contiguous(), eps, return_rstd=True)
+
+
+@_add_rms_norm_fwd.register_fake
+def _(x, r, w, eps):
+    return (torch.empty_like(x), torch.empty_like(x),
+            x.new_empty(x.shape[:-1], dtype=torch.float32))
+
+
+@torch.library.custom_op("addrms::add_rms_norm_bwd", mutates_args=())
+def _add_rms_norm_bwd(dy: Tensor, dres: Optional[Tensor], h: Tensor, w: Tensor,
+                      rstd: Tensor) -> Tuple[Tensor, Tensor]:
+    return add_rmsnorm_bwd(dy.contiguous(), None if dres is None else dres.contiguous(), h, w,
+                           rstd)
+
+
+@_add_rms_norm_bwd.register_fake
+def _(dy, dres, h, w, rstd):
+    return torch.empty_like(h), w.new_empty(w.shape, dtype=torch.float32)
+
+
+# ---- autograd ----------------------------------------------------------------
+
+def _rms_setup(ctx, inputs, output):
+    x, w, _ = inputs
+    _, rstd = output
+    ctx.save_for_backward(x, w, rstd)
+    ctx.mark_non_differentiable(rstd)
+
+
+def _rms_backward(ctx, dy, _drstd):
+    x, w, rstd = ctx.saved_tensors
+    if dy is None:
+        dy = torch.zeros_like(x)
+    dx, dw = _rms_norm_bwd(dy, x, w, rstd)
+    return dx, dw.to(w.dtype), None
+
+
+_rms_norm_fwd.register_autograd(_rms_backward, setup_context=_rms_setup)
+
+
+def _add_setup(ctx, inputs, output):
+    _, _, w, _ = inputs
+    _, res, rstd = output
+    ctx.save_for_backward(res, w, rstd)
+    ctx.mark_non_differentiable(rstd)
+
+
+def _add_backward(ctx, dy, dres, _drstd):
+    h, w, rstd = ctx.saved_tensors
+    if dy is None:
+        dy = torch.zeros_like(h)
+    dh, dw = _add_rms_norm_bwd(dy, dres, h, w, rstd)
+    return dh, dh, dw.to(w.dtype), None
+
+
+_add_rms_norm_fwd.register_autograd(_add_backward, setup_context=_add_setup)
+
+
+# ---- user-facing functions and modules ----------------------------------------
+
+def rms_norm(x: Tensor, w: Tensor, eps: float = 1e-6) -> Tensor:
+    """RMSNorm over the last dimension, differentiable in x and w."""
+    return _rms_norm_fwd(x, w, eps)[0]
+
+
+def add_rms_norm(x: Tensor, r: Tensor, w: Tensor, eps: float = 1e-6) -> Tuple[Tensor, Tensor]:
+    """Fused residual add + RMSNorm: returns (RMSNorm(x + r) * w, x + r),
+    differentiable in x, r and w (the residual output carries its own
+    gradient into dx and dr)."""
+    y, res, _ = _add_rms_norm_fwd(x, r, w, eps)
+    return y, res
+
+
+class RMSNorm(torch.nn.Module):
+    """y = RMSNorm(x) * weight, weight initialised to ones."""
+
+    def __init__(self, hidden: int, eps: float = 1e-6, dtype=torch.bfloat16, device=None):
+        super().__init__()
+        self.eps = eps
+        self.weight = torch.nn.Parameter(torch.ones(hidden, dtype=dtype, device=device))
+
+    def forward(self, x: Tensor) -> Tensor:
+        return rms_norm(x, self.weight, self.eps)
+
+
+class AddRMSNorm(torch.nn.Module):
+    """(y, residual) = (RMSNorm(x + residual) * weight, x + residual): the
+    pre-norm transformer's residual update and normalisation in one pass."""
+
+    def __init__(self, hidden: int, eps: float = 1e-6, dtype=torch.bfloat16, device=None):
+        super().__init__()
+        self.eps = eps
+        self.weight = torch.nn.Parameter(torch.ones(hidden, dtype=dtype, device=device))
+
+    def forward(self, x: Tensor, residual: Tensor) -> Tuple[Tensor, Tensor]:
+        return add_rms_norm(x, residual, self.weight, self.eps)

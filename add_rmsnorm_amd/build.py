@@ -1,6 +1,7 @@
 """Build libaddrms.so for gfx950 with hipcc, in-tree.
 
-    python -m add_rmsnorm_amd.build
+    python add_rmsnorm_amd/build.py        (a script: it must not import the
+                                            package, which loads the library)
 
 Compiles csrc/tables.hip once per (row dtype, weight dtype) combination and
 csrc/api.hip, in parallel, then links one shared library next to this file.

@@ -364,6 +364,89 @@ int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, 
     return launch(k, dim3(grid), 0, &a, s);
 }
 
+int bwd_common(const void *dy, const void *dres, const void *x, const void *w, const float *rstd,
+               void *dx, float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+               int dtype, int w_dtype, void *stream)
+{
+    const bool res = dres != nullptr;
+    // ---- validation (no HIP call) ----
+    // With M == 0 the row data is empty and may be NULL; dw is still written.
+    if (!w || !dw || (M != 0 && (!dy || !x || !rstd || !dx)))
+        return ADDRMS_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
+        return ADDRMS_ERR_DTYPE;
+    int rc = check_shape(M, N, dtype);
+    if (rc != ADDRMS_OK)
+        return rc;
+    const size_t need = rmsnorm_bwd_workspace_bytes(M, N);
+    if (M > 0 && (!workspace || workspace_bytes < need || need == 0))
+        return ADDRMS_ERR_WORKSPACE;
+    const size_t mat = (size_t)M * (size_t)N * esize(dtype);
+    const Span sdy = span(dy, mat), sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype));
+    const Span srs = span(rstd, (size_t)M * 4u), sdx = span(dx, mat), sdw = span(dw, (size_t)N * 4u);
+    const Span sws = workspace ? span(workspace, need) : Span{};
+    const Span sdr = res ? span(dres, mat) : Span{};
+    if (res && (bad_alias(sdx, sdr, true) || bad_alias(sdw, sdr, false) || bad_alias(sws, sdr, false)))
+        return ADDRMS_ERR_ALIAS;
+    if (bad_alias(sdx, sdy, true) || bad_alias(sdx, sx, true) || bad_alias(sdx, sw, false) ||
+        bad_alias(sdx, srs, false) || bad_alias(sdx, sdw, false) || bad_alias(sdx, sws, false))
+        return ADDRMS_ERR_ALIAS;
+    if (bad_alias(sdw, sdy, false) || bad_alias(sdw, sx, false) || bad_alias(sdw, sw, false) ||
+        bad_alias(sdw, srs, false) || bad_alias(sdw, sws, false))
+        return ADDRMS_ERR_ALIAS;
+    if (bad_alias(sws, sdy, false) || bad_alias(sws, sx, false) || bad_alias(sws, sw, false) ||
+        bad_alias(sws, srs, false))
+        return ADDRMS_ERR_ALIAS;
+
+    // ---- variant and launch ----
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (M == 0) // dw of an empty batch is zero: the column reduce over P = 0 rows writes it
+        return colreduce(workspace, 0, (int)N, dw, s);
+    const BwdTable &tab = bwd_table(combo(dtype, w_dtype));
+    const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u));
+    const int64_t pmax = ws_rows < kMaxPartials ? ws_rows : kMaxPartials;
+    BwdArgs a{dy, res ? dres : dy, x, w, rstd, dx, static_cast<float *>(workspace), M, (int)N, 0, 0, 0};
+
+    const int nv = vec_elems(dtype);
+    const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(dy) &&
+                        aligned16(x) && aligned16(w) && aligned16(dx) && aligned16(workspace) &&
+                        (!res || aligned16(dres));
+    int cus = 0;
+    if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
+        return rc;
+    int wi = 0, vi = 0;
+    if (vec_ok && pick_bwd(M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
+        a.nvec = (int)(N / nv);
+        const KernelRef &k = tab.vec[res ? 1 : 0][wi][vi];
+        const int rpb = 4 / kWprList[wi];
+        const size_t smem = (size_t)(rpb / 2) * (size_t)N * 4u;
+        int grid = 0;
+        if ((rc = persistent_grid(k, smem, (M + rpb - 1) / rpb, pmax, &grid)) != ADDRMS_OK)
+            return rc;
+        a.P = grid;
+        if ((rc = launch(k, dim3(grid), smem, &a, s)) != ADDRMS_OK)
+            return rc;
+    } else {
+        // element-wise: dw partials over row chunks first (reads dy, x intact),
+        // then dx (which may overwrite dy or x)
+        int64_t chunk = (M + pmax - 1) / pmax;
+        const int64_t P = (M + chunk - 1) / chunk;
+        a.P = (int)P;
+        a.chunk = chunk;
+        if ((rc = launch(tab.elem_dw, dim3((unsigned)((N + 63) / 64), (unsigned)P), 0, &a, s)) !=
+            ADDRMS_OK)
+            return rc;
+        int grid = 0;
+        const KernelRef &kdx = tab.elem_dx[res ? 1 : 0];
+        if ((rc = persistent_grid(kdx, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
+            return rc;
+        if ((rc = launch(kdx, dim3(grid), 0, &a, s)) != ADDRMS_OK)
+            return rc;
+    }
+    // dw = column sums of the partials, same stream (ordered after stage 1)
+    return colreduce(workspace, a.P, (int)N, dw, s);
+}
+
 } // namespace
 } // namespace addrms
 
@@ -398,77 +481,17 @@ int rmsnorm_bwd(const void *dy, const void *x, const void *w, const float *rstd,
                 float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
                 int dtype, int w_dtype, void *stream)
 {
-    // ---- validation (no HIP call) ----
-    // With M == 0 the row data is empty and may be NULL; dw is still written.
-    if (!w || !dw || (M != 0 && (!dy || !x || !rstd || !dx)))
-        return ADDRMS_ERR_NULL;
-    if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
-        return ADDRMS_ERR_DTYPE;
-    int rc = check_shape(M, N, dtype);
-    if (rc != ADDRMS_OK)
-        return rc;
-    const size_t need = rmsnorm_bwd_workspace_bytes(M, N);
-    if (M > 0 && (!workspace || workspace_bytes < need || need == 0))
-        return ADDRMS_ERR_WORKSPACE;
-    const size_t mat = (size_t)M * (size_t)N * esize(dtype);
-    const Span sdy = span(dy, mat), sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype));
-    const Span srs = span(rstd, (size_t)M * 4u), sdx = span(dx, mat), sdw = span(dw, (size_t)N * 4u);
-    const Span sws = workspace ? span(workspace, need) : Span{};
-    if (bad_alias(sdx, sdy, true) || bad_alias(sdx, sx, true) || bad_alias(sdx, sw, false) ||
-        bad_alias(sdx, srs, false) || bad_alias(sdx, sdw, false) || bad_alias(sdx, sws, false))
-        return ADDRMS_ERR_ALIAS;
-    if (bad_alias(sdw, sdy, false) || bad_alias(sdw, sx, false) || bad_alias(sdw, sw, false) ||
-        bad_alias(sdw, srs, false) || bad_alias(sdw, sws, false))
-        return ADDRMS_ERR_ALIAS;
-    if (bad_alias(sws, sdy, false) || bad_alias(sws, sx, false) || bad_alias(sws, sw, false) ||
-        bad_alias(sws, srs, false))
-        return ADDRMS_ERR_ALIAS;
+    return bwd_common(dy, nullptr, x, w, rstd, dx, dw, workspace, workspace_bytes, M, N, dtype,
+                      w_dtype, stream);
+}
 
-    // ---- variant and launch ----
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (M == 0) // dw of an empty batch is zero: the column reduce over P = 0 rows writes it
-        return colreduce(workspace, 0, (int)N, dw, s);
-    const BwdTable &tab = bwd_table(combo(dtype, w_dtype));
-    const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u));
-    const int64_t pmax = ws_rows < kMaxPartials ? ws_rows : kMaxPartials;
-    BwdArgs a{dy, x, w, rstd, dx, static_cast<float *>(workspace), M, (int)N, 0, 0, 0};
-
-    const int nv = vec_elems(dtype);
-    const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(dy) &&
-                        aligned16(x) && aligned16(w) && aligned16(dx) && aligned16(workspace);
-    int cus = 0;
-    if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
-        return rc;
-    int wi = 0, vi = 0;
-    if (vec_ok && pick_bwd(M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
-        a.nvec = (int)(N / nv);
-        const KernelRef &k = tab.vec[wi][vi];
-        const int rpb = 4 / kWprList[wi];
-        const size_t smem = (size_t)(rpb / 2) * (size_t)N * 4u;
-        int grid = 0;
-        if ((rc = persistent_grid(k, smem, (M + rpb - 1) / rpb, pmax, &grid)) != ADDRMS_OK)
-            return rc;
-        a.P = grid;
-        if ((rc = launch(k, dim3(grid), smem, &a, s)) != ADDRMS_OK)
-            return rc;
-    } else {
-        // element-wise: dw partials over row chunks first (reads dy, x intact),
-        // then dx (which may overwrite dy or x)
-        int64_t chunk = (M + pmax - 1) / pmax;
-        const int64_t P = (M + chunk - 1) / chunk;
-        a.P = (int)P;
-        a.chunk = chunk;
-        if ((rc = launch(tab.elem_dw, dim3((unsigned)((N + 63) / 64), (unsigned)P), 0, &a, s)) !=
-            ADDRMS_OK)
-            return rc;
-        int grid = 0;
-        if ((rc = persistent_grid(tab.elem_dx, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
-            return rc;
-        if ((rc = launch(tab.elem_dx, dim3(grid), 0, &a, s)) != ADDRMS_OK)
-            return rc;
-    }
-    // dw = column sums of the partials, same stream (ordered after stage 1)
-    return colreduce(workspace, a.P, (int)N, dw, s);
+int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void *w,
+                    const float *rstd, void *dh, float *dw, void *workspace,
+                    size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
+                    void *stream)
+{
+    return bwd_common(dy, dres, h, w, rstd, dh, dw, workspace, workspace_bytes, M, N, dtype,
+                      w_dtype, stream);
 }
 
 const char *addrms_status_str(int status)

@@ -22,9 +22,11 @@ struct FwdArgs {
     float eps;
 };
 
-// Backward arguments.
+// Backward arguments.  For the fused op's backward, x is the saved residual
+// h, dres the gradient of residual_out (added to dx), and dx receives dh.
 struct BwdArgs {
     const void *dy;
+    const void *dres; // fused backward only
     const void *x;
     const void *w;
     const float *rstd;
@@ -77,9 +79,10 @@ struct FwdTable {
     KernelRef vec[2][kNumWpr][kNumVpl];
     KernelRef elem[2];
 };
+// bwd vec / elem_dx: [with residual gradient][...].
 struct BwdTable {
-    KernelRef vec[kBwdNumWpr][kNumVpl];
-    KernelRef elem_dx;
+    KernelRef vec[2][kBwdNumWpr][kNumVpl];
+    KernelRef elem_dx[2];
     KernelRef elem_dw;
 };
 

@@ -221,8 +221,10 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 // registers across all rows it visits; at the end the block's row groups are
 // summed through LDS (pairwise, fixed order) and written as one row of the
 // workspace: ws[blockIdx.x, :].  Dynamic LDS: (RPB / 2) * N floats.
+// RES: the fused op's backward, which adds the residual gradient dres to dx
+// before its one rounding (dx then holds dh, the gradient of x and of r).
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, int WPR, int VPL>
+template <typename T, typename WT, bool RES, int WPR, int VPL>
 __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
@@ -251,21 +253,26 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
     // Loads of one row group into registers.  Vector indices past the row are
     // clamped to its last vector (in bounds) and masked out at use, so the
     // loads need no branches; a row past M reads row 0 and is not used.
-    auto load_row = [&](int64_t row, u32x4 (&dyv)[VPL], u32x4 (&xv)[VPL], float &rs) {
+    auto load_row = [&](int64_t row, u32x4 (&dyv)[VPL], u32x4 (&xv)[VPL],
+                        u32x4 (&drv)[RES ? VPL : 1], float &rs) {
         const bool act = row < a.M;
         const size_t base = (size_t)(act ? row : 0) * (size_t)N;
         const u32x4 *dyp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dy) + base);
         const u32x4 *xp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.x) + base);
+        const u32x4 *drp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dres) + base);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = vbase + k * VSTRIDE;
             const int vc = v < nvec ? v : nvec - 1;
             dyv[k] = ld_stream<kPol>(dyp + vc);
             xv[k] = ld_stream<kPol>(xp + vc);
+            if constexpr (RES)
+                drv[k] = ld_stream<kPol>(drp + vc);
         }
         rs = act ? a.rstd[row] : 0.0f;
     };
     u32x4 dyv[VPL], xv[VPL];
+    u32x4 drv[RES ? VPL : 1];
     float rs = 0.0f;
     int it = 0;
     for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < a.M; row0 += step, ++it) {
@@ -273,7 +280,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
         const bool active = row < a.M; // uniform per wave
         const size_t base = (size_t)(active ? row : 0) * (size_t)N;
         u32x4 *dxp = reinterpret_cast<u32x4 *>(static_cast<T *>(a.dx) + base);
-        load_row(row, dyv, xv, rs);
+        load_row(row, dyv, xv, drv, rs);
 
         // sum_j dy_j w_j x_j over the row
         CT p = 0;
@@ -308,15 +315,20 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
             for (int k = 0; k < VPL; ++k) {
                 const int v = vbase + k * VSTRIDE;
                 if (v < nvec) {
-                    float d[NV], xx[NV], wf[NV], o[NV];
+                    float d[NV], xx[NV], wf[NV], o[NV], dr[NV];
                     unpack<T>(dyv[k], d);
                     unpack<T>(xv[k], xx);
                     load_w<T, WT>(a.w, v, wf);
+                    if constexpr (RES)
+                        unpack<T>(drv[k], dr);
 #pragma unroll
                     for (int e = 0; e < NV; ++e) {
                         const CT xh = (CT)xx[e] * (CT)rs;
                         const CT g = (CT)d[e] * (CT)wf[e];
-                        o[e] = (float)((CT)rs * (g - xh * c));
+                        CT dxe = (CT)rs * (g - xh * c);
+                        if constexpr (RES)
+                            dxe += (CT)dr[e];
+                        o[e] = (float)dxe;
                         acc[k][e] = __builtin_fmaf(d[e], (float)xh, acc[k][e]);
                     }
                     st_stream<kPol>(dxp + v, pack<T>(o));
@@ -388,7 +400,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
 // two passes; dw partials per (column block, row chunk).  dw runs first, so dx
 // may overwrite dy or x.
 // ---------------------------------------------------------------------------
-template <typename T, typename WT>
+template <typename T, typename WT, bool RES>
 __global__ void __launch_bounds__(256) bwd_elem_dx_kernel(BwdArgs a)
 {
     using CT = typename BwdCompute<T>::type;
@@ -408,7 +420,10 @@ __global__ void __launch_bounds__(256) bwd_elem_dx_kernel(BwdArgs a)
         for (int j = tid; j < N; j += 256) {
             const CT xh = (CT)ld_elem<T>(a.x, base + j) * rs;
             const CT g = (CT)ld_elem<T>(a.dy, base + j) * (CT)ld_elem<WT>(a.w, j);
-            st_elem<T>(a.dx, base + j, (float)(rs * (g - xh * c)));
+            CT dxe = rs * (g - xh * c);
+            if constexpr (RES)
+                dxe += (CT)ld_elem<T>(a.dres, base + j);
+            st_elem<T>(a.dx, base + j, (float)dxe);
         }
     }
 }
@@ -549,23 +564,25 @@ template <typename T, typename WT> struct TableBuilder {
         return t;
     }
 
-    template <int WI, int... VI>
+    template <bool R, int WI, int... VI>
     static void bwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
     {
         ((row[VI] = KernelRef{reinterpret_cast<const void *>(
-                                  &bwd_vec_kernel<T, WT, kWprList[WI], kVplList[VI]>),
+                                  &bwd_vec_kernel<T, WT, R, kWprList[WI], kVplList[VI]>),
                               kBwdBlock}),
          ...);
     }
-    template <int... WI> static void bwd_all(BwdTable &t, std::integer_sequence<int, WI...>)
+    template <bool R, int... WI> static void bwd_all(BwdTable &t, std::integer_sequence<int, WI...>)
     {
-        (bwd_row<WI>(t.vec[WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
+        (bwd_row<R, WI>(t.vec[R ? 1 : 0][WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
     }
     static BwdTable bwd()
     {
         BwdTable t{};
-        bwd_all(t, std::make_integer_sequence<int, kBwdNumWpr>{});
-        t.elem_dx = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT>), 256};
+        bwd_all<false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        bwd_all<true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        t.elem_dx[0] = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, false>), 256};
+        t.elem_dx[1] = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, true>), 256};
         t.elem_dw = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dw_kernel<T>), 256};
         return t;
     }

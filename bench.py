@@ -311,7 +311,31 @@ def secondary(steps: int):
         "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
                                                                        HBM_PEAK_GBPS, 1),
         "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb}
-    del sets, ws
+    del sets
+    # backward of the fused op at the headline shape: dy, dres, h read; dh written
+    M, N = 16384, 7168
+    inp = synth.workload_inputs(WORKLOAD)
+    w = inp["w"].cuda()
+    h = inp["x"].cuda()
+    _, rstd = ar.rmsnorm_fwd(h, w, 1e-6, return_rstd=True)
+    dy, dres = inp["r"].cuda(), inp["x"].cuda()
+    sets = [(dy, dres, h, torch.empty_like(h)), (dres, dy, h, torch.empty_like(h))]
+    ws = torch.empty(ar.rmsnorm_bwd_workspace_bytes(M, N), dtype=torch.uint8, device="cuda")
+    dw = torch.empty(N, device="cuda")
+
+    def fbstep():
+        a, b, hh, dh = sets[i[0] & 1]
+        ar.add_rmsnorm_bwd(a, b, hh, w, rstd, dh=dh, dw=dw, workspace=ws)
+        i[0] += 1
+
+    _, ev = timed(fbstep, steps, 5)
+    nb = 8 * M * N + 4 * M + 2 * N + 4 * N
+    out["add_rmsnorm_bwd_bf16_16384x7168"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
+                                                                       HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
+        "note": "reads dy, d(residual_out), residual_out; writes dh (= dx = dr) and dw"}
+    del sets, ws, h, dy, dres
     # fused forward, 4096 x 4096 bf16 (134 MB: fits in the last-level cache; rotate 4 sets)
     inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_4096x4096")
     M, N = 4096, 4096

@@ -37,7 +37,8 @@
  * otherwise an element-wise path gives the same results.
  *
  * Aliasing: an output may be exactly the same buffer as an input of the same
- * shape (y == x; residual_out == r or x; dx == dy or x).  Any other overlap
+ * shape (y == x; residual_out == r or x; dx == dy or x; dh == dy, dres or h).
+ * Any other overlap
  * between an output and any other argument is ADDRMS_ERR_ALIAS.
  *
  * Errors: arguments are validated before any HIP call; on error nothing is
@@ -119,6 +120,31 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N);
 int rmsnorm_bwd(const void *dy, const void *x, const void *w, const float *rstd, void *dx,
                 float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
                 int dtype, int w_dtype, void *stream);
+
+/*
+ * Backward of the fused residual-Add + RMSNorm (KernelAgent-Oink's fused op;
+ * the Machete README's autograd helpers, "Built-In Areas").  The forward
+ * normalised h = residual_out and also returned it, so the gradient reaching
+ * h is the RMSNorm backward of dy plus the gradient of residual_out; since
+ * h = x + r, that one tensor is the gradient of both x and r:
+ *     dh_ij = round(rstd_i * (g_ij - hh_ij * c_i) + dres_ij),
+ *     g = dy * w,  hh = h * rstd_i,  c_i = mean_j(g_ij * hh_ij),
+ *     dw_j  = sum_i dy_ij * hh_ij                       (overwritten)
+ * (the rounding of the stored residual is treated as the identity).
+ *   dy    [M, N] dtype     gradient of y
+ *   dres  [M, N] dtype     gradient of residual_out; NULL means zero (then
+ *                          this equals rmsnorm_bwd with x = h)
+ *   h     [M, N] dtype     residual_out saved by the forward
+ *   w     [N]    w_dtype
+ *   rstd  [M]    float32   saved by the forward (required)
+ *   dh    [M, N] dtype     output; may be dy, dres or h
+ *   dw    [N]    float32   output, overwritten
+ *   workspace              as for rmsnorm_bwd (same size function)
+ */
+int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void *w,
+                    const float *rstd, void *dh, float *dw, void *workspace,
+                    size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
+                    void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *addrms_status_str(int status);

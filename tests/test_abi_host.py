@@ -34,6 +34,7 @@ def lib():
     lib.rmsnorm_bwd_workspace_bytes.restype = sz
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     return lib
@@ -41,8 +42,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd",
-                                  "rmsnorm_bwd_workspace_bytes", "addrms_status_str",
-                                  "addrms_last_hip_error"])
+                                  "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
+                                  "addrms_status_str", "addrms_last_hip_error"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -83,6 +84,24 @@ def bwd(lib, dy=A, x=C, w=W, rstd=E, dx=B, dw=D, ws=0x70000000, wsb=None, M=4, N
     if wsb is None:
         wsb = lib.rmsnorm_bwd_workspace_bytes(M, N)
     return lib.rmsnorm_bwd(dy, x, w, rstd, dx, dw, ws, wsb, M, N, dt, wdt, None)
+
+
+def abwd(lib, dy=A, dres=0x80000000, h=C, w=W, rstd=E, dh=B, dw=D, ws=0x70000000, wsb=None,
+         M=4, N=64, dt=BF16, wdt=BF16):
+    if wsb is None:
+        wsb = lib.rmsnorm_bwd_workspace_bytes(M, N)
+    return lib.add_rmsnorm_bwd(dy, dres, h, w, rstd, dh, dw, ws, wsb, M, N, dt, wdt, None)
+
+
+def test_fused_backward_validation(lib):
+    for k in ("dy", "h", "w", "rstd", "dh", "dw"):
+        assert abwd(lib, **{k: None}) == E_NULL, k
+    assert abwd(lib, M=-1) == E_SHAPE
+    assert abwd(lib, dt=9) == E_DTYPE
+    assert abwd(lib, ws=None) == E_WS
+    assert abwd(lib, dh=0x80000000 + 2) == E_ALIAS  # dh partially over dres
+    assert abwd(lib, dw=0x80000000) == E_ALIAS      # dw inside dres
+    assert abwd(lib, ws=0x80000000 + 64) == E_ALIAS
 
 
 def test_null_pointers(lib):

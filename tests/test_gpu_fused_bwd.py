@@ -1,0 +1,151 @@
+"""GPU parity of the fused op's backward (add_rmsnorm_bwd through the C ABI)
+and of the autograd custom ops, against the CPU oracle on seeded inputs."""
+import sys
+
+import pytest
+import torch
+
+import add_rmsnorm_amd as ar
+import add_rmsnorm_amd.autograd as ag
+import oracle
+import synth
+from parity import assert_close, assert_dw_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def fused_case(M, N, dtype, wdtype=None, seed=0):
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, wdtype, seed=seed, r_std=0.5)
+    _, h, rstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    dy = synth.store(synth.normal(seed, "dy", (M, N)), dtype)
+    dres = synth.store(synth.normal(seed + 1, "dy", (M, N)), dtype)
+    return dy, dres, h, inp["w"], rstd
+
+
+def check(dy, dres, h, w, rstd, what=""):
+    dh, dw = ar.add_rmsnorm_bwd(dy.to(DEV), None if dres is None else dres.to(DEV), h.to(DEV),
+                                w.to(DEV), rstd.to(DEV))
+    torch.cuda.synchronize()
+    rdh, rdw, mag = oracle.add_rmsnorm_bwd(dy, dres, h, w, rstd)
+    assert_close(dh.cpu(), rdh, f"dh {what}")
+    assert_dw_close(dw.cpu(), rdw, mag, f"dw {what}")
+
+
+@pytest.mark.parametrize("M,N", [(16384, 7168), (4096, 4096), (300, 1032)])
+def test_fused_bwd_bf16(M, N):
+    check(*fused_case(M, N, torch.bfloat16), f"{M}x{N}")
+
+
+@pytest.mark.parametrize("dtype,wdtype", [(torch.float32, torch.float32),
+                                          (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.bfloat16)])
+def test_fused_bwd_dtypes(dtype, wdtype):
+    check(*fused_case(777, 2048, dtype, wdtype, seed=5), str(dtype))
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4])
+def test_fused_bwd_forced_waves_per_row(monkeypatch, wpr):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", str(wpr))
+    check(*fused_case(1000, 4096, torch.bfloat16, seed=7), f"wpr={wpr}")
+
+
+@pytest.mark.parametrize("M,N", [(5, 4096), (129, 7), (64, 1000)])
+def test_fused_bwd_elementwise(monkeypatch, M, N):
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    check(*fused_case(M, N, torch.bfloat16, seed=9), f"elem {M}x{N}")
+
+
+@pytest.mark.parametrize("N", [1, 8, 65, 8193, 16384])
+def test_fused_bwd_edge_shapes(N):
+    check(*fused_case(33, N, torch.bfloat16, seed=N), f"N={N}")
+
+
+def test_fused_bwd_without_residual_gradient_is_plain_bwd():
+    dy, _, h, w, rstd = fused_case(512, 4096, torch.bfloat16, seed=11)
+    check(dy, None, h, w, rstd, "dres=None")
+    args = [dy.to(DEV), h.to(DEV), w.to(DEV), rstd.to(DEV)]
+    a = ar.add_rmsnorm_bwd(args[0], None, *args[1:])
+    b = ar.rmsnorm_bwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("target", ["dy", "dres", "h"])
+def test_fused_bwd_in_place(target):
+    dy, dres, h, w, rstd = fused_case(300, 4096, torch.bfloat16, seed=13)
+    rdh, rdw, mag = oracle.add_rmsnorm_bwd(dy, dres, h, w, rstd)
+    t = {"dy": dy.to(DEV), "dres": dres.to(DEV), "h": h.to(DEV)}
+    dh, dw = ar.add_rmsnorm_bwd(t["dy"], t["dres"], t["h"], w.to(DEV), rstd.to(DEV), dh=t[target])
+    assert dh.data_ptr() == t[target].data_ptr()
+    assert_close(t[target].cpu(), rdh, f"dh over {target}")
+    assert_dw_close(dw.cpu(), rdw, mag)
+
+
+# ---- autograd custom ops -------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.float32)])
+def test_add_rms_norm_autograd(dtype, wdtype):
+    M, N = 256, 4096
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, wdtype, seed=17, r_std=0.5)
+    gy = synth.store(synth.normal(17, "dy", (M, N)), dtype)
+    gres = synth.store(synth.normal(18, "dy", (M, N)), dtype)
+    x, r, w = (inp[k].to(DEV).requires_grad_(True) for k in ("x", "r", "w"))
+    y, res = ag.add_rms_norm(x, r, w, 1e-6)
+    torch.autograd.backward([y, res], [gy.to(DEV), gres.to(DEV)])
+    torch.cuda.synchronize()
+    ry, rres, rrstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    assert_close(y.detach().cpu(), ry, "y")
+    rdh, rdw, mag = oracle.add_rmsnorm_bwd(gy, gres, rres, inp["w"], rrstd)
+    assert_close(x.grad.cpu(), rdh, "x.grad")
+    assert_close(r.grad.cpu(), rdh, "r.grad")
+    assert w.grad.dtype == wdtype
+    assert_dw_close(w.grad.cpu(), rdw, mag, "w.grad")
+
+
+def test_rms_norm_autograd_and_modules():
+    M, N = 128, 2048
+    inp = synth.rmsnorm_bwd_inputs(M, N, torch.float32, seed=19)
+    x = inp["x"].to(DEV).requires_grad_(True)
+    w = inp["w"].to(DEV).requires_grad_(True)
+    y = ag.rms_norm(x, w, 1e-6)
+    y.backward(inp["dy"].to(DEV))
+    torch.cuda.synchronize()
+    ry, rrstd = oracle.rmsnorm_fwd(inp["x"], inp["w"], 1e-6)
+    rdx, rdw, mag = oracle.rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], rrstd)
+    assert_close(y.detach().cpu(), ry, "y")
+    assert_close(x.grad.cpu(), rdx, "x.grad")
+    assert_dw_close(w.grad.cpu(), rdw, mag, "w.grad")
+    # the module forms run and produce gradients for their weights
+    m = ag.AddRMSNorm(N, dtype=torch.bfloat16, device=DEV)
+    xb = inp["x"].to(DEV, torch.bfloat16).requires_grad_(True)
+    yb, resb = m(xb, torch.zeros_like(xb))
+    (yb.float().sum() + resb.float().sum()).backward()
+    assert m.weight.grad is not None and m.weight.grad.dtype == torch.bfloat16
+    assert xb.grad is not None and torch.isfinite(xb.grad.float()).all()
+    n = ag.RMSNorm(N, dtype=torch.bfloat16, device=DEV)
+    n(xb.detach()).float().sum().backward()
+    assert n.weight.grad is not None
+
+
+def test_custom_op_registration_checks():
+    """torch.library.opcheck: schema, fake implementation, autograd
+    registration of each op on real GPU tensors."""
+    M, N = 8, 512
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, torch.float32, seed=23)
+    x, r, w = (inp[k].to(DEV) for k in ("x", "r", "w"))
+    torch.library.opcheck(torch.ops.addrms.add_rms_norm_fwd, (x, r, w, 1e-6))
+    torch.library.opcheck(torch.ops.addrms.rms_norm_fwd, (x, w, 1e-6))
+    _, h, rstd = torch.ops.addrms.add_rms_norm_fwd(x, r, w, 1e-6)
+    torch.library.opcheck(torch.ops.addrms.add_rms_norm_bwd, (x, r, h, w, rstd))
+    torch.library.opcheck(torch.ops.addrms.rms_norm_bwd, (x, h, w, rstd))
