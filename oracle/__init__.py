@@ -64,6 +64,15 @@ def _load():
         lib.oracle_rmsnorm_bwd.restype = i32
         lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp,
                                            i64, i64]
+        lib.oracle_layernorm_fwd.restype = i32
+        lib.oracle_layernorm_fwd.argtypes = [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, i64,
+                                             i64, dbl]
+        lib.oracle_add_layernorm_fwd.restype = i32
+        lib.oracle_add_layernorm_fwd.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, vp, i32, vp,
+                                                 vp, i32, i64, i64, dbl]
+        lib.oracle_layernorm_bwd.restype = i32
+        lib.oracle_layernorm_bwd.argtypes = [vp, vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp,
+                                             i32, vp, vp, i64, i64]
         lib.oracle_add_rmsnorm_bwd.restype = i32
         lib.oracle_add_rmsnorm_bwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, vp, i32, vp,
                                                i32, vp, i64, i64]
@@ -180,3 +189,69 @@ def add_rmsnorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
                                           _ptr(dw), _code(dw), _ptr(dw_abs), M, N),
            "add_rmsnorm_bwd")
     return dh, dw, dw_abs
+
+
+def layernorm_fwd(x: torch.Tensor, w: torch.Tensor, b, eps: float, *, y_dtype=None,
+                  stat_dtype=torch.float32, eps_exact: bool = False):
+    """LayerNorm over the last dim: y = (x - mean) * rstd * w (+ b).
+    Returns (y, mean, rstd)."""
+    x, w = _cpu(x), _cpu(w)
+    if b is not None:
+        b = _cpu(b)
+        if b.dtype != w.dtype:
+            raise ValueError("oracle: b must have w's dtype")
+    N = x.shape[-1]
+    M = x.numel() // N
+    y = torch.empty(x.shape, dtype=y_dtype or x.dtype)
+    mean = torch.empty(x.shape[:-1], dtype=stat_dtype)
+    rstd = torch.empty(x.shape[:-1], dtype=stat_dtype)
+    e = float(eps) if eps_exact else eps_as_float32(eps)
+    _check(_load().oracle_layernorm_fwd(_ptr(x), _code(x), _ptr(w), _ptr(b), _code(w), _ptr(y),
+                                        _code(y), _ptr(mean), _ptr(rstd), _code(mean), M, N, e),
+           "layernorm_fwd")
+    return y, mean, rstd
+
+
+def add_layernorm_fwd(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, b, eps: float, *,
+                      y_dtype=None, res_dtype=None, stat_dtype=torch.float32,
+                      eps_exact: bool = False):
+    """residual_out = stored(x + r); y = LayerNorm(residual_out) * w (+ b).
+    Returns (y, residual_out, mean, rstd)."""
+    x, r, w = _cpu(x), _cpu(r), _cpu(w)
+    if b is not None:
+        b = _cpu(b)
+    if x.dtype != r.dtype or x.shape != r.shape:
+        raise ValueError("oracle: x and r must share dtype and shape")
+    N = x.shape[-1]
+    M = x.numel() // N
+    y = torch.empty(x.shape, dtype=y_dtype or x.dtype)
+    res = torch.empty(x.shape, dtype=res_dtype or x.dtype)
+    mean = torch.empty(x.shape[:-1], dtype=stat_dtype)
+    rstd = torch.empty(x.shape[:-1], dtype=stat_dtype)
+    e = float(eps) if eps_exact else eps_as_float32(eps)
+    _check(_load().oracle_add_layernorm_fwd(_ptr(x), _ptr(r), _code(x), _ptr(w), _ptr(b),
+                                            _code(w), _ptr(y), _code(y), _ptr(res), _code(res),
+                                            _ptr(mean), _ptr(rstd), _code(mean), M, N, e),
+           "add_layernorm_fwd")
+    return y, res, mean, rstd
+
+
+def layernorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, mean: torch.Tensor,
+                  rstd: torch.Tensor, *, dx_dtype=None, dwb_dtype=torch.float32):
+    """dx, dw, db from the saved mean and rstd.  Returns
+    (dx, dw, db, dw_abs, db_abs)."""
+    dy, x, w, mean, rstd = _cpu(dy), _cpu(x), _cpu(w), _cpu(mean), _cpu(rstd)
+    if mean.dtype != rstd.dtype:
+        raise ValueError("oracle: mean and rstd must share dtype")
+    N = x.shape[-1]
+    M = x.numel() // N
+    dx = torch.empty(x.shape, dtype=dx_dtype or x.dtype)
+    dw = torch.empty((N,), dtype=dwb_dtype)
+    db = torch.empty((N,), dtype=dwb_dtype)
+    dw_abs = torch.empty((N,), dtype=torch.float64)
+    db_abs = torch.empty((N,), dtype=torch.float64)
+    _check(_load().oracle_layernorm_bwd(_ptr(dy), _ptr(x), _code(x), _ptr(w), _code(w),
+                                        _ptr(mean), _ptr(rstd), _code(mean), _ptr(dx), _code(dx),
+                                        _ptr(dw), _ptr(db), _code(dw), _ptr(dw_abs),
+                                        _ptr(db_abs), M, N), "layernorm_bwd")
+    return dx, dw, db, dw_abs, db_abs

@@ -36,6 +36,22 @@
  * rounded to its storage type; the normalised value h is that stored
  * residual.  For binary64 inputs the add is a binary64 add.
  *
+ * LayerNorm (the "CuTe DSL" skill page lists a CTA-level LayerNorm example
+ * in Workflow 0's example index and names LayerNorm beside RMSNorm in its
+ * reduction pattern) is the textbook one (Ba, Kiros & Hinton 2016), with the
+ * biased variance and eps inside the square root:
+ *
+ *   mean_i = (1/N) * sum_j h_ij
+ *   var_i  = (1/N) * sum_j (h_ij - mean_i)^2
+ *   rstd_i = 1 / sqrt(var_i + eps)
+ *   y_ij   = (h_ij - mean_i) * rstd_i * w_j + b_j       (b optional)
+ *
+ * with the same choice of h for the fused residual variant, and backward
+ *
+ *   xh = (x - mean) * rstd,  g = dy * w
+ *   dx = rstd * (g - mean_j(g) - xh * mean_j(g * xh))
+ *   dw = sum_i dy * xh,      db = sum_i dy
+ *
  * Element types (codes): 0 = float32, 1 = bfloat16 (raw uint16 bits),
  * 2 = float64.  All arrays are row-major and contiguous, row stride N.
  */
@@ -281,4 +297,133 @@ int oracle_rmsnorm_bwd(const void *dy, const void *x, int in_dt, const void *w, 
 {
     return oracle_add_rmsnorm_bwd(dy, NULL, x, in_dt, w, w_dt, rstd, rstd_dt, dx, dx_dt, dw, dw_dt,
                                   dw_abs, M, N);
+}
+
+/* ---- LayerNorm ---------------------------------------------------------- */
+
+/* LayerNorm forward.  b, mean, rstd may be NULL; mean and rstd are rounded to
+ * stat_dt. */
+int oracle_layernorm_fwd(const void *x, int x_dt, const void *w, const void *b, int w_dt,
+                         void *y, int y_dt, void *mean, void *rstd, int stat_dt, int64_t M,
+                         int64_t N, double eps)
+{
+    if (!x || !w || !y || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || !dtype_ok(y_dt) || !dtype_ok(stat_dt))
+        return OR_ERR_ARG;
+
+    for (int64_t i = 0; i < M; i++) {
+        double sum = 0.0, sq = 0.0;
+        for (int64_t j = 0; j < N; j++)
+            sum += load_elem(x, x_dt, i * N + j);
+        double mu = sum / (double)N;
+        for (int64_t j = 0; j < N; j++) {
+            double d = load_elem(x, x_dt, i * N + j) - mu;
+            sq += d * d;
+        }
+        double var = sq / (double)N;
+        double rs = 1.0 / sqrt(var + eps);
+        if (mean)
+            store_elem(mean, stat_dt, i, mu);
+        if (rstd)
+            store_elem(rstd, stat_dt, i, rs);
+        for (int64_t j = 0; j < N; j++) {
+            double v = (load_elem(x, x_dt, i * N + j) - mu) * rs * load_elem(w, w_dt, j);
+            if (b)
+                v += load_elem(b, w_dt, j);
+            store_elem(y, y_dt, i * N + j, v);
+        }
+    }
+    return OR_OK;
+}
+
+/* Fused residual-Add + LayerNorm forward: residual_out = stored(x + r) (the
+ * binary32 add of the RMSNorm variant), then LayerNorm of the stored residual. */
+int oracle_add_layernorm_fwd(const void *x, const void *r, int in_dt, const void *w,
+                             const void *b, int w_dt, void *y, int y_dt, void *res, int res_dt,
+                             void *mean, void *rstd, int stat_dt, int64_t M, int64_t N,
+                             double eps)
+{
+    if (!x || !r || !w || !y || !res || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
+        return OR_ERR_ARG;
+    for (int64_t k = 0; k < M * N; k++) {
+        double s;
+        if (in_dt == OR_F64) {
+            s = load_elem(x, in_dt, k) + load_elem(r, in_dt, k);
+        } else {
+            float a32 = (float)load_elem(x, in_dt, k);
+            float b32 = (float)load_elem(r, in_dt, k);
+            float s32 = a32 + b32;
+            s = (double)s32;
+        }
+        store_elem(res, res_dt, k, s);
+    }
+    return oracle_layernorm_fwd(res, res_dt, w, b, w_dt, y, y_dt, mean, rstd, stat_dt, M, N, eps);
+}
+
+/* LayerNorm backward from the saved mean and rstd.  db may be NULL.  dw_abs
+ * and db_abs (nullable, binary64) receive the per-column sums of |dy * xh|
+ * and |dy|. */
+int oracle_layernorm_bwd(const void *dy, const void *x, int in_dt, const void *w, int w_dt,
+                         const void *mean, const void *rstd, int stat_dt, void *dx, int dx_dt,
+                         void *dw, void *db, int dwb_dt, double *dw_abs, double *db_abs,
+                         int64_t M, int64_t N)
+{
+    double *aw, *ab, *awa, *aba;
+
+    if (!dy || !x || !w || !mean || !rstd || !dx || !dw || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(in_dt) || !dtype_ok(w_dt) || !dtype_ok(stat_dt) || !dtype_ok(dx_dt) ||
+        !dtype_ok(dwb_dt))
+        return OR_ERR_ARG;
+    aw = (double *)calloc((size_t)N, sizeof(double));
+    ab = (double *)calloc((size_t)N, sizeof(double));
+    awa = (double *)calloc((size_t)N, sizeof(double));
+    aba = (double *)calloc((size_t)N, sizeof(double));
+    if (!aw || !ab || !awa || !aba) {
+        free(aw);
+        free(ab);
+        free(awa);
+        free(aba);
+        return OR_ERR_NOMEM;
+    }
+    for (int64_t i = 0; i < M; i++) {
+        double mu = load_elem(mean, stat_dt, i);
+        double rs = load_elem(rstd, stat_dt, i);
+        double mg = 0.0, mgx = 0.0;
+        for (int64_t j = 0; j < N; j++) {
+            double g = load_elem(dy, in_dt, i * N + j) * load_elem(w, w_dt, j);
+            double xh = (load_elem(x, in_dt, i * N + j) - mu) * rs;
+            mg += g;
+            mgx += g * xh;
+        }
+        mg /= (double)N;
+        mgx /= (double)N;
+        for (int64_t j = 0; j < N; j++) {
+            double d = load_elem(dy, in_dt, i * N + j);
+            double g = d * load_elem(w, w_dt, j);
+            double xh = (load_elem(x, in_dt, i * N + j) - mu) * rs;
+            store_elem(dx, dx_dt, i * N + j, rs * (g - mg - xh * mgx));
+            aw[j] += d * xh;
+            ab[j] += d;
+            awa[j] += fabs(d * xh);
+            aba[j] += fabs(d);
+        }
+    }
+    for (int64_t j = 0; j < N; j++) {
+        store_elem(dw, dwb_dt, j, aw[j]);
+        if (db)
+            store_elem(db, dwb_dt, j, ab[j]);
+        if (dw_abs)
+            dw_abs[j] = awa[j];
+        if (db_abs)
+            db_abs[j] = aba[j];
+    }
+    free(aw);
+    free(ab);
+    free(awa);
+    free(aba);
+    return OR_OK;
 }

@@ -14,7 +14,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "addrms_oracle.c")
-PINS = ["tests/test_oracle_bf16.py", "tests/test_oracle_fwd.py", "tests/test_oracle_bwd.py"]
+PINS = ["tests/test_oracle_bf16.py", "tests/test_oracle_fwd.py", "tests/test_oracle_bwd.py",
+        "tests/test_oracle_layernorm.py"]
 
 MUTANTS = {
     "eps_outside_root": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms) + eps"),
@@ -39,17 +40,44 @@ MUTANTS = {
     "bwd_dw_without_rstd": ("acc[j] += d * xh;", "acc[j] += d * load_elem(h, in_dt, i * N + j);"),
     "fused_bwd_drops_dres": ("rs * (g - xh * c) + extra);", "rs * (g - xh * c));"),
     "fused_bwd_subtracts_dres": ("rs * (g - xh * c) + extra);", "rs * (g - xh * c) - extra);"),
+    "ln_unbiased_variance": ("double var = sq / (double)N;", "double var = sq / (double)(N > 1 ? N - 1 : 1);"),
+    "ln_eps_outside_root": ("double rs = 1.0 / sqrt(var + eps);", "double rs = 1.0 / sqrt(var) + eps;"),
+    "ln_no_centering": ("double d = load_elem(x, x_dt, i * N + j) - mu;", "double d = load_elem(x, x_dt, i * N + j);"),
+    "ln_mean_divisor": ("double mu = sum / (double)N;", "double mu = sum / (double)(N + 1);"),
+    "ln_bias_dropped": ("v += load_elem(b, w_dt, j);", "v += 0.0;"),
+    "ln_bwd_no_mean_g": ("rs * (g - mg - xh * mgx)", "rs * (g - xh * mgx)"),
+    "ln_bwd_no_projection": ("rs * (g - mg - xh * mgx)", "rs * (g - mg)"),
+    "ln_db_weighted": ("ab[j] += d;", "ab[j] += g;"),
+    "ln_dw_uncentred": ("aw[j] += d * xh;", "aw[j] += d * load_elem(x, in_dt, i * N + j) * rs;"),
     "bwd_dx_missing_outer_rstd": ("rs * (g - xh * c)", "(g - xh * c)"),
 }
 
 
+# anchors that occur more than once: (old, new, which occurrence, count)
+MUTANTS.update({
+    "ln_bwd_g_without_weight": ("double g = load_elem(dy, in_dt, i * N + j) * load_elem(w, w_dt, j);",
+                                "double g = load_elem(dy, in_dt, i * N + j);", 1, 2),
+    "ln_bwd_dx_without_weight": ("double g = d * load_elem(w, w_dt, j);", "double g = d;", 1, 2),
+})
+for _k in ("bwd_g_without_weight", "bwd_dx_without_weight"):
+    MUTANTS[_k] = MUTANTS[_k] + (0, 2)
+
+
+def _plant(src: str, spec) -> str:
+    old, new = spec[0], spec[1]
+    which, count = (spec[2], spec[3]) if len(spec) > 2 else (0, 1)
+    assert src.count(old) == count, f"anchor {old!r} occurs {src.count(old)} times"
+    at = -1
+    for _ in range(which + 1):
+        at = src.index(old, at + 1)
+    return src[:at] + new + src[at + len(old):]
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_fail_on_planted_mistake(name, tmp_path):
-    old, new = MUTANTS[name]
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation anchor not unique for {name}"
     mutant = tmp_path / "mutant.c"
-    mutant.write_text(src.replace(old, new))
+    mutant.write_text(_plant(src, MUTANTS[name]))
     lib = tmp_path / "libmutant.so"
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                            "-o", str(lib), str(mutant), "-lm"])
