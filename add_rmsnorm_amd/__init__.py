@@ -11,6 +11,9 @@ Operations (same names as the C ABI):
     add_rmsnorm_fwd(x, r, w, eps)     -> y, residual_out (and rstd)
     rmsnorm_bwd(dy, x, w, rstd)       -> dx, dw
     add_rmsnorm_bwd(dy, dres, h, w, rstd) -> dh (gradient of x and of r), dw
+    layernorm_fwd(x, w, b, eps)       -> y (and mean, rstd)
+    add_layernorm_fwd(x, r, w, b, eps) -> y, residual_out (and mean, rstd)
+    layernorm_bwd(dy, x, w, mean, rstd) -> dx, dw, db
 """
 from __future__ import annotations
 
@@ -20,7 +23,8 @@ import os
 import torch
 
 __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_bwd",
-           "rmsnorm_bwd_workspace_bytes", "AddRmsError", "LIB_PATH", "lib"]
+           "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
+           "layernorm_bwd_workspace_bytes", "AddRmsError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -53,6 +57,14 @@ def _load():
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.add_rmsnorm_bwd.restype = i32
     lib.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.layernorm_fwd.restype = i32
+    lib.layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_layernorm_fwd.restype = i32
+    lib.add_layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.layernorm_bwd_workspace_bytes.restype = sz
+    lib.layernorm_bwd_workspace_bytes.argtypes = [i64, i64]
+    lib.layernorm_bwd.restype = i32
+    lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     lib.addrms_last_hip_error.restype = i32
@@ -248,3 +260,100 @@ def add_rmsnorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
     if st != 0:
         raise AddRmsError(st, "add_rmsnorm_bwd")
     return dh, dw
+
+
+def _stats(x, mean, rstd, want):
+    if want:
+        mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if mean is None else mean
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if rstd is None else rstd
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        if t is not None:
+            _dev(t, n, torch.float32, x.shape[:-1])
+    return mean, rstd
+
+
+def layernorm_fwd(x: torch.Tensor, w: torch.Tensor, b=None, eps: float = 1e-5, *, y=None,
+                  mean=None, rstd=None, return_stats: bool = False):
+    """y = (x - mean) / sqrt(var + eps) * w (+ b) over the last dimension.
+    Returns y, or (y, mean, rstd) with float32 statistics."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(w, "w", shape=(N,))
+    if b is not None:
+        _dev(b, "b", w.dtype, (N,))
+    y = torch.empty_like(x) if y is None else _dev(y, "y", x.dtype, x.shape)
+    mean, rstd = _stats(x, mean, rstd, return_stats)
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.layernorm_fwd(_p(x), _p(w), _p(b), _p(y), _p(mean), _p(rstd), M, N, float(eps),
+                                _code(x, "x"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "layernorm_fwd")
+    return (y, mean, rstd) if (return_stats or rstd is not None) else y
+
+
+def add_layernorm_fwd(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, b=None,
+                      eps: float = 1e-5, *, y=None, residual_out=None, mean=None, rstd=None,
+                      return_stats: bool = False):
+    """residual_out = x + r (float32 add, stored in x's dtype);
+    y = LayerNorm(residual_out) * w (+ b).  Returns (y, residual_out) or
+    (y, residual_out, mean, rstd)."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(r, "r", x.dtype, x.shape)
+    _dev(w, "w", shape=(N,))
+    if b is not None:
+        _dev(b, "b", w.dtype, (N,))
+    y = torch.empty_like(x) if y is None else _dev(y, "y", x.dtype, x.shape)
+    residual_out = (torch.empty_like(x) if residual_out is None
+                    else _dev(residual_out, "residual_out", x.dtype, x.shape))
+    mean, rstd = _stats(x, mean, rstd, return_stats)
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.add_layernorm_fwd(_p(x), _p(r), _p(w), _p(b), _p(y), _p(residual_out),
+                                    _p(mean), _p(rstd), M, N, float(eps), _code(x, "x"),
+                                    _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "add_layernorm_fwd")
+    if return_stats or rstd is not None:
+        return y, residual_out, mean, rstd
+    return y, residual_out
+
+
+def layernorm_bwd_workspace_bytes(M: int, N: int) -> int:
+    """Device scratch bytes layernorm_bwd needs for M rows of N."""
+    return int(_lib.layernorm_bwd_workspace_bytes(M, N))
+
+
+def layernorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, mean: torch.Tensor,
+                  rstd: torch.Tensor, *, dx=None, dw=None, db=None, with_db: bool = True,
+                  workspace: torch.Tensor | None = None):
+    """Gradients of LayerNorm from the saved float32 mean and rstd: returns
+    (dx, dw, db) with dw and db float32 (db None when with_db is False and no
+    db buffer is given).  `dx` may be `dy` or `x`."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(dy, "dy", x.dtype, x.shape)
+    _dev(w, "w", shape=(N,))
+    _dev(mean, "mean", torch.float32, x.shape[:-1])
+    _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    dx = torch.empty_like(x) if dx is None else _dev(dx, "dx", x.dtype, x.shape)
+    dw = (torch.empty(N, dtype=torch.float32, device=x.device) if dw is None
+          else _dev(dw, "dw", torch.float32, (N,)))
+    if db is None and with_db:
+        db = torch.empty(N, dtype=torch.float32, device=x.device)
+    elif db is not None:
+        _dev(db, "db", torch.float32, (N,))
+    need = layernorm_bwd_workspace_bytes(M, N)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    else:
+        _dev(workspace, "workspace")
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.layernorm_bwd(_p(dy), _p(x), _p(w), _p(mean), _p(rstd), _p(dx), _p(dw), _p(db),
+                                _p(workspace), workspace.numel() * workspace.element_size(), M,
+                                N, _code(x, "x"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "layernorm_bwd")
+    return dx, dw, db

@@ -300,8 +300,9 @@ int colreduce(const void *workspace, int P, int N, float *dw, hipStream_t s)
     return e == hipSuccess ? ADDRMS_OK : fail_hip(e);
 }
 
-int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, float *rstd,
-               int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream, bool fused)
+int fwd_common(int norm, const void *x, const void *r, const void *w, const void *b, void *y,
+               void *res, float *mean, float *rstd, int64_t M, int64_t N, float eps, int dtype,
+               int w_dtype, void *stream, bool fused)
 {
     // ---- validation (no HIP call) ----
     // With M == 0 the matrices are empty and may be NULL.
@@ -318,7 +319,18 @@ int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, 
     const Span sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype)), sy = span(y, mat);
     const Span sr = fused ? span(r, mat) : Span{}, sres = fused ? span(res, mat) : Span{};
     const Span srs = rstd ? span(rstd, (size_t)M * 4u) : Span{};
-    if (bad_alias(sy, sx, true) || bad_alias(sy, sw, false) || bad_alias(sy, srs, false))
+    const Span sb = b ? span(b, (size_t)N * esize(w_dtype)) : Span{};
+    const Span smu = mean ? span(mean, (size_t)M * 4u) : Span{};
+    if (bad_alias(sy, sx, true) || bad_alias(sy, sw, false) || bad_alias(sy, srs, false) ||
+        bad_alias(sy, sb, false) || bad_alias(sy, smu, false))
+        return ADDRMS_ERR_ALIAS;
+    if (fused && (bad_alias(sres, sb, false) || bad_alias(sres, smu, false)))
+        return ADDRMS_ERR_ALIAS;
+    if (mean && (bad_alias(smu, sx, false) || bad_alias(smu, sw, false) ||
+                 bad_alias(smu, sb, false) || bad_alias(smu, srs, false) ||
+                 (fused && bad_alias(smu, sr, false))))
+        return ADDRMS_ERR_ALIAS;
+    if (rstd && bad_alias(srs, sb, false))
         return ADDRMS_ERR_ALIAS;
     if (fused && (bad_alias(sy, sr, true) || bad_alias(sres, sx, true) ||
                   bad_alias(sres, sr, true) || bad_alias(sres, sw, false) ||
@@ -334,11 +346,11 @@ int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int c = combo(dtype, w_dtype);
     const FwdTable &tab = fwd_table(c);
-    FwdArgs a{x, fused ? r : x, w, y, fused ? res : y, rstd, M, (int)N, 0, eps};
+    FwdArgs a{x, fused ? r : x, w, b, y, fused ? res : y, mean, rstd, M, (int)N, 0, eps};
 
     const int nv = vec_elems(dtype);
     const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(x) &&
-                        aligned16(w) && aligned16(y) &&
+                        aligned16(w) && aligned16(y) && (!b || aligned16(b)) &&
                         (!fused || (aligned16(r) && aligned16(res)));
     int cus = 0;
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
@@ -346,7 +358,7 @@ int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, 
     int wi = 0, vi = 0;
     if (vec_ok && pick_fwd(M, (int)(N / nv), cus, &wi, &vi)) {
         a.nvec = (int)(N / nv);
-        const KernelRef &k = tab.vec[fused ? 1 : 0][wi][vi];
+        const KernelRef &k = tab.vec[norm][fused ? 1 : 0][wi][vi];
         const int rpb = kWprList[wi] == 1 ? 4 : 1;
         const int64_t blocks = (M + rpb - 1) / rpb;
         // One block per row group (the hardware dispatcher balances the
@@ -357,28 +369,30 @@ int fwd_common(const void *x, const void *r, const void *w, void *y, void *res, 
             return rc;
         return launch(k, dim3(grid), 0, &a, s);
     }
-    const KernelRef &k = tab.elem[fused ? 1 : 0];
+    const KernelRef &k = tab.elem[norm][fused ? 1 : 0];
     int grid = 0;
     if ((rc = persistent_grid(k, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
         return rc;
     return launch(k, dim3(grid), 0, &a, s);
 }
 
-int bwd_common(const void *dy, const void *dres, const void *x, const void *w, const float *rstd,
-               void *dx, float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
-               int dtype, int w_dtype, void *stream)
+int bwd_common(int norm, const void *dy, const void *dres, const void *x, const void *w,
+               const float *mean, const float *rstd, void *dx, float *dw, float *db,
+               void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
+               int w_dtype, void *stream)
 {
     const bool res = dres != nullptr;
+    const bool ln = norm == kLayer;
     // ---- validation (no HIP call) ----
     // With M == 0 the row data is empty and may be NULL; dw is still written.
-    if (!w || !dw || (M != 0 && (!dy || !x || !rstd || !dx)))
+    if (!w || !dw || (M != 0 && (!dy || !x || !rstd || !dx || (ln && !mean))))
         return ADDRMS_ERR_NULL;
     if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
         return ADDRMS_ERR_DTYPE;
     int rc = check_shape(M, N, dtype);
     if (rc != ADDRMS_OK)
         return rc;
-    const size_t need = rmsnorm_bwd_workspace_bytes(M, N);
+    const size_t need = ln ? layernorm_bwd_workspace_bytes(M, N) : rmsnorm_bwd_workspace_bytes(M, N);
     if (M > 0 && (!workspace || workspace_bytes < need || need == 0))
         return ADDRMS_ERR_WORKSPACE;
     const size_t mat = (size_t)M * (size_t)N * esize(dtype);
@@ -386,7 +400,17 @@ int bwd_common(const void *dy, const void *dres, const void *x, const void *w, c
     const Span srs = span(rstd, (size_t)M * 4u), sdx = span(dx, mat), sdw = span(dw, (size_t)N * 4u);
     const Span sws = workspace ? span(workspace, need) : Span{};
     const Span sdr = res ? span(dres, mat) : Span{};
+    const Span smu = (ln && mean) ? span(mean, (size_t)M * 4u) : Span{};
+    const Span sdb = db ? span(db, (size_t)N * 4u) : Span{};
     if (res && (bad_alias(sdx, sdr, true) || bad_alias(sdw, sdr, false) || bad_alias(sws, sdr, false)))
+        return ADDRMS_ERR_ALIAS;
+    if (bad_alias(sdx, smu, false) || bad_alias(sdw, smu, false) || bad_alias(sws, smu, false) ||
+        bad_alias(sdw, sdb, false))
+        return ADDRMS_ERR_ALIAS;
+    if (db && (bad_alias(sdb, sdy, false) || bad_alias(sdb, sx, false) || bad_alias(sdb, sw, false) ||
+               bad_alias(sdb, srs, false) || bad_alias(sdb, smu, false) ||
+               bad_alias(sdb, sws, false) || bad_alias(sdb, sdx, false) ||
+               (res && bad_alias(sdb, sdr, false))))
         return ADDRMS_ERR_ALIAS;
     if (bad_alias(sdx, sdy, true) || bad_alias(sdx, sx, true) || bad_alias(sdx, sw, false) ||
         bad_alias(sdx, srs, false) || bad_alias(sdx, sdw, false) || bad_alias(sdx, sws, false))
@@ -400,24 +424,30 @@ int bwd_common(const void *dy, const void *dres, const void *x, const void *w, c
 
     // ---- variant and launch ----
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (M == 0) // dw of an empty batch is zero: the column reduce over P = 0 rows writes it
-        return colreduce(workspace, 0, (int)N, dw, s);
+    if (M == 0) { // dw (db) of an empty batch is zero: the column reduce over P = 0 rows writes it
+        if ((rc = colreduce(workspace, 0, (int)N, dw, s)) != ADDRMS_OK)
+            return rc;
+        return db ? colreduce(workspace, 0, (int)N, db, s) : ADDRMS_OK;
+    }
     const BwdTable &tab = bwd_table(combo(dtype, w_dtype));
-    const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u));
+    // LayerNorm: the workspace holds dw partials then db partials, pmax rows each
+    const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u)) / (ln ? 2 : 1);
     const int64_t pmax = ws_rows < kMaxPartials ? ws_rows : kMaxPartials;
-    BwdArgs a{dy, res ? dres : dy, x, w, rstd, dx, static_cast<float *>(workspace), M, (int)N, 0, 0, 0};
+    float *ws = static_cast<float *>(workspace);
+    BwdArgs a{dy, res ? dres : dy, x, w, mean, rstd, dx, ws, ln ? ws + (size_t)pmax * N : ws,
+              M, (int)N, 0, 0, 0};
 
     const int nv = vec_elems(dtype);
     const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(dy) &&
                         aligned16(x) && aligned16(w) && aligned16(dx) && aligned16(workspace) &&
-                        (!res || aligned16(dres));
+                        (!res || aligned16(dres)) && (!ln || (pmax * N) % 4 == 0);
     int cus = 0;
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
         return rc;
     int wi = 0, vi = 0;
     if (vec_ok && pick_bwd(M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
         a.nvec = (int)(N / nv);
-        const KernelRef &k = tab.vec[res ? 1 : 0][wi][vi];
+        const KernelRef &k = tab.vec[norm][res ? 1 : 0][wi][vi];
         const int rpb = 4 / kWprList[wi];
         const size_t smem = (size_t)(rpb / 2) * (size_t)N * 4u;
         int grid = 0;
@@ -433,18 +463,20 @@ int bwd_common(const void *dy, const void *dres, const void *x, const void *w, c
         const int64_t P = (M + chunk - 1) / chunk;
         a.P = (int)P;
         a.chunk = chunk;
-        if ((rc = launch(tab.elem_dw, dim3((unsigned)((N + 63) / 64), (unsigned)P), 0, &a, s)) !=
+        if ((rc = launch(tab.elem_dw[norm], dim3((unsigned)((N + 63) / 64), (unsigned)P), 0, &a, s)) !=
             ADDRMS_OK)
             return rc;
         int grid = 0;
-        const KernelRef &kdx = tab.elem_dx[res ? 1 : 0];
+        const KernelRef &kdx = tab.elem_dx[norm][res ? 1 : 0];
         if ((rc = persistent_grid(kdx, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
             return rc;
         if ((rc = launch(kdx, dim3(grid), 0, &a, s)) != ADDRMS_OK)
             return rc;
     }
-    // dw = column sums of the partials, same stream (ordered after stage 1)
-    return colreduce(workspace, a.P, (int)N, dw, s);
+    // dw (db) = column sums of the partials, same stream (ordered after stage 1)
+    if ((rc = colreduce(a.ws, a.P, (int)N, dw, s)) != ADDRMS_OK)
+        return rc;
+    return (ln && db) ? colreduce(a.ws2, a.P, (int)N, db, s) : ADDRMS_OK;
 }
 
 } // namespace
@@ -457,14 +489,31 @@ extern "C" {
 int rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int64_t M, int64_t N,
                 float eps, int dtype, int w_dtype, void *stream)
 {
-    return fwd_common(x, nullptr, w, y, nullptr, rstd, M, N, eps, dtype, w_dtype, stream, false);
+    return fwd_common(kRms, x, nullptr, w, nullptr, y, nullptr, nullptr, rstd, M, N, eps, dtype,
+                      w_dtype, stream, false);
 }
 
 int add_rmsnorm_fwd(const void *x, const void *r, const void *w, void *y, void *residual_out,
                     float *rstd, int64_t M, int64_t N, float eps, int dtype, int w_dtype,
                     void *stream)
 {
-    return fwd_common(x, r, w, y, residual_out, rstd, M, N, eps, dtype, w_dtype, stream, true);
+    return fwd_common(kRms, x, r, w, nullptr, y, residual_out, nullptr, rstd, M, N, eps, dtype,
+                      w_dtype, stream, true);
+}
+
+int layernorm_fwd(const void *x, const void *w, const void *b, void *y, float *mean, float *rstd,
+                  int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream)
+{
+    return fwd_common(kLayer, x, nullptr, w, b, y, nullptr, mean, rstd, M, N, eps, dtype, w_dtype,
+                      stream, false);
+}
+
+int add_layernorm_fwd(const void *x, const void *r, const void *w, const void *b, void *y,
+                      void *residual_out, float *mean, float *rstd, int64_t M, int64_t N,
+                      float eps, int dtype, int w_dtype, void *stream)
+{
+    return fwd_common(kLayer, x, r, w, b, y, residual_out, mean, rstd, M, N, eps, dtype, w_dtype,
+                      stream, true);
 }
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N)
@@ -481,8 +530,8 @@ int rmsnorm_bwd(const void *dy, const void *x, const void *w, const float *rstd,
                 float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
                 int dtype, int w_dtype, void *stream)
 {
-    return bwd_common(dy, nullptr, x, w, rstd, dx, dw, workspace, workspace_bytes, M, N, dtype,
-                      w_dtype, stream);
+    return bwd_common(kRms, dy, nullptr, x, w, nullptr, rstd, dx, dw, nullptr, workspace,
+                      workspace_bytes, M, N, dtype, w_dtype, stream);
 }
 
 int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void *w,
@@ -490,8 +539,23 @@ int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void 
                     size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
                     void *stream)
 {
-    return bwd_common(dy, dres, h, w, rstd, dh, dw, workspace, workspace_bytes, M, N, dtype,
-                      w_dtype, stream);
+    return bwd_common(kRms, dy, dres, h, w, nullptr, rstd, dh, dw, nullptr, workspace,
+                      workspace_bytes, M, N, dtype, w_dtype, stream);
+}
+
+size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N)
+{
+    const size_t one = rmsnorm_bwd_workspace_bytes(M, N);
+    return one <= SIZE_MAX / 2 ? 2 * one : 0;
+}
+
+int layernorm_bwd(const void *dy, const void *x, const void *w, const float *mean,
+                  const float *rstd, void *dx, float *dw, float *db, void *workspace,
+                  size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
+                  void *stream)
+{
+    return bwd_common(kLayer, dy, nullptr, x, w, mean, rstd, dx, dw, db, workspace,
+                      workspace_bytes, M, N, dtype, w_dtype, stream);
 }
 
 const char *addrms_status_str(int status)

@@ -13,14 +13,19 @@ struct FwdArgs {
     const void *x;
     const void *r;
     const void *w;
+    const void *b; // LayerNorm bias (w's dtype); may be null
     void *y;
     void *res;
+    float *mean; // LayerNorm only; may be null
     float *rstd; // may be null
     int64_t M;
     int N;
     int nvec; // 16-byte vectors per row (vector path)
     float eps;
 };
+
+// Which normalisation a kernel computes.
+enum Norm : int { kRms = 0, kLayer = 1 };
 
 // Backward arguments.  For the fused op's backward, x is the saved residual
 // h, dres the gradient of residual_out (added to dx), and dx receives dh.
@@ -29,9 +34,11 @@ struct BwdArgs {
     const void *dres; // fused backward only
     const void *x;
     const void *w;
+    const float *mean; // LayerNorm only
     const float *rstd;
     void *dx;
-    float *ws; // [P, N] float partial sums of dw
+    float *ws;  // [P, N] float partial sums of dw
+    float *ws2; // [P, N] float partial sums of db (LayerNorm)
     int64_t M;
     int N;
     int nvec;
@@ -74,16 +81,18 @@ struct KernelRef {
 inline int combo(int dtype, int w_dtype) { return dtype * 2 + w_dtype; }
 
 // Kernel tables, one translation unit per dtype combination.
-// fwd_vec: [fused][wpr_idx][vpl_idx]; fwd_elem: [fused].
+// fwd vec: [norm][fused][wpr_idx][vpl_idx]; fwd elem: [norm][fused].
 struct FwdTable {
-    KernelRef vec[2][kNumWpr][kNumVpl];
-    KernelRef elem[2];
+    KernelRef vec[2][2][kNumWpr][kNumVpl];
+    KernelRef elem[2][2];
 };
-// bwd vec / elem_dx: [with residual gradient][...].
+// bwd vec: [norm][with residual gradient][wpr_idx][vpl_idx]; elem_dx:
+// [norm][with residual gradient]; elem_dw: [norm].  (LayerNorm has no fused
+// backward: its residual-gradient slots are empty.)
 struct BwdTable {
-    KernelRef vec[2][kBwdNumWpr][kNumVpl];
-    KernelRef elem_dx[2];
-    KernelRef elem_dw;
+    KernelRef vec[2][2][kBwdNumWpr][kNumVpl];
+    KernelRef elem_dx[2][2];
+    KernelRef elem_dw[2];
 };
 
 const FwdTable &fwd_table(int combo_idx);

@@ -1,13 +1,14 @@
-// HIP kernels for gfx950 (CDNA4): RMSNorm and fused residual-Add + RMSNorm,
-// forward and backward.
+// HIP kernels for gfx950 (CDNA4): RMSNorm, fused residual-Add + RMSNorm, and
+// the LayerNorm variants, forward and backward.
 //
 // The operations are the RMSNorm and fused Add + RMSNorm ops named by the
 // "Machete" README ("Built-In Areas") and the KernelAgent digest (the
-// KernelAgent-Oink summary); the row reduction follows the "CuTe DSL" skill
-// page's float32 pattern for RMSNorm (Workflow 0: per-thread loops, a
-// butterfly within the warp, then a cross-warp step through shared memory),
-// which here becomes per-lane FMAs, a DPP wave64 sum, and an LDS step only when
-// several waves share a row.
+// KernelAgent-Oink summary), and the LayerNorm that the "CuTe DSL" skill page
+// lists beside RMSNorm (Workflow 0: the CTA-norm example and the reduction
+// pattern).  The row reduction follows that page's float32 pattern (Workflow
+// 0: per-thread loops, a butterfly within the warp, then a cross-warp step
+// through shared memory), which here becomes per-lane FMAs, a DPP wave64 sum,
+// and an LDS step only when several waves share a row.
 //
 // Memory traffic is the whole cost (a few VALU ops per 2-4 bytes moved), so
 // the design is about HBM streaming, not arithmetic:
@@ -17,7 +18,7 @@
 //     once;
 //   * rows are spread over enough waves that each lane holds about two
 //     16-byte vectors per tensor: many short, independent row-blocks keep the
-//     most rows in flight (one LDS exchange per row when a row has several
+//     most rows in flight (one LDS exchange per row sum when a row has several
 //     waves; none when it has one);
 //   * every kernel walks rows with a grid stride, so the same code serves a
 //     one-block-per-row grid (the forward's default) and a persistent grid
@@ -44,10 +45,11 @@ constexpr int kPol = ADDRMS_STREAM_POLICY;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Arithmetic type of the backward's row reduction and dx.  float32 tensors use
-// binary64: dx = rstd * (g - xh * c) cancels when xh * c is close to g (always
-// so for very short rows), and the float32 products and sum would then leave
-// too few correct bits for a float32 result.  bfloat16 tensors use float32.
+// Arithmetic type of the backward's row reductions and dx.  float32 tensors
+// use binary64: dx = rstd * (g - xh * c) cancels when xh * c is close to g
+// (always so for very short rows), and the float32 products and sum would then
+// leave too few correct bits for a float32 result.  bfloat16 tensors use
+// float32.
 template <typename T> struct BwdCompute { using type = float; };
 template <> struct BwdCompute<float> { using type = double; };
 
@@ -61,8 +63,12 @@ __device__ __forceinline__ double fma_ct(double a, double b, double c) { return 
 // Forward, vector path.  WPR waves per row, VPL 16-byte vectors per lane:
 // lane `l` of wave `q` (of the row's WPR waves) owns vectors
 // v = q*64 + l + k*64*WPR, k < VPL.  Requires 16-byte aligned rows.
+// NORM = kRms: y = h * rstd * w, rstd = 1/sqrt(mean(h^2) + eps).
+// NORM = kLayer: y = (h - mean) * rstd * w (+ b), rstd = 1/sqrt(var + eps),
+// the variance taken about the mean from the registers (two passes over the
+// row, one over memory).
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, bool FUSED, int WPR, int VPL>
+template <typename T, typename WT, int NORM, bool FUSED, int WPR, int VPL>
 __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
@@ -76,15 +82,30 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
     const int nvec = a.nvec;
     const float inv_n = 1.0f / (float)a.N;
 
-    __shared__ float part[2][16];
+    // Sum of one value per lane over the row's WPR waves.  Each sum of a row
+    // has its own LDS slot; a slot is reused two rows later, after at least
+    // two barriers, so one barrier per sum suffices.
+    __shared__ float part[4][16];
+    auto row_sum = [&](float v, int slot) -> float {
+        float t = wave_sum(v);
+        if constexpr (WPR > 1) {
+            if (lane == 0)
+                part[slot][wir] = t;
+            __syncthreads();
+            t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i)
+                t += part[slot][i];
+        }
+        return t;
+    };
 
-    const int64_t step = (int64_t)gridDim.x * RPB;
     // Blocks are dealt to the 8 XCDs round-robin, so the rows in flight form
     // one compact window of memory; giving each XCD a contiguous range of rows
     // instead measured 8 % slower.
-    const unsigned bid = blockIdx.x;
+    const int64_t step = (int64_t)gridDim.x * RPB;
     int it = 0;
-    for (int64_t row = (int64_t)bid * RPB + rib; row < a.M; row += step, ++it) {
+    for (int64_t row = (int64_t)blockIdx.x * RPB + rib; row < a.M; row += step, ++it) {
         const size_t base = (size_t)row * (size_t)a.N;
         const u32x4 *xp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.x) + base);
         const u32x4 *rp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.r) + base);
@@ -108,9 +129,9 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
             }
         }
 
-        // 2. residual add (float32), store the residual as T, and sum squares
-        //    of the stored residual
-        float ss = 0.0f;
+        // 2. residual add (float32), store the residual as T, and accumulate
+        //    the first row sum of the stored residual: h^2 (RMS) or h (Layer)
+        float s1 = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             float h[NV];
@@ -129,25 +150,38 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
             }
 #pragma unroll
             for (int e = 0; e < NV; ++e)
-                ss = __builtin_fmaf(h[e], h[e], ss);
+                s1 = (NORM == kRms) ? __builtin_fmaf(h[e], h[e], s1) : s1 + h[e];
         }
 
-        // 3. row sum -> rstd
-        float tot = wave_sum(ss);
-        if constexpr (WPR > 1) {
-            if (lane == 0)
-                part[it & 1][wir] = tot;
-            __syncthreads();
-            tot = 0.0f;
+        // 3. row statistics
+        const int slot = (it & 1) * 2;
+        float mu = 0.0f, rs;
+        if constexpr (NORM == kRms) {
+            rs = 1.0f / __builtin_sqrtf(row_sum(s1, slot) * inv_n + a.eps);
+        } else {
+            mu = row_sum(s1, slot) * inv_n;
+            float s2 = 0.0f;
 #pragma unroll
-            for (int i = 0; i < WPR; ++i)
-                tot += part[it & 1][i];
+            for (int k = 0; k < VPL; ++k) {
+                if (vbase + k * VSTRIDE < nvec) {
+                    float h[NV];
+                    unpack<T>(hv[k], h);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) {
+                        const float d = h[e] - mu;
+                        s2 = __builtin_fmaf(d, d, s2);
+                    }
+                }
+            }
+            rs = 1.0f / __builtin_sqrtf(row_sum(s2, slot + 1) * inv_n + a.eps);
+            if (a.mean != nullptr && wir == 0 && lane == 0)
+                a.mean[row] = mu;
         }
-        const float rs = 1.0f / __builtin_sqrtf(tot * inv_n + a.eps);
         if (a.rstd != nullptr && wir == 0 && lane == 0)
             a.rstd[row] = rs;
 
-        // 4. y = h * rstd * w, rounded once to T
+        // 4. y = (h - mean) * rstd * w (+ b), rounded once to T
+        const bool bias = NORM == kLayer && a.b != nullptr;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = vbase + k * VSTRIDE;
@@ -157,17 +191,24 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
                 load_w<T, WT>(a.w, v, wf);
 #pragma unroll
                 for (int e = 0; e < NV; ++e)
-                    o[e] = (h[e] * rs) * wf[e];
+                    o[e] = ((NORM == kLayer ? h[e] - mu : h[e]) * rs) * wf[e];
+                if (bias) {
+                    float bf[NV];
+                    load_w<T, WT>(a.b, v, bf);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e)
+                        o[e] += bf[e];
+                }
                 st_stream<kPol>(yp + v, pack<T>(o));
             }
         }
     }
 }
 
-// Block-wide sum for 256-thread blocks; `slot` alternates between calls so one
-// barrier per call suffices.
-template <typename S>
-__device__ __forceinline__ S block256_sum(S v, S (&part)[2][4], int slot)
+// Block-wide sum for 256-thread blocks.  Each call site uses its own slot of
+// `part`, alternating between rows, so one barrier per call suffices.
+template <typename S, int NS>
+__device__ __forceinline__ S block256_sum(S v, S (&part)[NS][4], int slot)
 {
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -180,19 +221,23 @@ __device__ __forceinline__ S block256_sum(S v, S (&part)[2][4], int slot)
 
 // ---------------------------------------------------------------------------
 // Forward, element-wise path: any N, any alignment.  One 256-thread block per
-// row, two passes over the row (the second re-reads the stored residual).
+// row; the row is re-read from memory (mostly cache) for each pass: the sum,
+// the LayerNorm variance, and the output.  The fused op re-reads the stored
+// residual.
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, bool FUSED>
+template <typename T, typename WT, int NORM, bool FUSED>
 __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 {
-    __shared__ float part[2][4];
+    __shared__ float part[4][4];
     const int tid = threadIdx.x;
     const int N = a.N;
     const float inv_n = 1.0f / (float)N;
+    const void *src = FUSED ? a.res : a.x; // where h is read back from
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x, ++it) {
         const int64_t base = row * (int64_t)N;
-        float ss = 0.0f;
+        const int slot = (it & 1) * 2;
+        float s1 = 0.0f;
         for (int j = tid; j < N; j += 256) {
             float h;
             if constexpr (FUSED) {
@@ -202,37 +247,59 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
             } else {
                 h = ld_elem<T>(a.x, base + j);
             }
-            ss = __builtin_fmaf(h, h, ss);
+            s1 = (NORM == kRms) ? __builtin_fmaf(h, h, s1) : s1 + h;
         }
-        const float tot = block256_sum(ss, part, it & 1);
-        const float rs = 1.0f / __builtin_sqrtf(tot * inv_n + a.eps);
+        float mu = 0.0f, rs;
+        if constexpr (NORM == kRms) {
+            rs = 1.0f / __builtin_sqrtf(block256_sum(s1, part, slot) * inv_n + a.eps);
+        } else {
+            mu = block256_sum(s1, part, slot) * inv_n;
+            float s2 = 0.0f;
+            for (int j = tid; j < N; j += 256) {
+                const float d = ld_elem<T>(src, base + j) - mu;
+                s2 = __builtin_fmaf(d, d, s2);
+            }
+            rs = 1.0f / __builtin_sqrtf(block256_sum(s2, part, slot + 1) * inv_n + a.eps);
+            if (a.mean != nullptr && tid == 0)
+                a.mean[row] = mu;
+        }
         if (a.rstd != nullptr && tid == 0)
             a.rstd[row] = rs;
+        const bool bias = NORM == kLayer && a.b != nullptr;
         for (int j = tid; j < N; j += 256) {
-            const float h = FUSED ? ld_elem<T>(a.res, base + j) : ld_elem<T>(a.x, base + j);
-            st_elem<T>(a.y, base + j, (h * rs) * ld_elem<WT>(a.w, j));
+            const float h = ld_elem<T>(src, base + j);
+            float o = ((NORM == kLayer ? h - mu : h) * rs) * ld_elem<WT>(a.w, j);
+            if (bias)
+                o += ld_elem<WT>(a.b, j);
+            st_elem<T>(a.y, base + j, o);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Backward, vector path, 256-thread blocks, WPR in {1, 2, 4}: RPB = 4 / WPR
-// rows per block step.  Each lane keeps its columns' dw partial sums in
-// registers across all rows it visits; at the end the block's row groups are
-// summed through LDS (pairwise, fixed order) and written as one row of the
-// workspace: ws[blockIdx.x, :].  Dynamic LDS: (RPB / 2) * N floats.
-// RES: the fused op's backward, which adds the residual gradient dres to dx
-// before its one rounding (dx then holds dh, the gradient of x and of r).
+// rows per block step.  Each lane keeps its columns' dw (and, for LayerNorm,
+// db) partial sums in registers across all rows it visits; at the end the
+// block's row groups are summed through LDS (pairwise, fixed order) and
+// written as one row of the workspace: ws[blockIdx.x, :] (and ws2 for db).
+// Dynamic LDS: (RPB / 2) * N floats.
+// NORM = kRms: g = dy*w, xh = x*rstd, dx = rstd*(g - xh*mean(g*xh)).
+// NORM = kLayer: xh = (x - mean)*rstd, dx = rstd*(g - mean(g) - xh*mean(g*xh)),
+// db = sum dy.
+// RES (RMSNorm only): the fused op's backward, which adds the residual
+// gradient dres to dx before its one rounding (dx then holds dh, the gradient
+// of x and of r).
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, bool RES, int WPR, int VPL>
+template <typename T, typename WT, int NORM, bool RES, int WPR, int VPL>
 __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
     constexpr int VSTRIDE = 64 * WPR;
     constexpr int RPB = 4 / WPR;
+    constexpr bool LN = NORM == kLayer;
     using CT = typename BwdCompute<T>::type;
     extern __shared__ __attribute__((aligned(16))) float lds[];
-    __shared__ CT part[2][4];
+    __shared__ CT part[2][2][4]; // [row parity][sum][wave]
 
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -241,20 +308,25 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
     const int vbase = wir * 64 + lane;
     const int nvec = a.nvec;
     const int N = a.N;
+    const CT inv_n = inv_n_ct<CT>(N);
 
-    float acc[VPL][NV];
+    float accw[VPL][NV];
+    float accb[LN ? VPL : 1][LN ? NV : 1];
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
 #pragma unroll
-        for (int e = 0; e < NV; ++e)
-            acc[k][e] = 0.0f;
+        for (int e = 0; e < NV; ++e) {
+            accw[k][e] = 0.0f;
+            if constexpr (LN)
+                accb[k][e] = 0.0f;
+        }
 
     const int64_t step = (int64_t)gridDim.x * RPB;
     // Loads of one row group into registers.  Vector indices past the row are
     // clamped to its last vector (in bounds) and masked out at use, so the
     // loads need no branches; a row past M reads row 0 and is not used.
     auto load_row = [&](int64_t row, u32x4 (&dyv)[VPL], u32x4 (&xv)[VPL],
-                        u32x4 (&drv)[RES ? VPL : 1], float &rs) {
+                        u32x4 (&drv)[RES ? VPL : 1], float &rs, float &mu) {
         const bool act = row < a.M;
         const size_t base = (size_t)(act ? row : 0) * (size_t)N;
         const u32x4 *dyp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dy) + base);
@@ -270,20 +342,21 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
                 drv[k] = ld_stream<kPol>(drp + vc);
         }
         rs = act ? a.rstd[row] : 0.0f;
+        mu = (LN && act) ? a.mean[row] : 0.0f;
     };
     u32x4 dyv[VPL], xv[VPL];
     u32x4 drv[RES ? VPL : 1];
-    float rs = 0.0f;
+    float rs = 0.0f, mu = 0.0f;
     int it = 0;
     for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < a.M; row0 += step, ++it) {
         const int64_t row = row0 + rib;
         const bool active = row < a.M; // uniform per wave
         const size_t base = (size_t)(active ? row : 0) * (size_t)N;
         u32x4 *dxp = reinterpret_cast<u32x4 *>(static_cast<T *>(a.dx) + base);
-        load_row(row, dyv, xv, drv, rs);
+        load_row(row, dyv, xv, drv, rs, mu);
 
-        // sum_j dy_j w_j x_j over the row
-        CT p = 0;
+        // row sums: p = sum dy*w*x (RMS) or sum g (Layer); q = sum g*xh (Layer)
+        CT p = 0, q = 0;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = vbase + k * VSTRIDE;
@@ -293,22 +366,38 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
                 unpack<T>(xv[k], xx);
                 load_w<T, WT>(a.w, v, wf);
 #pragma unroll
-                for (int e = 0; e < NV; ++e)
-                    p = fma_ct((CT)d[e] * (CT)wf[e], (CT)xx[e], p);
+                for (int e = 0; e < NV; ++e) {
+                    const CT g = (CT)d[e] * (CT)wf[e];
+                    if constexpr (LN) {
+                        p += g;
+                        q = fma_ct(g, ((CT)xx[e] - (CT)mu) * (CT)rs, q);
+                    } else {
+                        p = fma_ct(g, (CT)xx[e], p);
+                    }
+                }
             }
         }
         p = wave_sum(p);
+        if constexpr (LN)
+            q = wave_sum(q);
         if constexpr (WPR > 1) {
-            if (lane == 0)
-                part[it & 1][wave] = p;
+            if (lane == 0) {
+                part[it & 1][0][wave] = p;
+                part[it & 1][1][wave] = q;
+            }
             __syncthreads();
             p = 0;
+            q = 0;
 #pragma unroll
-            for (int i = 0; i < WPR; ++i)
-                p += part[it & 1][rib * WPR + i];
+            for (int i = 0; i < WPR; ++i) {
+                p += part[it & 1][0][rib * WPR + i];
+                q += part[it & 1][1][rib * WPR + i];
+            }
         }
-        // c = mean_j(g_j * xh_j) = rstd * mean_j(dy_j w_j x_j)
-        const CT c = (p * (CT)rs) * (CT)inv_n_ct<CT>(N);
+        // RMS: c1 = 0, c2 = mean(g*xh) = rstd*mean(dy*w*x)
+        // Layer: c1 = mean(g), c2 = mean(g*xh)
+        const CT c1 = LN ? p * inv_n : (CT)0;
+        const CT c2 = LN ? q * inv_n : (p * (CT)rs) * inv_n;
 
         if (active) {
 #pragma unroll
@@ -323,13 +412,15 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
                         unpack<T>(drv[k], dr);
 #pragma unroll
                     for (int e = 0; e < NV; ++e) {
-                        const CT xh = (CT)xx[e] * (CT)rs;
+                        const CT xh = ((CT)xx[e] - (CT)mu) * (CT)rs;
                         const CT g = (CT)d[e] * (CT)wf[e];
-                        CT dxe = (CT)rs * (g - xh * c);
+                        CT dxe = (CT)rs * (g - c1 - xh * c2);
                         if constexpr (RES)
                             dxe += (CT)dr[e];
                         o[e] = (float)dxe;
-                        acc[k][e] = __builtin_fmaf(d[e], (float)xh, acc[k][e]);
+                        accw[k][e] = __builtin_fmaf(d[e], (float)xh, accw[k][e]);
+                        if constexpr (LN)
+                            accb[k][e] += d[e];
                     }
                     st_stream<kPol>(dxp + v, pack<T>(o));
                 }
@@ -337,29 +428,29 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
         }
     }
 
-    // dw: sum the block's RPB row groups (same columns) and write one row.
-    auto put = [&](float *dst) {
+    // dw (db): sum the block's RPB row groups (same columns) and write one row.
+    auto put = [&](auto &acc, float *dst) {
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = vbase + k * VSTRIDE;
             if (v < nvec) {
-                u32x4 *q = reinterpret_cast<u32x4 *>(dst + (size_t)v * NV);
+                u32x4 *qq = reinterpret_cast<u32x4 *>(dst + (size_t)v * NV);
 #pragma unroll
                 for (int h = 0; h < NV / 4; ++h)
-                    q[h] = u32x4{__float_as_uint(acc[k][4 * h]), __float_as_uint(acc[k][4 * h + 1]),
-                                 __float_as_uint(acc[k][4 * h + 2]), __float_as_uint(acc[k][4 * h + 3])};
+                    qq[h] = u32x4{__float_as_uint(acc[k][4 * h]), __float_as_uint(acc[k][4 * h + 1]),
+                                  __float_as_uint(acc[k][4 * h + 2]), __float_as_uint(acc[k][4 * h + 3])};
             }
         }
     };
-    auto add = [&](const float *src) {
+    auto add = [&](auto &acc, const float *src) {
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = vbase + k * VSTRIDE;
             if (v < nvec) {
-                const u32x4 *q = reinterpret_cast<const u32x4 *>(src + (size_t)v * NV);
+                const u32x4 *qq = reinterpret_cast<const u32x4 *>(src + (size_t)v * NV);
 #pragma unroll
                 for (int h = 0; h < NV / 4; ++h) {
-                    const u32x4 t = q[h];
+                    const u32x4 t = qq[h];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         acc[k][4 * h + i] += __uint_as_float(t[i]);
@@ -367,44 +458,51 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
             }
         }
     };
-    float *out = a.ws + (size_t)blockIdx.x * (size_t)N;
-    if constexpr (RPB == 4) {
-        if (rib >= 2)
-            put(lds + (size_t)(rib - 2) * N);
-        __syncthreads();
-        if (rib < 2)
-            add(lds + (size_t)rib * N);
-        __syncthreads();
-        if (rib == 1)
-            put(lds);
-        __syncthreads();
-        if (rib == 0) {
-            add(lds);
-            put(out);
+    auto merge = [&](auto &acc, float *out) {
+        if constexpr (RPB == 4) {
+            if (rib >= 2)
+                put(acc, lds + (size_t)(rib - 2) * N);
+            __syncthreads();
+            if (rib < 2)
+                add(acc, lds + (size_t)rib * N);
+            __syncthreads();
+            if (rib == 1)
+                put(acc, lds);
+            __syncthreads();
+            if (rib == 0) {
+                add(acc, lds);
+                put(acc, out);
+            }
+        } else if constexpr (RPB == 2) {
+            if (rib == 1)
+                put(acc, lds);
+            __syncthreads();
+            if (rib == 0) {
+                add(acc, lds);
+                put(acc, out);
+            }
+        } else {
+            put(acc, out);
         }
-    } else if constexpr (RPB == 2) {
-        if (rib == 1)
-            put(lds);
-        __syncthreads();
-        if (rib == 0) {
-            add(lds);
-            put(out);
-        }
-    } else {
-        put(out);
+    };
+    merge(accw, a.ws + (size_t)blockIdx.x * (size_t)N);
+    if constexpr (LN) {
+        __syncthreads(); // the LDS is reused for db
+        merge(accb, a.ws2 + (size_t)blockIdx.x * (size_t)N);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Backward, element-wise path (any N, any alignment): dx one block per row in
-// two passes; dw partials per (column block, row chunk).  dw runs first, so dx
-// may overwrite dy or x.
+// two passes; dw (db) partials per (column block, row chunk).  dw runs first,
+// so dx may overwrite dy or x.
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, bool RES>
+template <typename T, typename WT, int NORM, bool RES>
 __global__ void __launch_bounds__(256) bwd_elem_dx_kernel(BwdArgs a)
 {
     using CT = typename BwdCompute<T>::type;
-    __shared__ CT part[2][4];
+    constexpr bool LN = NORM == kLayer;
+    __shared__ CT part[4][4];
     const int tid = threadIdx.x;
     const int N = a.N;
     const CT inv_n = inv_n_ct<CT>(N);
@@ -412,15 +510,28 @@ __global__ void __launch_bounds__(256) bwd_elem_dx_kernel(BwdArgs a)
     for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x, ++it) {
         const int64_t base = row * (int64_t)N;
         const CT rs = (CT)a.rstd[row];
-        CT p = 0;
-        for (int j = tid; j < N; j += 256)
-            p = fma_ct((CT)ld_elem<T>(a.dy, base + j) * (CT)ld_elem<WT>(a.w, j),
-                       (CT)ld_elem<T>(a.x, base + j), p);
-        const CT c = (block256_sum(p, part, it & 1) * rs) * inv_n;
+        const CT mu = LN ? (CT)a.mean[row] : (CT)0;
+        CT p = 0, q = 0;
         for (int j = tid; j < N; j += 256) {
-            const CT xh = (CT)ld_elem<T>(a.x, base + j) * rs;
             const CT g = (CT)ld_elem<T>(a.dy, base + j) * (CT)ld_elem<WT>(a.w, j);
-            CT dxe = rs * (g - xh * c);
+            const CT xv = (CT)ld_elem<T>(a.x, base + j);
+            if constexpr (LN) {
+                p += g;
+                q = fma_ct(g, (xv - mu) * rs, q);
+            } else {
+                p = fma_ct(g, xv, p);
+            }
+        }
+        const int slot = (it & 1) * 2;
+        p = block256_sum(p, part, slot);
+        if constexpr (LN)
+            q = block256_sum(q, part, slot + 1);
+        const CT c1 = LN ? p * inv_n : (CT)0;
+        const CT c2 = LN ? q * inv_n : (p * rs) * inv_n;
+        for (int j = tid; j < N; j += 256) {
+            const CT xh = ((CT)ld_elem<T>(a.x, base + j) - mu) * rs;
+            const CT g = (CT)ld_elem<T>(a.dy, base + j) * (CT)ld_elem<WT>(a.w, j);
+            CT dxe = rs * (g - c1 - xh * c2);
             if constexpr (RES)
                 dxe += (CT)ld_elem<T>(a.dres, base + j);
             st_elem<T>(a.dx, base + j, (float)dxe);
@@ -428,25 +539,35 @@ __global__ void __launch_bounds__(256) bwd_elem_dx_kernel(BwdArgs a)
     }
 }
 
-template <typename T>
+template <typename T, int NORM>
 __global__ void __launch_bounds__(256) bwd_elem_dw_kernel(BwdArgs a)
 {
-    __shared__ float red[4][64];
+    constexpr bool LN = NORM == kLayer;
+    __shared__ float red[2][4][64];
     const int lane = threadIdx.x & 63;
     const int s = threadIdx.x >> 6;
     const int c = blockIdx.x * 64 + lane;
     const int64_t r0 = (int64_t)blockIdx.y * a.chunk;
     const int64_t r1 = r0 + a.chunk < a.M ? r0 + a.chunk : a.M;
-    float acc = 0.0f;
+    float aw = 0.0f, ab = 0.0f;
     if (c < a.N)
         for (int64_t i = r0 + s; i < r1; i += 4) {
             const int64_t idx = i * (int64_t)a.N + c;
-            acc = __builtin_fmaf(ld_elem<T>(a.dy, idx), ld_elem<T>(a.x, idx) * a.rstd[i], acc);
+            const float d = ld_elem<T>(a.dy, idx);
+            const float mu = LN ? a.mean[i] : 0.0f;
+            aw = __builtin_fmaf(d, (ld_elem<T>(a.x, idx) - mu) * a.rstd[i], aw);
+            ab += d;
         }
-    red[s][lane] = acc;
+    red[0][s][lane] = aw;
+    red[1][s][lane] = ab;
     __syncthreads();
-    if (s == 0 && c < a.N)
-        a.ws[(size_t)blockIdx.y * a.N + c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    if (s == 0 && c < a.N) {
+        a.ws[(size_t)blockIdx.y * a.N + c] =
+            (red[0][0][lane] + red[0][1][lane]) + (red[0][2][lane] + red[0][3][lane]);
+        if constexpr (LN)
+            a.ws2[(size_t)blockIdx.y * a.N + c] =
+                (red[1][0][lane] + red[1][1][lane]) + (red[1][2][lane] + red[1][3][lane]);
+    }
 }
 
 // dw[c] = sum_p ws[p, c], the second stage of the dw reduction.  The partial
@@ -536,54 +657,69 @@ __global__ void __launch_bounds__(256) dw_colreduce_kernel(const float *ws, int 
 // Kernel tables for one (row dtype, weight dtype) combination.
 // ---------------------------------------------------------------------------
 template <typename T, typename WT> struct TableBuilder {
-    template <bool F, int WPR, int VPL> static KernelRef fwd_ref()
+    template <int NM, bool F, int WPR, int VPL> static KernelRef fwd_ref()
     {
         if constexpr (fwd_built(WPR, VPL))
-            return KernelRef{reinterpret_cast<const void *>(&fwd_vec_kernel<T, WT, F, WPR, VPL>),
+            return KernelRef{reinterpret_cast<const void *>(&fwd_vec_kernel<T, WT, NM, F, WPR, VPL>),
                              kBlockFwd(WPR)};
         else
             return KernelRef{nullptr, 0};
     }
-    template <bool F, int WI, int... VI>
+    template <int NM, bool F, int WI, int... VI>
     static void fwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
     {
-        ((row[VI] = fwd_ref<F, kWprList[WI], kVplList[VI]>()), ...);
+        ((row[VI] = fwd_ref<NM, F, kWprList[WI], kVplList[VI]>()), ...);
     }
-    template <bool F, int... WI>
+    template <int NM, bool F, int... WI>
     static void fwd_all(FwdTable &t, std::integer_sequence<int, WI...>)
     {
-        (fwd_row<F, WI>(t.vec[F ? 1 : 0][WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
+        (fwd_row<NM, F, WI>(t.vec[NM][F ? 1 : 0][WI], std::make_integer_sequence<int, kNumVpl>{}),
+         ...);
+    }
+    template <int NM> static void fwd_norm(FwdTable &t)
+    {
+        fwd_all<NM, false>(t, std::make_integer_sequence<int, kNumWpr>{});
+        fwd_all<NM, true>(t, std::make_integer_sequence<int, kNumWpr>{});
+        t.elem[NM][0] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, false>), 256};
+        t.elem[NM][1] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, true>), 256};
     }
     static FwdTable fwd()
     {
         FwdTable t{};
-        fwd_all<false>(t, std::make_integer_sequence<int, kNumWpr>{});
-        fwd_all<true>(t, std::make_integer_sequence<int, kNumWpr>{});
-        t.elem[0] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, false>), 256};
-        t.elem[1] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, true>), 256};
+        fwd_norm<kRms>(t);
+        fwd_norm<kLayer>(t);
         return t;
     }
 
-    template <bool R, int WI, int... VI>
+    template <int NM, bool R, int WI, int... VI>
     static void bwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
     {
         ((row[VI] = KernelRef{reinterpret_cast<const void *>(
-                                  &bwd_vec_kernel<T, WT, R, kWprList[WI], kVplList[VI]>),
+                                  &bwd_vec_kernel<T, WT, NM, R, kWprList[WI], kVplList[VI]>),
                               kBwdBlock}),
          ...);
     }
-    template <bool R, int... WI> static void bwd_all(BwdTable &t, std::integer_sequence<int, WI...>)
+    template <int NM, bool R, int... WI>
+    static void bwd_all(BwdTable &t, std::integer_sequence<int, WI...>)
     {
-        (bwd_row<R, WI>(t.vec[R ? 1 : 0][WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
+        (bwd_row<NM, R, WI>(t.vec[NM][R ? 1 : 0][WI], std::make_integer_sequence<int, kNumVpl>{}),
+         ...);
     }
     static BwdTable bwd()
     {
         BwdTable t{};
-        bwd_all<false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
-        bwd_all<true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
-        t.elem_dx[0] = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, false>), 256};
-        t.elem_dx[1] = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, true>), 256};
-        t.elem_dw = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dw_kernel<T>), 256};
+        bwd_all<kRms, false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        bwd_all<kRms, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        bwd_all<kLayer, false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        t.elem_dx[kRms][0] =
+            KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kRms, false>), 256};
+        t.elem_dx[kRms][1] =
+            KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kRms, true>), 256};
+        t.elem_dx[kLayer][0] =
+            KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kLayer, false>), 256};
+        t.elem_dw[kRms] = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dw_kernel<T, kRms>), 256};
+        t.elem_dw[kLayer] =
+            KernelRef{reinterpret_cast<const void *>(&bwd_elem_dw_kernel<T, kLayer>), 256};
         return t;
     }
 };

@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, bf16 fused Add+RMSNorm M=16384 N=7168"
 WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
-HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, true, 8, 2>"
+HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 8, 2>"
 KERNEL_SOURCES = ["add_rmsnorm_amd/csrc/kernels.hpp", "add_rmsnorm_amd/csrc/device.hpp",
                   "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp",
                   "add_rmsnorm_amd/csrc/api.hip"]
@@ -443,7 +443,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "fwd_vec_kernel<bf16_t, bf16_t, true, 8, 2> (fused, 8 waves/row, "
+                     "kernel": "fwd_vec_kernel<bf16_t, bf16_t, kRms, true, 8, 2> (fused, 8 waves/row, "
                                "2 x 16 B per lane and tensor, one row per block)",
                      "avg_launch_us": round(h["ev"] / args.steps * 1e6, 3)},
     }

@@ -1,6 +1,6 @@
 /*
  * addrms.h -- C ABI of the RMSNorm / fused residual-Add + RMSNorm library
- * for AMD Instinct MI355X (gfx950).
+ * (with LayerNorm variants) for AMD Instinct MI355X (gfx950).
  *
  * Operations (the pages name them; the formula is the textbook RMSNorm,
  * Zhang & Sennrich 2019, with eps inside the square root):
@@ -145,6 +145,45 @@ int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void 
                     const float *rstd, void *dh, float *dw, void *workspace,
                     size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
                     void *stream);
+
+/*
+ * LayerNorm variants.  The "CuTe DSL" skill page lists a CTA-level LayerNorm
+ * example (Workflow 0, example index) and names LayerNorm beside RMSNorm in
+ * its float32 reduction pattern (Workflow 0); the formula is the textbook one
+ * (Ba, Kiros & Hinton 2016), biased variance, eps inside the square root:
+ *     mean_i = mean_j(h_ij),  rstd_i = 1 / sqrt(mean_j((h_ij - mean_i)^2) + eps)
+ *     y_ij   = round((h_ij - mean_i) * rstd_i * w_j + b_j)
+ * with h = x (layernorm_fwd) or h = residual_out = round(fp32(x) + fp32(r))
+ * (add_layernorm_fwd, as add_rmsnorm_fwd).  The variance is taken about the
+ * mean (two passes over the row held in registers), not as E[h^2] - mean^2.
+ *   b           [N]  w_dtype  bias; NULL for none
+ *   mean, rstd  [M]  float32  optional outputs (NULL: not written)
+ * Other arguments, aliasing and errors as for the RMSNorm calls.
+ */
+int layernorm_fwd(const void *x, const void *w, const void *b, void *y, float *mean, float *rstd,
+                  int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream);
+
+int add_layernorm_fwd(const void *x, const void *r, const void *w, const void *b, void *y,
+                      void *residual_out, float *mean, float *rstd, int64_t M, int64_t N,
+                      float eps, int dtype, int w_dtype, void *stream);
+
+/* Workspace for layernorm_bwd: dw and db partial sums, twice
+ * rmsnorm_bwd_workspace_bytes(M, N).  Pure arithmetic, no HIP call. */
+size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N);
+
+/*
+ * LayerNorm backward from the saved mean and rstd (both required):
+ *     xh = (x - mean_i) * rstd_i,  g = dy * w
+ *     dx = round(rstd_i * (g - mean_j(g) - xh * mean_j(g * xh)))
+ *     dw_j = sum_i dy_ij * xh_ij,  db_j = sum_i dy_ij    (overwritten)
+ *   db    [N] float32  output; NULL when there is no bias
+ *   workspace          >= layernorm_bwd_workspace_bytes(M, N) bytes
+ * Other arguments, aliasing (dx may be dy or x) and errors as rmsnorm_bwd.
+ */
+int layernorm_bwd(const void *dy, const void *x, const void *w, const float *mean,
+                  const float *rstd, void *dx, float *dw, float *db, void *workspace,
+                  size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
+                  void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *addrms_status_str(int status);

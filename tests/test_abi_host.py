@@ -35,6 +35,11 @@ def lib():
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.layernorm_bwd_workspace_bytes.restype = sz
+    lib.layernorm_bwd_workspace_bytes.argtypes = [i64, i64]
+    lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     return lib
@@ -43,6 +48,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd",
                                   "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
+                                  "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
+                                  "layernorm_bwd_workspace_bytes",
                                   "addrms_status_str", "addrms_last_hip_error"])
 
 
@@ -169,3 +176,30 @@ def test_empty_batch_is_a_noop_without_device(lib):
     assert add(lib, M=0, x=None, r=None, y=None, res=None) == OK
     assert fwd(lib, M=0, w=None) == E_NULL
     assert bwd(lib, M=0, dw=None) == E_NULL
+
+
+def test_layernorm_validation(lib):
+    WB = 0x68000000  # bias
+    ln = lambda **k: lib.layernorm_fwd(k.get("x", A), k.get("w", W), k.get("b", WB),
+                                       k.get("y", B), k.get("mean", None), k.get("rstd", None),
+                                       k.get("M", 4), k.get("N", 64), k.get("eps", 1e-5),
+                                       BF16, BF16, None)
+    assert ln(x=None) == E_NULL and ln(w=None) == E_NULL
+    assert ln(b=None, M=0) == OK and ln(M=0) == OK
+    assert ln(N=0) == E_SHAPE and ln(eps=-1.0) == E_EPS
+    assert ln(y=WB) == E_ALIAS            # y over the bias
+    assert ln(mean=A + 4) == E_ALIAS      # mean inside x
+    assert ln(mean=E, rstd=E + 8) == E_ALIAS  # mean and rstd overlap
+    aln = lambda **k: lib.add_layernorm_fwd(A, C, W, k.get("b", WB), B, k.get("res", D), None,
+                                            None, 4, 64, 1e-5, BF16, BF16, None)
+    assert aln(res=None) == E_NULL and aln(res=WB) == E_ALIAS
+    assert lib.layernorm_bwd_workspace_bytes(10, 8) == 2 * 10 * 8 * 4
+    assert lib.layernorm_bwd_workspace_bytes(0, 8) == 0
+    wsb = lib.layernorm_bwd_workspace_bytes(4, 64)
+    lb = lambda **k: lib.layernorm_bwd(A, C, W, k.get("mean", 0x58000000), E, B, D,
+                                       k.get("db", 0x48000000), k.get("ws", 0x70000000),
+                                       k.get("wsb", wsb), 4, 64, BF16, BF16, None)
+    assert lb(mean=None) == E_NULL
+    assert lb(wsb=wsb - 1) == E_WS
+    assert lb(db=D + 4) == E_ALIAS        # db overlaps dw
+    assert lb(db=0x70000000 + 64) == E_ALIAS  # db inside the workspace

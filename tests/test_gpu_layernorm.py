@@ -1,0 +1,168 @@
+"""GPU parity of the LayerNorm variants (HIP library through the C ABI)
+against the CPU oracle on seeded inputs: forward with and without bias and
+residual, the saved statistics, backward dx/dw/db, every kernel variant,
+ragged shapes, in-place buffers and the empty batch."""
+import sys
+
+import pytest
+import torch
+
+import add_rmsnorm_amd as ar
+import oracle
+import synth
+from parity import assert_bits_equal, assert_close, assert_dw_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+EPS = 1e-5
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def inputs(M, N, dtype, wdtype=None, seed=0, bias=True):
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, wdtype, seed=seed, r_std=0.5)
+    # activations with a non-zero mean, so the centring matters
+    inp["x"] = synth.store(synth.normal(seed, "x", (M, N), mean=0.75), dtype)
+    inp["b"] = synth.store(synth.normal(seed, "b", (N,), std=0.1), wdtype or dtype) if bias else None
+    return inp
+
+
+def check_fwd(inp, fused, what=""):
+    x, w, b = inp["x"], inp["w"], inp["b"]
+    g = lambda t: None if t is None else t.to(DEV)
+    if fused:
+        y, res, mean, rstd = ar.add_layernorm_fwd(g(x), g(inp["r"]), g(w), g(b), EPS,
+                                                  return_stats=True)
+        ry, rres, rmean, rrstd = oracle.add_layernorm_fwd(x, inp["r"], w, b, EPS)
+        assert_bits_equal(res.cpu(), rres, f"residual_out {what}")
+    else:
+        y, mean, rstd = ar.layernorm_fwd(g(x), g(w), g(b), EPS, return_stats=True)
+        ry, rmean, rrstd = oracle.layernorm_fwd(x, w, b, EPS)
+    torch.cuda.synchronize()
+    assert_close(y.cpu(), ry, f"y {what}")
+    assert_close(mean.cpu(), rmean, f"mean {what}", atol=1e-6, rtol=1e-5)
+    assert_close(rstd.cpu(), rrstd, f"rstd {what}", atol=0, rtol=1e-5)
+
+
+def check_bwd(inp, what="", with_db=True):
+    x, w = inp["x"], inp["w"]
+    M, N = x.shape
+    dy = synth.store(synth.normal(7, "dy", (M, N)), x.dtype)
+    _, mean, rstd = oracle.layernorm_fwd(x, w, inp["b"], EPS)
+    dx, dw, db = ar.layernorm_bwd(dy.to(DEV), x.to(DEV), w.to(DEV), mean.to(DEV), rstd.to(DEV),
+                                  with_db=with_db)
+    torch.cuda.synchronize()
+    rdx, rdw, rdb, mw, mb = oracle.layernorm_bwd(dy, x, w, mean, rstd)
+    assert_close(dx.cpu(), rdx, f"dx {what}")
+    assert_dw_close(dw.cpu(), rdw, mw, f"dw {what}")
+    if with_db:
+        assert_dw_close(db.cpu(), rdb, mb, f"db {what}")
+    else:
+        assert db is None
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("M,N", [(16384, 7168), (4096, 4096), (3, 8192)])
+def test_forward_bf16(fused, bias, M, N):
+    check_fwd(inputs(M, N, torch.bfloat16, seed=M + N, bias=bias), fused, f"{M}x{N}")
+
+
+@pytest.mark.parametrize("dtype,wdtype", [(torch.float32, torch.float32),
+                                          (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.bfloat16)])
+def test_forward_dtypes(dtype, wdtype):
+    inp = inputs(513, 2048, dtype, wdtype, seed=3)
+    check_fwd(inp, False, str(dtype))
+    check_fwd(inp, True, str(dtype))
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8, 16])
+def test_forward_forced_waves_per_row(monkeypatch, wpr):
+    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+    for M, N in [(37, 4096), (5, 1032)]:
+        inp = inputs(M, N, torch.bfloat16, seed=M, bias=True)
+        check_fwd(inp, True, f"wpr={wpr} {M}x{N}")
+        check_fwd(inp, False, f"wpr={wpr} {M}x{N}")
+
+
+@pytest.mark.parametrize("N", [1, 7, 64, 65, 4095, 8193, 65536])
+def test_forward_edge_shapes(N):
+    M = max(1, min(300, (1 << 22) // N))
+    inp = inputs(M, N, torch.bfloat16, seed=N)
+    check_fwd(inp, True, f"N={N}")
+    check_fwd(inp, False, f"N={N}")
+
+
+@pytest.mark.parametrize("M,N", [(4, 4096), (64, 1000)])
+def test_forward_elementwise(monkeypatch, M, N):
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    inp = inputs(M, N, torch.bfloat16, seed=11)
+    check_fwd(inp, True, "elem")
+    check_fwd(inp, False, "elem")
+
+
+def test_forward_in_place_and_empty():
+    inp = inputs(200, 4096, torch.bfloat16, seed=13)
+    ry, rres, _, _ = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
+    x, r = inp["x"].to(DEV), inp["r"].to(DEV)
+    ar.add_layernorm_fwd(x, r, inp["w"].to(DEV), inp["b"].to(DEV), EPS, y=x, residual_out=r)
+    torch.cuda.synchronize()
+    assert_bits_equal(r.cpu(), rres, "residual in r")
+    assert_close(x.cpu(), ry, "y in x")
+    e = torch.empty(0, 4096, dtype=torch.bfloat16, device=DEV)
+    y = ar.layernorm_fwd(e, inp["w"].to(DEV), None, EPS)
+    assert y.shape == (0, 4096)
+
+
+@pytest.mark.parametrize("M,N", [(32768, 4096), (3001, 1032), (7, 8192)])
+def test_backward_bf16(M, N):
+    check_bwd(inputs(M, N, torch.bfloat16, seed=M), f"{M}x{N}")
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4])
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.float32, torch.float32),
+                                          (torch.bfloat16, torch.float32)])
+def test_backward_variants(monkeypatch, wpr, dtype, wdtype):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", str(wpr))
+    check_bwd(inputs(1000, 2048, dtype, wdtype, seed=wpr), f"wpr={wpr}")
+
+
+@pytest.mark.parametrize("N", [1, 5, 65, 4100, 16392])
+def test_backward_edge_shapes(N):
+    check_bwd(inputs(max(1, min(500, (1 << 22) // N)), N, torch.bfloat16, seed=N), f"N={N}")
+
+
+@pytest.mark.parametrize("M,N", [(9, 4096), (130, 1000)])
+def test_backward_elementwise_and_no_db(monkeypatch, M, N):
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    check_bwd(inputs(M, N, torch.bfloat16, seed=17), "elem")
+    check_bwd(inputs(M, N, torch.float32, seed=18), "elem f32", with_db=False)
+
+
+def test_backward_in_place_and_empty():
+    inp = inputs(300, 4096, torch.bfloat16, seed=19)
+    x, w = inp["x"], inp["w"]
+    dy = synth.store(synth.normal(19, "dy", (300, 4096)), torch.bfloat16)
+    _, mean, rstd = oracle.layernorm_fwd(x, w, None, EPS)
+    rdx, rdw, rdb, mw, mb = oracle.layernorm_bwd(dy, x, w, mean, rstd)
+    d = dy.to(DEV)
+    dx, dw, db = ar.layernorm_bwd(d, x.to(DEV), w.to(DEV), mean.to(DEV), rstd.to(DEV), dx=d)
+    torch.cuda.synchronize()
+    assert_close(d.cpu(), rdx, "dx over dy")
+    assert_dw_close(dw.cpu(), rdw, mw)
+    assert_dw_close(db.cpu(), rdb, mb, "db")
+    e = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    z = torch.empty(0, dtype=torch.float32, device=DEV)
+    dw0 = torch.full((64,), 3.0, device=DEV)
+    db0 = torch.full((64,), 3.0, device=DEV)
+    ar.layernorm_bwd(e, e, w[:64].to(DEV), z, z, dw=dw0, db=db0)
+    torch.cuda.synchronize()
+    assert torch.all(dw0 == 0) and torch.all(db0 == 0)
