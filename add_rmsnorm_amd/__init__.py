@@ -14,6 +14,7 @@ Operations (same names as the C ABI):
     layernorm_fwd(x, w, b, eps)       -> y (and mean, rstd)
     add_layernorm_fwd(x, r, w, b, eps) -> y, residual_out (and mean, rstd)
     layernorm_bwd(dy, x, w, mean, rstd) -> dx, dw, db
+    add_layernorm_bwd(dy, dres, h, w, mean, rstd) -> dh, dw, db
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ import torch
 
 __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_bwd",
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
-           "layernorm_bwd_workspace_bytes", "AddRmsError", "LIB_PATH", "lib"]
+           "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "AddRmsError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -65,6 +66,9 @@ def _load():
     lib.layernorm_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.layernorm_bwd.restype = i32
     lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.add_layernorm_bwd.restype = i32
+    lib.add_layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32,
+                                      i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     lib.addrms_last_hip_error.restype = i32
@@ -357,3 +361,40 @@ def layernorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, mean: torc
     if st != 0:
         raise AddRmsError(st, "layernorm_bwd")
     return dx, dw, db
+
+
+def add_layernorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
+                      mean: torch.Tensor, rstd: torch.Tensor, *, dh=None, dw=None, db=None,
+                      with_db: bool = True, workspace: torch.Tensor | None = None):
+    """Backward of add_layernorm_fwd: from dy, the residual_out gradient dres
+    (None for zero), the saved residual_out h, mean and rstd, returns
+    (dh, dw, db); dh is the gradient of both x and r."""
+    _dev(h, "h")
+    M, N = _rows(h)
+    _dev(dy, "dy", h.dtype, h.shape)
+    if dres is not None:
+        _dev(dres, "dres", h.dtype, h.shape)
+    _dev(w, "w", shape=(N,))
+    _dev(mean, "mean", torch.float32, h.shape[:-1])
+    _dev(rstd, "rstd", torch.float32, h.shape[:-1])
+    dh = torch.empty_like(h) if dh is None else _dev(dh, "dh", h.dtype, h.shape)
+    dw = (torch.empty(N, dtype=torch.float32, device=h.device) if dw is None
+          else _dev(dw, "dw", torch.float32, (N,)))
+    if db is None and with_db:
+        db = torch.empty(N, dtype=torch.float32, device=h.device)
+    elif db is not None:
+        _dev(db, "db", torch.float32, (N,))
+    need = layernorm_bwd_workspace_bytes(M, N)
+    if workspace is None:
+        workspace = _workspace(h.device, need)
+    else:
+        _dev(workspace, "workspace")
+    dev = h.get_device()
+    with _OnDevice(dev):
+        st = _lib.add_layernorm_bwd(_p(dy), _p(dres), _p(h), _p(w), _p(mean), _p(rstd), _p(dh),
+                                    _p(dw), _p(db), _p(workspace),
+                                    workspace.numel() * workspace.element_size(), M, N,
+                                    _code(h, "h"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "add_layernorm_bwd")
+    return dh, dw, db

@@ -1,4 +1,5 @@
-"""PyTorch custom ops with autograd for RMSNorm and fused Add + RMSNorm.
+"""PyTorch custom ops with autograd for RMSNorm, LayerNorm and their fused
+residual-Add forms.
 
 The KernelAgent digest describes KernelAgent-Oink's RMSNorm and fused
 Add + RMSNorm as PyTorch custom operators, and the Machete README ("Built-In
@@ -22,9 +23,11 @@ from typing import Optional, Tuple
 import torch
 from torch import Tensor
 
-from . import add_rmsnorm_bwd, add_rmsnorm_fwd, rmsnorm_bwd, rmsnorm_fwd
+from . import (add_layernorm_bwd, add_layernorm_fwd, add_rmsnorm_bwd, add_rmsnorm_fwd,
+               layernorm_bwd, layernorm_fwd, rmsnorm_bwd, rmsnorm_fwd)
 
-__all__ = ["rms_norm", "add_rms_norm", "RMSNorm", "AddRMSNorm"]
+__all__ = ["rms_norm", "add_rms_norm", "layer_norm", "add_layer_norm", "RMSNorm", "AddRMSNorm",
+           "LayerNorm", "AddLayerNorm"]
 
 
 # ---- forward / backward ops -------------------------------------------------
@@ -110,6 +113,97 @@ def _add_backward(ctx, dy, dres, _drstd):
 _add_rms_norm_fwd.register_autograd(_add_backward, setup_context=_add_setup)
 
 
+# ---- LayerNorm ------------------------------------------------------------------
+
+@torch.library.custom_op("addrms::layer_norm_fwd", mutates_args=())
+def _layer_norm_fwd(x: Tensor, w: Tensor, b: Optional[Tensor],
+                    eps: float) -> Tuple[Tensor, Tensor, Tensor]:
+    return layernorm_fwd(x.contiguous(), w.contiguous(), None if b is None else b.contiguous(),
+                         eps, return_stats=True)
+
+
+@_layer_norm_fwd.register_fake
+def _(x, w, b, eps):
+    st = x.new_empty(x.shape[:-1], dtype=torch.float32)
+    return torch.empty_like(x), st, torch.empty_like(st)
+
+
+@torch.library.custom_op("addrms::add_layer_norm_fwd", mutates_args=())
+def _add_layer_norm_fwd(x: Tensor, r: Tensor, w: Tensor, b: Optional[Tensor],
+                        eps: float) -> Tuple[Tensor, Tensor, Tensor, Tensor]:
+    return add_layernorm_fwd(x.contiguous(), r.contiguous(), w.contiguous(),
+                             None if b is None else b.contiguous(), eps, return_stats=True)
+
+
+@_add_layer_norm_fwd.register_fake
+def _(x, r, w, b, eps):
+    st = x.new_empty(x.shape[:-1], dtype=torch.float32)
+    return torch.empty_like(x), torch.empty_like(x), st, torch.empty_like(st)
+
+
+@torch.library.custom_op("addrms::layer_norm_bwd", mutates_args=())
+def _layer_norm_bwd(dy: Tensor, x: Tensor, w: Tensor, mean: Tensor,
+                    rstd: Tensor) -> Tuple[Tensor, Tensor, Tensor]:
+    return layernorm_bwd(dy.contiguous(), x, w, mean, rstd, with_db=True)
+
+
+@_layer_norm_bwd.register_fake
+def _(dy, x, w, mean, rstd):
+    return (torch.empty_like(x), w.new_empty(w.shape, dtype=torch.float32),
+            w.new_empty(w.shape, dtype=torch.float32))
+
+
+@torch.library.custom_op("addrms::add_layer_norm_bwd", mutates_args=())
+def _add_layer_norm_bwd(dy: Tensor, dres: Optional[Tensor], h: Tensor, w: Tensor, mean: Tensor,
+                        rstd: Tensor) -> Tuple[Tensor, Tensor, Tensor]:
+    return add_layernorm_bwd(dy.contiguous(), None if dres is None else dres.contiguous(), h, w,
+                             mean, rstd, with_db=True)
+
+
+@_add_layer_norm_bwd.register_fake
+def _(dy, dres, h, w, mean, rstd):
+    return (torch.empty_like(h), w.new_empty(w.shape, dtype=torch.float32),
+            w.new_empty(w.shape, dtype=torch.float32))
+
+
+def _ln_setup(ctx, inputs, output):
+    x, w, b, _ = inputs
+    _, mean, rstd = output
+    ctx.has_b = b is not None
+    ctx.save_for_backward(x, w, mean, rstd)
+    ctx.mark_non_differentiable(mean, rstd)
+
+
+def _ln_backward(ctx, dy, _dmean, _drstd):
+    x, w, mean, rstd = ctx.saved_tensors
+    if dy is None:
+        dy = torch.zeros_like(x)
+    dx, dw, db = _layer_norm_bwd(dy, x, w, mean, rstd)
+    return dx, dw.to(w.dtype), (db.to(w.dtype) if ctx.has_b else None), None
+
+
+_layer_norm_fwd.register_autograd(_ln_backward, setup_context=_ln_setup)
+
+
+def _add_ln_setup(ctx, inputs, output):
+    _, _, w, b, _ = inputs
+    _, res, mean, rstd = output
+    ctx.has_b = b is not None
+    ctx.save_for_backward(res, w, mean, rstd)
+    ctx.mark_non_differentiable(mean, rstd)
+
+
+def _add_ln_backward(ctx, dy, dres, _dmean, _drstd):
+    h, w, mean, rstd = ctx.saved_tensors
+    if dy is None:
+        dy = torch.zeros_like(h)
+    dh, dw, db = _add_layer_norm_bwd(dy, dres, h, w, mean, rstd)
+    return dh, dh, dw.to(w.dtype), (db.to(w.dtype) if ctx.has_b else None), None
+
+
+_add_layer_norm_fwd.register_autograd(_add_ln_backward, setup_context=_add_ln_setup)
+
+
 # ---- user-facing functions and modules ----------------------------------------
 
 def rms_norm(x: Tensor, w: Tensor, eps: float = 1e-6) -> Tensor:
@@ -148,3 +242,37 @@ class AddRMSNorm(torch.nn.Module):
 
     def forward(self, x: Tensor, residual: Tensor) -> Tuple[Tensor, Tensor]:
         return add_rms_norm(x, residual, self.weight, self.eps)
+
+
+def layer_norm(x: Tensor, w: Tensor, b: Optional[Tensor] = None, eps: float = 1e-5) -> Tensor:
+    """LayerNorm over the last dimension, differentiable in x, w and b."""
+    return _layer_norm_fwd(x, w, b, eps)[0]
+
+
+def add_layer_norm(x: Tensor, r: Tensor, w: Tensor, b: Optional[Tensor] = None,
+                   eps: float = 1e-5) -> Tuple[Tensor, Tensor]:
+    """Fused residual add + LayerNorm: (LayerNorm(x + r) * w + b, x + r)."""
+    y, res, _, _ = _add_layer_norm_fwd(x, r, w, b, eps)
+    return y, res
+
+
+class LayerNorm(torch.nn.Module):
+    """y = LayerNorm(x) * weight + bias (weight ones, bias zeros)."""
+
+    def __init__(self, hidden: int, eps: float = 1e-5, bias: bool = True, dtype=torch.bfloat16,
+                 device=None):
+        super().__init__()
+        self.eps = eps
+        self.weight = torch.nn.Parameter(torch.ones(hidden, dtype=dtype, device=device))
+        self.bias = (torch.nn.Parameter(torch.zeros(hidden, dtype=dtype, device=device))
+                     if bias else None)
+
+    def forward(self, x: Tensor) -> Tensor:
+        return layer_norm(x, self.weight, self.bias, self.eps)
+
+
+class AddLayerNorm(LayerNorm):
+    """(y, residual) = (LayerNorm(x + residual) * weight + bias, x + residual)."""
+
+    def forward(self, x: Tensor, residual: Tensor) -> Tuple[Tensor, Tensor]:
+        return add_layer_norm(x, residual, self.weight, self.bias, self.eps)

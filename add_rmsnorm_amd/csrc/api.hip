@@ -558,6 +558,15 @@ int layernorm_bwd(const void *dy, const void *x, const void *w, const float *mea
                       workspace_bytes, M, N, dtype, w_dtype, stream);
 }
 
+int add_layernorm_bwd(const void *dy, const void *dres, const void *h, const void *w,
+                      const float *mean, const float *rstd, void *dh, float *dw, float *db,
+                      void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
+                      int w_dtype, void *stream)
+{
+    return bwd_common(kLayer, dy, dres, h, w, mean, rstd, dh, dw, db, workspace, workspace_bytes,
+                      M, N, dtype, w_dtype, stream);
+}
+
 const char *addrms_status_str(int status)
 {
     switch (status) {

@@ -87,8 +87,7 @@ struct FwdTable {
     KernelRef elem[2][2];
 };
 // bwd vec: [norm][with residual gradient][wpr_idx][vpl_idx]; elem_dx:
-// [norm][with residual gradient]; elem_dw: [norm].  (LayerNorm has no fused
-// backward: its residual-gradient slots are empty.)
+// [norm][with residual gradient]; elem_dw: [norm].
 struct BwdTable {
     KernelRef vec[2][2][kBwdNumWpr][kNumVpl];
     KernelRef elem_dx[2][2];

@@ -286,9 +286,8 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 // NORM = kRms: g = dy*w, xh = x*rstd, dx = rstd*(g - xh*mean(g*xh)).
 // NORM = kLayer: xh = (x - mean)*rstd, dx = rstd*(g - mean(g) - xh*mean(g*xh)),
 // db = sum dy.
-// RES (RMSNorm only): the fused op's backward, which adds the residual
-// gradient dres to dx before its one rounding (dx then holds dh, the gradient
-// of x and of r).
+// RES: the fused op's backward, which adds the residual gradient dres to dx
+// before its one rounding (dx then holds dh, the gradient of x and of r).
 // ---------------------------------------------------------------------------
 template <typename T, typename WT, int NORM, bool RES, int WPR, int VPL>
 __global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
@@ -711,12 +710,15 @@ template <typename T, typename WT> struct TableBuilder {
         bwd_all<kRms, false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         bwd_all<kRms, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         bwd_all<kLayer, false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        bwd_all<kLayer, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         t.elem_dx[kRms][0] =
             KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kRms, false>), 256};
         t.elem_dx[kRms][1] =
             KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kRms, true>), 256};
         t.elem_dx[kLayer][0] =
             KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kLayer, false>), 256};
+        t.elem_dx[kLayer][1] =
+            KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kLayer, true>), 256};
         t.elem_dw[kRms] = KernelRef{reinterpret_cast<const void *>(&bwd_elem_dw_kernel<T, kRms>), 256};
         t.elem_dw[kLayer] =
             KernelRef{reinterpret_cast<const void *>(&bwd_elem_dw_kernel<T, kLayer>), 256};

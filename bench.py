@@ -336,6 +336,52 @@ def secondary(steps: int):
         "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
         "note": "reads dy, d(residual_out), residual_out; writes dh (= dx = dr) and dw"}
     del sets, ws, h, dy, dres
+    # LayerNorm: fused forward with bias at the headline shape, backward (dw, db)
+    # at the backward workload's shape
+    M, N = 16384, 7168
+    inp = synth.workload_inputs(WORKLOAD)
+    w = inp["w"].cuda()
+    b = (inp["w"].float() - 1.0).to(torch.bfloat16).cuda()
+    sets = []
+    for _ in range(2):
+        x, r = inp["x"].cuda(), inp["r"].cuda()
+        sets.append((x, r, torch.empty_like(x), torch.empty_like(x)))
+
+    def lnf():
+        x, r, y, res = sets[i[0] & 1]
+        ar.add_layernorm_fwd(x, r, w, b, 1e-5, y=y, residual_out=res)
+        i[0] += 1
+
+    _, ev = timed(lnf, steps, 5)
+    nb = 8 * M * N + 4 * N
+    out["add_layernorm_fwd_bf16_16384x7168"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
+                                                                       HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb, "note": "with bias"}
+    del sets
+    M, N = 32768, 4096
+    inp = synth.workload_inputs("rmsnorm_bwd_bf16_32768x4096")
+    w = inp["w"].cuda()
+    sets = []
+    for _ in range(2):
+        x, dy = inp["x"].cuda(), inp["dy"].cuda()
+        _, mean, rstd = ar.layernorm_fwd(x, w, None, 1e-5, return_stats=True)
+        sets.append((dy, x, mean, rstd, torch.empty_like(x)))
+    ws = torch.empty(ar.layernorm_bwd_workspace_bytes(M, N), dtype=torch.uint8, device="cuda")
+    dw, db = torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+
+    def lnb():
+        dy, x, mean, rstd, dx = sets[i[0] & 1]
+        ar.layernorm_bwd(dy, x, w, mean, rstd, dx=dx, dw=dw, db=db, workspace=ws)
+        i[0] += 1
+
+    _, ev = timed(lnb, steps, 5)
+    nb = 6 * M * N + 8 * M + 2 * N + 8 * N
+    out["layernorm_bwd_bf16_32768x4096"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
+                                                                       HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb, "note": "dx, dw, db"}
+    del sets, ws
     # fused forward, 4096 x 4096 bf16 (134 MB: fits in the last-level cache; rotate 4 sets)
     inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_4096x4096")
     M, N = 4096, 4096

@@ -185,6 +185,20 @@ int layernorm_bwd(const void *dy, const void *x, const void *w, const float *mea
                   size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
                   void *stream);
 
+/*
+ * Backward of add_layernorm_fwd, as add_rmsnorm_bwd is for add_rmsnorm_fwd:
+ *     dh = round(rstd_i * (g - mean_j(g) - hh * mean_j(g * hh)) + dres)
+ * with hh = (h - mean_i) * rstd_i; dh is the gradient of both x and r.
+ *   dres  [M, N] dtype  gradient of residual_out; NULL means zero
+ *   h     [M, N] dtype  residual_out saved by the forward
+ *   dh    [M, N] dtype  output; may be dy, dres or h
+ * Other arguments as layernorm_bwd.
+ */
+int add_layernorm_bwd(const void *dy, const void *dres, const void *h, const void *w,
+                      const float *mean, const float *rstd, void *dh, float *dw, float *db,
+                      void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
+                      int w_dtype, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *addrms_status_str(int status);
 

@@ -70,6 +70,9 @@ def _load():
         lib.oracle_add_layernorm_fwd.restype = i32
         lib.oracle_add_layernorm_fwd.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, vp, i32, vp,
                                                  vp, i32, i64, i64, dbl]
+        lib.oracle_add_layernorm_bwd.restype = i32
+        lib.oracle_add_layernorm_bwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
+                                                 vp, vp, i32, vp, vp, i64, i64]
         lib.oracle_layernorm_bwd.restype = i32
         lib.oracle_layernorm_bwd.argtypes = [vp, vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp,
                                              i32, vp, vp, i64, i64]
@@ -255,3 +258,27 @@ def layernorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, mean: torc
                                         _ptr(dw), _ptr(db), _code(dw), _ptr(dw_abs),
                                         _ptr(db_abs), M, N), "layernorm_bwd")
     return dx, dw, db, dw_abs, db_abs
+
+
+def add_layernorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
+                      mean: torch.Tensor, rstd: torch.Tensor, *, dh_dtype=None,
+                      dwb_dtype=torch.float32):
+    """Backward of the fused Add + LayerNorm: dh (the gradient of x and of r),
+    dw, db from dy, the residual_out gradient dres (None for zero), the saved
+    residual h, mean and rstd.  Returns (dh, dw, db, dw_abs, db_abs)."""
+    dy, h, w, mean, rstd = _cpu(dy), _cpu(h), _cpu(w), _cpu(mean), _cpu(rstd)
+    if dres is not None:
+        dres = _cpu(dres)
+    N = h.shape[-1]
+    M = h.numel() // N
+    dh = torch.empty(h.shape, dtype=dh_dtype or h.dtype)
+    dw = torch.empty((N,), dtype=dwb_dtype)
+    db = torch.empty((N,), dtype=dwb_dtype)
+    dw_abs = torch.empty((N,), dtype=torch.float64)
+    db_abs = torch.empty((N,), dtype=torch.float64)
+    _check(_load().oracle_add_layernorm_bwd(_ptr(dy), _ptr(dres), _ptr(h), _code(h), _ptr(w),
+                                            _code(w), _ptr(mean), _ptr(rstd), _code(mean),
+                                            _ptr(dh), _code(dh), _ptr(dw), _ptr(db), _code(dw),
+                                            _ptr(dw_abs), _ptr(db_abs), M, N),
+           "add_layernorm_bwd")
+    return dh, dw, db, dw_abs, db_abs

@@ -363,13 +363,15 @@ int oracle_add_layernorm_fwd(const void *x, const void *r, int in_dt, const void
     return oracle_layernorm_fwd(res, res_dt, w, b, w_dt, y, y_dt, mean, rstd, stat_dt, M, N, eps);
 }
 
-/* LayerNorm backward from the saved mean and rstd.  db may be NULL.  dw_abs
- * and db_abs (nullable, binary64) receive the per-column sums of |dy * xh|
- * and |dy|. */
-int oracle_layernorm_bwd(const void *dy, const void *x, int in_dt, const void *w, int w_dt,
-                         const void *mean, const void *rstd, int stat_dt, void *dx, int dx_dt,
-                         void *dw, void *db, int dwb_dt, double *dw_abs, double *db_abs,
-                         int64_t M, int64_t N)
+/* Backward of the fused Add + LayerNorm from the saved mean and rstd: as for
+ * RMSNorm, the gradient reaching the stored residual x (= h) is the
+ * LayerNorm backward of dy plus dres (NULL: zero), and it is the gradient of
+ * both inputs of the add.  db may be NULL.  dw_abs and db_abs (nullable,
+ * binary64) receive the per-column sums of |dy * xh| and |dy|. */
+int oracle_add_layernorm_bwd(const void *dy, const void *dres, const void *x, int in_dt,
+                             const void *w, int w_dt, const void *mean, const void *rstd,
+                             int stat_dt, void *dx, int dx_dt, void *dw, void *db, int dwb_dt,
+                             double *dw_abs, double *db_abs, int64_t M, int64_t N)
 {
     double *aw, *ab, *awa, *aba;
 
@@ -405,7 +407,8 @@ int oracle_layernorm_bwd(const void *dy, const void *x, int in_dt, const void *w
             double d = load_elem(dy, in_dt, i * N + j);
             double g = d * load_elem(w, w_dt, j);
             double xh = (load_elem(x, in_dt, i * N + j) - mu) * rs;
-            store_elem(dx, dx_dt, i * N + j, rs * (g - mg - xh * mgx));
+            double extra = dres ? load_elem(dres, in_dt, i * N + j) : 0.0;
+            store_elem(dx, dx_dt, i * N + j, rs * (g - mg - xh * mgx) + extra);
             aw[j] += d * xh;
             ab[j] += d;
             awa[j] += fabs(d * xh);
@@ -426,4 +429,14 @@ int oracle_layernorm_bwd(const void *dy, const void *x, int in_dt, const void *w
     free(awa);
     free(aba);
     return OR_OK;
+}
+
+/* LayerNorm backward: the fused op's backward with no residual gradient. */
+int oracle_layernorm_bwd(const void *dy, const void *x, int in_dt, const void *w, int w_dt,
+                         const void *mean, const void *rstd, int stat_dt, void *dx, int dx_dt,
+                         void *dw, void *db, int dwb_dt, double *dw_abs, double *db_abs,
+                         int64_t M, int64_t N)
+{
+    return oracle_add_layernorm_bwd(dy, NULL, x, in_dt, w, w_dt, mean, rstd, stat_dt, dx, dx_dt,
+                                    dw, db, dwb_dt, dw_abs, db_abs, M, N);
 }

@@ -49,7 +49,7 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd",
                                   "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
                                   "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
-                                  "layernorm_bwd_workspace_bytes",
+                                  "layernorm_bwd_workspace_bytes", "add_layernorm_bwd",
                                   "addrms_status_str", "addrms_last_hip_error"])
 
 

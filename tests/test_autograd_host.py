@@ -20,3 +20,15 @@ def test_fake_shapes():
         assert dx.shape == x.shape and dw.shape == (96,) and dw.dtype == torch.float32
         dh, dw = torch.ops.addrms.add_rms_norm_bwd(x, None, x, w, rstd)
         assert dh.shape == x.shape and dw.dtype == torch.float32
+
+
+def test_fake_shapes_layernorm():
+    with FakeTensorMode():
+        x = torch.empty(6, 128, dtype=torch.bfloat16)
+        w = torch.empty(128, dtype=torch.bfloat16)
+        y, mean, rstd = torch.ops.addrms.layer_norm_fwd(x, w, w, 1e-5)
+        assert y.shape == x.shape and mean.shape == (6,) and rstd.dtype == torch.float32
+        y, res, mean, rstd = torch.ops.addrms.add_layer_norm_fwd(x, x, w, None, 1e-5)
+        assert res.shape == x.shape and mean.shape == (6,)
+        dh, dw, db = torch.ops.addrms.add_layer_norm_bwd(x, None, x, w, mean, rstd)
+        assert dh.shape == x.shape and dw.shape == db.shape == (128,)

@@ -166,3 +166,55 @@ def test_backward_in_place_and_empty():
     ar.layernorm_bwd(e, e, w[:64].to(DEV), z, z, dw=dw0, db=db0)
     torch.cuda.synchronize()
     assert torch.all(dw0 == 0) and torch.all(db0 == 0)
+
+
+# ---- fused backward and autograd ------------------------------------------------
+
+@pytest.mark.parametrize("M,N,dtype", [(4096, 4096, torch.bfloat16), (333, 1000, torch.bfloat16),
+                                       (500, 2048, torch.float32)])
+def test_fused_backward(M, N, dtype):
+    inp = inputs(M, N, dtype, seed=29)
+    _, h, mean, rstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
+    dy = synth.store(synth.normal(29, "dy", (M, N)), dtype)
+    dres = synth.store(synth.normal(30, "dy", (M, N)), dtype)
+    g = lambda t: t.to(DEV)
+    dh, dw, db = ar.add_layernorm_bwd(g(dy), g(dres), g(h), g(inp["w"]), g(mean), g(rstd))
+    torch.cuda.synchronize()
+    rdh, rdw, rdb, mw, mb = oracle.add_layernorm_bwd(dy, dres, h, inp["w"], mean, rstd)
+    assert_close(dh.cpu(), rdh, "dh")
+    assert_dw_close(dw.cpu(), rdw, mw, "dw")
+    assert_dw_close(db.cpu(), rdb, mb, "db")
+
+
+def test_layer_norm_autograd():
+    import add_rmsnorm_amd.autograd as ag
+    M, N = 256, 2048
+    inp = inputs(M, N, torch.float32, seed=31)
+    gy = synth.store(synth.normal(31, "dy", (M, N)), torch.float32)
+    gres = synth.store(synth.normal(32, "dy", (M, N)), torch.float32)
+    x, r, w, b = (inp[k].to(DEV).requires_grad_(True) for k in ("x", "r", "w", "b"))
+    y, res = ag.add_layer_norm(x, r, w, b, EPS)
+    torch.autograd.backward([y, res], [gy.to(DEV), gres.to(DEV)])
+    torch.cuda.synchronize()
+    ry, rres, rmean, rrstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
+    assert_close(y.detach().cpu(), ry, "y")
+    rdh, rdw, rdb, mw, mb = oracle.add_layernorm_bwd(gy, gres, rres, inp["w"], rmean, rrstd)
+    assert_close(x.grad.cpu(), rdh, "x.grad")
+    assert_close(r.grad.cpu(), rdh, "r.grad")
+    assert_dw_close(w.grad.cpu(), rdw, mw, "w.grad")
+    assert_dw_close(b.grad.cpu(), rdb, mb, "b.grad")
+    # plain layer_norm and the modules
+    x2 = inp["x"].to(DEV).requires_grad_(True)
+    y2 = ag.layer_norm(x2, w.detach(), None, EPS)
+    y2.backward(gy.to(DEV))
+    _, m2, s2 = oracle.layernorm_fwd(inp["x"], inp["w"], None, EPS)
+    rdx, _, _, _, _ = oracle.layernorm_bwd(gy, inp["x"], inp["w"], m2, s2)
+    assert_close(x2.grad.cpu(), rdx, "x2.grad")
+    mod = ag.AddLayerNorm(N, dtype=torch.bfloat16, device=DEV)
+    xb = inp["x"].to(DEV, torch.bfloat16).requires_grad_(True)
+    yb, rb = mod(xb, torch.zeros_like(xb))
+    (yb.float().sum() + rb.float().sum()).backward()
+    assert mod.weight.grad is not None and mod.bias.grad is not None
+    torch.library.opcheck(torch.ops.addrms.add_layer_norm_fwd,
+                          (x.detach(), r.detach(), w.detach(), b.detach(), EPS))
+    torch.library.opcheck(torch.ops.addrms.layer_norm_fwd, (x.detach(), w.detach(), None, EPS))

@@ -49,6 +49,7 @@ MUTANTS = {
     "ln_bwd_no_projection": ("rs * (g - mg - xh * mgx)", "rs * (g - mg)"),
     "ln_db_weighted": ("ab[j] += d;", "ab[j] += g;"),
     "ln_dw_uncentred": ("aw[j] += d * xh;", "aw[j] += d * load_elem(x, in_dt, i * N + j) * rs;"),
+    "ln_fused_bwd_drops_dres": ("rs * (g - mg - xh * mgx) + extra);", "rs * (g - mg - xh * mgx));"),
     "bwd_dx_missing_outer_rstd": ("rs * (g - xh * c)", "(g - xh * c)"),
 }
 
