@@ -432,7 +432,10 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     const BwdTable &tab = bwd_table(combo(dtype, w_dtype));
     // LayerNorm: the workspace holds dw partials then db partials, pmax rows each
     const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u)) / (ln ? 2 : 1);
-    const int64_t pmax = ws_rows < kMaxPartials ? ws_rows : kMaxPartials;
+    // ADDRMS_MAX_PARTIALS raises the partial-row cap when the caller passes a
+    // larger workspace (tuning); the size function assumes the default cap.
+    const int64_t cap = env_int("ADDRMS_MAX_PARTIALS") > 0 ? env_int("ADDRMS_MAX_PARTIALS") : kMaxPartials;
+    const int64_t pmax = ws_rows < cap ? ws_rows : cap;
     float *ws = static_cast<float *>(workspace);
     BwdArgs a{dy, res ? dres : dy, x, w, mean, rstd, dx, ws, ln ? ws + (size_t)pmax * N : ws,
               M, (int)N, 0, 0, 0};

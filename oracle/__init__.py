@@ -76,6 +76,17 @@ def _load():
         lib.oracle_layernorm_bwd.restype = i32
         lib.oracle_layernorm_bwd.argtypes = [vp, vp, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp,
                                              i32, vp, vp, i64, i64]
+        lib.oracle_fp8e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_fp8e4m3_encode.argtypes = [dbl]
+        lib.oracle_fp8e4m3_decode.restype = dbl
+        lib.oracle_fp8e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8e4m3_encode_array.restype = None
+        lib.oracle_fp8e4m3_encode_array.argtypes = [vp, vp, i64]
+        lib.oracle_rmsnorm_fwd_fp8.restype = i32
+        lib.oracle_rmsnorm_fwd_fp8.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i64, i64, dbl]
+        lib.oracle_add_rmsnorm_fwd_fp8.restype = i32
+        lib.oracle_add_rmsnorm_fwd_fp8.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, i32, vp, i32,
+                                                   i64, i64, dbl]
         lib.oracle_add_rmsnorm_bwd.restype = i32
         lib.oracle_add_rmsnorm_bwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, vp, i32, vp,
                                                i32, vp, i64, i64]
@@ -282,3 +293,44 @@ def add_layernorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
                                             _ptr(dw_abs), _ptr(db_abs), M, N),
            "add_layernorm_bwd")
     return dh, dw, db, dw_abs, db_abs
+
+
+def fp8e4m3_encode(v) -> np.ndarray:
+    """binary64 values -> E4M3 codes (uint8): RNE, saturating to +-448."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint8)
+    _load().oracle_fp8e4m3_encode_array(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def fp8e4m3_decode(codes) -> np.ndarray:
+    """E4M3 codes -> exact binary64 values."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_fp8e4m3_decode(int(b)) for b in c.ravel()]).reshape(c.shape)
+
+
+def rmsnorm_fwd_fp8(x: torch.Tensor, w: torch.Tensor, eps: float, *, residual=None,
+                    eps_exact: bool = False):
+    """RMSNorm with an E4M3 output and per-row scale.  With residual=r, the
+    fused form: x + r is stored first and normalised.  Returns
+    (q uint8, scale float32, rstd float32) or, fused, (q, scale, residual_out, rstd)."""
+    x, w = _cpu(x), _cpu(w)
+    N = x.shape[-1]
+    M = x.numel() // N
+    q = torch.empty(x.shape, dtype=torch.uint8)
+    scale = torch.empty(x.shape[:-1], dtype=torch.float32)
+    rstd = torch.empty(x.shape[:-1], dtype=torch.float32)
+    e = float(eps) if eps_exact else eps_as_float32(eps)
+    if residual is None:
+        _check(_load().oracle_rmsnorm_fwd_fp8(_ptr(x), _code(x), _ptr(w), _code(w), _ptr(q),
+                                              _ptr(scale), _ptr(rstd), _code(rstd), M, N, e),
+               "rmsnorm_fwd_fp8")
+        return q, scale, rstd
+    r = _cpu(residual)
+    res = torch.empty(x.shape, dtype=x.dtype)
+    _check(_load().oracle_add_rmsnorm_fwd_fp8(_ptr(x), _ptr(r), _code(x), _ptr(w), _code(w),
+                                              _ptr(q), _ptr(scale), _ptr(res), _code(res),
+                                              _ptr(rstd), _code(rstd), M, N, e),
+           "add_rmsnorm_fwd_fp8")
+    return q, scale, res, rstd

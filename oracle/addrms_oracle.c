@@ -440,3 +440,139 @@ int oracle_layernorm_bwd(const void *dy, const void *x, int in_dt, const void *w
     return oracle_add_layernorm_bwd(dy, NULL, x, in_dt, w, w_dt, mean, rstd, stat_dt, dx, dx_dt,
                                     dw, db, dwb_dt, dw_abs, db_abs, M, N);
 }
+
+/* ---- FP8 (E4M3) output with a dynamic per-row scale ----------------------- */
+
+/* OCP 8-bit float E4M3 (the "FN" variant: sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, subnormals, no infinities, S.1111.111 is NaN; largest
+ * finite value 1.75 * 2^8 = 448).  Encoding from binary64: round to nearest,
+ * ties to even significand, on the E4M3 grid; saturating: finite values of
+ * magnitude >= 448 and infinities give +-448; NaN gives S.1111.111. */
+uint8_t oracle_fp8e4m3_encode(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80u : 0u;
+    double a, ulp, lo, hi, mid, q;
+    int e;
+
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7Fu);
+    a = fabs(v);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7Eu); /* 448 = 1.110b * 2^8 */
+    if (a < 0x1p-6) {
+        ulp = 0x1p-9; /* subnormal spacing: 2^-6 / 2^3 */
+    } else {
+        frexp(a, &e); /* a in [2^(e-1), 2^e) */
+        ulp = ldexp(1.0, e - 4);
+    }
+    lo = floor(a / ulp) * ulp;
+    hi = lo + ulp;
+    mid = lo + 0.5 * ulp;
+    if (a < mid)
+        q = lo;
+    else if (a > mid)
+        q = hi;
+    else
+        q = (fmod(lo / ulp, 2.0) == 0.0) ? lo : hi;
+
+    if (q == 0.0)
+        return sign;
+    if (q < 0x1p-6) /* subnormal: exponent field 0, mantissa q / 2^-9 */
+        return (uint8_t)(sign | (uint8_t)(q / 0x1p-9));
+    frexp(q, &e); /* q = 1.mmm * 2^(e-1) */
+    {
+        int exp_field = (e - 1) + 7;
+        int mant = (int)((ldexp(q, -(e - 1)) - 1.0) * 8.0);
+        return (uint8_t)(sign | (uint8_t)(exp_field << 3) | (uint8_t)mant);
+    }
+}
+
+/* E4M3 code -> exact binary64 value (NaN for S.1111.111). */
+double oracle_fp8e4m3_decode(uint8_t c)
+{
+    const double sgn = (c & 0x80u) ? -1.0 : 1.0;
+    const int ef = (c >> 3) & 0xF, m = c & 7;
+    if (ef == 0xF && m == 7)
+        return NAN;
+    if (ef == 0)
+        return sgn * ldexp((double)m, -9);
+    return sgn * ldexp(1.0 + m / 8.0, ef - 7);
+}
+
+void oracle_fp8e4m3_encode_array(const double *v, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_fp8e4m3_encode(v[i]);
+}
+
+/* RMSNorm with an E4M3 output and a dynamic per-row scale, for a downstream
+ * FP8 GEMM.  Per row: y_j = h_j * rstd * w_j in binary64, rounded once to
+ * binary32 (yf_j); amax = max_j |yf_j|; the quantisation decisions are then
+ * taken in binary32, as the kernel takes them:
+ *     inv = 448 / amax,  scale = amax / 448   (binary32 divisions)
+ *     q_j = E4M3(yf_j * inv)                  (binary32 product, encoded)
+ * with inv = scale = 1 for a row with no non-zero finite |yf| (NaNs are
+ * ignored by the maximum and encode as NaN).  y_j ~= decode(q_j) * scale. */
+int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
+                           float *scale, void *rstd, int rstd_dt, int64_t M, int64_t N, double eps)
+{
+    float *yf;
+
+    if (!x || !w || !q || !scale || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || (rstd && !dtype_ok(rstd_dt)))
+        return OR_ERR_ARG;
+    yf = (float *)malloc((size_t)N * sizeof(float));
+    if (!yf)
+        return OR_ERR_NOMEM;
+    for (int64_t i = 0; i < M; i++) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < N; j++) {
+            double h = load_elem(x, x_dt, i * N + j);
+            ss += h * h;
+        }
+        double rs = 1.0 / sqrt(ss / (double)N + eps);
+        if (rstd)
+            store_elem(rstd, rstd_dt, i, rs);
+        float amax = 0.0f;
+        for (int64_t j = 0; j < N; j++) {
+            double h = load_elem(x, x_dt, i * N + j);
+            yf[j] = (float)(h * rs * load_elem(w, w_dt, j));
+            float m = fabsf(yf[j]);
+            if (m > amax) /* NaN never compares greater: NaNs do not set the scale */
+                amax = m;
+        }
+        float inv = 1.0f, sc = 1.0f;
+        if (amax != 0.0f) {
+            inv = 448.0f / amax;
+            sc = amax / 448.0f;
+        }
+        scale[i] = sc;
+        for (int64_t j = 0; j < N; j++) {
+            float v = yf[j] * inv;
+            q[i * N + j] = oracle_fp8e4m3_encode((double)v);
+        }
+    }
+    free(yf);
+    return OR_OK;
+}
+
+/* Fused residual-Add + RMSNorm with the E4M3 output: the residual as in
+ * oracle_add_rmsnorm_fwd, then oracle_rmsnorm_fwd_fp8 of the stored residual. */
+int oracle_add_rmsnorm_fwd_fp8(const void *x, const void *r, int in_dt, const void *w, int w_dt,
+                               uint8_t *q, float *scale, void *res, int res_dt, void *rstd,
+                               int rstd_dt, int64_t M, int64_t N, double eps)
+{
+    if (!x || !r || !res || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
+        return OR_ERR_ARG;
+    for (int64_t k = 0; k < M * N; k++) {
+        float a32 = (float)load_elem(x, in_dt, k);
+        float b32 = (float)load_elem(r, in_dt, k);
+        float s32 = a32 + b32; /* binary32 add, as the fused op's residual */
+        store_elem(res, res_dt, k, in_dt == OR_F64 ? load_elem(x, in_dt, k) + load_elem(r, in_dt, k)
+                                                   : (double)s32);
+    }
+    return oracle_rmsnorm_fwd_fp8(res, res_dt, w, w_dt, q, scale, rstd, rstd_dt, M, N, eps);
+}

@@ -1,0 +1,125 @@
+"""Pins for the oracle's E4M3 encoding and the FP8-output RMSNorm (CPU only).
+
+The encoder is checked against torch's float32 -> float8_e4m3fn conversion
+(round-to-nearest-even) wherever torch does not overflow (|v| < 464), against
+a brute-force nearest-value search over the table of all finite E4M3 values
+in exact rational arithmetic (ties, subnormals, saturation), and by the
+round trip of every code.  The row quantisation is checked against the
+binary64 RMSNorm (torch-pinned elsewhere): the largest element encodes as
++-448, every value is recovered within half an E4M3 step times the scale, and
+the special rows (zero, NaN) follow the stated rules."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+
+def _table():
+    """All non-negative finite E4M3 values, indexed by code 0x00..0x7E."""
+    return np.array([oracle.fp8e4m3_decode([c])[0] for c in range(0x7F)])
+
+
+def _brute(v: float, table: np.ndarray) -> int:
+    if np.isnan(v):
+        return -1
+    sign = 0x80 if np.signbit(v) else 0
+    a = abs(v)
+    if a >= 448:
+        return sign | 0x7E
+    k = int(np.searchsorted(table, a, side="right")) - 1
+    if table[k] == a:
+        return sign | k
+    lo, hi, A = Fraction(table[k]), Fraction(table[k + 1]), Fraction(a)
+    if A - lo < hi - A:
+        return sign | k
+    if hi - A < A - lo:
+        return sign | (k + 1)
+    return sign | (k if k % 2 == 0 else k + 1)
+
+
+def test_table_is_monotone_and_spans_the_format():
+    t = _table()
+    assert t[0] == 0 and t[1] == 2.0 ** -9 and t[8] == 2.0 ** -6 and t[-1] == 448.0
+    assert np.all(np.diff(t) > 0)
+
+
+def test_matches_torch_float8_e4m3fn_where_torch_is_in_range():
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = [0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234, 0xABCD]
+    f = np.concatenate([hi | np.uint32(lo) for lo in lows]).view(np.float32)
+    with np.errstate(invalid="ignore"):
+        keep = np.isnan(f) | (np.abs(f) < 464.0)
+    f = f[keep]
+    ours = oracle.fp8e4m3_encode(f.astype(np.float64))
+    ref = torch.from_numpy(f.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nan = np.isnan(f)
+    assert np.all((ours[nan] & 0x7F) == 0x7F)
+    bad = np.nonzero(ours[~nan] != ref[~nan])[0]
+    assert bad.size == 0, f"{bad.size} mismatches, e.g. {f[~nan][bad[:5]]}"
+
+
+def test_brute_force_grid_search():
+    t = _table()
+    rng = np.random.default_rng(123)
+    vals = list(np.sign(rng.standard_normal(4000)) * np.exp2(rng.uniform(-12, 10, 4000)))
+    k = rng.integers(0, t.size - 1, 500)
+    mids = (t[k] + t[k + 1]) / 2
+    vals += list(mids) + list(np.nextafter(mids, 0)) + list(np.nextafter(mids, np.inf))
+    vals += [0.0, -0.0, 448.0, 447.9, 464.0, 500.0, 1e30, -np.inf, np.inf, 2.0 ** -10,
+             2.0 ** -11, 3 * 2.0 ** -11, 2.0 ** -6, np.nextafter(2.0 ** -6, 0)]
+    vals = np.array(vals)
+    ours = oracle.fp8e4m3_encode(vals)
+    for v, o in zip(vals, ours):
+        assert int(o) == _brute(float(v), t), f"v={v!r}: got {int(o):#04x}"
+
+
+def test_round_trip_of_every_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.fp8e4m3_decode(codes)
+    back = oracle.fp8e4m3_encode(vals)
+    assert np.array_equal(back, codes)
+    assert all(np.isnan(oracle.fp8e4m3_decode([0x7F, 0xFF])))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_row_quantisation(fused):
+    M, N = 64, 1000
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=201)
+    x, r, w = inp["x"], inp["r"], inp["w"]
+    if fused:
+        q, scale, res, rstd = oracle.rmsnorm_fwd_fp8(x, w, 1e-6, residual=r)
+        _, res_ref, _ = oracle.add_rmsnorm_fwd(x, r, w, 1e-6)
+        assert torch.equal(res.view(torch.int16), res_ref.view(torch.int16))
+        y64, _ = oracle.rmsnorm_fwd(res, w, 1e-6, y_dtype=torch.float64)
+    else:
+        q, scale, rstd = oracle.rmsnorm_fwd_fp8(x, w, 1e-6)
+        y64, _ = oracle.rmsnorm_fwd(x, w, 1e-6, y_dtype=torch.float64)
+    y = y64.numpy()
+    qn = q.numpy()
+    s = scale.numpy().astype(np.float64)
+    amax = np.abs(y).max(axis=1)
+    np.testing.assert_allclose(s * 448.0, amax, rtol=1e-6)
+    arg = np.abs(y).argmax(axis=1)
+    assert np.all((qn[np.arange(M), arg] & 0x7F) == 0x7E)
+    deq = oracle.fp8e4m3_decode(qn) * s[:, None]
+    # half an E4M3 step at the value's magnitude (3 mantissa bits), or half the
+    # subnormal step, times the scale, plus float32 slack
+    mag = np.abs(y) / s[:, None]
+    step = np.where(mag < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-30))) - 3))
+    assert np.all(np.abs(deq - y) <= (0.5 * step * (1 + 1e-6) + 1e-6 * mag) * s[:, None])
+
+
+def test_special_rows():
+    N = 32
+    w = torch.ones(N, dtype=torch.bfloat16)
+    x = torch.zeros(3, N, dtype=torch.bfloat16)
+    x[1, 5] = float("nan")
+    x[2] = 1.0
+    q, scale, _ = oracle.rmsnorm_fwd_fp8(x, w, 1e-6)
+    assert scale[0].item() == 1.0 and torch.all(q[0] == 0)
+    assert scale[1].item() == 1.0 and torch.all((q[1] & 0x7F) == 0x7F)   # NaN row
+    assert torch.all(q[2] == 0x7E)                                       # constant row: all amax

@@ -15,7 +15,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "addrms_oracle.c")
 PINS = ["tests/test_oracle_bf16.py", "tests/test_oracle_fwd.py", "tests/test_oracle_bwd.py",
-        "tests/test_oracle_layernorm.py"]
+        "tests/test_oracle_layernorm.py", "tests/test_oracle_fp8.py"]
 
 MUTANTS = {
     "eps_outside_root": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms) + eps"),
@@ -60,8 +60,17 @@ MUTANTS.update({
                                 "double g = load_elem(dy, in_dt, i * N + j);", 1, 2),
     "ln_bwd_dx_without_weight": ("double g = d * load_elem(w, w_dt, j);", "double g = d;", 1, 2),
 })
-for _k in ("bwd_g_without_weight", "bwd_dx_without_weight"):
+for _k in ("bwd_g_without_weight", "bwd_dx_without_weight", "ties_away_from_zero"):
     MUTANTS[_k] = MUTANTS[_k] + (0, 2)
+MUTANTS.update({
+    "fp8_ties_up": ("(fmod(lo / ulp, 2.0) == 0.0) ? lo : hi", "hi", 1, 2),
+    "fp8_subnormal_spacing": ("ulp = 0x1p-9;", "ulp = 0x1p-10;"),
+    "fp8_ulp_exponent": ("ulp = ldexp(1.0, e - 4);", "ulp = ldexp(1.0, e - 5);"),
+    "fp8_exponent_bias": ("int exp_field = (e - 1) + 7;", "int exp_field = (e - 1) + 8;"),
+    "fp8_no_saturation": ("return (uint8_t)(sign | 0x7Eu); /* 448", "return (uint8_t)(sign | 0x7Fu); /* 448"),
+    "fp8_scale_inverted": ("sc = amax / 448.0f;", "sc = 448.0f / amax;"),
+    "fp8_quantises_unscaled": ("float v = yf[j] * inv;", "float v = yf[j];"),
+})
 
 
 def _plant(src: str, spec) -> str:
