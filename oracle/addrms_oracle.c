@@ -513,31 +513,33 @@ void oracle_fp8e4m3_encode_array(const double *v, uint8_t *out, int64_t n)
  *     q_j = E4M3(yf_j * inv)                  (binary32 product, encoded)
  * with inv = scale = 1 for a row with no non-zero finite |yf| (NaNs are
  * ignored by the maximum and encode as NaN).  y_j ~= decode(q_j) * scale. */
+static size_t elem_size(int dt) { return dt == OR_F32 ? 4 : dt == OR_BF16 ? 2 : 8; }
+
 int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
                            float *scale, void *rstd, int rstd_dt, int64_t M, int64_t N, double eps)
 {
+    double *y;
     float *yf;
 
     if (!x || !w || !q || !scale || M < 0 || N <= 0)
         return OR_ERR_ARG;
     if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || (rstd && !dtype_ok(rstd_dt)))
         return OR_ERR_ARG;
+    y = (double *)malloc((size_t)N * sizeof(double));
     yf = (float *)malloc((size_t)N * sizeof(float));
-    if (!yf)
+    if (!y || !yf) {
+        free(y);
+        free(yf);
         return OR_ERR_NOMEM;
+    }
     for (int64_t i = 0; i < M; i++) {
-        double ss = 0.0;
-        for (int64_t j = 0; j < N; j++) {
-            double h = load_elem(x, x_dt, i * N + j);
-            ss += h * h;
-        }
-        double rs = 1.0 / sqrt(ss / (double)N + eps);
-        if (rstd)
-            store_elem(rstd, rstd_dt, i, rs);
+        /* the row's RMSNorm in binary64, by the forward above */
+        const void *xi = (const char *)x + (size_t)(i * N) * elem_size(x_dt);
+        void *ri = rstd ? (void *)((char *)rstd + (size_t)i * elem_size(rstd_dt)) : NULL;
+        oracle_rmsnorm_fwd(xi, x_dt, w, w_dt, y, OR_F64, ri, rstd_dt, 1, N, eps);
         float amax = 0.0f;
         for (int64_t j = 0; j < N; j++) {
-            double h = load_elem(x, x_dt, i * N + j);
-            yf[j] = (float)(h * rs * load_elem(w, w_dt, j));
+            yf[j] = (float)y[j];
             float m = fabsf(yf[j]);
             if (m > amax) /* NaN never compares greater: NaNs do not set the scale */
                 amax = m;
@@ -553,6 +555,7 @@ int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uin
             q[i * N + j] = oracle_fp8e4m3_encode((double)v);
         }
     }
+    free(y);
     free(yf);
     return OR_OK;
 }

@@ -60,10 +60,12 @@ MUTANTS.update({
                                 "double g = load_elem(dy, in_dt, i * N + j);", 1, 2),
     "ln_bwd_dx_without_weight": ("double g = d * load_elem(w, w_dt, j);", "double g = d;", 1, 2),
 })
-for _k in ("bwd_g_without_weight", "bwd_dx_without_weight", "ties_away_from_zero"):
+for _k in ("bwd_g_without_weight", "bwd_dx_without_weight", "ties_away_from_zero",
+           "truncating_round"):
     MUTANTS[_k] = MUTANTS[_k] + (0, 2)
 MUTANTS.update({
     "fp8_ties_up": ("(fmod(lo / ulp, 2.0) == 0.0) ? lo : hi", "hi", 1, 2),
+    "fp8_truncating_round": ("if (a < mid)", "if (a < hi)", 1, 2),
     "fp8_subnormal_spacing": ("ulp = 0x1p-9;", "ulp = 0x1p-10;"),
     "fp8_ulp_exponent": ("ulp = ldexp(1.0, e - 4);", "ulp = ldexp(1.0, e - 5);"),
     "fp8_exponent_bias": ("int exp_field = (e - 1) + 7;", "int exp_field = (e - 1) + 8;"),
