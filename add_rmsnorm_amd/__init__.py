@@ -15,6 +15,8 @@ Operations (same names as the C ABI):
     add_layernorm_fwd(x, r, w, b, eps) -> y, residual_out (and mean, rstd)
     layernorm_bwd(dy, x, w, mean, rstd) -> dx, dw, db
     add_layernorm_bwd(dy, dres, h, w, mean, rstd) -> dh, dw, db
+    rmsnorm_fwd_fp8(x, w, eps)        -> y_fp8 (float8_e4m3fn), per-row scale
+    add_rmsnorm_fwd_fp8(x, r, w, eps) -> y_fp8, scale, residual_out
 """
 from __future__ import annotations
 
@@ -25,7 +27,8 @@ import torch
 
 __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_bwd",
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
-           "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "AddRmsError", "LIB_PATH", "lib"]
+           "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "rmsnorm_fwd_fp8",
+           "add_rmsnorm_fwd_fp8", "AddRmsError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -58,6 +61,10 @@ def _load():
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.add_rmsnorm_bwd.restype = i32
     lib.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.rmsnorm_fwd_fp8.restype = i32
+    lib.rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd_fp8.restype = i32
+    lib.add_rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.layernorm_fwd.restype = i32
     lib.layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.add_layernorm_fwd.restype = i32
@@ -398,3 +405,64 @@ def add_layernorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
     if st != 0:
         raise AddRmsError(st, "add_layernorm_bwd")
     return dh, dw, db
+
+
+_FP8 = getattr(torch, "float8_e4m3fn", None)
+
+
+def _fp8_out(x, y_fp8, y_scale):
+    if y_fp8 is None:
+        y_fp8 = torch.empty(x.shape, dtype=_FP8 if _FP8 is not None else torch.uint8,
+                            device=x.device)
+    else:
+        _dev(y_fp8, "y_fp8", shape=x.shape)
+        if y_fp8.element_size() != 1:
+            raise TypeError("y_fp8 must have 1-byte elements (float8_e4m3fn or uint8)")
+    if y_scale is None:
+        y_scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    else:
+        _dev(y_scale, "y_scale", torch.float32, x.shape[:-1])
+    return y_fp8, y_scale
+
+
+def rmsnorm_fwd_fp8(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, y_fp8=None,
+                    y_scale=None, rstd=None):
+    """RMSNorm with an OCP E4M3 output (torch.float8_e4m3fn) and a dynamic
+    per-row float32 scale: y ~= y_fp8.float() * y_scale[..., None].
+    Returns (y_fp8, y_scale)."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(w, "w", shape=(N,))
+    y_fp8, y_scale = _fp8_out(x, y_fp8, y_scale)
+    if rstd is not None:
+        _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.rmsnorm_fwd_fp8(_p(x), _p(w), _p(y_fp8), _p(y_scale), _p(rstd), M, N,
+                                  float(eps), _code(x, "x"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "rmsnorm_fwd_fp8")
+    return y_fp8, y_scale
+
+
+def add_rmsnorm_fwd_fp8(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                        *, y_fp8=None, y_scale=None, residual_out=None, rstd=None):
+    """Fused residual add + RMSNorm with an E4M3 output and per-row scale.
+    Returns (y_fp8, y_scale, residual_out)."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(r, "r", x.dtype, x.shape)
+    _dev(w, "w", shape=(N,))
+    y_fp8, y_scale = _fp8_out(x, y_fp8, y_scale)
+    residual_out = (torch.empty_like(x) if residual_out is None
+                    else _dev(residual_out, "residual_out", x.dtype, x.shape))
+    if rstd is not None:
+        _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.add_rmsnorm_fwd_fp8(_p(x), _p(r), _p(w), _p(y_fp8), _p(y_scale),
+                                      _p(residual_out), _p(rstd), M, N, float(eps),
+                                      _code(x, "x"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "add_rmsnorm_fwd_fp8")
+    return y_fp8, y_scale, residual_out

@@ -302,11 +302,15 @@ int colreduce(const void *workspace, int P, int N, float *dw, hipStream_t s)
 
 int fwd_common(int norm, const void *x, const void *r, const void *w, const void *b, void *y,
                void *res, float *mean, float *rstd, int64_t M, int64_t N, float eps, int dtype,
-               int w_dtype, void *stream, bool fused)
+               int w_dtype, void *stream, bool fused, uint8_t *q = nullptr, float *qscale = nullptr)
 {
     // ---- validation (no HIP call) ----
-    // With M == 0 the matrices are empty and may be NULL.
-    if (!w || (M != 0 && (!x || !y || (fused && (!r || !res)))))
+    // With M == 0 the matrices are empty and may be NULL.  The FP8 variant
+    // writes q and qscale in place of y.
+    const bool q8 = q != nullptr || qscale != nullptr;
+    if (q8)
+        y = q; // the output matrix, for the checks below (1 byte per element)
+    if (!w || (M != 0 && (!x || !y || (fused && (!r || !res)) || (q8 && (!q || !qscale)))))
         return ADDRMS_ERR_NULL;
     if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
         return ADDRMS_ERR_DTYPE;
@@ -316,7 +320,9 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     if (!(eps >= 0.0f) || !std::isfinite(eps))
         return ADDRMS_ERR_EPS;
     const size_t mat = (size_t)M * (size_t)N * esize(dtype);
-    const Span sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype)), sy = span(y, mat);
+    const Span sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype));
+    const Span sy = span(y, q8 ? (size_t)M * (size_t)N : mat);
+    const Span sqs = q8 ? span(qscale, (size_t)M * 4u) : Span{};
     const Span sr = fused ? span(r, mat) : Span{}, sres = fused ? span(res, mat) : Span{};
     const Span srs = rstd ? span(rstd, (size_t)M * 4u) : Span{};
     const Span sb = b ? span(b, (size_t)N * esize(w_dtype)) : Span{};
@@ -332,6 +338,11 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
         return ADDRMS_ERR_ALIAS;
     if (rstd && bad_alias(srs, sb, false))
         return ADDRMS_ERR_ALIAS;
+    if (q8 && (bad_alias(sy, sx, false) || (fused && bad_alias(sy, sr, false)) ||
+               bad_alias(sqs, sx, false) || bad_alias(sqs, sw, false) || bad_alias(sqs, sy, false) ||
+               bad_alias(sqs, srs, false) || (fused && (bad_alias(sqs, sr, false) ||
+                                                        bad_alias(sqs, sres, false)))))
+        return ADDRMS_ERR_ALIAS;
     if (fused && (bad_alias(sy, sr, true) || bad_alias(sres, sx, true) ||
                   bad_alias(sres, sr, true) || bad_alias(sres, sw, false) ||
                   bad_alias(sres, srs, false) || bad_alias(sres, sy, false)))
@@ -346,11 +357,12 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int c = combo(dtype, w_dtype);
     const FwdTable &tab = fwd_table(c);
-    FwdArgs a{x, fused ? r : x, w, b, y, fused ? res : y, mean, rstd, M, (int)N, 0, eps};
+    FwdArgs a{x, fused ? r : x, w, b, y, fused ? res : y, mean, rstd, q, qscale, M, (int)N, 0, eps};
 
     const int nv = vec_elems(dtype);
+    const bool y_ok = q8 ? (reinterpret_cast<uintptr_t>(q) % (uintptr_t)nv) == 0 : aligned16(y);
     const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(x) &&
-                        aligned16(w) && aligned16(y) && (!b || aligned16(b)) &&
+                        aligned16(w) && y_ok && (!b || aligned16(b)) &&
                         (!fused || (aligned16(r) && aligned16(res)));
     int cus = 0;
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
@@ -358,7 +370,7 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     int wi = 0, vi = 0;
     if (vec_ok && pick_fwd(M, (int)(N / nv), cus, &wi, &vi)) {
         a.nvec = (int)(N / nv);
-        const KernelRef &k = tab.vec[norm][fused ? 1 : 0][wi][vi];
+        const KernelRef &k = q8 ? tab.vec_q8[fused ? 1 : 0][wi][vi] : tab.vec[norm][fused ? 1 : 0][wi][vi];
         const int rpb = kWprList[wi] == 1 ? 4 : 1;
         const int64_t blocks = (M + rpb - 1) / rpb;
         // One block per row group (the hardware dispatcher balances the
@@ -369,7 +381,7 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
             return rc;
         return launch(k, dim3(grid), 0, &a, s);
     }
-    const KernelRef &k = tab.elem[norm][fused ? 1 : 0];
+    const KernelRef &k = q8 ? tab.elem_q8[fused ? 1 : 0] : tab.elem[norm][fused ? 1 : 0];
     int grid = 0;
     if ((rc = persistent_grid(k, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
         return rc;
@@ -502,6 +514,25 @@ int add_rmsnorm_fwd(const void *x, const void *r, const void *w, void *y, void *
 {
     return fwd_common(kRms, x, r, w, nullptr, y, residual_out, nullptr, rstd, M, N, eps, dtype,
                       w_dtype, stream, true);
+}
+
+int rmsnorm_fwd_fp8(const void *x, const void *w, void *y_fp8, float *y_scale, float *rstd,
+                    int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream)
+{
+    if (M != 0 && (!y_fp8 || !y_scale))
+        return ADDRMS_ERR_NULL;
+    return fwd_common(kRms, x, nullptr, w, nullptr, nullptr, nullptr, nullptr, rstd, M, N, eps,
+                      dtype, w_dtype, stream, false, static_cast<uint8_t *>(y_fp8), y_scale);
+}
+
+int add_rmsnorm_fwd_fp8(const void *x, const void *r, const void *w, void *y_fp8, float *y_scale,
+                        void *residual_out, float *rstd, int64_t M, int64_t N, float eps,
+                        int dtype, int w_dtype, void *stream)
+{
+    if (M != 0 && (!y_fp8 || !y_scale))
+        return ADDRMS_ERR_NULL;
+    return fwd_common(kRms, x, r, w, nullptr, nullptr, residual_out, nullptr, rstd, M, N, eps,
+                      dtype, w_dtype, stream, true, static_cast<uint8_t *>(y_fp8), y_scale);
 }
 
 int layernorm_fwd(const void *x, const void *w, const void *b, void *y, float *mean, float *rstd,

@@ -186,6 +186,63 @@ __device__ __forceinline__ float wave_sum(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
+// Maximum over the 64 lanes of a wave (same DPP pattern as wave_sum), result
+// in every lane.  v_max_f32 follows IEEE maxNum: a NaN operand is ignored.
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = __builtin_fmaxf(v, ADDRMS_DPP(v, 0xB1));
+    v = __builtin_fmaxf(v, ADDRMS_DPP(v, 0x4E));
+    v = __builtin_fmaxf(v, ADDRMS_DPP(v, 0x141));
+    v = __builtin_fmaxf(v, ADDRMS_DPP(v, 0x140));
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
+}
+
+// ---- FP8 (OCP E4M3) -----------------------------------------------------------
+
+// Clamp to the E4M3 range [-448, 448], keeping NaN (comparisons with NaN are
+// false, so NaN passes through unchanged).
+__device__ __forceinline__ float e4m3_clamp(float v)
+{
+    return v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);
+}
+
+#ifndef ADDRMS_FP8_SOFTWARE
+#define ADDRMS_FP8_SOFTWARE 0
+#endif
+
+// Two floats already in [-448, 448] (or NaN) -> two E4M3 codes in the low 16
+// bits (a in the low byte).  Hardware: v_cvt_pk_fp8_f32, gfx950's converter to
+// the OCP E4M3 format, round-to-nearest-even.  Software (the alternative,
+// written from the format): RNE on the binary32 bit pattern for normals,
+// rint(v * 2^9) on the subnormal grid.
+__device__ __forceinline__ uint32_t e4m3_sw(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return sign | 0x7Fu;
+    const float av = __uint_as_float(a);
+    if (av < 0x1p-6f)
+        return sign | (uint32_t)__builtin_rintf(av * 512.0f); // m * 2^-9, m <= 8
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) & 0xFFF00000u; // keep 3 mantissa bits
+    return sign | ((((r >> 23) - 127u + 7u) & 0xFu) << 3) | ((r >> 20) & 7u);
+}
+
+__device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b)
+{
+#if ADDRMS_FP8_SOFTWARE
+    return e4m3_sw(a) | (e4m3_sw(b) << 8);
+#else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+#endif
+}
+
 // The same sum for doubles (each DPP step moves both 32-bit halves).
 template <int CTRL> __device__ __forceinline__ double dpp_f64(double v)
 {

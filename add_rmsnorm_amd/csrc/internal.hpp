@@ -18,6 +18,8 @@ struct FwdArgs {
     void *res;
     float *mean; // LayerNorm only; may be null
     float *rstd; // may be null
+    uint8_t *q;     // FP8 output variant: E4M3 codes [M, N]
+    float *qscale;  // FP8 output variant: per-row scale [M]
     int64_t M;
     int N;
     int nvec; // 16-byte vectors per row (vector path)
@@ -85,6 +87,9 @@ inline int combo(int dtype, int w_dtype) { return dtype * 2 + w_dtype; }
 struct FwdTable {
     KernelRef vec[2][2][kNumWpr][kNumVpl];
     KernelRef elem[2][2];
+    // RMSNorm with an E4M3 output and per-row scale: [fused][wpr][vpl], [fused]
+    KernelRef vec_q8[2][kNumWpr][kNumVpl];
+    KernelRef elem_q8[2];
 };
 // bwd vec: [norm][with residual gradient][wpr_idx][vpl_idx]; elem_dx:
 // [norm][with residual gradient]; elem_dw: [norm].

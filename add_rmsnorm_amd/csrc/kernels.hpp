@@ -67,8 +67,11 @@ __device__ __forceinline__ double fma_ct(double a, double b, double c) { return 
 // NORM = kLayer: y = (h - mean) * rstd * w (+ b), rstd = 1/sqrt(var + eps),
 // the variance taken about the mean from the registers (two passes over the
 // row, one over memory).
+// Q8 (RMSNorm only): y is not stored; instead its row absmax sets a per-row
+// scale (scale = amax/448, inv = 448/amax, binary32) and y * inv is written as
+// OCP E4M3 codes, one byte per element, for a downstream FP8 GEMM.
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, int NORM, bool FUSED, int WPR, int VPL>
+template <typename T, typename WT, int NORM, bool FUSED, bool Q8, int WPR, int VPL>
 __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
@@ -82,9 +85,9 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
     const int nvec = a.nvec;
     const float inv_n = 1.0f / (float)a.N;
 
-    // Sum of one value per lane over the row's WPR waves.  Each sum of a row
-    // has its own LDS slot; a slot is reused two rows later, after at least
-    // two barriers, so one barrier per sum suffices.
+    // Sum (or max) of one value per lane over the row's WPR waves.  Each
+    // reduction of a row has its own LDS slot; a slot is reused two rows later,
+    // after at least two barriers, so one barrier per reduction suffices.
     __shared__ float part[4][16];
     auto row_sum = [&](float v, int slot) -> float {
         float t = wave_sum(v);
@@ -96,6 +99,19 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 #pragma unroll
             for (int i = 0; i < WPR; ++i)
                 t += part[slot][i];
+        }
+        return t;
+    };
+    auto row_max = [&](float v, int slot) -> float {
+        float t = wave_max(v);
+        if constexpr (WPR > 1) {
+            if (lane == 0)
+                part[slot][wir] = t;
+            __syncthreads();
+            t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i)
+                t = __builtin_fmaxf(t, part[slot][i]);
         }
         return t;
     };
@@ -180,6 +196,51 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
         if (a.rstd != nullptr && wir == 0 && lane == 0)
             a.rstd[row] = rs;
 
+        if constexpr (Q8) {
+            // 4'. y in registers, row absmax, scale, E4M3 codes
+            float o[VPL][NV];
+            float am = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int v = vbase + k * VSTRIDE;
+                float h[NV], wf[NV];
+                unpack<T>(hv[k], h);
+                if (v < nvec)
+                    load_w<T, WT>(a.w, v, wf);
+#pragma unroll
+                for (int e = 0; e < NV; ++e) {
+                    o[k][e] = v < nvec ? (h[e] * rs) * wf[e] : 0.0f;
+                    am = __builtin_fmaxf(am, __builtin_fabsf(o[k][e]));
+                }
+            }
+            am = row_max(am, slot + 1);
+            float inv = 1.0f, sc = 1.0f;
+            if (am != 0.0f) {
+                inv = 448.0f / am;
+                sc = am / 448.0f;
+            }
+            if (wir == 0 && lane == 0)
+                a.qscale[row] = sc;
+            uint8_t *qrow = a.q + base;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int v = vbase + k * VSTRIDE;
+                if (v < nvec) {
+                    uint32_t wd[NV / 4];
+#pragma unroll
+                    for (int i = 0; i < NV / 4; ++i)
+                        wd[i] = pack_e4m3x2(e4m3_clamp(o[k][4 * i] * inv), e4m3_clamp(o[k][4 * i + 1] * inv)) |
+                                (pack_e4m3x2(e4m3_clamp(o[k][4 * i + 2] * inv), e4m3_clamp(o[k][4 * i + 3] * inv)) << 16);
+                    if constexpr (NV == 8)
+                        __builtin_nontemporal_store(u32x2{wd[0], wd[1]},
+                                                    reinterpret_cast<u32x2 *>(qrow + (size_t)v * 8));
+                    else
+                        __builtin_nontemporal_store(wd[0], reinterpret_cast<uint32_t *>(qrow + (size_t)v * 4));
+                }
+            }
+            continue;
+        }
+
         // 4. y = (h - mean) * rstd * w (+ b), rounded once to T
         const bool bias = NORM == kLayer && a.b != nullptr;
 #pragma unroll
@@ -225,7 +286,21 @@ __device__ __forceinline__ S block256_sum(S v, S (&part)[NS][4], int slot)
 // the LayerNorm variance, and the output.  The fused op re-reads the stored
 // residual.
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, int NORM, bool FUSED>
+// Block-wide maximum, as block256_sum (IEEE maxNum: NaNs ignored).
+template <int NS>
+__device__ __forceinline__ float block256_max(float v, float (&part)[NS][4], int slot)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    float t = wave_max(v);
+    if (lane == 0)
+        part[slot][wave] = t;
+    __syncthreads();
+    return __builtin_fmaxf(__builtin_fmaxf(part[slot][0], part[slot][1]),
+                           __builtin_fmaxf(part[slot][2], part[slot][3]));
+}
+
+template <typename T, typename WT, int NORM, bool FUSED, bool Q8>
 __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 {
     __shared__ float part[4][4];
@@ -265,6 +340,25 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
         }
         if (a.rstd != nullptr && tid == 0)
             a.rstd[row] = rs;
+        if constexpr (Q8) {
+            float am = 0.0f;
+            for (int j = tid; j < N; j += 256)
+                am = __builtin_fmaxf(am, __builtin_fabsf((ld_elem<T>(src, base + j) * rs) *
+                                                         ld_elem<WT>(a.w, j)));
+            am = block256_max(am, part, slot + 1);
+            float inv = 1.0f, sc = 1.0f;
+            if (am != 0.0f) {
+                inv = 448.0f / am;
+                sc = am / 448.0f;
+            }
+            if (tid == 0)
+                a.qscale[row] = sc;
+            for (int j = tid; j < N; j += 256) {
+                const float o = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
+                a.q[base + j] = (uint8_t)pack_e4m3x2(e4m3_clamp(o * inv), 0.0f);
+            }
+            continue;
+        }
         const bool bias = NORM == kLayer && a.b != nullptr;
         for (int j = tid; j < N; j += 256) {
             const float h = ld_elem<T>(src, base + j);
@@ -656,37 +750,45 @@ __global__ void __launch_bounds__(256) dw_colreduce_kernel(const float *ws, int 
 // Kernel tables for one (row dtype, weight dtype) combination.
 // ---------------------------------------------------------------------------
 template <typename T, typename WT> struct TableBuilder {
-    template <int NM, bool F, int WPR, int VPL> static KernelRef fwd_ref()
+    template <int NM, bool F, bool Q8, int WPR, int VPL> static KernelRef fwd_ref()
     {
         if constexpr (fwd_built(WPR, VPL))
-            return KernelRef{reinterpret_cast<const void *>(&fwd_vec_kernel<T, WT, NM, F, WPR, VPL>),
-                             kBlockFwd(WPR)};
+            return KernelRef{
+                reinterpret_cast<const void *>(&fwd_vec_kernel<T, WT, NM, F, Q8, WPR, VPL>),
+                kBlockFwd(WPR)};
         else
             return KernelRef{nullptr, 0};
     }
-    template <int NM, bool F, int WI, int... VI>
+    template <int NM, bool F, bool Q8, int WI, int... VI>
     static void fwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
     {
-        ((row[VI] = fwd_ref<NM, F, kWprList[WI], kVplList[VI]>()), ...);
+        ((row[VI] = fwd_ref<NM, F, Q8, kWprList[WI], kVplList[VI]>()), ...);
     }
-    template <int NM, bool F, int... WI>
-    static void fwd_all(FwdTable &t, std::integer_sequence<int, WI...>)
+    template <int NM, bool F, bool Q8, int... WI>
+    static void fwd_all(KernelRef (&tab)[kNumWpr][kNumVpl], std::integer_sequence<int, WI...>)
     {
-        (fwd_row<NM, F, WI>(t.vec[NM][F ? 1 : 0][WI], std::make_integer_sequence<int, kNumVpl>{}),
-         ...);
+        (fwd_row<NM, F, Q8, WI>(tab[WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
     }
     template <int NM> static void fwd_norm(FwdTable &t)
     {
-        fwd_all<NM, false>(t, std::make_integer_sequence<int, kNumWpr>{});
-        fwd_all<NM, true>(t, std::make_integer_sequence<int, kNumWpr>{});
-        t.elem[NM][0] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, false>), 256};
-        t.elem[NM][1] = KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, true>), 256};
+        fwd_all<NM, false, false>(t.vec[NM][0], std::make_integer_sequence<int, kNumWpr>{});
+        fwd_all<NM, true, false>(t.vec[NM][1], std::make_integer_sequence<int, kNumWpr>{});
+        t.elem[NM][0] =
+            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, false, false>), 256};
+        t.elem[NM][1] =
+            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, true, false>), 256};
     }
     static FwdTable fwd()
     {
         FwdTable t{};
         fwd_norm<kRms>(t);
         fwd_norm<kLayer>(t);
+        fwd_all<kRms, false, true>(t.vec_q8[0], std::make_integer_sequence<int, kNumWpr>{});
+        fwd_all<kRms, true, true>(t.vec_q8[1], std::make_integer_sequence<int, kNumWpr>{});
+        t.elem_q8[0] =
+            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, kRms, false, true>), 256};
+        t.elem_q8[1] =
+            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, kRms, true, true>), 256};
         return t;
     }
 

@@ -147,6 +147,30 @@ int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void 
                     void *stream);
 
 /*
+ * RMSNorm / fused Add + RMSNorm with an FP8 output for a downstream FP8 GEMM
+ * (the norm followed by the quantised epilogue; the "Machete" README's
+ * "Built-In Areas" lists MXFP4 decode kernels, i.e. low-precision
+ * activations after the norm).  y is computed as in rmsnorm_fwd /
+ * add_rmsnorm_fwd in float32 but not stored; per row:
+ *     amax_i  = max_j |y_ij|        (NaNs ignored)
+ *     scale_i = amax_i / 448,  inv_i = 448 / amax_i   (float32; 1 and 1 when amax_i = 0)
+ *     q_ij    = E4M3(clamp(y_ij * inv_i, -448, 448))
+ * E4M3 is the OCP 8-bit float with 4 exponent bits (bias 7), 3 mantissa bits,
+ * no infinities, largest value 448 (torch.float8_e4m3fn), rounded to nearest
+ * even; y_ij ~= decode(q_ij) * scale_i.
+ *   y_fp8    [M, N]  uint8    output E4M3 codes; must not overlap anything
+ *   y_scale  [M]     float32  output per-row scale
+ * Other arguments as rmsnorm_fwd / add_rmsnorm_fwd (residual_out is still
+ * written in the input dtype).
+ */
+int rmsnorm_fwd_fp8(const void *x, const void *w, void *y_fp8, float *y_scale, float *rstd,
+                    int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream);
+
+int add_rmsnorm_fwd_fp8(const void *x, const void *r, const void *w, void *y_fp8, float *y_scale,
+                        void *residual_out, float *rstd, int64_t M, int64_t N, float eps,
+                        int dtype, int w_dtype, void *stream);
+
+/*
  * LayerNorm variants.  The "CuTe DSL" skill page lists a CTA-level LayerNorm
  * example (Workflow 0, example index) and names LayerNorm beside RMSNorm in
  * its float32 reduction pattern (Workflow 0); the formula is the textbook one

@@ -40,6 +40,8 @@ def lib():
     lib.layernorm_bwd_workspace_bytes.restype = sz
     lib.layernorm_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     return lib
@@ -50,6 +52,7 @@ def test_header_declares_the_entry_points():
                                   "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
                                   "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
                                   "layernorm_bwd_workspace_bytes", "add_layernorm_bwd",
+                                  "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8",
                                   "addrms_status_str", "addrms_last_hip_error"])
 
 
@@ -203,3 +206,16 @@ def test_layernorm_validation(lib):
     assert lb(wsb=wsb - 1) == E_WS
     assert lb(db=D + 4) == E_ALIAS        # db overlaps dw
     assert lb(db=0x70000000 + 64) == E_ALIAS  # db inside the workspace
+
+
+def test_fp8_validation(lib):
+    Q, S = 0x78000000, 0x7C000000
+    f = lambda **k: lib.rmsnorm_fwd_fp8(k.get("x", A), W, k.get("q", Q), k.get("s", S), None,
+                                        k.get("M", 4), 64, 1e-6, BF16, BF16, None)
+    assert f(q=None) == E_NULL and f(s=None) == E_NULL
+    assert f(M=0, q=None, s=None) == OK
+    assert f(q=A) == E_ALIAS          # codes over x (even though same start)
+    assert f(s=Q + 8) == E_ALIAS      # scale inside the codes
+    g = lambda **k: lib.add_rmsnorm_fwd_fp8(A, C, W, k.get("q", Q), S, k.get("res", D), None,
+                                            4, 64, 1e-6, BF16, BF16, None)
+    assert g(res=None) == E_NULL and g(q=C) == E_ALIAS and g(res=Q) == E_ALIAS
