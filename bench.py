@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, bf16 fused Add+RMSNorm M=16384 N=7168"
 WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
-HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 8, 2>"
+HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, false, 8, 2>"
 KERNEL_SOURCES = ["add_rmsnorm_amd/csrc/kernels.hpp", "add_rmsnorm_amd/csrc/device.hpp",
                   "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp",
                   "add_rmsnorm_amd/csrc/api.hip"]
@@ -236,7 +236,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands:
            f"    {commands['trace']}", "",
            "| kernel | calls | avg us | min us | max us | % of GPU time |",
            "|---|---|---|---|---|---|"]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:24]:
         out.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f} |")
@@ -336,6 +336,30 @@ def secondary(steps: int):
         "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
         "note": "reads dy, d(residual_out), residual_out; writes dh (= dx = dr) and dw"}
     del sets, ws, h, dy, dres
+    # FP8 output: fused Add+RMSNorm at the headline shape writing E4M3 codes
+    # and a per-row scale instead of bf16 y
+    M, N = 16384, 7168
+    inp = synth.workload_inputs(WORKLOAD)
+    w = inp["w"].cuda()
+    sets = []
+    for _ in range(2):
+        x, r = inp["x"].cuda(), inp["r"].cuda()
+        sets.append((x, r, torch.empty(M, N, dtype=torch.uint8, device="cuda"),
+                     torch.empty(M, device="cuda"), torch.empty_like(x)))
+
+    def f8():
+        x, r, q, sc, res = sets[i[0] & 1]
+        ar.add_rmsnorm_fwd_fp8(x, r, w, 1e-6, y_fp8=q, y_scale=sc, residual_out=res)
+        i[0] += 1
+
+    _, ev = timed(f8, steps, 5)
+    nb = 7 * M * N + 4 * M + 2 * N
+    out["add_rmsnorm_fwd_fp8_16384x7168"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
+                                                                       HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
+        "note": "bf16 x, r in; bf16 residual_out + E4M3 y + fp32 per-row scale out"}
+    del sets
     # LayerNorm: fused forward with bias at the headline shape, backward (dw, db)
     # at the backward workload's shape
     M, N = 16384, 7168
@@ -489,7 +513,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "fwd_vec_kernel<bf16_t, bf16_t, kRms, true, 8, 2> (fused, 8 waves/row, "
+                     "kernel": "fwd_vec_kernel<bf16_t, bf16_t, kRms, fused, bf16 out, 8, 2> (8 waves/row, "
                                "2 x 16 B per lane and tensor, one row per block)",
                      "avg_launch_us": round(h["ev"] / args.steps * 1e6, 3)},
     }
