@@ -174,3 +174,7 @@ def test_fused_backward_matches_torch_autograd_float64(M, N):
                                                    dwb_dtype=torch.float64)
     dx, dwp, dbp, _, _ = oracle.layernorm_bwd(dy, res, w, mean, rstd, dwb_dtype=torch.float64)
     assert torch.equal(dh0, dx) and torch.equal(dw0, dwp) and torch.equal(db0, dbp)
+    # no gradient of y: dh is the residual gradient exactly, dw = db = 0
+    dh1, dw1, db1, _, _ = oracle.add_layernorm_bwd(torch.zeros_like(dy), dres, res, w, mean, rstd,
+                                                   dwb_dtype=torch.float64)
+    assert torch.equal(dh1, dres) and torch.all(dw1 == 0) and torch.all(db1 == 0)
