@@ -47,7 +47,7 @@ class AddRmsError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m add_rmsnorm_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python add_rmsnorm_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_size_t)

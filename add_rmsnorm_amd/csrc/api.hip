@@ -251,9 +251,10 @@ bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
 // Backward variant: WPR in {1, 2, 4}; prefer at most 4 vectors per lane (the
 // dw accumulators live in registers, and short per-lane rows stream best:
 // bf16 32768 x 4096 measured 5.4 TB/s with 2 waves per row, 5.1 with one),
-// then 8, then 16; enough waves to fill the device; and a dw exchange that
-// fits in 64 KiB of LDS.  ADDRMS_BWD_WPR forces a WPR.
-bool pick_bwd(int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
+// then 8, then 16, among the instantiated variants; enough waves to fill the
+// device; and a dw exchange that fits in 64 KiB of LDS.  ADDRMS_BWD_WPR
+// forces a WPR.
+bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
 {
     const int forced = env_int("ADDRMS_BWD_WPR");
     int best_wi = -1, best_vi = -1;
@@ -264,7 +265,7 @@ bool pick_bwd(int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
             const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
             const int vi = vpl_index(need);
             const int rpb = 4 / wpr;
-            if (vi < 0 || kVplList[vi] > max_vpl)
+            if (vi < 0 || kVplList[vi] > max_vpl || !bwd_built(norm, res, kVplList[vi]))
                 continue;
             if ((size_t)(rpb / 2) * (size_t)N * 4u > kMaxDynLds)
                 continue;
@@ -460,7 +461,7 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
         return rc;
     int wi = 0, vi = 0;
-    if (vec_ok && pick_bwd(M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
+    if (vec_ok && pick_bwd(norm, res, M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
         a.nvec = (int)(N / nv);
         const KernelRef &k = tab.vec[norm][res ? 1 : 0][wi][vi];
         const int rpb = 4 / kWprList[wi];

@@ -68,6 +68,14 @@ constexpr bool fwd_built(int wpr, int vpl)
 {
     return wpr <= 4 || (wpr == 8 && vpl <= 8) || (wpr == 16 && vpl <= 4);
 }
+// Backward variants that are instantiated.  The LayerNorm backward with the
+// residual gradient at 16 vectors per lane needs more than the 512 VGPRs a
+// lane can hold and would spill to scratch; those rows take the element-wise
+// path instead.
+constexpr bool bwd_built(int norm, bool res, int vpl)
+{
+    return !(norm == kLayer && res && vpl > 14);
+}
 constexpr int kBwdBlock = 256;
 constexpr int kColReduceCols = 16; // dw columns per column-reduce block
 

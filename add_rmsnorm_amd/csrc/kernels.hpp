@@ -792,13 +792,19 @@ template <typename T, typename WT> struct TableBuilder {
         return t;
     }
 
+    template <int NM, bool R, int WPR, int VPL> static KernelRef bwd_ref()
+    {
+        if constexpr (bwd_built(NM, R, VPL))
+            return KernelRef{
+                reinterpret_cast<const void *>(&bwd_vec_kernel<T, WT, NM, R, WPR, VPL>),
+                kBwdBlock};
+        else
+            return KernelRef{nullptr, 0};
+    }
     template <int NM, bool R, int WI, int... VI>
     static void bwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
     {
-        ((row[VI] = KernelRef{reinterpret_cast<const void *>(
-                                  &bwd_vec_kernel<T, WT, NM, R, kWprList[WI], kVplList[VI]>),
-                              kBwdBlock}),
-         ...);
+        ((row[VI] = bwd_ref<NM, R, kWprList[WI], kVplList[VI]>()), ...);
     }
     template <int NM, bool R, int... WI>
     static void bwd_all(BwdTable &t, std::integer_sequence<int, WI...>)

@@ -64,7 +64,7 @@ def test_fused_bwd_elementwise(monkeypatch, M, N):
     check(*fused_case(M, N, torch.bfloat16, seed=9), f"elem {M}x{N}")
 
 
-@pytest.mark.parametrize("N", [1, 8, 65, 8193, 16384])
+@pytest.mark.parametrize("N", [1, 8, 65, 8193, 16384, 30720])
 def test_fused_bwd_edge_shapes(N):
     check(*fused_case(33, N, torch.bfloat16, seed=N), f"N={N}")
 

@@ -171,7 +171,11 @@ def test_backward_in_place_and_empty():
 # ---- fused backward and autograd ------------------------------------------------
 
 @pytest.mark.parametrize("M,N,dtype", [(4096, 4096, torch.bfloat16), (333, 1000, torch.bfloat16),
-                                       (500, 2048, torch.float32)])
+                                       (500, 2048, torch.float32),
+                                       # 12 vectors per lane; rows too long for the
+                                       # register-resident variants (element-wise path)
+                                       (24, 24576, torch.bfloat16), (24, 30720, torch.bfloat16),
+                                       (20, 16384, torch.float32)])
 def test_fused_backward(M, N, dtype):
     inp = inputs(M, N, dtype, seed=29)
     _, h, mean, rstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
