@@ -90,6 +90,9 @@ def _load():
         lib.oracle_add_rmsnorm_bwd.restype = i32
         lib.oracle_add_rmsnorm_bwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, vp, i32, vp,
                                                i32, vp, i64, i64]
+        lib.oracle_rmsnorm_rope.restype = i32
+        lib.oracle_rmsnorm_rope.argtypes = [vp, i32, i64, vp, i32, vp, vp, vp, i64, vp, i32, i64,
+                                            i64, i64, i64, i32, dbl]
         _lib = lib
     return _lib
 
@@ -334,3 +337,31 @@ def rmsnorm_fwd_fp8(x: torch.Tensor, w: torch.Tensor, eps: float, *, residual=No
                                               _ptr(rstd), _code(rstd), M, N, e),
            "add_rmsnorm_fwd_fp8")
     return q, scale, res, rstd
+
+
+def rmsnorm_rope(x: torch.Tensor, w: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                 pos: torch.Tensor, eps: float, *, interleaved: bool = False, y_dtype=None,
+                 eps_exact: bool = False) -> torch.Tensor:
+    """Per-head RMSNorm (weight w[D]) then RoPE by position, for heads x[T, H, D].
+
+    x may be a view with any token stride (e.g. the query or key part of a
+    packed projection output) as long as each token's H*D values are
+    contiguous.  cos, sin: float32 [P, D/2]; pos: int64 [T].  Returns a
+    contiguous [T, H, D] tensor in y_dtype (default x's dtype).  A position
+    outside [0, P) gives NaN heads."""
+    if x.device.type != "cpu" or x.dim() != 3:
+        raise ValueError("oracle: x must be a CPU [T, H, D] tensor")
+    T, H, D = x.shape
+    if x.stride(2) != 1 or (H > 1 and x.stride(1) != D):
+        x = x.contiguous()
+    w, cos, sin = _cpu(w), _cpu(cos), _cpu(sin)
+    pos = _cpu(pos)
+    if pos.dtype != torch.int64 or cos.dtype != torch.float32 or sin.dtype != torch.float32:
+        raise TypeError("oracle: pos int64, cos/sin float32")
+    y = torch.empty((T, H, D), dtype=y_dtype or x.dtype)
+    e = float(eps) if eps_exact else eps_as_float32(eps)
+    _check(_load().oracle_rmsnorm_rope(_ptr(x), _code(x), x.stride(0) if T > 1 else H * D,
+                                       _ptr(w), _code(w), _ptr(cos), _ptr(sin), _ptr(pos),
+                                       cos.shape[0], _ptr(y), _code(y), H * D, T, H, D,
+                                       int(bool(interleaved)), e), "rmsnorm_rope")
+    return y

@@ -579,3 +579,68 @@ int oracle_add_rmsnorm_fwd_fp8(const void *x, const void *r, int in_dt, const vo
     }
     return oracle_rmsnorm_fwd_fp8(res, res_dt, w, w_dt, q, scale, rstd, rstd_dt, M, N, eps);
 }
+
+/* ---- per-head RMSNorm followed by RoPE ------------------------------------ */
+
+/*
+ * The composition of two ops the "Machete" README lists side by side in
+ * "Built-In Areas" (RMSNorm, RoPE), as they meet in an attention layer: each
+ * query or key head of each token is RMS-normalised over its D values with a
+ * per-dimension weight w[D], then rotated by the token's position (rotary
+ * position embedding, Su et al. 2021, "RoFormer"). The rotation acts on pairs
+ * of normalised values:
+ *
+ *   rotate-half layout (interleaved = 0):  pair i = (n_i, n_{i+D/2})
+ *   interleaved layout (interleaved = 1):  pair i = (n_{2i}, n_{2i+1})
+ *   c = cos_t[p][i], s = sin_t[p][i], p = pos[t], i in [0, D/2)
+ *   (a, b) -> (a*c - b*s, b*c + a*s)
+ *
+ * The tables are float32 [P][D/2], widened exactly to binary64. The norm is
+ * oracle_rmsnorm_fwd of the head's row into binary64. The rotation is
+ * binary64, and each output is rounded once. A position outside [0, P) has
+ * no table row: that token's heads are all NaN.
+ *
+ * x: head h of token t starts at element t*x_stride + h*D (heads contiguous);
+ * y: the same with y_stride.  T tokens, H heads, D even.
+ */
+int oracle_rmsnorm_rope(const void *x, int x_dt, int64_t x_stride, const void *w, int w_dt,
+                        const float *cos_t, const float *sin_t, const int64_t *pos, int64_t P,
+                        void *y, int y_dt, int64_t y_stride, int64_t T, int64_t H, int64_t D,
+                        int interleaved, double eps)
+{
+    double *n;
+    const int64_t half = D / 2;
+
+    if (!x || !w || !cos_t || !sin_t || !pos || !y || T < 0 || H < 0 || D <= 0 || D % 2 != 0 ||
+        P < 0 || x_stride < H * D || y_stride < H * D)
+        return OR_ERR_ARG;
+    if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || !dtype_ok(y_dt))
+        return OR_ERR_ARG;
+    n = (double *)malloc((size_t)D * sizeof(double));
+    if (!n)
+        return OR_ERR_NOMEM;
+    for (int64_t t = 0; t < T; t++) {
+        const int64_t p = pos[t];
+        for (int64_t h = 0; h < H; h++) {
+            const int64_t xo = t * x_stride + h * D, yo = t * y_stride + h * D;
+            if (p < 0 || p >= P) {
+                for (int64_t j = 0; j < D; j++)
+                    store_elem(y, y_dt, yo + j, NAN);
+                continue;
+            }
+            const void *xh = (const char *)x + (size_t)xo * elem_size(x_dt);
+            oracle_rmsnorm_fwd(xh, x_dt, w, w_dt, n, OR_F64, NULL, OR_F32, 1, D, eps);
+            for (int64_t i = 0; i < half; i++) {
+                const int64_t ja = interleaved ? 2 * i : i;
+                const int64_t jb = interleaved ? 2 * i + 1 : i + half;
+                const double c = (double)cos_t[p * half + i];
+                const double s = (double)sin_t[p * half + i];
+                const double a = n[ja], b = n[jb];
+                store_elem(y, y_dt, yo + ja, a * c - b * s);
+                store_elem(y, y_dt, yo + jb, b * c + a * s);
+            }
+        }
+    }
+    free(n);
+    return OR_OK;
+}

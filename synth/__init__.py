@@ -8,7 +8,7 @@ Recipe (every tensor): a NumPy PCG64 stream keyed by (seed, tag) draws
 binary64 standard normals; they are scaled and shifted, rounded to binary32 by
 NumPy, and, for bfloat16, rounded again by torch's float32 -> bfloat16
 conversion (round-to-nearest-even).  Tags keep tensors independent: "x", "r",
-"w", "dy", "outlier-cols".
+"w", "dy", "outlier-cols", "pos", "wq", "wk".
 
 The pages run RMSNorm and fused Add + RMSNorm on bfloat16 LLM activations (the
 KernelAgent digest's SM100 benchmark suite of Quack and DeepSeek norm
@@ -42,9 +42,40 @@ def store(a: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
     return t if dtype == torch.float32 else t.to(dtype)
 
 
-def weight(seed: int, n: int, dtype: torch.dtype) -> torch.Tensor:
+def weight(seed: int, n: int, dtype: torch.dtype, tag: str = "w") -> torch.Tensor:
     """w = 1 + 0.1 * N(0, 1), the per-channel scale."""
-    return store(normal(seed, "w", (n,), mean=1.0, std=0.1), dtype)
+    return store(normal(seed, tag, (n,), mean=1.0, std=0.1), dtype)
+
+
+def positions(seed: int, T: int, P: int, seq_len: int | None = None) -> torch.Tensor:
+    """int64 positions of T tokens in [0, P): with seq_len, a batch of
+    sequences that each count 0, 1, ..., seq_len - 1 (a prefill batch);
+    otherwise independent uniform draws (tag "pos")."""
+    if seq_len is not None:
+        return torch.arange(T, dtype=torch.int64) % min(seq_len, P)
+    return torch.from_numpy(_rng(seed, "pos").integers(0, P, size=T, dtype=np.int64))
+
+
+def rope_table(P: int, D: int, base: float = 10000.0):
+    """cos and sin tables [P, D/2] float32 of the angles p * base^(-2i/D),
+    formed in binary64 and rounded once.  They are inputs of the RMSNorm +
+    RoPE op, which reads them and never forms an angle itself."""
+    i = np.arange(D // 2, dtype=np.float64)
+    ang = np.arange(P, dtype=np.float64)[:, None] * base ** (-2.0 * i / D)[None, :]
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)),
+            torch.from_numpy(np.sin(ang).astype(np.float32)))
+
+
+def rmsnorm_rope_inputs(T: int, Hq: int, Hk: int, D: int, dtype=torch.bfloat16, w_dtype=None,
+                        seed: int = 0, P: int = 32768, seq_len: int | None = None):
+    """A packed query/key/value projection output qkv [T, (Hq + 2 Hk) * D] ~ N(0, 1),
+    per-dimension query and key norm weights wq, wk [D] (tags "wq", "wk"),
+    rotary tables cos, sin [P, D/2] and positions pos [T]."""
+    cos, sin = rope_table(P, D)
+    return {"qkv": store(normal(seed, "x", (T, (Hq + 2 * Hk) * D)), dtype),
+            "wq": weight(seed, D, w_dtype or dtype, "wq"),
+            "wk": weight(seed, D, w_dtype or dtype, "wk"),
+            "cos": cos, "sin": sin, "pos": positions(seed, T, P, seq_len)}
 
 
 def outlier_columns(seed: int, n: int, frac: float = 0.01) -> np.ndarray:
@@ -99,6 +130,11 @@ WORKLOADS = {
     "rmsnorm_bwd_bf16_32768x4096": dict(
         op="rmsnorm_bwd", M=32768, N=4096, dtype=torch.bfloat16, w_dtype=torch.bfloat16,
         eps=1e-6),
+    # per-head RMSNorm + RoPE of the query and key heads: 4 sequences of 4096
+    # tokens, 32 query and 8 key heads of 128
+    "rmsnorm_rope_bf16_t16384_q32_k8_d128": dict(
+        op="rmsnorm_rope", T=16384, Hq=32, Hk=8, D=128, dtype=torch.bfloat16,
+        w_dtype=torch.bfloat16, eps=1e-6, P=32768, seq_len=4096),
 }
 
 
@@ -113,4 +149,7 @@ def workload_inputs(name: str, M: int | None = None, seed: int = 0):
                                       r_std=cfg.get("r_std", 1.0),
                                       outlier_frac=cfg.get("outlier_frac", 0.0),
                                       outlier_scale=cfg.get("outlier_scale", 300.0))
+    if cfg["op"] == "rmsnorm_rope":
+        return rmsnorm_rope_inputs(M if M is not None else cfg["T"], cfg["Hq"], cfg["Hk"], cfg["D"],
+                                   cfg["dtype"], cfg["w_dtype"], seed, cfg["P"], cfg["seq_len"])
     return rmsnorm_bwd_inputs(M, cfg["N"], cfg["dtype"], cfg["w_dtype"], seed)

@@ -5,7 +5,10 @@ it, and runs the oracle pin suite against that build in a subprocess: the
 suite must fail.  Mistakes cover every step of the definition: the eps
 placement, the mean's divisor, the square, the weight, the bfloat16 rounding
 rule, the fused op's choice of normalised value, the saved rstd, and each term
-of the backward, including the residual gradient of the fused op."""
+of the backward, including the residual gradient of the fused op; for
+LayerNorm, E4M3 and RMSNorm + RoPE, each step of their definitions (the RoPE
+signs, the cos/sin roles, the pairing of each layout, the table row, and the
+empty-table-row rule)."""
 import os
 import subprocess
 import sys
@@ -15,7 +18,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "addrms_oracle.c")
 PINS = ["tests/test_oracle_bf16.py", "tests/test_oracle_fwd.py", "tests/test_oracle_bwd.py",
-        "tests/test_oracle_layernorm.py", "tests/test_oracle_fp8.py"]
+        "tests/test_oracle_layernorm.py", "tests/test_oracle_fp8.py", "tests/test_oracle_rope.py"]
 
 MUTANTS = {
     "eps_outside_root": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms) + eps"),
@@ -72,6 +75,25 @@ MUTANTS.update({
     "fp8_no_saturation": ("return (uint8_t)(sign | 0x7Eu); /* 448", "return (uint8_t)(sign | 0x7Fu); /* 448"),
     "fp8_scale_inverted": ("sc = amax / 448.0f;", "sc = 448.0f / amax;"),
     "fp8_quantises_unscaled": ("float v = yf[j] * inv;", "float v = yf[j];"),
+    "rope_first_sign": ("store_elem(y, y_dt, yo + ja, a * c - b * s);",
+                        "store_elem(y, y_dt, yo + ja, a * c + b * s);"),
+    "rope_second_sign": ("store_elem(y, y_dt, yo + jb, b * c + a * s);",
+                         "store_elem(y, y_dt, yo + jb, b * c - a * s);"),
+    "rope_cos_sin_swapped": ("const double c = (double)cos_t[p * half + i];\n"
+                             "                const double s = (double)sin_t[p * half + i];",
+                             "const double c = (double)sin_t[p * half + i];\n"
+                             "                const double s = (double)cos_t[p * half + i];"),
+    "rope_token_index_not_position": ("const int64_t p = pos[t];", "const int64_t p = t;"),
+    "rope_layouts_swapped": ("const int64_t ja = interleaved ? 2 * i : i;\n"
+                             "                const int64_t jb = interleaved ? 2 * i + 1 : i + half;",
+                             "const int64_t ja = interleaved ? i : 2 * i;\n"
+                             "                const int64_t jb = interleaved ? i + half : 2 * i + 1;"),
+    "rope_half_pairs_adjacent": ("const int64_t jb = interleaved ? 2 * i + 1 : i + half;",
+                                 "const int64_t jb = interleaved ? 2 * i + 1 : (i + 1) % D;"),
+    "rope_out_of_range_not_nan": ("store_elem(y, y_dt, yo + j, NAN);",
+                                  "store_elem(y, y_dt, yo + j, 0.0);"),
+    "rope_norm_without_eps": ("oracle_rmsnorm_fwd(xh, x_dt, w, w_dt, n, OR_F64, NULL, OR_F32, 1, D, eps);",
+                           "oracle_rmsnorm_fwd(xh, x_dt, w, w_dt, n, OR_F64, NULL, OR_F32, 1, D, 0.0);"),
 })
 
 

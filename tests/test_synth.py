@@ -42,3 +42,21 @@ def test_decode_outlier_columns():
 def test_store_types(dtype):
     t = synth.store(synth.normal(0, "x", (3, 5)), dtype)
     assert t.dtype == dtype and t.is_contiguous()
+
+
+def test_rope_inputs():
+    inp = synth.workload_inputs("rmsnorm_rope_bf16_t16384_q32_k8_d128", M=8192)
+    assert inp["qkv"].shape == (8192, 48 * 128) and inp["qkv"].dtype == torch.bfloat16
+    assert inp["cos"].shape == (32768, 64) and inp["cos"].dtype == torch.float32
+    # a prefill batch of sequences of 4096 tokens
+    assert torch.equal(inp["pos"][:4096], torch.arange(4096))
+    assert torch.equal(inp["pos"][4096:8192], torch.arange(4096))
+    assert not torch.equal(inp["wq"], inp["wk"])
+    # the table holds cos and sin of p * 10000^(-2i/D), rounded once to float32
+    p, i = 1234, 5
+    ang = p * 10000.0 ** (-2.0 * i / 128)
+    assert inp["cos"][p, i].item() == np.float32(np.cos(ang))
+    assert inp["sin"][p, i].item() == np.float32(np.sin(ang))
+    u = synth.positions(3, 1000, 77)
+    assert u.dtype == torch.int64 and int(u.min()) >= 0 and int(u.max()) < 77
+    assert torch.equal(u, synth.positions(3, 1000, 77))
