@@ -28,7 +28,7 @@ import torch
 __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_bwd",
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
            "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "rmsnorm_fwd_fp8",
-           "add_rmsnorm_fwd_fp8", "AddRmsError", "LIB_PATH", "lib"]
+           "add_rmsnorm_fwd_fp8", "rmsnorm_rope_qk", "AddRmsError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -76,6 +76,9 @@ def _load():
     lib.add_layernorm_bwd.restype = i32
     lib.add_layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32,
                                       i32, vp]
+    lib.rmsnorm_rope_qk.restype = i32
+    lib.rmsnorm_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
+                                    i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     lib.addrms_last_hip_error.restype = i32
@@ -466,3 +469,65 @@ def add_rmsnorm_fwd_fp8(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: 
     if st != 0:
         raise AddRmsError(st, "add_rmsnorm_fwd_fp8")
     return y_fp8, y_scale, residual_out
+
+
+def _heads(t: torch.Tensor, what: str, dtype=None, T=None, D=None) -> int:
+    """Check a [T, H, D] GPU tensor whose heads of one token are contiguous
+    (any token stride, e.g. a view into a packed projection output) and
+    return its token stride in elements."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if t.dim() != 3:
+        raise ValueError(f"{what} must be [T, H, D], got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    Tt, H, Dd = t.shape
+    if (T is not None and Tt != T) or (D is not None and Dd != D):
+        raise ValueError(f"{what}: shape {tuple(t.shape)} does not match T={T}, D={D}")
+    if Dd > 0 and (t.stride(2) != 1 or (H > 1 and t.stride(1) != Dd)):
+        raise ValueError(f"{what}: the heads of one token must be contiguous")
+    return t.stride(0) if Tt > 1 else H * Dd
+
+
+def rmsnorm_rope_qk(q: torch.Tensor, k, wq: torch.Tensor, wk, cos: torch.Tensor,
+                    sin: torch.Tensor, pos: torch.Tensor, eps: float = 1e-6, *,
+                    interleaved: bool = False, q_out=None, k_out=None):
+    """Per-head RMSNorm (weights wq, wk [D]) then RoPE at each token's
+    position, for query heads q [T, Hq, D] and key heads k [T, Hk, D] (k may
+    be None).  q and k may be views with any token stride.  cos, sin: float32
+    [P, D/2]; pos: int64 [T].  interleaved selects pairs (2i, 2i+1) instead of
+    (i, i + D/2).  q_out=q, k_out=k update in place (e.g. a packed qkv
+    buffer).  Returns (q_out, k_out); a position outside [0, P) gives NaN
+    heads."""
+    T, Hq, D = q.shape if q.dim() == 3 else (None, None, None)
+    qs = _heads(q, "q")
+    Hk, ks = 0, 0
+    if k is not None:
+        ks = _heads(k, "k", q.dtype, T, D)
+        Hk = k.shape[1]
+    _dev(wq, "wq", shape=(D,))
+    if k is not None:
+        if wk is None:
+            raise ValueError("wk is required with k")
+        _dev(wk, "wk", wq.dtype, (D,))
+    _dev(cos, "cos", torch.float32)
+    if cos.dim() != 2 or cos.shape[1] != D // 2:
+        raise ValueError(f"cos must be [P, D/2], got {tuple(cos.shape)}")
+    _dev(sin, "sin", torch.float32, cos.shape)
+    _dev(pos, "pos", torch.int64, (T,))
+    q_out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device) if q_out is None else q_out
+    qos = _heads(q_out, "q_out", q.dtype, T, D)
+    kos = 0
+    if k is not None:
+        k_out = torch.empty((T, Hk, D), dtype=q.dtype, device=q.device) if k_out is None else k_out
+        kos = _heads(k_out, "k_out", q.dtype, T, D)
+    dev = q.get_device()
+    with _OnDevice(dev):
+        st = _lib.rmsnorm_rope_qk(_p(q), _p(k), _p(wq), _p(wk) if k is not None else None,
+                                  _p(cos), _p(sin), _p(pos), cos.shape[0], _p(q_out), _p(k_out),
+                                  T, Hq, Hk, D, qs, ks, qos, kos, float(eps),
+                                  1 if interleaved else 0, _code(q, "q"), _code(wq, "wq"),
+                                  _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "rmsnorm_rope_qk")
+    return q_out, k_out

@@ -3,8 +3,9 @@
     python add_rmsnorm_amd/build.py        (a script: it must not import the
                                             package, which loads the library)
 
-Compiles csrc/tables.hip once per (row dtype, weight dtype) combination and
-csrc/api.hip, in parallel, then links one shared library next to this file.
+Compiles csrc/tables.hip and csrc/rope.hip once per (row dtype, weight dtype)
+combination and csrc/api.hip, in parallel, then links one shared library next
+to this file.
 """
 from __future__ import annotations
 
@@ -43,6 +44,8 @@ def build(verbose: bool = False, extra_defines=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = [(os.path.join(CSRC, "tables.hip"), os.path.join(BUILD, f"tables_{c}.o"),
              (f"ADDRMS_COMBO={c}", *extra_defines)) for c in range(4)]
+    jobs += [(os.path.join(CSRC, "rope.hip"), os.path.join(BUILD, f"rope_{c}.o"),
+              (f"ADDRMS_COMBO={c}", *extra_defines)) for c in range(4)]
     jobs.append((os.path.join(CSRC, "api.hip"), os.path.join(BUILD, "api.o"),
                  tuple(extra_defines)))
     workers = min(len(jobs), max(1, min(16, os.cpu_count() or 1)))

@@ -37,6 +37,21 @@ const FwdTable &fwd_table(int c)
     }
 }
 
+const RopeTable &rope_table_0();
+const RopeTable &rope_table_1();
+const RopeTable &rope_table_2();
+const RopeTable &rope_table_3();
+
+const RopeTable &rope_table(int c)
+{
+    switch (c) {
+    case 0: return rope_table_0();
+    case 1: return rope_table_1();
+    case 2: return rope_table_2();
+    default: return rope_table_3();
+    }
+}
+
 const BwdTable &bwd_table(int c)
 {
     switch (c) {
@@ -52,6 +67,7 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxPartials = 1024; // dw partial rows (workspace rows)
+constexpr int kRopeHpl = 4;            // RMSNorm + RoPE: heads per lane group and step
 constexpr size_t kMaxDynLds = 65536;
 
 int fail_hip(hipError_t e)
@@ -495,6 +511,154 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     return (ln && db) ? colreduce(a.ws2, a.P, (int)N, db, s) : ADDRMS_OK;
 }
 
+// Do two strided sets of byte ranges, {a + i*sa + [0, la)} for i < na and
+// {b + j*sb + [0, lb)} for j < nb, share a byte?  Exact when the whole spans
+// are disjoint, and for equal strides with la, lb <= stride: the heads of one
+// packed projection buffer (query and key parts of every token) interleave
+// without touching.  Otherwise the answer is yes (conservative).
+bool strided_overlap(const void *pa, int64_t sa, int64_t la, int64_t na, const void *pb,
+                     int64_t sb, int64_t lb, int64_t nb)
+{
+    if (na <= 0 || nb <= 0 || la <= 0 || lb <= 0)
+        return false;
+    const Span A = span(pa, (size_t)((na - 1) * sa + la));
+    const Span B = span(pb, (size_t)((nb - 1) * sb + lb));
+    if (!overlaps(A, B))
+        return false;
+    if (sa == sb && la <= sa && lb <= sb) {
+        const int64_t d = (int64_t)(B.lo - A.lo);
+        int64_t r = d % sa;
+        if (r < 0)
+            r += sa;
+        return !(r >= la && r + lb <= sa);
+    }
+    return true;
+}
+
+// Per-head RMSNorm + RoPE (see rmsnorm_rope_qk in addrms.h).
+int rope_common(const void *q, const void *k, const void *wq, const void *wk, const float *cos,
+                const float *sin, const int64_t *pos, int64_t P, void *qo, void *ko, int64_t T,
+                int64_t Hq, int64_t Hk, int64_t D, int64_t q_stride, int64_t k_stride,
+                int64_t qo_stride, int64_t ko_stride, float eps, int interleaved, int dtype,
+                int w_dtype, hipStream_t s)
+{
+    if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
+        return ADDRMS_ERR_DTYPE;
+    if (T < 0 || Hq < 0 || Hk < 0 || P < 0 || D < 2 || D % 2 != 0 || D > INT_MAX ||
+        Hq > INT_MAX || Hk > INT_MAX || Hq + Hk > INT_MAX / D)
+        return ADDRMS_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return ADDRMS_ERR_EPS;
+    if (T == 0 || Hq + Hk == 0)
+        return ADDRMS_OK; // nothing to do; the pointers may be NULL
+    if (!cos || !sin || !pos || (Hq > 0 && (!q || !qo || !wq)) || (Hk > 0 && (!k || !ko || !wk)))
+        return ADDRMS_ERR_NULL;
+    const int64_t es = (int64_t)esize(dtype);
+    const int64_t lim = ((int64_t)1 << 62) / es;
+    // each token's heads fit inside its stride, and the last element is addressable
+    auto bad_stride = [&](int64_t H, int64_t st) {
+        return H > 0 && (st < H * D || st > lim / (T > 1 ? T : 1));
+    };
+    if (bad_stride(Hq, q_stride) || bad_stride(Hq, qo_stride) || bad_stride(Hk, k_stride) ||
+        bad_stride(Hk, ko_stride) || (int64_t)(P > 0 ? P : 1) > lim / D)
+        return ADDRMS_ERR_SHAPE;
+
+    // outputs: each may be its own input (same address and stride); nothing
+    // else overlaps an output
+    const Span sc = span(cos, (size_t)(P * (D / 2) * 4)), ssn = span(sin, (size_t)(P * (D / 2) * 4));
+    const Span sp = span(pos, (size_t)T * 8u);
+    const Span swq = Hq > 0 ? span(wq, (size_t)(D * (int64_t)esize(w_dtype))) : Span{};
+    const Span swk = Hk > 0 ? span(wk, (size_t)(D * (int64_t)esize(w_dtype))) : Span{};
+    struct Set {
+        const void *p;
+        int64_t stride, len;
+    };
+    const Set sq{q, q_stride * es, Hq * D * es}, sk{k, k_stride * es, Hk * D * es};
+    const Set sqo{qo, qo_stride * es, Hq * D * es}, sko{ko, ko_stride * es, Hk * D * es};
+    auto hit = [&](const Set &a, const Set &b) {
+        return strided_overlap(a.p, a.stride, a.len, T, b.p, b.stride, b.len, T);
+    };
+    auto whole = [&](const Set &a) {
+        return a.len > 0 ? span(a.p, (size_t)((T - 1) * a.stride + a.len)) : Span{};
+    };
+    const bool q_inplace = qo == q && qo_stride == q_stride;
+    const bool k_inplace = ko == k && ko_stride == k_stride;
+    if ((!q_inplace && hit(sqo, sq)) || (!k_inplace && hit(sko, sk)) || hit(sqo, sk) ||
+        hit(sko, sq) || hit(sqo, sko))
+        return ADDRMS_ERR_ALIAS;
+    for (const Set *o : {&sqo, &sko}) {
+        const Span so = whole(*o);
+        if (overlaps(so, sc) || overlaps(so, ssn) || overlaps(so, sp) || overlaps(so, swq) ||
+            overlaps(so, swk))
+            return ADDRMS_ERR_ALIAS;
+    }
+
+    RopeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.wq = wq;
+    a.wk = wk;
+    a.cos = cos;
+    a.sin = sin;
+    a.pos = pos;
+    a.qo = qo;
+    a.ko = ko;
+    a.q_stride = q_stride;
+    a.k_stride = k_stride;
+    a.qo_stride = qo_stride;
+    a.ko_stride = ko_stride;
+    a.T = T;
+    a.P = P;
+    a.Hq = (int)Hq;
+    a.Hk = (int)Hk;
+    a.D = (int)D;
+    a.eps = eps;
+
+    const RopeTable &tab = rope_table(combo(dtype, w_dtype));
+    const int il = interleaved ? 1 : 0;
+    const int64_t total = T * (Hq + Hk);
+    // vector path: D = 2 * E * G with G = 1, 2, 4, ..., 64 lanes per head,
+    // every pointer 16-byte aligned, every token stride a multiple of 16 bytes
+    const int E = vec_elems(dtype);
+    const int64_t G = D / (2 * E);
+    int lg = -1;
+    if (D % (2 * E) == 0)
+        for (int i = 0; i < kRopeNumGroups; ++i)
+            if (G == ((int64_t)1 << i))
+                lg = i;
+    auto al = [&](const void *p, int64_t H, int64_t st) {
+        return H == 0 || (aligned16(p) && (st * es) % 16 == 0);
+    };
+    const bool vec = env_int("ADDRMS_FORCE_ELEM") == 0 && lg >= 0 && al(q, Hq, q_stride) &&
+                     al(qo, Hq, qo_stride) && al(k, Hk, k_stride) && al(ko, Hk, ko_stride) &&
+                     (Hq == 0 || aligned16(wq)) && (Hk == 0 || aligned16(wk)) && aligned16(cos) &&
+                     aligned16(sin);
+    if (vec) {
+        // heads per lane group and loop step: ADDRMS_ROPE_HPL = 1, 2 or 4
+        // forces it; otherwise kRopeHpl
+        const int forced = env_int("ADDRMS_ROPE_HPL");
+        int hpl = forced == 1 || forced == 2 || forced == 4 ? forced : kRopeHpl;
+        if (!rope_built((int)G, hpl))
+            hpl = 2;
+        const int lh = hpl == 1 ? 0 : hpl == 2 ? 1 : 2;
+        const int64_t step = (kRopeBlock / G) * hpl;
+        int64_t blocks = (total + step - 1) / step;
+        // ADDRMS_ROPE_BLOCKS_PER_CU caps the grid at that many blocks per CU
+        // (each block then loops over several steps)
+        const int bpc = env_int("ADDRMS_ROPE_BLOCKS_PER_CU");
+        if (bpc > 0) {
+            int cus = 0, rc;
+            if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
+                return rc;
+            if (blocks > (int64_t)cus * bpc)
+                blocks = (int64_t)cus * bpc;
+        }
+        return launch(tab.vec[il][lg][lh],
+                      dim3((unsigned)(blocks < (1 << 30) ? blocks : (1 << 30))), 0, &a, s);
+    }
+    return launch(tab.elem[il], dim3((unsigned)(total < (1 << 24) ? total : (1 << 24))), 0, &a, s);
+}
+
 } // namespace
 } // namespace addrms
 
@@ -600,6 +764,17 @@ int add_layernorm_bwd(const void *dy, const void *dres, const void *h, const voi
 {
     return bwd_common(kLayer, dy, dres, h, w, mean, rstd, dh, dw, db, workspace, workspace_bytes,
                       M, N, dtype, w_dtype, stream);
+}
+
+int rmsnorm_rope_qk(const void *q, const void *k, const void *wq, const void *wk,
+                    const float *cos, const float *sin, const int64_t *pos, int64_t P, void *q_out,
+                    void *k_out, int64_t T, int64_t Hq, int64_t Hk, int64_t D, int64_t q_stride,
+                    int64_t k_stride, int64_t q_out_stride, int64_t k_out_stride, float eps,
+                    int interleaved, int dtype, int w_dtype, void *stream)
+{
+    return rope_common(q, k, wq, wk, cos, sin, pos, P, q_out, k_out, T, Hq, Hk, D, q_stride,
+                       k_stride, q_out_stride, k_out_stride, eps, interleaved, dtype, w_dtype,
+                       reinterpret_cast<hipStream_t>(stream));
 }
 
 const char *addrms_status_str(int status)

@@ -243,6 +243,13 @@ __device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b)
 #endif
 }
 
+// One DPP move of a float within 16-lane rows (source lanes must be active).
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 // The same sum for doubles (each DPP step moves both 32-bit halves).
 template <int CTRL> __device__ __forceinline__ double dpp_f64(double v)
 {

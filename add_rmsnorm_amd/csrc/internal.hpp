@@ -26,6 +26,26 @@ struct FwdArgs {
     float eps;
 };
 
+// Per-head RMSNorm + RoPE arguments.  Head h of token t is the D contiguous
+// values at q + t*q_stride + h*D (h < Hq) or k + t*k_stride + (h-Hq)*D;
+// strides are in elements.  cos/sin: float32 [P, D/2]; pos: int64 [T].
+struct RopeArgs {
+    const void *q;
+    const void *k;
+    const void *wq;
+    const void *wk;
+    const float *cos;
+    const float *sin;
+    const int64_t *pos;
+    void *qo;
+    void *ko;
+    int64_t q_stride, k_stride, qo_stride, ko_stride;
+    int64_t T;
+    int64_t P;
+    int Hq, Hk, D;
+    float eps;
+};
+
 // Which normalisation a kernel computes.
 enum Norm : int { kRms = 0, kLayer = 1 };
 
@@ -107,7 +127,22 @@ struct BwdTable {
     KernelRef elem_dw[2];
 };
 
+// RMSNorm + RoPE: vec [interleaved][log2 of the lanes per head, 0..6][log2
+// of the heads per lane group and loop step, 0..2] (the 16-byte vector path),
+// elem [interleaved].
+constexpr int kRopeNumGroups = 7;
+constexpr int kRopeNumHpl = 3;
+// With one lane per head, four heads per step spill scalar registers: not
+// instantiated (two are used instead).
+constexpr bool rope_built(int g, int hpl) { return !(g == 1 && hpl == 4); }
+constexpr int kRopeBlock = 256;
+struct RopeTable {
+    KernelRef vec[2][kRopeNumGroups][kRopeNumHpl];
+    KernelRef elem[2];
+};
+
 const FwdTable &fwd_table(int combo_idx);
+const RopeTable &rope_table(int combo_idx);
 const BwdTable &bwd_table(int combo_idx);
 KernelRef colreduce_kernel(bool vec);
 

@@ -406,6 +406,34 @@ def secondary(steps: int):
                                                                        HBM_PEAK_GBPS, 1),
         "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb, "note": "dx, dw, db"}
     del sets, ws
+    # per-head RMSNorm + RoPE of the query and key heads, in place on a packed
+    # projection buffer: 16384 tokens (4 sequences of 4096), 32 + 8 heads of 128
+    name = "rmsnorm_rope_bf16_t16384_q32_k8_d128"
+    c = synth.WORKLOADS[name]
+    inp = synth.workload_inputs(name)
+    T, Hq, Hk, D = c["T"], c["Hq"], c["Hk"], c["D"]
+    wq, wk, cos, sin, pos = (inp[n].cuda() for n in ("wq", "wk", "cos", "sin", "pos"))
+    bufs = [inp["qkv"].cuda() for _ in range(3)]  # 3 x 168 MB of heads: not cache-resident
+    views = [(b[:, :Hq * D].view(T, Hq, D), b[:, Hq * D:(Hq + Hk) * D].view(T, Hk, D))
+             for b in bufs]
+    i = [0]
+
+    def rstep():
+        q, k = views[i[0] % 3]
+        ar.rmsnorm_rope_qk(q, k, wq, wk, cos, sin, pos, c["eps"], q_out=q, k_out=k)
+        i[0] += 1
+
+    _, ev = timed(rstep, steps, 5)
+    npos = int(torch.unique(inp["pos"]).numel())
+    # heads read and written; positions; the table rows used (cos and sin,
+    # D/2 floats each); both weight vectors
+    nb = 4 * T * (Hq + Hk) * D + 8 * T + npos * D * 4 + 2 * D * 2
+    out[name] = {
+        "GBps": round(nb * steps / ev / 1e9, 1),
+        "pct_of_peak": round(100 * nb * steps / ev / 1e9 / HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
+        "note": "in place on packed qkv [16384, 48*128]; value heads untouched; 3 rotating sets"}
+    del bufs, views
     # fused forward, 4096 x 4096 bf16 (134 MB: fits in the last-level cache; rotate 4 sets)
     inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_4096x4096")
     M, N = 4096, 4096

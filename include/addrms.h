@@ -224,6 +224,45 @@ int add_layernorm_bwd(const void *dy, const void *dres, const void *h, const voi
                       int w_dtype, void *stream);
 
 /* Static, human-readable name of a status code. */
+/*
+ * Per-head RMSNorm followed by the rotary position embedding, for the query
+ * and key heads of an attention layer, in one pass.  The "Machete" README
+ * lists RMSNorm and RoPE side by side among the ops its persistent kernels
+ * compose ("Built-In Areas"); RoPE is the rotation of RoFormer (Su et al.
+ * 2021).  For every token t and every head (Hq query heads, then Hk key
+ * heads) of D values x:
+ *     rstd  = 1 / sqrt(mean_j(x_j^2) + eps)
+ *     n_j   = x_j * rstd * w_j              (w = wq for query heads, wk for key heads)
+ *     p     = pos[t];  c_i = cos[p][i],  s_i = sin[p][i],  i < D/2
+ *     pair i = (n_i, n_{i+D/2})   interleaved == 0 (rotate-half layout)
+ *            = (n_{2i}, n_{2i+1}) interleaved != 0
+ *     (a, b) -> (round(a*c_i - b*s_i), round(b*c_i + a*s_i))
+ * in float32, one rounding per output.  A position outside [0, P) has no
+ * table row: that token's heads are written as NaN (nothing outside the
+ * tables is read).
+ *   q      [T][Hq][D]  dtype    head h of token t at q + t*q_stride + h*D
+ *   k      [T][Hk][D]  dtype    likewise with k_stride (Hk may be 0, k NULL)
+ *   wq, wk [D]         w_dtype  per-dimension norm weights
+ *   cos, sin [P][D/2]  float32  rotary tables, row p for position p
+ *   pos    [T]         int64    token positions
+ *   q_out, k_out                outputs laid out as q, k with their own strides
+ * Strides are in elements (at least Hq*D, resp. Hk*D), so q and k may be
+ * views into one packed projection output.  D must be even.  q_out may be q
+ * (same stride) and k_out may be k, which updates a packed buffer in place;
+ * no other overlap of an output with any argument is allowed (query and key
+ * heads interleaved in one buffer do not overlap).  T == 0 or Hq + Hk == 0
+ * launches nothing and the pointers may be NULL.  The 16-byte vector path
+ * needs D = 2*E*G for G in {1, 2, 4, ..., 64} (E = 8 bf16, 4 float32 values
+ * per vector: D = 128 bf16 uses G = 8 lanes per head), 16-byte aligned
+ * pointers and token strides that are a multiple of 16 bytes; any other even
+ * D or alignment takes an element-wise path with the same results.
+ */
+int rmsnorm_rope_qk(const void *q, const void *k, const void *wq, const void *wk,
+                    const float *cos, const float *sin, const int64_t *pos, int64_t P, void *q_out,
+                    void *k_out, int64_t T, int64_t Hq, int64_t Hk, int64_t D, int64_t q_stride,
+                    int64_t k_stride, int64_t q_out_stride, int64_t k_out_stride, float eps,
+                    int interleaved, int dtype, int w_dtype, void *stream);
+
 const char *addrms_status_str(int status);
 
 /* The hipError_t of the last ADDRMS_ERR_HIP returned on this thread (0 if none). */

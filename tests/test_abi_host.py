@@ -42,6 +42,8 @@ def lib():
     lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.add_rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.rmsnorm_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
+                                    i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
     lib.addrms_status_str.argtypes = [i32]
     return lib
@@ -52,7 +54,7 @@ def test_header_declares_the_entry_points():
                                   "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
                                   "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
                                   "layernorm_bwd_workspace_bytes", "add_layernorm_bwd",
-                                  "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8",
+                                  "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8", "rmsnorm_rope_qk",
                                   "addrms_status_str", "addrms_last_hip_error"])
 
 
@@ -219,3 +221,41 @@ def test_fp8_validation(lib):
     g = lambda **k: lib.add_rmsnorm_fwd_fp8(A, C, W, k.get("q", Q), S, k.get("res", D), None,
                                             4, 64, 1e-6, BF16, BF16, None)
     assert g(res=None) == E_NULL and g(q=C) == E_ALIAS and g(res=Q) == E_ALIAS
+
+
+def test_rope_validation(lib):
+    # a packed projection buffer of T tokens: Hq query, Hk key, Hk value heads
+    T, Hq, Hk, D, P = 4, 4, 2, 64, 100
+    S = (Hq + 2 * Hk) * D  # token stride, elements
+    QKV, WQ, WK, COS, SIN, POS = 0x10000000, 0x60000000, 0x61000000, 0x62000000, 0x63000000, \
+        0x64000000
+    KB = QKV + Hq * D * 2  # key heads of token 0 (bf16)
+    OUT = 0x70000000
+
+    def rope(**k):
+        g = lambda n, d: k.get(n, d)
+        return lib.rmsnorm_rope_qk(g("q", QKV), g("k", KB), g("wq", WQ), g("wk", WK),
+                                   g("cos", COS), g("sin", SIN), g("pos", POS), g("P", P),
+                                   g("qo", OUT), g("ko", OUT + T * Hq * D * 2), g("T", T),
+                                   g("Hq", Hq), g("Hk", Hk), g("D", D), g("qs", S), g("ks", S),
+                                   g("qos", Hq * D), g("kos", Hk * D), g("eps", 1e-6),
+                                   g("il", 0), g("dt", BF16), g("wdt", BF16), None)
+
+    assert rope(dt=2) == E_DTYPE and rope(wdt=-1) == E_DTYPE
+    assert rope(D=63) == E_SHAPE and rope(D=0) == E_SHAPE and rope(T=-1) == E_SHAPE
+    assert rope(Hk=-1) == E_SHAPE and rope(P=-1) == E_SHAPE
+    assert rope(qs=Hq * D - 1) == E_SHAPE     # heads of a token wider than the stride
+    assert rope(kos=Hk * D - 8) == E_SHAPE
+    assert rope(eps=-1.0) == E_EPS and rope(eps=float("nan")) == E_EPS
+    # nothing to do: no launch, NULL pointers allowed
+    assert rope(T=0, q=None, k=None, qo=None, ko=None, pos=None, cos=None, sin=None) == OK
+    assert rope(Hq=0, Hk=0) == OK
+    assert rope(q=None) == E_NULL and rope(pos=None) == E_NULL and rope(cos=None) == E_NULL
+    assert rope(k=None) == E_NULL and rope(wk=None) == E_NULL and rope(ko=None) == E_NULL
+    # outputs overlapping an input other than their own, or each other
+    assert rope(qo=QKV + 2, qos=S) == E_ALIAS          # shifted view of q
+    assert rope(qo=KB, qos=S) == E_ALIAS               # query output over the key heads
+    assert rope(ko=QKV, kos=S) == E_ALIAS              # key output over the query heads
+    assert rope(ko=OUT + 64) == E_ALIAS                # key output inside the query output
+    assert rope(qo=COS) == E_ALIAS and rope(ko=POS - 16) == E_ALIAS
+    assert rope(qo=WQ - 8) == E_ALIAS

@@ -9,7 +9,10 @@ inspected with LLVM's readelf and objdump:
   per lane) streams rows with 128-bit non-temporal loads and stores and
   converts with the hardware bf16 instruction;
 - the FP8 forward converts with the hardware E4M3 instruction;
-- no kernel contains packed fp32 add/mul/fma (the build disables them).
+- the RMSNorm + RoPE kernel for bf16 heads of 128 streams each lane's two
+  vectors in and out with 128-bit non-temporal accesses;
+- no kernel contains packed fp32 add/mul/fma (the build disables them) or a
+  generic (flat) memory access.
 
 The vectorisation success sign the CuTe DSL skill page gives in Workflow 1
 (128-bit vector loads) is checked here on AMD code."""
@@ -28,6 +31,7 @@ MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 HEADLINE = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELb0ELi8ELi2EEEvNS_7FwdArgsE"
 FP8_FUSED = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELb1ELi8ELi2EEEvNS_7FwdArgsE"
+ROPE_D128 = "_ZN6addrms15rope_vec_kernelINS_6bf16_tES1_Li8ELb0ELi4EEEvNS_8RopeArgsE"
 
 
 def _tool(name):
@@ -138,10 +142,28 @@ def test_fp8_kernel_uses_hardware_e4m3_conversion(kernels):
     assert re.search(r"global_load_dwordx4 [^\n]* nt", asm)
 
 
-def test_no_packed_fp32_arithmetic(code_objects):
+def test_rope_kernel_streams_heads_non_temporal(kernels):
+    # bf16 heads of 128, 8 lanes per head, 4 heads per group and step (the
+    # default): two 16-byte vectors in and out per lane and head,
+    # non-temporal; tables and weights with the default policy
+    co, meta = kernels[ROPE_D128]
+    asm = _disasm(co, ROPE_D128)
+    loads = [l.split("//")[0].rstrip() for l in re.findall(r"global_load_dwordx4 [^\n]*", asm)]
+    stores = [l.split("//")[0].rstrip() for l in re.findall(r"global_store_dwordx4 [^\n]*", asm)]
+    assert sum(l.endswith(" nt") for l in loads) == 8, loads
+    assert len(stores) == 8 and all(l.endswith(" nt") for l in stores), stores
+    assert "v_cvt_pk_bf16_f32" in asm and "scratch_" not in asm
+    assert int(meta["vgpr_count"]) <= 168   # at least 3 waves per SIMD
+
+
+def test_no_packed_fp32_arithmetic_and_no_flat_memory_access(code_objects):
     if shutil.which(os.path.join(LLVM, "llvm-objdump")) is None:
         pytest.skip("llvm-objdump not available")
     for co in code_objects:
         asm = _disasm(co)
         hits = re.findall(r"v_pk_(?:add|mul|fma)_f32[^\n]*", asm)
         assert not hits, f"{co.name}: {hits[:3]}"
+        # every buffer is global memory: generic (flat) accesses would mean
+        # the compiler lost a pointer's address space
+        flat = re.findall(r"flat_(?:load|store|atomic)[^\n]*", asm)
+        assert not flat, f"{co.name}: {flat[:3]}"
