@@ -423,7 +423,8 @@ def secondary(steps: int):
         ar.rmsnorm_rope_qk(q, k, wq, wk, cos, sin, pos, c["eps"], q_out=q, k_out=k)
         i[0] += 1
 
-    _, ev = timed(rstep, steps, 5)
+    wall, ev = timed(rstep, steps, 5)
+    dev_s = graph_time(rstep, per_graph=30, replays=5)
     npos = int(torch.unique(inp["pos"]).numel())
     # heads read and written; positions; the table rows used (cos and sin,
     # D/2 floats each); both weight vectors
@@ -431,8 +432,11 @@ def secondary(steps: int):
     out[name] = {
         "GBps": round(nb * steps / ev / 1e9, 1),
         "pct_of_peak": round(100 * nb * steps / ev / 1e9 / HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
-        "note": "in place on packed qkv [16384, 48*128]; value heads untouched; 3 rotating sets"}
+        "us_per_call": round(ev / steps * 1e6, 2), "us_per_call_host": round(wall / steps * 1e6, 2),
+        "GBps_graph": round(nb / dev_s / 1e9, 1), "us_per_call_graph": round(dev_s * 1e6, 2),
+        "bytes": nb,
+        "note": "in place on packed qkv [16384, 48*128]; value heads untouched; 3 rotating sets; "
+                "_graph: device time from replaying captured calls"}
     del bufs, views
     # fused forward, 4096 x 4096 bf16 (134 MB: fits in the last-level cache; rotate 4 sets)
     inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_4096x4096")
