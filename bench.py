@@ -280,6 +280,30 @@ def cpu_baseline(inp, M: int, N: int, eps: float, target_s: float = 12.0):
                       f"{dt:.1f} s; rows/s {rows / dt:.0f}"}
 
 
+def cpu_baseline_all_cores(inp, M: int, N: int, eps: float, max_threads: int = 16):
+    """The same oracle, unchanged, run on disjoint slices of all M rows by one
+    host thread per available core (each slice is one call into the C
+    oracle, which releases the GIL), capped at max_threads."""
+    import concurrent.futures as cf
+    import oracle
+    x, r, w = inp["x"], inp["r"], inp["w"]
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    n = max(1, min(avail, max_threads))
+    bounds = [(k * M // n, (k + 1) * M // n) for k in range(n)]
+    log(f"cpu baseline: oracle on all {M} rows in {n} threads")
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(n) as ex:
+        list(ex.map(lambda b: oracle.add_rmsnorm_fwd(x[b[0]:b[1]], r[b[0]:b[1]], w, eps), bounds))
+    dt = time.perf_counter() - t0
+    nbytes = 8 * M * N + 2 * N
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"all {M} rows in {n} row slices, one pass, {dt:.2f} s; "
+                      f"rows/s {M / dt:.0f}; {avail} cores available"}
+
+
 def secondary(steps: int):
     """Backward, smaller forward shapes and decode latency, same protocol."""
     import torch
@@ -551,6 +575,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(h["inputs"], M, N, h["eps"])
+        rec["cpu_baseline_all_cores"] = cpu_baseline_all_cores(h["inputs"], M, N, h["eps"])
     del h
     if not args.only_headline:
         log("secondary figures")
