@@ -90,6 +90,12 @@ def _load():
         lib.oracle_add_rmsnorm_bwd.restype = i32
         lib.oracle_add_rmsnorm_bwd.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, vp, i32, vp,
                                                i32, vp, i64, i64]
+        lib.oracle_rmsnorm_fwd_fp8_grouped.restype = i32
+        lib.oracle_rmsnorm_fwd_fp8_grouped.argtypes = [vp, i32, vp, i32, vp, vp, i64, vp, i32, i64,
+                                                       i64, dbl]
+        lib.oracle_add_rmsnorm_fwd_fp8_grouped.restype = i32
+        lib.oracle_add_rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, i32, vp, i32, vp, vp, i64, vp,
+                                                           i32, vp, i32, i64, i64, dbl]
         lib.oracle_rmsnorm_rope.restype = i32
         lib.oracle_rmsnorm_rope.argtypes = [vp, i32, i64, vp, i32, vp, vp, vp, i64, vp, i32, i64,
                                             i64, i64, i64, i32, dbl]
@@ -314,27 +320,32 @@ def fp8e4m3_decode(codes) -> np.ndarray:
 
 
 def rmsnorm_fwd_fp8(x: torch.Tensor, w: torch.Tensor, eps: float, *, residual=None,
-                    eps_exact: bool = False):
-    """RMSNorm with an E4M3 output and per-row scale.  With residual=r, the
-    fused form: x + r is stored first and normalised.  Returns
-    (q uint8, scale float32, rstd float32) or, fused, (q, scale, residual_out, rstd)."""
+                    group: int = 0, eps_exact: bool = False):
+    """RMSNorm with an E4M3 output and dynamic scales: one per row (group=0)
+    or one per `group` consecutive columns (scale shape [M, ceil(N/group)]).
+    With residual=r, the fused form: x + r is stored first and normalised.
+    Returns (q uint8, scale float32, rstd float32) or, fused,
+    (q, scale, residual_out, rstd)."""
     x, w = _cpu(x), _cpu(w)
     N = x.shape[-1]
     M = x.numel() // N
+    g = max(0, int(group))
+    ng = (N + min(g, N) - 1) // min(g, N) if g else 0   # group >= N: one group per row
     q = torch.empty(x.shape, dtype=torch.uint8)
-    scale = torch.empty(x.shape[:-1], dtype=torch.float32)
+    scale = torch.empty(x.shape[:-1] + (ng,) if g else x.shape[:-1], dtype=torch.float32)
     rstd = torch.empty(x.shape[:-1], dtype=torch.float32)
     e = float(eps) if eps_exact else eps_as_float32(eps)
     if residual is None:
-        _check(_load().oracle_rmsnorm_fwd_fp8(_ptr(x), _code(x), _ptr(w), _code(w), _ptr(q),
-                                              _ptr(scale), _ptr(rstd), _code(rstd), M, N, e),
-               "rmsnorm_fwd_fp8")
+        _check(_load().oracle_rmsnorm_fwd_fp8_grouped(_ptr(x), _code(x), _ptr(w), _code(w),
+                                                      _ptr(q), _ptr(scale), g, _ptr(rstd),
+                                                      _code(rstd), M, N, e), "rmsnorm_fwd_fp8")
         return q, scale, rstd
     r = _cpu(residual)
     res = torch.empty(x.shape, dtype=x.dtype)
-    _check(_load().oracle_add_rmsnorm_fwd_fp8(_ptr(x), _ptr(r), _code(x), _ptr(w), _code(w),
-                                              _ptr(q), _ptr(scale), _ptr(res), _code(res),
-                                              _ptr(rstd), _code(rstd), M, N, e),
+    _check(_load().oracle_add_rmsnorm_fwd_fp8_grouped(_ptr(x), _ptr(r), _code(x), _ptr(w),
+                                                      _code(w), _ptr(q), _ptr(scale), g,
+                                                      _ptr(res), _code(res), _ptr(rstd),
+                                                      _code(rstd), M, N, e),
            "add_rmsnorm_fwd_fp8")
     return q, scale, res, rstd
 

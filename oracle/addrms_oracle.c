@@ -505,18 +505,22 @@ void oracle_fp8e4m3_encode_array(const double *v, uint8_t *out, int64_t n)
         out[i] = oracle_fp8e4m3_encode(v[i]);
 }
 
-/* RMSNorm with an E4M3 output and a dynamic per-row scale, for a downstream
- * FP8 GEMM.  Per row: y_j = h_j * rstd * w_j in binary64, rounded once to
- * binary32 (yf_j); amax = max_j |yf_j|; the quantisation decisions are then
- * taken in binary32, as the kernel takes them:
+/* RMSNorm with an E4M3 output and dynamic scales, for a downstream FP8 GEMM.
+ * The scales are per group of `group` consecutive columns of a row (the last
+ * group of a row may be shorter); group <= 0 means one group per row.  Per
+ * row: y_j = h_j * rstd * w_j in binary64, rounded once to binary32 (yf_j);
+ * per group: amax = max |yf_j| over the group's columns; the quantisation
+ * decisions are then taken in binary32, as the kernel takes them:
  *     inv = 448 / amax,  scale = amax / 448   (binary32 divisions)
  *     q_j = E4M3(yf_j * inv)                  (binary32 product, encoded)
- * with inv = scale = 1 for a row with no non-zero finite |yf| (NaNs are
- * ignored by the maximum and encode as NaN).  y_j ~= decode(q_j) * scale. */
+ * with inv = scale = 1 for a group with no non-zero finite |yf| (NaNs are
+ * ignored by the maximum and encode as NaN).  y_j ~= decode(q_j) * scale of
+ * its group.  scale is [M][ceil(N / group)], row-major. */
 static size_t elem_size(int dt) { return dt == OR_F32 ? 4 : dt == OR_BF16 ? 2 : 8; }
 
-int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
-                           float *scale, void *rstd, int rstd_dt, int64_t M, int64_t N, double eps)
+int oracle_rmsnorm_fwd_fp8_grouped(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
+                                   float *scale, int64_t group, void *rstd, int rstd_dt,
+                                   int64_t M, int64_t N, double eps)
 {
     double *y;
     float *yf;
@@ -525,6 +529,9 @@ int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uin
         return OR_ERR_ARG;
     if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || (rstd && !dtype_ok(rstd_dt)))
         return OR_ERR_ARG;
+    if (group <= 0 || group > N)
+        group = N;
+    const int64_t ngroups = (N + group - 1) / group;
     y = (double *)malloc((size_t)N * sizeof(double));
     yf = (float *)malloc((size_t)N * sizeof(float));
     if (!y || !yf) {
@@ -537,22 +544,26 @@ int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uin
         const void *xi = (const char *)x + (size_t)(i * N) * elem_size(x_dt);
         void *ri = rstd ? (void *)((char *)rstd + (size_t)i * elem_size(rstd_dt)) : NULL;
         oracle_rmsnorm_fwd(xi, x_dt, w, w_dt, y, OR_F64, ri, rstd_dt, 1, N, eps);
-        float amax = 0.0f;
-        for (int64_t j = 0; j < N; j++) {
+        for (int64_t j = 0; j < N; j++)
             yf[j] = (float)y[j];
-            float m = fabsf(yf[j]);
-            if (m > amax) /* NaN never compares greater: NaNs do not set the scale */
-                amax = m;
-        }
-        float inv = 1.0f, sc = 1.0f;
-        if (amax != 0.0f) {
-            inv = 448.0f / amax;
-            sc = amax / 448.0f;
-        }
-        scale[i] = sc;
-        for (int64_t j = 0; j < N; j++) {
-            float v = yf[j] * inv;
-            q[i * N + j] = oracle_fp8e4m3_encode((double)v);
+        for (int64_t g = 0; g < ngroups; g++) {
+            const int64_t j0 = g * group, j1 = j0 + group < N ? j0 + group : N;
+            float amax = 0.0f;
+            for (int64_t j = j0; j < j1; j++) {
+                float m = fabsf(yf[j]);
+                if (m > amax) /* NaN never compares greater: NaNs do not set the scale */
+                    amax = m;
+            }
+            float inv = 1.0f, sc = 1.0f;
+            if (amax != 0.0f) {
+                inv = 448.0f / amax;
+                sc = amax / 448.0f;
+            }
+            scale[i * ngroups + g] = sc;
+            for (int64_t j = j0; j < j1; j++) {
+                float v = yf[j] * inv;
+                q[i * N + j] = oracle_fp8e4m3_encode((double)v);
+            }
         }
     }
     free(y);
@@ -560,11 +571,20 @@ int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uin
     return OR_OK;
 }
 
+/* One scale per row: the grouped form with a single group per row. */
+int oracle_rmsnorm_fwd_fp8(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
+                           float *scale, void *rstd, int rstd_dt, int64_t M, int64_t N, double eps)
+{
+    return oracle_rmsnorm_fwd_fp8_grouped(x, x_dt, w, w_dt, q, scale, 0, rstd, rstd_dt, M, N, eps);
+}
+
 /* Fused residual-Add + RMSNorm with the E4M3 output: the residual as in
- * oracle_add_rmsnorm_fwd, then oracle_rmsnorm_fwd_fp8 of the stored residual. */
-int oracle_add_rmsnorm_fwd_fp8(const void *x, const void *r, int in_dt, const void *w, int w_dt,
-                               uint8_t *q, float *scale, void *res, int res_dt, void *rstd,
-                               int rstd_dt, int64_t M, int64_t N, double eps)
+ * oracle_add_rmsnorm_fwd, then oracle_rmsnorm_fwd_fp8_grouped of the stored
+ * residual (group <= 0: one scale per row). */
+int oracle_add_rmsnorm_fwd_fp8_grouped(const void *x, const void *r, int in_dt, const void *w,
+                                       int w_dt, uint8_t *q, float *scale, int64_t group,
+                                       void *res, int res_dt, void *rstd, int rstd_dt, int64_t M,
+                                       int64_t N, double eps)
 {
     if (!x || !r || !res || M < 0 || N <= 0)
         return OR_ERR_ARG;
@@ -577,7 +597,16 @@ int oracle_add_rmsnorm_fwd_fp8(const void *x, const void *r, int in_dt, const vo
         store_elem(res, res_dt, k, in_dt == OR_F64 ? load_elem(x, in_dt, k) + load_elem(r, in_dt, k)
                                                    : (double)s32);
     }
-    return oracle_rmsnorm_fwd_fp8(res, res_dt, w, w_dt, q, scale, rstd, rstd_dt, M, N, eps);
+    return oracle_rmsnorm_fwd_fp8_grouped(res, res_dt, w, w_dt, q, scale, group, rstd, rstd_dt, M,
+                                          N, eps);
+}
+
+int oracle_add_rmsnorm_fwd_fp8(const void *x, const void *r, int in_dt, const void *w, int w_dt,
+                               uint8_t *q, float *scale, void *res, int res_dt, void *rstd,
+                               int rstd_dt, int64_t M, int64_t N, double eps)
+{
+    return oracle_add_rmsnorm_fwd_fp8_grouped(x, r, in_dt, w, w_dt, q, scale, 0, res, res_dt,
+                                              rstd, rstd_dt, M, N, eps);
 }
 
 /* ---- per-head RMSNorm followed by RoPE ------------------------------------ */

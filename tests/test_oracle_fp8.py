@@ -123,3 +123,79 @@ def test_special_rows():
     assert scale[0].item() == 1.0 and torch.all(q[0] == 0)
     assert scale[1].item() == 1.0 and torch.all((q[1] & 0x7F) == 0x7F)   # NaN row
     assert torch.all(q[2] == 0x7E)                                       # constant row: all amax
+
+
+# ---- one scale per group of columns -----------------------------------------
+
+def test_group_of_the_whole_row_is_the_per_row_scale():
+    M, N = 16, 300
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=301)
+    q0, s0, _ = oracle.rmsnorm_fwd_fp8(inp["x"], inp["w"], 1e-6)
+    for g in (N, N + 5):
+        q1, s1, _ = oracle.rmsnorm_fwd_fp8(inp["x"], inp["w"], 1e-6, group=g)
+        assert torch.equal(q0, q1) and torch.equal(s0, s1.reshape(M))
+
+
+def test_constant_groups_have_closed_form_scales():
+    # one row: 128 columns of a, 128 of b, a ragged last group of 44 columns of c
+    a, b, c = 3.0, -0.25, 40.0
+    x = torch.tensor([[a] * 128 + [b] * 128 + [c] * 44], dtype=torch.float64)
+    w = torch.ones(300, dtype=torch.float64)
+    q, s, rstd = oracle.rmsnorm_fwd_fp8(x, w, 0.0, group=128, eps_exact=True)
+    assert s.shape == (1, 3)
+    rs = 1.0 / np.sqrt((128 * a * a + 128 * b * b + 44 * c * c) / 300)
+    for k, v in enumerate((a, b, c)):
+        yf = np.float32(v * rs)
+        assert s[0, k].item() == np.float32(np.abs(yf) / np.float32(448.0))
+    # every value is its group's maximum: the codes are +-448
+    qn = q.numpy()[0]
+    assert np.all(qn[:128] == 0x7E) and np.all(qn[128:256] == 0xFE) and np.all(qn[256:] == 0x7E)
+
+
+def test_groups_of_one_column():
+    M, N = 3, 64
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.float32, seed=303)
+    x = inp["x"].clone()
+    x[1, 7] = 0.0
+    q, s, _ = oracle.rmsnorm_fwd_fp8(x, inp["w"], 1e-6, group=1)
+    y, _ = oracle.rmsnorm_fwd(x, inp["w"], 1e-6, y_dtype=torch.float64)
+    yf = y.numpy().astype(np.float32)
+    np.testing.assert_array_equal(s.numpy(), np.where(yf == 0, np.float32(1),
+                                                      np.abs(yf) / np.float32(448)))
+    qn = q.numpy()
+    assert qn[1, 7] == 0
+    nz = yf != 0
+    assert np.all((qn[nz] & 0x7F) == 0x7E) and np.all((qn[nz] >> 7) == (yf[nz] < 0))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("N,group", [(1000, 128), (7168, 128), (300, 32)])
+def test_grouped_quantisation(fused, N, group):
+    M = 24
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=N + group)
+    x, r, w = inp["x"], inp["r"], inp["w"]
+    if fused:
+        q, scale, res, _ = oracle.rmsnorm_fwd_fp8(x, w, 1e-6, residual=r, group=group)
+        _, res_ref, _ = oracle.add_rmsnorm_fwd(x, r, w, 1e-6)
+        assert torch.equal(res.view(torch.int16), res_ref.view(torch.int16))
+        y64, _ = oracle.rmsnorm_fwd(res, w, 1e-6, y_dtype=torch.float64)
+    else:
+        q, scale, _ = oracle.rmsnorm_fwd_fp8(x, w, 1e-6, group=group)
+        y64, _ = oracle.rmsnorm_fwd(x, w, 1e-6, y_dtype=torch.float64)
+    ng = (N + group - 1) // group
+    assert scale.shape == (M, ng)
+    y = y64.numpy()
+    s = scale.numpy().astype(np.float64)
+    cols = np.arange(N) // group
+    sg = s[:, cols]                                   # each element's own scale
+    qn = q.numpy()
+    for g in range(ng):
+        blk = slice(g * group, min(N, (g + 1) * group))
+        amax = np.abs(y[:, blk]).max(axis=1)
+        np.testing.assert_allclose(s[:, g] * 448.0, amax, rtol=1e-6)
+        # the group's largest value encodes as +-448
+        assert np.all((qn[:, blk] & 0x7F).max(axis=1) == 0x7E)
+    deq = oracle.fp8e4m3_decode(qn) * sg
+    mag = np.abs(y) / sg
+    step = np.where(mag < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-30))) - 3))
+    assert np.all(np.abs(deq - y) <= (0.5 * step * (1 + 1e-6) + 1e-6 * mag) * sg)

@@ -75,6 +75,11 @@ MUTANTS.update({
     "fp8_no_saturation": ("return (uint8_t)(sign | 0x7Eu); /* 448", "return (uint8_t)(sign | 0x7Fu); /* 448"),
     "fp8_scale_inverted": ("sc = amax / 448.0f;", "sc = 448.0f / amax;"),
     "fp8_quantises_unscaled": ("float v = yf[j] * inv;", "float v = yf[j];"),
+    "fp8_group_is_whole_row": ("const int64_t j0 = g * group, j1 = j0 + group < N ? j0 + group : N;",
+                               "const int64_t j0 = g * group, j1 = N;"),
+    "fp8_group_scale_index": ("scale[i * ngroups + g] = sc;", "scale[i + g] = sc;"),
+    "fp8_group_amax_from_row_start": ("for (int64_t j = j0; j < j1; j++) {\n                float m",
+                                      "for (int64_t j = 0; j < j1; j++) {\n                float m"),
     "rope_first_sign": ("store_elem(y, y_dt, yo + ja, a * c - b * s);",
                         "store_elem(y, y_dt, yo + ja, a * c + b * s);"),
     "rope_second_sign": ("store_elem(y, y_dt, yo + jb, b * c + a * s);",
