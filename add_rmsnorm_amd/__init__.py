@@ -76,6 +76,11 @@ def _load():
     lib.add_layernorm_bwd.restype = i32
     lib.add_layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32,
                                       i32, vp]
+    lib.rmsnorm_fwd_fp8_grouped.restype = i32
+    lib.rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, vp, vp, i64, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd_fp8_grouped.restype = i32
+    lib.add_rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, f32,
+                                                i32, i32, vp]
     lib.rmsnorm_rope_qk.restype = i32
     lib.rmsnorm_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
                                     i64, i64, i64, i64, f32, i32, i32, i32, vp]
@@ -413,7 +418,12 @@ def add_layernorm_bwd(dy: torch.Tensor, dres, h: torch.Tensor, w: torch.Tensor,
 _FP8 = getattr(torch, "float8_e4m3fn", None)
 
 
-def _fp8_out(x, y_fp8, y_scale):
+def _fp8_out(x, y_fp8, y_scale, group=None):
+    """Output buffers of the FP8 variants: codes like x; scales [..] (one per
+    row) or, with a group, [.., ceil(N / group)]."""
+    N = x.shape[-1]
+    sshape = x.shape[:-1] if group is None else x.shape[:-1] + ((N + min(group, N) - 1) //
+                                                                min(group, N),)
     if y_fp8 is None:
         y_fp8 = torch.empty(x.shape, dtype=_FP8 if _FP8 is not None else torch.uint8,
                             device=x.device)
@@ -422,50 +432,73 @@ def _fp8_out(x, y_fp8, y_scale):
         if y_fp8.element_size() != 1:
             raise TypeError("y_fp8 must have 1-byte elements (float8_e4m3fn or uint8)")
     if y_scale is None:
-        y_scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        y_scale = torch.empty(sshape, dtype=torch.float32, device=x.device)
     else:
-        _dev(y_scale, "y_scale", torch.float32, x.shape[:-1])
+        _dev(y_scale, "y_scale", torch.float32, sshape)
     return y_fp8, y_scale
 
 
-def rmsnorm_fwd_fp8(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, y_fp8=None,
-                    y_scale=None, rstd=None):
-    """RMSNorm with an OCP E4M3 output (torch.float8_e4m3fn) and a dynamic
-    per-row float32 scale: y ~= y_fp8.float() * y_scale[..., None].
+def _group(group):
+    if group is None:
+        return None
+    g = int(group)
+    if g < 1:
+        raise ValueError(f"group must be >= 1, got {group}")
+    return g
+
+
+def rmsnorm_fwd_fp8(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, group=None,
+                    y_fp8=None, y_scale=None, rstd=None):
+    """RMSNorm with an OCP E4M3 output (torch.float8_e4m3fn) and dynamic
+    float32 scales: one per row (y ~= y_fp8.float() * y_scale[..., None]) or,
+    with group=G, one per G consecutive columns (y_scale [..., ceil(N/G)]).
     Returns (y_fp8, y_scale)."""
     _dev(x, "x")
     M, N = _rows(x)
     _dev(w, "w", shape=(N,))
-    y_fp8, y_scale = _fp8_out(x, y_fp8, y_scale)
+    g = _group(group)
+    y_fp8, y_scale = _fp8_out(x, y_fp8, y_scale, g)
     if rstd is not None:
         _dev(rstd, "rstd", torch.float32, x.shape[:-1])
     dev = x.get_device()
     with _OnDevice(dev):
-        st = _lib.rmsnorm_fwd_fp8(_p(x), _p(w), _p(y_fp8), _p(y_scale), _p(rstd), M, N,
-                                  float(eps), _code(x, "x"), _code(w, "w"), _stream(dev))
+        if g is None:
+            st = _lib.rmsnorm_fwd_fp8(_p(x), _p(w), _p(y_fp8), _p(y_scale), _p(rstd), M, N,
+                                      float(eps), _code(x, "x"), _code(w, "w"), _stream(dev))
+        else:
+            st = _lib.rmsnorm_fwd_fp8_grouped(_p(x), _p(w), _p(y_fp8), _p(y_scale), g, _p(rstd),
+                                              M, N, float(eps), _code(x, "x"), _code(w, "w"),
+                                              _stream(dev))
     if st != 0:
         raise AddRmsError(st, "rmsnorm_fwd_fp8")
     return y_fp8, y_scale
 
 
 def add_rmsnorm_fwd_fp8(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
-                        *, y_fp8=None, y_scale=None, residual_out=None, rstd=None):
-    """Fused residual add + RMSNorm with an E4M3 output and per-row scale.
+                        *, group=None, y_fp8=None, y_scale=None, residual_out=None, rstd=None):
+    """Fused residual add + RMSNorm with an E4M3 output and dynamic scales (per
+    row, or per `group` columns as rmsnorm_fwd_fp8).
     Returns (y_fp8, y_scale, residual_out)."""
     _dev(x, "x")
     M, N = _rows(x)
     _dev(r, "r", x.dtype, x.shape)
     _dev(w, "w", shape=(N,))
-    y_fp8, y_scale = _fp8_out(x, y_fp8, y_scale)
+    g = _group(group)
+    y_fp8, y_scale = _fp8_out(x, y_fp8, y_scale, g)
     residual_out = (torch.empty_like(x) if residual_out is None
                     else _dev(residual_out, "residual_out", x.dtype, x.shape))
     if rstd is not None:
         _dev(rstd, "rstd", torch.float32, x.shape[:-1])
     dev = x.get_device()
     with _OnDevice(dev):
-        st = _lib.add_rmsnorm_fwd_fp8(_p(x), _p(r), _p(w), _p(y_fp8), _p(y_scale),
-                                      _p(residual_out), _p(rstd), M, N, float(eps),
-                                      _code(x, "x"), _code(w, "w"), _stream(dev))
+        if g is None:
+            st = _lib.add_rmsnorm_fwd_fp8(_p(x), _p(r), _p(w), _p(y_fp8), _p(y_scale),
+                                          _p(residual_out), _p(rstd), M, N, float(eps),
+                                          _code(x, "x"), _code(w, "w"), _stream(dev))
+        else:
+            st = _lib.add_rmsnorm_fwd_fp8_grouped(_p(x), _p(r), _p(w), _p(y_fp8), _p(y_scale), g,
+                                                  _p(residual_out), _p(rstd), M, N, float(eps),
+                                                  _code(x, "x"), _code(w, "w"), _stream(dev))
     if st != 0:
         raise AddRmsError(st, "add_rmsnorm_fwd_fp8")
     return y_fp8, y_scale, residual_out

@@ -319,7 +319,8 @@ int colreduce(const void *workspace, int P, int N, float *dw, hipStream_t s)
 
 int fwd_common(int norm, const void *x, const void *r, const void *w, const void *b, void *y,
                void *res, float *mean, float *rstd, int64_t M, int64_t N, float eps, int dtype,
-               int w_dtype, void *stream, bool fused, uint8_t *q = nullptr, float *qscale = nullptr)
+               int w_dtype, void *stream, bool fused, uint8_t *q = nullptr, float *qscale = nullptr,
+               int64_t qgroup = 0)
 {
     // ---- validation (no HIP call) ----
     // With M == 0 the matrices are empty and may be NULL.  The FP8 variant
@@ -339,7 +340,14 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     const size_t mat = (size_t)M * (size_t)N * esize(dtype);
     const Span sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype));
     const Span sy = span(y, q8 ? (size_t)M * (size_t)N : mat);
-    const Span sqs = q8 ? span(qscale, (size_t)M * 4u) : Span{};
+    // FP8 scales: one per row (qgroup == 0, or a group spanning the row), else
+    // one per group of qgroup columns
+    if (qgroup < 0)
+        return ADDRMS_ERR_SHAPE;
+    if (qgroup >= N)
+        qgroup = 0;
+    const int64_t ngroups = qgroup > 0 ? (N + qgroup - 1) / qgroup : 1;
+    const Span sqs = q8 ? span(qscale, (size_t)M * (size_t)ngroups * 4u) : Span{};
     const Span sr = fused ? span(r, mat) : Span{}, sres = fused ? span(res, mat) : Span{};
     const Span srs = rstd ? span(rstd, (size_t)M * 4u) : Span{};
     const Span sb = b ? span(b, (size_t)N * esize(w_dtype)) : Span{};
@@ -375,17 +383,30 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     const int c = combo(dtype, w_dtype);
     const FwdTable &tab = fwd_table(c);
     FwdArgs a{x, fused ? r : x, w, b, y, fused ? res : y, mean, rstd, q, qscale, M, (int)N, 0, eps};
+    a.qgroup = (int)qgroup;
+    a.qgroups = (int)ngroups;
 
     const int nv = vec_elems(dtype);
+    // grouped scales on the vector path: a group is a power of two of whole
+    // vectors, at most one wave wide
+    int qlanes = 0;
+    if (qgroup > 0 && qgroup % nv == 0) {
+        const int64_t L = qgroup / nv;
+        if (L <= 64 && (L & (L - 1)) == 0)
+            qlanes = (int)L;
+    }
+    a.qlanes = qlanes;
     const bool y_ok = q8 ? (reinterpret_cast<uintptr_t>(q) % (uintptr_t)nv) == 0 : aligned16(y);
     const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(x) &&
                         aligned16(w) && y_ok && (!b || aligned16(b)) &&
-                        (!fused || (aligned16(r) && aligned16(res)));
+                        (!fused || (aligned16(r) && aligned16(res))) &&
+                        (qgroup == 0 || qlanes > 0);
     int cus = 0;
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
         return rc;
     int wi = 0, vi = 0;
-    if (vec_ok && pick_fwd(M, (int)(N / nv), cus, &wi, &vi)) {
+    if (vec_ok && pick_fwd(M, (int)(N / nv), cus, &wi, &vi) &&
+        (qlanes == 0 || kVplList[vi] <= kQGroupMaxVpl)) {
         a.nvec = (int)(N / nv);
         const KernelRef &k = q8 ? tab.vec_q8[fused ? 1 : 0][wi][vi] : tab.vec[norm][fused ? 1 : 0][wi][vi];
         const int rpb = kWprList[wi] == 1 ? 4 : 1;
@@ -698,6 +719,31 @@ int add_rmsnorm_fwd_fp8(const void *x, const void *r, const void *w, void *y_fp8
         return ADDRMS_ERR_NULL;
     return fwd_common(kRms, x, r, w, nullptr, nullptr, residual_out, nullptr, rstd, M, N, eps,
                       dtype, w_dtype, stream, true, static_cast<uint8_t *>(y_fp8), y_scale);
+}
+
+int rmsnorm_fwd_fp8_grouped(const void *x, const void *w, void *y_fp8, float *y_scale,
+                            int64_t group, float *rstd, int64_t M, int64_t N, float eps, int dtype,
+                            int w_dtype, void *stream)
+{
+    if (M != 0 && (!y_fp8 || !y_scale))
+        return ADDRMS_ERR_NULL;
+    if (group < 1)
+        return ADDRMS_ERR_SHAPE;
+    return fwd_common(kRms, x, nullptr, w, nullptr, nullptr, nullptr, nullptr, rstd, M, N, eps,
+                      dtype, w_dtype, stream, false, static_cast<uint8_t *>(y_fp8), y_scale, group);
+}
+
+int add_rmsnorm_fwd_fp8_grouped(const void *x, const void *r, const void *w, void *y_fp8,
+                                float *y_scale, int64_t group, void *residual_out, float *rstd,
+                                int64_t M, int64_t N, float eps, int dtype, int w_dtype,
+                                void *stream)
+{
+    if (M != 0 && (!y_fp8 || !y_scale))
+        return ADDRMS_ERR_NULL;
+    if (group < 1)
+        return ADDRMS_ERR_SHAPE;
+    return fwd_common(kRms, x, r, w, nullptr, nullptr, residual_out, nullptr, rstd, M, N, eps,
+                      dtype, w_dtype, stream, true, static_cast<uint8_t *>(y_fp8), y_scale, group);
 }
 
 int layernorm_fwd(const void *x, const void *w, const void *b, void *y, float *mean, float *rstd,

@@ -250,6 +250,24 @@ template <int CTRL> __device__ __forceinline__ float dpp_f32(float v)
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// Maximum over each aligned group of L lanes (L a power of two up to 64, the
+// same for the whole wave); every lane of a group gets the group's maximum.
+// The DPP steps of wave_max within 16-lane rows, then lane shuffles by 16 and
+// 32.  Every lane of a group must be active.
+__device__ __forceinline__ float group_max(float v, int L)
+{
+    // every step runs and its result is selected (no branches, so no exec
+    // masks to keep across a caller's unrolled loop)
+    v = __builtin_fmaxf(v, L >= 2 ? dpp_f32<0xB1>(v) : v);
+    v = __builtin_fmaxf(v, L >= 4 ? dpp_f32<0x4E>(v) : v);
+    v = __builtin_fmaxf(v, L >= 8 ? dpp_f32<0x141>(v) : v);
+    v = __builtin_fmaxf(v, L >= 16 ? dpp_f32<0x140>(v) : v);
+    const float t16 = __shfl_xor(v, 16);
+    v = __builtin_fmaxf(v, L >= 32 ? t16 : v);
+    const float t32 = __shfl_xor(v, 32);
+    return __builtin_fmaxf(v, L >= 64 ? t32 : v);
+}
+
 // The same sum for doubles (each DPP step moves both 32-bit halves).
 template <int CTRL> __device__ __forceinline__ double dpp_f64(double v)
 {

@@ -19,11 +19,17 @@ struct FwdArgs {
     float *mean; // LayerNorm only; may be null
     float *rstd; // may be null
     uint8_t *q;     // FP8 output variant: E4M3 codes [M, N]
-    float *qscale;  // FP8 output variant: per-row scale [M]
+    float *qscale;  // FP8 output variant: scales [M] or [M, qgroups]
     int64_t M;
     int N;
     int nvec; // 16-byte vectors per row (vector path)
     float eps;
+    // FP8 scale groups: qgroup = columns per scale (0: one scale per row),
+    // qgroups = scales per row, qlanes = lanes per group on the vector path
+    // (qgroup / values per vector, a power of two up to 64).
+    int qgroup;
+    int qgroups;
+    int qlanes;
 };
 
 // Per-head RMSNorm + RoPE arguments.  Head h of token t is the D contiguous
@@ -84,6 +90,10 @@ constexpr int kBlockFwd(int wpr) { return wpr == 1 ? 256 : 64 * wpr; }
 // Forward (WPR, VPL) pairs that are built: 512- and 1024-thread blocks get at
 // most 256 / 128 VGPRs per lane, so they only take rows short enough per lane
 // to stay in registers.
+// Grouped FP8 scales on the vector path: compiled for at most this many
+// vectors per lane (more would spill registers); longer rows take the
+// element-wise path.
+constexpr int kQGroupMaxVpl = 4;
 constexpr bool fwd_built(int wpr, int vpl)
 {
     return wpr <= 4 || (wpr == 8 && vpl <= 8) || (wpr == 16 && vpl <= 4);

@@ -67,9 +67,11 @@ __device__ __forceinline__ double fma_ct(double a, double b, double c) { return 
 // NORM = kLayer: y = (h - mean) * rstd * w (+ b), rstd = 1/sqrt(var + eps),
 // the variance taken about the mean from the registers (two passes over the
 // row, one over memory).
-// Q8 (RMSNorm only): y is not stored; instead its row absmax sets a per-row
-// scale (scale = amax/448, inv = 448/amax, binary32) and y * inv is written as
-// OCP E4M3 codes, one byte per element, for a downstream FP8 GEMM.
+// Q8 (RMSNorm only): y is not stored; instead its absmax sets a scale
+// (scale = amax/448, inv = 448/amax, binary32), per row or, with a.qlanes > 0,
+// per group of a.qlanes consecutive vectors (a group maximum over that many
+// lanes), and y * inv is written as OCP E4M3 codes, one byte per element, for
+// a downstream FP8 GEMM.
 // ---------------------------------------------------------------------------
 template <typename T, typename WT, int NORM, bool FUSED, bool Q8, int WPR, int VPL>
 __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
@@ -213,18 +215,45 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
                     am = __builtin_fmaxf(am, __builtin_fabsf(o[k][e]));
                 }
             }
-            am = row_max(am, slot + 1);
-            float inv = 1.0f, sc = 1.0f;
-            if (am != 0.0f) {
-                inv = 448.0f / am;
-                sc = am / 448.0f;
+            // one scale per row, or (qlanes > 0) one per group of qlanes
+            // consecutive vectors, which sit in qlanes consecutive lanes
+            float inv_k[VPL];
+            if (VPL > kQGroupMaxVpl || a.qlanes == 0) {
+                am = row_max(am, slot + 1);
+                float inv = 1.0f, sc = 1.0f;
+                if (am != 0.0f) {
+                    inv = 448.0f / am;
+                    sc = am / 448.0f;
+                }
+                if (wir == 0 && lane == 0)
+                    a.qscale[row] = sc;
+#pragma unroll
+                for (int k = 0; k < VPL; ++k)
+                    inv_k[k] = inv;
+            } else if constexpr (VPL <= kQGroupMaxVpl) {
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) {
+                    const int v = vbase + k * VSTRIDE;
+                    float g = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < NV; ++e)
+                        g = __builtin_fmaxf(g, __builtin_fabsf(o[k][e]));
+                    g = group_max(g, a.qlanes);
+                    float inv = 1.0f, sc = 1.0f;
+                    if (g != 0.0f) {
+                        inv = 448.0f / g;
+                        sc = g / 448.0f;
+                    }
+                    if (v < nvec && (lane & (a.qlanes - 1)) == 0)
+                        a.qscale[(size_t)row * (size_t)a.qgroups + (size_t)(v / a.qlanes)] = sc;
+                    inv_k[k] = inv;
+                }
             }
-            if (wir == 0 && lane == 0)
-                a.qscale[row] = sc;
             uint8_t *qrow = a.q + base;
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 const int v = vbase + k * VSTRIDE;
+                const float inv = inv_k[k];
                 if (v < nvec) {
                     uint32_t wd[NV / 4];
 #pragma unroll
@@ -341,6 +370,29 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
         if (a.rstd != nullptr && tid == 0)
             a.rstd[row] = rs;
         if constexpr (Q8) {
+            if (a.qgroup > 0) {
+                // one scale per group of qgroup columns: each thread takes
+                // whole groups
+                const int G = a.qgroup;
+                for (int g = tid; g < a.qgroups; g += 256) {
+                    const int j0 = g * G, j1 = j0 + G < N ? j0 + G : N;
+                    float am = 0.0f;
+                    for (int j = j0; j < j1; ++j)
+                        am = __builtin_fmaxf(am, __builtin_fabsf((ld_elem<T>(src, base + j) * rs) *
+                                                                 ld_elem<WT>(a.w, j)));
+                    float inv = 1.0f, sc = 1.0f;
+                    if (am != 0.0f) {
+                        inv = 448.0f / am;
+                        sc = am / 448.0f;
+                    }
+                    a.qscale[row * (int64_t)a.qgroups + g] = sc;
+                    for (int j = j0; j < j1; ++j) {
+                        const float o = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
+                        a.q[base + j] = (uint8_t)pack_e4m3x2(e4m3_clamp(o * inv), 0.0f);
+                    }
+                }
+                continue;
+            }
             float am = 0.0f;
             for (int j = tid; j < N; j += 256)
                 am = __builtin_fmaxf(am, __builtin_fabsf((ld_elem<T>(src, base + j) * rs) *

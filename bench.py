@@ -383,7 +383,23 @@ def secondary(steps: int):
                                                                        HBM_PEAK_GBPS, 1),
         "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
         "note": "bf16 x, r in; bf16 residual_out + E4M3 y + fp32 per-row scale out"}
-    del sets
+    # the same with one scale per 128 columns of a row
+    sg = [torch.empty(M, N // 128, device="cuda") for _ in range(2)]
+
+    def f8g():
+        x, r, q, _, res = sets[i[0] & 1]
+        ar.add_rmsnorm_fwd_fp8(x, r, w, 1e-6, group=128, y_fp8=q, y_scale=sg[i[0] & 1],
+                               residual_out=res)
+        i[0] += 1
+
+    _, ev = timed(f8g, steps, 5)
+    nb = 7 * M * N + 4 * M * (N // 128) + 2 * N
+    out["add_rmsnorm_fwd_fp8_g128_16384x7168"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
+                                                                       HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
+        "note": "as above with one fp32 scale per 128 columns (56 per row)"}
+    del sets, sg
     # LayerNorm: fused forward with bias at the headline shape, backward (dw, db)
     # at the backward workload's shape
     M, N = 16384, 7168

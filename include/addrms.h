@@ -171,6 +171,29 @@ int add_rmsnorm_fwd_fp8(const void *x, const void *r, const void *w, void *y_fp8
                         int dtype, int w_dtype, void *stream);
 
 /*
+ * The same with one scale per group of `group` consecutive columns of a row
+ * (per-block scales for an FP8 GEMM that scales activations per token and
+ * per channel block, e.g. group = 128); the last group of a row may be
+ * shorter.  For row i and group g (columns g*group .. min(N, (g+1)*group)-1):
+ *     amax_ig = max |y_ij| over the group (NaNs ignored)
+ *     scale_ig = amax_ig / 448,  inv_ig = 448 / amax_ig  (1 and 1 when 0)
+ *     q_ij = E4M3(clamp(y_ij * inv_ig, -448, 448))
+ *   y_scale  [M][ceil(N / group)]  float32  output, row-major
+ * group >= 1 (ADDRMS_ERR_SHAPE otherwise); group >= N gives one scale per
+ * row, as rmsnorm_fwd_fp8.  The vector path takes groups of a power of two
+ * of 16-byte vectors up to 64 (bf16: 8 .. 512 columns; float32: 4 .. 256);
+ * other group sizes take the element-wise path with the same results.
+ */
+int rmsnorm_fwd_fp8_grouped(const void *x, const void *w, void *y_fp8, float *y_scale,
+                            int64_t group, float *rstd, int64_t M, int64_t N, float eps, int dtype,
+                            int w_dtype, void *stream);
+
+int add_rmsnorm_fwd_fp8_grouped(const void *x, const void *r, const void *w, void *y_fp8,
+                                float *y_scale, int64_t group, void *residual_out, float *rstd,
+                                int64_t M, int64_t N, float eps, int dtype, int w_dtype,
+                                void *stream);
+
+/*
  * LayerNorm variants.  The "CuTe DSL" skill page lists a CTA-level LayerNorm
  * example (Workflow 0, example index) and names LayerNorm beside RMSNorm in
  * its float32 reduction pattern (Workflow 0); the formula is the textbook one

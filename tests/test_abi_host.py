@@ -42,6 +42,9 @@ def lib():
     lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.add_rmsnorm_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, vp, vp, i64, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, f32,
+                                                i32, i32, vp]
     lib.rmsnorm_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
                                     i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
@@ -54,7 +57,8 @@ def test_header_declares_the_entry_points():
                                   "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
                                   "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
                                   "layernorm_bwd_workspace_bytes", "add_layernorm_bwd",
-                                  "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8", "rmsnorm_rope_qk",
+                                  "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_fp8_grouped",
+                                  "add_rmsnorm_fwd_fp8_grouped", "rmsnorm_rope_qk",
                                   "addrms_status_str", "addrms_last_hip_error"])
 
 
@@ -259,3 +263,20 @@ def test_rope_validation(lib):
     assert rope(ko=OUT + 64) == E_ALIAS                # key output inside the query output
     assert rope(qo=COS) == E_ALIAS and rope(ko=POS - 16) == E_ALIAS
     assert rope(qo=WQ - 8) == E_ALIAS
+
+
+def test_fp8_grouped_validation(lib):
+    Q, S = 0x78000000, 0x7C000000
+    f = lambda **k: lib.rmsnorm_fwd_fp8_grouped(A, W, k.get("q", Q), k.get("s", S),
+                                                k.get("g", 128), None, k.get("M", 4),
+                                                k.get("N", 64), 1e-6, BF16, BF16, None)
+    assert f(g=0) == E_SHAPE and f(g=-128) == E_SHAPE
+    assert f(q=None) == E_NULL and f(s=None) == E_NULL
+    assert f(M=0, q=None, s=None) == OK and f(M=0) == OK
+    # 4 rows x ceil(64 / 16) = 4 scales per row: 64 bytes of scales
+    assert f(g=16, s=Q + 4 * 64 - 8) == E_ALIAS     # scales run into the codes' tail
+    assert f(g=16, s=W - 60) == E_ALIAS             # scales run into w
+    g = lambda **k: lib.add_rmsnorm_fwd_fp8_grouped(A, C, W, Q, k.get("s", S), k.get("g", 32),
+                                                    k.get("res", D), None, 4, 64, 1e-6, BF16,
+                                                    BF16, None)
+    assert g(g=0) == E_SHAPE and g(res=None) == E_NULL and g(s=D + 8) == E_ALIAS

@@ -31,19 +31,28 @@ def _announce(request):
     torch.cuda.synchronize()
 
 
-def check_codes(q_gpu, s_gpu, q_ref, s_ref, y64, what):
+def check_codes(q_gpu, s_gpu, q_ref, s_ref, y64, what, group=None):
     q = q_gpu.view(torch.uint8).cpu().numpy().astype(np.uint8)
     qr = q_ref.numpy()
     sg = s_gpu.cpu().numpy().astype(np.float64)
     sr = s_ref.numpy().astype(np.float64)
+    assert sg.shape == sr.shape, (sg.shape, sr.shape)
     np.testing.assert_allclose(sg, sr, rtol=1e-5, err_msg=f"scale {what}")
     y = y64.numpy()
+    M, N = y.shape
+    # each element's group: the whole row, or `group` consecutive columns
+    cols = np.arange(N) // group if group else np.zeros(N, dtype=np.int64)
+    se = (sg if sg.ndim == 2 else sg[:, None])[:, cols]
     nan = np.isnan(y)
     assert np.array_equal((q & 0x7F) == 0x7F, nan), f"NaN codes {what}"
     # the oracle's scaled values, and whether a tiny relative change of them
     # changes the code (a rounding boundary within reach)
-    v = (y.astype(np.float32).astype(np.float64) * (448.0 / np.maximum(np.abs(y).max(1), 1e-300))[:, None])
-    v = np.where(np.isfinite(v), v, 0.0)
+    yf = np.where(nan, 0.0, y.astype(np.float32).astype(np.float64))
+    ng = int(cols.max()) + 1
+    amax = np.zeros((M, ng))
+    np.maximum.at(amax, (np.arange(M)[:, None], cols[None, :]), np.abs(yf))
+    inv = np.where(amax > 0, 448.0 / np.maximum(amax, 1e-300), 1.0)[:, cols]
+    v = yf * inv
     lo = oracle.fp8e4m3_encode(v * (1 - 2.0 ** -15))
     hi = oracle.fp8e4m3_encode(v * (1 + 2.0 ** -15))
     robust = (lo == hi) & ~nan
@@ -51,30 +60,31 @@ def check_codes(q_gpu, s_gpu, q_ref, s_ref, y64, what):
     assert bad[0].size == 0, (f"codes {what}: {bad[0].size} robust codes differ, first at "
                               f"{bad[0][0], bad[1][0]}: gpu {q[bad][0]:#04x} ref {qr[bad][0]:#04x}")
     ok = ~nan
-    deq = oracle.fp8e4m3_decode(q[ok]) * np.broadcast_to(sg[:, None], q.shape)[ok]
-    mag = np.abs(y[ok]) / np.broadcast_to(sg[:, None], q.shape)[ok]
+    deq = oracle.fp8e4m3_decode(q[ok]) * se[ok]
+    mag = np.abs(y[ok]) / se[ok]
     step = np.where(mag < 2.0 ** -6, 2.0 ** -9,
                     2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-30))) - 3))
-    lim = (0.5 * step * (1 + 1e-5) + 1e-5 * mag) * np.broadcast_to(sg[:, None], q.shape)[ok]
+    lim = (0.5 * step * (1 + 1e-5) + 1e-5 * mag) * se[ok]
     err = np.abs(deq - y[ok])
     assert np.all(err <= lim), f"dequantised {what}: max excess {(err - lim).max()}"
 
 
-def run(x, r, w, eps, what):
+def run(x, r, w, eps, what, group=None):
     g = lambda t: t.to(DEV)
     if r is None:
-        q, s = ar.rmsnorm_fwd_fp8(g(x), g(w), eps)
-        qr, sr, _ = oracle.rmsnorm_fwd_fp8(x, w, eps)
+        q, s = ar.rmsnorm_fwd_fp8(g(x), g(w), eps, group=group)
+        qr, sr, _ = oracle.rmsnorm_fwd_fp8(x, w, eps, group=group or 0)
         y64, _ = oracle.rmsnorm_fwd(x, w, eps, y_dtype=torch.float64)
     else:
-        q, s, res = ar.add_rmsnorm_fwd_fp8(g(x), g(r), g(w), eps)
-        qr, sr, rres, _ = oracle.rmsnorm_fwd_fp8(x, w, eps, residual=r)
+        q, s, res = ar.add_rmsnorm_fwd_fp8(g(x), g(r), g(w), eps, group=group)
+        qr, sr, rres, _ = oracle.rmsnorm_fwd_fp8(x, w, eps, residual=r, group=group or 0)
         torch.cuda.synchronize()
         assert_bits_equal(res.cpu(), rres, f"residual_out {what}")
         y64, _ = oracle.rmsnorm_fwd(rres, w, eps, y_dtype=torch.float64)
     torch.cuda.synchronize()
     assert q.dtype == torch.float8_e4m3fn
-    check_codes(q, s, qr, sr, y64, what)
+    N = x.shape[-1]
+    check_codes(q, s, qr, sr, y64, what, group if group and group < N else None)
 
 
 @pytest.mark.parametrize("fused", [True, False])
@@ -132,3 +142,73 @@ def test_fp8_special_rows():
     deq = q.float().cpu()[3] * s[3].cpu()
     y, _ = oracle.rmsnorm_fwd(x[3:4], inp["w"], 1e-6, y_dtype=torch.float32)
     assert_close(deq, y[0], "dequantised row", atol=float(s[3]) * 2.0 ** -9, rtol=0.07)
+
+
+# ---- one scale per group of columns -----------------------------------------
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_grouped_128_full_shape(fused):
+    inp = synth.add_rmsnorm_fwd_inputs(16384, 7168, torch.bfloat16, seed=71, r_std=0.5)
+    run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, "16384x7168 g128", group=128)
+
+
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.float32, torch.float32),
+                                          (torch.bfloat16, torch.float32)])
+@pytest.mark.parametrize("group", [4, 8, 16, 32, 128, 256, 512, 100, 1, 7168, 9000])
+def test_grouped_sizes(dtype, wdtype, group):
+    # vector path where the group is a power of two of whole vectors (up to a
+    # wave), the element-wise path otherwise; the group spanning the row is the
+    # per-row scale
+    inp = synth.add_rmsnorm_fwd_inputs(40, 7168, dtype, wdtype, seed=group)
+    run(inp["x"], inp["r"], inp["w"], 1e-6, f"{dtype} g{group}", group=group)
+
+
+@pytest.mark.parametrize("M", [1, 32, 512])
+def test_grouped_decode_with_outliers(M):
+    inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_decode_n8192", M=M)
+    run(inp["x"], inp["r"], inp["w"], 1e-5, f"decode M={M} g128", group=128)
+
+
+@pytest.mark.parametrize("N", [136, 1000, 4104, 24576, 65536])
+def test_grouped_ragged_rows_and_long_rows(N):
+    # a last group shorter than 128; rows long enough for more than 4
+    # vectors per lane (65536) take the element-wise path
+    inp = synth.add_rmsnorm_fwd_inputs(9 if N < 65536 else 3, N, torch.bfloat16, seed=N)
+    run(inp["x"], inp["r"], inp["w"], 1e-6, f"N={N} g128", group=128)
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8, 16])
+def test_grouped_forced_waves_per_row(monkeypatch, wpr):
+    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+    inp = synth.add_rmsnorm_fwd_inputs(37, 4096, torch.bfloat16, seed=wpr + 50)
+    run(inp["x"], inp["r"], inp["w"], 1e-6, f"wpr={wpr} g128", group=128)
+
+
+def test_grouped_elementwise_forced(monkeypatch):
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    inp = synth.add_rmsnorm_fwd_inputs(11, 4096, torch.bfloat16, seed=77)
+    run(inp["x"], inp["r"], inp["w"], 1e-6, "elem g128", group=128)
+    run(inp["x"], None, inp["w"], 1e-6, "elem g64", group=64)
+
+
+def test_grouped_special_groups():
+    N = 1024
+    inp = synth.add_rmsnorm_fwd_inputs(3, N, torch.bfloat16, seed=79)
+    x = inp["x"].clone()
+    x[0, :128] = 0            # a zero group: scale 1, codes 0
+    x[1, 300] = float("nan")  # a NaN makes the whole row NaN (rstd is NaN)
+    x[2, 512:640] = 2.0       # a constant group
+    q, s = ar.rmsnorm_fwd_fp8(x.to(DEV), inp["w"].to(DEV), 1e-6, group=128)
+    torch.cuda.synchronize()
+    qb = q.view(torch.uint8).cpu()
+    assert s.shape == (3, 8)
+    assert s[0, 0].item() == 1.0 and torch.all(qb[0, :128] == 0)
+    assert torch.isfinite(s).all()
+    # NaN row: every code NaN; the maximum ignores NaNs, so every scale is 1
+    assert torch.all((qb[1] & 0x7F) == 0x7F) and torch.all(s[1].cpu() == 1.0)
+    # an ordinary group: its largest value encodes as +-448
+    assert int((qb[0, 128:256].to(torch.int32) & 0x7F).max()) == 0x7E
+    amax = 512 + int(torch.argmax(inp["w"][512:640].float().abs()))
+    assert (int(qb[2, amax]) & 0x7F) == 0x7E
+    run(x, None, inp["w"], 1e-6, "special groups", group=128)
