@@ -264,20 +264,22 @@ bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
     return true;
 }
 
-// Backward variant: WPR in {1, 2, 4}; prefer at most 4 vectors per lane (the
-// dw accumulators live in registers, and short per-lane rows stream best:
-// bf16 32768 x 4096 measured 5.4 TB/s with 2 waves per row, 5.1 with one),
-// then 8, then 16, among the instantiated variants; enough waves to fill the
-// device; and a dw exchange that fits in 64 KiB of LDS.  ADDRMS_BWD_WPR
+// Backward variant: WPR in {1, 2, 4}.  First choice: 2 waves per row with
+// up to 8 vectors per lane, or 1 or 4 waves with up to 4 (the dw accumulators
+// live in registers; measured on MI355X, bf16: 2 waves per row streams best,
+// 5.4 TB/s at 32768 x 4096 against 5.2 with 1 or 4, and at 16384 x 7168 its 7
+// vectors per lane beat 4 waves' 3.5-of-4 by 2-6 %), then up to 8, then up to
+// 16 vectors per lane, among the instantiated variants; enough waves to fill
+// the device; and a dw exchange that fits in 64 KiB of LDS.  ADDRMS_BWD_WPR
 // forces a WPR.
 bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
 {
     const int forced = env_int("ADDRMS_BWD_WPR");
     int best_wi = -1, best_vi = -1;
     for (int pass = 0; pass < 3 && best_wi < 0; ++pass) {
-        const int max_vpl = pass == 0 ? 4 : pass == 1 ? 8 : kMaxVpl;
         for (int wi = 0; wi < kBwdNumWpr; ++wi) {
             const int wpr = kWprList[wi];
+            const int max_vpl = pass == 0 ? (wpr == 2 ? 8 : 4) : pass == 1 ? 8 : kMaxVpl;
             const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
             const int vi = vpl_index(need);
             const int rpb = 4 / wpr;
@@ -305,14 +307,20 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
     return true;
 }
 
-// dw[c] = sum over P partial rows of ws[:, c] (P = 0 writes zeros; ws unread).
-int colreduce(const void *workspace, int P, int N, float *dw, hipStream_t s)
+// dw[c] = sum over P partial rows of ws[:, c], and, when db is given,
+// db[c] = sum of ws2[:, c], in one launch (P = 0 writes zeros; nothing read).
+int colreduce(const void *workspace, const void *workspace2, int P, int N, float *dw, float *db,
+              hipStream_t s)
 {
     const float *ws = static_cast<const float *>(workspace);
-    const bool vec = (N % 4) == 0 && aligned16(dw) && (P == 0 || aligned16(ws));
+    const float *ws2 = static_cast<const float *>(workspace2);
+    const bool vec = (N % 4) == 0 && aligned16(dw) && (!db || aligned16(db)) &&
+                     (P == 0 || (aligned16(ws) && (!db || aligned16(ws2))));
     const KernelRef k = colreduce_kernel(vec);
-    void *argv[] = {(void *)&ws, (void *)&P, (void *)&N, (void *)&dw};
-    hipError_t e = hipLaunchKernel(k.fn, dim3((unsigned)((N + kColReduceCols - 1) / kColReduceCols)),
+    void *argv[] = {(void *)&ws, (void *)&ws2, (void *)&P, (void *)&N, (void *)&dw, (void *)&db};
+    hipError_t e = hipLaunchKernel(k.fn,
+                                   dim3((unsigned)((N + kColReduceCols - 1) / kColReduceCols),
+                                        db ? 2u : 1u),
                                    dim3(k.block), argv, 0, s);
     return e == hipSuccess ? ADDRMS_OK : fail_hip(e);
 }
@@ -474,11 +482,8 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
 
     // ---- variant and launch ----
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (M == 0) { // dw (db) of an empty batch is zero: the column reduce over P = 0 rows writes it
-        if ((rc = colreduce(workspace, 0, (int)N, dw, s)) != ADDRMS_OK)
-            return rc;
-        return db ? colreduce(workspace, 0, (int)N, db, s) : ADDRMS_OK;
-    }
+    if (M == 0) // dw (db) of an empty batch is zero: the column reduce over P = 0 rows writes it
+        return colreduce(workspace, workspace, 0, (int)N, dw, db, s);
     const BwdTable &tab = bwd_table(combo(dtype, w_dtype));
     // LayerNorm: the workspace holds dw partials then db partials, pmax rows each
     const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u)) / (ln ? 2 : 1);
@@ -527,9 +532,7 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
             return rc;
     }
     // dw (db) = column sums of the partials, same stream (ordered after stage 1)
-    if ((rc = colreduce(a.ws, a.P, (int)N, dw, s)) != ADDRMS_OK)
-        return rc;
-    return (ln && db) ? colreduce(a.ws2, a.P, (int)N, db, s) : ADDRMS_OK;
+    return colreduce(a.ws, a.ws2, a.P, (int)N, dw, (ln && db) ? db : nullptr, s);
 }
 
 // Do two strided sets of byte ranges, {a + i*sa + [0, la)} for i < na and

@@ -715,43 +715,45 @@ __global__ void __launch_bounds__(256) bwd_elem_dw_kernel(BwdArgs a)
     }
 }
 
-// dw[c] = sum_p ws[p, c], the second stage of the dw reduction.  The partial
-// rows are few (P <= 1024) and the columns many, so a block takes a narrow
-// column strip and splits the rows over slices of threads; the slices are then
-// merged in LDS by a fixed-order tree, so the result is deterministic.
-// Vector form: 16-column strips read as 4 x 16-byte lanes, 64 row slices;
-// requires N % 4 == 0 and 16-byte aligned ws and dw.  (Templates only so that
-// each translation unit's copy is a weak symbol.)
+// dw[c] = sum_p ws[p, c], the second stage of the dw reduction (and, for
+// LayerNorm, db[c] = sum_p ws2[p, c] in the same launch: blockIdx.y = 1).  The
+// partial rows are few (P <= 1024) and the columns many, so a block takes a
+// narrow column strip and splits the rows over slices of threads; the slices
+// are then merged in LDS by a fixed-order tree, so the result is
+// deterministic.  Vector form: 16-column strips read as 4 x 16-byte lanes, 64
+// row slices, and up to 16 rows per thread loaded at once (the kernel is short
+// and latency-bound: every load of a thread is in flight together);
+// requires N % 4 == 0 and 16-byte aligned partials and outputs.  (Templates
+// only so that each translation unit's copy is a weak symbol.)
 template <int Unused = 0>
-__global__ void __launch_bounds__(256) dw_colreduce_vec_kernel(const float *ws, int P, int N, float *dw)
+__global__ void __launch_bounds__(256)
+    dw_colreduce_vec_kernel(const float *ws, const float *ws2, int P, int N, float *dw, float *db)
 {
     constexpr int Q = kColReduceCols / 4; // 16-byte lanes per strip row
     constexpr int S = 256 / Q;            // row slices
+    constexpr int U = 16;                 // rows per thread per load batch
     __shared__ u32x4 red[S][Q];
+    const float *src = blockIdx.y ? ws2 : ws;
+    float *dst = blockIdx.y ? db : dw;
     const int q = threadIdx.x % Q;
     const int sl = threadIdx.x / Q;
     const int n4 = N / 4;
     const int c4 = blockIdx.x * Q + q;
     float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (c4 < n4) {
-        const u32x4 *base = reinterpret_cast<const u32x4 *>(ws) + c4;
-        int p = sl;
-        for (; p + 3 * S < P; p += 4 * S) {
-            u32x4 v[4];
+        const u32x4 *base = reinterpret_cast<const u32x4 *>(src) + c4;
+        for (int p0 = sl; p0 < P; p0 += U * S) {
+            u32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                v[u] = base[(size_t)(p + u * S) * n4];
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + u * S;
+                v[u] = p < P ? base[(size_t)p * n4] : u32x4{0u, 0u, 0u, 0u};
+            }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     a[i] += __uint_as_float(v[u][i]);
-        }
-        for (; p < P; p += S) {
-            const u32x4 v = base[(size_t)p * n4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] += __uint_as_float(v[i]);
         }
     }
     red[sl][q] = u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
@@ -770,22 +772,25 @@ __global__ void __launch_bounds__(256) dw_colreduce_vec_kernel(const float *ws, 
         __syncthreads();
     }
     if (sl == 0 && c4 < n4)
-        reinterpret_cast<u32x4 *>(dw)[c4] = red[0][q];
+        reinterpret_cast<u32x4 *>(dst)[c4] = red[0][q];
 }
 
 // Element form for any N / alignment: 16-column strips, 16 row slices.
 template <int Unused = 0>
-__global__ void __launch_bounds__(256) dw_colreduce_kernel(const float *ws, int P, int N, float *dw)
+__global__ void __launch_bounds__(256)
+    dw_colreduce_kernel(const float *ws, const float *ws2, int P, int N, float *dw, float *db)
 {
     constexpr int W = 16, S = 256 / W;
     __shared__ float red[S][W];
+    const float *src = blockIdx.y ? ws2 : ws;
+    float *dst = blockIdx.y ? db : dw;
     const int q = threadIdx.x % W;
     const int sl = threadIdx.x / W;
     const int c = blockIdx.x * W + q;
     float acc = 0.0f;
     if (c < N)
         for (int p = sl; p < P; p += S)
-            acc += ws[(size_t)p * N + c];
+            acc += src[(size_t)p * N + c];
     red[sl][q] = acc;
     __syncthreads();
 #pragma unroll
@@ -795,7 +800,7 @@ __global__ void __launch_bounds__(256) dw_colreduce_kernel(const float *ws, int 
         __syncthreads();
     }
     if (sl == 0 && c < N)
-        dw[c] = red[0][q];
+        dst[c] = red[0][q];
 }
 
 // ---------------------------------------------------------------------------
