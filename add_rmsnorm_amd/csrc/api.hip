@@ -282,14 +282,16 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
             const int max_vpl = pass == 0 ? (wpr == 2 ? 8 : 4) : pass == 1 ? 8 : kMaxVpl;
             const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
             const int vi = vpl_index(need);
-            const int rpb = 4 / wpr;
-            if (vi < 0 || kVplList[vi] > max_vpl || !bwd_built(norm, res, kVplList[vi]))
+            const int rpb = bwd_rpb(wpr);
+            if (wpr == 8 && forced != 8) // 8 waves per row: only on request
+                continue;
+            if (vi < 0 || kVplList[vi] > max_vpl || !bwd_built(norm, res, wpr, kVplList[vi]))
                 continue;
             if ((size_t)(rpb / 2) * (size_t)N * 4u > kMaxDynLds)
                 continue;
             if (forced > 0 && wpr != forced)
                 continue;
-            if (forced > 0 || M * wpr >= 4LL * cus || wi == kBwdNumWpr - 1) {
+            if (forced > 0 || M * wpr >= 4LL * cus || wi == kBwdNumWpr - 2) {
                 best_wi = wi;
                 best_vi = vi;
                 break;
@@ -506,7 +508,7 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     if (vec_ok && pick_bwd(norm, res, M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
         a.nvec = (int)(N / nv);
         const KernelRef &k = tab.vec[norm][res ? 1 : 0][wi][vi];
-        const int rpb = 4 / kWprList[wi];
+        const int rpb = bwd_rpb(kWprList[wi]);
         const size_t smem = (size_t)(rpb / 2) * (size_t)N * 4u;
         int grid = 0;
         if ((rc = persistent_grid(k, smem, (M + rpb - 1) / rpb, pmax, &grid)) != ADDRMS_OK)

@@ -83,7 +83,7 @@ constexpr int kNumVpl = 12;
 constexpr int kMaxVpl = 16;
 
 // Backward vector kernels use 256-thread blocks and WPR in {1, 2, 4}.
-constexpr int kBwdNumWpr = 3;
+constexpr int kBwdNumWpr = 4; // backward: WPR in {1, 2, 4, 8}
 
 constexpr int kBlockFwd(int wpr) { return wpr == 1 ? 256 : 64 * wpr; }
 
@@ -101,12 +101,17 @@ constexpr bool fwd_built(int wpr, int vpl)
 // Backward variants that are instantiated.  The LayerNorm backward with the
 // residual gradient at 16 vectors per lane needs more than the 512 VGPRs a
 // lane can hold and would spill to scratch; those rows take the element-wise
-// path instead.
-constexpr bool bwd_built(int norm, bool res, int vpl)
+// path instead.  8 waves per row (512-thread blocks, at most 256 VGPRs a
+// lane) is built up to 4 vectors per lane.
+constexpr bool bwd_built(int norm, bool res, int wpr, int vpl)
 {
-    return !(norm == kLayer && res && vpl > 14);
+    return !(norm == kLayer && res && vpl > 14) && !(wpr == 8 && vpl > 4);
 }
 constexpr int kBwdBlock = 256;
+// Backward vector kernels: 256-thread blocks holding 4 / WPR rows per step,
+// except WPR = 8, whose 512-thread blocks hold one row.
+constexpr int kBwdBlockOf(int wpr) { return wpr == 8 ? 512 : kBwdBlock; }
+constexpr int bwd_rpb(int wpr) { return wpr == 8 ? 1 : 4 / wpr; }
 constexpr int kColReduceCols = 16; // dw columns per column-reduce block
 
 // A kernel entry: function, block size, dynamic LDS bytes (backward: per

@@ -423,8 +423,8 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Backward, vector path, 256-thread blocks, WPR in {1, 2, 4}: RPB = 4 / WPR
-// rows per block step.  Each lane keeps its columns' dw (and, for LayerNorm,
+// Backward, vector path, 256-thread blocks with WPR in {1, 2, 4} (RPB = 4 / WPR
+// rows per block step), or 512-thread blocks with WPR = 8 (one row per step).  Each lane keeps its columns' dw (and, for LayerNorm,
 // db) partial sums in registers across all rows it visits; at the end the
 // block's row groups are summed through LDS (pairwise, fixed order) and
 // written as one row of the workspace: ws[blockIdx.x, :] (and ws2 for db).
@@ -436,15 +436,15 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 // before its one rounding (dx then holds dh, the gradient of x and of r).
 // ---------------------------------------------------------------------------
 template <typename T, typename WT, int NORM, bool RES, int WPR, int VPL>
-__global__ void __launch_bounds__(kBwdBlock) bwd_vec_kernel(BwdArgs a)
+__global__ void __launch_bounds__(kBwdBlockOf(WPR)) bwd_vec_kernel(BwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
     constexpr int VSTRIDE = 64 * WPR;
-    constexpr int RPB = 4 / WPR;
+    constexpr int RPB = bwd_rpb(WPR);
     constexpr bool LN = NORM == kLayer;
     using CT = typename BwdCompute<T>::type;
     extern __shared__ __attribute__((aligned(16))) float lds[];
-    __shared__ CT part[2][2][4]; // [row parity][sum][wave]
+    __shared__ CT part[2][2][kBwdBlockOf(WPR) / 64]; // [row parity][sum][wave]
 
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -851,10 +851,10 @@ template <typename T, typename WT> struct TableBuilder {
 
     template <int NM, bool R, int WPR, int VPL> static KernelRef bwd_ref()
     {
-        if constexpr (bwd_built(NM, R, VPL))
+        if constexpr (bwd_built(NM, R, WPR, VPL))
             return KernelRef{
                 reinterpret_cast<const void *>(&bwd_vec_kernel<T, WT, NM, R, WPR, VPL>),
-                kBwdBlock};
+                kBwdBlockOf(WPR)};
         else
             return KernelRef{nullptr, 0};
     }

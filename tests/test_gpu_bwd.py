@@ -45,7 +45,7 @@ def test_rmsnorm_bwd_bf16_32768x4096():
     check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6)
 
 
-@pytest.mark.parametrize("wpr", [1, 2, 4])
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8])
 @pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
                                           (torch.bfloat16, torch.float32),
                                           (torch.float32, torch.float32),

@@ -52,7 +52,7 @@ def test_fused_bwd_dtypes(dtype, wdtype):
     check(*fused_case(777, 2048, dtype, wdtype, seed=5), str(dtype))
 
 
-@pytest.mark.parametrize("wpr", [1, 2, 4])
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8])
 def test_fused_bwd_forced_waves_per_row(monkeypatch, wpr):
     monkeypatch.setenv("ADDRMS_BWD_WPR", str(wpr))
     check(*fused_case(1000, 4096, torch.bfloat16, seed=7), f"wpr={wpr}")

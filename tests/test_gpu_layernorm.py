@@ -126,7 +126,7 @@ def test_backward_bf16(M, N):
     check_bwd(inputs(M, N, torch.bfloat16, seed=M), f"{M}x{N}")
 
 
-@pytest.mark.parametrize("wpr", [1, 2, 4])
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8])
 @pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
                                           (torch.float32, torch.float32),
                                           (torch.bfloat16, torch.float32)])
