@@ -24,10 +24,12 @@ import torch
 from torch import Tensor
 
 from . import (add_layernorm_bwd, add_layernorm_fwd, add_rmsnorm_bwd, add_rmsnorm_fwd,
-               layernorm_bwd, layernorm_fwd, rmsnorm_bwd, rmsnorm_fwd)
+               add_rmsnorm_fwd_fp8, layernorm_bwd, layernorm_fwd, rmsnorm_bwd, rmsnorm_fwd,
+               rmsnorm_fwd_fp8, rmsnorm_rope_qk)
 
-__all__ = ["rms_norm", "add_rms_norm", "layer_norm", "add_layer_norm", "RMSNorm", "AddRMSNorm",
-           "LayerNorm", "AddLayerNorm"]
+__all__ = ["rms_norm", "add_rms_norm", "layer_norm", "add_layer_norm", "rms_norm_fp8",
+           "add_rms_norm_fp8", "rms_norm_rope_qk", "RMSNorm", "AddRMSNorm", "LayerNorm",
+           "AddLayerNorm"]
 
 
 # ---- forward / backward ops -------------------------------------------------
@@ -204,7 +206,97 @@ def _add_ln_backward(ctx, dy, dres, _dmean, _drstd):
 _add_layer_norm_fwd.register_autograd(_add_ln_backward, setup_context=_add_ln_setup)
 
 
+# ---- forward-only ops: quantised output, RMSNorm + RoPE ---------------------------
+# Quantisation has no useful gradient and the composed norm + rotation has no
+# backward here; these ops are registered (with fake implementations) so that
+# they can sit in a traced or compiled graph.
+
+_FP8 = torch.float8_e4m3fn
+
+
+def _scale_shape(x: Tensor, group: int):
+    N = x.shape[-1]
+    if group <= 0:
+        return x.shape[:-1]
+    g = min(group, N)
+    return x.shape[:-1] + ((N + g - 1) // g,)
+
+
+@torch.library.custom_op("addrms::rms_norm_fp8", mutates_args=())
+def _rms_norm_fp8(x: Tensor, w: Tensor, eps: float, group: int) -> Tuple[Tensor, Tensor]:
+    return rmsnorm_fwd_fp8(x.contiguous(), w.contiguous(), eps,
+                           group=group if group > 0 else None)
+
+
+@_rms_norm_fp8.register_fake
+def _(x, w, eps, group):
+    return x.new_empty(x.shape, dtype=_FP8), x.new_empty(_scale_shape(x, group),
+                                                          dtype=torch.float32)
+
+
+@torch.library.custom_op("addrms::add_rms_norm_fp8", mutates_args=())
+def _add_rms_norm_fp8(x: Tensor, r: Tensor, w: Tensor, eps: float,
+                      group: int) -> Tuple[Tensor, Tensor, Tensor]:
+    return add_rmsnorm_fwd_fp8(x.contiguous(), r.contiguous(), w.contiguous(), eps,
+                               group=group if group > 0 else None)
+
+
+@_add_rms_norm_fp8.register_fake
+def _(x, r, w, eps, group):
+    return (x.new_empty(x.shape, dtype=_FP8),
+            x.new_empty(_scale_shape(x, group), dtype=torch.float32), torch.empty_like(x))
+
+
+@torch.library.custom_op("addrms::rms_norm_rope_qk", mutates_args=())
+def _rms_norm_rope_qk(q: Tensor, k: Tensor, wq: Tensor, wk: Tensor, cos: Tensor, sin: Tensor,
+                      pos: Tensor, eps: float, interleaved: bool) -> Tuple[Tensor, Tensor]:
+    return rmsnorm_rope_qk(q, k, wq, wk, cos, sin, pos, eps, interleaved=interleaved)
+
+
+@_rms_norm_rope_qk.register_fake
+def _(q, k, wq, wk, cos, sin, pos, eps, interleaved):
+    return q.new_empty(q.shape), k.new_empty(k.shape)
+
+
+@torch.library.custom_op("addrms::rms_norm_rope_qk_", mutates_args=("q", "k"))
+def _rms_norm_rope_qk_(q: Tensor, k: Tensor, wq: Tensor, wk: Tensor, cos: Tensor, sin: Tensor,
+                       pos: Tensor, eps: float, interleaved: bool) -> None:
+    rmsnorm_rope_qk(q, k, wq, wk, cos, sin, pos, eps, interleaved=interleaved, q_out=q, k_out=k)
+
+
+@_rms_norm_rope_qk_.register_fake
+def _(q, k, wq, wk, cos, sin, pos, eps, interleaved):
+    return None
+
+
 # ---- user-facing functions and modules ----------------------------------------
+
+def rms_norm_fp8(x: Tensor, w: Tensor, eps: float = 1e-6,
+                 group: Optional[int] = None) -> Tuple[Tensor, Tensor]:
+    """RMSNorm with an E4M3 output: (codes float8_e4m3fn, float32 scales), one
+    scale per row or per `group` columns.  Not differentiable."""
+    return _rms_norm_fp8(x, w, eps, int(group or 0))
+
+
+def add_rms_norm_fp8(x: Tensor, r: Tensor, w: Tensor, eps: float = 1e-6,
+                     group: Optional[int] = None) -> Tuple[Tensor, Tensor, Tensor]:
+    """Fused residual add + RMSNorm with an E4M3 output: (codes, scales,
+    residual).  Not differentiable."""
+    return _add_rms_norm_fp8(x, r, w, eps, int(group or 0))
+
+
+def rms_norm_rope_qk(q: Tensor, k: Tensor, wq: Tensor, wk: Tensor, cos: Tensor, sin: Tensor,
+                     pos: Tensor, eps: float = 1e-6, interleaved: bool = False,
+                     inplace: bool = False):
+    """Per-head RMSNorm then RoPE of query heads q [T, Hq, D] and key heads
+    k [T, Hk, D] (views of a packed projection output are fine).  Returns
+    (q_out, k_out), or, with inplace=True, updates q and k and returns them.
+    Not differentiable."""
+    if inplace:
+        _rms_norm_rope_qk_(q, k, wq, wk, cos, sin, pos, eps, interleaved)
+        return q, k
+    return _rms_norm_rope_qk(q, k, wq, wk, cos, sin, pos, eps, interleaved)
+
 
 def rms_norm(x: Tensor, w: Tensor, eps: float = 1e-6) -> Tensor:
     """RMSNorm over the last dimension, differentiable in x and w."""

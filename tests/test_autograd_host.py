@@ -32,3 +32,23 @@ def test_fake_shapes_layernorm():
         assert res.shape == x.shape and mean.shape == (6,)
         dh, dw, db = torch.ops.addrms.add_layer_norm_bwd(x, None, x, w, mean, rstd)
         assert dh.shape == x.shape and dw.shape == db.shape == (128,)
+
+
+def test_fake_shapes_fp8_and_rope():
+    with FakeTensorMode():
+        x = torch.empty(4, 7168, dtype=torch.bfloat16)
+        w = torch.empty(7168, dtype=torch.bfloat16)
+        q, s = torch.ops.addrms.rms_norm_fp8(x, w, 1e-6, 0)
+        assert q.dtype == torch.float8_e4m3fn and q.shape == x.shape and s.shape == (4,)
+        q, s, res = torch.ops.addrms.add_rms_norm_fp8(x, x, w, 1e-6, 128)
+        assert s.shape == (4, 56) and s.dtype == torch.float32 and res.shape == x.shape
+        q, s = torch.ops.addrms.rms_norm_fp8(x, w, 1e-6, 100000)
+        assert s.shape == (4, 1)
+        qh = torch.empty(8, 32, 128, dtype=torch.bfloat16)
+        kh = torch.empty(8, 8, 128, dtype=torch.bfloat16)
+        wq = torch.empty(128, dtype=torch.bfloat16)
+        cos = torch.empty(64, 64)
+        pos = torch.empty(8, dtype=torch.int64)
+        qo, ko = torch.ops.addrms.rms_norm_rope_qk(qh, kh, wq, wq, cos, cos, pos, 1e-6, False)
+        assert qo.shape == qh.shape and ko.shape == kh.shape and qo.dtype == torch.bfloat16
+        assert torch.ops.addrms.rms_norm_rope_qk_(qh, kh, wq, wq, cos, cos, pos, 1e-6, True) is None

@@ -212,3 +212,23 @@ def test_grouped_special_groups():
     amax = 512 + int(torch.argmax(inp["w"][512:640].float().abs()))
     assert (int(qb[2, amax]) & 0x7F) == 0x7E
     run(x, None, inp["w"], 1e-6, "special groups", group=128)
+
+
+def test_custom_ops_match_the_binding_and_compile():
+    import add_rmsnorm_amd.autograd as ag
+    inp = synth.add_rmsnorm_fwd_inputs(64, 4096, torch.bfloat16, seed=81)
+    x, r, w = (inp[k].to(DEV) for k in ("x", "r", "w"))
+    for group in (None, 128):
+        a = ar.add_rmsnorm_fwd_fp8(x, r, w, 1e-6, group=group)
+        b = ag.add_rms_norm_fp8(x, r, w, 1e-6, group=group)
+        f = torch.compile(lambda x, r, w: ag.add_rms_norm_fp8(x, r, w, 1e-6, group=group),
+                          backend="aot_eager", fullgraph=True)
+        c = f(x, r, w)
+        torch.cuda.synchronize()
+        for u, v, z in zip(a, b, c):
+            assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+            assert torch.equal(u.view(torch.uint8), z.view(torch.uint8))
+    q1, s1 = ar.rmsnorm_fwd_fp8(x, w, 1e-6)
+    q2, s2 = ag.rms_norm_fp8(x, w, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(q1.view(torch.uint8), q2.view(torch.uint8)) and torch.equal(s1, s2)

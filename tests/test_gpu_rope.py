@@ -213,3 +213,24 @@ def test_repeated_calls_are_bit_identical():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_custom_ops_out_of_place_and_in_place():
+    import add_rmsnorm_amd.autograd as ag
+    T, Hq, Hk, D = 256, 8, 2, 128
+    inp = synth.rmsnorm_rope_inputs(T, Hq, Hk, D, seed=17)
+    args = [inp[n].to(DEV) for n in ("wq", "wk", "cos", "sin", "pos")]
+    qkv = inp["qkv"].to(DEV)
+    q = qkv[:, :Hq * D].view(T, Hq, D)
+    k = qkv[:, Hq * D:(Hq + Hk) * D].view(T, Hk, D)
+    ref = ar.rmsnorm_rope_qk(q, k, *args, 1e-6, interleaved=True)
+    out = ag.rms_norm_rope_qk(q, k, *args, 1e-6, interleaved=True)
+    f = torch.compile(lambda q, k: ag.rms_norm_rope_qk(q, k, *args, 1e-6, True),
+                      backend="aot_eager", fullgraph=True)
+    comp = f(q, k)
+    ag.rms_norm_rope_qk(q, k, *args, 1e-6, interleaved=True, inplace=True)
+    torch.cuda.synchronize()
+    for r_, o_, c_, i_ in zip(ref, out, comp, (q, k)):
+        assert torch.equal(r_.view(torch.int16), o_.view(torch.int16))
+        assert torch.equal(r_.view(torch.int16), c_.view(torch.int16))
+        assert torch.equal(r_.view(torch.int16), i_.view(torch.int16))
