@@ -96,6 +96,17 @@ def _load():
         lib.oracle_add_rmsnorm_fwd_fp8_grouped.restype = i32
         lib.oracle_add_rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, i32, vp, i32, vp, vp, i64, vp,
                                                            i32, vp, i32, i64, i64, dbl]
+        lib.oracle_fp4e2m1_encode.restype = ctypes.c_uint8
+        lib.oracle_fp4e2m1_encode.argtypes = [dbl]
+        lib.oracle_fp4e2m1_decode.restype = dbl
+        lib.oracle_fp4e2m1_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp4e2m1_encode_array.restype = None
+        lib.oracle_fp4e2m1_encode_array.argtypes = [vp, vp, i64]
+        lib.oracle_rmsnorm_fwd_mxfp4.restype = i32
+        lib.oracle_rmsnorm_fwd_mxfp4.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i64, i64, dbl]
+        lib.oracle_add_rmsnorm_fwd_mxfp4.restype = i32
+        lib.oracle_add_rmsnorm_fwd_mxfp4.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, i32, vp, i32,
+                                                     i64, i64, dbl]
         lib.oracle_rmsnorm_rope.restype = i32
         lib.oracle_rmsnorm_rope.argtypes = [vp, i32, i64, vp, i32, vp, vp, vp, i64, vp, i32, i64,
                                             i64, i64, i64, i32, dbl]
@@ -376,3 +387,56 @@ def rmsnorm_rope(x: torch.Tensor, w: torch.Tensor, cos: torch.Tensor, sin: torch
                                        cos.shape[0], _ptr(y), _code(y), H * D, T, H, D,
                                        int(bool(interleaved)), e), "rmsnorm_rope")
     return y
+
+
+def fp4e2m1_encode(v) -> np.ndarray:
+    """E2M1 codes (uint8, 0..15) of binary64 values: nearest, ties to the even
+    code, saturating at +-6, sign kept."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint8)
+    _load().oracle_fp4e2m1_encode_array(a.ctypes.data_as(ctypes.c_void_p),
+                                        out.ctypes.data_as(ctypes.c_void_p), a.size)
+    return out
+
+
+def fp4e2m1_decode(c) -> np.ndarray:
+    """Exact binary64 values of E2M1 codes (the low 4 bits of each entry)."""
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    c = np.asarray(c, dtype=np.uint8)
+    return np.where(c & 0x8, -1.0, 1.0) * grid[c & 0x7]
+
+
+def unpack_fp4(q: torch.Tensor) -> np.ndarray:
+    """[.., N/2] packed bytes (element 2i in the low nibble) -> [.., N] codes."""
+    b = q.numpy() if isinstance(q, torch.Tensor) else np.asarray(q)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def rmsnorm_fwd_mxfp4(x: torch.Tensor, w: torch.Tensor, eps: float, *, residual=None,
+                      eps_exact: bool = False):
+    """RMSNorm with an MXFP4 output: E2M1 codes packed two per byte
+    (q uint8 [M, N/2]), one E8M0 scale byte per 32 columns (scale uint8
+    [M, ceil(N/32)]).  Returns (q, scale, rstd) or, with residual=r, the fused
+    form (q, scale, residual_out, rstd)."""
+    x, w = _cpu(x), _cpu(w)
+    N = x.shape[-1]
+    M = x.numel() // N
+    q = torch.empty(x.shape[:-1] + (N // 2,), dtype=torch.uint8)
+    scale = torch.empty(x.shape[:-1] + ((N + 31) // 32,), dtype=torch.uint8)
+    rstd = torch.empty(x.shape[:-1], dtype=torch.float32)
+    e = float(eps) if eps_exact else eps_as_float32(eps)
+    if residual is None:
+        _check(_load().oracle_rmsnorm_fwd_mxfp4(_ptr(x), _code(x), _ptr(w), _code(w), _ptr(q),
+                                                _ptr(scale), _ptr(rstd), _code(rstd), M, N, e),
+               "rmsnorm_fwd_mxfp4")
+        return q, scale, rstd
+    r = _cpu(residual)
+    res = torch.empty(x.shape, dtype=x.dtype)
+    _check(_load().oracle_add_rmsnorm_fwd_mxfp4(_ptr(x), _ptr(r), _code(x), _ptr(w), _code(w),
+                                                _ptr(q), _ptr(scale), _ptr(res), _code(res),
+                                                _ptr(rstd), _code(rstd), M, N, e),
+           "add_rmsnorm_fwd_mxfp4")
+    return q, scale, res, rstd

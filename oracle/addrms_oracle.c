@@ -673,3 +673,142 @@ int oracle_rmsnorm_rope(const void *x, int x_dt, int64_t x_stride, const void *w
     free(n);
     return OR_OK;
 }
+
+/* ---- MXFP4 output: E2M1 elements with a shared E8M0 scale per 32 ---------- */
+
+/* FP4 E2M1 (OCP Microscaling Formats v1.0: sign, 2 exponent bits with bias 1,
+ * 1 mantissa bit; no infinities or NaN).  Magnitudes of codes 0..7:
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Round to nearest on that grid, ties to the
+ * even code; magnitudes above 6 saturate to 6 (the MX conversion clamps
+ * normal values); the sign is kept, also for a zero result. */
+static const double e2m1_grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+uint8_t oracle_fp4e2m1_encode(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x8u : 0x0u;
+    const double a = fabs(v);
+    if (a >= 6.0)
+        return (uint8_t)(sign | 0x7u);
+    int k = 0;
+    while (k < 7 && e2m1_grid[k + 1] <= a)
+        k++; /* e2m1_grid[k] <= a < e2m1_grid[k + 1] */
+    const double lo = e2m1_grid[k], hi = e2m1_grid[k + 1];
+    const double mid = 0.5 * (lo + hi);
+    int code;
+    if (a < mid)
+        code = k;
+    else if (a > mid)
+        code = k + 1;
+    else
+        code = (k % 2 == 0) ? k : k + 1; /* the even code */
+    return (uint8_t)(sign | (uint8_t)code);
+}
+
+double oracle_fp4e2m1_decode(uint8_t c)
+{
+    const double m = e2m1_grid[c & 0x7u];
+    return (c & 0x8u) ? -m : m;
+}
+
+/* RMSNorm with an MXFP4 output (OCP MX v1.0): per row, y_j = h_j * rstd * w_j
+ * in binary64, rounded once to binary32 (yf_j); per block of 32 consecutive
+ * columns (the last block of a row may be shorter):
+ *     a block with a NaN:   scale code 0xFF (NaN), element codes 0
+ *     otherwise:            amax = max |yf_j|
+ *                           E = floor(log2(amax)) - 2, clamped to [-127, 127]
+ *                           (E = -127 when amax is 0: the smallest scale)
+ *                           scale code = E + 127 (E8M0), X = 2^E
+ *                           q_j = E2M1(yf_j / X)       (exact division)
+ * 2 is the exponent of E2M1's largest value (6 = 1.5 * 2^2), so the block's
+ * largest magnitude lands in [4, 8) and values above 6 saturate.  Codes are
+ * packed two per byte, element 2i in the low nibble: q [M][N/2] (N even);
+ * scale [M][ceil(N/32)].  y_j ~= decode(q_j) * 2^(scale - 127). */
+int oracle_rmsnorm_fwd_mxfp4(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
+                             uint8_t *scale, void *rstd, int rstd_dt, int64_t M, int64_t N,
+                             double eps)
+{
+    double *y;
+    float *yf;
+
+    if (!x || !w || !q || !scale || M < 0 || N <= 0 || N % 2 != 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(x_dt) || !dtype_ok(w_dt) || (rstd && !dtype_ok(rstd_dt)))
+        return OR_ERR_ARG;
+    const int64_t nb = (N + 31) / 32;
+    y = (double *)malloc((size_t)N * sizeof(double));
+    yf = (float *)malloc((size_t)N * sizeof(float));
+    if (!y || !yf) {
+        free(y);
+        free(yf);
+        return OR_ERR_NOMEM;
+    }
+    for (int64_t i = 0; i < M; i++) {
+        const void *xi = (const char *)x + (size_t)(i * N) * elem_size(x_dt);
+        void *ri = rstd ? (void *)((char *)rstd + (size_t)i * elem_size(rstd_dt)) : NULL;
+        oracle_rmsnorm_fwd(xi, x_dt, w, w_dt, y, OR_F64, ri, rstd_dt, 1, N, eps);
+        for (int64_t j = 0; j < N; j++)
+            yf[j] = (float)y[j];
+        for (int64_t b = 0; b < nb; b++) {
+            const int64_t j0 = b * 32, j1 = j0 + 32 < N ? j0 + 32 : N;
+            int has_nan = 0;
+            double amax = 0.0;
+            for (int64_t j = j0; j < j1; j++) {
+                if (isnan(yf[j]))
+                    has_nan = 1;
+                else if (fabs((double)yf[j]) > amax)
+                    amax = fabs((double)yf[j]);
+            }
+            uint8_t codes[32];
+            int E = -127;
+            if (has_nan) {
+                scale[i * nb + b] = 0xFF;
+                for (int64_t j = j0; j < j1; j++)
+                    codes[j - j0] = 0;
+            } else {
+                if (amax > 0.0) {
+                    int e2;
+                    frexp(amax, &e2); /* amax = f * 2^e2, f in [0.5, 1): floor(log2) = e2 - 1 */
+                    E = (e2 - 1) - 2;
+                    if (E < -127)
+                        E = -127;
+                    if (E > 127)
+                        E = 127;
+                }
+                scale[i * nb + b] = (uint8_t)(E + 127);
+                for (int64_t j = j0; j < j1; j++)
+                    codes[j - j0] = oracle_fp4e2m1_encode(ldexp((double)yf[j], -E));
+            }
+            for (int64_t j = j0; j < j1; j += 2)
+                q[(i * N + j) / 2] = (uint8_t)(codes[j - j0] | (codes[j + 1 - j0] << 4));
+        }
+    }
+    free(y);
+    free(yf);
+    return OR_OK;
+}
+
+/* Fused residual-Add + RMSNorm with the MXFP4 output: the residual as in
+ * oracle_add_rmsnorm_fwd, then oracle_rmsnorm_fwd_mxfp4 of the stored residual. */
+int oracle_add_rmsnorm_fwd_mxfp4(const void *x, const void *r, int in_dt, const void *w, int w_dt,
+                                 uint8_t *q, uint8_t *scale, void *res, int res_dt, void *rstd,
+                                 int rstd_dt, int64_t M, int64_t N, double eps)
+{
+    if (!x || !r || !res || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
+        return OR_ERR_ARG;
+    for (int64_t k = 0; k < M * N; k++) {
+        float a32 = (float)load_elem(x, in_dt, k);
+        float b32 = (float)load_elem(r, in_dt, k);
+        float s32 = a32 + b32; /* binary32 add, as the fused op's residual */
+        store_elem(res, res_dt, k, in_dt == OR_F64 ? load_elem(x, in_dt, k) + load_elem(r, in_dt, k)
+                                                   : (double)s32);
+    }
+    return oracle_rmsnorm_fwd_mxfp4(res, res_dt, w, w_dt, q, scale, rstd, rstd_dt, M, N, eps);
+}
+
+void oracle_fp4e2m1_encode_array(const double *v, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_fp4e2m1_encode(v[i]);
+}

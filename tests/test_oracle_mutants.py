@@ -18,7 +18,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "addrms_oracle.c")
 PINS = ["tests/test_oracle_bf16.py", "tests/test_oracle_fwd.py", "tests/test_oracle_bwd.py",
-        "tests/test_oracle_layernorm.py", "tests/test_oracle_fp8.py", "tests/test_oracle_rope.py"]
+        "tests/test_oracle_layernorm.py", "tests/test_oracle_fp8.py", "tests/test_oracle_rope.py",
+        "tests/test_oracle_mxfp4.py"]
 
 MUTANTS = {
     "eps_outside_root": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms) + eps"),
@@ -63,12 +64,13 @@ MUTANTS.update({
                                 "double g = load_elem(dy, in_dt, i * N + j);", 1, 2),
     "ln_bwd_dx_without_weight": ("double g = d * load_elem(w, w_dt, j);", "double g = d;", 1, 2),
 })
-for _k in ("bwd_g_without_weight", "bwd_dx_without_weight", "ties_away_from_zero",
-           "truncating_round"):
+for _k in ("bwd_g_without_weight", "bwd_dx_without_weight", "ties_away_from_zero"):
     MUTANTS[_k] = MUTANTS[_k] + (0, 2)
+MUTANTS["truncating_round"] = MUTANTS["truncating_round"] + (0, 3)
 MUTANTS.update({
     "fp8_ties_up": ("(fmod(lo / ulp, 2.0) == 0.0) ? lo : hi", "hi", 1, 2),
-    "fp8_truncating_round": ("if (a < mid)", "if (a < hi)", 1, 2),
+    "fp8_truncating_round": ("if (a < mid)", "if (a < hi)", 1, 3),
+    "fp4_truncating_round": ("if (a < mid)", "if (a < hi)", 2, 3),
     "fp8_subnormal_spacing": ("ulp = 0x1p-9;", "ulp = 0x1p-10;"),
     "fp8_ulp_exponent": ("ulp = ldexp(1.0, e - 4);", "ulp = ldexp(1.0, e - 5);"),
     "fp8_exponent_bias": ("int exp_field = (e - 1) + 7;", "int exp_field = (e - 1) + 8;"),
@@ -80,6 +82,17 @@ MUTANTS.update({
     "fp8_group_scale_index": ("scale[i * ngroups + g] = sc;", "scale[i + g] = sc;"),
     "fp8_group_amax_from_row_start": ("for (int64_t j = j0; j < j1; j++) {\n                float m",
                                       "for (int64_t j = 0; j < j1; j++) {\n                float m"),
+    "fp4_ties_to_odd": ("code = (k % 2 == 0) ? k : k + 1; /* the even code */",
+                        "code = (k % 2 == 1) ? k : k + 1;"),
+    "fp4_saturates_to_4": ("if (a >= 6.0)\n        return (uint8_t)(sign | 0x7u);",
+                           "if (a >= 6.0)\n        return (uint8_t)(sign | 0x6u);"),
+    "mx_exponent_offset": ("E = (e2 - 1) - 2;", "E = (e2 - 1) - 1;"),
+    "mx_scale_bias": ("scale[i * nb + b] = (uint8_t)(E + 127);",
+                      "scale[i * nb + b] = (uint8_t)(E + 126);"),
+    "mx_nibbles_swapped": ("(uint8_t)(codes[j - j0] | (codes[j + 1 - j0] << 4));",
+                           "(uint8_t)(codes[j + 1 - j0] | (codes[j - j0] << 4));"),
+    "mx_nan_block_scale": ("scale[i * nb + b] = 0xFF;", "scale[i * nb + b] = 0x00;"),
+    "mx_zero_block_scale": ("int E = -127;", "int E = 0;"),
     "rope_first_sign": ("store_elem(y, y_dt, yo + ja, a * c - b * s);",
                         "store_elem(y, y_dt, yo + ja, a * c + b * s);"),
     "rope_second_sign": ("store_elem(y, y_dt, yo + jb, b * c + a * s);",
