@@ -28,7 +28,8 @@ import torch
 __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_bwd",
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
            "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "rmsnorm_fwd_fp8",
-           "add_rmsnorm_fwd_fp8", "rmsnorm_rope_qk", "AddRmsError", "LIB_PATH", "lib"]
+           "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_mxfp4", "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
+           "AddRmsError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -81,6 +82,10 @@ def _load():
     lib.add_rmsnorm_fwd_fp8_grouped.restype = i32
     lib.add_rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, f32,
                                                 i32, i32, vp]
+    lib.rmsnorm_fwd_mxfp4.restype = i32
+    lib.rmsnorm_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd_mxfp4.restype = i32
+    lib.add_rmsnorm_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.rmsnorm_rope_qk.restype = i32
     lib.rmsnorm_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
                                     i64, i64, i64, i64, f32, i32, i32, i32, vp]
@@ -502,6 +507,76 @@ def add_rmsnorm_fwd_fp8(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: 
     if st != 0:
         raise AddRmsError(st, "add_rmsnorm_fwd_fp8")
     return y_fp8, y_scale, residual_out
+
+
+_FP4X2 = getattr(torch, "float4_e2m1fn_x2", None)
+_E8M0 = getattr(torch, "float8_e8m0fnu", None)
+
+
+def _mx_out(x, y_fp4, y_scale):
+    """MXFP4 output buffers: codes [.., N/2] (two per byte), E8M0 scales
+    [.., ceil(N/32)]; 1-byte element types (packed FP4 / E8M0, or uint8)."""
+    N = x.shape[-1]
+    if N % 2:
+        raise ValueError(f"MXFP4 needs an even last dimension, got {N}")
+    cshape = x.shape[:-1] + (N // 2,)
+    sshape = x.shape[:-1] + ((N + 31) // 32,)
+    if y_fp4 is None:
+        y_fp4 = torch.empty(cshape, dtype=_FP4X2 or torch.uint8, device=x.device)
+    else:
+        _dev(y_fp4, "y_fp4", shape=cshape)
+    if y_scale is None:
+        y_scale = torch.empty(sshape, dtype=_E8M0 or torch.uint8, device=x.device)
+    else:
+        _dev(y_scale, "y_scale", shape=sshape)
+    for t, n in ((y_fp4, "y_fp4"), (y_scale, "y_scale")):
+        if t.element_size() != 1:
+            raise TypeError(f"{n} must have 1-byte elements")
+    return y_fp4, y_scale
+
+
+def rmsnorm_fwd_mxfp4(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, y_fp4=None,
+                      y_scale=None, rstd=None):
+    """RMSNorm with an MXFP4 output (OCP MX): E2M1 codes two per byte
+    (torch.float4_e2m1fn_x2 [.., N/2], element 2i in the low nibble) and one
+    E8M0 scale per 32 values (torch.float8_e8m0fnu [.., ceil(N/32)]):
+    y ~= E2M1(code) * 2^(scale - 127).  Returns (y_fp4, y_scale)."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(w, "w", shape=(N,))
+    y_fp4, y_scale = _mx_out(x, y_fp4, y_scale)
+    if rstd is not None:
+        _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.rmsnorm_fwd_mxfp4(_p(x), _p(w), _p(y_fp4), _p(y_scale), _p(rstd), M, N,
+                                    float(eps), _code(x, "x"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "rmsnorm_fwd_mxfp4")
+    return y_fp4, y_scale
+
+
+def add_rmsnorm_fwd_mxfp4(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                          *, y_fp4=None, y_scale=None, residual_out=None, rstd=None):
+    """Fused residual add + RMSNorm with an MXFP4 output, as rmsnorm_fwd_mxfp4.
+    Returns (y_fp4, y_scale, residual_out)."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(r, "r", x.dtype, x.shape)
+    _dev(w, "w", shape=(N,))
+    y_fp4, y_scale = _mx_out(x, y_fp4, y_scale)
+    residual_out = (torch.empty_like(x) if residual_out is None
+                    else _dev(residual_out, "residual_out", x.dtype, x.shape))
+    if rstd is not None:
+        _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.add_rmsnorm_fwd_mxfp4(_p(x), _p(r), _p(w), _p(y_fp4), _p(y_scale),
+                                        _p(residual_out), _p(rstd), M, N, float(eps),
+                                        _code(x, "x"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "add_rmsnorm_fwd_mxfp4")
+    return y_fp4, y_scale, residual_out
 
 
 def _heads(t: torch.Tensor, what: str, dtype=None, T=None, D=None) -> int:

@@ -329,15 +329,15 @@ int colreduce(const void *workspace, const void *workspace2, int P, int N, float
 
 int fwd_common(int norm, const void *x, const void *r, const void *w, const void *b, void *y,
                void *res, float *mean, float *rstd, int64_t M, int64_t N, float eps, int dtype,
-               int w_dtype, void *stream, bool fused, uint8_t *q = nullptr, float *qscale = nullptr,
-               int64_t qgroup = 0)
+               int w_dtype, void *stream, bool fused, uint8_t *q = nullptr, void *qscale = nullptr,
+               int64_t qgroup = 0, int qfmt = 0)
 {
     // ---- validation (no HIP call) ----
     // With M == 0 the matrices are empty and may be NULL.  The FP8 variant
     // writes q and qscale in place of y.
     const bool q8 = q != nullptr || qscale != nullptr;
     if (q8)
-        y = q; // the output matrix, for the checks below (1 byte per element)
+        y = q; // the output matrix, for the checks below (1 byte per element; MXFP4: half)
     if (!w || (M != 0 && (!x || !y || (fused && (!r || !res)) || (q8 && (!q || !qscale)))))
         return ADDRMS_ERR_NULL;
     if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
@@ -349,15 +349,19 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
         return ADDRMS_ERR_EPS;
     const size_t mat = (size_t)M * (size_t)N * esize(dtype);
     const Span sx = span(x, mat), sw = span(w, (size_t)N * esize(w_dtype));
-    const Span sy = span(y, q8 ? (size_t)M * (size_t)N : mat);
+    const Span sy = span(y, q8 ? (size_t)M * (size_t)N / (qfmt == 1 ? 2 : 1) : mat);
     // FP8 scales: one per row (qgroup == 0, or a group spanning the row), else
     // one per group of qgroup columns
-    if (qgroup < 0)
+    // MXFP4 (qfmt 1): E2M1 codes two per byte, one E8M0 byte per 32 columns
+    const bool mx = qfmt == 1;
+    if (qgroup < 0 || (mx && N % 2 != 0))
         return ADDRMS_ERR_SHAPE;
-    if (qgroup >= N)
+    if (mx)
+        qgroup = 32;
+    else if (qgroup >= N)
         qgroup = 0;
     const int64_t ngroups = qgroup > 0 ? (N + qgroup - 1) / qgroup : 1;
-    const Span sqs = q8 ? span(qscale, (size_t)M * (size_t)ngroups * 4u) : Span{};
+    const Span sqs = q8 ? span(qscale, (size_t)M * (size_t)ngroups * (mx ? 1u : 4u)) : Span{};
     const Span sr = fused ? span(r, mat) : Span{}, sres = fused ? span(res, mat) : Span{};
     const Span srs = rstd ? span(rstd, (size_t)M * 4u) : Span{};
     const Span sb = b ? span(b, (size_t)N * esize(w_dtype)) : Span{};
@@ -395,6 +399,8 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     FwdArgs a{x, fused ? r : x, w, b, y, fused ? res : y, mean, rstd, q, qscale, M, (int)N, 0, eps};
     a.qgroup = (int)qgroup;
     a.qgroups = (int)ngroups;
+    // quantised mode, as an index of the tables (mode - 1)
+    const int qm = mx ? kQMx - 1 : qgroup > 0 ? kQGroup - 1 : kQRow - 1;
 
     const int nv = vec_elems(dtype);
     // grouped scales on the vector path: a group is a power of two of whole
@@ -406,7 +412,9 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
             qlanes = (int)L;
     }
     a.qlanes = qlanes;
-    const bool y_ok = q8 ? (reinterpret_cast<uintptr_t>(q) % (uintptr_t)nv) == 0 : aligned16(y);
+    // codes per 16-byte vector: nv bytes (E4M3) or nv / 2 (MXFP4), stored as one word
+    const bool y_ok = q8 ? (reinterpret_cast<uintptr_t>(q) % (uintptr_t)(mx ? nv / 2 : nv)) == 0
+                         : aligned16(y);
     const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(x) &&
                         aligned16(w) && y_ok && (!b || aligned16(b)) &&
                         (!fused || (aligned16(r) && aligned16(res))) &&
@@ -416,9 +424,10 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
         return rc;
     int wi = 0, vi = 0;
     if (vec_ok && pick_fwd(M, (int)(N / nv), cus, &wi, &vi) &&
-        (qlanes == 0 || kVplList[vi] <= kQGroupMaxVpl)) {
+        (!q8 || tab.vec_q8[fused ? 1 : 0][qm][wi][vi].fn != nullptr)) {
         a.nvec = (int)(N / nv);
-        const KernelRef &k = q8 ? tab.vec_q8[fused ? 1 : 0][wi][vi] : tab.vec[norm][fused ? 1 : 0][wi][vi];
+        const KernelRef &k =
+            q8 ? tab.vec_q8[fused ? 1 : 0][qm][wi][vi] : tab.vec[norm][fused ? 1 : 0][wi][vi];
         const int rpb = kWprList[wi] == 1 ? 4 : 1;
         const int64_t blocks = (M + rpb - 1) / rpb;
         // One block per row group (the hardware dispatcher balances the
@@ -429,7 +438,7 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
             return rc;
         return launch(k, dim3(grid), 0, &a, s);
     }
-    const KernelRef &k = q8 ? tab.elem_q8[fused ? 1 : 0] : tab.elem[norm][fused ? 1 : 0];
+    const KernelRef &k = q8 ? tab.elem_q8[fused ? 1 : 0][qm] : tab.elem[norm][fused ? 1 : 0];
     int grid = 0;
     if ((rc = persistent_grid(k, 0, M, INT_MAX, &grid)) != ADDRMS_OK)
         return rc;
@@ -749,6 +758,25 @@ int add_rmsnorm_fwd_fp8_grouped(const void *x, const void *r, const void *w, voi
         return ADDRMS_ERR_SHAPE;
     return fwd_common(kRms, x, r, w, nullptr, nullptr, residual_out, nullptr, rstd, M, N, eps,
                       dtype, w_dtype, stream, true, static_cast<uint8_t *>(y_fp8), y_scale, group);
+}
+
+int rmsnorm_fwd_mxfp4(const void *x, const void *w, void *y_fp4, void *y_scale, float *rstd,
+                      int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream)
+{
+    if (M != 0 && (!y_fp4 || !y_scale))
+        return ADDRMS_ERR_NULL;
+    return fwd_common(kRms, x, nullptr, w, nullptr, nullptr, nullptr, nullptr, rstd, M, N, eps,
+                      dtype, w_dtype, stream, false, static_cast<uint8_t *>(y_fp4), y_scale, 32, 1);
+}
+
+int add_rmsnorm_fwd_mxfp4(const void *x, const void *r, const void *w, void *y_fp4,
+                          void *y_scale, void *residual_out, float *rstd, int64_t M, int64_t N,
+                          float eps, int dtype, int w_dtype, void *stream)
+{
+    if (M != 0 && (!y_fp4 || !y_scale))
+        return ADDRMS_ERR_NULL;
+    return fwd_common(kRms, x, r, w, nullptr, nullptr, residual_out, nullptr, rstd, M, N, eps,
+                      dtype, w_dtype, stream, true, static_cast<uint8_t *>(y_fp4), y_scale, 32, 1);
 }
 
 int layernorm_fwd(const void *x, const void *w, const void *b, void *y, float *mean, float *rstd,

@@ -243,6 +243,30 @@ __device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b)
 #endif
 }
 
+// OCP FP4 E2M1 code (4 bits) of v: nearest of the magnitudes 0, 0.5, 1, 1.5,
+// 2, 3, 4, 6, ties to the even code, larger magnitudes saturating to 6, sign
+// kept.  The code is the number of rounding thresholds |v| has passed; each
+// threshold is a midpoint of the grid, taken with > where the lower code is
+// even (a tie stays) and >= where it is odd (a tie moves up).  NaN gives 0
+// or 8 (callers handle NaN blocks themselves).
+__device__ __forceinline__ uint32_t e2m1_code(float v)
+{
+    const float a = __builtin_fabsf(v);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// E8M0 exponent of an MX block from its largest magnitude g (finite, >= 0):
+// floor(log2(g)) - 2, clamped below at -127 (zero and tiny blocks).
+__device__ __forceinline__ int mx_exponent(float g)
+{
+    const int ef = (int)((__float_as_uint(g) >> 23) & 0xFFu);
+    const int e = ef == 0 ? -127 : ef - 129;
+    return e < -127 ? -127 : e;
+}
+
 // One DPP move of a float within 16-lane rows (source lanes must be active).
 template <int CTRL> __device__ __forceinline__ float dpp_f32(float v)
 {
@@ -266,6 +290,22 @@ __device__ __forceinline__ float group_max(float v, int L)
     v = __builtin_fmaxf(v, L >= 32 ? t16 : v);
     const float t32 = __shfl_xor(v, 32);
     return __builtin_fmaxf(v, L >= 64 ? t32 : v);
+}
+
+// Maximum over each aligned group of L lanes, L a compile-time power of two
+// up to 16 (the DPP steps of group_max only).
+template <int L> __device__ __forceinline__ float group_max_n(float v)
+{
+    static_assert(L >= 1 && L <= 16 && (L & (L - 1)) == 0, "L: power of two up to 16");
+    if constexpr (L >= 2)
+        v = __builtin_fmaxf(v, dpp_f32<0xB1>(v));
+    if constexpr (L >= 4)
+        v = __builtin_fmaxf(v, dpp_f32<0x4E>(v));
+    if constexpr (L >= 8)
+        v = __builtin_fmaxf(v, dpp_f32<0x141>(v));
+    if constexpr (L >= 16)
+        v = __builtin_fmaxf(v, dpp_f32<0x140>(v));
+    return v;
 }
 
 // The same sum for doubles (each DPP step moves both 32-bit halves).

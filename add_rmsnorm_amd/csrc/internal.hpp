@@ -18,8 +18,9 @@ struct FwdArgs {
     void *res;
     float *mean; // LayerNorm only; may be null
     float *rstd; // may be null
-    uint8_t *q;     // FP8 output variant: E4M3 codes [M, N]
-    float *qscale;  // FP8 output variant: scales [M] or [M, qgroups]
+    uint8_t *q;     // quantised output: E4M3 codes [M, N] or packed E2M1 [M, N/2]
+    void *qscale;   // its scales: float32 [M] or [M, qgroups] (E4M3), E8M0 bytes
+                    // [M, qgroups] (MXFP4)
     int64_t M;
     int N;
     int nvec; // 16-byte vectors per row (vector path)
@@ -90,13 +91,24 @@ constexpr int kBlockFwd(int wpr) { return wpr == 1 ? 256 : 64 * wpr; }
 // Forward (WPR, VPL) pairs that are built: 512- and 1024-thread blocks get at
 // most 256 / 128 VGPRs per lane, so they only take rows short enough per lane
 // to stay in registers.
-// Grouped FP8 scales on the vector path: compiled for at most this many
-// vectors per lane (more would spill registers); longer rows take the
-// element-wise path.
+// Quantised outputs with per-group scales (E4M3 groups, MXFP4 blocks) on the
+// vector path: instantiated for at most this many vectors per lane (with 8,
+// some variants spill registers); bf16 rows up to 32768 qualify, longer rows
+// take the element-wise path.
 constexpr int kQGroupMaxVpl = 4;
+constexpr int kMxMaxVpl = 4;
 constexpr bool fwd_built(int wpr, int vpl)
 {
     return wpr <= 4 || (wpr == 8 && vpl <= 8) || (wpr == 16 && vpl <= 4);
+}
+// Quantised outputs of the forward (RMSNorm): none; E4M3 with one float32
+// scale per row; E4M3 with one per group of columns; MXFP4 (E2M1 codes two
+// per byte, one E8M0 scale byte per 32 values).  Each is its own kernel.
+enum QMode : int { kQNone = 0, kQRow = 1, kQGroup = 2, kQMx = 3 };
+constexpr bool q_built(int qm, int wpr, int vpl)
+{
+    return fwd_built(wpr, vpl) && (qm != kQGroup || vpl <= kQGroupMaxVpl) &&
+           (qm != kQMx || vpl <= kMxMaxVpl);
 }
 // Backward variants that are instantiated.  The LayerNorm backward with the
 // residual gradient at 16 vectors per lane needs more than the 512 VGPRs a
@@ -130,9 +142,9 @@ inline int combo(int dtype, int w_dtype) { return dtype * 2 + w_dtype; }
 struct FwdTable {
     KernelRef vec[2][2][kNumWpr][kNumVpl];
     KernelRef elem[2][2];
-    // RMSNorm with an E4M3 output and per-row scale: [fused][wpr][vpl], [fused]
-    KernelRef vec_q8[2][kNumWpr][kNumVpl];
-    KernelRef elem_q8[2];
+    // RMSNorm with a quantised output: [fused][mode - 1][wpr][vpl], [fused][mode - 1]
+    KernelRef vec_q8[2][3][kNumWpr][kNumVpl];
+    KernelRef elem_q8[2][3];
 };
 // bwd vec: [norm][with residual gradient][wpr_idx][vpl_idx]; elem_dx:
 // [norm][with residual gradient]; elem_dw: [norm].

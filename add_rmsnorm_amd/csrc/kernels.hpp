@@ -67,13 +67,14 @@ __device__ __forceinline__ double fma_ct(double a, double b, double c) { return 
 // NORM = kLayer: y = (h - mean) * rstd * w (+ b), rstd = 1/sqrt(var + eps),
 // the variance taken about the mean from the registers (two passes over the
 // row, one over memory).
-// Q8 (RMSNorm only): y is not stored; instead its absmax sets a scale
-// (scale = amax/448, inv = 448/amax, binary32), per row or, with a.qlanes > 0,
-// per group of a.qlanes consecutive vectors (a group maximum over that many
-// lanes), and y * inv is written as OCP E4M3 codes, one byte per element, for
-// a downstream FP8 GEMM.
+// QM != kQNone (RMSNorm only): y is not stored but quantised for a
+// downstream low-precision GEMM.  kQRow / kQGroup: its absmax sets a scale
+// (scale = amax/448, inv = 448/amax, binary32), per row or per group of
+// a.qlanes consecutive vectors (a group maximum over that many lanes), and
+// y * inv is written as OCP E4M3 codes, one byte per element.  kQMx: MXFP4,
+// one E8M0 scale per 32 values and E2M1 codes, two per byte.
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, int NORM, bool FUSED, bool Q8, int WPR, int VPL>
+template <typename T, typename WT, int NORM, bool FUSED, int QM, int WPR, int VPL>
 __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
@@ -198,8 +199,8 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
         if (a.rstd != nullptr && wir == 0 && lane == 0)
             a.rstd[row] = rs;
 
-        if constexpr (Q8) {
-            // 4'. y in registers, row absmax, scale, E4M3 codes
+        if constexpr (QM != kQNone) {
+            // 4'. y in registers, then its quantised form instead of y
             float o[VPL][NV];
             float am = 0.0f;
 #pragma unroll
@@ -212,59 +213,102 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 #pragma unroll
                 for (int e = 0; e < NV; ++e) {
                     o[k][e] = v < nvec ? (h[e] * rs) * wf[e] : 0.0f;
-                    am = __builtin_fmaxf(am, __builtin_fabsf(o[k][e]));
+                    if constexpr (QM == kQRow)
+                        am = __builtin_fmaxf(am, __builtin_fabsf(o[k][e]));
                 }
             }
-            // one scale per row, or (qlanes > 0) one per group of qlanes
-            // consecutive vectors, which sit in qlanes consecutive lanes
-            float inv_k[VPL];
-            if (VPL > kQGroupMaxVpl || a.qlanes == 0) {
-                am = row_max(am, slot + 1);
-                float inv = 1.0f, sc = 1.0f;
-                if (am != 0.0f) {
-                    inv = 448.0f / am;
-                    sc = am / 448.0f;
-                }
-                if (wir == 0 && lane == 0)
-                    a.qscale[row] = sc;
-#pragma unroll
-                for (int k = 0; k < VPL; ++k)
-                    inv_k[k] = inv;
-            } else if constexpr (VPL <= kQGroupMaxVpl) {
+            if constexpr (QM == kQMx) {
+                // MXFP4: blocks of 32 values (32 / NV lanes); a NaN makes the
+                // block's maximum +Inf (y is never infinite), which marks the
+                // block NaN: scale 0xFF, codes 0
+                uint8_t *qrow4 = a.q + base / 2;
+                uint8_t *srow = static_cast<uint8_t *>(a.qscale) + (size_t)row * (size_t)a.qgroups;
 #pragma unroll
                 for (int k = 0; k < VPL; ++k) {
                     const int v = vbase + k * VSTRIDE;
                     float g = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < NV; ++e)
-                        g = __builtin_fmaxf(g, __builtin_fabsf(o[k][e]));
-                    g = group_max(g, a.qlanes);
-                    float inv = 1.0f, sc = 1.0f;
-                    if (g != 0.0f) {
-                        inv = 448.0f / g;
-                        sc = g / 448.0f;
+                    for (int e = 0; e < NV; ++e) {
+                        const float m = __builtin_fabsf(o[k][e]);
+                        g = __builtin_fmaxf(g, m != m ? __builtin_inff() : m);
                     }
-                    if (v < nvec && (lane & (a.qlanes - 1)) == 0)
-                        a.qscale[(size_t)row * (size_t)a.qgroups + (size_t)(v / a.qlanes)] = sc;
-                    inv_k[k] = inv;
+                    g = group_max_n<32 / NV>(g);
+                    const bool nanb = g == __builtin_inff();
+                    const int E = mx_exponent(g);
+                    const float inv = __uint_as_float((uint32_t)(127 - E) << 23); // 2^-E
+                    if (v < nvec && (lane & (32 / NV - 1)) == 0)
+                        srow[v / (32 / NV)] = nanb ? (uint8_t)0xFF : (uint8_t)(E + 127);
+                    if (v < nvec) {
+                        uint32_t word = 0;
+#pragma unroll
+                        for (int e = 0; e < NV; ++e)
+                            word |= (nanb ? 0u : e2m1_code(o[k][e] * inv)) << (4 * e);
+                        if constexpr (NV == 8)
+                            __builtin_nontemporal_store(
+                                word, reinterpret_cast<uint32_t *>(qrow4 + (size_t)v * 4));
+                        else
+                            __builtin_nontemporal_store(
+                                (uint16_t)word, reinterpret_cast<uint16_t *>(qrow4 + (size_t)v * 2));
+                    }
                 }
-            }
-            uint8_t *qrow = a.q + base;
+            } else {
+                // E4M3: one scale per row (kQRow), or one per group of
+                // a.qlanes consecutive vectors, which sit in as many
+                // consecutive lanes (kQGroup)
+                float inv_k[VPL];
+                if constexpr (QM == kQRow) {
+                    am = row_max(am, slot + 1);
+                    float inv = 1.0f, sc = 1.0f;
+                    if (am != 0.0f) {
+                        inv = 448.0f / am;
+                        sc = am / 448.0f;
+                    }
+                    if (wir == 0 && lane == 0)
+                        static_cast<float *>(a.qscale)[row] = sc;
 #pragma unroll
-            for (int k = 0; k < VPL; ++k) {
-                const int v = vbase + k * VSTRIDE;
-                const float inv = inv_k[k];
-                if (v < nvec) {
-                    uint32_t wd[NV / 4];
+                    for (int k = 0; k < VPL; ++k)
+                        inv_k[k] = inv;
+                } else {
+                    float *srow = static_cast<float *>(a.qscale) + (size_t)row * (size_t)a.qgroups;
 #pragma unroll
-                    for (int i = 0; i < NV / 4; ++i)
-                        wd[i] = pack_e4m3x2(e4m3_clamp(o[k][4 * i] * inv), e4m3_clamp(o[k][4 * i + 1] * inv)) |
-                                (pack_e4m3x2(e4m3_clamp(o[k][4 * i + 2] * inv), e4m3_clamp(o[k][4 * i + 3] * inv)) << 16);
-                    if constexpr (NV == 8)
-                        __builtin_nontemporal_store(u32x2{wd[0], wd[1]},
-                                                    reinterpret_cast<u32x2 *>(qrow + (size_t)v * 8));
-                    else
-                        __builtin_nontemporal_store(wd[0], reinterpret_cast<uint32_t *>(qrow + (size_t)v * 4));
+                    for (int k = 0; k < VPL; ++k) {
+                        const int v = vbase + k * VSTRIDE;
+                        float g = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < NV; ++e)
+                            g = __builtin_fmaxf(g, __builtin_fabsf(o[k][e]));
+                        g = group_max(g, a.qlanes);
+                        float inv = 1.0f, sc = 1.0f;
+                        if (g != 0.0f) {
+                            inv = 448.0f / g;
+                            sc = g / 448.0f;
+                        }
+                        if (v < nvec && (lane & (a.qlanes - 1)) == 0)
+                            srow[v / a.qlanes] = sc;
+                        inv_k[k] = inv;
+                    }
+                }
+                uint8_t *qrow = a.q + base;
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) {
+                    const int v = vbase + k * VSTRIDE;
+                    const float inv = inv_k[k];
+                    if (v < nvec) {
+                        uint32_t wd[NV / 4];
+#pragma unroll
+                        for (int i = 0; i < NV / 4; ++i)
+                            wd[i] = pack_e4m3x2(e4m3_clamp(o[k][4 * i] * inv),
+                                                e4m3_clamp(o[k][4 * i + 1] * inv)) |
+                                    (pack_e4m3x2(e4m3_clamp(o[k][4 * i + 2] * inv),
+                                                 e4m3_clamp(o[k][4 * i + 3] * inv))
+                                     << 16);
+                        if constexpr (NV == 8)
+                            __builtin_nontemporal_store(
+                                u32x2{wd[0], wd[1]}, reinterpret_cast<u32x2 *>(qrow + (size_t)v * 8));
+                        else
+                            __builtin_nontemporal_store(
+                                wd[0], reinterpret_cast<uint32_t *>(qrow + (size_t)v * 4));
+                    }
                 }
             }
             continue;
@@ -329,7 +373,7 @@ __device__ __forceinline__ float block256_max(float v, float (&part)[NS][4], int
                            __builtin_fmaxf(part[slot][2], part[slot][3]));
 }
 
-template <typename T, typename WT, int NORM, bool FUSED, bool Q8>
+template <typename T, typename WT, int NORM, bool FUSED, int QM>
 __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 {
     __shared__ float part[4][4];
@@ -369,30 +413,54 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
         }
         if (a.rstd != nullptr && tid == 0)
             a.rstd[row] = rs;
-        if constexpr (Q8) {
-            if (a.qgroup > 0) {
-                // one scale per group of qgroup columns: each thread takes
-                // whole groups
-                const int G = a.qgroup;
-                for (int g = tid; g < a.qgroups; g += 256) {
-                    const int j0 = g * G, j1 = j0 + G < N ? j0 + G : N;
-                    float am = 0.0f;
-                    for (int j = j0; j < j1; ++j)
-                        am = __builtin_fmaxf(am, __builtin_fabsf((ld_elem<T>(src, base + j) * rs) *
-                                                                 ld_elem<WT>(a.w, j)));
-                    float inv = 1.0f, sc = 1.0f;
-                    if (am != 0.0f) {
-                        inv = 448.0f / am;
-                        sc = am / 448.0f;
-                    }
-                    a.qscale[row * (int64_t)a.qgroups + g] = sc;
-                    for (int j = j0; j < j1; ++j) {
-                        const float o = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
-                        a.q[base + j] = (uint8_t)pack_e4m3x2(e4m3_clamp(o * inv), 0.0f);
-                    }
+        if constexpr (QM == kQMx) {
+            // MXFP4: each thread takes whole blocks of 32 columns
+            for (int g = tid; g < a.qgroups; g += 256) {
+                const int j0 = g * 32, j1 = j0 + 32 < N ? j0 + 32 : N;
+                float am = 0.0f;
+                bool nanb = false;
+                for (int j = j0; j < j1; ++j) {
+                    const float o = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
+                    nanb = nanb || o != o;
+                    am = __builtin_fmaxf(am, __builtin_fabsf(o));
                 }
-                continue;
+                const int E = mx_exponent(am);
+                const float inv = __uint_as_float((uint32_t)(127 - E) << 23);
+                static_cast<uint8_t *>(a.qscale)[row * (int64_t)a.qgroups + g] =
+                    nanb ? (uint8_t)0xFF : (uint8_t)(E + 127);
+                for (int j = j0; j < j1; j += 2) {
+                    const float o0 = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
+                    const float o1 = (ld_elem<T>(src, base + j + 1) * rs) * ld_elem<WT>(a.w, j + 1);
+                    a.q[(base + j) / 2] =
+                        nanb ? (uint8_t)0 : (uint8_t)(e2m1_code(o0 * inv) | (e2m1_code(o1 * inv) << 4));
+                }
             }
+            continue;
+        }
+        if constexpr (QM == kQGroup) {
+            // one scale per group of qgroup columns: each thread takes whole
+            // groups
+            const int G = a.qgroup;
+            for (int g = tid; g < a.qgroups; g += 256) {
+                const int j0 = g * G, j1 = j0 + G < N ? j0 + G : N;
+                float am = 0.0f;
+                for (int j = j0; j < j1; ++j)
+                    am = __builtin_fmaxf(am, __builtin_fabsf((ld_elem<T>(src, base + j) * rs) *
+                                                             ld_elem<WT>(a.w, j)));
+                float inv = 1.0f, sc = 1.0f;
+                if (am != 0.0f) {
+                    inv = 448.0f / am;
+                    sc = am / 448.0f;
+                }
+                static_cast<float *>(a.qscale)[row * (int64_t)a.qgroups + g] = sc;
+                for (int j = j0; j < j1; ++j) {
+                    const float o = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
+                    a.q[base + j] = (uint8_t)pack_e4m3x2(e4m3_clamp(o * inv), 0.0f);
+                }
+            }
+            continue;
+        }
+        if constexpr (QM == kQRow) {
             float am = 0.0f;
             for (int j = tid; j < N; j += 256)
                 am = __builtin_fmaxf(am, __builtin_fabsf((ld_elem<T>(src, base + j) * rs) *
@@ -404,7 +472,7 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
                 sc = am / 448.0f;
             }
             if (tid == 0)
-                a.qscale[row] = sc;
+                static_cast<float *>(a.qscale)[row] = sc;
             for (int j = tid; j < N; j += 256) {
                 const float o = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
                 a.q[base + j] = (uint8_t)pack_e4m3x2(e4m3_clamp(o * inv), 0.0f);
@@ -807,45 +875,53 @@ __global__ void __launch_bounds__(256)
 // Kernel tables for one (row dtype, weight dtype) combination.
 // ---------------------------------------------------------------------------
 template <typename T, typename WT> struct TableBuilder {
-    template <int NM, bool F, bool Q8, int WPR, int VPL> static KernelRef fwd_ref()
+    template <int NM, bool F, int QM, int WPR, int VPL> static KernelRef fwd_ref()
     {
-        if constexpr (fwd_built(WPR, VPL))
+        if constexpr (QM == kQNone ? fwd_built(WPR, VPL) : q_built(QM, WPR, VPL))
             return KernelRef{
-                reinterpret_cast<const void *>(&fwd_vec_kernel<T, WT, NM, F, Q8, WPR, VPL>),
+                reinterpret_cast<const void *>(&fwd_vec_kernel<T, WT, NM, F, QM, WPR, VPL>),
                 kBlockFwd(WPR)};
         else
             return KernelRef{nullptr, 0};
     }
-    template <int NM, bool F, bool Q8, int WI, int... VI>
+    template <int NM, bool F, int QM, int WI, int... VI>
     static void fwd_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
     {
-        ((row[VI] = fwd_ref<NM, F, Q8, kWprList[WI], kVplList[VI]>()), ...);
+        ((row[VI] = fwd_ref<NM, F, QM, kWprList[WI], kVplList[VI]>()), ...);
     }
-    template <int NM, bool F, bool Q8, int... WI>
+    template <int NM, bool F, int QM, int... WI>
     static void fwd_all(KernelRef (&tab)[kNumWpr][kNumVpl], std::integer_sequence<int, WI...>)
     {
-        (fwd_row<NM, F, Q8, WI>(tab[WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
+        (fwd_row<NM, F, QM, WI>(tab[WI], std::make_integer_sequence<int, kNumVpl>{}), ...);
+    }
+    template <bool F, int QM> static KernelRef elem_ref()
+    {
+        return KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, kRms, F, QM>), 256};
     }
     template <int NM> static void fwd_norm(FwdTable &t)
     {
-        fwd_all<NM, false, false>(t.vec[NM][0], std::make_integer_sequence<int, kNumWpr>{});
-        fwd_all<NM, true, false>(t.vec[NM][1], std::make_integer_sequence<int, kNumWpr>{});
-        t.elem[NM][0] =
-            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, false, false>), 256};
-        t.elem[NM][1] =
-            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, true, false>), 256};
+        fwd_all<NM, false, kQNone>(t.vec[NM][0], std::make_integer_sequence<int, kNumWpr>{});
+        fwd_all<NM, true, kQNone>(t.vec[NM][1], std::make_integer_sequence<int, kNumWpr>{});
+        t.elem[NM][0] = KernelRef{
+            reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, false, kQNone>), 256};
+        t.elem[NM][1] = KernelRef{
+            reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, NM, true, kQNone>), 256};
+    }
+    template <int QM> static void fwd_quant(FwdTable &t)
+    {
+        fwd_all<kRms, false, QM>(t.vec_q8[0][QM - 1], std::make_integer_sequence<int, kNumWpr>{});
+        fwd_all<kRms, true, QM>(t.vec_q8[1][QM - 1], std::make_integer_sequence<int, kNumWpr>{});
+        t.elem_q8[0][QM - 1] = elem_ref<false, QM>();
+        t.elem_q8[1][QM - 1] = elem_ref<true, QM>();
     }
     static FwdTable fwd()
     {
         FwdTable t{};
         fwd_norm<kRms>(t);
         fwd_norm<kLayer>(t);
-        fwd_all<kRms, false, true>(t.vec_q8[0], std::make_integer_sequence<int, kNumWpr>{});
-        fwd_all<kRms, true, true>(t.vec_q8[1], std::make_integer_sequence<int, kNumWpr>{});
-        t.elem_q8[0] =
-            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, kRms, false, true>), 256};
-        t.elem_q8[1] =
-            KernelRef{reinterpret_cast<const void *>(&fwd_elem_kernel<T, WT, kRms, true, true>), 256};
+        fwd_quant<kQRow>(t);
+        fwd_quant<kQGroup>(t);
+        fwd_quant<kQMx>(t);
         return t;
     }
 

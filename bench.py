@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, bf16 fused Add+RMSNorm M=16384 N=7168"
 WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
-HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, false, 8, 2>"
+HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 0, 8, 2>"
 KERNEL_SOURCES = ["add_rmsnorm_amd/csrc/kernels.hpp", "add_rmsnorm_amd/csrc/device.hpp",
                   "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp",
                   "add_rmsnorm_amd/csrc/api.hip"]
@@ -399,7 +399,24 @@ def secondary(steps: int):
                                                                        HBM_PEAK_GBPS, 1),
         "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
         "note": "as above with one fp32 scale per 128 columns (56 per row)"}
-    del sets, sg
+    # MXFP4: E2M1 codes two per byte, one E8M0 scale byte per 32 values
+    mq = [torch.empty(M, N // 2, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ms = [torch.empty(M, N // 32, dtype=torch.uint8, device="cuda") for _ in range(2)]
+
+    def mx():
+        x, r, _, _, res = sets[i[0] & 1]
+        ar.add_rmsnorm_fwd_mxfp4(x, r, w, 1e-6, y_fp4=mq[i[0] & 1], y_scale=ms[i[0] & 1],
+                                 residual_out=res)
+        i[0] += 1
+
+    _, ev = timed(mx, steps, 5)
+    nb = 4 * M * N + 2 * M * N + M * N // 2 + M * (N // 32) + 2 * N
+    out["add_rmsnorm_fwd_mxfp4_16384x7168"] = {
+        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
+                                                                       HBM_PEAK_GBPS, 1),
+        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
+        "note": "bf16 x, r in; bf16 residual_out + MXFP4 y (E2M1 x2 per byte + E8M0 per 32) out"}
+    del sets, sg, mq, ms
     # LayerNorm: fused forward with bias at the headline shape, backward (dw, db)
     # at the backward workload's shape
     M, N = 16384, 7168

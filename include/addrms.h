@@ -194,6 +194,33 @@ int add_rmsnorm_fwd_fp8_grouped(const void *x, const void *r, const void *w, voi
                                 void *stream);
 
 /*
+ * RMSNorm / fused Add + RMSNorm with an MXFP4 output (the "Machete" README's
+ * "Built-In Areas" lists MXFP4 decode kernels; the format is OCP Microscaling
+ * Formats v1.0 MXFP4).  y is computed as in rmsnorm_fwd / add_rmsnorm_fwd in
+ * float32 but not stored.  For each block of 32 consecutive values of a row
+ * (the last block may be shorter):
+ *     a NaN in the block:  scale byte 0xFF (NaN), codes 0
+ *     otherwise:           E = floor(log2(max |y|)) - 2, clamped below at -127
+ *                          (an all-zero block has E = -127)
+ *                          scale byte = E + 127 (E8M0: the scale is 2^E)
+ *                          q_j = E2M1(y_j / 2^E)
+ * E2M1 is the 4-bit float (sign, 2 exponent bits, 1 mantissa bit) with the
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, rounded to nearest with ties to the
+ * even code and saturating at 6; y_j ~= decode(q_j) * 2^E.
+ *   y_fp4    [M, N/2]         uint8  output, two codes per byte, element 2i
+ *                                    in the low nibble; N must be even
+ *   y_scale  [M, ceil(N/32)]  uint8  output E8M0 scale bytes
+ * Other arguments as rmsnorm_fwd / add_rmsnorm_fwd (residual_out is still
+ * written in the input dtype).
+ */
+int rmsnorm_fwd_mxfp4(const void *x, const void *w, void *y_fp4, void *y_scale, float *rstd,
+                      int64_t M, int64_t N, float eps, int dtype, int w_dtype, void *stream);
+
+int add_rmsnorm_fwd_mxfp4(const void *x, const void *r, const void *w, void *y_fp4,
+                          void *y_scale, void *residual_out, float *rstd, int64_t M, int64_t N,
+                          float eps, int dtype, int w_dtype, void *stream);
+
+/*
  * LayerNorm variants.  The "CuTe DSL" skill page lists a CTA-level LayerNorm
  * example (Workflow 0, example index) and names LayerNorm beside RMSNorm in
  * its float32 reduction pattern (Workflow 0); the formula is the textbook one

@@ -45,6 +45,8 @@ def lib():
     lib.rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, vp, vp, i64, vp, i64, i64, f32, i32, i32, vp]
     lib.add_rmsnorm_fwd_fp8_grouped.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, f32,
                                                 i32, i32, vp]
+    lib.rmsnorm_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.add_rmsnorm_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.rmsnorm_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
                                     i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.addrms_status_str.restype = ctypes.c_char_p
@@ -58,7 +60,8 @@ def test_header_declares_the_entry_points():
                                   "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
                                   "layernorm_bwd_workspace_bytes", "add_layernorm_bwd",
                                   "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_fp8_grouped",
-                                  "add_rmsnorm_fwd_fp8_grouped", "rmsnorm_rope_qk",
+                                  "add_rmsnorm_fwd_fp8_grouped", "rmsnorm_fwd_mxfp4",
+                                  "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
                                   "addrms_status_str", "addrms_last_hip_error"])
 
 
@@ -280,3 +283,19 @@ def test_fp8_grouped_validation(lib):
                                                     k.get("res", D), None, 4, 64, 1e-6, BF16,
                                                     BF16, None)
     assert g(g=0) == E_SHAPE and g(res=None) == E_NULL and g(s=D + 8) == E_ALIAS
+
+
+def test_mxfp4_validation(lib):
+    Q, S = 0x78000000, 0x7C000000
+    f = lambda **k: lib.rmsnorm_fwd_mxfp4(k.get("x", A), W, k.get("q", Q), k.get("s", S), None,
+                                          k.get("M", 4), k.get("N", 64), 1e-6, BF16, BF16, None)
+    assert f(N=63) == E_SHAPE                       # two codes per byte: N must be even
+    assert f(q=None) == E_NULL and f(s=None) == E_NULL
+    assert f(M=0, q=None, s=None) == OK
+    # codes: 4 rows x 32 bytes = 128 bytes; scales: 4 x 2 = 8 bytes
+    assert f(s=Q + 124) == E_ALIAS                  # scales run into the codes' tail
+    assert f(q=A + 64) == E_ALIAS                   # codes inside x
+    g = lambda **k: lib.add_rmsnorm_fwd_mxfp4(A, C, W, k.get("q", Q), k.get("s", S),
+                                              k.get("res", D), None, 4, 64, 1e-6, BF16, BF16,
+                                              None)
+    assert g(res=None) == E_NULL and g(q=C) == E_ALIAS and g(s=D + 8) == E_ALIAS

@@ -1,0 +1,158 @@
+"""GPU parity of the MXFP4-output RMSNorm (rmsnorm_fwd_mxfp4 /
+add_rmsnorm_fwd_mxfp4 through the C ABI) against the CPU oracle.
+
+The residual is compared bit for bit. The GPU computes y in float32; the
+oracle rounds a binary64 y once to float32. Their block scales and element
+codes can therefore differ only where a decision is within a relative 2^-20
+of its boundary: a block maximum next to a power of two (the scale), or a
+scaled value next to an E2M1 midpoint (the code). Every decision away from a
+boundary must match exactly. Every scale must be within one of the oracle's.
+Every element must decode, at the GPU's own scale, to within half a grid
+step of the binary64 y (or to +-6 times the scale when saturated). NaN rows
+give NaN scales (0xFF) and zero codes."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import add_rmsnorm_amd as ar
+import oracle
+import synth
+from parity import assert_bits_equal
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+REL = 2.0 ** -20
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def check_mx(q_gpu, s_gpu, q_ref, s_ref, y64, what):
+    assert q_gpu.dtype == torch.float4_e2m1fn_x2 and s_gpu.dtype == torch.float8_e8m0fnu
+    # the scale bytes decode through torch's own E8M0 type as 2^(byte - 127)
+    sb = s_gpu.view(torch.uint8).cpu().numpy().astype(np.int64)
+    sf = s_gpu.cpu().float().numpy().astype(np.float64)
+    fin = sb != 255
+    np.testing.assert_array_equal(sf[fin], np.exp2(sb[fin] - 127.0))
+    codes = oracle.unpack_fp4(q_gpu.view(torch.uint8).cpu())
+    rcodes = oracle.unpack_fp4(q_ref)
+    rs = s_ref.numpy().astype(np.int64)
+    y = y64.numpy()
+    M, N = y.shape
+    nb = (N + 31) // 32
+    assert sb.shape == rs.shape == (M, nb)
+    nanrow = np.isnan(y).any(axis=1)
+    assert np.all(sb[nanrow] == 255) and np.all(codes[nanrow] == 0), f"NaN rows {what}"
+    assert np.all(sb[~nanrow] != 255), f"finite rows {what}"
+    yf = y.astype(np.float32).astype(np.float64)
+    blk = np.arange(N) // 32
+    for b in range(nb):
+        cols = blk == b
+        amax = np.abs(yf[:, cols]).max(axis=1)
+        e_lo = np.floor(np.log2(np.maximum(amax * (1 - REL), 1e-300)))
+        e_hi = np.floor(np.log2(np.maximum(amax * (1 + REL), 1e-300)))
+        robust = (e_lo == e_hi) | (amax == 0)
+        ok = ~nanrow
+        bad = ok & robust & (sb[:, b] != rs[:, b])
+        assert not bad.any(), (f"scales {what}: block {b}, rows {np.nonzero(bad)[0][:5]}, "
+                               f"gpu {sb[bad, b][:5]} ref {rs[bad, b][:5]}")
+        assert np.all(np.abs(sb[ok, b] - rs[ok, b]) <= 1), f"scales {what}: block {b} off by > 1"
+        # codes: exact where the block scale agrees and the scaled value is not
+        # next to a midpoint
+        X = np.exp2(rs[:, b] - 127.0)[:, None]
+        v = yf[:, cols] / X
+        lo = oracle.fp4e2m1_encode(v * (1 - REL))
+        hi = oracle.fp4e2m1_encode(v * (1 + REL))
+        same = (sb[:, b] == rs[:, b])[:, None] & (lo == hi) & ok[:, None]
+        cg, cr = codes[:, cols], rcodes[:, cols]
+        canon = lambda c: np.where((c & 0x7) == 0, 0, c)   # a zero may carry either sign
+        mism = same & (canon(cg) != canon(cr))
+        assert not mism.any(), (f"codes {what}: block {b}, {int(mism.sum())} differ; "
+                                f"first gpu {cg[mism][0]:#x} ref {cr[mism][0]:#x}")
+        # every element at the GPU's own scale
+        Xg = np.exp2(sb[:, b] - 127.0)[:, None]
+        vg = y[:, cols] / Xg
+        deq = oracle.fp4e2m1_decode(cg)
+        spacing = np.where(np.abs(vg) < 2, 0.5, np.where(np.abs(vg) < 4, 1.0, 2.0))
+        sat = np.abs(vg) > 6
+        err_ok = np.where(sat, deq == np.sign(vg) * 6,
+                          np.abs(deq - vg) <= spacing / 2 * (1 + 1e-5) + 1e-5 * np.abs(vg))
+        assert np.all(err_ok[ok]), f"dequantised {what}: block {b}"
+
+
+def run(x, r, w, eps, what):
+    g = lambda t: t.to(DEV)
+    if r is None:
+        q, s = ar.rmsnorm_fwd_mxfp4(g(x), g(w), eps)
+        qr, sr, _ = oracle.rmsnorm_fwd_mxfp4(x, w, eps)
+        y64, _ = oracle.rmsnorm_fwd(x, w, eps, y_dtype=torch.float64)
+    else:
+        q, s, res = ar.add_rmsnorm_fwd_mxfp4(g(x), g(r), g(w), eps)
+        qr, sr, rres, _ = oracle.rmsnorm_fwd_mxfp4(x, w, eps, residual=r)
+        torch.cuda.synchronize()
+        assert_bits_equal(res.cpu(), rres, f"residual_out {what}")
+        y64, _ = oracle.rmsnorm_fwd(rres, w, eps, y_dtype=torch.float64)
+    torch.cuda.synchronize()
+    check_mx(q, s, qr, sr, y64, what)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_full_shape(fused):
+    inp = synth.add_rmsnorm_fwd_inputs(16384, 7168, torch.bfloat16, seed=91, r_std=0.5)
+    run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, "16384x7168")
+
+
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.float32, torch.float32),
+                                          (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.bfloat16)])
+@pytest.mark.parametrize("N", [32, 48, 64, 1000, 4096, 8192, 16384, 24576, 65536])
+def test_shapes_and_dtypes(dtype, wdtype, N):
+    # 48 and 1000: a ragged last block; 65536: more than 4 vectors per lane,
+    # the element-wise path
+    M = max(2, min(40, (1 << 20) // N))
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, wdtype, seed=N + 7)
+    run(inp["x"], inp["r"], inp["w"], 1e-6, f"{dtype} N={N}")
+
+
+@pytest.mark.parametrize("M", [1, 32, 512])
+def test_decode_with_outliers(M):
+    inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_decode_n8192", M=M)
+    run(inp["x"], inp["r"], inp["w"], 1e-5, f"decode M={M}")
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8, 16])
+def test_forced_waves_per_row(monkeypatch, wpr):
+    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+    inp = synth.add_rmsnorm_fwd_inputs(37, 4096, torch.bfloat16, seed=wpr + 90)
+    run(inp["x"], inp["r"], inp["w"], 1e-6, f"wpr={wpr}")
+
+
+def test_elementwise_forced(monkeypatch):
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    inp = synth.add_rmsnorm_fwd_inputs(13, 4096, torch.bfloat16, seed=93)
+    run(inp["x"], inp["r"], inp["w"], 1e-6, "elem")
+    run(inp["x"], None, inp["w"], 1e-6, "elem plain")
+
+
+def test_special_rows():
+    N = 1024
+    inp = synth.add_rmsnorm_fwd_inputs(4, N, torch.bfloat16, seed=95)
+    x = inp["x"].clone()
+    x[0] = 0                   # zero row: every scale 2^-127 (byte 0), codes 0
+    x[1, 77] = float("nan")    # NaN row
+    x[2] = 2.0                 # constant row
+    q, s = ar.rmsnorm_fwd_mxfp4(x.to(DEV), inp["w"].to(DEV), 1e-6)
+    torch.cuda.synchronize()
+    sb = s.view(torch.uint8).cpu()
+    qb = q.view(torch.uint8).cpu()
+    assert torch.all(sb[0] == 0) and torch.all(qb[0] == 0)
+    assert torch.all(sb[1] == 255) and torch.all(qb[1] == 0)
+    run(x, None, inp["w"], 1e-6, "special rows")

@@ -29,8 +29,8 @@ LIB = os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms.so")
 LLVM = "/opt/rocm/llvm/bin"
 MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
-HEADLINE = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELb0ELi8ELi2EEEvNS_7FwdArgsE"
-FP8_FUSED = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELb1ELi8ELi2EEEvNS_7FwdArgsE"
+HEADLINE = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELi0ELi8ELi2EEEvNS_7FwdArgsE"
+FP8_FUSED = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELi1ELi8ELi2EEEvNS_7FwdArgsE"
 ROPE_D128 = "_ZN6addrms15rope_vec_kernelINS_6bf16_tES1_Li8ELb0ELi4EEEvNS_8RopeArgsE"
 
 
