@@ -24,12 +24,12 @@ import torch
 from torch import Tensor
 
 from . import (add_layernorm_bwd, add_layernorm_fwd, add_rmsnorm_bwd, add_rmsnorm_fwd,
-               add_rmsnorm_fwd_fp8, layernorm_bwd, layernorm_fwd, rmsnorm_bwd, rmsnorm_fwd,
-               rmsnorm_fwd_fp8, rmsnorm_rope_qk)
+               add_rmsnorm_fwd_fp8, add_rmsnorm_fwd_mxfp4, layernorm_bwd, layernorm_fwd,
+               rmsnorm_bwd, rmsnorm_fwd, rmsnorm_fwd_fp8, rmsnorm_fwd_mxfp4, rmsnorm_rope_qk)
 
 __all__ = ["rms_norm", "add_rms_norm", "layer_norm", "add_layer_norm", "rms_norm_fp8",
-           "add_rms_norm_fp8", "rms_norm_rope_qk", "RMSNorm", "AddRMSNorm", "LayerNorm",
-           "AddLayerNorm"]
+           "add_rms_norm_fp8", "rms_norm_mxfp4", "add_rms_norm_mxfp4", "rms_norm_rope_qk",
+           "RMSNorm", "AddRMSNorm", "LayerNorm", "AddLayerNorm"]
 
 
 # ---- forward / backward ops -------------------------------------------------
@@ -247,6 +247,34 @@ def _(x, r, w, eps, group):
             x.new_empty(_scale_shape(x, group), dtype=torch.float32), torch.empty_like(x))
 
 
+def _mx_shapes(x: Tensor):
+    N = x.shape[-1]
+    return x.shape[:-1] + (N // 2,), x.shape[:-1] + ((N + 31) // 32,)
+
+
+@torch.library.custom_op("addrms::rms_norm_mxfp4", mutates_args=())
+def _rms_norm_mxfp4(x: Tensor, w: Tensor, eps: float) -> Tuple[Tensor, Tensor]:
+    return rmsnorm_fwd_mxfp4(x.contiguous(), w.contiguous(), eps)
+
+
+@_rms_norm_mxfp4.register_fake
+def _(x, w, eps):
+    cs, ss = _mx_shapes(x)
+    return x.new_empty(cs, dtype=torch.float4_e2m1fn_x2), x.new_empty(ss, dtype=torch.float8_e8m0fnu)
+
+
+@torch.library.custom_op("addrms::add_rms_norm_mxfp4", mutates_args=())
+def _add_rms_norm_mxfp4(x: Tensor, r: Tensor, w: Tensor, eps: float) -> Tuple[Tensor, Tensor, Tensor]:
+    return add_rmsnorm_fwd_mxfp4(x.contiguous(), r.contiguous(), w.contiguous(), eps)
+
+
+@_add_rms_norm_mxfp4.register_fake
+def _(x, r, w, eps):
+    cs, ss = _mx_shapes(x)
+    return (x.new_empty(cs, dtype=torch.float4_e2m1fn_x2),
+            x.new_empty(ss, dtype=torch.float8_e8m0fnu), torch.empty_like(x))
+
+
 @torch.library.custom_op("addrms::rms_norm_rope_qk", mutates_args=())
 def _rms_norm_rope_qk(q: Tensor, k: Tensor, wq: Tensor, wk: Tensor, cos: Tensor, sin: Tensor,
                       pos: Tensor, eps: float, interleaved: bool) -> Tuple[Tensor, Tensor]:
@@ -283,6 +311,19 @@ def add_rms_norm_fp8(x: Tensor, r: Tensor, w: Tensor, eps: float = 1e-6,
     """Fused residual add + RMSNorm with an E4M3 output: (codes, scales,
     residual).  Not differentiable."""
     return _add_rms_norm_fp8(x, r, w, eps, int(group or 0))
+
+
+def rms_norm_mxfp4(x: Tensor, w: Tensor, eps: float = 1e-6) -> Tuple[Tensor, Tensor]:
+    """RMSNorm with an MXFP4 output: (codes float4_e2m1fn_x2 [.., N/2], scales
+    float8_e8m0fnu [.., ceil(N/32)]).  Not differentiable."""
+    return _rms_norm_mxfp4(x, w, eps)
+
+
+def add_rms_norm_mxfp4(x: Tensor, r: Tensor, w: Tensor,
+                       eps: float = 1e-6) -> Tuple[Tensor, Tensor, Tensor]:
+    """Fused residual add + RMSNorm with an MXFP4 output: (codes, scales,
+    residual).  Not differentiable."""
+    return _add_rms_norm_mxfp4(x, r, w, eps)
 
 
 def rms_norm_rope_qk(q: Tensor, k: Tensor, wq: Tensor, wk: Tensor, cos: Tensor, sin: Tensor,

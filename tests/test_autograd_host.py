@@ -52,3 +52,14 @@ def test_fake_shapes_fp8_and_rope():
         qo, ko = torch.ops.addrms.rms_norm_rope_qk(qh, kh, wq, wq, cos, cos, pos, 1e-6, False)
         assert qo.shape == qh.shape and ko.shape == kh.shape and qo.dtype == torch.bfloat16
         assert torch.ops.addrms.rms_norm_rope_qk_(qh, kh, wq, wq, cos, cos, pos, 1e-6, True) is None
+
+
+def test_fake_shapes_mxfp4():
+    with FakeTensorMode():
+        x = torch.empty(4, 7168, dtype=torch.bfloat16)
+        w = torch.empty(7168, dtype=torch.bfloat16)
+        q, s = torch.ops.addrms.rms_norm_mxfp4(x, w, 1e-6)
+        assert q.shape == (4, 3584) and q.dtype == torch.float4_e2m1fn_x2
+        assert s.shape == (4, 224) and s.dtype == torch.float8_e8m0fnu
+        q, s, res = torch.ops.addrms.add_rms_norm_mxfp4(x, x, w, 1e-6)
+        assert res.shape == x.shape and s.shape == (4, 224)

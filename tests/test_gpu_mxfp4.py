@@ -156,3 +156,16 @@ def test_special_rows():
     assert torch.all(sb[0] == 0) and torch.all(qb[0] == 0)
     assert torch.all(sb[1] == 255) and torch.all(qb[1] == 0)
     run(x, None, inp["w"], 1e-6, "special rows")
+
+
+def test_custom_ops_match_the_binding():
+    import add_rmsnorm_amd.autograd as ag
+    inp = synth.add_rmsnorm_fwd_inputs(64, 4096, torch.bfloat16, seed=97)
+    x, r, w = (inp[k].to(DEV) for k in ("x", "r", "w"))
+    a = ar.add_rmsnorm_fwd_mxfp4(x, r, w, 1e-6)
+    b = ag.add_rms_norm_mxfp4(x, r, w, 1e-6)
+    c = ag.rms_norm_mxfp4(x, w, 1e-6)
+    d = ar.rmsnorm_fwd_mxfp4(x, w, 1e-6)
+    torch.cuda.synchronize()
+    for u, v in list(zip(a, b)) + list(zip(c, d)):
+        assert u.dtype == v.dtype and torch.equal(u.view(torch.uint8), v.view(torch.uint8))
