@@ -199,19 +199,14 @@ int oracle_rmsnorm_fwd(const void *x, int x_dt, const void *w, int w_dt, void *y
     return OR_OK;
 }
 
-/* Fused residual-Add + RMSNorm forward.  residual_out = stored(x + r), with
- * the add in binary32 for float32/bfloat16 inputs; then y is RMSNorm of the
- * stored residual (the residual as written is what gets normalised). */
-int oracle_add_rmsnorm_fwd(const void *x, const void *r, int in_dt, const void *w, int w_dt,
-                           void *y, int y_dt, void *res, int res_dt, void *rstd, int rstd_dt,
-                           int64_t M, int64_t N, double eps)
+/* The residual of every fused op: res = stored(x + r), n elements.  For
+ * float32/bfloat16 inputs the add is binary32 (both operands widened exactly,
+ * one RNE rounding), then one rounding to res_dt; binary64 inputs add in
+ * binary64. */
+static void residual_sum(const void *x, const void *r, int in_dt, void *res, int res_dt,
+                         int64_t n)
 {
-    if (!x || !r || !w || !y || !res || M < 0 || N <= 0)
-        return OR_ERR_ARG;
-    if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
-        return OR_ERR_ARG;
-
-    for (int64_t k = 0; k < M * N; k++) {
+    for (int64_t k = 0; k < n; k++) {
         double s;
         if (in_dt == OR_F64) {
             s = load_elem(x, in_dt, k) + load_elem(r, in_dt, k);
@@ -223,6 +218,20 @@ int oracle_add_rmsnorm_fwd(const void *x, const void *r, int in_dt, const void *
         }
         store_elem(res, res_dt, k, s);
     }
+}
+
+/* Fused residual-Add + RMSNorm forward.  residual_out = stored(x + r), with
+ * the add in binary32 for float32/bfloat16 inputs; then y is RMSNorm of the
+ * stored residual (the residual as written is what gets normalised). */
+int oracle_add_rmsnorm_fwd(const void *x, const void *r, int in_dt, const void *w, int w_dt,
+                           void *y, int y_dt, void *res, int res_dt, void *rstd, int rstd_dt,
+                           int64_t M, int64_t N, double eps)
+{
+    if (!x || !r || !w || !y || !res || M < 0 || N <= 0)
+        return OR_ERR_ARG;
+    if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
+        return OR_ERR_ARG;
+    residual_sum(x, r, in_dt, res, res_dt, M * N);
     return oracle_rmsnorm_fwd(res, res_dt, w, w_dt, y, y_dt, rstd, rstd_dt, M, N, eps);
 }
 
@@ -348,18 +357,7 @@ int oracle_add_layernorm_fwd(const void *x, const void *r, int in_dt, const void
         return OR_ERR_ARG;
     if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
         return OR_ERR_ARG;
-    for (int64_t k = 0; k < M * N; k++) {
-        double s;
-        if (in_dt == OR_F64) {
-            s = load_elem(x, in_dt, k) + load_elem(r, in_dt, k);
-        } else {
-            float a32 = (float)load_elem(x, in_dt, k);
-            float b32 = (float)load_elem(r, in_dt, k);
-            float s32 = a32 + b32;
-            s = (double)s32;
-        }
-        store_elem(res, res_dt, k, s);
-    }
+    residual_sum(x, r, in_dt, res, res_dt, M * N);
     return oracle_layernorm_fwd(res, res_dt, w, b, w_dt, y, y_dt, mean, rstd, stat_dt, M, N, eps);
 }
 
@@ -590,13 +588,7 @@ int oracle_add_rmsnorm_fwd_fp8_grouped(const void *x, const void *r, int in_dt, 
         return OR_ERR_ARG;
     if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
         return OR_ERR_ARG;
-    for (int64_t k = 0; k < M * N; k++) {
-        float a32 = (float)load_elem(x, in_dt, k);
-        float b32 = (float)load_elem(r, in_dt, k);
-        float s32 = a32 + b32; /* binary32 add, as the fused op's residual */
-        store_elem(res, res_dt, k, in_dt == OR_F64 ? load_elem(x, in_dt, k) + load_elem(r, in_dt, k)
-                                                   : (double)s32);
-    }
+    residual_sum(x, r, in_dt, res, res_dt, M * N);
     return oracle_rmsnorm_fwd_fp8_grouped(res, res_dt, w, w_dt, q, scale, group, rstd, rstd_dt, M,
                                           N, eps);
 }
@@ -797,13 +789,7 @@ int oracle_add_rmsnorm_fwd_mxfp4(const void *x, const void *r, int in_dt, const 
         return OR_ERR_ARG;
     if (!dtype_ok(in_dt) || !dtype_ok(res_dt))
         return OR_ERR_ARG;
-    for (int64_t k = 0; k < M * N; k++) {
-        float a32 = (float)load_elem(x, in_dt, k);
-        float b32 = (float)load_elem(r, in_dt, k);
-        float s32 = a32 + b32; /* binary32 add, as the fused op's residual */
-        store_elem(res, res_dt, k, in_dt == OR_F64 ? load_elem(x, in_dt, k) + load_elem(r, in_dt, k)
-                                                   : (double)s32);
-    }
+    residual_sum(x, r, in_dt, res, res_dt, M * N);
     return oracle_rmsnorm_fwd_mxfp4(res, res_dt, w, w_dt, q, scale, rstd, rstd_dt, M, N, eps);
 }
 
