@@ -264,22 +264,36 @@ bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
     return true;
 }
 
-// Backward variant: WPR in {1, 2, 4}.  First choice: 2 waves per row with
-// up to 8 vectors per lane, or 1 or 4 waves with up to 4 (the dw accumulators
-// live in registers; measured on MI355X, bf16: 2 waves per row streams best,
-// 5.4 TB/s at 32768 x 4096 against 5.2 with 1 or 4, and at 16384 x 7168 its 7
-// vectors per lane beat 4 waves' 3.5-of-4 by 2-6 %), then up to 8, then up to
-// 16 vectors per lane, among the instantiated variants; enough waves to fill
-// the device; and a dw exchange that fits in 64 KiB of LDS.  ADDRMS_BWD_WPR
-// forces a WPR.
+// Backward variant.  The fused and LayerNorm backwards of rows of 768 to 2048
+// vectors take 8 waves per row (512-thread blocks, one row per step): they
+// hold the most per lane (dres, or the db sums), and with 2 waves per row their
+// 7 or 8 vectors per lane leave 1 or 2 waves per SIMD (measured on MI355X,
+// bf16, 7168 and 8192 columns: fused 5.9-6.0 TB/s against 5.5-5.7, LayerNorm
+// 5.1 against 3.8-3.9).  Otherwise WPR in {1, 2, 4}: first choice 2 waves per
+// row with up to 8 vectors per lane, or 1 or 4 waves with up to 4 (2 waves per
+// row streams best for the plain backward at 4096 to 8192 columns), except
+// that the fused RMS backward also takes 1 wave per row with up to 8 (no
+// barrier per row: 5.9 TB/s at 4096 columns against 5.56 with 2 waves), then
+// up to 8, then up to 16 vectors per lane, among the instantiated variants;
+// enough waves to fill the device; and a dw exchange that fits in 64 KiB of
+// LDS.  ADDRMS_BWD_WPR forces a WPR.
 bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
 {
     const int forced = env_int("ADDRMS_BWD_WPR");
     int best_wi = -1, best_vi = -1;
+    if (forced == 0 && (res || norm == kLayer) && nvec >= 768 && M * 8 >= 4LL * cus) {
+        const int vi = vpl_index((nvec + 511) / 512);
+        if (vi >= 0 && bwd_built(norm, res, 8, kVplList[vi])) {
+            *wi_out = kBwdNumWpr - 1;
+            *vi_out = vi;
+            return true;
+        }
+    }
     for (int pass = 0; pass < 3 && best_wi < 0; ++pass) {
         for (int wi = 0; wi < kBwdNumWpr; ++wi) {
             const int wpr = kWprList[wi];
-            const int max_vpl = pass == 0 ? (wpr == 2 ? 8 : 4) : pass == 1 ? 8 : kMaxVpl;
+            const int max_vpl = pass == 0 ? ((wpr == 2 || (wpr == 1 && res && norm == kRms)) ? 8 : 4)
+                                          : pass == 1 ? 8 : kMaxVpl;
             const int need = (nvec + 64 * wpr - 1) / (64 * wpr);
             const int vi = vpl_index(need);
             const int rpb = bwd_rpb(wpr);

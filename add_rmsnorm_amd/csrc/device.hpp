@@ -107,32 +107,58 @@ __device__ __forceinline__ void st_stream(u32x4 *p, const u32x4 &v)
 }
 
 // The weights matching vector index v of a row of T: Vec<T>::n consecutive
-// elements of w (stored as WT), as floats.  w is 16-byte aligned.
+// elements of w (stored as WT), kept in their stored form (2, 4 or 8 dwords)
+// so that a kernel can hold them in registers across rows and widen them at
+// each use.  w is 16-byte aligned.
+template <typename T, typename WT> struct WRaw {
+    static constexpr int dw = Vec<T>::n * (int)sizeof(WT) / 4;
+    uint32_t d[dw];
+};
+
+template <typename T, typename WT>
+__device__ __forceinline__ WRaw<T, WT> ld_w_raw(const void *w, int v)
+{
+    constexpr int dw = WRaw<T, WT>::dw;
+    WRaw<T, WT> r;
+    if constexpr (dw == 2) { // bf16 weights, float rows
+        const u32x2 a = reinterpret_cast<const u32x2 *>(w)[v];
+        r.d[0] = a[0];
+        r.d[1] = a[1];
+    } else {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(w) + (dw / 4) * v;
+#pragma unroll
+        for (int h = 0; h < dw / 4; ++h) {
+            const u32x4 a = p[h];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                r.d[4 * h + i] = a[i];
+        }
+    }
+    return r;
+}
+
+template <typename T, typename WT>
+__device__ __forceinline__ void unpack_w(const WRaw<T, WT> &r, float (&f)[Vec<T>::n])
+{
+    constexpr int n = Vec<T>::n;
+    if constexpr (sizeof(WT) == 4) {
+#pragma unroll
+        for (int i = 0; i < n; ++i)
+            f[i] = __uint_as_float(r.d[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+            f[2 * i] = bf16_lo(r.d[i]);
+            f[2 * i + 1] = bf16_hi(r.d[i]);
+        }
+    }
+}
+
+// The same weights loaded and widened to floats in one step.
 template <typename T, typename WT>
 __device__ __forceinline__ void load_w(const void *w, int v, float (&f)[Vec<T>::n])
 {
-    constexpr int n = Vec<T>::n;
-    if constexpr (sizeof(WT) == 4 && n == 4) { // float weights, float rows
-        u32x4 a = reinterpret_cast<const u32x4 *>(w)[v];
-        unpack<float>(a, f);
-    } else if constexpr (sizeof(WT) == 4 && n == 8) { // float weights, bf16 rows
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(w) + 2 * v;
-        u32x4 a = p[0], b = p[1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[i] = __uint_as_float(a[i]);
-            f[4 + i] = __uint_as_float(b[i]);
-        }
-    } else if constexpr (sizeof(WT) == 2 && n == 8) { // bf16 weights, bf16 rows
-        u32x4 a = reinterpret_cast<const u32x4 *>(w)[v];
-        unpack<bf16_t>(a, f);
-    } else { // bf16 weights, float rows
-        u32x2 a = reinterpret_cast<const u32x2 *>(w)[v];
-        f[0] = bf16_lo(a[0]);
-        f[1] = bf16_hi(a[0]);
-        f[2] = bf16_lo(a[1]);
-        f[3] = bf16_hi(a[1]);
-    }
+    unpack_w<T, WT>(ld_w_raw<T, WT>(w, v), f);
 }
 
 // Scalar element access for the unaligned/element-wise path.

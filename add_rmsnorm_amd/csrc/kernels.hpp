@@ -74,6 +74,26 @@ __device__ __forceinline__ double fma_ct(double a, double b, double c) { return 
 // y * inv is written as OCP E4M3 codes, one byte per element.  kQMx: MXFP4,
 // one E8M0 scale per 32 values and E2M1 codes, two per byte.
 // ---------------------------------------------------------------------------
+// Whether a forward vector kernel holds the weights of a lane's columns in
+// registers, in their stored form, loaded once before the row loop so that
+// their fetch overlaps the row's loads.  The quantised modes do (measured on
+// MI355X, bf16, 2048 to 8192 columns: MXFP4 3-7 % and grouped E4M3 2.5-5 %
+// faster): their output pass is longer and its per-vector weight loads sat
+// on the critical path.  The other modes keep the registers for occupancy
+// and load the weights at each use (holding them measured 6-11 % slower for
+// the plain LayerNorm and up to 10 % slower at 512 rows of 8192).  Held only
+// within 32 dwords a lane and a lane state (row vectors, quantiser values,
+// weights) within 3/8 of the registers the block size allows (512- and
+// 1024-thread blocks: 256 and 128), which keeps every variant free of spills.
+template <typename T, typename WT, int NORM, bool FUSED, int QM, int WPR, int VPL>
+constexpr bool fwd_hold_w()
+{
+    constexpr int dw = WRaw<T, WT>::dw;
+    constexpr int state = VPL * (4 * (FUSED ? 2 : 1) + (QM != kQNone ? Vec<T>::n : 0) + dw);
+    constexpr int cap = 512 * 256 / (kBlockFwd(WPR) > 256 ? kBlockFwd(WPR) : 256);
+    return QM != kQNone && VPL * dw <= 32 && 8 * state <= 3 * cap;
+}
+
 template <typename T, typename WT, int NORM, bool FUSED, int QM, int WPR, int VPL>
 __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 {
@@ -117,6 +137,25 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
                 t = __builtin_fmaxf(t, part[slot][i]);
         }
         return t;
+    };
+
+    // The weights of the lane's columns (fwd_hold_w).  A vector past the row
+    // reads the row's last vector (in bounds) and is masked at use, so the
+    // loads need no branch and issue together.
+    constexpr bool HOLD_W = fwd_hold_w<T, WT, NORM, FUSED, QM, WPR, VPL>();
+    WRaw<T, WT> wr[HOLD_W ? VPL : 1];
+    if constexpr (HOLD_W) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            wr[k] = ld_w_raw<T, WT>(a.w, v < nvec ? v : nvec - 1);
+        }
+    }
+    auto weights = [&](int k, int v, float (&wf)[NV]) {
+        if constexpr (HOLD_W)
+            unpack_w<T, WT>(wr[k], wf);
+        else
+            load_w<T, WT>(a.w, v < nvec ? v : nvec - 1, wf);
     };
 
     // Blocks are dealt to the 8 XCDs round-robin, so the rows in flight form
@@ -208,8 +247,7 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
                 const int v = vbase + k * VSTRIDE;
                 float h[NV], wf[NV];
                 unpack<T>(hv[k], h);
-                if (v < nvec)
-                    load_w<T, WT>(a.w, v, wf);
+                weights(k, v, wf);
 #pragma unroll
                 for (int e = 0; e < NV; ++e) {
                     o[k][e] = v < nvec ? (h[e] * rs) * wf[e] : 0.0f;
@@ -322,7 +360,7 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
             if (v < nvec) {
                 float h[NV], wf[NV], o[NV];
                 unpack<T>(hv[k], h);
-                load_w<T, WT>(a.w, v, wf);
+                weights(k, v, wf);
 #pragma unroll
                 for (int e = 0; e < NV; ++e)
                     o[e] = ((NORM == kLayer ? h[e] - mu : h[e]) * rs) * wf[e];
@@ -490,6 +528,30 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
     }
 }
 
+// Backward register budget.  A lane holds across a row its vectors of dy, x
+// and (RES) dres, 4 dwords each; one float sum per element for dw (and db);
+// the weights when it keeps them (HOLD_W below); and, for float32 rows, whose
+// arithmetic is binary64, about one more dword per element of temporaries.
+// The kernel asks the register allocator (amdgpu_waves_per_eu) for the most
+// waves per SIMD, of 4, 3 and 2 (at most 128, 168 and 256 VGPRs a lane),
+// whose budget holds that state plus 28 + 5 * VPL for addresses and
+// temporaries.  Without a request the allocator spends registers on
+// instruction-level parallelism and lands below these levels; the margin was
+// fitted to the variants' compiled register counts so that none spills.
+template <typename T, typename WT> constexpr bool bwd_hold_w(int vpl)
+{
+    return vpl * WRaw<T, WT>::dw <= 32;
+}
+template <typename T, typename WT, int NORM, bool RES, int VPL> constexpr int bwd_waves()
+{
+    constexpr int nv = Vec<T>::n;
+    constexpr int state = VPL * (4 * (2 + (RES ? 1 : 0)) + nv * (NORM == kLayer ? 2 : 1) +
+                                 (bwd_hold_w<T, WT>(VPL) ? WRaw<T, WT>::dw : 0) +
+                                 (sizeof(T) == 4 ? nv : 0));
+    constexpr int need = state + 28 + 5 * VPL;
+    return need <= 128 ? 4 : need <= 168 ? 3 : need <= 256 ? 2 : 1;
+}
+
 // ---------------------------------------------------------------------------
 // Backward, vector path, 256-thread blocks with WPR in {1, 2, 4} (RPB = 4 / WPR
 // rows per block step), or 512-thread blocks with WPR = 8 (one row per step).  Each lane keeps its columns' dw (and, for LayerNorm,
@@ -504,7 +566,8 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
 // before its one rounding (dx then holds dh, the gradient of x and of r).
 // ---------------------------------------------------------------------------
 template <typename T, typename WT, int NORM, bool RES, int WPR, int VPL>
-__global__ void __launch_bounds__(kBwdBlockOf(WPR)) bwd_vec_kernel(BwdArgs a)
+__global__ void __launch_bounds__(kBwdBlockOf(WPR))
+    __attribute__((amdgpu_waves_per_eu(bwd_waves<T, WT, NORM, RES, VPL>()))) bwd_vec_kernel(BwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
     constexpr int VSTRIDE = 64 * WPR;
@@ -533,6 +596,28 @@ __global__ void __launch_bounds__(kBwdBlockOf(WPR)) bwd_vec_kernel(BwdArgs a)
             if constexpr (LN)
                 accb[k][e] = 0.0f;
         }
+
+    // w is the same for every row: each lane loads its columns' weights once,
+    // in their stored form, and widens them at each use.  The row passes below
+    // then issue no loads, so no wait inside them stalls on a weight fetch or
+    // on the acknowledgement of an earlier store.  Long rows (more than 32
+    // dwords of weights per lane) load them at each use instead, which keeps
+    // those variants free of spills.
+    constexpr bool HOLD_W = bwd_hold_w<T, WT>(VPL);
+    WRaw<T, WT> wr[HOLD_W ? VPL : 1];
+    if constexpr (HOLD_W) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vbase + k * VSTRIDE;
+            wr[k] = ld_w_raw<T, WT>(a.w, v < nvec ? v : nvec - 1);
+        }
+    }
+    auto weights = [&](int k, int v, float (&wf)[NV]) {
+        if constexpr (HOLD_W)
+            unpack_w<T, WT>(wr[k], wf);
+        else
+            load_w<T, WT>(a.w, v, wf);
+    };
 
     const int64_t step = (int64_t)gridDim.x * RPB;
     // Loads of one row group into registers.  Vector indices past the row are
@@ -577,7 +662,7 @@ __global__ void __launch_bounds__(kBwdBlockOf(WPR)) bwd_vec_kernel(BwdArgs a)
                 float d[NV], xx[NV], wf[NV];
                 unpack<T>(dyv[k], d);
                 unpack<T>(xv[k], xx);
-                load_w<T, WT>(a.w, v, wf);
+                weights(k, v, wf);
 #pragma unroll
                 for (int e = 0; e < NV; ++e) {
                     const CT g = (CT)d[e] * (CT)wf[e];
@@ -620,7 +705,7 @@ __global__ void __launch_bounds__(kBwdBlockOf(WPR)) bwd_vec_kernel(BwdArgs a)
                     float d[NV], xx[NV], wf[NV], o[NV], dr[NV];
                     unpack<T>(dyv[k], d);
                     unpack<T>(xv[k], xx);
-                    load_w<T, WT>(a.w, v, wf);
+                    weights(k, v, wf);
                     if constexpr (RES)
                         unpack<T>(drv[k], dr);
 #pragma unroll
