@@ -333,10 +333,9 @@ int colreduce(const void *workspace, const void *workspace2, int P, int N, float
     const bool vec = (N % 4) == 0 && aligned16(dw) && (!db || aligned16(db)) &&
                      (P == 0 || (aligned16(ws) && (!db || aligned16(ws2))));
     const KernelRef k = colreduce_kernel(vec);
+    const int cols = vec ? kColReduceVecCols : kColReduceCols;
     void *argv[] = {(void *)&ws, (void *)&ws2, (void *)&P, (void *)&N, (void *)&dw, (void *)&db};
-    hipError_t e = hipLaunchKernel(k.fn,
-                                   dim3((unsigned)((N + kColReduceCols - 1) / kColReduceCols),
-                                        db ? 2u : 1u),
+    hipError_t e = hipLaunchKernel(k.fn, dim3((unsigned)((N + cols - 1) / cols), db ? 2u : 1u),
                                    dim3(k.block), argv, 0, s);
     return e == hipSuccess ? ADDRMS_OK : fail_hip(e);
 }

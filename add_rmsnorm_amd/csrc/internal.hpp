@@ -124,7 +124,9 @@ constexpr int kBwdBlock = 256;
 // except WPR = 8, whose 512-thread blocks hold one row.
 constexpr int kBwdBlockOf(int wpr) { return wpr == 8 ? 512 : kBwdBlock; }
 constexpr int bwd_rpb(int wpr) { return wpr == 8 ? 1 : 4 / wpr; }
-constexpr int kColReduceCols = 16; // dw columns per column-reduce block
+constexpr int kColReduceCols = 16;    // dw columns per element-wise column-reduce block
+constexpr int kColReduceVecCols = 32; // per vector column-reduce block (128-byte rows)
+constexpr int kColReduceVecBlock = 1024;
 
 // A kernel entry: function, block size, dynamic LDS bytes (backward: per
 // column of N), and whether it is an element-wise fallback.

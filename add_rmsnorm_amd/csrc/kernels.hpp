@@ -873,18 +873,21 @@ __global__ void __launch_bounds__(256) bwd_elem_dw_kernel(BwdArgs a)
 // partial rows are few (P <= 1024) and the columns many, so a block takes a
 // narrow column strip and splits the rows over slices of threads; the slices
 // are then merged in LDS by a fixed-order tree, so the result is
-// deterministic.  Vector form: 16-column strips read as 4 x 16-byte lanes, 64
-// row slices, and up to 16 rows per thread loaded at once (the kernel is short
-// and latency-bound: every load of a thread is in flight together);
-// requires N % 4 == 0 and 16-byte aligned partials and outputs.  (Templates
-// only so that each translation unit's copy is a weak symbol.)
+// deterministic.  Vector form: 32-column strips, so that each block reads
+// whole 128-byte lines of every partial row (with 16-column strips two blocks
+// fetched each line, and 1024 partial rows of 7168 columns took 11 us instead
+// of 3.6); 8 x 16-byte lanes by 128 row slices, and up to 8 rows per thread
+// loaded at once (the kernel is short and latency-bound: every load of a
+// thread is in flight together).  Requires N % 4 == 0 and 16-byte aligned
+// partials and outputs.  (Templates only so that each translation unit's copy
+// is a weak symbol.)
 template <int Unused = 0>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kColReduceVecBlock)
     dw_colreduce_vec_kernel(const float *ws, const float *ws2, int P, int N, float *dw, float *db)
 {
-    constexpr int Q = kColReduceCols / 4; // 16-byte lanes per strip row
-    constexpr int S = 256 / Q;            // row slices
-    constexpr int U = 16;                 // rows per thread per load batch
+    constexpr int Q = kColReduceVecCols / 4;   // 16-byte lanes per strip row
+    constexpr int S = kColReduceVecBlock / Q;  // row slices
+    constexpr int U = 8;                       // rows per thread per load batch
     __shared__ u32x4 red[S][Q];
     const float *src = blockIdx.y ? ws2 : ws;
     float *dst = blockIdx.y ? db : dw;

@@ -42,7 +42,7 @@ const BwdTable &ADDRMS_CAT(bwd_table_, ADDRMS_COMBO)()
 #if ADDRMS_COMBO == 0
 KernelRef colreduce_kernel(bool vec)
 {
-    return vec ? KernelRef{reinterpret_cast<const void *>(&dw_colreduce_vec_kernel<0>), 256}
+    return vec ? KernelRef{reinterpret_cast<const void *>(&dw_colreduce_vec_kernel<0>), kColReduceVecBlock}
                : KernelRef{reinterpret_cast<const void *>(&dw_colreduce_kernel<0>), 256};
 }
 #endif

@@ -40,9 +40,18 @@ def check(dy, dres, h, w, rstd, what=""):
     assert_dw_close(dw.cpu(), rdw, mag, f"dw {what}")
 
 
-@pytest.mark.parametrize("M,N", [(16384, 7168), (4096, 4096), (300, 1032)])
+# default choices: 16384 x 7168 and 600 x 6152 (769 vectors, ragged) take 8
+# waves per row; 4096 x 4096 one wave per row with 8 vectors a lane
+@pytest.mark.parametrize("M,N", [(16384, 7168), (600, 6152), (4096, 4096), (300, 1032)])
 def test_fused_bwd_bf16(M, N):
     check(*fused_case(M, N, torch.bfloat16), f"{M}x{N}")
+
+
+# float32 rows on the same default paths: 1024 vectors (8 waves per row) and
+# 512 vectors with enough rows for one wave per row
+@pytest.mark.parametrize("M,N", [(500, 4096), (1500, 2048)])
+def test_fused_bwd_f32_default_paths(M, N):
+    check(*fused_case(M, N, torch.float32, seed=M), f"f32 {M}x{N}")
 
 
 @pytest.mark.parametrize("dtype,wdtype", [(torch.float32, torch.float32),

@@ -121,7 +121,9 @@ def test_forward_in_place_and_empty():
     assert y.shape == (0, 4096)
 
 
-@pytest.mark.parametrize("M,N", [(32768, 4096), (3001, 1032), (7, 8192)])
+# 16384 x 7168 and 600 x 6152 (769 vectors, the last one ragged) take 8 waves
+# per row by default
+@pytest.mark.parametrize("M,N", [(32768, 4096), (16384, 7168), (600, 6152), (3001, 1032), (7, 8192)])
 def test_backward_bf16(M, N):
     check_bwd(inputs(M, N, torch.bfloat16, seed=M), f"{M}x{N}")
 
@@ -172,6 +174,8 @@ def test_backward_in_place_and_empty():
 
 @pytest.mark.parametrize("M,N,dtype", [(4096, 4096, torch.bfloat16), (333, 1000, torch.bfloat16),
                                        (500, 2048, torch.float32),
+                                       # 8 waves per row by default (769 and 1792 vectors)
+                                       (1000, 6152, torch.bfloat16), (600, 7168, torch.float32),
                                        # 12 vectors per lane; rows too long for the
                                        # register-resident variants (element-wise path)
                                        (24, 24576, torch.bfloat16), (24, 30720, torch.bfloat16),
