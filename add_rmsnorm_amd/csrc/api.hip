@@ -227,13 +227,18 @@ int vpl_index(int need)
 }
 
 // Forward variant.  A row is spread over enough waves that each lane holds
-// about ADDRMS_FWD_VPL (default 2) 16-byte vectors per tensor: measured on
-// MI355X, short per-lane chains in many small row-blocks keep more rows in
-// flight and stream fastest (fused bf16 16384 x 7168: 8 waves per row reach
-// 6.2 TB/s, one wave per row 5.5 TB/s).  When there are too few rows to give
-// every SIMD a wave, rows get more waves still.  ADDRMS_FWD_WPR forces a WPR
-// when it is built.
-bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
+// about ADDRMS_FWD_VPL (default 2) 16-byte vectors per tensor, or up to 4 with
+// 8 waves per row: measured on MI355X, short per-lane chains in many small
+// row-blocks keep more rows in flight and stream fastest (fused bf16 16384 x
+// 7168: 8 waves per row reach 6.2 TB/s, one wave per row 5.5 TB/s), but
+// 1024-thread blocks (16 waves per row) hold at most two rows per CU: at
+// 12288 and 16384 columns 8 waves with 3 or 4 vectors a lane beat 16 with 2
+// (fused 6.0-6.1 against 5.8-5.9 TB/s; the E4M3 and MXFP4 outputs, with a
+// second row reduction or more registers, 5.7-6.2 against 4.5-5.1).  When
+// there are too few rows to give every SIMD a wave, rows get more waves
+// still.  qm (a quantised mode, or kQNone) restricts the choice to built
+// variants of that mode.  ADDRMS_FWD_WPR forces a WPR when it is built.
+bool pick_fwd(int64_t M, int nvec, int cus, int qm, int *wi_out, int *vi_out)
 {
     const int forced = env_int("ADDRMS_FWD_WPR");
     const int env_vpl = env_int("ADDRMS_FWD_VPL");
@@ -241,7 +246,8 @@ bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
     auto need_of = [&](int wi) { return (nvec + 64 * kWprList[wi] - 1) / (64 * kWprList[wi]); };
     auto ok = [&](int wi) {
         const int vi = vpl_index(need_of(wi));
-        return vi >= 0 && fwd_built(kWprList[wi], kVplList[vi]);
+        return vi >= 0 && (qm == kQNone ? fwd_built(kWprList[wi], kVplList[vi])
+                                        : q_built(qm, kWprList[wi], kVplList[vi]));
     };
     if (forced > 0)
         for (int wi = 0; wi < kNumWpr; ++wi)
@@ -251,7 +257,8 @@ bool pick_fwd(int64_t M, int nvec, int cus, int *wi_out, int *vi_out)
                 return true;
             }
     int wi = 0;
-    while (wi < kNumWpr - 1 && need_of(wi) > target)
+    while (wi < kNumWpr - 1 &&
+           need_of(wi) > (kWprList[wi] == 8 && env_vpl <= 0 ? 4 : target))
         ++wi;
     while (wi < kNumWpr - 1 && M * kWprList[wi] < 4LL * cus && need_of(wi) > 1)
         ++wi;
@@ -436,7 +443,7 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
         return rc;
     int wi = 0, vi = 0;
-    if (vec_ok && pick_fwd(M, (int)(N / nv), cus, &wi, &vi) &&
+    if (vec_ok && pick_fwd(M, (int)(N / nv), cus, q8 ? qm + 1 : (int)kQNone, &wi, &vi) &&
         (!q8 || tab.vec_q8[fused ? 1 : 0][qm][wi][vi].fn != nullptr)) {
         a.nvec = (int)(N / nv);
         const KernelRef &k =
