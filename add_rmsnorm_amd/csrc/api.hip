@@ -330,6 +330,31 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
     return true;
 }
 
+// The wide backward (one 1024-thread block per CU, 8 rows of 2 waves per
+// step) instead of four 256-thread blocks of 2 rows: the same waves per CU
+// and the same per-row work, with a quarter of the dw partial rows for the
+// column reduce to read, but a barrier per row step that spans 16 waves.
+// Measured on MI355X, bf16, wide / 256-thread time: 3 vectors a lane (3072
+// columns) 0.69-0.98 at 2048 to 32768 rows; 4 vectors a lane (4096
+// columns) 0.67 / 0.81 / 0.95 at 2048 / 4096 / 8192 rows, 1.01-1.03 at
+// 12288 rows and more.  So it is taken when the picker chose 2 waves per row,
+// the variant is built, its LDS tree fits, every CU gets a block, and the row
+// has at most 3 vectors a lane or the batch has at most 32 rows per CU.
+// ADDRMS_BWD_WIDE=1 forces it where built, ADDRMS_BWD_WIDE=2 turns it off.
+bool use_wide_bwd(const BwdTable &tab, int norm, bool res, int64_t M, int64_t N, int wi, int vi,
+                  int cus)
+{
+    const int mode = env_int("ADDRMS_BWD_WIDE");
+    if (mode == 2 || kWprList[wi] != kBwdWideWpr || tab.wide[norm][res ? 1 : 0][vi].fn == nullptr)
+        return false;
+    const int rpb = bwd_rpb(kBwdWideWpr, true);
+    if ((size_t)(rpb / 2) * (size_t)N * 4u > kMaxDynLds)
+        return false;
+    if (mode == 1)
+        return true;
+    return M >= (int64_t)rpb * cus && (kVplList[vi] <= 3 || M <= 32LL * cus);
+}
+
 // dw[c] = sum over P partial rows of ws[:, c], and, when db is given,
 // db[c] = sum of ws2[:, c], in one launch (P = 0 writes zeros; nothing read).
 int colreduce(const void *workspace, const void *workspace2, int P, int N, float *dw, float *db,
@@ -536,8 +561,9 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     int wi = 0, vi = 0;
     if (vec_ok && pick_bwd(norm, res, M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
         a.nvec = (int)(N / nv);
-        const KernelRef &k = tab.vec[norm][res ? 1 : 0][wi][vi];
-        const int rpb = bwd_rpb(kWprList[wi]);
+        const bool wide = use_wide_bwd(tab, norm, res, M, N, wi, vi, cus);
+        const KernelRef &k = wide ? tab.wide[norm][res ? 1 : 0][vi] : tab.vec[norm][res ? 1 : 0][wi][vi];
+        const int rpb = bwd_rpb(kWprList[wi], wide);
         const size_t smem = (size_t)(rpb / 2) * (size_t)N * 4u;
         int grid = 0;
         if ((rc = persistent_grid(k, smem, (M + rpb - 1) / rpb, pmax, &grid)) != ADDRMS_OK)

@@ -120,10 +120,20 @@ constexpr bool bwd_built(int norm, bool res, int wpr, int vpl)
     return !(norm == kLayer && res && vpl > 14) && !(wpr == 8 && vpl > 4);
 }
 constexpr int kBwdBlock = 256;
+constexpr int kBwdWideBlock = 1024;
 // Backward vector kernels: 256-thread blocks holding 4 / WPR rows per step,
-// except WPR = 8, whose 512-thread blocks hold one row.
-constexpr int kBwdBlockOf(int wpr) { return wpr == 8 ? 512 : kBwdBlock; }
-constexpr int bwd_rpb(int wpr) { return wpr == 8 ? 1 : 4 / wpr; }
+// except WPR = 8, whose 512-thread blocks hold one row.  The wide variant
+// (WIDE) is one 1024-thread block per CU with 2 waves per row, 8 rows per
+// step: a quarter of the dw partial rows of four 256-thread blocks.
+constexpr int kBwdBlockOf(int wpr, bool wide = false)
+{
+    return wide ? kBwdWideBlock : wpr == 8 ? 512 : kBwdBlock;
+}
+constexpr int bwd_rpb(int wpr, bool wide = false)
+{
+    return wide ? kBwdWideBlock / (64 * wpr) : wpr == 8 ? 1 : 4 / wpr;
+}
+constexpr int kBwdWideWpr = 2;
 constexpr int kColReduceCols = 16;    // dw columns per element-wise column-reduce block
 constexpr int kColReduceVecCols = 32; // per vector column-reduce block (128-byte rows)
 constexpr int kColReduceVecBlock = 1024;
@@ -152,6 +162,7 @@ struct FwdTable {
 // [norm][with residual gradient]; elem_dw: [norm].
 struct BwdTable {
     KernelRef vec[2][2][kBwdNumWpr][kNumVpl];
+    KernelRef wide[2][2][kNumVpl]; // WPR = kBwdWideWpr in 1024-thread blocks; null where not built
     KernelRef elem_dx[2][2];
     KernelRef elem_dw[2];
 };

@@ -554,7 +554,8 @@ template <typename T, typename WT, int NORM, bool RES, int VPL> constexpr int bw
 
 // ---------------------------------------------------------------------------
 // Backward, vector path, 256-thread blocks with WPR in {1, 2, 4} (RPB = 4 / WPR
-// rows per block step), or 512-thread blocks with WPR = 8 (one row per step).  Each lane keeps its columns' dw (and, for LayerNorm,
+// rows per block step), or 512-thread blocks with WPR = 8 (one row per step),
+// or (WIDE) 1024-thread blocks with WPR = 2 (8 rows per step).  Each lane keeps its columns' dw (and, for LayerNorm,
 // db) partial sums in registers across all rows it visits; at the end the
 // block's row groups are summed through LDS (pairwise, fixed order) and
 // written as one row of the workspace: ws[blockIdx.x, :] (and ws2 for db).
@@ -565,17 +566,17 @@ template <typename T, typename WT, int NORM, bool RES, int VPL> constexpr int bw
 // RES: the fused op's backward, which adds the residual gradient dres to dx
 // before its one rounding (dx then holds dh, the gradient of x and of r).
 // ---------------------------------------------------------------------------
-template <typename T, typename WT, int NORM, bool RES, int WPR, int VPL>
-__global__ void __launch_bounds__(kBwdBlockOf(WPR))
+template <typename T, typename WT, int NORM, bool RES, int WPR, int VPL, bool WIDE = false>
+__global__ void __launch_bounds__(kBwdBlockOf(WPR, WIDE))
     __attribute__((amdgpu_waves_per_eu(bwd_waves<T, WT, NORM, RES, VPL>()))) bwd_vec_kernel(BwdArgs a)
 {
     constexpr int NV = Vec<T>::n;
     constexpr int VSTRIDE = 64 * WPR;
-    constexpr int RPB = bwd_rpb(WPR);
+    constexpr int RPB = bwd_rpb(WPR, WIDE);
     constexpr bool LN = NORM == kLayer;
     using CT = typename BwdCompute<T>::type;
     extern __shared__ __attribute__((aligned(16))) float lds[];
-    __shared__ CT part[2][2][kBwdBlockOf(WPR) / 64]; // [row parity][sum][wave]
+    __shared__ CT part[2][2][kBwdBlockOf(WPR, WIDE) / 64]; // [row parity][sum][wave]
 
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -756,32 +757,22 @@ __global__ void __launch_bounds__(kBwdBlockOf(WPR))
             }
         }
     };
+    // Pairwise tree over the RPB row groups (a power of two), fixed order:
+    // at each level the upper half of the remaining groups parks its sums in
+    // LDS ((RPB / 2) * N floats) and the lower half adds them.
     auto merge = [&](auto &acc, float *out) {
-        if constexpr (RPB == 4) {
-            if (rib >= 2)
-                put(acc, lds + (size_t)(rib - 2) * N);
+#pragma unroll
+        for (int half = RPB / 2; half >= 1; half /= 2) {
+            if (rib >= half && rib < 2 * half)
+                put(acc, lds + (size_t)(rib - half) * N);
             __syncthreads();
-            if (rib < 2)
+            if (rib < half)
                 add(acc, lds + (size_t)rib * N);
-            __syncthreads();
-            if (rib == 1)
-                put(acc, lds);
-            __syncthreads();
-            if (rib == 0) {
-                add(acc, lds);
-                put(acc, out);
-            }
-        } else if constexpr (RPB == 2) {
-            if (rib == 1)
-                put(acc, lds);
-            __syncthreads();
-            if (rib == 0) {
-                add(acc, lds);
-                put(acc, out);
-            }
-        } else {
-            put(acc, out);
+            if (half > 1)
+                __syncthreads(); // the next level's parking overwrites these slots
         }
+        if (rib == 0)
+            put(acc, out);
     };
     merge(accw, a.ws + (size_t)blockIdx.x * (size_t)N);
     if constexpr (LN) {
@@ -1027,6 +1018,24 @@ template <typename T, typename WT> struct TableBuilder {
     {
         ((row[VI] = bwd_ref<NM, R, kWprList[WI], kVplList[VI]>()), ...);
     }
+    // The wide variant: built where a lane's state fits the 128 VGPRs that 16
+    // waves per CU leave (4 waves per SIMD) and the row takes at most 8
+    // vectors a lane.
+    template <int NM, bool R, int VPL> static KernelRef bwd_wide_ref()
+    {
+        if constexpr (bwd_built(NM, R, kBwdWideWpr, VPL) && VPL <= 8 &&
+                      bwd_waves<T, WT, NM, R, VPL>() == 4)
+            return KernelRef{
+                reinterpret_cast<const void *>(&bwd_vec_kernel<T, WT, NM, R, kBwdWideWpr, VPL, true>),
+                kBwdBlockOf(kBwdWideWpr, true)};
+        else
+            return KernelRef{nullptr, 0};
+    }
+    template <int NM, bool R, int... VI>
+    static void bwd_wide_row(KernelRef (&row)[kNumVpl], std::integer_sequence<int, VI...>)
+    {
+        ((row[VI] = bwd_wide_ref<NM, R, kVplList[VI]>()), ...);
+    }
     template <int NM, bool R, int... WI>
     static void bwd_all(BwdTable &t, std::integer_sequence<int, WI...>)
     {
@@ -1040,6 +1049,10 @@ template <typename T, typename WT> struct TableBuilder {
         bwd_all<kRms, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         bwd_all<kLayer, false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         bwd_all<kLayer, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        bwd_wide_row<kRms, false>(t.wide[kRms][0], std::make_integer_sequence<int, kNumVpl>{});
+        bwd_wide_row<kRms, true>(t.wide[kRms][1], std::make_integer_sequence<int, kNumVpl>{});
+        bwd_wide_row<kLayer, false>(t.wide[kLayer][0], std::make_integer_sequence<int, kNumVpl>{});
+        bwd_wide_row<kLayer, true>(t.wide[kLayer][1], std::make_integer_sequence<int, kNumVpl>{});
         t.elem_dx[kRms][0] =
             KernelRef{reinterpret_cast<const void *>(&bwd_elem_dx_kernel<T, WT, kRms, false>), 256};
         t.elem_dx[kRms][1] =

@@ -57,6 +57,31 @@ def test_forced_waves_per_row(monkeypatch, wpr, dtype, wdtype):
         check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"wpr={wpr} {M}x{N}")
 
 
+# The wide variant (1024-thread blocks, 8 rows of 2 waves per step) forced
+# on every dtype pair: 1 to 4 vectors a lane, ragged last vectors, fewer rows
+# than one step of the grid, and more rows than 8 per CU (several steps).
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.float32),
+                                          (torch.float32, torch.bfloat16)])
+def test_wide_variant_forced(monkeypatch, dtype, wdtype):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+    cases = [(1000, 4096), (3001, 3072), (7, 1032), (2049, 520), (9000, 1536)] if dtype == torch.bfloat16 \
+        else [(1000, 2048), (3001, 1536), (7, 516), (2049, 260), (9000, 768)]
+    for M, N in cases:
+        inp = synth.rmsnorm_bwd_inputs(M, N, dtype, wdtype, seed=M + 3 * N)
+        check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"wide {M}x{N}")
+
+
+# default choices of the wide variant: 3 vectors a lane at any batch, 4 up to
+# 32 rows per CU; the 32768 x 4096 workload stays on 256-thread blocks
+@pytest.mark.parametrize("M,N", [(2048, 3072), (32768, 3072), (4096, 4096), (8192, 4096)])
+def test_wide_variant_default_shapes(M, N):
+    inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=M + N)
+    check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"{M}x{N}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("M,N", [(5, 4096), (2000, 7168), (3, 8), (1025, 1000)])
 def test_elementwise_path(monkeypatch, dtype, M, N):

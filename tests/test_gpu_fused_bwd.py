@@ -67,6 +67,16 @@ def test_fused_bwd_forced_waves_per_row(monkeypatch, wpr):
     check(*fused_case(1000, 4096, torch.bfloat16, seed=7), f"wpr={wpr}")
 
 
+# The wide variant (1024-thread blocks, 2 waves per row) where it is built
+# for the fused backward: up to 3 vectors a lane
+@pytest.mark.parametrize("dtype,M,N", [(torch.bfloat16, 3001, 3072), (torch.bfloat16, 9000, 1040),
+                                       (torch.float32, 1000, 1536)])
+def test_fused_bwd_wide_variant(monkeypatch, dtype, M, N):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+    check(*fused_case(M, N, dtype, seed=M), f"wide {M}x{N}")
+
+
 @pytest.mark.parametrize("M,N", [(5, 4096), (129, 7), (64, 1000)])
 def test_fused_bwd_elementwise(monkeypatch, M, N):
     monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")

@@ -137,6 +137,16 @@ def test_backward_variants(monkeypatch, wpr, dtype, wdtype):
     check_bwd(inputs(1000, 2048, dtype, wdtype, seed=wpr), f"wpr={wpr}")
 
 
+# The wide variant (1024-thread blocks, 2 waves per row; dw and db share its
+# LDS tree) where it is built for LayerNorm: up to 3 vectors a lane
+@pytest.mark.parametrize("dtype,M,N", [(torch.bfloat16, 3001, 3072), (torch.bfloat16, 9000, 1040),
+                                       (torch.float32, 1000, 1536)])
+def test_backward_wide_variant(monkeypatch, dtype, M, N):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+    check_bwd(inputs(M, N, dtype, seed=M), f"wide {M}x{N}")
+
+
 @pytest.mark.parametrize("N", [1, 5, 65, 4100, 16392])
 def test_backward_edge_shapes(N):
     check_bwd(inputs(max(1, min(500, (1 << 22) // N)), N, torch.bfloat16, seed=N), f"N={N}")
