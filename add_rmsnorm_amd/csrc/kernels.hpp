@@ -81,7 +81,11 @@ __device__ __forceinline__ double fma_ct(double a, double b, double c) { return 
 // faster): their output pass is longer and its per-vector weight loads sat
 // on the critical path.  The other modes keep the registers for occupancy
 // and load the weights at each use (holding them measured 6-11 % slower for
-// the plain LayerNorm and up to 10 % slower at 512 rows of 8192).  Held only
+// the plain LayerNorm and up to 10 % slower at 512 rows of 8192), except the
+// variant with 16 waves per row and one vector a lane, which serves batches
+// too small to give every SIMD a wave: there the early fetch takes the weight
+// load off the path after the row reduction (2.62 -> 2.45 us for one row of
+// 8192 with float32 weights).  Held only
 // within 32 dwords a lane and a lane state (row vectors, quantiser values,
 // weights) within 3/8 of the registers the block size allows (512- and
 // 1024-thread blocks: 256 and 128), which keeps every variant free of spills.
@@ -91,7 +95,7 @@ constexpr bool fwd_hold_w()
     constexpr int dw = WRaw<T, WT>::dw;
     constexpr int state = VPL * (4 * (FUSED ? 2 : 1) + (QM != kQNone ? Vec<T>::n : 0) + dw);
     constexpr int cap = 512 * 256 / (kBlockFwd(WPR) > 256 ? kBlockFwd(WPR) : 256);
-    return QM != kQNone && VPL * dw <= 32 && 8 * state <= 3 * cap;
+    return (QM != kQNone || (WPR == 16 && VPL == 1)) && VPL * dw <= 32 && 8 * state <= 3 * cap;
 }
 
 template <typename T, typename WT, int NORM, bool FUSED, int QM, int WPR, int VPL>
