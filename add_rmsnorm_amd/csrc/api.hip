@@ -355,6 +355,20 @@ bool use_wide_bwd(const BwdTable &tab, int norm, bool res, int64_t M, int64_t N,
     return M >= (int64_t)rpb * cus && (kVplList[vi] <= 3 || M <= 32LL * cus);
 }
 
+// The RMS backward with the next row's loads in flight across the current
+// row's exchange and output pass (the PF kernels): 1.5-3.6 % faster at 4
+// vectors a lane (2 waves per row, 3584 to 4096 bf16 or 1792 to 2048 float32
+// columns, 12288 to 65536 rows, measured on MI355X), so it is the default
+// there.  ADDRMS_BWD_PREFETCH=1 takes it wherever it is built (up to 4
+// vectors a lane), ADDRMS_BWD_PREFETCH=2 never.
+bool use_prefetch_bwd(const BwdTable &tab, int norm, bool res, int wi, int vi)
+{
+    const int mode = env_int("ADDRMS_BWD_PREFETCH");
+    if (mode == 2 || tab.pf[norm][res ? 1 : 0][wi][vi].fn == nullptr)
+        return false;
+    return mode == 1 || kVplList[vi] == 4;
+}
+
 // dw[c] = sum over P partial rows of ws[:, c], and, when db is given,
 // db[c] = sum of ws2[:, c], in one launch (P = 0 writes zeros; nothing read).
 int colreduce(const void *workspace, const void *workspace2, int P, int N, float *dw, float *db,
@@ -562,7 +576,10 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     if (vec_ok && pick_bwd(norm, res, M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
         a.nvec = (int)(N / nv);
         const bool wide = use_wide_bwd(tab, norm, res, M, N, wi, vi, cus);
-        const KernelRef &k = wide ? tab.wide[norm][res ? 1 : 0][vi] : tab.vec[norm][res ? 1 : 0][wi][vi];
+        const bool pf = !wide && use_prefetch_bwd(tab, norm, res, wi, vi);
+        const KernelRef &k = wide ? tab.wide[norm][res ? 1 : 0][vi]
+                             : pf ? tab.pf[norm][res ? 1 : 0][wi][vi]
+                                  : tab.vec[norm][res ? 1 : 0][wi][vi];
         const int rpb = bwd_rpb(kWprList[wi], wide);
         const size_t smem = (size_t)(rpb / 2) * (size_t)N * 4u;
         int grid = 0;

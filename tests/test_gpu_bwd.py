@@ -74,9 +74,36 @@ def test_wide_variant_forced(monkeypatch, dtype, wdtype):
         check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"wide {M}x{N}")
 
 
+# The next-row prefetch variant (2 waves per row) forced on every dtype pair,
+# 1 to 4 vectors a lane, ragged rows, a batch that ends mid-step, and with
+# ADDRMS_BWD_PREFETCH=2 the plain kernel at 4 vectors a lane (the prefetch's
+# default): dx bit-identical between the two.
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.float32),
+                                          (torch.float32, torch.bfloat16)])
+def test_prefetch_variant_forced(monkeypatch, dtype, wdtype):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+    monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
+    monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+    cases = [(1001, 4096), (3001, 3072), (7, 1032), (2049, 520), (9001, 1536)] if dtype == torch.bfloat16 \
+        else [(1001, 2048), (3001, 1536), (7, 516), (2049, 260), (9001, 768)]
+    for M, N in cases:
+        inp = synth.rmsnorm_bwd_inputs(M, N, dtype, wdtype, seed=M + 5 * N)
+        dx, _ = check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"prefetch {M}x{N}")
+        if N in (4096, 2048):
+            monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "2")
+            dx2, _ = check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"no prefetch {M}x{N}")
+            monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+            assert torch.equal(dx.view(torch.int16) if dtype == torch.bfloat16 else dx,
+                               dx2.view(torch.int16) if dtype == torch.bfloat16 else dx2)
+
+
 # default choices of the wide variant: 3 vectors a lane at any batch, 4 up to
-# 32 rows per CU; the 32768 x 4096 workload stays on 256-thread blocks
-@pytest.mark.parametrize("M,N", [(2048, 3072), (32768, 3072), (4096, 4096), (8192, 4096)])
+# 32 rows per CU; the 32768 x 4096 workload stays on 256-thread blocks (with
+# the next-row prefetch), as do 12288 x 4096 and 32768 x 3584
+@pytest.mark.parametrize("M,N", [(2048, 3072), (32768, 3072), (4096, 4096), (8192, 4096),
+                                 (12288, 4096), (32768, 3584)])
 def test_wide_variant_default_shapes(M, N):
     inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=M + N)
     check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"{M}x{N}")
