@@ -355,12 +355,14 @@ bool use_wide_bwd(const BwdTable &tab, int norm, bool res, int64_t M, int64_t N,
     return M >= (int64_t)rpb * cus && (kVplList[vi] <= 3 || M <= 32LL * cus);
 }
 
-// The RMS backward with the next row's loads in flight across the current
-// row's exchange and output pass (the PF kernels): 1.5-3.6 % faster at 4
-// vectors a lane (2 waves per row, 3584 to 4096 bf16 or 1792 to 2048 float32
-// columns, 12288 to 65536 rows, measured on MI355X), so it is the default
-// there.  ADDRMS_BWD_PREFETCH=1 takes it wherever it is built (up to 4
-// vectors a lane), ADDRMS_BWD_PREFETCH=2 never.
+// The RMS and LayerNorm backwards with the next row's loads in flight across
+// the current row's exchange and output pass (the PF kernels), measured on
+// MI355X at 4 vectors a lane and 2 waves per row: RMS 1.5-3.6 % faster (3584
+// to 4096 bf16 or 1792 to 2048 float32 columns, 12288 to 65536 rows),
+// LayerNorm 3.5-5.8 % (3584 to 4096 bf16 columns, 8192 to 32768 rows); so
+// it is the default there.  (In the fused backwards, 8 waves per row, it was
+// 4-9 % slower and is not built.)  ADDRMS_BWD_PREFETCH=1 takes it wherever
+// it is built (up to 4 vectors a lane), ADDRMS_BWD_PREFETCH=2 never.
 bool use_prefetch_bwd(const BwdTable &tab, int norm, bool res, int wi, int vi)
 {
     const int mode = env_int("ADDRMS_BWD_PREFETCH");

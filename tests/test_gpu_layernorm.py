@@ -147,6 +147,23 @@ def test_backward_wide_variant(monkeypatch, dtype, M, N):
     check_bwd(inputs(M, N, dtype, seed=M), f"wide {M}x{N}")
 
 
+# The next-row prefetch variant (2 waves per row): forced at 1 to 4 vectors a
+# lane and ragged rows, and on its default shapes (4 vectors a lane)
+@pytest.mark.parametrize("dtype,M,N", [(torch.bfloat16, 3001, 4096), (torch.bfloat16, 777, 2056),
+                                       (torch.bfloat16, 2049, 520), (torch.float32, 1001, 2048),
+                                       (torch.float32, 9, 772)])
+def test_backward_prefetch_forced(monkeypatch, dtype, M, N):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+    monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
+    monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+    check_bwd(inputs(M, N, dtype, seed=M + N), f"prefetch {M}x{N}")
+
+
+@pytest.mark.parametrize("M,N", [(8192, 4096), (32768, 3584)])
+def test_backward_prefetch_default_shapes(M, N):
+    check_bwd(inputs(M, N, torch.bfloat16, seed=M), f"{M}x{N}")
+
+
 @pytest.mark.parametrize("N", [1, 5, 65, 4100, 16392])
 def test_backward_edge_shapes(N):
     check_bwd(inputs(max(1, min(500, (1 << 22) // N)), N, torch.bfloat16, seed=N), f"N={N}")
