@@ -143,9 +143,16 @@ def test_many_rows_exceed_partial_rows():
     check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, "70000x256")
 
 
-@pytest.mark.parametrize("force_elem", ["0", "1"])
+@pytest.mark.parametrize("force_elem", ["0", "1", "prefetch"])
 def test_dx_in_place(monkeypatch, force_elem):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", force_elem)
+    """dx over dy or x; "prefetch": the next-row prefetch kernel, whose loads
+    of the next row go out before the current row's dx stores."""
+    if force_elem == "prefetch":
+        monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+        monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
+        monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+    else:
+        monkeypatch.setenv("ADDRMS_FORCE_ELEM", force_elem)
     M, N = 300, 4096
     inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=29)
     rstd = oracle_rstd(inp["x"], inp["w"], 1e-6)

@@ -176,7 +176,14 @@ def test_backward_elementwise_and_no_db(monkeypatch, M, N):
     check_bwd(inputs(M, N, torch.float32, seed=18), "elem f32", with_db=False)
 
 
-def test_backward_in_place_and_empty():
+@pytest.mark.parametrize("prefetch", ["0", "1"])
+def test_backward_in_place_and_empty(monkeypatch, prefetch):
+    """dx over dy; with prefetch = 1 through the next-row prefetch kernel,
+    whose loads of the next row go out before the current row's dx stores."""
+    if prefetch == "1":
+        monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+        monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
+        monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
     inp = inputs(300, 4096, torch.bfloat16, seed=19)
     x, w = inp["x"], inp["w"]
     dy = synth.store(synth.normal(19, "dy", (300, 4096)), torch.bfloat16)
