@@ -265,6 +265,17 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands:
     log(f"wrote {TRAFFIC_FILE}")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, M: int, N: int, eps: float, target_s: float = 12.0):
     """The CPU oracle (single-threaded plain C, binary64) on the first rows of
     the same inputs; the row count is sized for about target_s seconds."""
@@ -282,7 +293,7 @@ def cpu_baseline(inp, M: int, N: int, eps: float, target_s: float = 12.0):
     nbytes = 8 * rows * N + 2 * N
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {rows} of {M} rows of the same inputs, one pass, "
-                      f"{dt:.1f} s; rows/s {rows / dt:.0f}"}
+                      f"{dt:.1f} s; rows/s {rows / dt:.0f}", "cpu": _cpu_model()}
 
 
 def cpu_baseline_all_cores(inp, M: int, N: int, eps: float, max_threads: int = 16):
@@ -306,7 +317,7 @@ def cpu_baseline_all_cores(inp, M: int, N: int, eps: float, max_threads: int = 1
     nbytes = 8 * M * N + 2 * N
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
             "sample": f"all {M} rows in {n} row slices, one pass, {dt:.2f} s; "
-                      f"rows/s {M / dt:.0f}; {avail} cores available"}
+                      f"rows/s {M / dt:.0f}; {avail} cores available", "cpu": _cpu_model()}
 
 
 def secondary(steps: int):
