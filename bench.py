@@ -33,6 +33,9 @@ METRIC = "achieved HBM GB/s (% of peak) + rows/s, bf16 fused Add+RMSNorm M=16384
 WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
 HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 0, 8, 2>"
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_vec_kernel_rmsnorm_bf16_32768x4096.md")
+BWD_KERNEL = "bwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, false, 2, 4, false, true>"
+COLREDUCE_KERNEL = "dw_colreduce_vec_kernel"
 KERNEL_SOURCES = ["add_rmsnorm_amd/csrc/kernels.hpp", "add_rmsnorm_amd/csrc/device.hpp",
                   "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp",
                   "add_rmsnorm_amd/csrc/api.hip"]
@@ -263,6 +266,56 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands:
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(out))
     log(f"wrote {TRAFFIC_FILE}")
+    if counter(fetch, BWD_KERNEL):
+        summarize_bwd(stats, fetch, write, f_scale, w_scale, commands)
+
+
+def summarize_bwd(stats, fetch, write, f_scale: float, w_scale: float, commands: dict):
+    """The RMS backward's traffic (bf16 32768 x 4096): the main kernel and the
+    column reduce that follows each of its dispatches, from the same counter
+    runs and calibration as the headline."""
+    M, N = 32768, 4096
+
+    def seq(rows):
+        rows = sorted(rows, key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0))))
+        main, red = [], []
+        for k, r in enumerate(rows):
+            if BWD_KERNEL in r["Kernel_Name"]:
+                main.append(float(r["Counter_Value"]))
+                nxt = next((q for q in rows[k + 1:] if COLREDUCE_KERNEL in q["Kernel_Name"]), None)
+                if nxt is not None:
+                    red.append(float(nxt["Counter_Value"]))
+        return sum(main) / len(main), sum(red) / len(red)
+
+    fm, fr = seq(fetch)
+    wm, wr = seq(write)
+    rd_main, wr_main = fm * f_scale * 1024, wm * w_scale * 1024
+    rd_red, wr_red = fr * f_scale * 1024, wr * w_scale * 1024
+    alg_read = 2 * 2 * M * N + 4 * M + 2 * N
+    alg_write = 2 * M * N + 4 * N
+    st = {r["Name"]: r for r in stats}
+    main_us = next(float(r["AverageNs"]) / 1e3 for n, r in st.items() if BWD_KERNEL in n)
+    out = [f"# {BWD_KERNEL}: RMSNorm backward, bf16, M={M} N={N}", "",
+           "Kernel time from the kernel trace of the default bench command:", "",
+           f"    {commands['trace']}", "",
+           f"- main kernel average: {main_us:.2f} us over its dispatches "
+           f"(algorithmic bytes {alg_read + alg_write} -> {(alg_read + alg_write) / main_us / 1e3:.1f} GB/s "
+           f"for the main kernel alone)", "",
+           "HBM traffic per call (the same two counter runs as the headline summary, "
+           "with the RMS backward timed after it, and the same device-copy calibration):", "",
+           f"    {commands['fetch']}", f"    {commands['write']}", "",
+           "| kernel | read bytes | written bytes |", "|---|---|---|",
+           f"| main (dy, x, rstd, w in; dx out; one dw partial row per block out) | {rd_main:.0f} | {wr_main:.0f} |",
+           f"| column reduce (partial rows in; dw out) | {rd_red:.0f} | {wr_red:.0f} |",
+           f"| algorithmic (dy, x, rstd, w in; dx, dw out) | {alg_read} | {alg_write} |", "",
+           f"Whole call (main kernel + column reduce) against the algorithmic bytes: read "
+           f"{(rd_main + rd_red) / alg_read:.4f}, written {(wr_main + wr_red) / alg_write:.4f}. "
+           f"The excess is the dw partial rows, 4 bytes per column per block of the persistent "
+           f"grid (here about {(wr_main - 2 * M * N) / (4 * N):.0f} rows), written once by the "
+           f"main kernel and read once by the column reduce.", ""]
+    with open(BWD_TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out))
+    log(f"wrote {BWD_TRAFFIC_FILE}")
 
 
 def _cpu_model() -> str:
@@ -320,14 +373,13 @@ def cpu_baseline_all_cores(inp, M: int, N: int, eps: float, max_threads: int = 1
                       f"rows/s {M / dt:.0f}; {avail} cores available", "cpu": _cpu_model()}
 
 
-def secondary(steps: int):
-    """Backward, smaller forward shapes and decode latency, same protocol."""
+def rms_bwd(steps: int):
+    """The RMS backward, bf16 32768 x 4096, rstd from the GPU forward."""
     import torch
     import add_rmsnorm_amd as ar
     import synth
 
     out = {}
-    # backward, bf16 32768 x 4096, rstd from the GPU forward
     cfg = synth.WORKLOADS["rmsnorm_bwd_bf16_32768x4096"]
     M, N = cfg["M"], cfg["N"]
     inp = synth.workload_inputs("rmsnorm_bwd_bf16_32768x4096")
@@ -352,6 +404,17 @@ def secondary(steps: int):
                                                                        HBM_PEAK_GBPS, 1),
         "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb}
     del sets
+    return out
+
+
+def secondary(steps: int):
+    """Backward, smaller forward shapes and decode latency, same protocol."""
+    import torch
+    import add_rmsnorm_amd as ar
+    import synth
+
+    out = rms_bwd(steps)
+    i = [0]
     # backward of the fused op at the headline shape: dy, dres, h read; dh written
     M, N = 16384, 7168
     inp = synth.workload_inputs(WORKLOAD)
@@ -565,6 +628,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true",
                     help="skip the secondary figures (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--with-rms-bwd", action="store_true",
+                    help="with --only-headline: also time the RMS backward (for counter runs)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output and exit")
     ap.add_argument("--profile-commands", default="{}",
@@ -630,6 +695,8 @@ def main():
     if not args.only_headline:
         log("secondary figures")
         rec["secondary"] = secondary(min(args.steps, 100))
+    elif args.with_rms_bwd:
+        rec["secondary"] = rms_bwd(args.steps)
     print(json.dumps(rec), flush=True)
 
 
