@@ -284,6 +284,27 @@ __device__ __forceinline__ uint32_t e2m1_code(float v)
     return c | ((__float_as_uint(v) >> 28) & 0x8u);
 }
 
+#ifndef ADDRMS_FP4_SOFTWARE
+#define ADDRMS_FP4_SOFTWARE 0
+#endif
+
+// Two floats, already divided by their block's scale, -> two E2M1 codes in
+// byte SEL of `old` (a in the low nibble), the other bytes of `old` kept.
+// Hardware: gfx950's v_cvt_scalef32_pk_fp4_f32 with a scale of 1.  Checked
+// on MI355X against the oracle's encoder over every grid point, midpoint and
+// neighbouring float of the E2M1 range, a dense sweep of [-10, 10], zeros and
+// subnormals, with power-of-two scales: round to nearest even, saturating at
+// 6, the sign kept for zero and subnormal inputs; the instruction divides by
+// its scale.  Software (the alternative): e2m1_code above.
+template <int SEL> __device__ __forceinline__ uint32_t pack_e2m1x2(uint32_t old, float a, float b)
+{
+#if ADDRMS_FP4_SOFTWARE
+    return (old & ~(0xFFu << (8 * SEL))) | ((e2m1_code(a) | (e2m1_code(b) << 4)) << (8 * SEL));
+#else
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+#endif
+}
+
 // E8M0 exponent of an MX block from its largest magnitude g (finite, >= 0):
 // floor(log2(g)) - 2, clamped below at -127 (zero and tiny blocks).
 __device__ __forceinline__ int mx_exponent(float g)

@@ -281,10 +281,14 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
                     if (v < nvec && (lane & (32 / NV - 1)) == 0)
                         srow[v / (32 / NV)] = nanb ? (uint8_t)0xFF : (uint8_t)(E + 127);
                     if (v < nvec) {
-                        uint32_t word = 0;
-#pragma unroll
-                        for (int e = 0; e < NV; ++e)
-                            word |= (nanb ? 0u : e2m1_code(o[k][e] * inv)) << (4 * e);
+                        uint32_t word = pack_e2m1x2<0>(0u, o[k][0] * inv, o[k][1] * inv);
+                        word = pack_e2m1x2<1>(word, o[k][2] * inv, o[k][3] * inv);
+                        if constexpr (NV == 8) {
+                            word = pack_e2m1x2<2>(word, o[k][4] * inv, o[k][5] * inv);
+                            word = pack_e2m1x2<3>(word, o[k][6] * inv, o[k][7] * inv);
+                        }
+                        if (nanb)
+                            word = 0u;
                         if constexpr (NV == 8)
                             __builtin_nontemporal_store(
                                 word, reinterpret_cast<uint32_t *>(qrow4 + (size_t)v * 4));
@@ -473,8 +477,7 @@ __global__ void __launch_bounds__(256) fwd_elem_kernel(FwdArgs a)
                 for (int j = j0; j < j1; j += 2) {
                     const float o0 = (ld_elem<T>(src, base + j) * rs) * ld_elem<WT>(a.w, j);
                     const float o1 = (ld_elem<T>(src, base + j + 1) * rs) * ld_elem<WT>(a.w, j + 1);
-                    a.q[(base + j) / 2] =
-                        nanb ? (uint8_t)0 : (uint8_t)(e2m1_code(o0 * inv) | (e2m1_code(o1 * inv) << 4));
+                    a.q[(base + j) / 2] = nanb ? (uint8_t)0 : (uint8_t)pack_e2m1x2<0>(0u, o0 * inv, o1 * inv);
                 }
             }
             continue;

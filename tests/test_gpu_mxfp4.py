@@ -169,3 +169,57 @@ def test_custom_ops_match_the_binding():
     torch.cuda.synchronize()
     for u, v in list(zip(a, b)) + list(zip(c, d)):
         assert u.dtype == v.dtype and torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+
+
+def _tie_rows(dtype):
+    """Two rows of 512 columns whose y is exact on both sides, so that every
+    E2M1 decision, ties included, must match bit for bit: block 0 holds the
+    seven E2M1 midpoints and their negatives (scale 2^0), block 1 twice them
+    (2^1), block 2 sixteen times them (2^4), block 3 grid points, values just
+    off midpoints and a saturating 7; the rest are zeros.  eps tops the mean
+    square up to 4^k and w = 2^k, so rstd = 2^-k and y = x exactly."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    row = np.zeros(512)
+    row[0:14] = mids + [-m for m in mids]
+    row[32:46] = [2 * m for m in mids] + [-2 * m for m in mids]
+    row[64:78] = [16 * m for m in mids] + [-16 * m for m in mids]
+    row[96:112] = [0.5, 1, 1.5, 2, 3, 4, 6, 7, -0.5, -1, -3, -6, 0.3125, 0.6875, 2.25, -4.5]
+    ms = float((row ** 2).sum() / row.size)
+    k = 0
+    while 4.0 ** k < ms:
+        k += 1
+    eps = 4.0 ** k - ms
+    assert np.float32(eps) == eps and np.float32(ms) == ms
+    x = torch.tensor(np.stack([row, -row]), dtype=torch.float64).to(dtype)
+    assert torch.equal(x.double(), torch.tensor(np.stack([row, -row])))
+    w = torch.full((512,), 2.0 ** k, dtype=dtype)
+    return x, w, eps
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("force_elem", ["0", "1"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_e2m1_ties_exact(monkeypatch, dtype, force_elem, fused):
+    """Round-half-to-even and saturation of the E2M1 encoding (on the GPU the
+    hardware conversion), bit for bit against the oracle."""
+    monkeypatch.setenv("ADDRMS_FORCE_ELEM", force_elem)
+    x, w, eps = _tie_rows(dtype)
+    if fused:
+        r = torch.zeros_like(x)
+        q, s, res = ar.add_rmsnorm_fwd_mxfp4(x.to(DEV), r.to(DEV), w.to(DEV), eps)
+        qr, sr, _, _ = oracle.rmsnorm_fwd_mxfp4(x, w, eps, residual=r)
+    else:
+        q, s = ar.rmsnorm_fwd_mxfp4(x.to(DEV), w.to(DEV), eps)
+        qr, sr, _ = oracle.rmsnorm_fwd_mxfp4(x, w, eps)
+    torch.cuda.synchronize()
+    sb = s.view(torch.uint8).cpu()
+    assert torch.equal(sb, sr), (sb[:, :4], sr[:, :4])
+    assert list(sr[0, :4]) == [127, 128, 131, 127]
+    codes = oracle.unpack_fp4(q.view(torch.uint8).cpu())
+    rcodes = oracle.unpack_fp4(qr)
+    assert np.array_equal(codes, rcodes), np.nonzero(codes != rcodes)
+    # the ties themselves, read from the pages' grid: 0.25 -> 0, 0.75 -> 1.0,
+    # 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0
+    assert list(codes[0, :7]) == [0, 2, 2, 4, 4, 6, 6]
+    assert list(codes[0, 7:14]) == [8, 10, 10, 12, 12, 14, 14]
+    assert list(codes[1, :7]) == [8, 10, 10, 12, 12, 14, 14]

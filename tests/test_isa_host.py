@@ -31,6 +31,7 @@ MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 HEADLINE = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELi0ELi8ELi2EEEvNS_7FwdArgsE"
 FP8_FUSED = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELi1ELi8ELi2EEEvNS_7FwdArgsE"
+MXFP4_FUSED = "_ZN6addrms14fwd_vec_kernelINS_6bf16_tES1_Li0ELb1ELi3ELi8ELi2EEEvNS_7FwdArgsE"
 ROPE_D128 = "_ZN6addrms15rope_vec_kernelINS_6bf16_tES1_Li8ELb0ELi4EEEvNS_8RopeArgsE"
 
 
@@ -139,6 +140,14 @@ def test_fp8_kernel_uses_hardware_e4m3_conversion(kernels):
     co, _ = kernels[FP8_FUSED]
     asm = _disasm(co, FP8_FUSED)
     assert "v_cvt_pk_fp8_f32" in asm
+    assert re.search(r"global_load_dwordx4 [^\n]* nt", asm)
+
+
+def test_mxfp4_kernel_uses_hardware_e2m1_conversion(kernels):
+    # four packed conversions per 16-byte vector (8 bf16 values), 2 vectors a lane
+    co, _ = kernels[MXFP4_FUSED]
+    asm = _disasm(co, MXFP4_FUSED)
+    assert len(re.findall(r"v_cvt_scalef32_pk_fp4_f32", asm)) >= 8
     assert re.search(r"global_load_dwordx4 [^\n]* nt", asm)
 
 
