@@ -192,8 +192,13 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
         }
 
         // 2. residual add (float32), store the residual as T, and accumulate
-        //    the first row sum of the stored residual: h^2 (RMS) or h (Layer)
-        float s1 = 0.0f;
+        //    the first row sum of the stored residual: h^2 (RMS) or h (Layer).
+        //    E4M3 with a per-row scale and held weights: also max |h * w|,
+        //    so that the row's absmax, rstd * max |h * w| (rstd > 0), comes
+        //    from the same exchange as the sum instead of a second one after
+        //    y (it differs from max |y| only in float32 rounding).
+        constexpr bool EARLY_MAX = QM == kQRow && HOLD_W;
+        float s1 = 0.0f, hwmax = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             float h[NV];
@@ -213,12 +218,38 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 #pragma unroll
             for (int e = 0; e < NV; ++e)
                 s1 = (NORM == kRms) ? __builtin_fmaf(h[e], h[e], s1) : s1 + h[e];
+            if constexpr (EARLY_MAX) {
+                float wf[NV];
+                unpack_w<T, WT>(wr[k], wf);
+#pragma unroll
+                for (int e = 0; e < NV; ++e)
+                    hwmax = __builtin_fmaxf(hwmax, __builtin_fabsf(h[e] * wf[e]));
+            }
         }
 
         // 3. row statistics
         const int slot = (it & 1) * 2;
         float mu = 0.0f, rs;
-        if constexpr (NORM == kRms) {
+        if constexpr (EARLY_MAX) {
+            // the sum and the maximum through one LDS exchange and barrier
+            float t = wave_sum(s1), m = wave_max(hwmax);
+            if constexpr (WPR > 1) {
+                if (lane == 0) {
+                    part[slot][wir] = t;
+                    part[slot + 1][wir] = m;
+                }
+                __syncthreads();
+                t = 0.0f;
+                m = 0.0f;
+#pragma unroll
+                for (int i = 0; i < WPR; ++i) {
+                    t += part[slot][i];
+                    m = __builtin_fmaxf(m, part[slot + 1][i]);
+                }
+            }
+            rs = 1.0f / __builtin_sqrtf(t * inv_n + a.eps);
+            hwmax = m;
+        } else if constexpr (NORM == kRms) {
             rs = 1.0f / __builtin_sqrtf(row_sum(s1, slot) * inv_n + a.eps);
         } else {
             mu = row_sum(s1, slot) * inv_n;
@@ -255,7 +286,7 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
 #pragma unroll
                 for (int e = 0; e < NV; ++e) {
                     o[k][e] = v < nvec ? (h[e] * rs) * wf[e] : 0.0f;
-                    if constexpr (QM == kQRow)
+                    if constexpr (QM == kQRow && !EARLY_MAX)
                         am = __builtin_fmaxf(am, __builtin_fabsf(o[k][e]));
                 }
             }
@@ -303,7 +334,13 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
                 // consecutive lanes (kQGroup)
                 float inv_k[VPL];
                 if constexpr (QM == kQRow) {
-                    am = row_max(am, slot + 1);
+                    if constexpr (EARLY_MAX) {
+                        am = rs * hwmax;
+                        if (!(am == am)) // NaN row (rstd NaN) or 0 * inf: as max |y| over no finite y
+                            am = 0.0f;
+                    } else {
+                        am = row_max(am, slot + 1);
+                    }
                     float inv = 1.0f, sc = 1.0f;
                     if (am != 0.0f) {
                         inv = 448.0f / am;
