@@ -144,6 +144,30 @@ def test_fp8_special_rows():
     assert_close(deq, y[0], "dequantised row", atol=float(s[3]) * 2.0 ** -9, rtol=0.07)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_fp8_infinite_rows(fused):
+    """A row holding +-Inf: rstd is 0, so y is NaN there and a zero of either
+    sign elsewhere; the row's scale stays 1 (no finite nonzero y), as in the
+    oracle."""
+    N = 4096
+    inp = synth.add_rmsnorm_fwd_inputs(2, N, torch.bfloat16, seed=5)
+    x = inp["x"].clone()
+    x[0, 7] = float("inf")
+    x[1, 9] = float("-inf")
+    if fused:
+        r = torch.zeros_like(x)
+        q, s, _ = ar.add_rmsnorm_fwd_fp8(x.to(DEV), r.to(DEV), inp["w"].to(DEV), 1e-6)
+    else:
+        q, s = ar.rmsnorm_fwd_fp8(x.to(DEV), inp["w"].to(DEV), 1e-6)
+    torch.cuda.synchronize()
+    qr, sr = oracle.rmsnorm_fwd_fp8(x, inp["w"], 1e-6)[:2]
+    assert torch.equal(s.cpu(), sr) and torch.all(sr == 1.0)
+    qb = q.view(torch.uint8).cpu().numpy() & 0x7F
+    rb = qr.view(torch.uint8).numpy() & 0x7F
+    assert np.array_equal(qb, rb)
+    assert qb[0, 7] == 0x7F and qb[1, 9] == 0x7F and int((qb != 0).sum()) == 2
+
+
 # ---- one scale per group of columns -----------------------------------------
 
 @pytest.mark.parametrize("fused", [True, False])
