@@ -215,6 +215,20 @@ def test_backward_in_place_and_empty(monkeypatch, prefetch):
                                        (24, 24576, torch.bfloat16), (24, 30720, torch.bfloat16),
                                        (20, 16384, torch.float32)])
 def test_fused_backward(M, N, dtype):
+    _fused_backward_case(M, N, dtype)
+
+
+# the fused LayerNorm backward in the wide variant (1024-thread blocks, 2
+# waves per row), built up to 2 vectors a lane: forced, with a ragged row
+@pytest.mark.parametrize("M,N,dtype", [(3001, 2048, torch.bfloat16), (777, 1032, torch.bfloat16),
+                                       (500, 1024, torch.float32)])
+def test_fused_backward_wide_variant(monkeypatch, M, N, dtype):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+    _fused_backward_case(M, N, dtype)
+
+
+def _fused_backward_case(M, N, dtype):
     inp = inputs(M, N, dtype, seed=29)
     _, h, mean, rstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
     dy = synth.store(synth.normal(29, "dy", (M, N)), dtype)
