@@ -288,6 +288,16 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
 {
     const int forced = env_int("ADDRMS_BWD_WPR");
     int best_wi = -1, best_vi = -1;
+    // The fused RMS backward at 4 vectors a lane with 2 waves per row (385 to
+    // 512 vectors) takes the next-row prefetch kernel rather than 1 wave per
+    // row with 7 or 8 vectors: measured on MI355X, bf16, 24576 x 3584 120.8
+    // against 127.9 us, 32768 x 4096 and 16384 x 4096 level or 0.8 % faster.
+    if (forced == 0 && res && norm == kRms && (nvec + 127) / 128 == 4 && M * 2 >= 4LL * cus &&
+        env_int("ADDRMS_BWD_PREFETCH") != 2 && bwd_built(norm, res, 2, 4)) {
+        *wi_out = 1; // kWprList[1] == 2
+        *vi_out = vpl_index(4);
+        return true;
+    }
     if (forced == 0 && (res || norm == kLayer) && nvec >= 768 && M * 8 >= 4LL * cus) {
         const int vi = vpl_index((nvec + 511) / 512);
         if (vi >= 0 && bwd_built(norm, res, 8, kVplList[vi])) {
@@ -355,14 +365,15 @@ bool use_wide_bwd(const BwdTable &tab, int norm, bool res, int64_t M, int64_t N,
     return M >= (int64_t)rpb * cus && (kVplList[vi] <= 3 || M <= 32LL * cus);
 }
 
-// The RMS and LayerNorm backwards with the next row's loads in flight across
-// the current row's exchange and output pass (the PF kernels), measured on
-// MI355X at 4 vectors a lane and 2 waves per row: RMS 1.5-3.6 % faster (3584
-// to 4096 bf16 or 1792 to 2048 float32 columns, 12288 to 65536 rows),
-// LayerNorm 3.5-5.8 % (3584 to 4096 bf16 columns, 8192 to 32768 rows); so
-// it is the default there.  (In the fused backwards, 8 waves per row, it was
-// 4-9 % slower and is not built.)  ADDRMS_BWD_PREFETCH=1 takes it wherever
-// it is built (up to 4 vectors a lane), ADDRMS_BWD_PREFETCH=2 never.
+// The backwards with the next row's loads in flight across the current row's
+// exchange and output pass (the PF kernels), measured on MI355X at 4 vectors
+// a lane and 2 waves per row: RMS 1.5-3.6 % faster (3584 to 4096 bf16 or
+// 1792 to 2048 float32 columns, 12288 to 65536 rows), LayerNorm 3.5-5.8 %
+// (3584 to 4096 bf16 columns, 8192 to 32768 rows), fused LayerNorm 2-5 %
+// (bf16, 3584 and 4096 columns); so it is the default there.  The fused RMS
+// backward takes it too (see pick_bwd).  ADDRMS_BWD_PREFETCH=1 takes it
+// wherever it is built (2 waves per row, up to 4 vectors a lane),
+// ADDRMS_BWD_PREFETCH=2 never.
 bool use_prefetch_bwd(const BwdTable &tab, int norm, bool res, int wi, int vi)
 {
     const int mode = env_int("ADDRMS_BWD_PREFETCH");

@@ -163,7 +163,7 @@ struct FwdTable {
 struct BwdTable {
     KernelRef vec[2][2][kBwdNumWpr][kNumVpl];
     KernelRef wide[2][2][kNumVpl]; // WPR = kBwdWideWpr in 1024-thread blocks; null where not built
-    KernelRef pf[2][2][kBwdNumWpr][kNumVpl]; // next-row prefetch (2 waves per row, no residual gradient); null where not built
+    KernelRef pf[2][2][kBwdNumWpr][kNumVpl]; // next-row prefetch (2 waves per row); null where not built
     KernelRef elem_dx[2][2];
     KernelRef elem_dw[2];
 };

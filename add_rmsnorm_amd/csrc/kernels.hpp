@@ -693,11 +693,10 @@ __global__ void __launch_bounds__(kBwdBlockOf(WPR, WIDE))
     // PF: the next row's loads go out after this row's sums, so they are in
     // flight across the row exchange and the output pass.  The lane then holds
     // two rows, so fewer waves fit per SIMD (RMS at 4 vectors a lane: 3
-    // instead of 4), and the kernel still streams faster: 1.5-3.6 % for the
-    // RMS backward and 3.5-5.8 % for the LayerNorm backward at 4 vectors a
-    // lane, 2 waves per row (measured on MI355X).  dx is bit-identical; dw
-    // differs only in how rows group into partial sums (the grid follows
-    // residency).
+    // instead of 4), and the kernel still streams faster at 4 vectors a lane
+    // and 2 waves per row (measured on MI355X: RMS 1.5-3.6 %, LayerNorm
+    // 3.5-5.8 %, fused LayerNorm 2-5 %).  dx is bit-identical; dw differs
+    // only in how rows group into partial sums (the grid follows residency).
     u32x4 ndy[PF ? VPL : 1], nx[PF ? VPL : 1];
     u32x4 ndr[(PF && RES) ? VPL : 1];
     float nrs = 0.0f, nmu = 0.0f;
@@ -1117,11 +1116,10 @@ template <typename T, typename WT> struct TableBuilder {
     {
         ((row[VI] = bwd_wide_ref<NM, R, kVplList[VI]>()), ...);
     }
-    // Next-row prefetch variants: the RMS and LayerNorm backwards without the
-    // residual gradient, 2 waves per row, up to 4 vectors a lane.
+    // Next-row prefetch variants: 2 waves per row, up to 4 vectors a lane.
     template <int NM, bool R, int WPR, int VPL> static KernelRef bwd_pf_ref()
     {
-        if constexpr (!R && WPR == 2 && VPL <= 4 && bwd_built(NM, R, WPR, VPL))
+        if constexpr (WPR == 2 && VPL <= 4 && bwd_built(NM, R, WPR, VPL))
             return KernelRef{
                 reinterpret_cast<const void *>(&bwd_vec_kernel<T, WT, NM, R, WPR, VPL, false, true>),
                 kBwdBlockOf(WPR)};
@@ -1153,6 +1151,8 @@ template <typename T, typename WT> struct TableBuilder {
         bwd_all<kLayer, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         bwd_pf_all<kRms, false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         bwd_pf_all<kLayer, false>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        bwd_pf_all<kRms, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
+        bwd_pf_all<kLayer, true>(t, std::make_integer_sequence<int, kBwdNumWpr>{});
         bwd_wide_row<kRms, false>(t.wide[kRms][0], std::make_integer_sequence<int, kNumVpl>{});
         bwd_wide_row<kRms, true>(t.wide[kRms][1], std::make_integer_sequence<int, kNumVpl>{});
         bwd_wide_row<kLayer, false>(t.wide[kLayer][0], std::make_integer_sequence<int, kNumVpl>{});

@@ -41,7 +41,8 @@ def check(dy, dres, h, w, rstd, what=""):
 
 
 # default choices: 16384 x 7168 and 600 x 6152 (769 vectors, ragged) take 8
-# waves per row; 4096 x 4096 one wave per row with 8 vectors a lane
+# waves per row; 4096 x 4096 the next-row prefetch kernel (2 waves per row,
+# 4 vectors a lane)
 @pytest.mark.parametrize("M,N", [(16384, 7168), (600, 6152), (4096, 4096), (300, 1032)])
 def test_fused_bwd_bf16(M, N):
     check(*fused_case(M, N, torch.bfloat16), f"{M}x{N}")
@@ -75,6 +76,27 @@ def test_fused_bwd_wide_variant(monkeypatch, dtype, M, N):
     monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
     monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
     check(*fused_case(M, N, dtype, seed=M), f"wide {M}x{N}")
+
+
+# The next-row prefetch kernel (2 waves per row): forced at 1 to 4 vectors a
+# lane on every dtype pair, and on its default shapes (4 vectors a lane)
+@pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.float32),
+                                          (torch.float32, torch.bfloat16)])
+def test_fused_bwd_prefetch_forced(monkeypatch, dtype, wdtype):
+    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+    monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
+    monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+    cases = [(1001, 4096), (777, 2056), (9, 520)] if dtype == torch.bfloat16 \
+        else [(1001, 2048), (777, 1028), (9, 260)]
+    for M, N in cases:
+        check(*fused_case(M, N, dtype, wdtype, seed=M + N), f"prefetch {M}x{N}")
+
+
+@pytest.mark.parametrize("M,N", [(24576, 3584), (16384, 4096)])
+def test_fused_bwd_prefetch_default_shapes(M, N):
+    check(*fused_case(M, N, torch.bfloat16, seed=M), f"{M}x{N}")
 
 
 @pytest.mark.parametrize("M,N", [(5, 4096), (129, 7), (64, 1000)])

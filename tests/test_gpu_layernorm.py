@@ -228,6 +228,20 @@ def test_fused_backward_wide_variant(monkeypatch, M, N, dtype):
     _fused_backward_case(M, N, dtype)
 
 
+# the fused LayerNorm backward through the next-row prefetch kernel: forced
+# at 2 and 4 vectors a lane, and on a default shape (4 vectors a lane)
+@pytest.mark.parametrize("M,N,dtype,force", [(1001, 4096, torch.bfloat16, True),
+                                             (777, 2056, torch.bfloat16, True),
+                                             (500, 2048, torch.float32, True),
+                                             (16384, 4096, torch.bfloat16, False)])
+def test_fused_backward_prefetch(monkeypatch, M, N, dtype, force):
+    if force:
+        monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
+        monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
+        monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+    _fused_backward_case(M, N, dtype)
+
+
 def _fused_backward_case(M, N, dtype):
     inp = inputs(M, N, dtype, seed=29)
     _, h, mean, rstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
