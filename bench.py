@@ -407,6 +407,52 @@ def rms_bwd(steps: int):
     return out
 
 
+def cpu_baseline_configs(target_s: float = 2.0):
+    """The oracle (single-threaded, unchanged) on each of the other workloads:
+    a bounded sample of rows (all rows when they fit in about target_s),
+    rows/s and GB/s over the same algorithmic bytes as the GPU figures."""
+    import oracle
+    import synth
+    out = {}
+
+    def run(name, fn, per_row_bytes, once_bytes, M):
+        probe = min(M, 16)
+        t0 = time.perf_counter()
+        fn(probe)
+        per_row = (time.perf_counter() - t0) / probe
+        rows = int(min(M, max(probe, target_s / max(per_row, 1e-9))))
+        t0 = time.perf_counter()
+        fn(rows)
+        dt = time.perf_counter() - t0
+        out[name] = {"rows": rows, "of_rows": M, "seconds": round(dt, 3),
+                     "rows_per_s": round(rows / dt, 1),
+                     "GBps": round((per_row_bytes * rows + once_bytes) / dt / 1e9, 4), "cores": 1}
+
+    c = synth.WORKLOADS["rmsnorm_fwd_f32_256x4096"]
+    inp = synth.workload_inputs("rmsnorm_fwd_f32_256x4096")
+    run("rmsnorm_fwd_f32_256x4096", lambda n: oracle.rmsnorm_fwd(inp["x"][:n], inp["w"], c["eps"]),
+        8 * c["N"], 4 * c["N"], c["M"])
+    c = synth.WORKLOADS["add_rmsnorm_fwd_bf16_4096x4096"]
+    inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_4096x4096", M=2048)
+    run("add_rmsnorm_fwd_bf16_4096x4096",
+        lambda n: oracle.add_rmsnorm_fwd(inp["x"][:n], inp["r"][:n], inp["w"], c["eps"]),
+        8 * c["N"], 2 * c["N"], 2048)
+    out["add_rmsnorm_fwd_bf16_4096x4096"]["of_rows"] = c["M"]
+    c = synth.WORKLOADS["add_rmsnorm_fwd_bf16_decode_n8192"]
+    inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_decode_n8192", M=512)
+    run("add_rmsnorm_fwd_bf16_decode_n8192_m512",
+        lambda n: oracle.add_rmsnorm_fwd(inp["x"][:n], inp["r"][:n], inp["w"], c["eps"]),
+        8 * c["N"], 4 * c["N"], 512)
+    c = synth.WORKLOADS["rmsnorm_bwd_bf16_32768x4096"]
+    inp = synth.workload_inputs("rmsnorm_bwd_bf16_32768x4096", M=2048)
+    rstd = oracle.rmsnorm_fwd(inp["x"], inp["w"], c["eps"])[1]
+    run("rmsnorm_bwd_bf16_32768x4096",
+        lambda n: oracle.rmsnorm_bwd(inp["dy"][:n], inp["x"][:n], inp["w"], rstd[:n]),
+        6 * c["N"] + 4, 6 * c["N"], 2048)
+    out["rmsnorm_bwd_bf16_32768x4096"]["of_rows"] = c["M"]
+    return out
+
+
 def secondary(steps: int):
     """Backward, smaller forward shapes and decode latency, same protocol."""
     import torch
@@ -691,6 +737,8 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(h["inputs"], M, N, h["eps"])
         rec["cpu_baseline_all_cores"] = cpu_baseline_all_cores(h["inputs"], M, N, h["eps"])
+        log("cpu baseline: oracle on the other workloads")
+        rec["cpu_baseline_configs"] = cpu_baseline_configs()
     del h
     if not args.only_headline:
         log("secondary figures")

@@ -71,3 +71,12 @@ def test_summaries_scale_counters_and_pair_the_column_reduce(tmp_path, monkeypat
     assert f"| column reduce (partial rows in; dw out) | {P * bn * 4} | {4 * bn} |" in b
     assert f"(here about {P} rows)" in b
     assert "main kernel average: 137.00 us" in b
+
+
+def test_oracle_baselines_of_the_other_workloads():
+    out = bench.cpu_baseline_configs(target_s=0.05)
+    assert set(out) == {"rmsnorm_fwd_f32_256x4096", "add_rmsnorm_fwd_bf16_4096x4096",
+                        "add_rmsnorm_fwd_bf16_decode_n8192_m512", "rmsnorm_bwd_bf16_32768x4096"}
+    for name, r in out.items():
+        assert 1 <= r["rows"] <= r["of_rows"] and r["rows_per_s"] > 0 and r["GBps"] > 0, name
+        assert r["cores"] == 1
