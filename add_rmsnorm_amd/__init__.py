@@ -25,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_bwd",
+__all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc", "add_rmsnorm_bwd",
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
            "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "rmsnorm_fwd_fp8",
            "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_mxfp4", "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
@@ -60,6 +60,8 @@ def _load():
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.rmsnorm_bwd.restype = i32
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.rmsnorm_bwd_noalloc.restype = i32
+    lib.rmsnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, vp]
     lib.add_rmsnorm_bwd.restype = i32
     lib.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.rmsnorm_fwd_fp8.restype = i32
@@ -251,6 +253,30 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
                               _code(x, "x"), _code(w, "w"), _stream(dev))
     if st != 0:
         raise AddRmsError(st, "rmsnorm_bwd")
+    return dx, dw
+
+
+def rmsnorm_bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor,
+                        *, dx=None, dw=None):
+    """rmsnorm_bwd without a workspace: the library keeps the dw partial sums
+    in a fixed device scratch of its own (16 MiB per GPU), so the library call
+    allocates nothing (pass dx and dw to allocate nothing at all).  Calls that
+    may overlap on one GPU share that scratch and must be serialised.
+    Returns (dx, dw)."""
+    _dev(x, "x")
+    M, N = _rows(x)
+    _dev(dy, "dy", x.dtype, x.shape)
+    _dev(w, "w", shape=(N,))
+    _dev(rstd, "rstd", torch.float32, x.shape[:-1])
+    dx = torch.empty_like(x) if dx is None else _dev(dx, "dx", x.dtype, x.shape)
+    dw = (torch.empty(N, dtype=torch.float32, device=x.device) if dw is None
+          else _dev(dw, "dw", torch.float32, (N,)))
+    dev = x.get_device()
+    with _OnDevice(dev):
+        st = _lib.rmsnorm_bwd_noalloc(_p(dy), _p(x), _p(w), _p(rstd), _p(dx), _p(dw), M, N,
+                                      _code(x, "x"), _code(w, "w"), _stream(dev))
+    if st != 0:
+        raise AddRmsError(st, "rmsnorm_bwd_noalloc")
     return dx, dw
 
 

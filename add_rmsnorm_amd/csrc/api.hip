@@ -517,10 +517,13 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     return launch(k, dim3(grid), 0, &a, s);
 }
 
+// fit_ws: the workspace has a fixed capacity (the no-allocation entry point's
+// scratch): the call uses as many dw partial rows as fit in it, at least one,
+// instead of requiring the size rmsnorm_bwd_workspace_bytes gives.
 int bwd_common(int norm, const void *dy, const void *dres, const void *x, const void *w,
                const float *mean, const float *rstd, void *dx, float *dw, float *db,
                void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
-               int w_dtype, void *stream)
+               int w_dtype, void *stream, bool fit_ws = false)
 {
     const bool res = dres != nullptr;
     const bool ln = norm == kLayer;
@@ -533,7 +536,13 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     int rc = check_shape(M, N, dtype);
     if (rc != ADDRMS_OK)
         return rc;
-    const size_t need = ln ? layernorm_bwd_workspace_bytes(M, N) : rmsnorm_bwd_workspace_bytes(M, N);
+    size_t need = ln ? layernorm_bwd_workspace_bytes(M, N) : rmsnorm_bwd_workspace_bytes(M, N);
+    if (fit_ws && M > 0 && need > workspace_bytes) {
+        // one partial row (two for LayerNorm) is the least a call can use
+        if ((uint64_t)N > (uint64_t)workspace_bytes / 4u / (ln ? 2u : 1u))
+            return ADDRMS_ERR_SCRATCH;
+        need = workspace_bytes;
+    }
     if (M > 0 && (!workspace || workspace_bytes < need || need == 0))
         return ADDRMS_ERR_WORKSPACE;
     const size_t mat = (size_t)M * (size_t)N * esize(dtype);
@@ -775,6 +784,40 @@ int rope_common(const void *q, const void *k, const void *wq, const void *wk, co
 
 using namespace addrms;
 
+// Scratch of the no-allocation backward: the dw partial rows live in this
+// file-scope device array instead of a caller's workspace.  Each device that
+// loads the library holds its own copy until the process ends.  In host code
+// `scratch` only names a host-side stand-in: its device address on the
+// current device comes from hipGetSymbolAddress, taken once per device and
+// kept in g_scratch; only that address is ever passed to a kernel.
+static __device__ __align__(256) float scratch[ADDRMS_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch;
+
+int scratch_ptr(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return fail_hip(e);
+        if (p == nullptr)
+            return fail_hip(hipErrorInvalidSymbol);
+        it = g_scratch.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return ADDRMS_OK;
+}
+} // namespace
+
 extern "C" {
 
 int rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int64_t M, int64_t N,
@@ -888,6 +931,26 @@ int rmsnorm_bwd(const void *dy, const void *x, const void *w, const float *rstd,
                       workspace_bytes, M, N, dtype, w_dtype, stream);
 }
 
+int rmsnorm_bwd_noalloc(const void *dy, const void *x, const void *w, const float *rstd, void *dx,
+                        float *dw, int64_t M, int64_t N, int dtype, int w_dtype, void *stream)
+{
+    // validate what needs no device first, so that bad arguments make no HIP call
+    if (!w || !dw || (M != 0 && (!dy || !x || !rstd || !dx)))
+        return ADDRMS_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
+        return ADDRMS_ERR_DTYPE;
+    int rc = check_shape(M, N, dtype);
+    if (rc != ADDRMS_OK)
+        return rc;
+    if ((uint64_t)N > ADDRMS_NOALLOC_SCRATCH_BYTES / sizeof(float))
+        return ADDRMS_ERR_SCRATCH;
+    void *ws = nullptr;
+    if ((rc = scratch_ptr(&ws)) != ADDRMS_OK)
+        return rc;
+    return bwd_common(kRms, dy, nullptr, x, w, nullptr, rstd, dx, dw, nullptr, ws,
+                      ADDRMS_NOALLOC_SCRATCH_BYTES, M, N, dtype, w_dtype, stream, true);
+}
+
 int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void *w,
                     const float *rstd, void *dh, float *dw, void *workspace,
                     size_t workspace_bytes, int64_t M, int64_t N, int dtype, int w_dtype,
@@ -943,6 +1006,8 @@ const char *addrms_status_str(int status)
     case ADDRMS_ERR_ALIAS: return "output overlaps another argument";
     case ADDRMS_ERR_WORKSPACE: return "workspace missing or too small";
     case ADDRMS_ERR_HIP: return "HIP call failed";
+    case ADDRMS_ERR_SCRATCH:
+        return "a row is wider than the no-allocation backward's built-in scratch holds";
     default: return "unknown status";
     }
 }

@@ -69,6 +69,7 @@ extern "C" {
 #define ADDRMS_ERR_ALIAS -5     /* forbidden overlap between buffers */
 #define ADDRMS_ERR_WORKSPACE -6 /* workspace NULL or smaller than required */
 #define ADDRMS_ERR_HIP -7       /* a HIP call failed; see addrms_last_hip_error() */
+#define ADDRMS_ERR_SCRATCH -8   /* a row is wider than rmsnorm_bwd_noalloc's scratch holds */
 
 /*
  * RMSNorm forward.
@@ -120,6 +121,27 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N);
 int rmsnorm_bwd(const void *dy, const void *x, const void *w, const float *rstd, void *dx,
                 float *dw, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
                 int dtype, int w_dtype, void *stream);
+
+/*
+ * rmsnorm_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The dw partial sums live in a scratch array of
+ * ADDRMS_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU it runs on, from the first call on that GPU until the process ends;
+ * the call itself allocates nothing.  It uses as many partial rows as fit
+ * (min(M, 1024, scratch / (4 N)) of them), so dx is the same as rmsnorm_bwd's
+ * and dw differs from it only in summation order when N > 4096.
+ *   Arguments, layout, aliasing and errors as rmsnorm_bwd, without the
+ *   workspace; N above ADDRMS_NOALLOC_SCRATCH_BYTES / 4 is
+ *   ADDRMS_ERR_SCRATCH.
+ * Every call on one GPU shares that GPU's scratch (nothing in it needs to
+ * start at zero): calls that may overlap on one GPU, from several streams or
+ * threads, race on it and must be serialised by the caller.
+ */
+#define ADDRMS_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int rmsnorm_bwd_noalloc(const void *dy, const void *x, const void *w, const float *rstd, void *dx,
+                        float *dw, int64_t M, int64_t N, int dtype, int w_dtype, void *stream);
 
 /*
  * Backward of the fused residual-Add + RMSNorm (KernelAgent-Oink's fused op;

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "addrms.h")
 LIB = os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms.so")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_EPS, E_ALIAS, E_WS = 0, -1, -2, -3, -4, -5, -6
+OK, E_NULL, E_SHAPE, E_DTYPE, E_EPS, E_ALIAS, E_WS, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -8
 F32, BF16 = 0, 1
 
 
@@ -35,6 +35,7 @@ def lib():
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.rmsnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, vp]
     lib.layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.add_layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.layernorm_bwd_workspace_bytes.restype = sz
@@ -56,7 +57,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd",
-                                  "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
+                                  "rmsnorm_bwd_noalloc", "add_rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
                                   "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
                                   "layernorm_bwd_workspace_bytes", "add_layernorm_bwd",
                                   "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_fp8_grouped",
@@ -71,7 +72,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_EPS, E_ALIAS, E_WS, -7):
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_EPS, E_ALIAS, E_WS, -7, E_SCRATCH):
         assert lib.addrms_status_str(st)
     assert lib.addrms_status_str(12345) == b"unknown status"
 
@@ -299,3 +300,19 @@ def test_mxfp4_validation(lib):
                                               k.get("res", D), None, 4, 64, 1e-6, BF16, BF16,
                                               None)
     assert g(res=None) == E_NULL and g(q=C) == E_ALIAS and g(s=D + 8) == E_ALIAS
+
+
+def test_noalloc_validation(lib):
+    """rmsnorm_bwd_noalloc rejects bad arguments before any HIP call, rows
+    wider than its 16 MiB scratch holds (4 Mi float32 columns) included."""
+    f = lib.rmsnorm_bwd_noalloc
+    A, B, C, D, E, G = (0x10000 * k for k in range(1, 7))
+    assert f(A, B, C, D, E, None, 4, 64, BF16, BF16, None) == E_NULL
+    assert f(None, B, C, D, E, G, 4, 64, BF16, BF16, None) == E_NULL
+    assert f(A, B, None, D, E, G, 4, 64, BF16, BF16, None) == E_NULL
+    assert f(A, B, C, None, E, G, 4, 64, BF16, BF16, None) == E_NULL
+    assert f(A, B, C, D, E, G, 4, 64, 7, BF16, None) == E_DTYPE
+    assert f(A, B, C, D, E, G, -1, 64, BF16, BF16, None) == E_SHAPE
+    assert f(A, B, C, D, E, G, 4, 0, BF16, BF16, None) == E_SHAPE
+    assert f(A, B, C, D, E, G, 1, (16 << 20) // 4 + 1, BF16, BF16, None) == E_SCRATCH
+    assert f(A, B, C, D, E, G, 1, (16 << 20) // 4 + 8, F32, F32, None) == E_SCRATCH
