@@ -1,22 +1,43 @@
 // Measurement aid for the benchmark, built as its own small library
 // (libaddrms_probe.so) and never linked into libaddrms.so.
 //
-// The fused forward reads two streams and writes two.  This kernel does only
-// that -- c = a + b, d = a ^ b on 16-byte vectors, with the same 128-bit
-// non-temporal accesses as the row kernels and no reduction -- so its
-// bandwidth is the practical ceiling of that access mix on the device, which
-// the benchmark reports beside the 8 TB/s nominal peak.
+// The fused forward reads two streams and writes two; the backwards read two
+// or three and write one.  These kernels do only the streaming -- no
+// reduction, one or two integer ops per 16-byte vector -- so their bandwidth
+// is the practical ceiling of each access mix on the device, against which
+// the row kernels are judged.  The matrix covers:
+//   * the access mix: 1 or 2 read-only streams, 1 or 2 write-only streams,
+//     1R1W, 2R1W, 2R2W (the fused forward), 3R1W (the fused backward);
+//   * the launch shape: threads per block and 16-byte vectors per lane, one
+//     block per chunk (as the row kernels launch), so a block reads its
+//     whole chunk and then writes it (the read/write phase granularity);
+//   * the cache policy of loads and stores (buffer instructions with the
+//     sc0, sc1 and nt bits set per variant);
+//   * loads through LDS (global_load_lds_dwordx4: the data goes straight to
+//     LDS, so a lane keeps more bytes in flight without holding registers);
+//   * a persistent grid whose blocks issue the next chunk's loads before the
+//     current chunk's stores (software pipelining);
+//   * persistent grids with a fixed share of chunks per block, against ones
+//     whose blocks take chunks from a work counter;
+//   * in-place outputs (the host passes the input buffers as outputs).
 //
-//   int addrms_probe_stream_2r2w(const void *a, const void *b, void *c, void *d,
-//                                size_t bytes_each, int shape, void *stream);
-//   bytes_each: size of each of the four device buffers, a multiple of 16.
-//   shape: 0 = 256-thread blocks, 4 vectors a lane per stream (16 KiB per
-//   block and stream); 1 = 512-thread blocks, 2 vectors a lane (the same
-//   bytes per block with 8 waves, the row kernels' shape).  Of the shapes
-//   swept on MI355X these two stream fastest (6.1-6.3 TB/s); the benchmark
-//   reports the better one.
-//   Returns the hipError_t of the launch (0 on success).
+//   int   addrms_probe_count(void);
+//   const char *addrms_probe_name(int id);          static string
+//   int   addrms_probe_streams(int id, int *nin, int *nout, int *needs_counter);
+//   int   addrms_probe_run(int id, const void *const *in, void *const *out,
+//                          size_t bytes_each, unsigned *counter, void *stream);
+//     in: nin device buffers of bytes_each bytes (read); out: nout device
+//     buffers of bytes_each bytes (written); a read-only probe takes one
+//     output buffer of at least 16 bytes as a sink, written only if the data
+//     xor to an impossible value.  bytes_each: a multiple of 16, below 4 GiB.
+//     counter: a device word that is zero at launch, for the probes that take
+//     chunks from a work counter (needs_counter); ignored by the others.
+//     Returns the hipError_t of the launch (0 on success), or
+//     hipErrorInvalidValue for bad arguments.
 #include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
 
 #include "device.hpp"
 
@@ -24,51 +45,359 @@ namespace {
 
 using addrms::u32x4;
 
-template <int B, int kUnroll>
-__global__ void __launch_bounds__(B)
-stream_2r2w_kernel(const u32x4 *a, const u32x4 *b, u32x4 *c, u32x4 *d, size_t n)
+struct PArgs {
+    const u32x4 *in[3];
+    u32x4 *out[2];
+    size_t n; // 16-byte vectors per stream
+};
+
+// Cache-policy bits of the buffer instructions (the aux operand): 1 = sc0,
+// 2 = nt, 16 = sc1.  Policy -1 selects the global instructions the row
+// kernels use, non-temporal (global_load/store_dwordx4 ... nt).
+constexpr int kGlobalNt = -1;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, size_t n)
 {
-    const size_t stride = (size_t)gridDim.x * B * kUnroll;
-    for (size_t base = (size_t)blockIdx.x * B * kUnroll + threadIdx.x; base < n; base += stride) {
-        u32x4 va[kUnroll], vb[kUnroll];
+    // raw buffer, no stride; 0x00020000: 32-bit data format, the value used
+    // for untyped buffer access on gfx9-family parts
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)(n * 16), 0x00020000);
+}
+
+template <int POL>
+__device__ __forceinline__ u32x4 ld(const u32x4 *base, size_t n, size_t i)
+{
+    if constexpr (POL == kGlobalNt) {
+        return __builtin_nontemporal_load(base + i);
+    } else {
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base, n), (int)(i * 16), 0, POL);
+    }
+}
+
+template <int POL>
+__device__ __forceinline__ void st(u32x4 *base, size_t n, size_t i, const u32x4 &v)
+{
+    if constexpr (POL == kGlobalNt) {
+        __builtin_nontemporal_store(v, base + i);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base, n), (int)(i * 16), 0, POL);
+    }
+}
+
+// Output w of the values read: the sum and the xor of the inputs (a write-only
+// probe writes the vector index).
+template <int NR>
+__device__ __forceinline__ u32x4 out_val(const u32x4 (&v)[NR > 0 ? NR : 1], int w, size_t i)
+{
+    if constexpr (NR == 0) {
+        const unsigned k = (unsigned)i;
+        return u32x4{k, k ^ 1u, k ^ 2u, k ^ 3u} + (unsigned)w;
+    } else {
+        u32x4 s = v[0], x = v[0];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const size_t i = base + (size_t)u * B;
-            if (i < n) {
-                va[u] = addrms::ld_stream<3>(a + i);
-                vb[u] = addrms::ld_stream<3>(b + i);
-            }
+        for (int r = 1; r < NR; ++r) {
+            s += v[r];
+            x ^= v[r];
         }
+        return w == 0 ? s : x;
+    }
+}
+
+// One block per chunk of B * U vectors of each stream: every load of the
+// chunk, then every store.
+template <int NR, int NW, int B, int U, int LP, int SP>
+__global__ void __launch_bounds__(B) mix_kernel(PArgs a, unsigned *)
+{
+    const size_t base = (size_t)blockIdx.x * B * U + threadIdx.x;
+    u32x4 v[U][NR > 0 ? NR : 1];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
+        const size_t i = base + (size_t)u * B;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            v[u][r] = i < a.n ? ld<LP>(a.in[r], a.n, i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (NW == 0) {
+        u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                acc ^= v[u][r];
+        // inputs hold small values, so the top bits of the xor are clear
+        if ((acc[0] & acc[1] & acc[2] & acc[3]) == 0xFFFFFFFFu)
+            a.out[0][0] = acc;
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             const size_t i = base + (size_t)u * B;
-            if (i < n) {
-                addrms::st_stream<3>(c + i, va[u] + vb[u]);
-                addrms::st_stream<3>(d + i, va[u] ^ vb[u]);
+            if (i < a.n) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    st<SP>(a.out[w], a.n, i, out_val<NR>(v[u], w, i));
             }
         }
     }
 }
 
+// 2R2W with the loads going straight to LDS (global_load_lds_dwordx4, nt):
+// a wave's 64 lanes fill 1 KiB of LDS per instruction, lane l at byte 16*l of
+// the wave's region; after every load of the chunk has landed, each lane
+// reads its own vectors back and stores them.
 template <int B, int U>
-hipError_t launch_probe(const void *a, const void *b, void *c, void *d, size_t n, hipStream_t s)
+__global__ void __launch_bounds__(B) lds_kernel(PArgs a, unsigned *)
 {
-    const size_t blocks = (n + B * U - 1) / (B * U);
-    const unsigned grid = (unsigned)(blocks < 0x7fffffffu ? (blocks ? blocks : 1) : 0x7fffffffu);
-    hipLaunchKernelGGL((stream_2r2w_kernel<B, U>), dim3(grid), dim3(B), 0, s,
-                       static_cast<const u32x4 *>(a), static_cast<const u32x4 *>(b),
-                       static_cast<u32x4 *>(c), static_cast<u32x4 *>(d), n);
-    return hipGetLastError();
+    __shared__ u32x4 buf[2][U][B];
+    const int wbase = threadIdx.x & ~63;
+    const size_t base = (size_t)blockIdx.x * B * U + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t i = base + (size_t)u * B;
+        if (i < a.n) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(a.in[r] + i),
+                    (__attribute__((address_space(3))) void *)&buf[r][u][wbase], 16, 0, 2);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t i = base + (size_t)u * B;
+        if (i < a.n) {
+            const u32x4 x = buf[0][u][threadIdx.x], y = buf[1][u][threadIdx.x];
+            __builtin_nontemporal_store(x + y, a.out[0] + i);
+            __builtin_nontemporal_store(x ^ y, a.out[1] + i);
+        }
+    }
 }
+
+// 2R2W on a persistent grid: a block walks chunks of B * U vectors with a
+// grid stride and issues the next chunk's loads before the current chunk's
+// stores, so reads stay in flight while it writes.
+template <int B, int U>
+__global__ void __launch_bounds__(B) pipe_kernel(PArgs a, unsigned *)
+{
+    const size_t chunk = (size_t)B * U;
+    const size_t nchunks = (a.n + chunk - 1) / chunk;
+    u32x4 cur[U][2], nxt[U][2];
+    auto load = [&](size_t c, u32x4 (&v)[U][2]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = c * chunk + threadIdx.x + (size_t)u * B;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                v[u][r] = i < a.n ? __builtin_nontemporal_load(a.in[r] + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    size_t c = blockIdx.x;
+    if (c < nchunks)
+        load(c, cur);
+    for (; c < nchunks; c += gridDim.x) {
+        if (c + gridDim.x < nchunks)
+            load(c + gridDim.x, nxt);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = c * chunk + threadIdx.x + (size_t)u * B;
+            if (i < a.n) {
+                __builtin_nontemporal_store(cur[u][0] + cur[u][1], a.out[0] + i);
+                __builtin_nontemporal_store(cur[u][0] ^ cur[u][1], a.out[1] + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            cur[u][0] = nxt[u][0];
+            cur[u][1] = nxt[u][1];
+        }
+    }
+}
+
+// NR reads and NW writes on a persistent grid (as many blocks as fit at once),
+// a chunk of B * U vectors per step.  QUEUE = false: block b takes chunks b,
+// b + grid, b + 2 grid, ... (a fixed share, as the backward's persistent grid
+// does).  QUEUE = true: each step's chunk is the next ticket of a global
+// counter (a vector-memory atomic; *ctr is zero at launch), so blocks on
+// faster CUs take more chunks, as the hardware dispatcher balances a grid of
+// one block per chunk.  Every block leaves once the tickets pass the chunk
+// count.
+template <int NR, int NW, int B, int U, bool QUEUE>
+__global__ void __launch_bounds__(B) pers_kernel(PArgs a, unsigned *ctr)
+{
+    __shared__ unsigned ticket;
+    const size_t chunk = (size_t)B * U;
+    const size_t nchunks = (a.n + chunk - 1) / chunk;
+    size_t c = blockIdx.x;
+    for (;;) {
+        if constexpr (QUEUE) {
+            if (threadIdx.x == 0)
+                ticket = atomicAdd(ctr, 1u);
+            __syncthreads();
+            c = ticket;
+            __syncthreads(); // every lane has read the ticket before the next is written
+        }
+        if (c >= nchunks)
+            break;
+        u32x4 v[U][NR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = c * chunk + threadIdx.x + (size_t)u * B;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                v[u][r] = i < a.n ? __builtin_nontemporal_load(a.in[r] + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = c * chunk + threadIdx.x + (size_t)u * B;
+            if (i < a.n) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    __builtin_nontemporal_store(out_val<NR>(v[u], w, i), a.out[w] + i);
+            }
+        }
+        if constexpr (!QUEUE)
+            c += gridDim.x;
+    }
+}
+
+struct Probe {
+    const char *name;
+    const void *fn;
+    int block;
+    int per_block; // vectors of each stream per block (chunk)
+    int nin, nout;
+    bool persistent;
+    bool queue; // needs a zeroed counter
+};
+
+#define MIX(NR, NW, B, U, LP, SP, NAME) \
+    Probe{NAME, reinterpret_cast<const void *>(&mix_kernel<NR, NW, B, U, LP, SP>), B, B * U, NR, NW, false, false}
+#define PERS(NR, NW, B, U, Q, NAME) \
+    Probe{NAME, reinterpret_cast<const void *>(&pers_kernel<NR, NW, B, U, Q>), B, B * U, NR, NW, true, Q}
+
+constexpr int G = kGlobalNt;
+
+const Probe kProbes[] = {
+    // access mix, global nt loads and stores, the two shapes the row kernels use
+    MIX(1, 0, 256, 4, G, G, "r1_b256_u4"),
+    MIX(1, 0, 512, 2, G, G, "r1_b512_u2"),
+    MIX(2, 0, 256, 4, G, G, "r2_b256_u4"),
+    MIX(2, 0, 512, 2, G, G, "r2_b512_u2"),
+    MIX(0, 1, 256, 4, G, G, "w1_b256_u4"),
+    MIX(0, 1, 512, 2, G, G, "w1_b512_u2"),
+    MIX(0, 2, 256, 4, G, G, "w2_b256_u4"),
+    MIX(0, 2, 512, 2, G, G, "w2_b512_u2"),
+    MIX(1, 1, 256, 4, G, G, "r1w1_b256_u4"),
+    MIX(1, 1, 512, 2, G, G, "r1w1_b512_u2"),
+    MIX(2, 1, 256, 4, G, G, "r2w1_b256_u4"),
+    MIX(2, 1, 512, 2, G, G, "r2w1_b512_u2"),
+    MIX(2, 2, 256, 4, G, G, "r2w2_b256_u4"),
+    MIX(2, 2, 512, 2, G, G, "r2w2_b512_u2"),
+    MIX(3, 1, 256, 4, G, G, "r3w1_b256_u4"),
+    MIX(3, 1, 512, 2, G, G, "r3w1_b512_u2"),
+    // 2R2W read/write phase granularity: vectors a lane loads before storing
+    MIX(2, 2, 256, 1, G, G, "r2w2_b256_u1"),
+    MIX(2, 2, 256, 2, G, G, "r2w2_b256_u2"),
+    MIX(2, 2, 256, 8, G, G, "r2w2_b256_u8"),
+    MIX(2, 2, 512, 1, G, G, "r2w2_b512_u1"),
+    MIX(2, 2, 512, 4, G, G, "r2w2_b512_u4"),
+    MIX(2, 2, 1024, 1, G, G, "r2w2_b1024_u1"),
+    MIX(2, 2, 1024, 2, G, G, "r2w2_b1024_u2"),
+    // 2R2W cache policy (buffer instructions): loads nt; stores none, sc0,
+    // sc1, nt, sc0|nt, sc1|nt, sc0|sc1|nt
+    MIX(2, 2, 512, 2, 2, 0, "r2w2_b512_u2_ld-nt_st-none"),
+    MIX(2, 2, 512, 2, 2, 1, "r2w2_b512_u2_ld-nt_st-sc0"),
+    MIX(2, 2, 512, 2, 2, 16, "r2w2_b512_u2_ld-nt_st-sc1"),
+    MIX(2, 2, 512, 2, 2, 2, "r2w2_b512_u2_ld-nt_st-nt"),
+    MIX(2, 2, 512, 2, 2, 3, "r2w2_b512_u2_ld-nt_st-sc0nt"),
+    MIX(2, 2, 512, 2, 2, 18, "r2w2_b512_u2_ld-nt_st-sc1nt"),
+    MIX(2, 2, 512, 2, 2, 19, "r2w2_b512_u2_ld-nt_st-sc0sc1nt"),
+    MIX(2, 2, 512, 2, 0, 2, "r2w2_b512_u2_ld-none_st-nt"),
+    MIX(2, 2, 512, 2, 16, 2, "r2w2_b512_u2_ld-sc1_st-nt"),
+    // write-only cache policy
+    MIX(0, 2, 512, 2, G, 0, "w2_b512_u2_st-none"),
+    MIX(0, 2, 512, 2, G, 16, "w2_b512_u2_st-sc1"),
+    MIX(0, 2, 512, 2, G, 18, "w2_b512_u2_st-sc1nt"),
+    MIX(0, 2, 512, 2, G, 19, "w2_b512_u2_st-sc0sc1nt"),
+    // 2R2W with loads through LDS
+    Probe{"r2w2_lds_b256_u4", reinterpret_cast<const void *>(&lds_kernel<256, 4>), 256, 1024, 2, 2, false, false},
+    Probe{"r2w2_lds_b256_u8", reinterpret_cast<const void *>(&lds_kernel<256, 8>), 256, 2048, 2, 2, false, false},
+    Probe{"r2w2_lds_b512_u2", reinterpret_cast<const void *>(&lds_kernel<512, 2>), 512, 1024, 2, 2, false, false},
+    Probe{"r2w2_lds_b512_u4", reinterpret_cast<const void *>(&lds_kernel<512, 4>), 512, 2048, 2, 2, false, false},
+    // 2R2W, persistent, next chunk's loads before the current chunk's stores
+    Probe{"r2w2_pipe_b256_u2", reinterpret_cast<const void *>(&pipe_kernel<256, 2>), 256, 512, 2, 2, true, false},
+    Probe{"r2w2_pipe_b256_u4", reinterpret_cast<const void *>(&pipe_kernel<256, 4>), 256, 1024, 2, 2, true, false},
+    Probe{"r2w2_pipe_b512_u2", reinterpret_cast<const void *>(&pipe_kernel<512, 2>), 512, 1024, 2, 2, true, false},
+    // persistent grids: a fixed share of chunks per block, or chunks taken
+    // from a work counter (the backwards' mixes and the forward's)
+    PERS(2, 1, 256, 4, false, "r2w1_pers_b256_u4"),
+    PERS(2, 1, 256, 4, true, "r2w1_queue_b256_u4"),
+    PERS(2, 1, 512, 2, false, "r2w1_pers_b512_u2"),
+    PERS(2, 1, 512, 2, true, "r2w1_queue_b512_u2"),
+    PERS(2, 2, 512, 2, false, "r2w2_pers_b512_u2"),
+    PERS(2, 2, 512, 2, true, "r2w2_queue_b512_u2"),
+    PERS(3, 1, 512, 2, false, "r3w1_pers_b512_u2"),
+    PERS(3, 1, 512, 2, true, "r3w1_queue_b512_u2"),
+};
+constexpr int kNumProbes = (int)(sizeof(kProbes) / sizeof(kProbes[0]));
 
 } // namespace
 
-extern "C" int addrms_probe_stream_2r2w(const void *a, const void *b, void *c, void *d,
-                                        size_t bytes_each, int shape, void *stream)
+extern "C" {
+
+int addrms_probe_count(void) { return kNumProbes; }
+
+const char *addrms_probe_name(int id) { return id >= 0 && id < kNumProbes ? kProbes[id].name : ""; }
+
+int addrms_probe_streams(int id, int *nin, int *nout, int *needs_counter)
 {
-    if (!a || !b || !c || !d || bytes_each % 16 != 0 || shape < 0 || shape > 1)
+    if (id < 0 || id >= kNumProbes || !nin || !nout || !needs_counter)
         return (int)hipErrorInvalidValue;
-    const size_t n = bytes_each / 16;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    return (int)(shape == 0 ? launch_probe<256, 4>(a, b, c, d, n, s) : launch_probe<512, 2>(a, b, c, d, n, s));
+    *nin = kProbes[id].nin;
+    *nout = kProbes[id].nout;
+    *needs_counter = kProbes[id].queue ? 1 : 0;
+    return 0;
 }
+
+int addrms_probe_run(int id, const void *const *in, void *const *out, size_t bytes_each,
+                     unsigned *counter, void *stream)
+{
+    if (id < 0 || id >= kNumProbes || bytes_each == 0 || bytes_each % 16 != 0 ||
+        bytes_each >= ((size_t)1 << 32))
+        return (int)hipErrorInvalidValue;
+    const Probe &p = kProbes[id];
+    if (p.queue && !counter)
+        return (int)hipErrorInvalidValue;
+    PArgs a{};
+    for (int r = 0; r < p.nin; ++r) {
+        if (!in || !in[r])
+            return (int)hipErrorInvalidValue;
+        a.in[r] = static_cast<const u32x4 *>(in[r]);
+    }
+    // a read-only probe writes at most one vector of its sink
+    const int nout = p.nout > 0 ? p.nout : 1;
+    for (int w = 0; w < nout; ++w) {
+        if (!out || !out[w])
+            return (int)hipErrorInvalidValue;
+        a.out[w] = static_cast<u32x4 *>(out[w]);
+    }
+    a.n = bytes_each / 16;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    size_t blocks = (a.n + p.per_block - 1) / p.per_block;
+    if (p.persistent) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, p.fn, p.block, 0);
+        if (e != hipSuccess)
+            return (int)e;
+        const size_t cap = (size_t)cus * (size_t)(per_cu > 0 ? per_cu : 1);
+        if (blocks > cap)
+            blocks = cap;
+    }
+    void *argv[] = {&a, &counter};
+    return (int)hipLaunchKernel(p.fn, dim3((unsigned)blocks), dim3(p.block), argv, 0, s);
+}
+
+} // extern "C"

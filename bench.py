@@ -113,42 +113,168 @@ def copy_ceiling(nbytes: int, steps: int = 20):
     return 2 * n * steps / ev / 1e9
 
 
-def stream_ceiling(nbytes: int, steps: int = 20):
-    """GB/s of the probe kernel that only streams two reads and two writes of
-    nbytes/4 each (libaddrms_probe.so): the practical ceiling of the fused
-    forward's access mix, measured in the same run.  The better of the
-    probe's two launch shapes, each timed twice."""
-    import ctypes
+def per_call(fn, calls: int, warmup: int = 5) -> dict:
+    """Device time of each of `calls` calls of fn(), from a pair of HIP events
+    recorded around each call on the current stream (where fn launches):
+    median, 10th and 90th percentile and mean, in microseconds."""
     import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+    def pct(q):
+        return us[min(len(us) - 1, int(round(q * (len(us) - 1))))]
+
+    return {"median_us": round(pct(0.5), 3), "p10_us": round(pct(0.1), 3),
+            "p90_us": round(pct(0.9), 3), "mean_us": round(sum(us) / len(us), 3), "calls": calls}
+
+
+def _probe_lib():
+    import ctypes
     path = os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms_probe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
-    lib.addrms_probe_stream_2r2w.restype = ctypes.c_int
-    lib.addrms_probe_stream_2r2w.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_int,
-                                                                      ctypes.c_void_p]
-    each = (nbytes // 4) // 16 * 16
-    sets = [[torch.empty(each, dtype=torch.uint8, device="cuda") for _ in range(4)]
-            for _ in range(2)]
-    for st in sets:
-        st[0].fill_(1)
-        st[1].fill_(2)
-    i = [0]
-    shape = [0]
+    vp = ctypes.c_void_p
+    lib.addrms_probe_count.restype = ctypes.c_int
+    lib.addrms_probe_name.restype = ctypes.c_char_p
+    lib.addrms_probe_name.argtypes = [ctypes.c_int]
+    lib.addrms_probe_streams.restype = ctypes.c_int
+    lib.addrms_probe_streams.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int)] * 3
+    lib.addrms_probe_run.restype = ctypes.c_int
+    lib.addrms_probe_run.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                     ctypes.c_size_t, vp, vp]
+    return lib
 
-    def step():
-        a, b, c, d = sets[i[0] & 1]
-        rc = lib.addrms_probe_stream_2r2w(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
-                                          each, shape[0], torch.cuda.current_stream().cuda_stream)
-        if rc != 0:
-            raise RuntimeError(f"stream probe failed: hipError {rc}")
+
+# 2R2W probes that also run in place (outputs = inputs)
+INPLACE_PROBES = {"r2w2_b256_u4", "r2w2_b512_u2", "r2w2_lds_b256_u4"}
+
+
+def probe_matrix(each_bytes: int, calls: int = 30, only=None, inplace: bool = True) -> dict:
+    """The stream probes of libaddrms_probe.so (pure streaming kernels; see
+    add_rmsnorm_amd/csrc/stream_probe.hip), each stream `each_bytes` long,
+    two buffer sets alternating so that no call reads what the previous one
+    left in the 256 MB last-level cache.  Per probe: GB/s over the bytes it
+    moves at the median, 10th and 90th percentile call time.  With `inplace`
+    the 2R2W probes also run with the inputs passed as the outputs.  `only`:
+    names to run (None: all)."""
+    import ctypes
+    import torch
+    lib = _probe_lib()
+    if lib is None:
+        return {}
+    vp = ctypes.c_void_p
+    each = each_bytes // 16 * 16
+    pool = [[torch.empty(each, dtype=torch.uint8, device="cuda") for _ in range(4)]
+            for _ in range(2)]
+    for st in pool:
+        for k, t in enumerate(st):
+            t.fill_(k + 1)
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    out = {}
+    for pid in range(lib.addrms_probe_count()):
+        name = lib.addrms_probe_name(pid).decode()
+        if only is not None and name not in only:
+            continue
+        nin, nout, needs_ctr = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        lib.addrms_probe_streams(pid, ctypes.byref(nin), ctypes.byref(nout), ctypes.byref(needs_ctr))
+        # work-counter probes: a fresh zeroed word for every call
+        ctrs = (torch.zeros(2 * (calls + 8), dtype=torch.int32, device="cuda")
+                if needs_ctr.value else None)
+        modes = [False] + ([True] if inplace and name in INPLACE_PROBES else [])
+        for ip in modes:
+            args = []
+            for st in pool:
+                ins = [st[k].data_ptr() for k in range(nin.value)]
+                if ip:
+                    outs = ins[:]
+                elif nout.value:
+                    outs = [st[nin.value + k].data_ptr() for k in range(nout.value)]
+                else:
+                    outs = [sink.data_ptr()]
+                args.append(((vp * 3)(*ins, *([None] * (3 - len(ins)))),
+                             (vp * 2)(*outs, *([None] * (2 - len(outs))))))
+            i = [0]
+            if ctrs is not None:
+                ctrs.zero_()
+
+            def step():
+                a_in, a_out = args[i[0] & 1]
+                ctr = ctrs[i[0]].data_ptr() if ctrs is not None else None
+                rc = lib.addrms_probe_run(pid, a_in, a_out, each, ctr,
+                                          torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"probe {name} failed: hipError {rc}")
+                i[0] += 1
+
+            t = per_call(step, calls, 3)
+            nb = (nin.value + nout.value) * each
+            key = name + ("_inplace" if ip else "")
+            out[key] = {"GBps": round(nb / t["median_us"] / 1e3, 1),
+                        "GBps_p10_call": round(nb / t["p90_us"] / 1e3, 1),
+                        "GBps_p90_call": round(nb / t["p10_us"] / 1e3, 1),
+                        "median_us": t["median_us"], "bytes": nb, "calls": calls}
+            log(f"probe {key}: {out[key]['GBps']} GB/s")
+    del pool
+    return out
+
+
+def fused_fwd_inplace_compare(calls: int) -> dict:
+    """The headline fused forward beside the probes: out of place (the
+    workload) and in place (y written over x, residual_out over r, the form
+    an inference engine's residual stream uses), same bytes and protocol."""
+    import torch
+    import add_rmsnorm_amd as ar
+    import synth
+    inp = synth.workload_inputs(WORKLOAD)
+    cfg = synth.WORKLOADS[WORKLOAD]
+    M, N, eps = cfg["M"], cfg["N"], cfg["eps"]
+    w = inp["w"].cuda()
+    sets = [(inp["x"].cuda(), inp["r"].cuda()) for _ in range(2)]
+    outs = [(torch.empty_like(x), torch.empty_like(x)) for x, _ in sets]
+    nb = 8 * M * N + 2 * N
+    res = {}
+    i = [0]
+
+    def oop():
+        (x, r), (y, ro) = sets[i[0] & 1], outs[i[0] & 1]
+        ar.add_rmsnorm_fwd(x, r, w, eps, y=y, residual_out=ro)
         i[0] += 1
 
-    best = 0.0
-    for shape[0] in (0, 1, 0, 1):
-        _, ev = timed(step, steps, 3)
-        best = max(best, 4 * each * steps / ev / 1e9)
-    return best
+    def inp_():
+        x, r = sets[i[0] & 1]
+        ar.add_rmsnorm_fwd(x, r, w, eps, y=x, residual_out=r)
+        i[0] += 1
+
+    for name, fn in (("kernel_fused_fwd", oop), ("kernel_fused_fwd_inplace", inp_)):
+        t = per_call(fn, calls, 3)
+        res[name] = {"GBps": round(nb / t["median_us"] / 1e3, 1),
+                     "GBps_p10_call": round(nb / t["p90_us"] / 1e3, 1),
+                     "GBps_p90_call": round(nb / t["p10_us"] / 1e3, 1),
+                     "median_us": t["median_us"], "bytes": nb, "calls": calls}
+        log(f"{name}: {res[name]['GBps']} GB/s")
+    return res
+
+
+def stream_ceiling(nbytes: int, calls: int = 30):
+    """GB/s of the probe kernels that only stream two reads and two writes of
+    nbytes/4 each (libaddrms_probe.so), in the two launch shapes the row
+    kernels use and 1024 x 1 (the fastest shapes of the probe matrix): the
+    practical ceiling of the fused forward's access mix, measured in the same
+    run.  The best median is reported."""
+    res = probe_matrix(nbytes // 4, calls, only={"r2w2_b256_u4", "r2w2_b512_u2", "r2w2_b1024_u1"},
+                       inplace=False)
+    return max((v["GBps"] for v in res.values()), default=None)
 
 
 def headline(steps: int, warmup: int):
@@ -316,6 +442,125 @@ def summarize_bwd(stats, fetch, write, f_scale: float, w_scale: float, commands:
     with open(BWD_TRAFFIC_FILE, "w") as f:
         f.write("\n".join(out))
     log(f"wrote {BWD_TRAFFIC_FILE}")
+
+
+PROBE_PROFILE = os.path.join(ROOT, "profiles", "stream_probes_16384x7168.md")
+PROBE_KERNELS = ("mix_kernel", "lds_kernel", "pipe_kernel", "pers_kernel", "fwd_vec_kernel")
+
+
+def _probe_streams(kernel_name: str):
+    """(reads, writes) of a probe kernel from its template arguments."""
+    import re
+    m = re.search(r"(?:mix|pers)_kernel<(\d+), (\d+)", kernel_name)
+    if m:
+        return int(m.group(1)), int(m.group(2))
+    return 2, 2  # lds_kernel, pipe_kernel and the fused forward
+
+
+def summarize_probes(timing_json: str, trace_dir: str, pmc_dirs: dict, commands: dict):
+    """Write profiles/stream_probes_16384x7168.md: for every stream probe (and
+    the fused forward beside them) the event-timed bandwidth and, from four
+    rocprofv3 counter passes, the bytes moved, the fraction of L2 (TCC)
+    cycles its requests to memory were stalled for lack of DRAM credits, the
+    average request latency and the L2 busy fraction; then the kernel-trace
+    durations and the figures they pin.  The counter runs list the entries
+    in dispatch order (bench.py --probe-matrix --probe-calls 4: 3 warm-up and
+    4 counted dispatches each); the counted dispatches are averaged."""
+    import csv
+    import glob
+    timing = json.load(open(timing_json))
+    tmatrix = timing["probe_matrix"]
+    each = timing["bytes_each_stream"]
+
+    def counters(d):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        disp = {}
+        for r in csv.DictReader(open(f)):
+            if any(k in r["Kernel_Name"] for k in PROBE_KERNELS):
+                disp.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = \
+                    float(r["Counter_Value"])
+        return [disp[k] for k in sorted(disp)]
+
+    log_text = open(pmc_dirs["fetch"] + ".log").read()
+    order = list(json.loads(next(ln for ln in log_text.splitlines()
+                                 if ln.startswith('{"probe_matrix"')))["probe_matrix"])
+    warm, calls = 3, 4
+    per = {n: {} for n in order}
+    for d in pmc_dirs.values():
+        seq = counters(d)
+        if len(seq) != len(order) * (warm + calls):
+            raise SystemExit(f"{d}: {len(seq)} dispatches, expected {len(order) * (warm + calls)}")
+        for i, n in enumerate(order):
+            grp = seq[i * (warm + calls) + warm:(i + 1) * (warm + calls)]
+            for c in grp[0]:
+                per[n][c] = sum(g[c] for g in grp) / len(grp)
+    # byte calibration: the one-stream read and write probes of known size
+    f_cal = each / (per["r1_b512_u2"]["FETCH_SIZE"] * 1024)
+    w_cal = each / (per["w1_b512_u2"]["WRITE_SIZE"] * 1024)
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    traced = [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+              for r in csv.DictReader(open(f)) if any(k in r["Name"] for k in PROBE_KERNELS)]
+
+    out = ["# Stream probes and the fused forward at the headline byte count (bf16 16384 x 7168)",
+           "",
+           "Pure streaming kernels (`add_rmsnorm_amd/csrc/stream_probe.hip`), each stream "
+           f"{each} bytes (a quarter of the fused forward's 939,538,432), and the fused "
+           "forward itself (`kernel_fused_fwd`, in place: `..._inplace`), on one MI355X.",
+           "", "Commands (from the repository root):", ""]
+    out += [f"    {commands[k]}" for k in ("timing", "trace", "fetch", "write", "level", "busy")
+            if k in commands]
+    out += ["",
+            f"Byte calibration: FETCH_SIZE x {f_cal:.4f} and WRITE_SIZE x {w_cal:.4f} (the "
+            "one-stream read and write probes of known size). Stall columns: cycles the L2's "
+            "read or write requests to memory waited for DRAM credits, as a fraction of L2 "
+            "cycles (TCC_EA0_RDREQ/WRREQ_DRAM_CREDIT_STALL_sum / TCC_CYCLE_sum). Latency: "
+            "average L2 cycles a request is in flight (TCC_EA0_*REQ_LEVEL_sum / "
+            "TCC_EA0_*REQ_sum). Busy: TCC_BUSY_sum / TCC_CYCLE_sum.", "",
+            "| entry | GB/s, event median | read, write bytes / stream | write stall | "
+            "read stall | read latency | write latency | L2 busy |",
+            "|---|---|---|---|---|---|---|---|"]
+    for n in order:
+        c = per[n]
+        cyc = c.get("TCC_CYCLE_sum") or 1.0
+        rl = c["TCC_EA0_RDREQ_LEVEL_sum"] / max(c["TCC_EA0_RDREQ_sum"], 1.0)
+        wl = c["TCC_EA0_WRREQ_LEVEL_sum"] / max(c["TCC_EA0_WRREQ_sum"], 1.0)
+        out.append(f"| `{n}` | {tmatrix[n]['GBps']:.0f} | "
+                   f"{c['FETCH_SIZE'] * 1024 * f_cal / each:.2f}, "
+                   f"{c['WRITE_SIZE'] * 1024 * w_cal / each:.2f} | "
+                   f"{100 * c['TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum'] / cyc:.1f} % | "
+                   f"{100 * c['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / cyc:.1f} % | "
+                   f"{rl:.0f} | {wl:.0f} | {100 * c['TCC_BUSY_sum'] / cyc:.0f} % |")
+    out += ["", "Kernel-trace durations (an in-place entry shares its kernel with the "
+            "out-of-place one and is averaged in):", "",
+            "| kernel | calls | avg us | GB/s |", "|---|---|---|---|"]
+    rates = {}
+    for name, n_calls, us in sorted(traced):
+        rd, wr = _probe_streams(name)
+        gbps = (rd + wr) * each / us / 1e3
+        rates[name] = (rd, wr, gbps, us)
+        short = name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+        out.append(f"| `{short}` | {n_calls} | {us:.2f} | {gbps:.0f} |")
+    best = lambda rd, wr: max((v[2] for k, v in rates.items()
+                               if v[0] == rd and v[1] == wr and "fwd_vec" not in k), default=0.0)
+    r2, w2 = best(2, 0), best(0, 2)
+    bound = 2.0 / (1.0 / r2 + 1.0 / w2)
+    fused = next((v for k, v in rates.items() if HEADLINE_KERNEL in k), None)
+    out += ["", "Figures these traces pin (GB/s over the bytes each kernel moves):", "",
+            f"- read-only, one stream / two streams, best shape: {best(1, 0):.0f} / {r2:.0f}",
+            f"- write-only, one stream / two streams, best shape: {best(0, 1):.0f} / {w2:.0f}",
+            f"- two reads and two writes if the reads ran at the two-stream read rate, the "
+            f"writes at the two-stream write rate, and never both at once "
+            f"(2 / (1/read + 1/write)): {bound:.0f}",
+            f"- 2 reads / 2 writes, best probe: {best(2, 2):.0f}",
+            f"- 2 reads / 1 write, best probe: {best(2, 1):.0f}; 3 reads / 1 write: "
+            f"{best(3, 1):.0f}"]
+    if fused:
+        out.append(f"- the fused forward: {fused[2]:.0f} ({fused[3]:.2f} us), "
+                   f"{100 * fused[2] / best(2, 2):.1f} % of the best 2R2W probe, "
+                   f"{100 * fused[2] / 8000:.1f} % of 8 TB/s")
+    with open(PROBE_PROFILE, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    log(f"wrote {PROBE_PROFILE}")
 
 
 def _cpu_model() -> str:
@@ -676,11 +921,27 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--with-rms-bwd", action="store_true",
                     help="with --only-headline: also time the RMS backward (for counter runs)")
+    ap.add_argument("--probe-matrix", action="store_true",
+                    help="time every stream probe over the headline's byte count, print one "
+                         "JSON line and exit")
+    ap.add_argument("--probe-calls", type=int, default=30)
+    ap.add_argument("--probe-only", default="",
+                    help="comma-separated probe names for --probe-matrix (default: all)")
+    ap.add_argument("--summarize-probes", nargs=2, metavar=("TIMING_JSON", "OUT_DIR"),
+                    help="write the probe profile summary from the timing JSON and the "
+                         "trace_probes and pmc_{fetch,write,level,busy} rocprofv3 runs under "
+                         "OUT_DIR, and exit")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output and exit")
     ap.add_argument("--profile-commands", default="{}",
                     help="JSON {trace, fetch, write}: the commands that made the CSVs")
     args = ap.parse_args()
+    if args.summarize_probes:
+        tj, d = args.summarize_probes
+        summarize_probes(tj, os.path.join(d, "trace_probes"),
+                         {k: os.path.join(d, f"pmc_{k}") for k in ("fetch", "write", "level", "busy")},
+                         json.loads(args.profile_commands))
+        return
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, commands=json.loads(args.profile_commands))
         return
@@ -694,6 +955,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.probe_matrix:
+        each = (8 * 16384 * 7168) // 4
+        only = set(args.probe_only.split(",")) if args.probe_only else None
+        res = probe_matrix(each, args.probe_calls, only=only)
+        if not args.probe_only:
+            res.update(fused_fwd_inplace_compare(args.probe_calls))
+        print(json.dumps({"probe_matrix": res, "bytes_each_stream": each,
+                          "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
 
     h = headline(args.steps, args.warmup)
     M, N, nb = h["M"], h["N"], h["nbytes"]
