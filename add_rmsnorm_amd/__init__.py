@@ -29,7 +29,7 @@ __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
            "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "rmsnorm_fwd_fp8",
            "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_mxfp4", "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
-           "AddRmsError", "LIB_PATH", "lib"]
+           "AddRmsError", "LIB_PATH", "lib", "KNOBS", "set_knob", "tuning"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -95,11 +95,49 @@ def _load():
     lib.addrms_status_str.argtypes = [i32]
     lib.addrms_last_hip_error.restype = i32
     lib.addrms_last_hip_error.argtypes = []
+    lib.addrms_tune.restype = i32
+    lib.addrms_tune.argtypes = [i32, i32]
     return lib
 
 
 _lib = _load()
 lib = _lib
+
+
+# Tuning knobs of the library's dispatcher (ADDRMS_KNOB_* in addrms.h).
+KNOBS = {"FWD_WPR": 0, "FWD_VPL": 1, "BWD_WPR": 2, "BWD_WIDE": 3, "BWD_PREFETCH": 4,
+         "FORCE_ELEM": 5, "MAX_PARTIALS": 6, "BLOCKS_PER_CU": 7, "ROPE_BLOCKS_PER_CU": 8,
+         "ROPE_HPL": 9}
+
+
+def set_knob(name: str, value: int) -> int:
+    """Set a tuning knob of the library (0: the default choice) for the whole
+    process and return its previous value."""
+    k = KNOBS.get(name.upper().removeprefix("ADDRMS_"))
+    if k is None:
+        raise KeyError(f"unknown tuning knob {name!r}; known: {sorted(KNOBS)}")
+    prev = _lib.addrms_tune(k, int(value))
+    if prev < 0:
+        raise AddRmsError(prev, "addrms_tune")
+    return prev
+
+
+class tuning:
+    """Context manager: `with tuning(BWD_WPR=2, BWD_WIDE=1): ...` sets the
+    knobs for its body and restores their previous values after."""
+
+    def __init__(self, **knobs):
+        self.knobs = knobs
+        self.prev = {}
+
+    def __enter__(self):
+        for name, v in self.knobs.items():
+            self.prev[name] = set_knob(name, v)
+        return self
+
+    def __exit__(self, *exc):
+        for name, v in self.prev.items():
+            set_knob(name, v)
 
 
 def _code(t: torch.Tensor, what: str) -> int:
@@ -220,7 +258,13 @@ _ws_cache: dict = {}
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     """A per-device scratch buffer, grown on demand and reused across calls on
-    the current stream (calls on other streams must pass their own)."""
+    the current stream (calls on other streams must pass their own).  Under
+    graph capture every call gets its own buffer from the capture's memory
+    pool instead: a replay then writes only memory the graph owns, and the
+    cache is left alone (replacing a cached buffer would free memory that a
+    captured graph still writes)."""
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     key = (device.index, _stream(device.index))
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:

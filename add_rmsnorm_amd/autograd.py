@@ -33,6 +33,13 @@ __all__ = ["rms_norm", "add_rms_norm", "layer_norm", "add_layer_norm", "rms_norm
 
 
 # ---- forward / backward ops -------------------------------------------------
+# The ops take inputs of any strides (they run on contiguous copies) and
+# return contiguous outputs; the fake implementations say the same.
+
+def _like(t: Tensor, dtype=None) -> Tensor:
+    """An empty contiguous tensor of t's shape (and dtype unless given)."""
+    return torch.empty(t.shape, dtype=dtype or t.dtype, device=t.device)
+
 
 @torch.library.custom_op("addrms::rms_norm_fwd", mutates_args=())
 def _rms_norm_fwd(x: Tensor, w: Tensor, eps: float) -> Tuple[Tensor, Tensor]:
@@ -41,17 +48,17 @@ def _rms_norm_fwd(x: Tensor, w: Tensor, eps: float) -> Tuple[Tensor, Tensor]:
 
 @_rms_norm_fwd.register_fake
 def _(x, w, eps):
-    return torch.empty_like(x), x.new_empty(x.shape[:-1], dtype=torch.float32)
+    return _like(x), x.new_empty(x.shape[:-1], dtype=torch.float32)
 
 
 @torch.library.custom_op("addrms::rms_norm_bwd", mutates_args=())
 def _rms_norm_bwd(dy: Tensor, x: Tensor, w: Tensor, rstd: Tensor) -> Tuple[Tensor, Tensor]:
-    return rmsnorm_bwd(dy.contiguous(), x, w, rstd)
+    return rmsnorm_bwd(dy.contiguous(), x.contiguous(), w.contiguous(), rstd.contiguous())
 
 
 @_rms_norm_bwd.register_fake
 def _(dy, x, w, rstd):
-    return torch.empty_like(x), w.new_empty(w.shape, dtype=torch.float32)
+    return _like(x), w.new_empty(w.shape, dtype=torch.float32)
 
 
 @torch.library.custom_op("addrms::add_rms_norm_fwd", mutates_args=())
@@ -61,20 +68,19 @@ def _add_rms_norm_fwd(x: Tensor, r: Tensor, w: Tensor, eps: float) -> Tuple[Tens
 
 @_add_rms_norm_fwd.register_fake
 def _(x, r, w, eps):
-    return (torch.empty_like(x), torch.empty_like(x),
-            x.new_empty(x.shape[:-1], dtype=torch.float32))
+    return _like(x), _like(x), x.new_empty(x.shape[:-1], dtype=torch.float32)
 
 
 @torch.library.custom_op("addrms::add_rms_norm_bwd", mutates_args=())
 def _add_rms_norm_bwd(dy: Tensor, dres: Optional[Tensor], h: Tensor, w: Tensor,
                       rstd: Tensor) -> Tuple[Tensor, Tensor]:
-    return add_rmsnorm_bwd(dy.contiguous(), None if dres is None else dres.contiguous(), h, w,
-                           rstd)
+    return add_rmsnorm_bwd(dy.contiguous(), None if dres is None else dres.contiguous(),
+                           h.contiguous(), w.contiguous(), rstd.contiguous())
 
 
 @_add_rms_norm_bwd.register_fake
 def _(dy, dres, h, w, rstd):
-    return torch.empty_like(h), w.new_empty(w.shape, dtype=torch.float32)
+    return _like(h), w.new_empty(w.shape, dtype=torch.float32)
 
 
 # ---- autograd ----------------------------------------------------------------
@@ -89,7 +95,7 @@ def _rms_setup(ctx, inputs, output):
 def _rms_backward(ctx, dy, _drstd):
     x, w, rstd = ctx.saved_tensors
     if dy is None:
-        dy = torch.zeros_like(x)
+        dy = torch.zeros(x.shape, dtype=x.dtype, device=x.device)
     dx, dw = _rms_norm_bwd(dy, x, w, rstd)
     return dx, dw.to(w.dtype), None
 
@@ -107,7 +113,7 @@ def _add_setup(ctx, inputs, output):
 def _add_backward(ctx, dy, dres, _drstd):
     h, w, rstd = ctx.saved_tensors
     if dy is None:
-        dy = torch.zeros_like(h)
+        dy = torch.zeros(h.shape, dtype=h.dtype, device=h.device)
     dh, dw = _add_rms_norm_bwd(dy, dres, h, w, rstd)
     return dh, dh, dw.to(w.dtype), None
 
@@ -127,7 +133,7 @@ def _layer_norm_fwd(x: Tensor, w: Tensor, b: Optional[Tensor],
 @_layer_norm_fwd.register_fake
 def _(x, w, b, eps):
     st = x.new_empty(x.shape[:-1], dtype=torch.float32)
-    return torch.empty_like(x), st, torch.empty_like(st)
+    return _like(x), st, torch.empty_like(st)
 
 
 @torch.library.custom_op("addrms::add_layer_norm_fwd", mutates_args=())
@@ -140,31 +146,33 @@ def _add_layer_norm_fwd(x: Tensor, r: Tensor, w: Tensor, b: Optional[Tensor],
 @_add_layer_norm_fwd.register_fake
 def _(x, r, w, b, eps):
     st = x.new_empty(x.shape[:-1], dtype=torch.float32)
-    return torch.empty_like(x), torch.empty_like(x), st, torch.empty_like(st)
+    return _like(x), _like(x), st, torch.empty_like(st)
 
 
 @torch.library.custom_op("addrms::layer_norm_bwd", mutates_args=())
 def _layer_norm_bwd(dy: Tensor, x: Tensor, w: Tensor, mean: Tensor,
                     rstd: Tensor) -> Tuple[Tensor, Tensor, Tensor]:
-    return layernorm_bwd(dy.contiguous(), x, w, mean, rstd, with_db=True)
+    return layernorm_bwd(dy.contiguous(), x.contiguous(), w.contiguous(), mean.contiguous(),
+                         rstd.contiguous(), with_db=True)
 
 
 @_layer_norm_bwd.register_fake
 def _(dy, x, w, mean, rstd):
-    return (torch.empty_like(x), w.new_empty(w.shape, dtype=torch.float32),
+    return (_like(x), w.new_empty(w.shape, dtype=torch.float32),
             w.new_empty(w.shape, dtype=torch.float32))
 
 
 @torch.library.custom_op("addrms::add_layer_norm_bwd", mutates_args=())
 def _add_layer_norm_bwd(dy: Tensor, dres: Optional[Tensor], h: Tensor, w: Tensor, mean: Tensor,
                         rstd: Tensor) -> Tuple[Tensor, Tensor, Tensor]:
-    return add_layernorm_bwd(dy.contiguous(), None if dres is None else dres.contiguous(), h, w,
-                             mean, rstd, with_db=True)
+    return add_layernorm_bwd(dy.contiguous(), None if dres is None else dres.contiguous(),
+                             h.contiguous(), w.contiguous(), mean.contiguous(), rstd.contiguous(),
+                             with_db=True)
 
 
 @_add_layer_norm_bwd.register_fake
 def _(dy, dres, h, w, mean, rstd):
-    return (torch.empty_like(h), w.new_empty(w.shape, dtype=torch.float32),
+    return (_like(h), w.new_empty(w.shape, dtype=torch.float32),
             w.new_empty(w.shape, dtype=torch.float32))
 
 
@@ -179,7 +187,7 @@ def _ln_setup(ctx, inputs, output):
 def _ln_backward(ctx, dy, _dmean, _drstd):
     x, w, mean, rstd = ctx.saved_tensors
     if dy is None:
-        dy = torch.zeros_like(x)
+        dy = torch.zeros(x.shape, dtype=x.dtype, device=x.device)
     dx, dw, db = _layer_norm_bwd(dy, x, w, mean, rstd)
     return dx, dw.to(w.dtype), (db.to(w.dtype) if ctx.has_b else None), None
 
@@ -198,7 +206,7 @@ def _add_ln_setup(ctx, inputs, output):
 def _add_ln_backward(ctx, dy, dres, _dmean, _drstd):
     h, w, mean, rstd = ctx.saved_tensors
     if dy is None:
-        dy = torch.zeros_like(h)
+        dy = torch.zeros(h.shape, dtype=h.dtype, device=h.device)
     dh, dw, db = _add_layer_norm_bwd(dy, dres, h, w, mean, rstd)
     return dh, dh, dw.to(w.dtype), (db.to(w.dtype) if ctx.has_b else None), None
 
@@ -244,7 +252,7 @@ def _add_rms_norm_fp8(x: Tensor, r: Tensor, w: Tensor, eps: float,
 @_add_rms_norm_fp8.register_fake
 def _(x, r, w, eps, group):
     return (x.new_empty(x.shape, dtype=_FP8),
-            x.new_empty(_scale_shape(x, group), dtype=torch.float32), torch.empty_like(x))
+            x.new_empty(_scale_shape(x, group), dtype=torch.float32), _like(x))
 
 
 def _mx_shapes(x: Tensor):
@@ -272,7 +280,7 @@ def _add_rms_norm_mxfp4(x: Tensor, r: Tensor, w: Tensor, eps: float) -> Tuple[Te
 def _(x, r, w, eps):
     cs, ss = _mx_shapes(x)
     return (x.new_empty(cs, dtype=torch.float4_e2m1fn_x2),
-            x.new_empty(ss, dtype=torch.float8_e8m0fnu), torch.empty_like(x))
+            x.new_empty(ss, dtype=torch.float8_e8m0fnu), _like(x))
 
 
 @torch.library.custom_op("addrms::rms_norm_rope_qk", mutates_args=())

@@ -5,6 +5,7 @@
 // only state is a per-device cache of CU counts and kernel occupancies.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdlib>
@@ -81,13 +82,31 @@ size_t esize(int d) { return d == ADDRMS_F32 ? 4 : 2; }
 int vec_elems(int d) { return d == ADDRMS_F32 ? 4 : 8; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Integer knob from the environment (0 when unset or not a number).  Read on
-// every call so that tests can switch variants inside one process.
-int env_int(const char *name)
-{
-    const char *s = std::getenv(name);
-    return s ? std::atoi(s) : 0;
-}
+// Tuning knobs (ADDRMS_KNOB_* in addrms.h): 0 means the measured default.
+// Each starts from its environment variable, read once when the library is
+// loaded; addrms_tune changes it afterwards (tests use it to force every
+// variant through parity inside one process).
+const char *const kKnobEnv[ADDRMS_NUM_KNOBS] = {
+    "ADDRMS_FWD_WPR",      "ADDRMS_FWD_VPL",        "ADDRMS_BWD_WPR",
+    "ADDRMS_BWD_WIDE",     "ADDRMS_BWD_PREFETCH",   "ADDRMS_FORCE_ELEM",
+    "ADDRMS_MAX_PARTIALS", "ADDRMS_BLOCKS_PER_CU",  "ADDRMS_ROPE_BLOCKS_PER_CU",
+    "ADDRMS_ROPE_HPL",
+};
+
+struct Knobs {
+    std::atomic<int> v[ADDRMS_NUM_KNOBS];
+    Knobs()
+    {
+        for (int k = 0; k < ADDRMS_NUM_KNOBS; ++k) {
+            const char *s = std::getenv(kKnobEnv[k]);
+            const int x = s ? std::atoi(s) : 0;
+            v[k].store(x > 0 ? x : 0, std::memory_order_relaxed);
+        }
+    }
+};
+Knobs g_knobs; // constructed when the library is loaded
+
+int knob(int k) { return g_knobs.v[k].load(std::memory_order_relaxed); }
 
 // Byte range of a buffer.
 struct Span {
@@ -146,10 +165,10 @@ int device_cus(int dev, int *cus)
     return ADDRMS_OK;
 }
 
-// Resident blocks per CU of a kernel (ADDRMS_BLOCKS_PER_CU overrides).
+// Resident blocks per CU of a kernel (the BLOCKS_PER_CU knob overrides).
 int blocks_per_cu(int dev, const KernelRef &k, size_t smem, int *out)
 {
-    const int forced = env_int("ADDRMS_BLOCKS_PER_CU");
+    const int forced = knob(ADDRMS_KNOB_BLOCKS_PER_CU);
     if (forced > 0) {
         *out = forced;
         return ADDRMS_OK;
@@ -240,8 +259,8 @@ int vpl_index(int need)
 // variants of that mode.  ADDRMS_FWD_WPR forces a WPR when it is built.
 bool pick_fwd(int64_t M, int nvec, int cus, int qm, int *wi_out, int *vi_out)
 {
-    const int forced = env_int("ADDRMS_FWD_WPR");
-    const int env_vpl = env_int("ADDRMS_FWD_VPL");
+    const int forced = knob(ADDRMS_KNOB_FWD_WPR);
+    const int env_vpl = knob(ADDRMS_KNOB_FWD_VPL);
     const int target = env_vpl > 0 ? env_vpl : 2;
     auto need_of = [&](int wi) { return (nvec + 64 * kWprList[wi] - 1) / (64 * kWprList[wi]); };
     auto ok = [&](int wi) {
@@ -286,14 +305,14 @@ bool pick_fwd(int64_t M, int nvec, int cus, int qm, int *wi_out, int *vi_out)
 // LDS.  ADDRMS_BWD_WPR forces a WPR.
 bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_out, int *vi_out)
 {
-    const int forced = env_int("ADDRMS_BWD_WPR");
+    const int forced = knob(ADDRMS_KNOB_BWD_WPR);
     int best_wi = -1, best_vi = -1;
     // The fused RMS backward at 4 vectors a lane with 2 waves per row (385 to
     // 512 vectors) takes the next-row prefetch kernel rather than 1 wave per
     // row with 7 or 8 vectors: measured on MI355X, bf16, 24576 x 3584 120.8
     // against 127.9 us, 32768 x 4096 and 16384 x 4096 level or 0.8 % faster.
     if (forced == 0 && res && norm == kRms && (nvec + 127) / 128 == 4 && M * 2 >= 4LL * cus &&
-        env_int("ADDRMS_BWD_PREFETCH") != 2 && bwd_built(norm, res, 2, 4)) {
+        knob(ADDRMS_KNOB_BWD_PREFETCH) != 2 && bwd_built(norm, res, 2, 4)) {
         *wi_out = 1; // kWprList[1] == 2
         *vi_out = vpl_index(4);
         return true;
@@ -354,7 +373,7 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
 bool use_wide_bwd(const BwdTable &tab, int norm, bool res, int64_t M, int64_t N, int wi, int vi,
                   int cus)
 {
-    const int mode = env_int("ADDRMS_BWD_WIDE");
+    const int mode = knob(ADDRMS_KNOB_BWD_WIDE);
     if (mode == 2 || kWprList[wi] != kBwdWideWpr || tab.wide[norm][res ? 1 : 0][vi].fn == nullptr)
         return false;
     const int rpb = bwd_rpb(kBwdWideWpr, true);
@@ -376,7 +395,7 @@ bool use_wide_bwd(const BwdTable &tab, int norm, bool res, int64_t M, int64_t N,
 // ADDRMS_BWD_PREFETCH=2 never.
 bool use_prefetch_bwd(const BwdTable &tab, int norm, bool res, int wi, int vi)
 {
-    const int mode = env_int("ADDRMS_BWD_PREFETCH");
+    const int mode = knob(ADDRMS_KNOB_BWD_PREFETCH);
     if (mode == 2 || tab.pf[norm][res ? 1 : 0][wi][vi].fn == nullptr)
         return false;
     return mode == 1 || kVplList[vi] == 4;
@@ -487,7 +506,7 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     // codes per 16-byte vector: nv bytes (E4M3) or nv / 2 (MXFP4), stored as one word
     const bool y_ok = q8 ? (reinterpret_cast<uintptr_t>(q) % (uintptr_t)(mx ? nv / 2 : nv)) == 0
                          : aligned16(y);
-    const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(x) &&
+    const bool vec_ok = knob(ADDRMS_KNOB_FORCE_ELEM) == 0 && (N % nv) == 0 && aligned16(x) &&
                         aligned16(w) && y_ok && (!b || aligned16(b)) &&
                         (!fused || (aligned16(r) && aligned16(res))) &&
                         (qgroup == 0 || qlanes > 0);
@@ -505,7 +524,7 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
         // One block per row group (the hardware dispatcher balances the
         // tail); ADDRMS_BLOCKS_PER_CU > 0 selects a persistent grid instead.
         int grid = (int)(blocks < INT_MAX ? blocks : INT_MAX);
-        if (env_int("ADDRMS_BLOCKS_PER_CU") > 0 &&
+        if (knob(ADDRMS_KNOB_BLOCKS_PER_CU) > 0 &&
             (rc = persistent_grid(k, 0, blocks, INT_MAX, &grid)) != ADDRMS_OK)
             return rc;
         return launch(k, dim3(grid), 0, &a, s);
@@ -581,14 +600,14 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     const int64_t ws_rows = (int64_t)(workspace_bytes / ((size_t)N * 4u)) / (ln ? 2 : 1);
     // ADDRMS_MAX_PARTIALS raises the partial-row cap when the caller passes a
     // larger workspace (tuning); the size function assumes the default cap.
-    const int64_t cap = env_int("ADDRMS_MAX_PARTIALS") > 0 ? env_int("ADDRMS_MAX_PARTIALS") : kMaxPartials;
+    const int64_t cap = knob(ADDRMS_KNOB_MAX_PARTIALS) > 0 ? knob(ADDRMS_KNOB_MAX_PARTIALS) : kMaxPartials;
     const int64_t pmax = ws_rows < cap ? ws_rows : cap;
     float *ws = static_cast<float *>(workspace);
     BwdArgs a{dy, res ? dres : dy, x, w, mean, rstd, dx, ws, ln ? ws + (size_t)pmax * N : ws,
               M, (int)N, 0, 0, 0};
 
     const int nv = vec_elems(dtype);
-    const bool vec_ok = env_int("ADDRMS_FORCE_ELEM") == 0 && (N % nv) == 0 && aligned16(dy) &&
+    const bool vec_ok = knob(ADDRMS_KNOB_FORCE_ELEM) == 0 && (N % nv) == 0 && aligned16(dy) &&
                         aligned16(x) && aligned16(w) && aligned16(dx) && aligned16(workspace) &&
                         (!res || aligned16(dres)) && (!ln || (pmax * N) % 4 == 0);
     int cus = 0;
@@ -749,14 +768,14 @@ int rope_common(const void *q, const void *k, const void *wq, const void *wk, co
     auto al = [&](const void *p, int64_t H, int64_t st) {
         return H == 0 || (aligned16(p) && (st * es) % 16 == 0);
     };
-    const bool vec = env_int("ADDRMS_FORCE_ELEM") == 0 && lg >= 0 && al(q, Hq, q_stride) &&
+    const bool vec = knob(ADDRMS_KNOB_FORCE_ELEM) == 0 && lg >= 0 && al(q, Hq, q_stride) &&
                      al(qo, Hq, qo_stride) && al(k, Hk, k_stride) && al(ko, Hk, ko_stride) &&
                      (Hq == 0 || aligned16(wq)) && (Hk == 0 || aligned16(wk)) && aligned16(cos) &&
                      aligned16(sin);
     if (vec) {
         // heads per lane group and loop step: ADDRMS_ROPE_HPL = 1, 2 or 4
         // forces it; otherwise kRopeHpl
-        const int forced = env_int("ADDRMS_ROPE_HPL");
+        const int forced = knob(ADDRMS_KNOB_ROPE_HPL);
         int hpl = forced == 1 || forced == 2 || forced == 4 ? forced : kRopeHpl;
         if (!rope_built((int)G, hpl))
             hpl = 2;
@@ -765,7 +784,7 @@ int rope_common(const void *q, const void *k, const void *wq, const void *wk, co
         int64_t blocks = (total + step - 1) / step;
         // ADDRMS_ROPE_BLOCKS_PER_CU caps the grid at that many blocks per CU
         // (each block then loops over several steps)
-        const int bpc = env_int("ADDRMS_ROPE_BLOCKS_PER_CU");
+        const int bpc = knob(ADDRMS_KNOB_ROPE_BLOCKS_PER_CU);
         if (bpc > 0) {
             int cus = 0, rc;
             if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
@@ -1006,6 +1025,7 @@ const char *addrms_status_str(int status)
     case ADDRMS_ERR_ALIAS: return "output overlaps another argument";
     case ADDRMS_ERR_WORKSPACE: return "workspace missing or too small";
     case ADDRMS_ERR_HIP: return "HIP call failed";
+    case ADDRMS_ERR_KNOB: return "unknown tuning knob";
     case ADDRMS_ERR_SCRATCH:
         return "a row is wider than the no-allocation backward's built-in scratch holds";
     default: return "unknown status";
@@ -1013,5 +1033,14 @@ const char *addrms_status_str(int status)
 }
 
 int addrms_last_hip_error(void) { return g_last_hip_error; }
+
+int addrms_tune(int knob_id, int value)
+{
+    if (knob_id < 0 || knob_id >= ADDRMS_NUM_KNOBS)
+        return ADDRMS_ERR_KNOB;
+    if (value < 0)
+        return knob(knob_id);
+    return g_knobs.v[knob_id].exchange(value, std::memory_order_relaxed);
+}
 
 } // extern "C"

@@ -70,6 +70,7 @@ extern "C" {
 #define ADDRMS_ERR_WORKSPACE -6 /* workspace NULL or smaller than required */
 #define ADDRMS_ERR_HIP -7       /* a HIP call failed; see addrms_last_hip_error() */
 #define ADDRMS_ERR_SCRATCH -8   /* a row is wider than rmsnorm_bwd_noalloc's scratch holds */
+#define ADDRMS_ERR_KNOB -9      /* unknown tuning knob (addrms_tune) */
 
 /*
  * RMSNorm forward.
@@ -295,7 +296,6 @@ int add_layernorm_bwd(const void *dy, const void *dres, const void *h, const voi
                       void *workspace, size_t workspace_bytes, int64_t M, int64_t N, int dtype,
                       int w_dtype, void *stream);
 
-/* Static, human-readable name of a status code. */
 /*
  * Per-head RMSNorm followed by the rotary position embedding, for the query
  * and key heads of an attention layer, in one pass.  The "Machete" README
@@ -335,7 +335,48 @@ int rmsnorm_rope_qk(const void *q, const void *k, const void *wq, const void *wk
                     int64_t k_stride, int64_t q_out_stride, int64_t k_out_stride, float eps,
                     int interleaved, int dtype, int w_dtype, void *stream);
 
+/* Static, human-readable name of a status code. */
 const char *addrms_status_str(int status);
+
+/*
+ * Tuning knobs of the dispatcher: which kernel variant and grid a call uses.
+ * 0 means the measured default.  Every knob starts from the environment
+ * variable named beside it, read once when the library is loaded, and
+ * addrms_tune changes it for the whole process (all threads and devices)
+ * from then on.  Results do not depend on the knobs except dw's (and db's)
+ * summation order where they change the partial rows; a forced variant that
+ * is not built for a shape falls back to the default choice.
+ *   FWD_WPR            forward waves per row (1, 2, 4, 8, 16)      ADDRMS_FWD_WPR
+ *   FWD_VPL            forward target 16-byte vectors a lane       ADDRMS_FWD_VPL
+ *   BWD_WPR            backward waves per row (1, 2, 4, 8)         ADDRMS_BWD_WPR
+ *   BWD_WIDE           1: 1024-thread backward where built; 2: never   ADDRMS_BWD_WIDE
+ *   BWD_PREFETCH       1: next-row prefetch backward where built; 2: never
+ *                                                                  ADDRMS_BWD_PREFETCH
+ *   FORCE_ELEM         1: the element-wise kernels                 ADDRMS_FORCE_ELEM
+ *   MAX_PARTIALS       cap on dw partial rows (a larger workspace must be
+ *                      passed than the size functions give)        ADDRMS_MAX_PARTIALS
+ *   BLOCKS_PER_CU      persistent grid of this many blocks per CU (the
+ *                      forward: instead of one block per row group) ADDRMS_BLOCKS_PER_CU
+ *   ROPE_BLOCKS_PER_CU RMSNorm + RoPE grid cap, blocks per CU      ADDRMS_ROPE_BLOCKS_PER_CU
+ *   ROPE_HPL           RMSNorm + RoPE heads per lane group and step (1, 2, 4)
+ *                                                                  ADDRMS_ROPE_HPL
+ */
+#define ADDRMS_KNOB_FWD_WPR 0
+#define ADDRMS_KNOB_FWD_VPL 1
+#define ADDRMS_KNOB_BWD_WPR 2
+#define ADDRMS_KNOB_BWD_WIDE 3
+#define ADDRMS_KNOB_BWD_PREFETCH 4
+#define ADDRMS_KNOB_FORCE_ELEM 5
+#define ADDRMS_KNOB_MAX_PARTIALS 6
+#define ADDRMS_KNOB_BLOCKS_PER_CU 7
+#define ADDRMS_KNOB_ROPE_BLOCKS_PER_CU 8
+#define ADDRMS_KNOB_ROPE_HPL 9
+#define ADDRMS_NUM_KNOBS 10
+
+/* Set knob `knob` to `value` (>= 0) and return its previous value; with
+ * value < 0 only return the current value.  ADDRMS_ERR_KNOB for an unknown
+ * knob.  No HIP call.  Calls already enqueued are not affected. */
+int addrms_tune(int knob, int value);
 
 /* The hipError_t of the last ADDRMS_ERR_HIP returned on this thread (0 if none). */
 int addrms_last_hip_error(void);

@@ -23,3 +23,29 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+class _Knobs:
+    """Sets the library's tuning knobs (the ADDRMS_* names of addrms.h) for
+    one test and restores them afterwards."""
+
+    def __init__(self):
+        self.prev = {}
+
+    def setenv(self, name: str, value):
+        import add_rmsnorm_amd as ar
+        prev = ar.set_knob(name, int(value))
+        self.prev.setdefault(name, prev)
+
+    def restore(self):
+        import add_rmsnorm_amd as ar
+        for name, v in self.prev.items():
+            ar.set_knob(name, v)
+        self.prev.clear()
+
+
+@pytest.fixture
+def knobs():
+    k = _Knobs()
+    yield k
+    k.restore()

@@ -10,7 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "addrms.h")
-LIB = os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms.so")
+# another build of the library (e.g. one with host-side sanitizers) may be tested
+LIB = os.environ.get("ADDRMS_TEST_LIB") or os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms.so")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_EPS, E_ALIAS, E_WS, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -8
 F32, BF16 = 0, 1
@@ -63,7 +64,7 @@ def test_header_declares_the_entry_points():
                                   "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_fp8_grouped",
                                   "add_rmsnorm_fwd_fp8_grouped", "rmsnorm_fwd_mxfp4",
                                   "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
-                                  "addrms_status_str", "addrms_last_hip_error"])
+                                  "addrms_status_str", "addrms_last_hip_error", "addrms_tune"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -316,3 +317,19 @@ def test_noalloc_validation(lib):
     assert f(A, B, C, D, E, G, 4, 0, BF16, BF16, None) == E_SHAPE
     assert f(A, B, C, D, E, G, 1, (16 << 20) // 4 + 1, BF16, BF16, None) == E_SCRATCH
     assert f(A, B, C, D, E, G, 1, (16 << 20) // 4 + 8, F32, F32, None) == E_SCRATCH
+
+
+def test_tuning_knobs(lib):
+    """addrms_tune: set returns the previous value, a negative value only
+    reads, an unknown knob is ADDRMS_ERR_KNOB; no HIP call."""
+    f = lib.addrms_tune
+    f.argtypes = [ctypes.c_int, ctypes.c_int]
+    E_KNOB = -9
+    assert f(10, 1) == E_KNOB and f(-1, 0) == E_KNOB
+    for k in range(10):
+        prev = f(k, -1)
+        assert prev >= 0
+        assert f(k, prev + 3) == prev
+        assert f(k, -1) == prev + 3
+        assert f(k, prev) == prev + 3
+        assert f(k, -1) == prev

@@ -50,8 +50,8 @@ def test_rmsnorm_bwd_bf16_32768x4096():
                                           (torch.bfloat16, torch.float32),
                                           (torch.float32, torch.float32),
                                           (torch.float32, torch.bfloat16)])
-def test_forced_waves_per_row(monkeypatch, wpr, dtype, wdtype):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", str(wpr))
+def test_forced_waves_per_row(knobs, wpr, dtype, wdtype):
+    knobs.setenv("ADDRMS_BWD_WPR", str(wpr))
     for M, N in [(1000, 4096), (7, 1032), (3001, 256)]:
         inp = synth.rmsnorm_bwd_inputs(M, N, dtype, wdtype, seed=M + N)
         check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"wpr={wpr} {M}x{N}")
@@ -64,9 +64,9 @@ def test_forced_waves_per_row(monkeypatch, wpr, dtype, wdtype):
                                           (torch.bfloat16, torch.float32),
                                           (torch.float32, torch.float32),
                                           (torch.float32, torch.bfloat16)])
-def test_wide_variant_forced(monkeypatch, dtype, wdtype):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+def test_wide_variant_forced(knobs, dtype, wdtype):
+    knobs.setenv("ADDRMS_BWD_WPR", "2")
+    knobs.setenv("ADDRMS_BWD_WIDE", "1")
     cases = [(1000, 4096), (3001, 3072), (7, 1032), (2049, 520), (9000, 1536)] if dtype == torch.bfloat16 \
         else [(1000, 2048), (3001, 1536), (7, 516), (2049, 260), (9000, 768)]
     for M, N in cases:
@@ -82,19 +82,19 @@ def test_wide_variant_forced(monkeypatch, dtype, wdtype):
                                           (torch.bfloat16, torch.float32),
                                           (torch.float32, torch.float32),
                                           (torch.float32, torch.bfloat16)])
-def test_prefetch_variant_forced(monkeypatch, dtype, wdtype):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-    monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
-    monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+def test_prefetch_variant_forced(knobs, dtype, wdtype):
+    knobs.setenv("ADDRMS_BWD_WPR", "2")
+    knobs.setenv("ADDRMS_BWD_WIDE", "2")
+    knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
     cases = [(1001, 4096), (3001, 3072), (7, 1032), (2049, 520), (9001, 1536)] if dtype == torch.bfloat16 \
         else [(1001, 2048), (3001, 1536), (7, 516), (2049, 260), (9001, 768)]
     for M, N in cases:
         inp = synth.rmsnorm_bwd_inputs(M, N, dtype, wdtype, seed=M + 5 * N)
         dx, _ = check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"prefetch {M}x{N}")
         if N in (4096, 2048):
-            monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "2")
+            knobs.setenv("ADDRMS_BWD_PREFETCH", "2")
             dx2, _ = check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, f"no prefetch {M}x{N}")
-            monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+            knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
             assert torch.equal(dx.view(torch.int16) if dtype == torch.bfloat16 else dx,
                                dx2.view(torch.int16) if dtype == torch.bfloat16 else dx2)
 
@@ -111,8 +111,8 @@ def test_wide_variant_default_shapes(M, N):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("M,N", [(5, 4096), (2000, 7168), (3, 8), (1025, 1000)])
-def test_elementwise_path(monkeypatch, dtype, M, N):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+def test_elementwise_path(knobs, dtype, M, N):
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     inp = synth.rmsnorm_bwd_inputs(M, N, dtype, seed=5)
     check_bwd(inp["dy"], inp["x"], inp["w"], 1e-6, "elem")
 
@@ -144,15 +144,15 @@ def test_many_rows_exceed_partial_rows():
 
 
 @pytest.mark.parametrize("force_elem", ["0", "1", "prefetch"])
-def test_dx_in_place(monkeypatch, force_elem):
+def test_dx_in_place(knobs, force_elem):
     """dx over dy or x; "prefetch": the next-row prefetch kernel, whose loads
     of the next row go out before the current row's dx stores."""
     if force_elem == "prefetch":
-        monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-        monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
-        monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+        knobs.setenv("ADDRMS_BWD_WPR", "2")
+        knobs.setenv("ADDRMS_BWD_WIDE", "2")
+        knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
     else:
-        monkeypatch.setenv("ADDRMS_FORCE_ELEM", force_elem)
+        knobs.setenv("ADDRMS_FORCE_ELEM", force_elem)
     M, N = 300, 4096
     inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=29)
     rstd = oracle_rstd(inp["x"], inp["w"], 1e-6)

@@ -109,17 +109,17 @@ def test_fp8_float32_rows(dtype, wdtype):
 
 
 @pytest.mark.parametrize("wpr", [1, 2, 4, 8, 16])
-def test_fp8_forced_waves_per_row(monkeypatch, wpr):
-    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+def test_fp8_forced_waves_per_row(knobs, wpr):
+    knobs.setenv("ADDRMS_FWD_WPR", str(wpr))
     inp = synth.add_rmsnorm_fwd_inputs(37, 4096, torch.bfloat16, seed=wpr)
     run(inp["x"], inp["r"], inp["w"], 1e-6, f"wpr={wpr}")
 
 
 @pytest.mark.parametrize("N", [1, 7, 65, 8193])
-def test_fp8_edge_and_elementwise(monkeypatch, N):
+def test_fp8_edge_and_elementwise(knobs, N):
     inp = synth.add_rmsnorm_fwd_inputs(17, N, torch.bfloat16, seed=N)
     run(inp["x"], inp["r"], inp["w"], 1e-6, f"N={N}")
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     inp = synth.add_rmsnorm_fwd_inputs(9, 4096, torch.bfloat16, seed=N + 1)
     run(inp["x"], inp["r"], inp["w"], 1e-6, f"elem N={N}")
 
@@ -203,14 +203,14 @@ def test_grouped_ragged_rows_and_long_rows(N):
 
 
 @pytest.mark.parametrize("wpr", [1, 2, 4, 8, 16])
-def test_grouped_forced_waves_per_row(monkeypatch, wpr):
-    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+def test_grouped_forced_waves_per_row(knobs, wpr):
+    knobs.setenv("ADDRMS_FWD_WPR", str(wpr))
     inp = synth.add_rmsnorm_fwd_inputs(37, 4096, torch.bfloat16, seed=wpr + 50)
     run(inp["x"], inp["r"], inp["w"], 1e-6, f"wpr={wpr} g128", group=128)
 
 
-def test_grouped_elementwise_forced(monkeypatch):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+def test_grouped_elementwise_forced(knobs):
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     inp = synth.add_rmsnorm_fwd_inputs(11, 4096, torch.bfloat16, seed=77)
     run(inp["x"], inp["r"], inp["w"], 1e-6, "elem g128", group=128)
     run(inp["x"], None, inp["w"], 1e-6, "elem g64", group=64)

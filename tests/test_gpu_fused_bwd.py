@@ -63,8 +63,8 @@ def test_fused_bwd_dtypes(dtype, wdtype):
 
 
 @pytest.mark.parametrize("wpr", [1, 2, 4, 8])
-def test_fused_bwd_forced_waves_per_row(monkeypatch, wpr):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", str(wpr))
+def test_fused_bwd_forced_waves_per_row(knobs, wpr):
+    knobs.setenv("ADDRMS_BWD_WPR", str(wpr))
     check(*fused_case(1000, 4096, torch.bfloat16, seed=7), f"wpr={wpr}")
 
 
@@ -72,9 +72,9 @@ def test_fused_bwd_forced_waves_per_row(monkeypatch, wpr):
 # for the fused backward: up to 3 vectors a lane
 @pytest.mark.parametrize("dtype,M,N", [(torch.bfloat16, 3001, 3072), (torch.bfloat16, 9000, 1040),
                                        (torch.float32, 1000, 1536)])
-def test_fused_bwd_wide_variant(monkeypatch, dtype, M, N):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+def test_fused_bwd_wide_variant(knobs, dtype, M, N):
+    knobs.setenv("ADDRMS_BWD_WPR", "2")
+    knobs.setenv("ADDRMS_BWD_WIDE", "1")
     check(*fused_case(M, N, dtype, seed=M), f"wide {M}x{N}")
 
 
@@ -84,10 +84,10 @@ def test_fused_bwd_wide_variant(monkeypatch, dtype, M, N):
                                           (torch.bfloat16, torch.float32),
                                           (torch.float32, torch.float32),
                                           (torch.float32, torch.bfloat16)])
-def test_fused_bwd_prefetch_forced(monkeypatch, dtype, wdtype):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-    monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
-    monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+def test_fused_bwd_prefetch_forced(knobs, dtype, wdtype):
+    knobs.setenv("ADDRMS_BWD_WPR", "2")
+    knobs.setenv("ADDRMS_BWD_WIDE", "2")
+    knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
     cases = [(1001, 4096), (777, 2056), (9, 520)] if dtype == torch.bfloat16 \
         else [(1001, 2048), (777, 1028), (9, 260)]
     for M, N in cases:
@@ -100,8 +100,8 @@ def test_fused_bwd_prefetch_default_shapes(M, N):
 
 
 @pytest.mark.parametrize("M,N", [(5, 4096), (129, 7), (64, 1000)])
-def test_fused_bwd_elementwise(monkeypatch, M, N):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+def test_fused_bwd_elementwise(knobs, M, N):
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     check(*fused_case(M, N, torch.bfloat16, seed=9), f"elem {M}x{N}")
 
 
@@ -190,3 +190,54 @@ def test_custom_op_registration_checks():
     _, h, rstd = torch.ops.addrms.add_rms_norm_fwd(x, r, w, 1e-6)
     torch.library.opcheck(torch.ops.addrms.add_rms_norm_bwd, (x, r, h, w, rstd))
     torch.library.opcheck(torch.ops.addrms.rms_norm_bwd, (x, h, w, rstd))
+
+
+def test_autograd_non_contiguous_inputs():
+    """Transposed and column-sliced activations: forward and backward run on
+    contiguous copies and give the same bits as contiguous inputs; every
+    output is contiguous (as the fake implementations declare), and opcheck
+    accepts the strided samples."""
+    M, N = 384, 1024
+    inp = synth.add_rmsnorm_fwd_inputs(N, M, torch.bfloat16, seed=29, r_std=0.5)
+    xt = inp["x"].to(DEV).t()                       # [M, N], transposed view
+    wide = synth.store(synth.normal(29, "x", (M, 2 * N)), torch.bfloat16).to(DEV)
+    xs = wide[:, ::2]                               # [M, N], column stride 2
+    r = synth.store(synth.normal(29, "r", (M, N)), torch.bfloat16).to(DEV)
+    w = synth.weight(29, N, torch.bfloat16).to(DEV)
+    b = synth.store(synth.normal(29, "b", (N,), std=0.1), torch.bfloat16).to(DEV)
+    dy = synth.store(synth.normal(29, "dy", (M, N)), torch.bfloat16).to(DEV)
+    dres = synth.store(synth.normal(30, "dy", (M, N)), torch.bfloat16).to(DEV)
+
+    def grads(fn, xv, *rest):
+        leaves = [xv.detach().clone() if xv.is_contiguous() else xv.detach(), *rest]
+        leaves = [t.requires_grad_(True) if t is not None else None for t in leaves]
+        out = fn(*leaves)
+        outs = out if isinstance(out, tuple) else (out,)
+        for o in outs:
+            assert o.is_contiguous()
+        torch.autograd.backward(list(outs), [dy, dres][:len(outs)])
+        torch.cuda.synchronize()
+        return [o.detach() for o in outs], [t.grad for t in leaves if t is not None]
+
+    cases = [
+        ("rms_norm", lambda x, w_: ag.rms_norm(x, w_, 1e-6), (w,)),
+        ("add_rms_norm", lambda x, r_, w_: ag.add_rms_norm(x, r_, w_, 1e-6), (r, w)),
+        ("layer_norm", lambda x, w_, b_: ag.layer_norm(x, w_, b_, 1e-5), (w, b)),
+        ("add_layer_norm", lambda x, r_, w_, b_: ag.add_layer_norm(x, r_, w_, b_, 1e-5),
+         (r, w, b)),
+    ]
+    for name, fn, rest in cases:
+        for xv in (xt, xs):
+            assert not xv.is_contiguous()
+            rest_a = [t.detach().clone() for t in rest]
+            rest_b = [t.detach().clone() for t in rest]
+            out_nc, g_nc = grads(fn, xv, *rest_a)
+            out_c, g_c = grads(fn, xv.contiguous(), *rest_b)
+            for a, c in zip(out_nc + g_nc, out_c + g_c):
+                assert torch.equal(a.contiguous().view(torch.uint8),
+                                   c.contiguous().view(torch.uint8)), name
+    torch.library.opcheck(torch.ops.addrms.rms_norm_fwd, (xt, w, 1e-6))
+    torch.library.opcheck(torch.ops.addrms.add_rms_norm_fwd, (xs, r, w, 1e-6))
+    torch.library.opcheck(torch.ops.addrms.layer_norm_fwd, (xt, w, b, 1e-5))
+    _, h, rstd = torch.ops.addrms.add_rms_norm_fwd(xs, r, w, 1e-6)
+    torch.library.opcheck(torch.ops.addrms.rms_norm_bwd, (dy.t().contiguous().t(), xt, w, rstd))

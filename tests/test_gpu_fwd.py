@@ -86,8 +86,8 @@ def test_decode_bf16_fp32_weight_n8192(M):
                                           (torch.bfloat16, torch.float32),
                                           (torch.float32, torch.float32),
                                           (torch.float32, torch.bfloat16)])
-def test_forced_waves_per_row(monkeypatch, wpr, dtype, wdtype):
-    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+def test_forced_waves_per_row(knobs, wpr, dtype, wdtype):
+    knobs.setenv("ADDRMS_FWD_WPR", str(wpr))
     for M, N in [(37, 4096), (5, 1032), (300, 512)]:
         inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, wdtype, seed=M + N)
         check_fused(inp["x"], inp["r"], inp["w"], 1e-6, f"wpr={wpr} {M}x{N}")
@@ -98,8 +98,8 @@ def test_forced_waves_per_row(monkeypatch, wpr, dtype, wdtype):
                                           (torch.float32, torch.float32),
                                           (torch.bfloat16, torch.float32)])
 @pytest.mark.parametrize("M,N", [(3, 4096), (64, 7168), (2, 8)])
-def test_elementwise_path(monkeypatch, dtype, wdtype, M, N):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+def test_elementwise_path(knobs, dtype, wdtype, M, N):
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, wdtype, seed=7)
     check_fused(inp["x"], inp["r"], inp["w"], 1e-6, "elem")
     check_plain(inp["x"], inp["w"], 1e-6, "elem")
@@ -164,8 +164,8 @@ def test_unaligned_views_take_elementwise_path(offset):
 
 
 @pytest.mark.parametrize("force_elem", ["0", "1"])
-def test_in_place(monkeypatch, force_elem):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", force_elem)
+def test_in_place(knobs, force_elem):
+    knobs.setenv("ADDRMS_FORCE_ELEM", force_elem)
     M, N = 257, 4096
     inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=11)
     ry, rres, _ = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)

@@ -111,3 +111,59 @@ def test_graph_replays_match_eager(M, N):
             assert_close(got["rstd"].cpu(), rrstd, "rstd (replay)", atol=0, rtol=1e-5)
             assert_bits_equal(got["qres"].cpu(), rres, "fp8 residual_out (replay)")
     del g
+
+
+def test_graph_capture_through_implicit_workspace():
+    """Forward and backward of the autograd ops captured in one graph, the
+    backward's workspace taken implicitly (no workspace argument).  Between
+    replays, eager backwards at larger sizes grow and replace the binding's
+    cached workspace; each replay must still equal the eager result bit for
+    bit, so the graph does not write into a cached buffer that was freed."""
+    from add_rmsnorm_amd import autograd as ag
+    M, N = 512, 4096
+    bf = torch.bfloat16
+    x = torch.empty(M, N, dtype=bf, device=DEV, requires_grad=True)
+    w = torch.empty(N, dtype=bf, device=DEV, requires_grad=True)
+    dy = torch.empty(M, N, dtype=bf, device=DEV)
+
+    def load(seed):
+        inp = synth.rmsnorm_bwd_inputs(M, N, bf, seed=seed)
+        with torch.no_grad():
+            x.copy_(inp["x"].to(DEV))
+            w.copy_(inp["w"].to(DEV))
+            dy.copy_(inp["dy"].to(DEV))
+        torch.cuda.synchronize()
+
+    def step():
+        y = ag.rms_norm(x, w, EPS)
+        gx, gw = torch.autograd.grad(y, (x, w), grad_outputs=dy)
+        return y, gx, gw
+
+    load(200)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        static = step()
+    torch.cuda.synchronize()
+    for k in range(4):
+        load(k)
+        # eager backwards that grow the cached workspace in between
+        big = synth.rmsnorm_bwd_inputs(M * (k + 2), N, bf, seed=300 + k)
+        bx, bw, bdy = (big[n].to(DEV) for n in ("x", "w", "dy"))
+        _, brstd = ar.rmsnorm_fwd(bx, bw, EPS, return_rstd=True)
+        ar.rmsnorm_bwd(bdy, bx, bw, brstd)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.detach().clone() for t in static]
+        ref = [t.detach() for t in step()]
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "dx", "dw"), got, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                f"replay {k}: {name} differs from the eager call"
+    del g

@@ -84,8 +84,8 @@ def test_forward_dtypes(dtype, wdtype):
 
 
 @pytest.mark.parametrize("wpr", [1, 2, 4, 8, 16])
-def test_forward_forced_waves_per_row(monkeypatch, wpr):
-    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+def test_forward_forced_waves_per_row(knobs, wpr):
+    knobs.setenv("ADDRMS_FWD_WPR", str(wpr))
     for M, N in [(37, 4096), (5, 1032)]:
         inp = inputs(M, N, torch.bfloat16, seed=M, bias=True)
         check_fwd(inp, True, f"wpr={wpr} {M}x{N}")
@@ -101,8 +101,8 @@ def test_forward_edge_shapes(N):
 
 
 @pytest.mark.parametrize("M,N", [(4, 4096), (64, 1000)])
-def test_forward_elementwise(monkeypatch, M, N):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+def test_forward_elementwise(knobs, M, N):
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     inp = inputs(M, N, torch.bfloat16, seed=11)
     check_fwd(inp, True, "elem")
     check_fwd(inp, False, "elem")
@@ -132,8 +132,8 @@ def test_backward_bf16(M, N):
 @pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
                                           (torch.float32, torch.float32),
                                           (torch.bfloat16, torch.float32)])
-def test_backward_variants(monkeypatch, wpr, dtype, wdtype):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", str(wpr))
+def test_backward_variants(knobs, wpr, dtype, wdtype):
+    knobs.setenv("ADDRMS_BWD_WPR", str(wpr))
     check_bwd(inputs(1000, 2048, dtype, wdtype, seed=wpr), f"wpr={wpr}")
 
 
@@ -141,9 +141,9 @@ def test_backward_variants(monkeypatch, wpr, dtype, wdtype):
 # LDS tree) where it is built for LayerNorm: up to 3 vectors a lane
 @pytest.mark.parametrize("dtype,M,N", [(torch.bfloat16, 3001, 3072), (torch.bfloat16, 9000, 1040),
                                        (torch.float32, 1000, 1536)])
-def test_backward_wide_variant(monkeypatch, dtype, M, N):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+def test_backward_wide_variant(knobs, dtype, M, N):
+    knobs.setenv("ADDRMS_BWD_WPR", "2")
+    knobs.setenv("ADDRMS_BWD_WIDE", "1")
     check_bwd(inputs(M, N, dtype, seed=M), f"wide {M}x{N}")
 
 
@@ -152,10 +152,10 @@ def test_backward_wide_variant(monkeypatch, dtype, M, N):
 @pytest.mark.parametrize("dtype,M,N", [(torch.bfloat16, 3001, 4096), (torch.bfloat16, 777, 2056),
                                        (torch.bfloat16, 2049, 520), (torch.float32, 1001, 2048),
                                        (torch.float32, 9, 772)])
-def test_backward_prefetch_forced(monkeypatch, dtype, M, N):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-    monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
-    monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+def test_backward_prefetch_forced(knobs, dtype, M, N):
+    knobs.setenv("ADDRMS_BWD_WPR", "2")
+    knobs.setenv("ADDRMS_BWD_WIDE", "2")
+    knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
     check_bwd(inputs(M, N, dtype, seed=M + N), f"prefetch {M}x{N}")
 
 
@@ -170,20 +170,20 @@ def test_backward_edge_shapes(N):
 
 
 @pytest.mark.parametrize("M,N", [(9, 4096), (130, 1000)])
-def test_backward_elementwise_and_no_db(monkeypatch, M, N):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+def test_backward_elementwise_and_no_db(knobs, M, N):
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     check_bwd(inputs(M, N, torch.bfloat16, seed=17), "elem")
     check_bwd(inputs(M, N, torch.float32, seed=18), "elem f32", with_db=False)
 
 
 @pytest.mark.parametrize("prefetch", ["0", "1"])
-def test_backward_in_place_and_empty(monkeypatch, prefetch):
+def test_backward_in_place_and_empty(knobs, prefetch):
     """dx over dy; with prefetch = 1 through the next-row prefetch kernel,
     whose loads of the next row go out before the current row's dx stores."""
     if prefetch == "1":
-        monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-        monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
-        monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+        knobs.setenv("ADDRMS_BWD_WPR", "2")
+        knobs.setenv("ADDRMS_BWD_WIDE", "2")
+        knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
     inp = inputs(300, 4096, torch.bfloat16, seed=19)
     x, w = inp["x"], inp["w"]
     dy = synth.store(synth.normal(19, "dy", (300, 4096)), torch.bfloat16)
@@ -222,9 +222,9 @@ def test_fused_backward(M, N, dtype):
 # waves per row), built up to 2 vectors a lane: forced, with a ragged row
 @pytest.mark.parametrize("M,N,dtype", [(3001, 2048, torch.bfloat16), (777, 1032, torch.bfloat16),
                                        (500, 1024, torch.float32)])
-def test_fused_backward_wide_variant(monkeypatch, M, N, dtype):
-    monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-    monkeypatch.setenv("ADDRMS_BWD_WIDE", "1")
+def test_fused_backward_wide_variant(knobs, M, N, dtype):
+    knobs.setenv("ADDRMS_BWD_WPR", "2")
+    knobs.setenv("ADDRMS_BWD_WIDE", "1")
     _fused_backward_case(M, N, dtype)
 
 
@@ -234,11 +234,11 @@ def test_fused_backward_wide_variant(monkeypatch, M, N, dtype):
                                              (777, 2056, torch.bfloat16, True),
                                              (500, 2048, torch.float32, True),
                                              (16384, 4096, torch.bfloat16, False)])
-def test_fused_backward_prefetch(monkeypatch, M, N, dtype, force):
+def test_fused_backward_prefetch(knobs, M, N, dtype, force):
     if force:
-        monkeypatch.setenv("ADDRMS_BWD_WPR", "2")
-        monkeypatch.setenv("ADDRMS_BWD_WIDE", "2")
-        monkeypatch.setenv("ADDRMS_BWD_PREFETCH", "1")
+        knobs.setenv("ADDRMS_BWD_WPR", "2")
+        knobs.setenv("ADDRMS_BWD_WIDE", "2")
+        knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
     _fused_backward_case(M, N, dtype)
 
 

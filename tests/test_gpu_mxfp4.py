@@ -129,14 +129,14 @@ def test_decode_with_outliers(M):
 
 
 @pytest.mark.parametrize("wpr", [1, 2, 4, 8, 16])
-def test_forced_waves_per_row(monkeypatch, wpr):
-    monkeypatch.setenv("ADDRMS_FWD_WPR", str(wpr))
+def test_forced_waves_per_row(knobs, wpr):
+    knobs.setenv("ADDRMS_FWD_WPR", str(wpr))
     inp = synth.add_rmsnorm_fwd_inputs(37, 4096, torch.bfloat16, seed=wpr + 90)
     run(inp["x"], inp["r"], inp["w"], 1e-6, f"wpr={wpr}")
 
 
-def test_elementwise_forced(monkeypatch):
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+def test_elementwise_forced(knobs):
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     inp = synth.add_rmsnorm_fwd_inputs(13, 4096, torch.bfloat16, seed=93)
     run(inp["x"], inp["r"], inp["w"], 1e-6, "elem")
     run(inp["x"], None, inp["w"], 1e-6, "elem plain")
@@ -199,10 +199,10 @@ def _tie_rows(dtype):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("force_elem", ["0", "1"])
 @pytest.mark.parametrize("fused", [False, True])
-def test_e2m1_ties_exact(monkeypatch, dtype, force_elem, fused):
+def test_e2m1_ties_exact(knobs, dtype, force_elem, fused):
     """Round-half-to-even and saturation of the E2M1 encoding (on the GPU the
     hardware conversion), bit for bit against the oracle."""
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", force_elem)
+    knobs.setenv("ADDRMS_FORCE_ELEM", force_elem)
     x, w, eps = _tie_rows(dtype)
     if fused:
         r = torch.zeros_like(x)

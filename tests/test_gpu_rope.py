@@ -115,9 +115,9 @@ def test_every_lane_group_width(interleaved, dtype, wdtype, G):
 
 @pytest.mark.parametrize("hpl", [1, 2, 4])
 @pytest.mark.parametrize("D", [16, 128, 1024])
-def test_heads_per_group_with_ragged_tails(monkeypatch, hpl, D):
+def test_heads_per_group_with_ragged_tails(knobs, hpl, D):
     # head counts that leave a partial final step: 37 tokens x (5 + 2) heads
-    monkeypatch.setenv("ADDRMS_ROPE_HPL", str(hpl))
+    knobs.setenv("ADDRMS_ROPE_HPL", str(hpl))
     run_packed(37, 5, 2, D, torch.bfloat16, torch.bfloat16, hpl == 2, seed=hpl * D)
 
 
@@ -128,9 +128,9 @@ def test_other_head_sizes_take_the_elementwise_path(D, interleaved):
 
 
 @pytest.mark.parametrize("interleaved", [False, True])
-def test_forced_elementwise_and_odd_strides(monkeypatch, interleaved):
+def test_forced_elementwise_and_odd_strides(knobs, interleaved):
     run_packed(65, 2, 2, 128, torch.float32, torch.float32, interleaved, seed=3)
-    monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+    knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     run_packed(65, 5, 3, 128, torch.bfloat16, torch.bfloat16, interleaved, seed=4)
 
 
@@ -181,9 +181,9 @@ def test_separate_buffers_with_their_own_strides():
 
 
 @pytest.mark.parametrize("vec", [True, False])
-def test_positions_outside_the_table_give_nan_heads(monkeypatch, vec):
+def test_positions_outside_the_table_give_nan_heads(knobs, vec):
     if not vec:
-        monkeypatch.setenv("ADDRMS_FORCE_ELEM", "1")
+        knobs.setenv("ADDRMS_FORCE_ELEM", "1")
     T, P = 9, 64
     pos = synth.positions(9, T, P)
     pos[2], pos[5], pos[7] = -1, P, 1 << 40
