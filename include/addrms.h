@@ -176,8 +176,10 @@ int add_rmsnorm_bwd(const void *dy, const void *dres, const void *h, const void 
  * activations after the norm).  y is computed as in rmsnorm_fwd /
  * add_rmsnorm_fwd in float32 but not stored; per row:
  *     amax_i  = max_j |y_ij|        (NaNs ignored)
- *     scale_i = amax_i / 448,  inv_i = 448 / amax_i   (float32; 1 and 1 when amax_i = 0)
- *     q_ij    = E4M3(clamp(y_ij * inv_i, -448, 448))
+ *     scale_i = amax_i / 448        (float32; 1 when amax_i = 0)
+ *     q_ij    = E4M3(clamp(y_ij / scale_i, -448, 448))
+ * (computed as y_ij * (448 / amax_i) in float32, which agrees with the
+ * quotient to about 1e-6 relative)
  * E4M3 is the OCP 8-bit float with 4 exponent bits (bias 7), 3 mantissa bits,
  * no infinities, largest value 448 (torch.float8_e4m3fn), rounded to nearest
  * even; y_ij ~= decode(q_ij) * scale_i.
@@ -199,8 +201,8 @@ int add_rmsnorm_fwd_fp8(const void *x, const void *r, const void *w, void *y_fp8
  * per channel block, e.g. group = 128); the last group of a row may be
  * shorter.  For row i and group g (columns g*group .. min(N, (g+1)*group)-1):
  *     amax_ig = max |y_ij| over the group (NaNs ignored)
- *     scale_ig = amax_ig / 448,  inv_ig = 448 / amax_ig  (1 and 1 when 0)
- *     q_ij = E4M3(clamp(y_ij * inv_ig, -448, 448))
+ *     scale_ig = amax_ig / 448  (1 when amax_ig = 0)
+ *     q_ij = E4M3(clamp(y_ij / scale_ig, -448, 448))
  *   y_scale  [M][ceil(N / group)]  float32  output, row-major
  * group >= 1 (ADDRMS_ERR_SHAPE otherwise); group >= N gives one scale per
  * row, as rmsnorm_fwd_fp8.  The vector path takes groups of a power of two

@@ -506,14 +506,15 @@ void oracle_fp8e4m3_encode_array(const double *v, uint8_t *out, int64_t n)
 /* RMSNorm with an E4M3 output and dynamic scales, for a downstream FP8 GEMM.
  * The scales are per group of `group` consecutive columns of a row (the last
  * group of a row may be shorter); group <= 0 means one group per row.  Per
- * row: y_j = h_j * rstd * w_j in binary64, rounded once to binary32 (yf_j);
- * per group: amax = max |yf_j| over the group's columns; the quantisation
- * decisions are then taken in binary32, as the kernel takes them:
- *     inv = 448 / amax,  scale = amax / 448   (binary32 divisions)
- *     q_j = E4M3(yf_j * inv)                  (binary32 product, encoded)
- * with inv = scale = 1 for a group with no non-zero finite |yf| (NaNs are
- * ignored by the maximum and encode as NaN).  y_j ~= decode(q_j) * scale of
- * its group.  scale is [M][ceil(N / group)], row-major. */
+ * row: y_j = h_j * rstd * w_j in binary64; per group, by the definition of a
+ * dynamic scale (the group's largest magnitude maps to E4M3's largest value,
+ * 448) and of the codes relative to the scale the caller receives:
+ *     amax  = max |y_j| over the group's columns      (binary64; NaNs ignored)
+ *     scale = binary32(amax / 448)                     (the stored scale)
+ *     q_j   = E4M3(y_j / scale)                        (binary64 quotient, one rounding)
+ * with scale = 1 for a group with no non-zero finite |y| (a NaN encodes as
+ * NaN).  y_j ~= decode(q_j) * scale of its group.  scale is
+ * [M][ceil(N / group)], row-major. */
 static size_t elem_size(int dt) { return dt == OR_F32 ? 4 : dt == OR_BF16 ? 2 : 8; }
 
 int oracle_rmsnorm_fwd_fp8_grouped(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
@@ -521,7 +522,6 @@ int oracle_rmsnorm_fwd_fp8_grouped(const void *x, int x_dt, const void *w, int w
                                    int64_t M, int64_t N, double eps)
 {
     double *y;
-    float *yf;
 
     if (!x || !w || !q || !scale || M < 0 || N <= 0)
         return OR_ERR_ARG;
@@ -531,41 +531,30 @@ int oracle_rmsnorm_fwd_fp8_grouped(const void *x, int x_dt, const void *w, int w
         group = N;
     const int64_t ngroups = (N + group - 1) / group;
     y = (double *)malloc((size_t)N * sizeof(double));
-    yf = (float *)malloc((size_t)N * sizeof(float));
-    if (!y || !yf) {
-        free(y);
-        free(yf);
+    if (!y)
         return OR_ERR_NOMEM;
-    }
     for (int64_t i = 0; i < M; i++) {
         /* the row's RMSNorm in binary64, by the forward above */
         const void *xi = (const char *)x + (size_t)(i * N) * elem_size(x_dt);
         void *ri = rstd ? (void *)((char *)rstd + (size_t)i * elem_size(rstd_dt)) : NULL;
         oracle_rmsnorm_fwd(xi, x_dt, w, w_dt, y, OR_F64, ri, rstd_dt, 1, N, eps);
-        for (int64_t j = 0; j < N; j++)
-            yf[j] = (float)y[j];
         for (int64_t g = 0; g < ngroups; g++) {
             const int64_t j0 = g * group, j1 = j0 + group < N ? j0 + group : N;
-            float amax = 0.0f;
+            double amax = 0.0;
             for (int64_t j = j0; j < j1; j++) {
-                float m = fabsf(yf[j]);
+                double m = fabs(y[j]);
                 if (m > amax) /* NaN never compares greater: NaNs do not set the scale */
                     amax = m;
             }
-            float inv = 1.0f, sc = 1.0f;
-            if (amax != 0.0f) {
-                inv = 448.0f / amax;
-                sc = amax / 448.0f;
-            }
+            float sc = 1.0f;
+            if (amax != 0.0)
+                sc = (float)(amax / 448.0);
             scale[i * ngroups + g] = sc;
-            for (int64_t j = j0; j < j1; j++) {
-                float v = yf[j] * inv;
-                q[i * N + j] = oracle_fp8e4m3_encode((double)v);
-            }
+            for (int64_t j = j0; j < j1; j++)
+                q[i * N + j] = oracle_fp8e4m3_encode(y[j] / (double)sc);
         }
     }
     free(y);
-    free(yf);
     return OR_OK;
 }
 

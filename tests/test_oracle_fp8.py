@@ -145,8 +145,7 @@ def test_constant_groups_have_closed_form_scales():
     assert s.shape == (1, 3)
     rs = 1.0 / np.sqrt((128 * a * a + 128 * b * b + 44 * c * c) / 300)
     for k, v in enumerate((a, b, c)):
-        yf = np.float32(v * rs)
-        assert s[0, k].item() == np.float32(np.abs(yf) / np.float32(448.0))
+        assert s[0, k].item() == np.float32(np.abs(v * rs) / 448.0)
     # every value is its group's maximum: the codes are +-448
     qn = q.numpy()[0]
     assert np.all(qn[:128] == 0x7E) and np.all(qn[128:256] == 0xFE) and np.all(qn[256:] == 0x7E)
@@ -159,13 +158,13 @@ def test_groups_of_one_column():
     x[1, 7] = 0.0
     q, s, _ = oracle.rmsnorm_fwd_fp8(x, inp["w"], 1e-6, group=1)
     y, _ = oracle.rmsnorm_fwd(x, inp["w"], 1e-6, y_dtype=torch.float64)
-    yf = y.numpy().astype(np.float32)
-    np.testing.assert_array_equal(s.numpy(), np.where(yf == 0, np.float32(1),
-                                                      np.abs(yf) / np.float32(448)))
+    y = y.numpy()
+    np.testing.assert_array_equal(s.numpy(), np.where(y == 0, np.float32(1),
+                                                      (np.abs(y) / 448.0).astype(np.float32)))
     qn = q.numpy()
     assert qn[1, 7] == 0
-    nz = yf != 0
-    assert np.all((qn[nz] & 0x7F) == 0x7E) and np.all((qn[nz] >> 7) == (yf[nz] < 0))
+    nz = y != 0
+    assert np.all((qn[nz] & 0x7F) == 0x7E) and np.all((qn[nz] >> 7) == (y[nz] < 0))
 
 
 @pytest.mark.parametrize("fused", [False, True])

@@ -75,13 +75,14 @@ MUTANTS.update({
     "fp8_ulp_exponent": ("ulp = ldexp(1.0, e - 4);", "ulp = ldexp(1.0, e - 5);"),
     "fp8_exponent_bias": ("int exp_field = (e - 1) + 7;", "int exp_field = (e - 1) + 8;"),
     "fp8_no_saturation": ("return (uint8_t)(sign | 0x7Eu); /* 448", "return (uint8_t)(sign | 0x7Fu); /* 448"),
-    "fp8_scale_inverted": ("sc = amax / 448.0f;", "sc = 448.0f / amax;"),
-    "fp8_quantises_unscaled": ("float v = yf[j] * inv;", "float v = yf[j];"),
+    "fp8_scale_inverted": ("sc = (float)(amax / 448.0);", "sc = (float)(448.0 / amax);"),
+    "fp8_quantises_unscaled": ("oracle_fp8e4m3_encode(y[j] / (double)sc);",
+                               "oracle_fp8e4m3_encode(y[j]);"),
     "fp8_group_is_whole_row": ("const int64_t j0 = g * group, j1 = j0 + group < N ? j0 + group : N;",
                                "const int64_t j0 = g * group, j1 = N;"),
     "fp8_group_scale_index": ("scale[i * ngroups + g] = sc;", "scale[i + g] = sc;"),
-    "fp8_group_amax_from_row_start": ("for (int64_t j = j0; j < j1; j++) {\n                float m",
-                                      "for (int64_t j = 0; j < j1; j++) {\n                float m"),
+    "fp8_group_amax_from_row_start": ("for (int64_t j = j0; j < j1; j++) {\n                double m",
+                                      "for (int64_t j = 0; j < j1; j++) {\n                double m"),
     "fp4_ties_to_odd": ("code = (k % 2 == 0) ? k : k + 1; /* the even code */",
                         "code = (k % 2 == 1) ? k : k + 1;"),
     "fp4_saturates_to_4": ("if (a >= 6.0)\n        return (uint8_t)(sign | 0x7u);",
