@@ -12,7 +12,7 @@ import torch
 import add_rmsnorm_amd as ar
 import oracle
 import synth
-from parity import assert_close, assert_dw_close
+from parity import assert_close, assert_correctly_rounded, assert_dw_close
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -151,6 +151,10 @@ def test_dx_in_place(knobs, force_elem):
         knobs.setenv("ADDRMS_BWD_WPR", "2")
         knobs.setenv("ADDRMS_BWD_WIDE", "2")
         knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
+        # 16 partial rows cap the grid at 16 blocks, so each block walks many
+        # row steps: the next row's loads are in flight while this row's dx is
+        # stored over its input
+        knobs.setenv("ADDRMS_MAX_PARTIALS", "16")
     else:
         knobs.setenv("ADDRMS_FORCE_ELEM", force_elem)
     M, N = 300, 4096
@@ -210,3 +214,25 @@ def test_workspace_too_small_is_an_error():
     ws = torch.empty(ar.rmsnorm_bwd_workspace_bytes(M, N) - 4, dtype=torch.uint8, device=DEV)
     with pytest.raises(ar.AddRmsError, match="workspace"):
         ar.rmsnorm_bwd(inp["dy"].to(DEV), inp["x"].to(DEV), inp["w"].to(DEV), rstd, workspace=ws)
+
+
+def _dx_terms(dy, x, w, rstd, dres=None):
+    """Per element, the magnitude of the terms dx = rstd (g - xh c) (+ dres)
+    is computed from, binary64: the scale of float32 error in dx."""
+    g = dy.double() * w.double()
+    xh = x.double() * rstd.double()[:, None]
+    c = (g * xh).mean(dim=1, keepdim=True)
+    mag = rstd.double()[:, None] * (g.abs() + xh.abs() * c.abs())
+    return mag if dres is None else mag + dres.double().abs()
+
+
+def test_dx_is_rounded_once_32768x4096():
+    """dx within half a bf16 ulp of the binary64 value plus float32 noise
+    scaled by its terms: one rounding of rstd * (g - xh * c)."""
+    inp = synth.workload_inputs("rmsnorm_bwd_bf16_32768x4096")
+    dy, x, w = inp["dy"], inp["x"], inp["w"]
+    rstd = oracle_rstd(x, w, 1e-6)
+    dx, _ = ar.rmsnorm_bwd(dy.to(DEV), x.to(DEV), w.to(DEV), rstd.to(DEV))
+    torch.cuda.synchronize()
+    dx64 = oracle.rmsnorm_bwd(dy, x, w, rstd, dx_dtype=torch.float64)[0]
+    assert_correctly_rounded(dx, dx64, _dx_terms(dy, x, w, rstd), "dx")

@@ -92,6 +92,10 @@ def test_fused_bwd_prefetch_forced(knobs, dtype, wdtype):
         else [(1001, 2048), (777, 1028), (9, 260)]
     for M, N in cases:
         check(*fused_case(M, N, dtype, wdtype, seed=M + N), f"prefetch {M}x{N}")
+    # the grid capped at 16 blocks: every block walks many row steps
+    knobs.setenv("ADDRMS_MAX_PARTIALS", "16")
+    for M, N in cases:
+        check(*fused_case(M, N, dtype, wdtype, seed=M + N), f"prefetch, 16 blocks, {M}x{N}")
 
 
 @pytest.mark.parametrize("M,N", [(24576, 3584), (16384, 4096)])
@@ -121,8 +125,17 @@ def test_fused_bwd_without_residual_gradient_is_plain_bwd():
     assert torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("prefetch", [False, True])
 @pytest.mark.parametrize("target", ["dy", "dres", "h"])
-def test_fused_bwd_in_place(target):
+def test_fused_bwd_in_place(knobs, target, prefetch):
+    """dh over each of its inputs; with prefetch, through the next-row
+    prefetch kernel on a grid of 16 blocks, so the next row's loads of dy,
+    dres and h are in flight while this row's dh is stored over one of them."""
+    if prefetch:
+        knobs.setenv("ADDRMS_BWD_WPR", "2")
+        knobs.setenv("ADDRMS_BWD_WIDE", "2")
+        knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
+        knobs.setenv("ADDRMS_MAX_PARTIALS", "16")
     dy, dres, h, w, rstd = fused_case(300, 4096, torch.bfloat16, seed=13)
     rdh, rdw, mag = oracle.add_rmsnorm_bwd(dy, dres, h, w, rstd)
     t = {"dy": dy.to(DEV), "dres": dres.to(DEV), "h": h.to(DEV)}
@@ -241,3 +254,21 @@ def test_autograd_non_contiguous_inputs():
     torch.library.opcheck(torch.ops.addrms.layer_norm_fwd, (xt, w, b, 1e-5))
     _, h, rstd = torch.ops.addrms.add_rms_norm_fwd(xs, r, w, 1e-6)
     torch.library.opcheck(torch.ops.addrms.rms_norm_bwd, (dy.t().contiguous().t(), xt, w, rstd))
+
+
+def test_dh_is_rounded_once_16384x7168():
+    """dh within half a bf16 ulp of the binary64 value plus float32 noise
+    scaled by its terms: one rounding of rstd * (g - hh * c) + dres."""
+    from test_gpu_bwd import _dx_terms
+    from parity import assert_correctly_rounded
+    M, N = 16384, 7168
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=41, r_std=0.5)
+    h = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)[1]
+    w = inp["w"]
+    rstd = oracle.rmsnorm_fwd(h, w, 1e-6)[1]
+    dy = synth.store(synth.normal(41, "dy", (M, N)), torch.bfloat16)
+    dres = synth.store(synth.normal(42, "dy", (M, N)), torch.bfloat16)
+    dh, _ = ar.add_rmsnorm_bwd(dy.to(DEV), dres.to(DEV), h.to(DEV), w.to(DEV), rstd.to(DEV))
+    torch.cuda.synchronize()
+    dh64 = oracle.add_rmsnorm_bwd(dy, dres, h, w, rstd, dh_dtype=torch.float64)[0]
+    assert_correctly_rounded(dh, dh64, _dx_terms(dy, h, w, rstd, dres), "dh")

@@ -12,7 +12,7 @@ import torch
 import add_rmsnorm_amd as ar
 import oracle
 import synth
-from parity import assert_bits_equal, assert_close
+from parity import assert_bits_equal, assert_close, assert_correctly_rounded
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -244,3 +244,21 @@ def test_residual_add_exhaustive_sweep():
     _, res, _ = gpu_fused(x, r, w, 1e-6)
     _, rres, _ = oracle.add_rmsnorm_fwd(x, r, w, 1e-6)
     assert_bits_equal(res, rres, "residual sweep")
+
+
+# ---- one rounding (reading R5) ---------------------------------------------------
+
+@pytest.mark.parametrize("name,M", [("add_rmsnorm_fwd_bf16_16384x7168", None),
+                                    ("add_rmsnorm_fwd_bf16_4096x4096", None),
+                                    ("add_rmsnorm_fwd_bf16_decode_n8192", 512)])
+def test_fused_y_is_rounded_once(name, M):
+    """y within half a bf16 ulp of the binary64 value (plus float32 noise):
+    h * rstd * w is rounded once, with no bf16 step in between."""
+    inp = synth.workload_inputs(name, M=M)
+    eps = synth.WORKLOADS[name]["eps"]
+    y, _, _ = gpu_fused(inp["x"], inp["r"], inp["w"], eps)
+    y64 = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], eps, y_dtype=torch.float64)[0]
+    assert_correctly_rounded(y, y64, None, f"y {name}")
+    yp, _ = gpu_plain(inp["x"], inp["w"], eps)
+    yp64 = oracle.rmsnorm_fwd(inp["x"], inp["w"], eps, y_dtype=torch.float64)[0]
+    assert_correctly_rounded(yp, yp64, None, f"plain y {name}")

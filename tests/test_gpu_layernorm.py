@@ -184,6 +184,10 @@ def test_backward_in_place_and_empty(knobs, prefetch):
         knobs.setenv("ADDRMS_BWD_WPR", "2")
         knobs.setenv("ADDRMS_BWD_WIDE", "2")
         knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
+        # 16 partial rows cap the grid at 16 blocks, so each block walks many
+        # row steps: the next row's loads are in flight while this row's dx is
+        # stored over its input
+        knobs.setenv("ADDRMS_MAX_PARTIALS", "16")
     inp = inputs(300, 4096, torch.bfloat16, seed=19)
     x, w = inp["x"], inp["w"]
     dy = synth.store(synth.normal(19, "dy", (300, 4096)), torch.bfloat16)
@@ -230,20 +234,26 @@ def test_fused_backward_wide_variant(knobs, M, N, dtype):
 
 # the fused LayerNorm backward through the next-row prefetch kernel: forced
 # at 2 and 4 vectors a lane, and on a default shape (4 vectors a lane)
-@pytest.mark.parametrize("M,N,dtype,force", [(1001, 4096, torch.bfloat16, True),
-                                             (777, 2056, torch.bfloat16, True),
-                                             (500, 2048, torch.float32, True),
-                                             (16384, 4096, torch.bfloat16, False)])
-def test_fused_backward_prefetch(knobs, M, N, dtype, force):
+# (forced cases also with the grid capped at 16 blocks, so that every block
+# walks many row steps with the next row's loads in flight; float32 rows,
+# and bf16 rows with float32 weights)
+@pytest.mark.parametrize("M,N,dtype,wdtype,force", [
+    (1001, 4096, torch.bfloat16, None, True), (777, 2056, torch.bfloat16, None, True),
+    (500, 2048, torch.float32, None, True), (1001, 4096, torch.bfloat16, torch.float32, True),
+    (700, 2048, torch.float32, torch.bfloat16, True), (16384, 4096, torch.bfloat16, None, False)])
+def test_fused_backward_prefetch(knobs, M, N, dtype, wdtype, force):
     if force:
         knobs.setenv("ADDRMS_BWD_WPR", "2")
         knobs.setenv("ADDRMS_BWD_WIDE", "2")
         knobs.setenv("ADDRMS_BWD_PREFETCH", "1")
-    _fused_backward_case(M, N, dtype)
+    _fused_backward_case(M, N, dtype, wdtype)
+    if force:
+        knobs.setenv("ADDRMS_MAX_PARTIALS", "16")
+        _fused_backward_case(M, N, dtype, wdtype)
 
 
-def _fused_backward_case(M, N, dtype):
-    inp = inputs(M, N, dtype, seed=29)
+def _fused_backward_case(M, N, dtype, wdtype=None):
+    inp = inputs(M, N, dtype, wdtype, seed=29)
     _, h, mean, rstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
     dy = synth.store(synth.normal(29, "dy", (M, N)), dtype)
     dres = synth.store(synth.normal(30, "dy", (M, N)), dtype)
@@ -288,3 +298,35 @@ def test_layer_norm_autograd():
     torch.library.opcheck(torch.ops.addrms.add_layer_norm_fwd,
                           (x.detach(), r.detach(), w.detach(), b.detach(), EPS))
     torch.library.opcheck(torch.ops.addrms.layer_norm_fwd, (x.detach(), w.detach(), None, EPS))
+
+
+def test_rounded_once_full_size():
+    """LayerNorm y (fused, 16384 x 7168, with bias) and dx (32768 x 4096)
+    within half a bf16 ulp of the binary64 values plus float32 noise scaled
+    by the terms each is computed from."""
+    from parity import assert_correctly_rounded
+    inp = inputs(16384, 7168, torch.bfloat16, seed=51)
+    x, r, w, b = inp["x"], inp["r"], inp["w"], inp["b"]
+    g = lambda t: t.to(DEV)
+    y, res = ar.add_layernorm_fwd(g(x), g(r), g(w), g(b), EPS)
+    torch.cuda.synchronize()
+    y64, h, mean, rstd = oracle.add_layernorm_fwd(x, r, w, b, EPS, y_dtype=torch.float64,
+                                                  stat_dtype=torch.float64)
+    hd, mu, rs = h.double(), mean.double()[:, None], rstd.double()[:, None]
+    mag = rs * w.double().abs() * ((hd - mu).abs() + mu.abs()) + b.double().abs()
+    assert_correctly_rounded(y, y64, mag, "LayerNorm y")
+    del y, res, y64, h, hd, mag
+    inp = inputs(32768, 4096, torch.bfloat16, seed=52)
+    x, w = inp["x"], inp["w"]
+    M, N = x.shape
+    dy = synth.store(synth.normal(53, "dy", (M, N)), x.dtype)
+    _, mean, rstd = oracle.layernorm_fwd(x, w, inp["b"], EPS)
+    dx, _, _ = ar.layernorm_bwd(g(dy), g(x), g(w), g(mean), g(rstd))
+    torch.cuda.synchronize()
+    dx64 = oracle.layernorm_bwd(dy, x, w, mean, rstd, dx_dtype=torch.float64)[0]
+    gg = dy.double() * w.double()
+    xh = (x.double() - mean.double()[:, None]) * rstd.double()[:, None]
+    c1 = gg.mean(dim=1, keepdim=True)
+    c2 = (gg * xh).mean(dim=1, keepdim=True)
+    mag = rstd.double()[:, None] * (gg.abs() + c1.abs() + xh.abs() * c2.abs())
+    assert_correctly_rounded(dx, dx64, mag, "LayerNorm dx")
