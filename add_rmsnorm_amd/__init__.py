@@ -4,7 +4,11 @@ A thin ctypes binding over the C ABI in ``include/addrms.h`` (library
 ``libaddrms.so`` next to this file).  It only marshals arguments: torch
 supplies device memory and the current stream; every step of the computation
 runs in the library's HIP kernels.  There is no fallback: if the library is
-missing, importing this package raises.
+missing, importing this package raises.  The two latency-bound forwards
+(rmsnorm_fwd, add_rmsnorm_fwd) are bound natively (module _native, built
+beside the library) when it is built, with the same arguments, checks,
+results and errors; rmsnorm_fwd_ctypes and add_rmsnorm_fwd_ctypes stay
+available.
 
 Operations (same names as the C ABI):
     rmsnorm_fwd(x, w, eps)            -> y (and rstd)
@@ -29,7 +33,8 @@ __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
            "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "rmsnorm_fwd_fp8",
            "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_mxfp4", "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
-           "AddRmsError", "LIB_PATH", "lib", "KNOBS", "set_knob", "tuning"]
+           "AddRmsError", "LIB_PATH", "lib", "KNOBS", "set_knob", "tuning",
+           "rmsnorm_fwd_ctypes", "add_rmsnorm_fwd_ctypes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
@@ -199,22 +204,46 @@ def _p(t):
     return t.data_ptr() if t is not None else None
 
 
+_get_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+
+
+def _ok(t, dtype, shape) -> bool:
+    """The checks of _dev in one expression (the per-call fast path of the
+    latency-bound forwards); on False the caller runs _dev for the message."""
+    return t.is_cuda and t.dtype == dtype and t.shape == shape and t.is_contiguous()
+
+
+def _call(dev: int, fn, *args) -> int:
+    """fn(*args) with `dev` the current device (switched only when needed)."""
+    cur = _get_device()
+    if cur == dev:
+        return fn(*args)
+    torch.cuda.set_device(dev)
+    try:
+        return fn(*args)
+    finally:
+        torch.cuda.set_device(cur)
+
+
 def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, *, y=None, rstd=None,
                 return_rstd: bool = False):
     """y = x / sqrt(mean(x^2, -1) + eps) * w, normalising the last dimension.
     `y` may be `x` (in place).  Returns y, or (y, rstd) with float32 rstd."""
     _dev(x, "x")
     M, N = _rows(x)
-    _dev(w, "w", shape=(N,))
-    y = torch.empty_like(x) if y is None else _dev(y, "y", x.dtype, x.shape)
+    if not _ok(w, w.dtype, (N,)):
+        _dev(w, "w", shape=(N,))
+    if y is None:
+        y = torch.empty_like(x)
+    elif not _ok(y, x.dtype, x.shape):
+        _dev(y, "y", x.dtype, x.shape)
     if rstd is None and return_rstd:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     elif rstd is not None:
         _dev(rstd, "rstd", torch.float32, x.shape[:-1])
     dev = x.get_device()
-    with _OnDevice(dev):
-        st = _lib.rmsnorm_fwd(_p(x), _p(w), _p(y), _p(rstd), M, N, float(eps),
-                              _code(x, "x"), _code(w, "w"), _stream(dev))
+    st = _call(dev, _lib.rmsnorm_fwd, x.data_ptr(), w.data_ptr(), y.data_ptr(), _p(rstd), M, N,
+               float(eps), _code(x, "x"), _code(w, "w"), _stream(dev))
     if st != 0:
         raise AddRmsError(st, "rmsnorm_fwd")
     return (y, rstd) if (return_rstd or rstd is not None) else y
@@ -228,19 +257,27 @@ def add_rmsnorm_fwd(x: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: floa
     `x` or `r`.  Returns (y, residual_out) or (y, residual_out, rstd)."""
     _dev(x, "x")
     M, N = _rows(x)
-    _dev(r, "r", x.dtype, x.shape)
-    _dev(w, "w", shape=(N,))
-    y = torch.empty_like(x) if y is None else _dev(y, "y", x.dtype, x.shape)
-    residual_out = (torch.empty_like(x) if residual_out is None
-                    else _dev(residual_out, "residual_out", x.dtype, x.shape))
+    dt, shp = x.dtype, x.shape
+    if not _ok(r, dt, shp):
+        _dev(r, "r", dt, shp)
+    if not _ok(w, w.dtype, (N,)):
+        _dev(w, "w", shape=(N,))
+    if y is None:
+        y = torch.empty_like(x)
+    elif not _ok(y, dt, shp):
+        _dev(y, "y", dt, shp)
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    elif not _ok(residual_out, dt, shp):
+        _dev(residual_out, "residual_out", dt, shp)
     if rstd is None and return_rstd:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     elif rstd is not None:
         _dev(rstd, "rstd", torch.float32, x.shape[:-1])
     dev = x.get_device()
-    with _OnDevice(dev):
-        st = _lib.add_rmsnorm_fwd(_p(x), _p(r), _p(w), _p(y), _p(residual_out), _p(rstd), M, N,
-                                  float(eps), _code(x, "x"), _code(w, "w"), _stream(dev))
+    st = _call(dev, _lib.add_rmsnorm_fwd, x.data_ptr(), r.data_ptr(), w.data_ptr(), y.data_ptr(),
+               residual_out.data_ptr(), _p(rstd), M, N, float(eps), _code(x, "x"), _code(w, "w"),
+               _stream(dev))
     if st != 0:
         raise AddRmsError(st, "add_rmsnorm_fwd")
     if return_rstd or rstd is not None:
@@ -709,3 +746,20 @@ def rmsnorm_rope_qk(q: torch.Tensor, k, wq: torch.Tensor, wk, cos: torch.Tensor,
     if st != 0:
         raise AddRmsError(st, "rmsnorm_rope_qk")
     return q_out, k_out
+
+
+# The native binding of the latency-bound forwards (csrc/binding.cpp, built
+# beside the library as _native*.so): the same arguments, checks and results
+# as rmsnorm_fwd and add_rmsnorm_fwd above, with the tensor checks in C++
+# (at decode sizes the call is launch-bound and the Python checks cost about
+# as much as the launch).  When it is built it replaces them; if it is built
+# but cannot load, the import fails.  The ctypes versions stay available as
+# rmsnorm_fwd_ctypes and add_rmsnorm_fwd_ctypes.
+rmsnorm_fwd_ctypes, add_rmsnorm_fwd_ctypes = rmsnorm_fwd, add_rmsnorm_fwd
+native = None
+if any(f.startswith("_native") and f.endswith(".so")
+       for f in os.listdir(os.path.dirname(os.path.abspath(__file__)))):
+    import importlib
+    native = importlib.import_module(__name__ + "._native")
+    rmsnorm_fwd = native.rmsnorm_fwd
+    add_rmsnorm_fwd = native.add_rmsnorm_fwd

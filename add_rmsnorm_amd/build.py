@@ -5,7 +5,9 @@
 
 Compiles csrc/tables.hip and csrc/rope.hip once per (row dtype, weight dtype)
 combination and csrc/api.hip, in parallel, then links one shared library next
-to this file.
+to this file.  The native Python binding of the latency-bound forwards
+(csrc/binding.cpp, host C++ against torch's headers) is compiled in the same
+pool and linked against that library as _native*.so.
 """
 from __future__ import annotations
 
@@ -40,6 +42,51 @@ def _compile(src: str, obj: str, defines=()):
     return obj
 
 
+def _torch_paths():
+    """Include and library directories of the installed torch, and the
+    Python extension suffix, for the native binding."""
+    import sysconfig
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or spec.origin is None:
+        return None
+    td = os.path.dirname(spec.origin)
+    return (td, sysconfig.get_paths()["include"], sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+NATIVE_SRC = os.path.join(CSRC, "binding.cpp")
+
+
+def _native_compile(obj: str):
+    """Compile the native Python binding (binding.cpp) with the host C++
+    compiler against torch's headers: no device code."""
+    td, pyinc, _ = _torch_paths()
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", "-DUSE_ROCM",
+           "-I", os.path.join(td, "include"),
+           "-I", os.path.join(td, "include", "torch", "csrc", "api", "include"),
+           "-I", pyinc, "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+           "-c", NATIVE_SRC, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def _native_link(obj: str) -> str:
+    td, _, suffix = _torch_paths()
+    out = os.path.join(PKG, "_native" + suffix)
+    lib = os.path.join(td, "lib")
+    tmp = out + ".tmp"
+    cmd = ["g++", "-shared", "-fPIC", "-o", tmp, obj, "-L", lib, "-lc10", "-lc10_hip", "-ltorch",
+           "-ltorch_cpu", "-ltorch_python", f"-Wl,-rpath,{lib}", "-L", PKG, "-l:libaddrms.so",
+           "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False, extra_defines=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = [(os.path.join(CSRC, "tables.hip"), os.path.join(BUILD, f"tables_{c}.o"),
@@ -48,15 +95,21 @@ def build(verbose: bool = False, extra_defines=()) -> str:
               (f"ADDRMS_COMBO={c}", *extra_defines)) for c in range(4)]
     jobs.append((os.path.join(CSRC, "api.hip"), os.path.join(BUILD, "api.o"),
                  tuple(extra_defines)))
-    workers = min(len(jobs), max(1, min(16, os.cpu_count() or 1)))
+    workers = min(len(jobs) + 1, max(1, min(16, os.cpu_count() or 1)))
+    native_obj = os.path.join(BUILD, "binding.o")
     with cf.ThreadPoolExecutor(workers) as ex:
+        native = ex.submit(_native_compile, native_obj) if _torch_paths() else None
         objs = list(ex.map(lambda j: _compile(*j), jobs))
+        if native is not None:
+            native.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    if native is not None:
+        _native_link(native_obj)
     # the benchmark's stream-ceiling probe: a separate library, never linked
     # into libaddrms.so
     _compile(os.path.join(CSRC, "stream_probe.hip"), os.path.join(BUILD, "stream_probe.o"))
@@ -68,7 +121,7 @@ def build(verbose: bool = False, extra_defines=()) -> str:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
+        print(f"built {LIB}, {PROBE_LIB}" + (" and the native binding" if native else ""))
     return LIB
 
 

@@ -233,7 +233,18 @@ int device_cus_current(int *cus)
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return fail_hip(e);
-    return device_cus(dev, cus);
+    // the last device this thread asked about, without the lock and map
+    thread_local int tl_dev = -1, tl_cus = 0;
+    if (dev == tl_dev) {
+        *cus = tl_cus;
+        return ADDRMS_OK;
+    }
+    const int rc = device_cus(dev, cus);
+    if (rc == ADDRMS_OK) {
+        tl_dev = dev;
+        tl_cus = *cus;
+    }
+    return rc;
 }
 
 // Index of the smallest supported VPL >= need, or -1.
