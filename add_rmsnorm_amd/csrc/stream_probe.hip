@@ -17,8 +17,9 @@
 //     LDS, so a lane keeps more bytes in flight without holding registers);
 //   * a persistent grid whose blocks issue the next chunk's loads before the
 //     current chunk's stores (software pipelining);
-//   * persistent grids with a fixed share of chunks per block, against ones
-//     whose blocks take chunks from a work counter;
+//   * persistent grids with a fixed share of chunks per block (on the grid
+//     that fits at once, or 2 or 4 times it), against ones whose blocks take
+//     chunks from a work counter;
 //   * in-place outputs (the host passes the input buffers as outputs).
 //
 //   int   addrms_probe_count(void);
@@ -259,6 +260,45 @@ __global__ void __launch_bounds__(B) pers_kernel(PArgs a, unsigned *ctr)
     }
 }
 
+// As pers_kernel with QUEUE, but the next chunk's ticket is requested at the
+// start of the current step, so the atomic's round trip overlaps the loads;
+// thread 0 publishes it through LDS at the step's one barrier.  The first
+// chunk of block b is b; tickets count on from gridDim.x.
+template <int NR, int NW, int B, int U>
+__global__ void __launch_bounds__(B) queue2_kernel(PArgs a, unsigned *ctr)
+{
+    __shared__ unsigned slot[2];
+    const size_t chunk = (size_t)B * U;
+    const size_t nchunks = (a.n + chunk - 1) / chunk;
+    size_t c = blockIdx.x;
+    for (int it = 0; c < nchunks; ++it) {
+        unsigned nxt = 0;
+        if (threadIdx.x == 0)
+            nxt = gridDim.x + atomicAdd(ctr, 1u);
+        u32x4 v[U][NR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = c * chunk + threadIdx.x + (size_t)u * B;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                v[u][r] = i < a.n ? __builtin_nontemporal_load(a.in[r] + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (threadIdx.x == 0)
+            slot[it & 1] = nxt;
+        __syncthreads(); // slot[it & 1] is rewritten two steps later, after another barrier
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = c * chunk + threadIdx.x + (size_t)u * B;
+            if (i < a.n) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    __builtin_nontemporal_store(out_val<NR>(v[u], w, i), a.out[w] + i);
+            }
+        }
+        c = slot[it & 1];
+    }
+}
+
 struct Probe {
     const char *name;
     const void *fn;
@@ -266,7 +306,8 @@ struct Probe {
     int per_block; // vectors of each stream per block (chunk)
     int nin, nout;
     bool persistent;
-    bool queue; // needs a zeroed counter
+    bool queue;     // needs a zeroed counter
+    int oversub = 1; // persistent grids: this many times the blocks that fit at once
 };
 
 #define MIX(NR, NW, B, U, LP, SP, NAME) \
@@ -337,6 +378,23 @@ const Probe kProbes[] = {
     PERS(2, 2, 512, 2, true, "r2w2_queue_b512_u2"),
     PERS(3, 1, 512, 2, false, "r3w1_pers_b512_u2"),
     PERS(3, 1, 512, 2, true, "r3w1_queue_b512_u2"),
+    // the fixed share on 2 and 4 times the resident grid (the dispatcher
+    // balances whole blocks), and the work counter with its ticket requested
+    // a step ahead
+    Probe{"r2w1_pers2x_b512_u2", reinterpret_cast<const void *>(&pers_kernel<2, 1, 512, 2, false>),
+          512, 1024, 2, 1, true, false, 2},
+    Probe{"r2w1_pers4x_b512_u2", reinterpret_cast<const void *>(&pers_kernel<2, 1, 512, 2, false>),
+          512, 1024, 2, 1, true, false, 4},
+    Probe{"r2w1_pers4x_b1024_u1", reinterpret_cast<const void *>(&pers_kernel<2, 1, 1024, 1, false>),
+          1024, 1024, 2, 1, true, false, 4},
+    Probe{"r2w1_queue2_b512_u2", reinterpret_cast<const void *>(&queue2_kernel<2, 1, 512, 2>), 512,
+          1024, 2, 1, true, true},
+    Probe{"r2w1_queue2_b256_u4", reinterpret_cast<const void *>(&queue2_kernel<2, 1, 256, 4>), 256,
+          1024, 2, 1, true, true},
+    Probe{"r3w1_queue2_b512_u2", reinterpret_cast<const void *>(&queue2_kernel<3, 1, 512, 2>), 512,
+          1024, 3, 1, true, true},
+    Probe{"r2w2_queue2_b512_u2", reinterpret_cast<const void *>(&queue2_kernel<2, 2, 512, 2>), 512,
+          1024, 2, 2, true, true},
 };
 constexpr int kNumProbes = (int)(sizeof(kProbes) / sizeof(kProbes[0]));
 
@@ -392,7 +450,7 @@ int addrms_probe_run(int id, const void *const *in, void *const *out, size_t byt
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, p.fn, p.block, 0);
         if (e != hipSuccess)
             return (int)e;
-        const size_t cap = (size_t)cus * (size_t)(per_cu > 0 ? per_cu : 1);
+        const size_t cap = (size_t)cus * (size_t)(per_cu > 0 ? per_cu : 1) * (size_t)p.oversub;
         if (blocks > cap)
             blocks = cap;
     }

@@ -138,6 +138,25 @@ def per_call(fn, calls: int, warmup: int = 5) -> dict:
             "p90_us": round(pct(0.9), 3), "mean_us": round(sum(us) / len(us), 3), "calls": calls}
 
 
+def figure(fn, nb: int, calls: int, **extra) -> dict:
+    """One secondary figure: per-call event pairs around `calls` calls of fn
+    (after 5 warm-up calls); GB/s over the algorithmic bytes nb at the median
+    call, and the median, 10th and 90th percentile call times.  Then the same
+    number of calls back to back between one pair of events: for short
+    kernels an event pair per call also times the launch, which back-to-back
+    calls overlap with the previous kernel."""
+    t = per_call(fn, calls, 5)
+    _, ev = timed(fn, calls, 0)
+    gbps = nb / t["median_us"] / 1e3
+    d = {"GBps": round(gbps, 1), "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+         "us_per_call": t["median_us"], "median_us": t["median_us"], "p10_us": t["p10_us"],
+         "p90_us": t["p90_us"], "mean_us": t["mean_us"], "calls": calls,
+         "us_per_call_back_to_back": round(ev / calls * 1e6, 3),
+         "GBps_back_to_back": round(nb * calls / ev / 1e9, 1), "bytes": nb}
+    d.update(extra)
+    return d
+
+
 def _probe_lib():
     import ctypes
     path = os.path.join(ROOT, "add_rmsnorm_amd", "libaddrms_probe.so")
@@ -302,7 +321,7 @@ def headline(steps: int, warmup: int):
 
     log(f"timing {steps} steps after {warmup} warmup")
     wall, ev = timed(step, steps, warmup)
-    return dict(M=M, N=N, eps=eps, nbytes=nbytes, wall=wall, ev=ev, inputs=inp)
+    return dict(M=M, N=N, eps=eps, nbytes=nbytes, wall=wall, ev=ev, inputs=inp, step=step)
 
 
 def traffic_from_profile(nbytes_alg: int):
@@ -362,8 +381,10 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands:
     fetch_b = sum(kf) / len(kf) * f_scale * 1024
     write_b = sum(kw) / len(kw) * w_scale * 1024
     alg_read, alg_write = 4 * 16384 * 7168 + 2 * 7168, 4 * 16384 * 7168
-    st = [r for r in stats if HEADLINE_KERNEL in r["Name"]][0]
-    avg_us = float(st["AverageNs"]) / 1e3
+    # the headline's own dispatches (warm-up and timed steps) come first; the
+    # same kernel also serves the per-call and in-place figures later
+    first = _trace_durations(trace_dir, HEADLINE_KERNEL)[:commands.get("headline_dispatches", 10 ** 9)]
+    avg_us = sum(first) / len(first)
 
     out = [f"# {HEADLINE_KERNEL}: fused Add+RMSNorm, bf16, M=16384 N=7168", "",
            "Kernel trace (rocprofv3 --kernel-trace --stats) of the default bench command:", "",
@@ -384,6 +405,8 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands:
             f"|---|---|---|---|---|",
             f"| read | {sum(kf) / len(kf):.1f} | {fetch_b:.0f} | {alg_read} | {fetch_b / alg_read:.4f} |",
             f"| write | {sum(kw) / len(kw):.1f} | {write_b:.0f} | {alg_write} | {write_b / alg_write:.4f} |",
+            "", f"Kernel average over the headline's {len(first)} dispatches (warm-up and timed "
+                f"steps) in the trace: {avg_us:.2f} us.",
             "", "Values read by bench.py:", "",
             f"- kernel_source_digest: {kernel_source_digest()}",
             f"- traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
@@ -394,6 +417,122 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands:
     log(f"wrote {TRAFFIC_FILE}")
     if counter(fetch, BWD_KERNEL):
         summarize_bwd(stats, fetch, write, f_scale, w_scale, commands)
+    summarize_secondary(trace_dir, fetch, write, f_scale, w_scale, commands)
+
+
+def _following_durations(trace_dir: str, name_part: str, follow: str):
+    """Durations (us) of the first `follow` kernel dispatched after each
+    dispatch of `name_part` (the column reduce that completes a backward)."""
+    rows, _ = _csv_rows(trace_dir, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    out = []
+    for k, r in enumerate(rows):
+        if name_part in r["Kernel_Name"]:
+            nxt = next((q for q in rows[k + 1:] if follow in q["Kernel_Name"]), None)
+            if nxt is not None:
+                out.append((int(nxt["End_Timestamp"]) - int(nxt["Start_Timestamp"])) / 1e3)
+    return out
+
+
+def _trace_durations(trace_dir: str, name_part: str):
+    """Durations (us) of a kernel's dispatches in dispatch order, from a
+    rocprofv3 kernel trace."""
+    rows, _ = _csv_rows(trace_dir, "kernel_trace.csv")
+    rows = [r for r in rows if name_part in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+
+
+# Secondary workloads whose kernels each serve one figure of the bench line:
+# (profile file stem, title, kernel name, follow-up kernel or None,
+#  algorithmic read bytes, algorithmic write bytes)
+def _secondary_specs():
+    B = "addrms::bf16_t"
+    M, N = 16384, 7168
+    m2, n2 = 4096, 4096
+    mb, nbk = 32768, 4096
+    return [
+        ("fwd_vec_kernel_add_rmsnorm_bf16_4096x4096", "fused Add+RMSNorm, bf16, M=4096 N=4096",
+         f"fwd_vec_kernel<{B}, {B}, 0, true, 0, 4, 2>", None, 4 * m2 * n2 + 2 * n2, 4 * m2 * n2),
+        ("fwd_vec_kernel_add_rmsnorm_fp8_row_bf16_16384x7168",
+         "fused Add+RMSNorm with E4M3 output, one scale per row, bf16, M=16384 N=7168",
+         f"fwd_vec_kernel<{B}, {B}, 0, true, 1, 8, 2>", None, 4 * M * N + 2 * N,
+         3 * M * N + 4 * M),
+        ("fwd_vec_kernel_add_rmsnorm_fp8_g128_bf16_16384x7168",
+         "fused Add+RMSNorm with E4M3 output, one scale per 128 columns, bf16, M=16384 N=7168",
+         f"fwd_vec_kernel<{B}, {B}, 0, true, 2, 8, 2>", None, 4 * M * N + 2 * N,
+         3 * M * N + 4 * M * (N // 128)),
+        ("fwd_vec_kernel_add_rmsnorm_mxfp4_bf16_16384x7168",
+         "fused Add+RMSNorm with MXFP4 output, bf16, M=16384 N=7168",
+         f"fwd_vec_kernel<{B}, {B}, 0, true, 3, 8, 2>", None, 4 * M * N + 2 * N,
+         2 * M * N + M * N // 2 + M * (N // 32)),
+        ("fwd_vec_kernel_add_layernorm_bf16_16384x7168",
+         "fused Add+LayerNorm with bias, bf16, M=16384 N=7168",
+         f"fwd_vec_kernel<{B}, {B}, 1, true, 0, 8, 2>", None, 4 * M * N + 4 * N, 4 * M * N),
+        ("bwd_vec_kernel_layernorm_bf16_32768x4096", "LayerNorm backward (dx, dw, db), bf16, "
+         "M=32768 N=4096", f"bwd_vec_kernel<{B}, {B}, 1, false, 2, 4, false, true>",
+         COLREDUCE_KERNEL, 4 * mb * nbk + 8 * mb + 2 * nbk, 2 * mb * nbk + 8 * nbk),
+        ("bwd_vec_kernel_add_rmsnorm_bf16_16384x7168", "fused Add+RMSNorm backward (dh, dw), "
+         "bf16, M=16384 N=7168", f"bwd_vec_kernel<{B}, {B}, 0, true, 8, 2, false, false>",
+         COLREDUCE_KERNEL, 6 * M * N + 4 * M + 2 * N, 2 * M * N + 4 * N),
+    ]
+
+
+def summarize_secondary(trace_dir: str, fetch, write, f_scale: float, w_scale: float,
+                        commands: dict):
+    """One profile summary per secondary workload: its kernel's traced
+    duration in the default bench command, and its HBM bytes per call from the
+    counter runs (the main kernel plus, for the backwards, the column reduce
+    that follows it), against the algorithmic bytes."""
+    def seq(rows, name, follow):
+        rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+        main, red = [], []
+        for k, r in enumerate(rows):
+            if name in r["Kernel_Name"]:
+                main.append(float(r["Counter_Value"]))
+                if follow:
+                    nxt = next((q for q in rows[k + 1:] if follow in q["Kernel_Name"]), None)
+                    red.append(float(nxt["Counter_Value"]) if nxt else 0.0)
+        return main, red
+
+    for stem, title, name, follow, alg_r, alg_w in _secondary_specs():
+        fm, fr = seq(fetch, name, follow)
+        wm, wr = seq(write, name, follow)
+        durs = _trace_durations(trace_dir, name)
+        red = _following_durations(trace_dir, name, follow) if follow else []
+        if not fm or not wm or not durs:
+            log(f"no dispatches of {name}; {stem} not written")
+            continue
+        rd = (sum(fm) / len(fm) + (sum(fr) / len(fr) if fr else 0.0)) * f_scale * 1024
+        wt = (sum(wm) / len(wm) + (sum(wr) / len(wr) if wr else 0.0)) * w_scale * 1024
+        us = sum(durs) / len(durs)
+        srt = sorted(durs)
+        med = srt[len(srt) // 2]
+        out = [f"# {name}: {title}", "",
+               "Kernel trace of the default bench command:", "", f"    {commands['trace']}", "",
+               f"- dispatches: {len(durs)}; average {us:.2f} us, median {med:.2f} us, "
+               f"min {srt[0]:.2f} us, max {srt[-1]:.2f} us",
+               f"- algorithmic bytes {alg_r + alg_w} -> {(alg_r + alg_w) / us / 1e3:.1f} GB/s at "
+               f"the average ({100 * (alg_r + alg_w) / us / 1e3 / HBM_PEAK_GBPS:.1f} % of 8 TB/s), "
+               f"{(alg_r + alg_w) / med / 1e3:.1f} GB/s at the median"]
+        if red:
+            ra = sum(red) / len(red)
+            out.append(f"- the column reduce after each: average {ra:.2f} us; the call "
+                       f"(main kernel + column reduce) {us + ra:.2f} us -> "
+                       f"{(alg_r + alg_w) / (us + ra) / 1e3:.1f} GB/s")
+        out += ["",
+               "HBM traffic per call from the counter runs"
+               + (" (the main kernel plus the column reduce after it)" if follow else "")
+               + ", with the device-copy calibration of the headline summary (FETCH_SIZE x "
+               f"{f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}):", "",
+               f"    {commands['fetch']}", f"    {commands['write']}", "",
+               "| | bytes per call | algorithmic bytes | ratio |", "|---|---|---|---|",
+               f"| read | {rd:.0f} | {alg_r} | {rd / alg_r:.4f} |",
+               f"| write | {wt:.0f} | {alg_w} | {wt / alg_w:.4f} |", ""]
+        path = os.path.join(ROOT, "profiles", stem + ".md")
+        with open(path, "w") as fh:
+            fh.write("\n".join(out))
+        log(f"wrote {path}")
 
 
 def summarize_bwd(stats, fetch, write, f_scale: float, w_scale: float, commands: dict):
@@ -618,7 +757,7 @@ def cpu_baseline_all_cores(inp, M: int, N: int, eps: float, max_threads: int = 1
                       f"rows/s {M / dt:.0f}; {avail} cores available", "cpu": _cpu_model()}
 
 
-def rms_bwd(steps: int):
+def rms_bwd(calls: int):
     """The RMS backward, bf16 32768 x 4096, rstd from the GPU forward."""
     import torch
     import add_rmsnorm_amd as ar
@@ -642,12 +781,9 @@ def rms_bwd(steps: int):
         ar.rmsnorm_bwd(dy, x, w, rstd, dx=dx, dw=dw, workspace=ws)
         i[0] += 1
 
-    _, ev = timed(bstep, steps, 5)
     nb = 6 * M * N + 4 * M + 2 * N + 4 * N
-    out["rmsnorm_bwd_bf16_32768x4096"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
-                                                                       HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb}
+    out["rmsnorm_bwd_bf16_32768x4096"] = figure(bstep, nb, calls,
+                                                note="dx, dw; main kernel + column reduce")
     del sets
     return out
 
@@ -698,13 +834,31 @@ def cpu_baseline_configs(target_s: float = 2.0):
     return out
 
 
-def secondary(steps: int):
-    """Backward, smaller forward shapes and decode latency, same protocol."""
+def secondary(calls: int, profile_run: bool = False):
+    """Backward, quantised and LayerNorm forwards, RMSNorm + RoPE, smaller
+    forward shapes and decode latency: every figure from per-call event
+    pairs over `calls` calls (median, p10, p90)."""
     import torch
     import add_rmsnorm_amd as ar
     import synth
 
-    out = rms_bwd(steps)
+    out = rms_bwd(calls)
+    # the headline forward in place (y over x, residual_out over r), as an
+    # inference engine updates its residual stream
+    inp = synth.workload_inputs(WORKLOAD)
+    M, N = 16384, 7168
+    w = inp["w"].cuda()
+    sets = [(inp["x"].cuda(), inp["r"].cuda()) for _ in range(2)]
+    i = [0]
+
+    def ipstep():
+        x, r = sets[i[0] & 1]
+        ar.add_rmsnorm_fwd(x, r, w, 1e-6, y=x, residual_out=r)
+        i[0] += 1
+
+    out["add_rmsnorm_fwd_bf16_16384x7168_inplace"] = figure(
+        ipstep, 8 * M * N + 2 * N, calls, note="y written over x, residual_out over r")
+    del sets
     i = [0]
     # backward of the fused op at the headline shape: dy, dres, h read; dh written
     M, N = 16384, 7168
@@ -722,13 +876,10 @@ def secondary(steps: int):
         ar.add_rmsnorm_bwd(a, b, hh, w, rstd, dh=dh, dw=dw, workspace=ws)
         i[0] += 1
 
-    _, ev = timed(fbstep, steps, 5)
     nb = 8 * M * N + 4 * M + 2 * N + 4 * N
-    out["add_rmsnorm_bwd_bf16_16384x7168"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
-                                                                       HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
-        "note": "reads dy, d(residual_out), residual_out; writes dh (= dx = dr) and dw"}
+    out["add_rmsnorm_bwd_bf16_16384x7168"] = figure(
+        fbstep, nb, calls,
+        note="reads dy, d(residual_out), residual_out; writes dh (= dx = dr) and dw")
     del sets, ws, h, dy, dres
     # FP8 output: fused Add+RMSNorm at the headline shape writing E4M3 codes
     # and a per-row scale instead of bf16 y
@@ -746,13 +897,9 @@ def secondary(steps: int):
         ar.add_rmsnorm_fwd_fp8(x, r, w, 1e-6, y_fp8=q, y_scale=sc, residual_out=res)
         i[0] += 1
 
-    _, ev = timed(f8, steps, 5)
     nb = 7 * M * N + 4 * M + 2 * N
-    out["add_rmsnorm_fwd_fp8_16384x7168"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
-                                                                       HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
-        "note": "bf16 x, r in; bf16 residual_out + E4M3 y + fp32 per-row scale out"}
+    out["add_rmsnorm_fwd_fp8_16384x7168"] = figure(
+        f8, nb, calls, note="bf16 x, r in; bf16 residual_out + E4M3 y + fp32 per-row scale out")
     # the same with one scale per 128 columns of a row
     sg = [torch.empty(M, N // 128, device="cuda") for _ in range(2)]
 
@@ -762,13 +909,9 @@ def secondary(steps: int):
                                residual_out=res)
         i[0] += 1
 
-    _, ev = timed(f8g, steps, 5)
     nb = 7 * M * N + 4 * M * (N // 128) + 2 * N
-    out["add_rmsnorm_fwd_fp8_g128_16384x7168"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
-                                                                       HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
-        "note": "as above with one fp32 scale per 128 columns (56 per row)"}
+    out["add_rmsnorm_fwd_fp8_g128_16384x7168"] = figure(
+        f8g, nb, calls, note="as above with one fp32 scale per 128 columns (56 per row)")
     # MXFP4: E2M1 codes two per byte, one E8M0 scale byte per 32 values
     mq = [torch.empty(M, N // 2, dtype=torch.uint8, device="cuda") for _ in range(2)]
     ms = [torch.empty(M, N // 32, dtype=torch.uint8, device="cuda") for _ in range(2)]
@@ -779,13 +922,10 @@ def secondary(steps: int):
                                  residual_out=res)
         i[0] += 1
 
-    _, ev = timed(mx, steps, 5)
     nb = 4 * M * N + 2 * M * N + M * N // 2 + M * (N // 32) + 2 * N
-    out["add_rmsnorm_fwd_mxfp4_16384x7168"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
-                                                                       HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb,
-        "note": "bf16 x, r in; bf16 residual_out + MXFP4 y (E2M1 x2 per byte + E8M0 per 32) out"}
+    out["add_rmsnorm_fwd_mxfp4_16384x7168"] = figure(
+        mx, nb, calls,
+        note="bf16 x, r in; bf16 residual_out + MXFP4 y (E2M1 x2 per byte + E8M0 per 32) out")
     del sets, sg, mq, ms
     # LayerNorm: fused forward with bias at the headline shape, backward (dw, db)
     # at the backward workload's shape
@@ -803,12 +943,8 @@ def secondary(steps: int):
         ar.add_layernorm_fwd(x, r, w, b, 1e-5, y=y, residual_out=res)
         i[0] += 1
 
-    _, ev = timed(lnf, steps, 5)
     nb = 8 * M * N + 4 * N
-    out["add_layernorm_fwd_bf16_16384x7168"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
-                                                                       HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb, "note": "with bias"}
+    out["add_layernorm_fwd_bf16_16384x7168"] = figure(lnf, nb, calls, note="with bias")
     del sets
     M, N = 32768, 4096
     inp = synth.workload_inputs("rmsnorm_bwd_bf16_32768x4096")
@@ -826,12 +962,8 @@ def secondary(steps: int):
         ar.layernorm_bwd(dy, x, w, mean, rstd, dx=dx, dw=dw, db=db, workspace=ws)
         i[0] += 1
 
-    _, ev = timed(lnb, steps, 5)
     nb = 6 * M * N + 8 * M + 2 * N + 8 * N
-    out["layernorm_bwd_bf16_32768x4096"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "pct_of_peak": round(100 * nb * steps / ev / 1e9 /
-                                                                       HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "bytes": nb, "note": "dx, dw, db"}
+    out["layernorm_bwd_bf16_32768x4096"] = figure(lnb, nb, calls, note="dx, dw, db")
     del sets, ws
     # per-head RMSNorm + RoPE of the query and key heads, in place on a packed
     # projection buffer: 16384 tokens (4 sequences of 4096), 32 + 8 heads of 128
@@ -850,20 +982,16 @@ def secondary(steps: int):
         ar.rmsnorm_rope_qk(q, k, wq, wk, cos, sin, pos, c["eps"], q_out=q, k_out=k)
         i[0] += 1
 
-    wall, ev = timed(rstep, steps, 5)
-    dev_s = graph_time(rstep, per_graph=30, replays=5)
     npos = int(torch.unique(inp["pos"]).numel())
     # heads read and written; positions; the table rows used (cos and sin,
     # D/2 floats each); both weight vectors
     nb = 4 * T * (Hq + Hk) * D + 8 * T + npos * D * 4 + 2 * D * 2
-    out[name] = {
-        "GBps": round(nb * steps / ev / 1e9, 1),
-        "pct_of_peak": round(100 * nb * steps / ev / 1e9 / HBM_PEAK_GBPS, 1),
-        "us_per_call": round(ev / steps * 1e6, 2), "us_per_call_host": round(wall / steps * 1e6, 2),
-        "GBps_graph": round(nb / dev_s / 1e9, 1), "us_per_call_graph": round(dev_s * 1e6, 2),
-        "bytes": nb,
-        "note": "in place on packed qkv [16384, 48*128]; value heads untouched; 3 rotating sets; "
-                "_graph: device time from replaying captured calls"}
+    dev_s = graph_time(rstep, per_graph=30, replays=5) if not profile_run else None
+    out[name] = figure(
+        rstep, nb, calls, GBps_graph=round(nb / dev_s / 1e9, 1) if dev_s else None,
+        us_per_call_graph=round(dev_s * 1e6, 2) if dev_s else None,
+        note="in place on packed qkv [16384, 48*128]; value heads untouched; 3 rotating sets; "
+             "_graph: device time from replaying captured calls")
     del bufs, views
     # fused forward, 4096 x 4096 bf16 (134 MB: fits in the last-level cache; rotate 4 sets)
     inp = synth.workload_inputs("add_rmsnorm_fwd_bf16_4096x4096")
@@ -877,21 +1005,24 @@ def secondary(steps: int):
         ar.add_rmsnorm_fwd(x, r, w, 1e-6, y=y, residual_out=res)
         i[0] += 1
 
-    _, ev = timed(fstep, steps, 5)
     nb = 8 * M * N + 2 * N
-    out["add_rmsnorm_fwd_bf16_4096x4096"] = {
-        "GBps": round(nb * steps / ev / 1e9, 1), "us_per_call": round(ev / steps * 1e6, 2),
-        "bytes": nb, "note": "4 rotating buffer sets (537 MB)"}
+    out["add_rmsnorm_fwd_bf16_4096x4096"] = figure(fstep, nb, calls,
+                                                   note="4 rotating buffer sets (537 MB)")
     del sets
     # plain fp32 forward 256 x 4096 (8 MB: cache-resident, launch-bound)
     inp = synth.workload_inputs("rmsnorm_fwd_f32_256x4096")
     x, w = inp["x"].cuda(), inp["w"].cuda()
     y = torch.empty_like(x)
-    dev_s = graph_time(lambda: ar.rmsnorm_fwd(x, w, 1e-6, y=y))
+    plain = lambda: ar.rmsnorm_fwd(x, w, 1e-6, y=y)
+    if profile_run:  # counter runs: no graph replays, no decode loop
+        return out
+    dev_s = graph_time(plain)
     nb = 8 * 256 * 4096 + 4 * 4096
-    out["rmsnorm_fwd_f32_256x4096"] = {"GBps": round(nb / dev_s / 1e9, 1),
-                                       "us_per_call_device": round(dev_s * 1e6, 2), "bytes": nb,
-                                       "note": "cache-resident; device time from graph replay"}
+    out["rmsnorm_fwd_f32_256x4096"] = figure(
+        plain, nb, calls, GBps_graph=round(nb / dev_s / 1e9, 1),
+        us_per_call_graph=round(dev_s * 1e6, 2),
+        note="cache-resident, launch-bound: the event pairs time each eagerly launched call; "
+             "_graph: device time per call replaying a captured graph of 50 calls")
     # decode: N = 8192, fp32 w, M in {1, 8, 32, 128, 512}: device time per call
     # (replay of a captured graph of calls) and host wall time per eager call
     dec = {}
@@ -901,12 +1032,17 @@ def secondary(steps: int):
         y, res = torch.empty_like(x), torch.empty_like(x)
         call = lambda: ar.add_rmsnorm_fwd(x, r, w, 1e-5, y=y, residual_out=res)
         dev_s = graph_time(call)
-        n = max(steps, 200)
+        n = max(calls, 200)
         wall, _ = timed(call, n, 20)
         nb = 8 * M * 8192 + 4 * 8192
+        t = per_call(call, calls, 5)
         dec[str(M)] = {"us_per_call_device": round(dev_s * 1e6, 2),
                        "us_per_call_host": round(wall / n * 1e6, 2),
-                       "GBps_device": round(nb / dev_s / 1e9, 1), "bytes": nb}
+                       "GBps_device": round(nb / dev_s / 1e9, 1), "bytes": nb,
+                       "event_pair_median_us": t["median_us"], "event_pair_p10_us": t["p10_us"],
+                       "event_pair_p90_us": t["p90_us"], "calls": calls}
+    dec["binding"] = "native" if ar.add_rmsnorm_fwd is getattr(ar.native, "add_rmsnorm_fwd", 0) \
+        else "ctypes"
     out["add_rmsnorm_fwd_bf16_decode_n8192"] = dec
     return out
 
@@ -919,6 +1055,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true",
                     help="skip the secondary figures (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="for counter runs: secondary figures over 6 calls each, without graph "
+                         "replays or the decode loop")
     ap.add_argument("--with-rms-bwd", action="store_true",
                     help="with --only-headline: also time the RMS backward (for counter runs)")
     ap.add_argument("--probe-matrix", action="store_true",
@@ -971,6 +1110,9 @@ def main():
     achieved = nb * args.steps / h["ev"] / 1e9  # per-launch average from the events
     log(f"fused fwd: {achieved:.1f} GB/s ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s), "
         f"{h['ev'] / args.steps * 1e6:.2f} us per launch")
+    per_call_dist = figure(h["step"], nb, max(100, args.steps))
+    log(f"fused fwd per call: median {per_call_dist['median_us']} us, p10 {per_call_dist['p10_us']}, "
+        f"p90 {per_call_dist['p90_us']}")
     log("copy-kernel and stream ceilings")
     copy = copy_ceiling(nb)
     stream = stream_ceiling(nb)
@@ -997,6 +1139,7 @@ def main():
         "pct_of_copy_ceiling": round(100 * gbps / copy, 1),
         "stream_2r2w_ceiling_GBps": round(stream, 1) if stream else None,
         "pct_of_stream_ceiling": round(100 * gbps / stream, 1) if stream else None,
+        "per_call": per_call_dist,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
@@ -1012,9 +1155,10 @@ def main():
     del h
     if not args.only_headline:
         log("secondary figures")
-        rec["secondary"] = secondary(min(args.steps, 100))
+        rec["secondary"] = (secondary(6, profile_run=True) if args.profile_run
+                            else secondary(max(100, args.steps)))
     elif args.with_rms_bwd:
-        rec["secondary"] = rms_bwd(args.steps)
+        rec["secondary"] = rms_bwd(max(100, args.steps))
     print(json.dumps(rec), flush=True)
 
 

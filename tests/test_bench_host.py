@@ -60,7 +60,14 @@ def test_summaries_scale_counters_and_pair_the_column_reduce(tmp_path, monkeypat
              {"Name": bwd, "Calls": 2, "TotalDurationNs": 274000, "AverageNs": 137000.0,
               "MinNs": 136000, "MaxNs": 138000, "Percentage": 45.0}]
     _write(str(tmp_path / "t" / "x_kernel_stats.csv"), stats, list(stats[0].keys()))
-    cmds = {"trace": "T", "fetch": "F", "write": "W"}
+    # per-dispatch trace: the headline's two dispatches (149 and 151 us), then
+    # a later use of the same kernel (a per-call or in-place figure) that the
+    # headline's average must leave out
+    trace = [{"Dispatch_Id": k + 1, "Kernel_Name": head, "Start_Timestamp": 1000 * k * 1000,
+              "End_Timestamp": 1000 * k * 1000 + d}
+             for k, d in enumerate((149000, 151000, 400000))]
+    _write(str(tmp_path / "t" / "x_kernel_trace.csv"), trace, list(trace[0].keys()))
+    cmds = {"trace": "T", "fetch": "F", "write": "W", "headline_dispatches": 2}
     bench.summarize_profiles(str(tmp_path / "t"), str(tmp_path / "f"), str(tmp_path / "w"), cmds)
 
     fwd = (tmp_path / "fwd.md").read_text()
