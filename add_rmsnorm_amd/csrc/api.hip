@@ -266,9 +266,17 @@ int vpl_index(int need)
 // (fused 6.0-6.1 against 5.8-5.9 TB/s; the E4M3 and MXFP4 outputs, with a
 // second row reduction or more registers, 5.7-6.2 against 4.5-5.1).  When
 // there are too few rows to give every SIMD a wave, rows get more waves
-// still.  qm (a quantised mode, or kQNone) restricts the choice to built
-// variants of that mode.  ADDRMS_FWD_WPR forces a WPR when it is built.
-bool pick_fwd(int64_t M, int nvec, int cus, int qm, int *wi_out, int *vi_out)
+// still.  One exception: the fused Add+RMSNorm with a plain output, 641 to
+// 1024 vectors a row and at least 8 rows per CU takes 16 waves of one vector
+// a lane rather than 8 of two (measured on MI355X, bf16, 16384 rows: 5120 to
+// 8192 columns 1-2 % faster, 4608 columns 1 % slower; 2048 to 8192 rows of
+// 7168 2-5 % faster, 512 rows 17 % slower; float32 16384 x 4096 1 % faster).
+// With 16 waves the plain RMSNorm is 3-29 % slower, and LayerNorm and the
+// E4M3 and MXFP4 outputs 2-18 %, so they keep 8.  qm (a quantised mode, or
+// kQNone) restricts the choice to built variants of that mode.
+// ADDRMS_FWD_WPR forces a WPR when it is built.
+bool pick_fwd(int64_t M, int nvec, int cus, int norm, bool fused, int qm, int *wi_out,
+              int *vi_out)
 {
     const int forced = knob(ADDRMS_KNOB_FWD_WPR);
     const int env_vpl = knob(ADDRMS_KNOB_FWD_VPL);
@@ -282,6 +290,14 @@ bool pick_fwd(int64_t M, int nvec, int cus, int qm, int *wi_out, int *vi_out)
     if (forced > 0)
         for (int wi = 0; wi < kNumWpr; ++wi)
             if (kWprList[wi] == forced && ok(wi)) {
+                *wi_out = wi;
+                *vi_out = vpl_index(need_of(wi));
+                return true;
+            }
+    if (norm == kRms && fused && qm == kQNone && env_vpl <= 0 && nvec > 640 && nvec <= 1024 &&
+        M >= 8LL * cus)
+        for (int wi = 0; wi < kNumWpr; ++wi)
+            if (kWprList[wi] == 16 && ok(wi)) {
                 *wi_out = wi;
                 *vi_out = vpl_index(need_of(wi));
                 return true;
@@ -525,7 +541,8 @@ int fwd_common(int norm, const void *x, const void *r, const void *w, const void
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
         return rc;
     int wi = 0, vi = 0;
-    if (vec_ok && pick_fwd(M, (int)(N / nv), cus, q8 ? qm + 1 : (int)kQNone, &wi, &vi) &&
+    if (vec_ok &&
+        pick_fwd(M, (int)(N / nv), cus, norm, fused, q8 ? qm + 1 : (int)kQNone, &wi, &vi) &&
         (!q8 || tab.vec_q8[fused ? 1 : 0][qm][wi][vi].fn != nullptr)) {
         a.nvec = (int)(N / nv);
         const KernelRef &k =

@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, bf16 fused Add+RMSNorm M=16384 N=7168"
 WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
-HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 0, 8, 2>"
+HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 0, 16, 1>"
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_vec_kernel_rmsnorm_bf16_32768x4096.md")
 BWD_KERNEL = "bwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, false, 2, 4, false, true>"
 COLREDUCE_KERNEL = "dw_colreduce_vec_kernel"
@@ -155,6 +155,110 @@ def figure(fn, nb: int, calls: int, **extra) -> dict:
          "GBps_back_to_back": round(nb * calls / ev / 1e9, 1), "bytes": nb}
     d.update(extra)
     return d
+
+
+ROW_SWEEP_N = (4096, 7168)
+ROW_SWEEP_M = (512, 1024, 2048, 4096, 8192, 16384)
+ROW_SWEEP_CALLS = 100
+ROW_SWEEP_WARMUP = 5
+
+
+def row_sweep(calls: int = ROW_SWEEP_CALLS) -> dict:
+    """The fused bf16 forward at fixed widths over a range of row counts, in
+    the order ROW_SWEEP_N x ROW_SWEEP_M, ROW_SWEEP_WARMUP + `calls` calls
+    each; enough rotating input/output sets that the calls of one shape
+    stream at least 1 GB (never from the 256 MB last-level cache).  Per-call
+    event pairs per shape, and the least-squares line t = t0 + bytes / B over
+    the medians: B is the marginal stream rate, t0 the fixed cost of a launch
+    (the ramp to a full device and the tail of the last blocks)."""
+    import numpy as np
+    import torch
+    import add_rmsnorm_amd as ar
+    import synth
+    out = {}
+    for N in ROW_SWEEP_N:
+        pts = []
+        for M in ROW_SWEEP_M:
+            inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=1, r_std=0.5)
+            w = inp["w"].cuda()
+            x0, r0 = inp["x"].cuda(), inp["r"].cuda()
+            nb = 8 * M * N + 2 * N
+            nsets = max(2, min(64, -(-(1 << 30) // nb)))
+            sets = [(x0.clone(), r0.clone(), torch.empty_like(x0), torch.empty_like(x0))
+                    for _ in range(nsets)]
+            i = [0]
+
+            def step():
+                x, r, y, ro = sets[i[0] % nsets]
+                ar.add_rmsnorm_fwd(x, r, w, 1e-6, y=y, residual_out=ro)
+                i[0] += 1
+
+            t = per_call(step, calls, ROW_SWEEP_WARMUP)
+            out[f"{M}x{N}"] = dict(t, bytes=nb, GBps=round(nb / t["median_us"] / 1e3, 1),
+                                   sets=nsets)
+            pts.append((nb, t["median_us"]))
+            log(f"row sweep {M}x{N}: median {t['median_us']} us")
+            del sets, x0, r0
+            torch.cuda.empty_cache()
+        b, a = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
+        out[f"fit_N{N}"] = {"t0_us": round(float(a), 3), "marginal_GBps": round(1e-3 / float(b), 1)}
+    return out
+
+
+def summarize_row_sweep(trace_dir: str, out_path: str, commands: dict):
+    """Profile summary of a traced --row-sweep run: the fused forward's traced
+    durations grouped by shape (dispatches in the sweep's order, one group
+    per shape, the warm-up calls dropped), the median per shape, and per
+    width the least-squares line t = t0 + bytes / B over those medians."""
+    import numpy as np
+    rows, _ = _csv_rows(trace_dir, "kernel_trace.csv")
+    rows = [r for r in rows if "fwd_vec_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    per = ROW_SWEEP_WARMUP + ROW_SWEEP_CALLS
+    shapes = [(M, N) for N in ROW_SWEEP_N for M in ROW_SWEEP_M]
+    if len(rows) != per * len(shapes):
+        raise SystemExit(f"expected {per * len(shapes)} forward dispatches, found {len(rows)}")
+    lines = ["# Fused Add+RMSNorm forward, bf16: launch time against rows",
+             "",
+             "Traced kernel durations of the fused forward over a range of row counts at",
+             "two widths, and per width the least-squares line t = t0 + bytes / B over",
+             "the medians: B is the marginal stream rate of one more row, t0 the fixed",
+             "cost of a launch (the ramp to a full device plus the tail of the last",
+             "blocks).  Bytes are the algorithmic 8 M N + 2 N.",
+             "",
+             "Commands:", ""]
+    for k, v in commands.items():
+        lines.append(f"- {k}: `{v}`")
+    lines += [""]
+    for N in ROW_SWEEP_N:
+        lines += [f"## N = {N}", "",
+                  "| M | kernel | blocks x threads | median us | p10 us | p90 us | GB/s | fit us |",
+                  "|---|---|---|---|---|---|---|---|"]
+        pts = []
+        info = []
+        for k, (M, NN) in enumerate(shapes):
+            if NN != N:
+                continue
+            grp = rows[k * per + ROW_SWEEP_WARMUP:(k + 1) * per]
+            d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+            med, p10, p90 = d[len(d) // 2], d[int(0.1 * (len(d) - 1))], d[int(0.9 * (len(d) - 1))]
+            wg = int(grp[0]["Workgroup_Size_X"])
+            blocks = int(grp[0]["Grid_Size_X"]) // wg
+            name = grp[0]["Kernel_Name"]
+            targs = name[name.find("<") + 1:name.rfind(">")].split(",")
+            nb = 8 * M * N + 2 * N
+            pts.append((nb, med))
+            info.append((M, f"WPR {targs[-2].strip()}, VPL {targs[-1].strip()}", blocks, wg,
+                         med, p10, p90, nb))
+        b, a = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
+        for M, kern, blocks, wg, med, p10, p90, nb in info:
+            lines.append(f"| {M} | {kern} | {blocks} x {wg} | {med:.2f} | {p10:.2f} | {p90:.2f} | "
+                         f"{nb / med / 1e3:.0f} | {a + b * nb:.2f} |")
+        lines += ["", f"Fit: t0 = {a:.2f} us, B = {1e-3 / b:.0f} GB/s "
+                      f"({100e-3 / b / HBM_PEAK_GBPS:.1f} % of 8 TB/s).", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out_path}")
 
 
 def _probe_lib():
@@ -1064,6 +1168,11 @@ def main():
                     help="time every stream probe over the headline's byte count, print one "
                          "JSON line and exit")
     ap.add_argument("--probe-calls", type=int, default=30)
+    ap.add_argument("--row-sweep", action="store_true",
+                    help="time the fused forward over a range of row counts at two widths, "
+                         "print one JSON line and exit")
+    ap.add_argument("--summarize-row-sweep", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                    help="write the row-sweep profile summary from a traced --row-sweep run")
     ap.add_argument("--probe-only", default="",
                     help="comma-separated probe names for --probe-matrix (default: all)")
     ap.add_argument("--summarize-probes", nargs=2, metavar=("TIMING_JSON", "OUT_DIR"),
@@ -1084,6 +1193,9 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, commands=json.loads(args.profile_commands))
         return
+    if args.summarize_row_sweep:
+        summarize_row_sweep(*args.summarize_row_sweep, commands=json.loads(args.profile_commands))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: rows are independent, so more GPUs would each "
               "run this kernel on their own row block with no exchange; run with --gpus 1",
@@ -1102,6 +1214,11 @@ def main():
             res.update(fused_fwd_inplace_compare(args.probe_calls))
         print(json.dumps({"probe_matrix": res, "bytes_each_stream": each,
                           "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
+
+    if args.row_sweep:
+        print(json.dumps({"row_sweep": row_sweep(), "device": torch.cuda.get_device_name(0)}),
+              flush=True)
         return
 
     h = headline(args.steps, args.warmup)
@@ -1143,8 +1260,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "fwd_vec_kernel<bf16_t, bf16_t, kRms, fused, bf16 out, 8, 2> (8 waves/row, "
-                               "2 x 16 B per lane and tensor, one row per block)",
+                     "kernel": "fwd_vec_kernel<bf16_t, bf16_t, kRms, fused, bf16 out, 16, 1> (16 waves/row, "
+                               "one 16 B vector per lane and tensor, one row per block)",
                      "avg_launch_us": round(h["ev"] / args.steps * 1e6, 3)},
     }
     if not args.no_cpu_baseline:

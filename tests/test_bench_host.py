@@ -87,3 +87,30 @@ def test_oracle_baselines_of_the_other_workloads():
     for name, r in out.items():
         assert 1 <= r["rows"] <= r["of_rows"] and r["rows_per_s"] > 0 and r["GBps"] > 0, name
         assert r["cores"] == 1
+
+
+def test_row_sweep_summary_recovers_the_line(tmp_path):
+    """Synthetic trace: every dispatch of shape (M, N) lasts t0 + bytes / B
+    (warm-up calls 3 us slower, with copies interleaved); the summary must
+    drop the warm-up calls and recover t0 and B."""
+    t0, B = 1.7, 6200.0  # us, GB/s
+    rows, did, ts = [], 0, 10_000_000
+    name = ("void addrms::fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 0, 16, 1>"
+            "(addrms::FwdArgs)")
+    for N in bench.ROW_SWEEP_N:
+        for M in bench.ROW_SWEEP_M:
+            nb = 8 * M * N + 2 * N
+            for k in range(bench.ROW_SWEEP_WARMUP + bench.ROW_SWEEP_CALLS):
+                us = t0 + nb / B / 1e3 + (3.0 if k < bench.ROW_SWEEP_WARMUP else 0.0)
+                for kname, dur in (("__amd_rocclr_copyBuffer", 1.0), (name, us)):
+                    did += 1
+                    rows.append({"Dispatch_Id": did, "Kernel_Name": kname, "Start_Timestamp": ts,
+                                 "End_Timestamp": ts + int(round(dur * 1e3)),
+                                 "Workgroup_Size_X": 1024, "Grid_Size_X": 1024 * M})
+                    ts += 1_000_000
+    _write(str(tmp_path / "t" / "rows_kernel_trace.csv"), rows, list(rows[0].keys()))
+    out = str(tmp_path / "rows.md")
+    bench.summarize_row_sweep(str(tmp_path / "t"), out, {"trace": "rocprofv3 ... --row-sweep"})
+    text = open(out).read()
+    assert text.count(f"Fit: t0 = {t0:.2f} us, B = {B:.0f} GB/s") == len(bench.ROW_SWEEP_N)
+    assert "| 16384 | WPR 16, VPL 1 | 16384 x 1024 |" in text
