@@ -817,9 +817,10 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(inp, M: int, N: int, eps: float, target_s: float = 12.0):
+def cpu_baseline(inp, M: int, N: int, eps: float, target_s: float = 6.0, passes: int = 3):
     """The CPU oracle (single-threaded plain C, binary64) on the first rows of
-    the same inputs; the row count is sized for about target_s seconds."""
+    the same inputs, the median of `passes` passes; the row count is sized
+    for about target_s seconds a pass (all M rows when they fit)."""
     import oracle
     x, r, w = inp["x"], inp["r"], inp["w"]
     probe = 256
@@ -827,14 +828,18 @@ def cpu_baseline(inp, M: int, N: int, eps: float, target_s: float = 12.0):
     oracle.add_rmsnorm_fwd(x[:probe], r[:probe], w, eps)
     per_row = (time.perf_counter() - t0) / probe
     rows = int(min(M, max(probe, target_s / max(per_row, 1e-9))))
-    log(f"cpu baseline: oracle on {rows} rows (~{rows * per_row:.1f} s)")
-    t0 = time.perf_counter()
-    oracle.add_rmsnorm_fwd(x[:rows], r[:rows], w, eps)
-    dt = time.perf_counter() - t0
+    log(f"cpu baseline: oracle on {rows} rows, {passes} passes (~{rows * per_row:.1f} s each)")
+    times = []
+    for _ in range(passes):
+        t0 = time.perf_counter()
+        oracle.add_rmsnorm_fwd(x[:rows], r[:rows], w, eps)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     nbytes = 8 * rows * N + 2 * N
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {M} rows of the same inputs, one pass, "
-                      f"{dt:.1f} s; rows/s {rows / dt:.0f}", "cpu": _cpu_model()}
+            "sample": f"first {rows} of {M} rows of the same inputs, median of {passes} passes "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s); rows/s {rows / dt:.0f}",
+            "cpu": _cpu_model()}
 
 
 def cpu_baseline_all_cores(inp, M: int, N: int, eps: float, max_threads: int = 16):
@@ -850,15 +855,20 @@ def cpu_baseline_all_cores(inp, M: int, N: int, eps: float, max_threads: int = 1
         avail = os.cpu_count() or 1
     n = max(1, min(avail, max_threads))
     bounds = [(k * M // n, (k + 1) * M // n) for k in range(n)]
-    log(f"cpu baseline: oracle on all {M} rows in {n} threads")
-    t0 = time.perf_counter()
+    log(f"cpu baseline: oracle on all {M} rows in {n} threads, 3 passes")
+    times = []
     with cf.ThreadPoolExecutor(n) as ex:
-        list(ex.map(lambda b: oracle.add_rmsnorm_fwd(x[b[0]:b[1]], r[b[0]:b[1]], w, eps), bounds))
-    dt = time.perf_counter() - t0
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(lambda b: oracle.add_rmsnorm_fwd(x[b[0]:b[1]], r[b[0]:b[1]], w, eps),
+                        bounds))
+            times.append(time.perf_counter() - t0)
+    dt = sorted(times)[1]
     nbytes = 8 * M * N + 2 * N
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
-            "sample": f"all {M} rows in {n} row slices, one pass, {dt:.2f} s; "
-                      f"rows/s {M / dt:.0f}; {avail} cores available", "cpu": _cpu_model()}
+            "sample": f"all {M} rows in {n} row slices, median of 3 passes "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s); rows/s {M / dt:.0f}; "
+                      f"{avail} cores available (sched_getaffinity)", "cpu": _cpu_model()}
 
 
 def rms_bwd(calls: int):
@@ -892,10 +902,11 @@ def rms_bwd(calls: int):
     return out
 
 
-def cpu_baseline_configs(target_s: float = 2.0):
+def cpu_baseline_configs(target_s: float = 1.0):
     """The oracle (single-threaded, unchanged) on each of the other workloads:
-    a bounded sample of rows (all rows when they fit in about target_s),
-    rows/s and GB/s over the same algorithmic bytes as the GPU figures."""
+    a bounded sample of rows (all rows when they fit in about target_s), the
+    median of 3 passes, rows/s and GB/s over the same algorithmic bytes as
+    the GPU figures."""
     import oracle
     import synth
     out = {}
@@ -906,10 +917,13 @@ def cpu_baseline_configs(target_s: float = 2.0):
         fn(probe)
         per_row = (time.perf_counter() - t0) / probe
         rows = int(min(M, max(probe, target_s / max(per_row, 1e-9))))
-        t0 = time.perf_counter()
-        fn(rows)
-        dt = time.perf_counter() - t0
-        out[name] = {"rows": rows, "of_rows": M, "seconds": round(dt, 3),
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn(rows)
+            times.append(time.perf_counter() - t0)
+        dt = sorted(times)[1]
+        out[name] = {"rows": rows, "of_rows": M, "seconds": round(dt, 3), "passes": 3,
                      "rows_per_s": round(rows / dt, 1),
                      "GBps": round((per_row_bytes * rows + once_bytes) / dt / 1e9, 4), "cores": 1}
 
