@@ -35,6 +35,11 @@
 //     chunks from a work counter (needs_counter); ignored by the others.
 //     Returns the hipError_t of the launch (0 on success), or
 //     hipErrorInvalidValue for bad arguments.
+//   int   addrms_probe_floor(int kind, const void *in, void *out, void *stream);
+//     The launch floor of a one-row call (the decode shapes): kind 0, an empty
+//     kernel of one 64-thread block; kind 1, one 1024-thread block that copies
+//     16 KiB (one 16-byte vector a thread) from in to out, each of at least
+//     16 KiB.  Same return convention.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -400,7 +405,31 @@ constexpr int kNumProbes = (int)(sizeof(kProbes) / sizeof(kProbes[0]));
 
 } // namespace
 
+__global__ void __launch_bounds__(64) floor_empty_kernel() {}
+
+__global__ void __launch_bounds__(1024) floor_row_kernel(const u32x4 *in, u32x4 *out)
+{
+    out[threadIdx.x] = __builtin_nontemporal_load(in + threadIdx.x);
+}
+
 extern "C" {
+
+int addrms_probe_floor(int kind, const void *in, void *out, void *stream)
+{
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (kind == 0) {
+        void *argv[] = {nullptr};
+        return (int)hipLaunchKernel(reinterpret_cast<const void *>(&floor_empty_kernel), dim3(1),
+                                    dim3(64), argv, 0, s);
+    }
+    if (kind != 1 || !in || !out)
+        return (int)hipErrorInvalidValue;
+    const u32x4 *pi = static_cast<const u32x4 *>(in);
+    u32x4 *po = static_cast<u32x4 *>(out);
+    void *argv[] = {&pi, &po};
+    return (int)hipLaunchKernel(reinterpret_cast<const void *>(&floor_row_kernel), dim3(1),
+                                dim3(1024), argv, 0, s);
+}
 
 int addrms_probe_count(void) { return kNumProbes; }
 

@@ -276,7 +276,30 @@ def _probe_lib():
     lib.addrms_probe_run.restype = ctypes.c_int
     lib.addrms_probe_run.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                      ctypes.c_size_t, vp, vp]
+    lib.addrms_probe_floor.restype = ctypes.c_int
+    lib.addrms_probe_floor.argtypes = [ctypes.c_int, vp, vp, vp]
     return lib
+
+
+def launch_floor() -> dict:
+    """Device time per call, replaying a captured graph of 50 calls, of an
+    empty one-block kernel and of one 1024-thread block copying 16 KiB: the
+    floor under a one-row call."""
+    import torch
+    lib = _probe_lib()
+    if lib is None:
+        return {}
+    a = torch.zeros(16384, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for kind, name in ((0, "empty_kernel_us"), (1, "row_copy_16KiB_us")):
+        def call(kind=kind):
+            rc = lib.addrms_probe_floor(kind, a.data_ptr(), b.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"addrms_probe_floor({kind}) failed: hipError {rc}")
+        out[name] = round(graph_time(call) * 1e6, 3)
+    return out
 
 
 # 2R2W probes that also run in place (outputs = inputs)
@@ -1161,6 +1184,7 @@ def secondary(calls: int, profile_run: bool = False):
                        "event_pair_p90_us": t["p90_us"], "calls": calls}
     dec["binding"] = "native" if ar.add_rmsnorm_fwd is getattr(ar.native, "add_rmsnorm_fwd", 0) \
         else "ctypes"
+    dec["launch_floor"] = launch_floor()
     out["add_rmsnorm_fwd_bf16_decode_n8192"] = dec
     return out
 
