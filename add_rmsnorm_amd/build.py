@@ -7,7 +7,8 @@ Compiles csrc/tables.hip and csrc/rope.hip once per (row dtype, weight dtype)
 combination and csrc/api.hip, in parallel, then links one shared library next
 to this file.  The native Python binding of the latency-bound forwards
 (csrc/binding.cpp, host C++ against torch's headers) is compiled in the same
-pool and linked against that library as _native*.so.
+pool and linked against that library as _native*.so.  The plain C client
+that the GPU tests run (tests/c_client) is linked against it too.
 """
 from __future__ import annotations
 
@@ -87,6 +88,25 @@ def _native_link(obj: str) -> str:
     return out
 
 
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "addrms_client.c")
+CLIENT = os.path.join(ROOT, "tests", "c_client", "addrms_client")
+
+
+def _client_build() -> str:
+    """The plain C client of the library that the GPU tests run (host code
+    against the HIP runtime and libaddrms.so, found by a relative rpath)."""
+    tmp = CLIENT + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+           "-I", os.path.join(ROOT, "include"), CLIENT_SRC, "-o", tmp, "-L", PKG, "-l:libaddrms.so",
+           "-Wl,-rpath,$ORIGIN/../../add_rmsnorm_amd", "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CLIENT)
+    return CLIENT
+
+
 def build(verbose: bool = False, extra_defines=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = [(os.path.join(CSRC, "tables.hip"), os.path.join(BUILD, f"tables_{c}.o"),
@@ -110,6 +130,8 @@ def build(verbose: bool = False, extra_defines=()) -> str:
     os.replace(tmp, LIB)
     if native is not None:
         _native_link(native_obj)
+    if os.path.exists(CLIENT_SRC):
+        _client_build()
     # the benchmark's stream-ceiling probe: a separate library, never linked
     # into libaddrms.so
     _compile(os.path.join(CSRC, "stream_probe.hip"), os.path.join(BUILD, "stream_probe.o"))
