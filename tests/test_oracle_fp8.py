@@ -54,7 +54,8 @@ def test_matches_torch_float8_e4m3fn_where_torch_is_in_range():
     with np.errstate(invalid="ignore"):
         keep = np.isnan(f) | (np.abs(f) < 464.0)
     f = f[keep]
-    ours = oracle.fp8e4m3_encode(f.astype(np.float64))
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns raise the flag when widened
+        ours = oracle.fp8e4m3_encode(f.astype(np.float64))
     ref = torch.from_numpy(f.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     nan = np.isnan(f)
     assert np.all((ours[nan] & 0x7F) == 0x7F)
