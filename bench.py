@@ -545,6 +545,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, commands:
     if counter(fetch, BWD_KERNEL):
         summarize_bwd(stats, fetch, write, f_scale, w_scale, commands)
     summarize_secondary(trace_dir, fetch, write, f_scale, w_scale, commands)
+    summarize_decode(trace_dir, commands)
 
 
 def _following_durations(trace_dir: str, name_part: str, follow: str):
@@ -660,6 +661,53 @@ def summarize_secondary(trace_dir: str, fetch, write, f_scale: float, w_scale: f
         with open(path, "w") as fh:
             fh.write("\n".join(out))
         log(f"wrote {path}")
+
+
+DECODE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, float, 0, true, 0, "
+DECODE_N = 8192
+
+
+def summarize_decode(trace_dir: str, commands: dict):
+    """Profile summary of the decode workload (bf16 rows of 8192 with float32
+    weights, the only workload of the bench with float32 weights): the traced
+    kernel durations per batch size M, which the trace gives as the number of
+    one-row blocks; kernel execution only, without the launch."""
+    rows, _ = _csv_rows(trace_dir, "kernel_trace.csv")
+    by_m = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if DECODE_KERNEL not in name:
+            continue
+        M = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+        targs = name[name.find("<") + 1:name.rfind(">")].split(",")
+        kern = f"WPR {targs[-2].strip()}, VPL {targs[-1].strip()}"
+        by_m.setdefault(M, (kern, []))[1].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if not by_m:
+        log("no decode dispatches in the trace; decode summary not written")
+        return
+    out = [f"# fwd_vec_kernel (bf16 rows, float32 weights): decode-shaped fused Add+RMSNorm, "
+           f"N={DECODE_N}", "",
+           "Kernel trace of the default bench command (eager calls and graph replays alike):",
+           "", f"    {commands['trace']}", "",
+           "Traced kernel execution per call, by batch size (one row per block); the bench "
+           "line's decode entry gives the device time per call in a graph replay, the host "
+           "time per eager call and the launch floor beside it.  Bytes: 8 M N + 4 N "
+           "(x, r read; y, residual_out written; float32 w).  The counter runs skip this "
+           "loop: at these sizes the bytes are the launch's, not a stream's.", "",
+           "| M | kernel | dispatches | median us | p10 us | p90 us | GB/s at the median |",
+           "|---|---|---|---|---|---|---|"]
+    for M in sorted(by_m):
+        kern, d = by_m[M]
+        d = sorted(d)
+        med, p10, p90 = d[len(d) // 2], d[int(0.1 * (len(d) - 1))], d[int(0.9 * (len(d) - 1))]
+        nb = 8 * M * DECODE_N + 4 * DECODE_N
+        out.append(f"| {M} | {kern} | {len(d)} | {med:.2f} | {p10:.2f} | {p90:.2f} | "
+                   f"{nb / med / 1e3:.1f} |")
+    path = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_f32w_decode_n8192.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    log(f"wrote {path}")
 
 
 def summarize_bwd(stats, fetch, write, f_scale: float, w_scale: float, commands: dict):
