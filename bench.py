@@ -161,6 +161,8 @@ ROW_SWEEP_N = (4096, 7168)
 ROW_SWEEP_M = (512, 1024, 2048, 4096, 8192, 16384)
 ROW_SWEEP_CALLS = 100
 ROW_SWEEP_WARMUP = 5
+ROW_SWEEP_PROBE = "r2w2_b1024_u1"       # the 2R2W probe timed beside each shape
+ROW_SWEEP_PROBE_KERNEL = "mix_kernel<2, 2, 1024, 1,"
 
 
 def row_sweep(calls: int = ROW_SWEEP_CALLS) -> dict:
@@ -170,14 +172,23 @@ def row_sweep(calls: int = ROW_SWEEP_CALLS) -> dict:
     stream at least 1 GB (never from the 256 MB last-level cache).  Per-call
     event pairs per shape, and the least-squares line t = t0 + bytes / B over
     the medians: B is the marginal stream rate, t0 the fixed cost of a launch
-    (the ramp to a full device and the tail of the last blocks)."""
+    (the ramp to a full device and the tail of the last blocks).  After each
+    shape, the 2-read/2-write stream probe ROW_SWEEP_PROBE over the same
+    buffers, the same number of calls, and its own line: the launch cost of
+    streaming alone."""
     import numpy as np
     import torch
     import add_rmsnorm_amd as ar
     import synth
+    import ctypes
+    lib = _probe_lib()
+    pid = None
+    if lib is not None:
+        names = [lib.addrms_probe_name(k).decode() for k in range(lib.addrms_probe_count())]
+        pid = names.index(ROW_SWEEP_PROBE)
     out = {}
     for N in ROW_SWEEP_N:
-        pts = []
+        pts, ppts = [], []
         for M in ROW_SWEEP_M:
             inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=1, r_std=0.5)
             w = inp["w"].cuda()
@@ -198,33 +209,68 @@ def row_sweep(calls: int = ROW_SWEEP_CALLS) -> dict:
                                    sets=nsets)
             pts.append((nb, t["median_us"]))
             log(f"row sweep {M}x{N}: median {t['median_us']} us")
+            # the 2-read/2-write stream probe over the same buffers: the
+            # launch cost of pure streaming at this size
+            if lib is not None:
+                vp = ctypes.c_void_p
+                pargs = [((vp * 3)(x.data_ptr(), r.data_ptr(), None),
+                          (vp * 2)(y.data_ptr(), ro.data_ptr())) for x, r, y, ro in sets]
+                j = [0]
+
+                def pstep():
+                    a_in, a_out = pargs[j[0] % nsets]
+                    rc = lib.addrms_probe_run(pid, a_in, a_out, 2 * M * N, None,
+                                              torch.cuda.current_stream().cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"probe {ROW_SWEEP_PROBE} failed: hipError {rc}")
+                    j[0] += 1
+
+                tp = per_call(pstep, calls, ROW_SWEEP_WARMUP)
+                out[f"{M}x{N}"]["probe_median_us"] = tp["median_us"]
+                ppts.append((8 * M * N, tp["median_us"]))
             del sets, x0, r0
             torch.cuda.empty_cache()
         b, a = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
         out[f"fit_N{N}"] = {"t0_us": round(float(a), 3), "marginal_GBps": round(1e-3 / float(b), 1)}
+        if ppts:
+            b, a = np.polyfit([p[0] for p in ppts], [p[1] for p in ppts], 1)
+            out[f"probe_fit_N{N}"] = {"t0_us": round(float(a), 3),
+                                      "marginal_GBps": round(1e-3 / float(b), 1)}
     return out
 
 
 def summarize_row_sweep(trace_dir: str, out_path: str, commands: dict):
-    """Profile summary of a traced --row-sweep run: the fused forward's traced
-    durations grouped by shape (dispatches in the sweep's order, one group
-    per shape, the warm-up calls dropped), the median per shape, and per
-    width the least-squares line t = t0 + bytes / B over those medians."""
+    """Profile summary of a traced --row-sweep run: the fused forward's and
+    the stream probe's traced durations grouped by shape (dispatches in the
+    sweep's order, one group per shape, the warm-up calls dropped), the
+    median per shape, and per width the least-squares line t = t0 + bytes / B
+    over those medians for each."""
     import numpy as np
-    rows, _ = _csv_rows(trace_dir, "kernel_trace.csv")
-    rows = [r for r in rows if "fwd_vec_kernel" in r["Kernel_Name"]]
-    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    all_rows, _ = _csv_rows(trace_dir, "kernel_trace.csv")
+    all_rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    fwd = [r for r in all_rows if "fwd_vec_kernel" in r["Kernel_Name"]]
+    probe = [r for r in all_rows if ROW_SWEEP_PROBE_KERNEL in r["Kernel_Name"]]
     per = ROW_SWEEP_WARMUP + ROW_SWEEP_CALLS
     shapes = [(M, N) for N in ROW_SWEEP_N for M in ROW_SWEEP_M]
-    if len(rows) != per * len(shapes):
-        raise SystemExit(f"expected {per * len(shapes)} forward dispatches, found {len(rows)}")
+    if len(fwd) != per * len(shapes):
+        raise SystemExit(f"expected {per * len(shapes)} forward dispatches, found {len(fwd)}")
+    if probe and len(probe) != per * len(shapes):
+        raise SystemExit(f"expected {per * len(shapes)} probe dispatches, found {len(probe)}")
+
+    def stats(rows, k):
+        grp = rows[k * per + ROW_SWEEP_WARMUP:(k + 1) * per]
+        d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
+        return grp[0], d[len(d) // 2], d[int(0.1 * (len(d) - 1))], d[int(0.9 * (len(d) - 1))]
+
     lines = ["# Fused Add+RMSNorm forward, bf16: launch time against rows",
              "",
              "Traced kernel durations of the fused forward over a range of row counts at",
              "two widths, and per width the least-squares line t = t0 + bytes / B over",
              "the medians: B is the marginal stream rate of one more row, t0 the fixed",
              "cost of a launch (the ramp to a full device plus the tail of the last",
-             "blocks).  Bytes are the algorithmic 8 M N + 2 N.",
+             "blocks).  Bytes are the algorithmic 8 M N + 2 N.  Beside each shape, the",
+             f"2-read/2-write stream probe ({ROW_SWEEP_PROBE}: pure streaming, no reduction)",
+             "over the same buffers (8 M N bytes), with its own line.",
              "",
              "Commands:", ""]
     for k, v in commands.items():
@@ -232,30 +278,40 @@ def summarize_row_sweep(trace_dir: str, out_path: str, commands: dict):
     lines += [""]
     for N in ROW_SWEEP_N:
         lines += [f"## N = {N}", "",
-                  "| M | kernel | blocks x threads | median us | p10 us | p90 us | GB/s | fit us |",
-                  "|---|---|---|---|---|---|---|---|"]
-        pts = []
-        info = []
+                  "| M | kernel | blocks x threads | median us | p10 us | p90 us | GB/s | fit us |"
+                  + (" probe median us | probe GB/s |" if probe else ""),
+                  "|---|---|---|---|---|---|---|---|" + ("---|---|" if probe else "")]
+        pts, ppts, info = [], [], []
         for k, (M, NN) in enumerate(shapes):
             if NN != N:
                 continue
-            grp = rows[k * per + ROW_SWEEP_WARMUP:(k + 1) * per]
-            d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp)
-            med, p10, p90 = d[len(d) // 2], d[int(0.1 * (len(d) - 1))], d[int(0.9 * (len(d) - 1))]
-            wg = int(grp[0]["Workgroup_Size_X"])
-            blocks = int(grp[0]["Grid_Size_X"]) // wg
-            name = grp[0]["Kernel_Name"]
+            first, med, p10, p90 = stats(fwd, k)
+            wg = int(first["Workgroup_Size_X"])
+            blocks = int(first["Grid_Size_X"]) // wg
+            name = first["Kernel_Name"]
             targs = name[name.find("<") + 1:name.rfind(">")].split(",")
             nb = 8 * M * N + 2 * N
             pts.append((nb, med))
+            pmed = None
+            if probe:
+                pmed = stats(probe, k)[1]
+                ppts.append((8 * M * N, pmed))
             info.append((M, f"WPR {targs[-2].strip()}, VPL {targs[-1].strip()}", blocks, wg,
-                         med, p10, p90, nb))
+                         med, p10, p90, nb, pmed))
         b, a = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
-        for M, kern, blocks, wg, med, p10, p90, nb in info:
-            lines.append(f"| {M} | {kern} | {blocks} x {wg} | {med:.2f} | {p10:.2f} | {p90:.2f} | "
-                         f"{nb / med / 1e3:.0f} | {a + b * nb:.2f} |")
+        for M, kern, blocks, wg, med, p10, p90, nb, pmed in info:
+            row = (f"| {M} | {kern} | {blocks} x {wg} | {med:.2f} | {p10:.2f} | {p90:.2f} | "
+                   f"{nb / med / 1e3:.0f} | {a + b * nb:.2f} |")
+            if pmed is not None:
+                row += f" {pmed:.2f} | {8 * M * N / pmed / 1e3:.0f} |"
+            lines.append(row)
         lines += ["", f"Fit: t0 = {a:.2f} us, B = {1e-3 / b:.0f} GB/s "
-                      f"({100e-3 / b / HBM_PEAK_GBPS:.1f} % of 8 TB/s).", ""]
+                      f"({100e-3 / b / HBM_PEAK_GBPS:.1f} % of 8 TB/s)."]
+        if ppts:
+            pb, pa = np.polyfit([p[0] for p in ppts], [p[1] for p in ppts], 1)
+            lines += ["", f"Probe fit: t0 = {pa:.2f} us, B = {1e-3 / pb:.0f} GB/s "
+                          f"({100e-3 / pb / HBM_PEAK_GBPS:.1f} % of 8 TB/s)."]
+        lines += [""]
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
     print(f"wrote {out_path}")

@@ -90,27 +90,33 @@ def test_oracle_baselines_of_the_other_workloads():
 
 
 def test_row_sweep_summary_recovers_the_line(tmp_path):
-    """Synthetic trace: every dispatch of shape (M, N) lasts t0 + bytes / B
-    (warm-up calls 3 us slower, with copies interleaved); the summary must
-    drop the warm-up calls and recover t0 and B."""
+    """Synthetic trace: every dispatch of shape (M, N) lasts t0 + bytes / B,
+    the forward's and the probe's on lines of their own (warm-up calls 3 us
+    slower, with copies interleaved); the summary must drop the warm-up calls
+    and recover both lines."""
     t0, B = 1.7, 6200.0  # us, GB/s
+    pt0, pB = 1.5, 6300.0  # the probe's line
     rows, did, ts = [], 0, 10_000_000
     name = ("void addrms::fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 0, 16, 1>"
             "(addrms::FwdArgs)")
+    pname = ("void (anonymous namespace)::" + bench.ROW_SWEEP_PROBE_KERNEL
+             + " -1, -1>((anonymous namespace)::PArgs, unsigned int*)")
     for N in bench.ROW_SWEEP_N:
         for M in bench.ROW_SWEEP_M:
             nb = 8 * M * N + 2 * N
-            for k in range(bench.ROW_SWEEP_WARMUP + bench.ROW_SWEEP_CALLS):
-                us = t0 + nb / B / 1e3 + (3.0 if k < bench.ROW_SWEEP_WARMUP else 0.0)
-                for kname, dur in (("__amd_rocclr_copyBuffer", 1.0), (name, us)):
-                    did += 1
-                    rows.append({"Dispatch_Id": did, "Kernel_Name": kname, "Start_Timestamp": ts,
-                                 "End_Timestamp": ts + int(round(dur * 1e3)),
-                                 "Workgroup_Size_X": 1024, "Grid_Size_X": 1024 * M})
-                    ts += 1_000_000
+            for kname, line in ((name, (t0, B, nb)), (pname, (pt0, pB, 8 * M * N))):
+                for k in range(bench.ROW_SWEEP_WARMUP + bench.ROW_SWEEP_CALLS):
+                    us = line[0] + line[2] / line[1] / 1e3 + (3.0 if k < bench.ROW_SWEEP_WARMUP else 0.0)
+                    for kn, dur in (("__amd_rocclr_copyBuffer", 1.0), (kname, us)):
+                        did += 1
+                        rows.append({"Dispatch_Id": did, "Kernel_Name": kn, "Start_Timestamp": ts,
+                                     "End_Timestamp": ts + int(round(dur * 1e3)),
+                                     "Workgroup_Size_X": 1024, "Grid_Size_X": 1024 * M})
+                        ts += 1_000_000
     _write(str(tmp_path / "t" / "rows_kernel_trace.csv"), rows, list(rows[0].keys()))
     out = str(tmp_path / "rows.md")
     bench.summarize_row_sweep(str(tmp_path / "t"), out, {"trace": "rocprofv3 ... --row-sweep"})
     text = open(out).read()
     assert text.count(f"Fit: t0 = {t0:.2f} us, B = {B:.0f} GB/s") == len(bench.ROW_SWEEP_N)
+    assert text.count(f"Probe fit: t0 = {pt0:.2f} us, B = {pB:.0f} GB/s") == len(bench.ROW_SWEEP_N)
     assert "| 16384 | WPR 16, VPL 1 | 16384 x 1024 |" in text
