@@ -658,13 +658,14 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
         // rather than the 3 or 4 that fit.  Fewer blocks write fewer dw partial
         // rows (2 P N floats of extra traffic, and the column reduce reads
         // them), and the rows divide into whole steps more often.  Measured on
-        // MI355X, bf16, per-call medians: 2048 columns 3.7-7.3 % faster and
-        // 4096 columns 2.5-2.9 % at 12288 to 65536 rows, the fused form 3-5 %
-        // at 2048 columns; slower below 12288 rows at 4096 columns (6-14 %),
-        // for LayerNorm (9 % at 32768 x 2048) and at 1024 columns, which keep
-        // the grid that fits.
-        if (norm == kRms && !wide && knob(ADDRMS_KNOB_BLOCKS_PER_CU) == 0 && a.nvec >= 256 &&
-            M >= 48LL * cus && grid > 2 * cus)
+        // MI355X, per-call medians against the grid that fits: bf16, 4096
+        // columns 2.1-2.8 % faster at 16384 to 65536 rows, 2048 columns
+        // 3.4-6.7 %, the fused form 9 % at 16384 x 2048; float32, 2048
+        // columns 1-3 %, fused 2 %.  Slower, so keeping the grid that fits:
+        // 1024 bf16 or float32 columns (1-2 %), fewer than 12288 rows of 4096
+        // bf16 columns (6-14 %), and LayerNorm (9 % at 32768 x 2048).
+        if (norm == kRms && !wide && knob(ADDRMS_KNOB_BLOCKS_PER_CU) == 0 &&
+            a.nvec >= (dtype == ADDRMS_F32 ? 512 : 256) && M >= 48LL * cus && grid > 2 * cus)
             grid = 2 * cus;
         a.P = grid;
         if ((rc = launch(k, dim3(grid), smem, &a, s)) != ADDRMS_OK)
