@@ -26,8 +26,8 @@ _SRC = os.path.join(_HERE, "addrms_oracle.c")
 # mutation test builds deliberately broken copies to show the pins catch them).
 _LIB_PATH = os.environ.get("ADDRMS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, F64 = 0, 1, 2
-_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.float64: F64}
+F32, BF16, F64, F16 = 0, 1, 2, 3
+_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.float64: F64, torch.float16: F16}
 
 
 def build(force: bool = True) -> str:
@@ -56,6 +56,12 @@ def _load():
         lib.oracle_bf16_round.argtypes = [dbl]
         lib.oracle_bf16_round_array.restype = None
         lib.oracle_bf16_round_array.argtypes = [vp, vp, i64]
+        lib.oracle_f16_round.restype = ctypes.c_uint16
+        lib.oracle_f16_round.argtypes = [dbl]
+        lib.oracle_f16_round_array.restype = None
+        lib.oracle_f16_round_array.argtypes = [vp, vp, i64]
+        lib.oracle_f16_decode_array.restype = None
+        lib.oracle_f16_decode_array.argtypes = [vp, vp, i64]
         lib.oracle_rmsnorm_fwd.restype = i32
         lib.oracle_rmsnorm_fwd.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, i64, i64, dbl]
         lib.oracle_add_rmsnorm_fwd.restype = i32
@@ -138,6 +144,22 @@ def _check(rc: int, what: str):
 def eps_as_float32(eps: float) -> float:
     """The eps value the GPU library sees: the binary32 nearest to eps."""
     return float(np.float32(eps))
+
+
+def f16_round(v) -> np.ndarray:
+    """binary64 values -> IEEE binary16 bit patterns (uint16), one RNE rounding."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_f16_round_array(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def f16_decode(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> their exact binary64 values."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_f16_decode_array(b.ctypes.data, out.ctypes.data, b.size)
+    return out
 
 
 def bf16_round(v) -> np.ndarray:

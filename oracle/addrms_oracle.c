@@ -53,7 +53,8 @@
  *   dw = sum_i dy * xh,      db = sum_i dy
  *
  * Element types (codes): 0 = float32, 1 = bfloat16 (raw uint16 bits),
- * 2 = float64.  All arrays are row-major and contiguous, row stride N.
+ * 2 = float64, 3 = float16 (IEEE binary16, raw uint16 bits).  All arrays
+ * are row-major and contiguous, row stride N.
  */
 #include <math.h>
 #include <stdint.h>
@@ -63,6 +64,7 @@
 #define OR_F32 0
 #define OR_BF16 1
 #define OR_F64 2
+#define OR_F16 3
 
 #define OR_OK 0
 #define OR_ERR_ARG -1
@@ -138,7 +140,85 @@ void oracle_bf16_round_array(const double *v, uint16_t *out, int64_t n)
         out[i] = oracle_bf16_round(v[i]);
 }
 
-static int dtype_ok(int dt) { return dt == OR_F32 || dt == OR_BF16 || dt == OR_F64; }
+/* ---- binary16 <-> binary64 (IEEE 754 binary16: 1 sign bit, 5 exponent
+ * bits with bias 15, 10 fraction bits) ------------------------------------ */
+
+/* The value of a binary16 pattern, exact in binary64: exponent field 0 is
+ * the subnormal range fraction * 2^-24, field 31 is infinity (fraction 0) or
+ * NaN, otherwise (1 + fraction / 2^10) * 2^(field - 15). */
+double oracle_f16_bits_to_double(uint16_t b)
+{
+    const int sign = (b >> 15) & 1, field = (b >> 10) & 0x1F, frac = b & 0x3FF;
+    double m;
+    if (field == 31)
+        m = frac ? NAN : INFINITY;
+    else if (field == 0)
+        m = ldexp((double)frac, -24);
+    else
+        m = ldexp(1.0 + (double)frac / 1024.0, field - 15);
+    return sign ? -m : m;
+}
+
+/* Round a binary64 value to binary16, round-to-nearest ties-to-even, written
+ * out from the definition as the bfloat16 rounding above: the neighbouring
+ * binary16 values lo <= |v| < hi on the grid of spacing ulp (11 significant
+ * bits; 2^-24 in the subnormal range below 2^-14), the midpoint decides, a
+ * tie takes the even significand.  Beyond the largest finite value 65504 the
+ * result is infinity (|v| >= 65520 rounds up past it).  NaN gives a quiet
+ * NaN with the sign kept. */
+uint16_t oracle_f16_round(double v)
+{
+    const double f16_max = 65504.0;
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a, ulp, lo, hi, mid, q;
+
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7E00u);
+    a = fabs(v);
+    if (isinf(v) || a >= 0x1p17)
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < 0x1p-14) {
+        ulp = 0x1p-24;
+    } else {
+        int e;
+        frexp(a, &e); /* a in [2^(e-1), 2^e) */
+        ulp = ldexp(1.0, e - 11);
+    }
+    lo = floor(a / ulp) * ulp;
+    hi = lo + ulp;
+    mid = lo + 0.5 * ulp;
+    if (a < mid)
+        q = lo;
+    else if (a > mid)
+        q = hi;
+    else
+        q = (fmod(lo / ulp, 2.0) == 0.0) ? lo : hi;
+
+    if (q > f16_max)
+        return (uint16_t)(sign | 0x7C00u);
+    if (q < 0x1p-14) /* subnormal or zero: fraction = q / 2^-24 */
+        return (uint16_t)(sign | (uint16_t)(q * 0x1p24));
+    int e;
+    const double m = frexp(q, &e); /* q = m * 2^e, m in [0.5, 1) */
+    const int field = e - 1 + 15;
+    const int frac = (int)((2.0 * m - 1.0) * 1024.0);
+    return (uint16_t)(sign | (uint16_t)(field << 10) | (uint16_t)frac);
+}
+
+/* Bulk forms, for the converter's own checks. */
+void oracle_f16_round_array(const double *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f16_round(v[i]);
+}
+
+void oracle_f16_decode_array(const uint16_t *b, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f16_bits_to_double(b[i]);
+}
+
+static int dtype_ok(int dt) { return dt == OR_F32 || dt == OR_BF16 || dt == OR_F64 || dt == OR_F16; }
 
 static double load_elem(const void *p, int dt, int64_t i)
 {
@@ -147,6 +227,8 @@ static double load_elem(const void *p, int dt, int64_t i)
         return (double)((const float *)p)[i];
     case OR_BF16:
         return bf16_bits_to_double(((const uint16_t *)p)[i]);
+    case OR_F16:
+        return oracle_f16_bits_to_double(((const uint16_t *)p)[i]);
     default:
         return ((const double *)p)[i];
     }
@@ -162,6 +244,9 @@ static void store_elem(void *p, int dt, int64_t i, double v)
         break;
     case OR_BF16:
         ((uint16_t *)p)[i] = oracle_bf16_round(v);
+        break;
+    case OR_F16:
+        ((uint16_t *)p)[i] = oracle_f16_round(v);
         break;
     default:
         ((double *)p)[i] = v;
@@ -515,7 +600,7 @@ void oracle_fp8e4m3_encode_array(const double *v, uint8_t *out, int64_t n)
  * with scale = 1 for a group with no non-zero finite |y| (a NaN encodes as
  * NaN).  y_j ~= decode(q_j) * scale of its group.  scale is
  * [M][ceil(N / group)], row-major. */
-static size_t elem_size(int dt) { return dt == OR_F32 ? 4 : dt == OR_BF16 ? 2 : 8; }
+static size_t elem_size(int dt) { return dt == OR_F32 ? 4 : dt == OR_F64 ? 8 : 2; }
 
 int oracle_rmsnorm_fwd_fp8_grouped(const void *x, int x_dt, const void *w, int w_dt, uint8_t *q,
                                    float *scale, int64_t group, void *rstd, int rstd_dt,

@@ -3,8 +3,9 @@
 Each case below plants one mistake in a copy of the oracle's C source, builds
 it, and runs the oracle pin suite against that build in a subprocess: the
 suite must fail.  Mistakes cover every step of the definition: the eps
-placement, the mean's divisor, the square, the weight, the bfloat16 rounding
-rule, the fused op's choice of normalised value, the saved rstd, and each term
+placement, the mean's divisor, the square, the weight, the bfloat16 and
+float16 rounding rules (ties, truncation, spacing, exponent bias, overflow),
+the fused op's choice of normalised value, the saved rstd, and each term
 of the backward, including the residual gradient of the fused op; for
 LayerNorm, E4M3 and RMSNorm + RoPE, each step of their definitions (the RoPE
 signs, the cos/sin roles, the pairing of each layout, the table row, and the
@@ -19,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "addrms_oracle.c")
 PINS = ["tests/test_oracle_bf16.py", "tests/test_oracle_fwd.py", "tests/test_oracle_bwd.py",
         "tests/test_oracle_layernorm.py", "tests/test_oracle_fp8.py", "tests/test_oracle_rope.py",
-        "tests/test_oracle_mxfp4.py"]
+        "tests/test_oracle_mxfp4.py", "tests/test_oracle_f16.py"]
 
 MUTANTS = {
     "eps_outside_root": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms) + eps"),
@@ -64,13 +65,26 @@ MUTANTS.update({
                                 "double g = load_elem(dy, in_dt, i * N + j);", 1, 2),
     "ln_bwd_dx_without_weight": ("double g = d * load_elem(w, w_dt, j);", "double g = d;", 1, 2),
 })
-for _k in ("bwd_g_without_weight", "bwd_dx_without_weight", "ties_away_from_zero"):
+for _k in ("bwd_g_without_weight", "bwd_dx_without_weight"):
     MUTANTS[_k] = MUTANTS[_k] + (0, 2)
-MUTANTS["truncating_round"] = MUTANTS["truncating_round"] + (0, 3)
+# the ties and truncation anchors occur in the bfloat16, float16, E4M3 (and
+# E2M1) converters, in that order
+MUTANTS["ties_away_from_zero"] = MUTANTS["ties_away_from_zero"] + (0, 3)
+MUTANTS["truncating_round"] = MUTANTS["truncating_round"] + (0, 4)
 MUTANTS.update({
-    "fp8_ties_up": ("(fmod(lo / ulp, 2.0) == 0.0) ? lo : hi", "hi", 1, 2),
-    "fp8_truncating_round": ("if (a < mid)", "if (a < hi)", 1, 3),
-    "fp4_truncating_round": ("if (a < mid)", "if (a < hi)", 2, 3),
+    "f16_ties_away_from_zero": ("(fmod(lo / ulp, 2.0) == 0.0) ? lo : hi", "hi", 1, 3),
+    "f16_truncating_round": ("if (a < mid)", "if (a < hi)", 1, 4),
+    "f16_subnormal_spacing": ("ulp = 0x1p-24;", "ulp = 0x1p-23;"),
+    "f16_significand_bits": ("ulp = ldexp(1.0, e - 11);", "ulp = ldexp(1.0, e - 10);"),
+    "f16_exponent_bias": ("const int field = e - 1 + 15;", "const int field = e - 1 + 16;"),
+    "f16_overflow_saturates": ("if (q > f16_max)\n        return (uint16_t)(sign | 0x7C00u);",
+                               "if (q > f16_max)\n        q = f16_max;"),
+    "f16_decode_bias": ("ldexp(1.0 + (double)frac / 1024.0, field - 15)",
+                        "ldexp(1.0 + (double)frac / 1024.0, field - 16)"),
+    "f16_decode_subnormal_scale": ("m = ldexp((double)frac, -24);", "m = ldexp((double)frac, -25);"),
+    "fp8_ties_up": ("(fmod(lo / ulp, 2.0) == 0.0) ? lo : hi", "hi", 2, 3),
+    "fp8_truncating_round": ("if (a < mid)", "if (a < hi)", 2, 4),
+    "fp4_truncating_round": ("if (a < mid)", "if (a < hi)", 3, 4),
     "fp8_subnormal_spacing": ("ulp = 0x1p-9;", "ulp = 0x1p-10;"),
     "fp8_ulp_exponent": ("ulp = ldexp(1.0, e - 4);", "ulp = ldexp(1.0, e - 5);"),
     "fp8_exponent_bias": ("int exp_field = (e - 1) + 7;", "int exp_field = (e - 1) + 8;"),
@@ -116,7 +130,8 @@ MUTANTS.update({
 })
 
 
-FAMILY = [("fp4_", "tests/test_oracle_mxfp4.py"), ("mx_", "tests/test_oracle_mxfp4.py"),
+FAMILY = [("f16_", "tests/test_oracle_f16.py"),
+          ("fp4_", "tests/test_oracle_mxfp4.py"), ("mx_", "tests/test_oracle_mxfp4.py"),
           ("rope_", "tests/test_oracle_rope.py"), ("fp8", "tests/test_oracle_fp8.py"),
           ("ln_", "tests/test_oracle_layernorm.py"), ("bwd_", "tests/test_oracle_bwd.py"),
           ("fused_bwd", "tests/test_oracle_bwd.py"), ("fused_", "tests/test_oracle_fwd.py")]
