@@ -38,8 +38,8 @@ __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
 
-F32, BF16 = 0, 1
-_CODES = {torch.float32: F32, torch.bfloat16: BF16}
+F32, BF16, F16 = 0, 1, 2
+_CODES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 
 class AddRmsError(RuntimeError):
@@ -148,7 +148,7 @@ class tuning:
 def _code(t: torch.Tensor, what: str) -> int:
     c = _CODES.get(t.dtype)
     if c is None:
-        raise TypeError(f"{what}: dtype {t.dtype} not supported (float32, bfloat16)")
+        raise TypeError(f"{what}: dtype {t.dtype} not supported (float32, bfloat16, float16)")
     return c
 
 

@@ -25,6 +25,7 @@ LIB = os.path.join(PKG, "libaddrms.so")
 PROBE_LIB = os.path.join(PKG, "libaddrms_probe.so")
 
 ARCH = os.environ.get("ADDRMS_OFFLOAD_ARCH", "gfx950")
+NUM_COMBOS = 9  # (row dtype, weight dtype) pairs of float32, bfloat16, float16
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
@@ -109,10 +110,11 @@ def _client_build() -> str:
 
 def build(verbose: bool = False, extra_defines=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    # one object per (row dtype, weight dtype) combination: 3 x 3
     jobs = [(os.path.join(CSRC, "tables.hip"), os.path.join(BUILD, f"tables_{c}.o"),
-             (f"ADDRMS_COMBO={c}", *extra_defines)) for c in range(4)]
+             (f"ADDRMS_COMBO={c}", *extra_defines)) for c in range(NUM_COMBOS)]
     jobs += [(os.path.join(CSRC, "rope.hip"), os.path.join(BUILD, f"rope_{c}.o"),
-              (f"ADDRMS_COMBO={c}", *extra_defines)) for c in range(4)]
+              (f"ADDRMS_COMBO={c}", *extra_defines)) for c in range(NUM_COMBOS)]
     jobs.append((os.path.join(CSRC, "api.hip"), os.path.join(BUILD, "api.o"),
                  tuple(extra_defines)))
     workers = min(len(jobs) + 1, max(1, min(16, os.cpu_count() or 1)))

@@ -19,49 +19,40 @@
 
 namespace addrms {
 
-const FwdTable &fwd_table_0();
-const FwdTable &fwd_table_1();
-const FwdTable &fwd_table_2();
-const FwdTable &fwd_table_3();
-const BwdTable &bwd_table_0();
-const BwdTable &bwd_table_1();
-const BwdTable &bwd_table_2();
-const BwdTable &bwd_table_3();
+// One table of each kind per (row dtype, weight dtype) combination, from
+// tables.hip and rope.hip compiled once per ADDRMS_COMBO (0..8).
+#define ADDRMS_DECLARE_COMBO(c)                                                                   \
+    const FwdTable &fwd_table_##c();                                                              \
+    const BwdTable &bwd_table_##c();                                                              \
+    const RopeTable &rope_table_##c();
+ADDRMS_DECLARE_COMBO(0)
+ADDRMS_DECLARE_COMBO(1)
+ADDRMS_DECLARE_COMBO(2)
+ADDRMS_DECLARE_COMBO(3)
+ADDRMS_DECLARE_COMBO(4)
+ADDRMS_DECLARE_COMBO(5)
+ADDRMS_DECLARE_COMBO(6)
+ADDRMS_DECLARE_COMBO(7)
+ADDRMS_DECLARE_COMBO(8)
+#undef ADDRMS_DECLARE_COMBO
 
-const FwdTable &fwd_table(int c)
-{
-    switch (c) {
-    case 0: return fwd_table_0();
-    case 1: return fwd_table_1();
-    case 2: return fwd_table_2();
-    default: return fwd_table_3();
+#define ADDRMS_TABLE_SWITCH(kind, c)                                                              \
+    switch (c) {                                                                                  \
+    case 0: return kind##_0();                                                                    \
+    case 1: return kind##_1();                                                                    \
+    case 2: return kind##_2();                                                                    \
+    case 3: return kind##_3();                                                                    \
+    case 4: return kind##_4();                                                                    \
+    case 5: return kind##_5();                                                                    \
+    case 6: return kind##_6();                                                                    \
+    case 7: return kind##_7();                                                                    \
+    default: return kind##_8();                                                                   \
     }
-}
 
-const RopeTable &rope_table_0();
-const RopeTable &rope_table_1();
-const RopeTable &rope_table_2();
-const RopeTable &rope_table_3();
-
-const RopeTable &rope_table(int c)
-{
-    switch (c) {
-    case 0: return rope_table_0();
-    case 1: return rope_table_1();
-    case 2: return rope_table_2();
-    default: return rope_table_3();
-    }
-}
-
-const BwdTable &bwd_table(int c)
-{
-    switch (c) {
-    case 0: return bwd_table_0();
-    case 1: return bwd_table_1();
-    case 2: return bwd_table_2();
-    default: return bwd_table_3();
-    }
-}
+const FwdTable &fwd_table(int c) { ADDRMS_TABLE_SWITCH(fwd_table, c) }
+const BwdTable &bwd_table(int c) { ADDRMS_TABLE_SWITCH(bwd_table, c) }
+const RopeTable &rope_table(int c) { ADDRMS_TABLE_SWITCH(rope_table, c) }
+#undef ADDRMS_TABLE_SWITCH
 
 namespace {
 
@@ -77,7 +68,7 @@ int fail_hip(hipError_t e)
     return ADDRMS_ERR_HIP;
 }
 
-bool dtype_ok(int d) { return d == ADDRMS_F32 || d == ADDRMS_BF16; }
+bool dtype_ok(int d) { return d == ADDRMS_F32 || d == ADDRMS_BF16 || d == ADDRMS_F16; }
 size_t esize(int d) { return d == ADDRMS_F32 ? 4 : 2; }
 int vec_elems(int d) { return d == ADDRMS_F32 ? 4 : 8; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -34,9 +34,10 @@ int code_of(const at::Tensor &t, const char *what)
     switch (t.scalar_type()) {
     case at::kFloat: return ADDRMS_F32;
     case at::kBFloat16: return ADDRMS_BF16;
+    case at::kHalf: return ADDRMS_F16;
     default:
         throw py::type_error(std::string(what) + ": dtype " + dtype_str(t.scalar_type()) +
-                             " not supported (float32, bfloat16)");
+                             " not supported (float32, bfloat16, float16)");
     }
 }
 

@@ -1,5 +1,6 @@
 // Device-side building blocks for the gfx950 RMSNorm kernels: 128-bit vector
-// element access, bfloat16 packing, and the wave64 / workgroup float sums.
+// element access, bfloat16 and float16 packing, and the wave64 / workgroup
+// float sums.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,9 +12,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Storage tag for bfloat16 (the upper half of a binary32); never computed on.
+// Storage tags for bfloat16 (the upper half of a binary32) and IEEE binary16;
+// never computed on.
 struct bf16_t {
+    uint16_t bits;
+};
+struct f16_t {
     uint16_t bits;
 };
 
@@ -21,6 +27,7 @@ struct bf16_t {
 template <typename T> struct Vec;
 template <> struct Vec<float> { static constexpr int n = 4; };
 template <> struct Vec<bf16_t> { static constexpr int n = 8; };
+template <> struct Vec<f16_t> { static constexpr int n = 8; };
 
 // ---- bfloat16 <-> float ------------------------------------------------------
 
@@ -36,6 +43,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 }
 
 __device__ __forceinline__ uint16_t to_bf16(float a) { return (uint16_t)pack_bf16x2(a, 0.0f); }
+
+// ---- binary16 <-> float ----------------------------------------------------
+
+// The two binary16 values of a dword (low half first), widened exactly.
+__device__ __forceinline__ f32x2 f16x2_to_f32(uint32_t u)
+{
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+}
+
+// Two floats -> two binary16 in one dword (a in the low half), each rounded
+// to nearest-even by the hardware conversion (overflow to infinity, subnormal
+// results kept, NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
+{
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+__device__ __forceinline__ uint16_t to_f16(float a) { return (uint16_t)pack_f16x2(a, 0.0f); }
+
+// The two 16-bit values of a dword of type T (bf16_t or f16_t), as floats.
+template <typename T> __device__ __forceinline__ void widen2(uint32_t u, float &lo, float &hi)
+{
+    if constexpr (__is_same(T, f16_t)) {
+        const f32x2 f = f16x2_to_f32(u);
+        lo = f[0];
+        hi = f[1];
+    } else {
+        lo = bf16_lo(u);
+        hi = bf16_hi(u);
+    }
+}
 
 // ---- one 16-byte vector <-> floats -------------------------------------------
 
@@ -60,6 +99,14 @@ __device__ __forceinline__ void unpack<bf16_t>(const u32x4 &v, float (&f)[8])
     }
 }
 
+template <>
+__device__ __forceinline__ void unpack<f16_t>(const u32x4 &v, float (&f)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        widen2<f16_t>(v[i], f[2 * i], f[2 * i + 1]);
+}
+
 template <typename T>
 __device__ __forceinline__ u32x4 pack(const float (&f)[Vec<T>::n]);
 
@@ -80,6 +127,16 @@ __device__ __forceinline__ u32x4 pack<bf16_t>(const float (&f)[8])
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return v;
+}
+
+template <>
+__device__ __forceinline__ u32x4 pack<f16_t>(const float (&f)[8])
+{
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        v[i] = pack_f16x2(f[2 * i], f[2 * i + 1]);
     return v;
 }
 
@@ -147,10 +204,8 @@ __device__ __forceinline__ void unpack_w(const WRaw<T, WT> &r, float (&f)[Vec<T>
             f[i] = __uint_as_float(r.d[i]);
     } else {
 #pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-            f[2 * i] = bf16_lo(r.d[i]);
-            f[2 * i + 1] = bf16_hi(r.d[i]);
-        }
+        for (int i = 0; i < n / 2; ++i)
+            widen2<WT>(r.d[i], f[2 * i], f[2 * i + 1]);
     }
 }
 
@@ -171,6 +226,10 @@ template <> __device__ __forceinline__ float ld_elem<bf16_t>(const void *p, int6
 {
     return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
 }
+template <> __device__ __forceinline__ float ld_elem<f16_t>(const void *p, int64_t i)
+{
+    return (float)reinterpret_cast<const _Float16 *>(p)[i];
+}
 template <typename T> __device__ __forceinline__ void st_elem(void *p, int64_t i, float v);
 template <> __device__ __forceinline__ void st_elem<float>(void *p, int64_t i, float v)
 {
@@ -180,12 +239,20 @@ template <> __device__ __forceinline__ void st_elem<bf16_t>(void *p, int64_t i, 
 {
     reinterpret_cast<uint16_t *>(p)[i] = to_bf16(v);
 }
+template <> __device__ __forceinline__ void st_elem<f16_t>(void *p, int64_t i, float v)
+{
+    reinterpret_cast<uint16_t *>(p)[i] = to_f16(v);
+}
 // The value an element has once stored as T (the rounding a store applies).
 template <typename T> __device__ __forceinline__ float as_stored(float v);
 template <> __device__ __forceinline__ float as_stored<float>(float v) { return v; }
 template <> __device__ __forceinline__ float as_stored<bf16_t>(float v)
 {
     return __uint_as_float((uint32_t)to_bf16(v) << 16);
+}
+template <> __device__ __forceinline__ float as_stored<f16_t>(float v)
+{
+    return (float)__builtin_bit_cast(_Float16, to_f16(v));
 }
 
 // ---- reductions --------------------------------------------------------------

@@ -145,9 +145,9 @@ struct KernelRef {
     int block;
 };
 
-// Dtype combination index: (row dtype, weight dtype) -> 0..3, with
-// dtype codes ADDRMS_F32 = 0, ADDRMS_BF16 = 1.
-inline int combo(int dtype, int w_dtype) { return dtype * 2 + w_dtype; }
+// Dtype combination index: (row dtype, weight dtype) -> 0..8, with
+// dtype codes ADDRMS_F32 = 0, ADDRMS_BF16 = 1, ADDRMS_F16 = 2.
+inline int combo(int dtype, int w_dtype) { return dtype * 3 + w_dtype; }
 
 // Kernel tables, one translation unit per dtype combination.
 // fwd vec: [norm][fused][wpr_idx][vpl_idx]; fwd elem: [norm][fused].

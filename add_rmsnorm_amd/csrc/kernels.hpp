@@ -112,20 +112,38 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
     const int nvec = a.nvec;
     const float inv_n = 1.0f / (float)a.N;
 
-    // Sum (or max) of one value per lane over the row's WPR waves.  Each
-    // reduction of a row has its own LDS slot; a slot is reused two rows later,
-    // after at least two barriers, so one barrier per reduction suffices.
-    __shared__ float part[4][16];
-    auto row_sum = [&](float v, int slot) -> float {
-        float t = wave_sum(v);
+    // Row sums.  With up to 2 vectors a lane (NS = VPL), in one order
+    // whatever the launch shape: each vector's values are summed in order,
+    // each block of 64 consecutive vectors (a wave's lanes at one k) by the
+    // fixed DPP tree of wave_sum, and the blocks, b = v / 64 = wir + k * WPR,
+    // one after another from the first; blocks past the row hold exactly
+    // zero.  So those shapes all give the same float32 sum, bit for bit, and
+    // the plain and the fused forward agree on the same residual even where
+    // the dispatcher gives them different shapes (16 waves of one vector
+    // against 8 of two).  Longer per-lane chains (NS = 1) sum a lane's
+    // vectors together first, then the waves in order: a tree per vector
+    // would hold more registers than those shapes have.  Each reduction of a
+    // row has its own LDS slot; a slot is reused two rows later, after at
+    // least two barriers, so one barrier per reduction suffices.
+    constexpr int NS = VPL <= 2 ? VPL : 1;
+    __shared__ float part[4][WPR * NS > 16 ? WPR * NS : 16];
+    auto row_sum = [&](const float (&v)[NS], int slot) -> float {
+        float t = 0.0f;
         if constexpr (WPR > 1) {
-            if (lane == 0)
-                part[slot][wir] = t;
-            __syncthreads();
-            t = 0.0f;
 #pragma unroll
-            for (int i = 0; i < WPR; ++i)
-                t += part[slot][i];
+            for (int j = 0; j < NS; ++j) {
+                const float tj = wave_sum(v[j]);
+                if (lane == 0)
+                    part[slot][j * WPR + wir] = tj;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < WPR * NS; ++b)
+                t += part[slot][b];
+        } else {
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                t += wave_sum(v[j]);
         }
         return t;
     };
@@ -198,7 +216,10 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
         //    from the same exchange as the sum instead of a second one after
         //    y (it differs from max |y| only in float32 rounding).
         constexpr bool EARLY_MAX = QM == kQRow && HOLD_W;
-        float s1 = 0.0f, hwmax = 0.0f;
+        float s1[NS], hwmax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            s1[j] = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             float h[NV];
@@ -215,9 +236,10 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
                 if (v < nvec)
                     st_stream<kPol>(resp + v, hv[k]);
             }
+            float &acc = s1[NS == VPL ? k : 0];
 #pragma unroll
             for (int e = 0; e < NV; ++e)
-                s1 = (NORM == kRms) ? __builtin_fmaf(h[e], h[e], s1) : s1 + h[e];
+                acc = (NORM == kRms) ? __builtin_fmaf(h[e], h[e], acc) : acc + h[e];
             if constexpr (EARLY_MAX) {
                 float wf[NV];
                 unpack_w<T, WT>(wr[k], wf);
@@ -231,21 +253,30 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
         const int slot = (it & 1) * 2;
         float mu = 0.0f, rs;
         if constexpr (EARLY_MAX) {
-            // the sum and the maximum through one LDS exchange and barrier
-            float t = wave_sum(s1), m = wave_max(hwmax);
+            // the sum (in the order of row_sum) and the maximum through one
+            // LDS exchange and barrier
+            float t = 0.0f, m = wave_max(hwmax);
             if constexpr (WPR > 1) {
-                if (lane == 0) {
-                    part[slot][wir] = t;
-                    part[slot + 1][wir] = m;
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    const float tj = wave_sum(s1[j]);
+                    if (lane == 0)
+                        part[slot][j * WPR + wir] = tj;
                 }
+                if (lane == 0)
+                    part[slot + 1][wir] = m;
                 __syncthreads();
-                t = 0.0f;
                 m = 0.0f;
 #pragma unroll
-                for (int i = 0; i < WPR; ++i) {
-                    t += part[slot][i];
+                for (int b = 0; b < WPR * NS; ++b)
+                    t += part[slot][b];
+#pragma unroll
+                for (int i = 0; i < WPR; ++i)
                     m = __builtin_fmaxf(m, part[slot + 1][i]);
-                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NS; ++j)
+                    t += wave_sum(s1[j]);
             }
             rs = 1.0f / __builtin_sqrtf(t * inv_n + a.eps);
             hwmax = m;
@@ -253,16 +284,20 @@ __global__ void __launch_bounds__(kBlockFwd(WPR)) fwd_vec_kernel(FwdArgs a)
             rs = 1.0f / __builtin_sqrtf(row_sum(s1, slot) * inv_n + a.eps);
         } else {
             mu = row_sum(s1, slot) * inv_n;
-            float s2 = 0.0f;
+            float s2[NS];
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                s2[j] = 0.0f;
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 if (vbase + k * VSTRIDE < nvec) {
                     float h[NV];
                     unpack<T>(hv[k], h);
+                    float &acc = s2[NS == VPL ? k : 0];
 #pragma unroll
                     for (int e = 0; e < NV; ++e) {
                         const float d = h[e] - mu;
-                        s2 = __builtin_fmaf(d, d, s2);
+                        acc = __builtin_fmaf(d, d, acc);
                     }
                 }
             }

@@ -1,7 +1,7 @@
 // Per-head RMSNorm followed by the rotary position embedding, in one pass, for
 // the query and key heads of an attention layer: HIP kernels for gfx950 and
 // their table for one (row dtype, weight dtype) combination, selected at
-// compile time by ADDRMS_COMBO as in tables.hip.
+// compile time by ADDRMS_COMBO (combo_types.hpp).
 //
 // The "Machete" README lists RMSNorm and RoPE side by side among the ops its
 // persistent kernels compose ("Built-In Areas").  They meet where each query
@@ -26,26 +26,7 @@
 #include "device.hpp"
 #include "internal.hpp"
 
-#ifndef ADDRMS_COMBO
-#error "define ADDRMS_COMBO (0..3)"
-#endif
-
-#if ADDRMS_COMBO == 0
-#define ADDRMS_ROW_T float
-#define ADDRMS_W_T float
-#elif ADDRMS_COMBO == 1
-#define ADDRMS_ROW_T float
-#define ADDRMS_W_T addrms::bf16_t
-#elif ADDRMS_COMBO == 2
-#define ADDRMS_ROW_T addrms::bf16_t
-#define ADDRMS_W_T float
-#else
-#define ADDRMS_ROW_T addrms::bf16_t
-#define ADDRMS_W_T addrms::bf16_t
-#endif
-
-#define ADDRMS_CAT2(a, b) a##b
-#define ADDRMS_CAT(a, b) ADDRMS_CAT2(a, b)
+#include "combo_types.hpp"
 
 #ifndef ADDRMS_STREAM_POLICY
 #define ADDRMS_STREAM_POLICY 3

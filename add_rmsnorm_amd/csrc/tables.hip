@@ -1,29 +1,8 @@
 // Kernel tables for one (row dtype, weight dtype) combination, selected at
-// compile time by ADDRMS_COMBO = 2 * row_dtype + weight_dtype (0 = float32,
-// 1 = bfloat16).  The build compiles this file once per combination so the
-// instantiations compile in parallel.
+// compile time by ADDRMS_COMBO (combo_types.hpp).
 #include "kernels.hpp"
 
-#ifndef ADDRMS_COMBO
-#error "define ADDRMS_COMBO (0..3)"
-#endif
-
-#if ADDRMS_COMBO == 0
-#define ADDRMS_ROW_T float
-#define ADDRMS_W_T float
-#elif ADDRMS_COMBO == 1
-#define ADDRMS_ROW_T float
-#define ADDRMS_W_T addrms::bf16_t
-#elif ADDRMS_COMBO == 2
-#define ADDRMS_ROW_T addrms::bf16_t
-#define ADDRMS_W_T float
-#else
-#define ADDRMS_ROW_T addrms::bf16_t
-#define ADDRMS_W_T addrms::bf16_t
-#endif
-
-#define ADDRMS_CAT2(a, b) a##b
-#define ADDRMS_CAT(a, b) ADDRMS_CAT2(a, b)
+#include "combo_types.hpp"
 
 namespace addrms {
 

@@ -12,7 +12,9 @@
  *         rstd_i = 1 / sqrt(mean_j(h_ij^2) + eps)
  *         y_ij   = round(h_ij * rstd_i * w_j)
  *     The fused op normalises the residual exactly as it is stored, so its y
- *     equals rmsnorm_fwd applied to residual_out, bit for bit.
+ *     equals rmsnorm_fwd applied to residual_out, bit for bit (with the
+ *     kernel variants the library chooses; the tuning knobs below can force
+ *     variants whose sums round differently).
  *   - The backward the Machete README's autograd helpers ("Built-In Areas")
  *     imply, the exact derivative given the saved rstd:
  *         g = dy * w,  xh = x * rstd_i,  c_i = mean_j(g_ij * xh_ij)
@@ -21,6 +23,9 @@
  *
  * Arithmetic: float32 throughout on the GPU; each output is rounded once to
  * its storage type, round-to-nearest-even.  The residual add is a float32 add.
+ * Storage types (dtype for the matrices, w_dtype for the weights, chosen
+ * independently): ADDRMS_F32, ADDRMS_BF16, ADDRMS_F16.  A float16 result
+ * beyond its range (65504) is infinite, as a float16 store rounds it.
  *
  * Layout: every matrix is row-major and contiguous, M rows of N elements
  * (row stride N).  w, dw have N elements; rstd has M.
@@ -59,6 +64,7 @@ extern "C" {
 /* Element types. */
 #define ADDRMS_F32 0  /* IEEE binary32 */
 #define ADDRMS_BF16 1 /* bfloat16: the upper 16 bits of a binary32 */
+#define ADDRMS_F16 2  /* IEEE binary16 (half precision) */
 
 /* Status codes: 0 on success, negative on error. */
 #define ADDRMS_OK 0

@@ -2,6 +2,8 @@
 
 Tolerances (floating-point outputs, |gpu - oracle| <= atol + rtol * |oracle|):
     bfloat16 y, dx : atol 1e-2, rtol 1.6e-2
+    float16  y, dx : atol 1e-4, rtol 2e-3 (two float16 ulps relative; the
+                     absolute term covers float32 cancellation near zero)
     float32  y, dx : atol 1e-6, rtol 1e-5
     float32  rstd  : rtol 1e-5 (bf16 inputs) -- one float32 rounding of the
                      sum of squares and of 1/sqrt
@@ -10,18 +12,19 @@ Tolerances (floating-point outputs, |gpu - oracle| <= atol + rtol * |oracle|):
                      can reach); columns with |dw| >= 1e-2 of that magnitude
                      also meet rtol 1e-3 alone
     bf16 y, dx, dh : also within half a bf16 ulp of the binary64 value plus
-                     float32 noise (one rounding; assert_correctly_rounded)
+                     float32 noise (one rounding; assert_correctly_rounded),
+                     and float16 outputs within half a float16 ulp
 Residuals are compared bit for bit; NaN must sit where the oracle has NaN.
 """
 import numpy as np
 import torch
 
-TOL = {torch.bfloat16: (1e-2, 1.6e-2), torch.float32: (1e-6, 1e-5)}
+TOL = {torch.bfloat16: (1e-2, 1.6e-2), torch.float32: (1e-6, 1e-5), torch.float16: (1e-4, 2e-3)}
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu().contiguous()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
@@ -80,25 +83,32 @@ def assert_dw_close(gpu: torch.Tensor, ref: torch.Tensor, mag: torch.Tensor, wha
 
 def assert_correctly_rounded(gpu: torch.Tensor, ref64: torch.Tensor, mag, what: str,
                              noise: float = 2.0 ** -18):
-    """bfloat16 outputs rounded once (reading R5): every finite element lies
-    within half a bf16 ulp of the oracle's binary64 value plus the float32
-    arithmetic's own error, noise * mag, where mag (a tensor, or None for
-    |ref64|) bounds the magnitude of the terms the element was computed
-    from.  Rounding the float32 result once to bf16 stays within half an ulp
-    of its float32 value; an extra bf16 rounding on the way (of h * rstd, or
-    of the row terms of dx) adds up to another half ulp, 2^-9 relative,
-    thousands of times the noise term."""
+    """bfloat16 or float16 outputs rounded once (reading R5): every finite
+    element lies within half an ulp of its storage type from the oracle's
+    binary64 value plus the float32 arithmetic's own error, noise * mag,
+    where mag (a tensor, or None for |ref64|) bounds the magnitude of the
+    terms the element was computed from.  Rounding the float32 result once
+    stays within half an ulp of its float32 value; an extra rounding on the
+    way (of h * rstd, or of the row terms of dx) adds up to another half ulp,
+    2^-9 (bf16) or 2^-12 (float16) relative, hundreds of times the noise
+    term."""
     g = gpu.detach().cpu().float().numpy().astype(np.float64)
     r = ref64.detach().cpu().numpy().astype(np.float64)
     m = np.abs(r) if mag is None else np.asarray(mag.detach().cpu().numpy() if hasattr(mag, "detach")
                                                  else mag, dtype=np.float64)
     m = np.broadcast_to(m, r.shape)
     fin = np.isfinite(r)
-    a = np.maximum(np.abs(r[fin]), 2.0 ** -126)
-    half_ulp = 2.0 ** (np.floor(np.log2(a)) - 8)   # bf16 keeps 8 significant bits
+    if gpu.dtype == torch.float16:   # 11 significant bits; subnormal spacing 2^-24
+        a = np.maximum(np.abs(r[fin]), 2.0 ** -14)
+        half_ulp = 2.0 ** (np.floor(np.log2(a)) - 11)
+        name, floor_ = "float16", 2.0 ** -25
+    else:                            # bf16 keeps 8 significant bits
+        a = np.maximum(np.abs(r[fin]), 2.0 ** -126)
+        half_ulp = 2.0 ** (np.floor(np.log2(a)) - 8)
+        name, floor_ = "bf16", 2.0 ** -133
     err = np.abs(g[fin] - r[fin])
-    lim = half_ulp + noise * m[fin] + 2.0 ** -133
+    lim = half_ulp + noise * m[fin] + floor_
     bad = err > lim
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} elements more than half a "
-                           f"bf16 ulp (+ float32 noise) from the binary64 value; worst excess "
+                           f"{name} ulp (+ float32 noise) from the binary64 value; worst excess "
                            f"{float((err - lim).max())}")

@@ -146,7 +146,7 @@ def test_shapes(lib):
 
 
 def test_dtypes(lib):
-    assert fwd(lib, dt=2) == E_DTYPE
+    assert fwd(lib, dt=3) == E_DTYPE
     assert fwd(lib, wdt=-1) == E_DTYPE
     assert add(lib, dt=7) == E_DTYPE
     assert bwd(lib, wdt=3) == E_DTYPE
@@ -250,7 +250,7 @@ def test_rope_validation(lib):
                                    g("qos", Hq * D), g("kos", Hk * D), g("eps", 1e-6),
                                    g("il", 0), g("dt", BF16), g("wdt", BF16), None)
 
-    assert rope(dt=2) == E_DTYPE and rope(wdt=-1) == E_DTYPE
+    assert rope(dt=3) == E_DTYPE and rope(wdt=-1) == E_DTYPE
     assert rope(D=63) == E_SHAPE and rope(D=0) == E_SHAPE and rope(T=-1) == E_SHAPE
     assert rope(Hk=-1) == E_SHAPE and rope(P=-1) == E_SHAPE
     assert rope(qs=Hq * D - 1) == E_SHAPE     # heads of a token wider than the stride

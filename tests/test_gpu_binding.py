@@ -38,6 +38,8 @@ def test_native_binding_is_loaded():
 
 
 @pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
+                                          (torch.float16, torch.float16),
+                                          (torch.float16, torch.float32),
                                           (torch.bfloat16, torch.float32),
                                           (torch.float32, torch.float32)])
 def test_results_match_the_ctypes_binding(dtype, wdtype):
@@ -77,7 +79,7 @@ def test_errors_match_the_ctypes_binding():
     cases = [
         ("x on the CPU", x.cpu(), x, w, {}),
         ("x strided", strided, x, w, {}),
-        ("x float16", x.half(), x.half(), w, {}),
+        ("x float64", x.double(), x.double(), w, {}),
         ("x empty rows", x[:, :0], x[:, :0], w[:0], {}),
         ("r dtype", x, x.float(), w, {}),
         ("r shape", x, x[:3], w, {}),
@@ -85,7 +87,7 @@ def test_errors_match_the_ctypes_binding():
         ("w shape", x, x, w[:63], {}),
         ("w 2-d", x, x, w.view(1, 64), {}),
         ("w on the CPU", x, x, w.cpu(), {}),
-        ("w float16", x, x, w.half(), {}),
+        ("w float64", x, x, w.double(), {}),
         ("y shape", x, x, w, {"y": x[:2]}),
         ("y dtype", x, x, w, {"y": x.float()}),
         ("y strided", x, x, w, {"y": strided}),

@@ -189,9 +189,15 @@ def test_in_place(knobs, force_elem):
 
 # ---- properties the GPU path must keep ----------------------------------------
 
-@pytest.mark.parametrize("N", [4096, 7168, 1000])
-def test_fused_equals_plain_on_residual_bit_exact(N):
-    inp = synth.add_rmsnorm_fwd_inputs(512, N, torch.bfloat16, seed=13)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,N", [(512, 4096), (512, 7168), (512, 1000), (4096, 7168),
+                                 (16384, 7168), (2048, 5632), (4096, 8192), (3000, 6000)])
+def test_fused_equals_plain_on_residual_bit_exact(M, N, dtype):
+    """The fused y is the plain forward of the stored residual, bit for bit,
+    also where the two take different launch shapes (at 641 to 1024
+    vectors a row and 8 or more rows per CU the fused forward runs 16 waves
+    of one vector, the plain one 8 waves of two)."""
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, seed=13)
     y, res, rstd = gpu_fused(inp["x"], inp["r"], inp["w"], 1e-6)
     y2, rstd2 = gpu_plain(res, inp["w"], 1e-6)
     assert_bits_equal(y, y2, "y fused vs plain")

@@ -79,7 +79,7 @@ def _dev_inputs(*ts):
 
 
 DTYPES = [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
-          (torch.bfloat16, torch.float32)]
+          (torch.bfloat16, torch.float32), (torch.float16, torch.float16)]
 FWD_SHAPES = [(1, 8), (37, 1000), (70, 1001), (129, 7168), (3, 16392), (1500, 2056)]
 
 

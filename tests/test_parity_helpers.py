@@ -1,7 +1,7 @@
 """The GPU parity tests' own checkers, on the CPU: the one-rounding check
 (assert_correctly_rounded) accepts a float32 computation of y rounded once
-to bf16 and rejects the same computation with an extra bf16 rounding of
-h * rstd; the dw check holds columns without cancellation to rtol 1e-3
+to bf16 or float16 and rejects the same computation with an extra rounding
+of h * rstd to that type; the dw check holds columns without cancellation to rtol 1e-3
 alone."""
 import numpy as np
 import pytest
@@ -12,32 +12,34 @@ import synth
 from parity import assert_correctly_rounded, assert_dw_close
 
 
-def _inputs():
-    inp = synth.add_rmsnorm_fwd_inputs(64, 4096, torch.bfloat16, seed=3, r_std=0.5)
+def _inputs(dtype=torch.bfloat16):
+    inp = synth.add_rmsnorm_fwd_inputs(64, 4096, dtype, seed=3, r_std=0.5)
     y64 = oracle.rmsnorm_fwd(inp["x"], inp["w"], 1e-6, y_dtype=torch.float64)[0]
     return inp["x"], inp["w"], y64
 
 
 def _float32_y(x, w, double_round: bool):
     """The forward as float32 arithmetic: rstd from a float32 sum of squares,
-    then (h * rstd) * w, rounded to bf16 once, or with h * rstd rounded to
-    bf16 first."""
+    then (h * rstd) * w, rounded to the storage type once, or with h * rstd
+    rounded to it first."""
     h = x.float()
     rs = 1.0 / torch.sqrt((h * h).sum(dim=1, keepdim=True) / h.shape[1] + 1e-6)
     t = h * rs
     if double_round:
-        t = t.to(torch.bfloat16).float()
-    return (t * w.float()).to(torch.bfloat16)
+        t = t.to(x.dtype).float()
+    return (t * w.float()).to(x.dtype)
 
 
-def test_single_rounding_passes():
-    x, w, y64 = _inputs()
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_single_rounding_passes(dtype):
+    x, w, y64 = _inputs(dtype)
     assert_correctly_rounded(_float32_y(x, w, False), y64, None, "y")
 
 
-def test_double_rounding_fails():
-    x, w, y64 = _inputs()
-    with pytest.raises(AssertionError, match="half a bf16 ulp"):
+@pytest.mark.parametrize("dtype,name", [(torch.bfloat16, "bf16"), (torch.float16, "float16")])
+def test_double_rounding_fails(dtype, name):
+    x, w, y64 = _inputs(dtype)
+    with pytest.raises(AssertionError, match=f"half a {name} ulp"):
         assert_correctly_rounded(_float32_y(x, w, True), y64, None, "y")
 
 

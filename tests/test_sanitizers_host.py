@@ -62,7 +62,7 @@ def _kernel_objects():
     absent."""
     objs = sorted(glob.glob(os.path.join(BUILD, "tables_*.o")) +
                   glob.glob(os.path.join(BUILD, "rope_*.o")))
-    if len(objs) != 8:
+    if len(objs) != 18:  # tables_c.o and rope_c.o for the 9 dtype combinations
         subprocess.check_call([sys.executable, os.path.join(ROOT, "add_rmsnorm_amd", "build.py")])
         objs = sorted(glob.glob(os.path.join(BUILD, "tables_*.o")) +
                       glob.glob(os.path.join(BUILD, "rope_*.o")))
