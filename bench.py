@@ -1104,6 +1104,22 @@ def secondary(calls: int, profile_run: bool = False):
     out["add_rmsnorm_fwd_bf16_16384x7168_inplace"] = figure(
         ipstep, 8 * M * N + 2 * N, calls, note="y written over x, residual_out over r")
     del sets
+    # the headline shape with float16 storage (x, r, w, y, residual_out)
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.float16, seed=0, r_std=0.5)
+    w = inp["w"].cuda()
+    sets = []
+    for _ in range(2):
+        x, r = inp["x"].cuda(), inp["r"].cuda()
+        sets.append((x, r, torch.empty_like(x), torch.empty_like(x)))
+
+    def h16():
+        x, r, y, res = sets[i[0] & 1]
+        ar.add_rmsnorm_fwd(x, r, w, 1e-6, y=y, residual_out=res)
+        i[0] += 1
+
+    out["add_rmsnorm_fwd_f16_16384x7168"] = figure(
+        h16, 8 * M * N + 2 * N, calls, note="float16 x, r, w in; float16 y, residual_out out")
+    del sets, inp
     i = [0]
     # backward of the fused op at the headline shape: dy, dres, h read; dh written
     M, N = 16384, 7168

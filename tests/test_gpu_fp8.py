@@ -8,7 +8,11 @@ the GPU's are E4M3(y * (448 / amax)) in float32.  Both values agree to about
 v = y / scale lies within 2^-15 (relative) of an E4M3 rounding boundary:
 every code whose value is not that close must match exactly, and every code,
 close or not, must decode to within half an E4M3 step (times the scale) of
-the binary64 y."""
+the binary64 y.
+
+At 16384x7168 the GPU runs the whole matrix, in the launch the library takes
+for that shape, and 2048 of its rows (the first and last 64, the rest seeded
+random) are checked against the oracle; smaller shapes are checked whole."""
 import sys
 
 import numpy as np
@@ -66,19 +70,36 @@ def check_codes(q_gpu, s_gpu, q_ref, s_ref, y64, what, group=None):
     assert np.all(err <= lim), f"dequantised {what}: max excess {(err - lim).max()}"
 
 
-def run(x, r, w, eps, what, group=None):
+def sample_rows(M, k=2048, seed=0):
+    """Row indices for the full-shape cases: the first and last 64 rows and
+    seeded random ones, k in all (every row is computed on its own, so a
+    sample of rows checks the full launch)."""
+    rng = np.random.default_rng(seed)
+    rows = set(range(64)) | set(range(M - 64, M))
+    while len(rows) < k:
+        rows.add(int(rng.integers(0, M)))
+    return torch.tensor(sorted(rows))
+
+
+def run(x, r, w, eps, what, group=None, rows=None):
+    """The GPU over all of x (and r); the oracle over all rows, or over the
+    rows `rows` only, compared with the same rows of the GPU's outputs."""
     g = lambda t: t.to(DEV)
+    pick = (lambda t: t) if rows is None else (lambda t: t[rows.to(t.device)])
+    xs, rs_ = pick(x), None if r is None else pick(r)
     if r is None:
         q, s = ar.rmsnorm_fwd_fp8(g(x), g(w), eps, group=group)
-        qr, sr, _ = oracle.rmsnorm_fwd_fp8(x, w, eps, group=group or 0)
-        y64, _ = oracle.rmsnorm_fwd(x, w, eps, y_dtype=torch.float64)
+        qr, sr, _ = oracle.rmsnorm_fwd_fp8(xs, w, eps, group=group or 0)
+        y64, _ = oracle.rmsnorm_fwd(xs, w, eps, y_dtype=torch.float64)
     else:
         q, s, res = ar.add_rmsnorm_fwd_fp8(g(x), g(r), g(w), eps, group=group)
-        qr, sr, rres, _ = oracle.rmsnorm_fwd_fp8(x, w, eps, residual=r, group=group or 0)
+        qr, sr, rres, _ = oracle.rmsnorm_fwd_fp8(xs, w, eps, residual=rs_, group=group or 0)
         torch.cuda.synchronize()
-        assert_bits_equal(res.cpu(), rres, f"residual_out {what}")
+        assert_bits_equal(pick(res).cpu(), rres, f"residual_out {what}")
         y64, _ = oracle.rmsnorm_fwd(rres, w, eps, y_dtype=torch.float64)
     torch.cuda.synchronize()
+    # index the codes as bytes (float8 tensors need not support indexing)
+    q, s = pick(q.view(torch.uint8)).view(q.dtype), pick(s)
     assert q.dtype == torch.float8_e4m3fn
     N = x.shape[-1]
     check_codes(q, s, qr, sr, y64, what, group if group and group < N else None)
@@ -88,7 +109,8 @@ def run(x, r, w, eps, what, group=None):
 @pytest.mark.parametrize("M,N", [(16384, 7168), (4096, 4096), (33, 1032)])
 def test_fp8_bf16(fused, M, N):
     inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=M + N, r_std=0.5)
-    run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, f"{M}x{N}")
+    rows = sample_rows(M) if M * N > (1 << 25) else None
+    run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, f"{M}x{N}", rows=rows)
 
 
 @pytest.mark.parametrize("M", [1, 32, 512])
@@ -170,7 +192,8 @@ def test_fp8_infinite_rows(fused):
 @pytest.mark.parametrize("fused", [True, False])
 def test_grouped_128_full_shape(fused):
     inp = synth.add_rmsnorm_fwd_inputs(16384, 7168, torch.bfloat16, seed=71, r_std=0.5)
-    run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, "16384x7168 g128", group=128)
+    run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, "16384x7168 g128", group=128,
+        rows=sample_rows(16384, seed=71))
 
 
 @pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),

@@ -113,6 +113,10 @@ def test_graph_replays_match_eager(M, N):
     del g
 
 
+# torch warns when a leaf's gradient node, made under capture on the capture
+# stream, later serves an eager backward on the default stream; here that is
+# intended (the eager call is the reference)
+@pytest.mark.filterwarnings("ignore:The AccumulateGrad node's stream:UserWarning")
 def test_graph_capture_through_implicit_workspace():
     """Forward and backward of the autograd ops captured in one graph, the
     backward's workspace taken implicitly (no workspace argument).  Between

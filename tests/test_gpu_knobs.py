@@ -75,9 +75,9 @@ def _mxfp4_rows(inp, eps, what):
 def test_forward_persistent_grid_many_rows_per_block(knobs, per_cu, wpr):
     knobs.setenv("ADDRMS_BLOCKS_PER_CU", per_cu)
     knobs.setenv("ADDRMS_FWD_WPR", wpr)
-    # 4133 rows on 256 or 512 blocks: 8 to 17 rows per block (4 per step with
+    # 2087 rows on 256 or 512 blocks: 4 to 9 rows per block (4 per step with
     # one wave per row), and a last sweep that leaves some blocks idle
-    M, N = 4133, 4096
+    M, N = 2087, 4096
     inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=wpr + 10 * per_cu, r_std=0.5)
     what = f"blocks/CU={per_cu} wpr={wpr}"
     _fused_rms(inp, 1e-6, what)
