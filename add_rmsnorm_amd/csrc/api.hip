@@ -257,43 +257,78 @@ int vpl_index(int need)
 // (fused 6.0-6.1 against 5.8-5.9 TB/s; the E4M3 and MXFP4 outputs, with a
 // second row reduction or more registers, 5.7-6.2 against 4.5-5.1).  When
 // there are too few rows to give every SIMD a wave, rows get more waves
-// still.  One exception: the fused Add+RMSNorm with a plain output, 641 to
-// 1024 vectors a row and at least 8 rows per CU takes 16 waves of one vector
-// a lane rather than 8 of two (measured on MI355X, bf16, 16384 rows: 5120 to
-// 8192 columns 1-2 % faster, 4608 columns 1 % slower; 2048 to 8192 rows of
-// 7168 2-5 % faster, 512 rows 17 % slower; float32 16384 x 4096 1 % faster).
-// With 16 waves the plain RMSNorm is 3-29 % slower, and LayerNorm and the
-// E4M3 and MXFP4 outputs 2-18 %, so they keep 8.  qm (a quantised mode, or
-// kQNone) restricts the choice to built variants of that mode.
-// ADDRMS_FWD_WPR forces a WPR when it is built.
+// still.
+//
+// Measured exceptions for plain (unquantised) outputs, from per-call medians
+// on MI355X over bf16 rows of 2048 to 8192 columns and 2048 to 32768 rows,
+// every waves-per-row choice timed side by side:
+// - fused Add+RMSNorm, at least 8 rows per CU: one vector a lane, in 16
+//   waves for 601 to 1024 vectors a row (5120 to 8192 columns 0.3-1.9 %
+//   faster than 8 waves of two, 4608 columns level; 512 rows 17 % slower),
+//   in 8 waves for 257 to 448 from 16 rows per CU (2560 to 3584 columns
+//   2.2-4.7 % faster than 4 waves of two; 2-3 % slower at 8 rows per CU),
+//   and in 8 waves for 449 to 512 from 64 rows per CU (4096
+//   columns: 1-2.5 % faster at 16384 and 32768 rows, level at 8192, 1.6 %
+//   slower at 4096).  With one or two vectors a lane the row sums do not
+//   depend on the launch shape, so the fused y stays the plain forward of
+//   residual_out bit for bit; the plain RMSNorm keeps two vectors a lane
+//   (one is 3-29 % slower there);
+// - fused Add+LayerNorm: one vector a lane in 8 waves for 257 to 512 vectors
+//   from 16 rows per CU (2.5-5.6 % faster than 4 waves of two), in 4 waves
+//   for 193 to 256 from 32 rows per CU (3.0-4.1 %; 7-11 % slower at 4096
+//   rows), and 4 waves of up to 4 vectors for 769 to 1024 from 16 rows per
+//   CU (6656 to 8192 columns 0.8-2.4 % faster than 8 waves of two);
+// - LayerNorm without the residual: each lane up to 4 vectors, in the fewest
+//   waves that hold the row that way, and at least 2 waves for rows of more
+//   than 128 vectors (at 2048 columns 2 waves of two match 1 of four at 16384
+//   rows and beat it by 3 % at 4096): 2560 to 7168
+//   columns 4-40 % faster than 8 waves of two or 4 of one (the statistics
+//   take two exchanges per row, which more waves make dearer), 8192 columns
+//   1-3 %.
+// qm (a quantised mode, or kQNone) restricts the choice to built variants of
+// that mode.  ADDRMS_FWD_WPR forces a WPR when it is built.
 bool pick_fwd(int64_t M, int nvec, int cus, int norm, bool fused, int qm, int *wi_out,
               int *vi_out)
 {
     const int forced = knob(ADDRMS_KNOB_FWD_WPR);
     const int env_vpl = knob(ADDRMS_KNOB_FWD_VPL);
-    const int target = env_vpl > 0 ? env_vpl : 2;
+    const bool plain_ln = norm == kLayer && !fused && qm == kQNone && env_vpl <= 0;
+    const int target = env_vpl > 0 ? env_vpl : plain_ln ? 4 : 2;
     auto need_of = [&](int wi) { return (nvec + 64 * kWprList[wi] - 1) / (64 * kWprList[wi]); };
     auto ok = [&](int wi) {
         const int vi = vpl_index(need_of(wi));
         return vi >= 0 && (qm == kQNone ? fwd_built(kWprList[wi], kVplList[vi])
                                         : q_built(qm, kWprList[wi], kVplList[vi]));
     };
-    if (forced > 0)
+    auto take = [&](int wpr) {
         for (int wi = 0; wi < kNumWpr; ++wi)
-            if (kWprList[wi] == forced && ok(wi)) {
+            if (kWprList[wi] == wpr && ok(wi)) {
                 *wi_out = wi;
                 *vi_out = vpl_index(need_of(wi));
                 return true;
             }
-    if (norm == kRms && fused && qm == kQNone && env_vpl <= 0 && nvec > 640 && nvec <= 1024 &&
-        M >= 8LL * cus)
-        for (int wi = 0; wi < kNumWpr; ++wi)
-            if (kWprList[wi] == 16 && ok(wi)) {
-                *wi_out = wi;
-                *vi_out = vpl_index(need_of(wi));
+        return false;
+    };
+    if (forced > 0 && take(forced))
+        return true;
+    if (qm == kQNone && env_vpl <= 0 && fused && M >= 8LL * cus) {
+        const int64_t per_cu = M / cus;
+        if (norm == kRms) {
+            if (nvec > 600 && nvec <= 1024 && take(16))
                 return true;
-            }
-    int wi = 0;
+            if (nvec > 256 && ((nvec <= 448 && per_cu >= 16) || (nvec <= 512 && per_cu >= 64)) &&
+                take(8))
+                return true;
+        } else {
+            if (nvec > 256 && nvec <= 512 && per_cu >= 16 && take(8))
+                return true;
+            if (nvec > 192 && nvec <= 256 && per_cu >= 32 && take(4))
+                return true;
+            if (nvec > 768 && nvec <= 1024 && per_cu >= 16 && take(4))
+                return true;
+        }
+    }
+    int wi = plain_ln && nvec > 128 ? 1 : 0; // LayerNorm without the residual: 2 waves or more
     while (wi < kNumWpr - 1 &&
            need_of(wi) > (kWprList[wi] == 8 && env_vpl <= 0 ? 4 : target))
         ++wi;

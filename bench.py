@@ -652,7 +652,7 @@ def _secondary_specs():
          2 * M * N + M * N // 2 + M * (N // 32)),
         ("fwd_vec_kernel_add_layernorm_bf16_16384x7168",
          "fused Add+LayerNorm with bias, bf16, M=16384 N=7168",
-         f"fwd_vec_kernel<{B}, {B}, 1, true, 0, 8, 2>", None, 4 * M * N + 4 * N, 4 * M * N),
+         f"fwd_vec_kernel<{B}, {B}, 1, true, 0, 4, 4>", None, 4 * M * N + 4 * N, 4 * M * N),
         ("bwd_vec_kernel_layernorm_bf16_32768x4096", "LayerNorm backward (dx, dw, db), bf16, "
          "M=32768 N=4096", f"bwd_vec_kernel<{B}, {B}, 1, false, 2, 4, false, true>",
          COLREDUCE_KERNEL, 4 * mb * nbk + 8 * mb + 2 * nbk, 2 * mb * nbk + 8 * nbk),

@@ -191,12 +191,14 @@ def test_in_place(knobs, force_elem):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("M,N", [(512, 4096), (512, 7168), (512, 1000), (4096, 7168),
-                                 (16384, 7168), (2048, 5632), (4096, 8192), (3000, 6000)])
+                                 (16384, 7168), (2048, 5632), (4096, 8192), (3000, 6000),
+                                 (8192, 3072), (16384, 4096), (4096, 2560)])
 def test_fused_equals_plain_on_residual_bit_exact(M, N, dtype):
     """The fused y is the plain forward of the stored residual, bit for bit,
-    also where the two take different launch shapes (at 641 to 1024
-    vectors a row and 8 or more rows per CU the fused forward runs 16 waves
-    of one vector, the plain one 8 waves of two)."""
+    also where the two take different launch shapes (with 8 or more rows per
+    CU the fused forward runs one vector a lane, in 16 waves at 601 to 1024
+    vectors a row, and in 8 waves at 257 to 448 from 16 rows per CU and at
+    449 to 512 from 64; the plain one two vectors a lane)."""
     inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, seed=13)
     y, res, rstd = gpu_fused(inp["x"], inp["r"], inp["w"], 1e-6)
     y2, rstd2 = gpu_plain(res, inp["w"], 1e-6)
