@@ -412,6 +412,68 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
     return true;
 }
 
+// Backward launch shapes measured over every choice, for 16-bit rows of 257
+// to 512 vectors (2056 to 4096 bf16 or float16 columns), and for the plain
+// RMS backward also 641 to 768 and 961 to 1024, with at least 32 rows per
+// CU: per-call medians on MI355X of each forced shape (2, 4 or 8 waves per
+// row, the next-row prefetch on or off, the wide block, 2 or 3 blocks per
+// CU) at 2048 to 8192 columns and 4096 to 65536 rows, in alternating
+// rounds, against the default of the rules below (2 waves with the
+// prefetch at 4 vectors a lane, the wide block at 3):
+//
+//   vectors   RMS            fused RMS      LayerNorm      fused LayerNorm
+//   257-384   2, no pf       2, pf          2, pf          2, pf
+//   385-448   8              2, no pf       8              8
+//   449-512   8              8              8              8
+//   641-768   4              (rules)        (rules)        (rules)
+//   961-1024  8              (rules)        (rules)        (rules)
+//
+// all on 2 blocks per CU (waves per row, prefetch).  Gains, rerun with the
+// table in place against the former default: 2560 and 3072 columns 3-13 %;
+// 3584 columns 3-10 %; 4096 columns 2-11 % (the RMS backward at 32768 x
+// 4096: 135.4 against 139.3 us per call); 6144 columns, RMS 3-6 %; 8192
+// columns, RMS 2-4 %.  Every table entry is within 0.8 % of the fastest
+// forced shape at every measured size.  At 8 waves a row takes one vector
+// a lane, and 2 blocks per CU (16 waves) beat the 3 or 4 that fit by 6-11 %
+// for LayerNorm (fewer dw partial rows, whole row steps).  Returns false
+// (the rules below decide) for other shapes, float32 rows, or when a
+// tuning knob is set.
+bool bwd_measured_choice(int norm, bool res, bool half, int64_t M, int nvec, int cus, int *wpr,
+                         int *pf)
+{
+    if (!half || M < 32LL * cus || knob(ADDRMS_KNOB_BWD_WPR) != 0 ||
+        knob(ADDRMS_KNOB_BWD_PREFETCH) != 0 || knob(ADDRMS_KNOB_BWD_WIDE) != 0 ||
+        knob(ADDRMS_KNOB_BLOCKS_PER_CU) != 0)
+        return false;
+    const bool ln = norm == kLayer;
+    if (nvec > 256 && nvec <= 384) {
+        *wpr = 2;
+        *pf = (ln || res) ? 1 : 0;
+        return true;
+    }
+    if (nvec > 384 && nvec <= 448) {
+        *wpr = (res && !ln) ? 2 : 8;
+        *pf = 0;
+        return true;
+    }
+    if (nvec > 448 && nvec <= 512) {
+        *wpr = 8;
+        *pf = 0;
+        return true;
+    }
+    if (nvec > 640 && nvec <= 768 && !ln && !res) {
+        *wpr = 4;
+        *pf = 0;
+        return true;
+    }
+    if (nvec > 960 && nvec <= 1024 && !ln && !res) {
+        *wpr = 8;
+        *pf = 0;
+        return true;
+    }
+    return false;
+}
+
 // The wide backward (one 1024-thread block per CU, 8 rows of 2 waves per
 // step) instead of four 256-thread blocks of 2 rows: the same waves per CU
 // and the same per-row work, with a quarter of the dw partial rows for the
@@ -667,11 +729,25 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
     int cus = 0;
     if ((rc = device_cus_current(&cus)) != ADDRMS_OK)
         return rc;
-    int wi = 0, vi = 0;
-    if (vec_ok && pick_bwd(norm, res, M, (int)N, (int)(N / nv), cus, &wi, &vi)) {
-        a.nvec = (int)(N / nv);
-        const bool wide = use_wide_bwd(tab, norm, res, M, N, wi, vi, cus);
-        const bool pf = !wide && use_prefetch_bwd(tab, norm, res, wi, vi);
+    int wi = 0, vi = 0, m_wpr = 0, m_pf = 0;
+    const int nvec = (int)(N / nv);
+    // the measured table first, where it covers the shape and its variant is built
+    bool measured = vec_ok && bwd_measured_choice(norm, res, dtype != ADDRMS_F32, M, nvec, cus,
+                                                  &m_wpr, &m_pf);
+    if (measured) {
+        const int need = (nvec + 64 * m_wpr - 1) / (64 * m_wpr);
+        vi = vpl_index(need);
+        wi = m_wpr == 2 ? 1 : m_wpr == 4 ? 2 : m_wpr == 8 ? 3 : -1; // kWprList: 1, 2, 4, 8
+        measured = vi >= 0 && wi >= 0 && kWprList[wi] == m_wpr &&
+                   bwd_built(norm, res, m_wpr, kVplList[vi]) &&
+                   (size_t)(bwd_rpb(m_wpr) / 2) * (size_t)N * 4u <= kMaxDynLds &&
+                   (m_pf == 1 ? tab.pf[norm][res ? 1 : 0][wi][vi].fn
+                              : tab.vec[norm][res ? 1 : 0][wi][vi].fn) != nullptr;
+    }
+    if (measured || (vec_ok && pick_bwd(norm, res, M, (int)N, nvec, cus, &wi, &vi))) {
+        a.nvec = nvec;
+        const bool wide = !measured && use_wide_bwd(tab, norm, res, M, N, wi, vi, cus);
+        const bool pf = measured ? m_pf == 1 : !wide && use_prefetch_bwd(tab, norm, res, wi, vi);
         const KernelRef &k = wide ? tab.wide[norm][res ? 1 : 0][vi]
                              : pf ? tab.pf[norm][res ? 1 : 0][wi][vi]
                                   : tab.vec[norm][res ? 1 : 0][wi][vi];
@@ -692,6 +768,8 @@ int bwd_common(int norm, const void *dy, const void *dres, const void *x, const 
         // bf16 columns (6-14 %), and LayerNorm (9 % at 32768 x 2048).
         if (norm == kRms && !wide && knob(ADDRMS_KNOB_BLOCKS_PER_CU) == 0 &&
             a.nvec >= (dtype == ADDRMS_F32 ? 512 : 256) && M >= 48LL * cus && grid > 2 * cus)
+            grid = 2 * cus;
+        if (measured && grid > 2 * cus) // the measured table's shapes: 2 blocks per CU
             grid = 2 * cus;
         a.P = grid;
         if ((rc = launch(k, dim3(grid), smem, &a, s)) != ADDRMS_OK)

@@ -34,7 +34,7 @@ WORKLOAD = "add_rmsnorm_fwd_bf16_16384x7168"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_vec_kernel_add_rmsnorm_bf16_16384x7168.md")
 HEADLINE_KERNEL = "fwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, true, 0, 16, 1>"
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_vec_kernel_rmsnorm_bf16_32768x4096.md")
-BWD_KERNEL = "bwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, false, 2, 4, false, true>"
+BWD_KERNEL = "bwd_vec_kernel<addrms::bf16_t, addrms::bf16_t, 0, false, 8, 1, false, false>"
 COLREDUCE_KERNEL = "dw_colreduce_vec_kernel"
 KERNEL_SOURCES = ["add_rmsnorm_amd/csrc/kernels.hpp", "add_rmsnorm_amd/csrc/device.hpp",
                   "add_rmsnorm_amd/csrc/tables.hip", "add_rmsnorm_amd/csrc/internal.hpp",
@@ -654,7 +654,7 @@ def _secondary_specs():
          "fused Add+LayerNorm with bias, bf16, M=16384 N=7168",
          f"fwd_vec_kernel<{B}, {B}, 1, true, 0, 4, 4>", None, 4 * M * N + 4 * N, 4 * M * N),
         ("bwd_vec_kernel_layernorm_bf16_32768x4096", "LayerNorm backward (dx, dw, db), bf16, "
-         "M=32768 N=4096", f"bwd_vec_kernel<{B}, {B}, 1, false, 2, 4, false, true>",
+         "M=32768 N=4096", f"bwd_vec_kernel<{B}, {B}, 1, false, 8, 1, false, false>",
          COLREDUCE_KERNEL, 4 * mb * nbk + 8 * mb + 2 * nbk, 2 * mb * nbk + 8 * nbk),
         ("bwd_vec_kernel_add_rmsnorm_bf16_16384x7168", "fused Add+RMSNorm backward (dh, dw), "
          "bf16, M=16384 N=7168", f"bwd_vec_kernel<{B}, {B}, 0, true, 8, 2, false, false>",

@@ -218,11 +218,15 @@ def test_workspace_too_small_is_an_error():
 
 def _dx_terms(dy, x, w, rstd, dres=None):
     """Per element, the magnitude of the terms dx = rstd (g - xh c) (+ dres)
-    is computed from, binary64: the scale of float32 error in dx."""
+    is computed from, binary64: the scale of float32 error in dx.  c is a
+    float32 sum over the row, so its own error scales with the mean of |g xh|
+    (its terms), not with |c|, which cancellation can make far smaller."""
     g = dy.double() * w.double()
     xh = x.double() * rstd.double()[:, None]
-    c = (g * xh).mean(dim=1, keepdim=True)
-    mag = rstd.double()[:, None] * (g.abs() + xh.abs() * c.abs())
+    t = g * xh
+    c = t.mean(dim=1, keepdim=True)
+    c_terms = t.abs().mean(dim=1, keepdim=True)
+    mag = rstd.double()[:, None] * (g.abs() + xh.abs() * (c.abs() + c_terms))
     return mag if dres is None else mag + dres.double().abs()
 
 

@@ -133,10 +133,8 @@ def test_rms_backward(dtype, wdtype, M, N):
     assert_dw_close(dw.cpu(), rdw, mag, f"dw {M}x{N}")
     if dtype == H and M == 32768:
         dx64 = oracle.rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], rstd, dx_dtype=torch.float64)[0]
-        g = inp["dy"].double() * inp["w"].double()
-        xh = inp["x"].double() * rstd.double()[:, None]
-        c = (g * xh).mean(-1, keepdim=True)
-        terms = rstd.double()[:, None] * (g.abs() + xh.abs() * c.abs())
+        from test_gpu_bwd import _dx_terms
+        terms = _dx_terms(inp["dy"], inp["x"], inp["w"], rstd)
         assert_correctly_rounded(dx.cpu(), dx64, terms, "float16 dx")
 
 

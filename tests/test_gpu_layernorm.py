@@ -328,5 +328,10 @@ def test_rounded_once_full_size():
     xh = (x.double() - mean.double()[:, None]) * rstd.double()[:, None]
     c1 = gg.mean(dim=1, keepdim=True)
     c2 = (gg * xh).mean(dim=1, keepdim=True)
-    mag = rstd.double()[:, None] * (gg.abs() + c1.abs() + xh.abs() * c2.abs())
+    # c1 and c2 are float32 sums over the row: their error scales with the
+    # mean magnitude of their terms
+    c1_terms = gg.abs().mean(dim=1, keepdim=True)
+    c2_terms = (gg * xh).abs().mean(dim=1, keepdim=True)
+    mag = rstd.double()[:, None] * (gg.abs() + c1.abs() + c1_terms +
+                                    xh.abs() * (c2.abs() + c2_terms))
     assert_correctly_rounded(dx, dx64, mag, "LayerNorm dx")
