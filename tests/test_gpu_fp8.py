@@ -196,6 +196,20 @@ def test_grouped_128_full_shape(fused):
         rows=sample_rows(16384, seed=71))
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("M,N", [(2048, 5120), (2048, 6144), (2048, 4608)])
+def test_four_waves_of_three(fused, M, N):
+    # 513 to 768 vectors a row (to 640 per row) with 8 or more rows per CU:
+    # the E4M3 forwards take 4 waves of 3 vectors a lane (a group of 128
+    # columns then spans lanes of one wave in a different pattern than with
+    # 2 vectors)
+    inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=M + N + 7, r_std=0.5)
+    r = inp["r"] if fused else None
+    run(inp["x"], r, inp["w"], 1e-6, f"{M}x{N} g128", group=128)
+    if N <= 5120:
+        run(inp["x"], r, inp["w"], 1e-6, f"{M}x{N} per row")
+
+
 @pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
                                           (torch.float32, torch.float32),
                                           (torch.bfloat16, torch.float32)])

@@ -110,6 +110,14 @@ def test_full_shape(fused):
     run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, "16384x7168")
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_four_waves_of_three(fused):
+    # 513 to 640 vectors a row with 8 or more rows per CU: 4 waves of 3
+    # vectors a lane
+    inp = synth.add_rmsnorm_fwd_inputs(2048, 4608, torch.bfloat16, seed=93, r_std=0.5)
+    run(inp["x"], inp["r"] if fused else None, inp["w"], 1e-6, "2048x4608")
+
+
 @pytest.mark.parametrize("dtype,wdtype", [(torch.bfloat16, torch.bfloat16),
                                           (torch.float32, torch.float32),
                                           (torch.bfloat16, torch.float32),
