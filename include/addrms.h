@@ -23,6 +23,11 @@
  *
  * Arithmetic: float32 throughout on the GPU; each output is rounded once to
  * its storage type, round-to-nearest-even.  The residual add is a float32 add.
+ * A row's sums (and dw's column sums) are float32 sums in an order that
+ * follows the launch shape, which the library picks from N and M: the last
+ * bit of y, dx, dw and db can differ between batch sizes or tuning knobs,
+ * never beyond the tolerances the results are tested to.  The same call on
+ * the same shape returns the same bits every time (dw included).
  * Storage types (dtype for the matrices, w_dtype for the weights, chosen
  * independently): ADDRMS_F32, ADDRMS_BF16, ADDRMS_F16.  A float16 result
  * beyond its range (65504) is infinite, as a float16 store rounds it.
@@ -351,9 +356,10 @@ const char *addrms_status_str(int status);
  * 0 means the measured default.  Every knob starts from the environment
  * variable named beside it, read once when the library is loaded, and
  * addrms_tune changes it for the whole process (all threads and devices)
- * from then on.  Results do not depend on the knobs except dw's (and db's)
- * summation order where they change the partial rows; a forced variant that
- * is not built for a shape falls back to the default choice.
+ * from then on.  The knobs change only the summation order of row and
+ * column sums (see Arithmetic above), and so at most the last bit of a
+ * result; a forced variant that is not built for a shape falls back to the
+ * default choice.
  *   FWD_WPR            forward waves per row (1, 2, 4, 8, 16)      ADDRMS_FWD_WPR
  *   FWD_VPL            forward target 16-byte vectors a lane       ADDRMS_FWD_VPL
  *   BWD_WPR            backward waves per row (1, 2, 4, 8)         ADDRMS_BWD_WPR
