@@ -276,8 +276,10 @@ int vpl_index(int need)
 // - fused Add+LayerNorm: one vector a lane in 8 waves for 257 to 512 vectors
 //   from 16 rows per CU (2.5-5.6 % faster than 4 waves of two), in 4 waves
 //   for 193 to 256 from 32 rows per CU (3.0-4.1 %; 7-11 % slower at 4096
-//   rows), and 4 waves of up to 4 vectors for 769 to 1024 from 16 rows per
-//   CU (6656 to 8192 columns 0.8-2.4 % faster than 8 waves of two);
+//   rows), 4 waves of up to 4 vectors for 769 to 960 from 16 rows per CU
+//   (6656 to 7680 columns 0.8-2.4 % faster than 8 waves of two), and 16
+//   waves of one for 961 to 1024 (bf16 8192 columns 1.8-2.7 %, level with 4
+//   waves; float32 4096 columns 2.6-3.6 %, where 4 waves gain 0-1 %);
 // - LayerNorm without the residual: each lane up to 4 vectors, in the fewest
 //   waves that hold the row that way, and at least 2 waves for rows of more
 //   than 128 vectors (at 2048 columns 2 waves of two match 1 of four at 16384
@@ -332,7 +334,9 @@ bool pick_fwd(int64_t M, int nvec, int cus, int norm, bool fused, int qm, int *w
                 return true;
             if (nvec > 192 && nvec <= 256 && per_cu >= 32 && take(4))
                 return true;
-            if (nvec > 768 && nvec <= 1024 && per_cu >= 16 && take(4))
+            if (nvec > 960 && nvec <= 1024 && per_cu >= 16 && take(16))
+                return true;
+            if (nvec > 768 && nvec <= 960 && per_cu >= 16 && take(4))
                 return true;
         }
     }
@@ -420,8 +424,9 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
     return true;
 }
 
-// Backward launch shapes measured over every choice, for 16-bit rows of 257
-// to 512 vectors (2056 to 4096 bf16 or float16 columns), and for the plain
+// Backward launch shapes measured over every choice (float32 rows: in the
+// body), for 16-bit rows of 257 to 512 vectors (2056 to 4096 bf16 or float16
+// columns), and for the plain
 // RMS backward also 641 to 768 and 961 to 1024, with at least 32 rows per
 // CU: per-call medians on MI355X of each forced shape (2, 4 or 8 waves per
 // row, the next-row prefetch on or off, the wide block, 2 or 3 blocks per
@@ -444,16 +449,34 @@ bool pick_bwd(int norm, bool res, int64_t M, int N, int nvec, int cus, int *wi_o
 // forced shape at every measured size.  At 8 waves a row takes one vector
 // a lane, and 2 blocks per CU (16 waves) beat the 3 or 4 that fit by 6-11 %
 // for LayerNorm (fewer dw partial rows, whole row steps).  Returns false
-// (the rules below decide) for other shapes, float32 rows, or when a
-// tuning knob is set.
+// (the rules below decide) for other shapes or when a tuning knob is set.
 bool bwd_measured_choice(int norm, bool res, bool half, int64_t M, int nvec, int cus, int *wpr,
                          int *pf)
 {
-    if (!half || M < 32LL * cus || knob(ADDRMS_KNOB_BWD_WPR) != 0 ||
-        knob(ADDRMS_KNOB_BWD_PREFETCH) != 0 || knob(ADDRMS_KNOB_BWD_WIDE) != 0 ||
-        knob(ADDRMS_KNOB_BLOCKS_PER_CU) != 0)
+    if (M < 32LL * cus || knob(ADDRMS_KNOB_BWD_WPR) != 0 || knob(ADDRMS_KNOB_BWD_PREFETCH) != 0 ||
+        knob(ADDRMS_KNOB_BWD_WIDE) != 0 || knob(ADDRMS_KNOB_BLOCKS_PER_CU) != 0)
         return false;
     const bool ln = norm == kLayer;
+    if (!half) {
+        // float32 rows (binary64 row arithmetic), swept the same way at 1024
+        // to 4096 columns: 2 waves with the prefetch at 257 to 384 vectors
+        // (1536 columns: 4-8 % faster) and for the fused forms at 193 to 256
+        // (1024 columns: 4-7 %; the plain forms stay on the grid that fits,
+        // 2 blocks per CU being 5-8 % slower there), 8 waves at 449 to 512
+        // (2048 columns: 3-11 %), and for the RMS backwards 8 waves at 961
+        // to 1024 (4096 columns: 1-6 %); level elsewhere
+        if ((nvec > 256 && nvec <= 384) || (nvec > 192 && nvec <= 256 && res)) {
+            *wpr = 2;
+            *pf = 1;
+            return true;
+        }
+        if ((nvec > 448 && nvec <= 512) || (nvec > 960 && nvec <= 1024 && !ln)) {
+            *wpr = 8;
+            *pf = 0;
+            return true;
+        }
+        return false;
+    }
     if (nvec > 256 && nvec <= 384) {
         *wpr = 2;
         *pf = (ln || res) ? 1 : 0;

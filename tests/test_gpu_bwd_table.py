@@ -1,11 +1,12 @@
 """GPU parity of the backward launch shapes the dispatcher takes from its
-measured table (16-bit rows, at least 32 rows per CU, 2 blocks per CU): the
+measured table (at least 32 rows per CU, 2 blocks per CU): the
 RMS, fused RMS, LayerNorm and fused LayerNorm backwards at widths in each of
 the table's ranges (257-384, 385-448 and 449-512 vectors a row, and for the
 RMS backward 641-768 and 961-1024), against the CPU oracle through the C ABI.
-dx (dh) to the bf16 or float16 tolerance, dw and db to the dw tolerance.
-8192 rows fill 32 rows per CU on a 256-CU device, the table's threshold; the
-float16 cases take the same shapes."""
+dx (dh) to the bf16, float16 or float32 tolerance, dw and db to the dw
+tolerance.  8192 rows fill 32 rows per CU on a 256-CU device, the table's
+threshold; the float16 cases take the same shapes, and float32 rows their
+own entries (193-384, 449-512 and 961-1024 vectors)."""
 import sys
 
 import pytest
@@ -58,6 +59,37 @@ def test_fused_rms(dtype, N):
     rdh, rdw, mag = oracle.add_rmsnorm_bwd(dy, dres, x, w, rstd)
     assert_close(dh.cpu(), rdh, f"dh {M}x{N}")
     assert_dw_close(dw.cpu(), rdw, mag, f"dw {M}x{N}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("N", [1024, 1536, 2048, 4096])
+def test_float32_rows(fused, N):
+    # float32 rows: 2 waves with the prefetch at 257 to 384 vectors (and for
+    # the fused forms at 193 to 256), 8 waves at 449 to 512 and (the RMS
+    # backwards) 961 to 1024
+    x, w, dy, dres = _inputs(N, torch.float32, N + 3)
+    rstd = oracle.rmsnorm_fwd(x, w, 1e-6)[1]
+    g = lambda t: t.to(DEV)
+    if fused:
+        dx, dw = ar.add_rmsnorm_bwd(g(dy), g(dres), g(x), g(w), g(rstd))
+        rdx, rdw, mag = oracle.add_rmsnorm_bwd(dy, dres, x, w, rstd)
+    else:
+        dx, dw = ar.rmsnorm_bwd(g(dy), g(x), g(w), g(rstd))
+        rdx, rdw, mag = oracle.rmsnorm_bwd(dy, x, w, rstd)
+    torch.cuda.synchronize()
+    assert_close(dx.cpu(), rdx, f"dx {M}x{N} float32")
+    assert_dw_close(dw.cpu(), rdw, mag, f"dw {M}x{N} float32")
+    _, mean, lrstd = oracle.layernorm_fwd(x, w, None, 1e-5)
+    if fused:
+        dx, dw, db = ar.add_layernorm_bwd(g(dy), g(dres), g(x), g(w), g(mean), g(lrstd))
+        rdx, rdw, rdb, mw, mb = oracle.add_layernorm_bwd(dy, dres, x, w, mean, lrstd)
+    else:
+        dx, dw, db = ar.layernorm_bwd(g(dy), g(x), g(w), g(mean), g(lrstd))
+        rdx, rdw, rdb, mw, mb = oracle.layernorm_bwd(dy, x, w, mean, lrstd)
+    torch.cuda.synchronize()
+    assert_close(dx.cpu(), rdx, f"LayerNorm dx {M}x{N} float32")
+    assert_dw_close(dw.cpu(), rdw, mw, f"LayerNorm dw {M}x{N} float32")
+    assert_dw_close(db.cpu(), rdb, mb, f"LayerNorm db {M}x{N} float32")
 
 
 @pytest.mark.parametrize("fused", [False, True])
