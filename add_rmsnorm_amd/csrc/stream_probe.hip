@@ -5,7 +5,7 @@
 // or three and write one.  These kernels do only the streaming -- no
 // reduction, one or two integer ops per 16-byte vector -- so their bandwidth
 // is the practical ceiling of each access mix on the device, against which
-// the row kernels are judged.  The matrix covers:
+// the row kernels are measured.  The matrix covers:
 //   * the access mix: 1 or 2 read-only streams, 1 or 2 write-only streams,
 //     1R1W, 2R1W, 2R2W (the fused forward), 3R1W (the fused backward);
 //   * the launch shape: threads per block and 16-byte vectors per lane, one
