@@ -33,7 +33,7 @@ __all__ = ["rmsnorm_fwd", "add_rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc
            "rmsnorm_bwd_workspace_bytes", "layernorm_fwd", "add_layernorm_fwd", "layernorm_bwd",
            "layernorm_bwd_workspace_bytes", "add_layernorm_bwd", "rmsnorm_fwd_fp8",
            "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_mxfp4", "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
-           "AddRmsError", "LIB_PATH", "lib", "KNOBS", "set_knob", "tuning",
+           "AddRmsError", "LIB_PATH", "lib", "KNOBS", "set_knob", "tuning", "plan",
            "rmsnorm_fwd_ctypes", "add_rmsnorm_fwd_ctypes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddrms.so")
@@ -102,7 +102,16 @@ def _load():
     lib.addrms_last_hip_error.argtypes = []
     lib.addrms_tune.restype = i32
     lib.addrms_tune.argtypes = [i32, i32]
+    lib.addrms_plan.restype = i32
+    lib.addrms_plan.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, i32, i32,
+                                ctypes.POINTER(_Plan)]
     return lib
+
+
+class _Plan(ctypes.Structure):
+    """addrms_plan_t of addrms.h."""
+    _fields_ = [(n, ctypes.c_int) for n in ("vector", "waves_per_row", "vectors_per_lane",
+                                            "prefetch", "wide", "blocks_per_cu")]
 
 
 _lib = _load()
@@ -127,6 +136,27 @@ def set_knob(name: str, value: int) -> int:
     return prev
 
 
+_QMODES = {None: 0, "fp8": 1, "fp8_group": 2, "mxfp4": 3}
+
+
+def plan(op: str, M: int, N: int, dtype=torch.bfloat16, w_dtype=None, *, norm: str = "rms",
+         fused: bool = True, qmode=None, group: int = 0, cus: int = 256) -> dict:
+    """The kernel variant a call would take (addrms_plan in addrms.h): op
+    "fwd" or "bwd"; norm "rms" or "layer"; qmode None, "fp8", "fp8_group"
+    (with `group` columns per scale) or "mxfp4"; for aligned contiguous
+    tensors on a device of `cus` compute units, with the current knobs.
+    Returns the fields of addrms_plan_t as a dict.  No GPU needed."""
+    if op not in ("fwd", "bwd") or norm not in ("rms", "layer") or qmode not in _QMODES:
+        raise ValueError(f"plan: op {op!r}, norm {norm!r}, qmode {qmode!r}")
+    out = _Plan()
+    rc = _lib.addrms_plan(0 if op == "fwd" else 1, 0 if norm == "rms" else 1, int(fused),
+                          _QMODES[qmode], int(group), int(M), int(N), _dtype_code(dtype, "dtype"),
+                          _dtype_code(w_dtype or dtype, "w_dtype"), int(cus), ctypes.byref(out))
+    if rc != 0:
+        raise AddRmsError(rc, "addrms_plan")
+    return {n: getattr(out, n) for n, _ in _Plan._fields_}
+
+
 class tuning:
     """Context manager: `with tuning(BWD_WPR=2, BWD_WIDE=1): ...` sets the
     knobs for its body and restores their previous values after."""
@@ -145,11 +175,15 @@ class tuning:
             set_knob(name, v)
 
 
-def _code(t: torch.Tensor, what: str) -> int:
-    c = _CODES.get(t.dtype)
+def _dtype_code(dtype, what: str) -> int:
+    c = _CODES.get(dtype)
     if c is None:
-        raise TypeError(f"{what}: dtype {t.dtype} not supported (float32, bfloat16, float16)")
+        raise TypeError(f"{what}: dtype {dtype} not supported (float32, bfloat16, float16)")
     return c
+
+
+def _code(t: torch.Tensor, what: str) -> int:
+    return _dtype_code(t.dtype, what)
 
 
 def _dev(t: torch.Tensor, what: str, dtype=None, shape=None) -> torch.Tensor:

@@ -1219,4 +1219,70 @@ int addrms_tune(int knob_id, int value)
     return g_knobs.v[knob_id].exchange(value, std::memory_order_relaxed);
 }
 
+// The choices fwd_common and bwd_common make, through the same helpers, for
+// aligned contiguous tensors and a given CU count.
+int addrms_plan(int op, int norm, int fused, int qmode, int64_t qgroup, int64_t M, int64_t N,
+                int dtype, int w_dtype, int cus, addrms_plan_t *out)
+{
+    if (!out)
+        return ADDRMS_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(w_dtype))
+        return ADDRMS_ERR_DTYPE;
+    if (M < 1 || N < 1 || N > INT_MAX || cus < 1 || (op != ADDRMS_PLAN_FWD && op != ADDRMS_PLAN_BWD) ||
+        (norm != kRms && norm != kLayer) || qmode < 0 || qmode > 3 || qgroup < 0 ||
+        (qmode != 0 && (op != ADDRMS_PLAN_FWD || norm != kRms)))
+        return ADDRMS_ERR_SHAPE;
+    *out = addrms_plan_t{0, 0, 0, 0, 0, 0};
+    const bool res = fused != 0;
+    const int nv = vec_elems(dtype);
+    const bool vec_ok = knob(ADDRMS_KNOB_FORCE_ELEM) == 0 && N % nv == 0;
+    const int nvec = (int)(N / nv);
+    int wi = 0, vi = 0;
+    if (op == ADDRMS_PLAN_FWD) {
+        const FwdTable &tab = fwd_table(combo(dtype, w_dtype));
+        const bool q8 = qmode != 0;
+        const bool mx = qmode == 3;
+        int64_t g = mx ? 32 : qmode == 2 ? (qgroup >= N ? 0 : qgroup) : 0;
+        int qlanes = 0;
+        if (g > 0 && g % nv == 0) {
+            const int64_t L = g / nv;
+            if (L <= 64 && (L & (L - 1)) == 0)
+                qlanes = (int)L;
+        }
+        const int qm = mx ? kQMx - 1 : g > 0 ? kQGroup - 1 : kQRow - 1;
+        if (vec_ok && (g == 0 || qlanes > 0) &&
+            pick_fwd(M, nvec, cus, norm, res, q8 ? qm + 1 : (int)kQNone, &wi, &vi) &&
+            (!q8 || tab.vec_q8[res ? 1 : 0][qm][wi][vi].fn != nullptr)) {
+            out->vector = 1;
+            out->waves_per_row = kWprList[wi];
+            out->vectors_per_lane = kVplList[vi];
+        }
+        return ADDRMS_OK;
+    }
+    const BwdTable &tab = bwd_table(combo(dtype, w_dtype));
+    int m_wpr = 0, m_pf = 0;
+    bool measured =
+        vec_ok && bwd_measured_choice(norm, res, dtype != ADDRMS_F32, M, nvec, cus, &m_wpr, &m_pf);
+    if (measured) {
+        vi = vpl_index((nvec + 64 * m_wpr - 1) / (64 * m_wpr));
+        wi = m_wpr == 2 ? 1 : m_wpr == 4 ? 2 : m_wpr == 8 ? 3 : -1;
+        measured = vi >= 0 && wi >= 0 && bwd_built(norm, res, m_wpr, kVplList[vi]) &&
+                   (size_t)(bwd_rpb(m_wpr) / 2) * (size_t)N * 4u <= kMaxDynLds &&
+                   (m_pf == 1 ? tab.pf[norm][res ? 1 : 0][wi][vi].fn
+                              : tab.vec[norm][res ? 1 : 0][wi][vi].fn) != nullptr;
+    }
+    if (measured || (vec_ok && pick_bwd(norm, res, M, (int)N, nvec, cus, &wi, &vi))) {
+        const bool wide = !measured && use_wide_bwd(tab, norm, res, M, N, wi, vi, cus);
+        out->vector = 1;
+        out->waves_per_row = wide ? kBwdWideWpr : kWprList[wi];
+        out->vectors_per_lane = kVplList[vi];
+        out->wide = wide ? 1 : 0;
+        out->prefetch = (measured ? m_pf == 1 : !wide && use_prefetch_bwd(tab, norm, res, wi, vi)) ? 1 : 0;
+        const bool two = measured || (norm == kRms && !wide && knob(ADDRMS_KNOB_BLOCKS_PER_CU) == 0 &&
+                                      nvec >= (dtype == ADDRMS_F32 ? 512 : 256) && M >= 48LL * cus);
+        out->blocks_per_cu = two ? 2 : 0;
+    }
+    return ADDRMS_OK;
+}
+
 } // extern "C"

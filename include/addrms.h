@@ -395,6 +395,43 @@ int addrms_tune(int knob, int value);
 /* The hipError_t of the last ADDRMS_ERR_HIP returned on this thread (0 if none). */
 int addrms_last_hip_error(void);
 
+/*
+ * Launch plan: the kernel variant a call would take, for tools and tests.
+ * Assumes contiguous tensors whose pointers are 16-byte aligned, a device of
+ * `cus` compute units, and the tuning knobs as they stand.  No HIP call.
+ *   op       ADDRMS_PLAN_FWD (the forwards: rmsnorm_fwd, add_rmsnorm_fwd, the
+ *            LayerNorm and quantised forms) or ADDRMS_PLAN_BWD (the backwards)
+ *   norm     ADDRMS_PLAN_RMS or ADDRMS_PLAN_LAYER
+ *   fused    1 for the residual-Add forms
+ *   qmode    forward output: 0 plain, 1 E4M3 with one scale per row, 2 E4M3
+ *            with one scale per `qgroup` columns, 3 MXFP4; 0 for the backward
+ *   out      written on success:
+ *     vector            1: a vector kernel, 0: the element-wise kernels
+ *     waves_per_row     waves a row is spread over (vector kernels)
+ *     vectors_per_lane  16-byte vectors each lane holds per tensor
+ *     prefetch          backward: the next-row prefetch kernel
+ *     wide              backward: 1024-thread blocks
+ *     blocks_per_cu     backward: 2 when the persistent grid is held to 2
+ *                       blocks per CU, 0 when it takes the blocks that fit
+ * Returns ADDRMS_OK, or ADDRMS_ERR_NULL (out), ADDRMS_ERR_DTYPE,
+ * ADDRMS_ERR_SHAPE (M < 1, N < 1, cus < 1, qgroup < 0, an unknown op, norm or
+ * qmode, or a quantised output asked of a backward or a LayerNorm).
+ */
+#define ADDRMS_PLAN_FWD 0
+#define ADDRMS_PLAN_BWD 1
+#define ADDRMS_PLAN_RMS 0
+#define ADDRMS_PLAN_LAYER 1
+typedef struct {
+    int vector;
+    int waves_per_row;
+    int vectors_per_lane;
+    int prefetch;
+    int wide;
+    int blocks_per_cu;
+} addrms_plan_t;
+int addrms_plan(int op, int norm, int fused, int qmode, int64_t qgroup, int64_t M, int64_t N,
+                int dtype, int w_dtype, int cus, addrms_plan_t *out);
+
 #ifdef __cplusplus
 }
 #endif

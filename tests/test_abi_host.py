@@ -64,7 +64,8 @@ def test_header_declares_the_entry_points():
                                   "rmsnorm_fwd_fp8", "add_rmsnorm_fwd_fp8", "rmsnorm_fwd_fp8_grouped",
                                   "add_rmsnorm_fwd_fp8_grouped", "rmsnorm_fwd_mxfp4",
                                   "add_rmsnorm_fwd_mxfp4", "rmsnorm_rope_qk",
-                                  "addrms_status_str", "addrms_last_hip_error", "addrms_tune"])
+                                  "addrms_status_str", "addrms_last_hip_error", "addrms_tune",
+                                  "addrms_plan"])
 
 
 def test_every_declared_symbol_is_exported(lib):
