@@ -5,6 +5,7 @@
  * what it writes against the oracle.
  *
  *   addrms_client IN OUT
+ *   addrms_client --plan M N
  *
  * IN (little-endian): int64 M, int64 N, then bf16 arrays x [M][N], r [M][N],
  * w [N], dy [M][N], h [M][N] and float32 rstd [M] (h and rstd: the saved
@@ -23,6 +24,10 @@
  *      nothing.
  * Exit status 0 and "ok" on stdout when every step succeeded; otherwise a
  * message naming the step and a non-zero status.
+ *
+ * With --plan, no file and no HIP call: the launch plans (addrms_plan) of
+ * the bf16 add_rmsnorm_fwd and rmsnorm_bwd of M x N on a 256-CU device, one
+ * line each, as name key=value ...
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -54,8 +59,35 @@ static int fail(const char *step, const char *what)
 
 static int read_all(FILE *f, void *p, size_t n) { return fread(p, 1, n, f) == n; }
 
+static int print_plans(const char *ms, const char *ns)
+{
+    char *end;
+    const long long M = strtoll(ms, &end, 10);
+    if (end == ms || *end)
+        return fail("plan", "bad M");
+    const long long N = strtoll(ns, &end, 10);
+    if (end == ns || *end)
+        return fail("plan", "bad N");
+    static const struct {
+        const char *name;
+        int op, fused;
+    } calls[] = {{"add_rmsnorm_fwd", ADDRMS_PLAN_FWD, 1}, {"rmsnorm_bwd", ADDRMS_PLAN_BWD, 0}};
+    for (int i = 0; i < 2; ++i) {
+        addrms_plan_t p;
+        LIB_OK("plan", addrms_plan(calls[i].op, ADDRMS_PLAN_RMS, calls[i].fused, 0, 0, M, N,
+                                   ADDRMS_BF16, ADDRMS_BF16, 256, &p));
+        printf("%s vector=%d waves_per_row=%d vectors_per_lane=%d prefetch=%d wide=%d "
+               "blocks_per_cu=%d\n",
+               calls[i].name, p.vector, p.waves_per_row, p.vectors_per_lane, p.prefetch, p.wide,
+               p.blocks_per_cu);
+    }
+    return 0;
+}
+
 int main(int argc, char **argv)
 {
+    if (argc == 4 && strcmp(argv[1], "--plan") == 0)
+        return print_plans(argv[2], argv[3]);
     if (argc != 3)
         return fail("arguments", "usage: addrms_client IN OUT");
     FILE *in = fopen(argv[1], "rb");
