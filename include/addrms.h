@@ -399,6 +399,9 @@ int addrms_last_hip_error(void);
  * Launch plan: the kernel variant a call would take, for tools and tests.
  * Assumes contiguous tensors whose pointers are 16-byte aligned, a device of
  * `cus` compute units, and the tuning knobs as they stand.  No HIP call.
+ * It does not repeat the calls' own argument checks: for a call they would
+ * reject (MXFP4 output of an odd N, null, misaligned or overlapping
+ * buffers) the plan describes nothing that runs.
  *   op       ADDRMS_PLAN_FWD (the forwards: rmsnorm_fwd, add_rmsnorm_fwd, the
  *            LayerNorm and quantised forms) or ADDRMS_PLAN_BWD (the backwards)
  *   norm     ADDRMS_PLAN_RMS or ADDRMS_PLAN_LAYER
