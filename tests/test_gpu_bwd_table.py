@@ -14,6 +14,7 @@ import torch
 
 import add_rmsnorm_amd as ar
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_close, assert_dw_close
 
@@ -41,7 +42,7 @@ def _inputs(N, dtype, seed):
 @pytest.mark.parametrize("N", [2560, 3584, 4096, 6144, 8192])
 def test_rms(dtype, N):
     x, w, dy, _ = _inputs(N, dtype, N)
-    rstd = oracle.rmsnorm_fwd(x, w, 1e-6)[1]
+    rstd = by_rows(oracle.rmsnorm_fwd, x, w, 1e-6)[1]
     dx, dw = ar.rmsnorm_bwd(dy.to(DEV), x.to(DEV), w.to(DEV), rstd.to(DEV))
     torch.cuda.synchronize()
     rdx, rdw, mag = oracle.rmsnorm_bwd(dy, x, w, rstd)
@@ -53,7 +54,7 @@ def test_rms(dtype, N):
 @pytest.mark.parametrize("N", [3072, 3584, 4096])
 def test_fused_rms(dtype, N):
     x, w, dy, dres = _inputs(N, dtype, N + 1)
-    rstd = oracle.rmsnorm_fwd(x, w, 1e-6)[1]
+    rstd = by_rows(oracle.rmsnorm_fwd, x, w, 1e-6)[1]
     dh, dw = ar.add_rmsnorm_bwd(dy.to(DEV), dres.to(DEV), x.to(DEV), w.to(DEV), rstd.to(DEV))
     torch.cuda.synchronize()
     rdh, rdw, mag = oracle.add_rmsnorm_bwd(dy, dres, x, w, rstd)
@@ -68,7 +69,7 @@ def test_float32_rows(fused, N):
     # the fused forms at 193 to 256), 8 waves at 449 to 512 and (the RMS
     # backwards) 961 to 1024
     x, w, dy, dres = _inputs(N, torch.float32, N + 3)
-    rstd = oracle.rmsnorm_fwd(x, w, 1e-6)[1]
+    rstd = by_rows(oracle.rmsnorm_fwd, x, w, 1e-6)[1]
     g = lambda t: t.to(DEV)
     if fused:
         dx, dw = ar.add_rmsnorm_bwd(g(dy), g(dres), g(x), g(w), g(rstd))
@@ -79,7 +80,7 @@ def test_float32_rows(fused, N):
     torch.cuda.synchronize()
     assert_close(dx.cpu(), rdx, f"dx {M}x{N} float32")
     assert_dw_close(dw.cpu(), rdw, mag, f"dw {M}x{N} float32")
-    _, mean, lrstd = oracle.layernorm_fwd(x, w, None, 1e-5)
+    _, mean, lrstd = by_rows(oracle.layernorm_fwd, x, w, None, 1e-5)
     if fused:
         dx, dw, db = ar.add_layernorm_bwd(g(dy), g(dres), g(x), g(w), g(mean), g(lrstd))
         rdx, rdw, rdb, mw, mb = oracle.add_layernorm_bwd(dy, dres, x, w, mean, lrstd)
@@ -96,7 +97,7 @@ def test_float32_rows(fused, N):
 @pytest.mark.parametrize("N", [2560, 3584, 4096])
 def test_layernorm(fused, N):
     x, w, dy, dres = _inputs(N, torch.bfloat16, N + 2)
-    _, mean, rstd = oracle.layernorm_fwd(x, w, None, 1e-5)
+    _, mean, rstd = by_rows(oracle.layernorm_fwd, x, w, None, 1e-5)
     g = lambda t: t.to(DEV)
     if fused:
         dx, dw, db = ar.add_layernorm_bwd(g(dy), g(dres), g(x), g(w), g(mean), g(rstd))

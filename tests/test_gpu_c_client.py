@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal, assert_close, assert_dw_close
 
@@ -36,7 +37,7 @@ def test_c_client(tmp_path, M, N):
     assert os.path.exists(CLIENT), f"{CLIENT} is not built; run python add_rmsnorm_amd/build.py"
     inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=M + N, r_std=0.5)
     dy = synth.store(synth.normal(M + N, "dy", (M, N)), torch.bfloat16)
-    ry, rres, rrstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    ry, rres, rrstd = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     src = tmp_path / "in.bin"
     with open(src, "wb") as f:
         f.write(np.array([M, N], dtype="<i8").tobytes())

@@ -22,6 +22,7 @@ import torch
 import add_rmsnorm_amd as ar
 import add_rmsnorm_amd.autograd as ag
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal, assert_close, assert_correctly_rounded, assert_dw_close
 from test_gpu_fwd import check_fused, check_plain, gpu_fused, gpu_plain
@@ -44,10 +45,10 @@ def _announce(request):
 def test_fused_16384x7168_rounded_once():
     inp = synth.add_rmsnorm_fwd_inputs(16384, 7168, H, seed=61, r_std=0.5)
     y, res, _ = check_fused(inp["x"], inp["r"], inp["w"], 1e-6, "float16 16384x7168")
-    y64 = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6, y_dtype=torch.float64)[0]
+    y64 = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6, y_dtype=torch.float64)[0]
     assert_correctly_rounded(y, y64, None, "float16 y")
     yp, _ = gpu_plain(inp["x"], inp["w"], 1e-6)
-    yp64 = oracle.rmsnorm_fwd(inp["x"], inp["w"], 1e-6, y_dtype=torch.float64)[0]
+    yp64 = by_rows(oracle.rmsnorm_fwd, inp["x"], inp["w"], 1e-6, y_dtype=torch.float64)[0]
     assert_correctly_rounded(yp, yp64, None, "float16 plain y")
     # fused = plain on the residual, bit for bit (the two take different
     # launch shapes at this size)
@@ -100,7 +101,7 @@ def test_residual_add_exhaustive_sweep():
     r = torch.from_numpy(np.repeat(rs, xs.size).view(np.int16)).view(H).view(-1, N)
     w = torch.ones(N, dtype=H)
     _, res, _ = gpu_fused(x, r, w, 1e-6)
-    _, rres, _ = oracle.add_rmsnorm_fwd(x, r, w, 1e-6)
+    _, rres, _ = by_rows(oracle.add_rmsnorm_fwd, x, r, w, 1e-6)
     assert_bits_equal(res, rres, "float16 residual sweep")
 
 
@@ -125,7 +126,7 @@ def test_rms_backward(dtype, wdtype, M, N):
     if M * N > 1 << 26 and (dtype, wdtype) != (H, H):
         M = 4096
     inp = synth.rmsnorm_bwd_inputs(M, N, dtype, wdtype, seed=M + N)
-    rstd = oracle.rmsnorm_fwd(inp["x"], inp["w"], 1e-6)[1]
+    rstd = by_rows(oracle.rmsnorm_fwd, inp["x"], inp["w"], 1e-6)[1]
     dx, dw = ar.rmsnorm_bwd(inp["dy"].to(DEV), inp["x"].to(DEV), inp["w"].to(DEV), rstd.to(DEV))
     torch.cuda.synchronize()
     rdx, rdw, mag = oracle.rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], rstd)
@@ -142,7 +143,7 @@ def test_rms_backward(dtype, wdtype, M, N):
 def test_rms_backward_forced_waves_per_row(knobs, wpr):
     knobs.setenv("ADDRMS_BWD_WPR", str(wpr))
     inp = synth.rmsnorm_bwd_inputs(777, 4096, H, seed=wpr)
-    rstd = oracle.rmsnorm_fwd(inp["x"], inp["w"], 1e-6)[1]
+    rstd = by_rows(oracle.rmsnorm_fwd, inp["x"], inp["w"], 1e-6)[1]
     dx, dw = ar.rmsnorm_bwd(inp["dy"].to(DEV), inp["x"].to(DEV), inp["w"].to(DEV), rstd.to(DEV))
     torch.cuda.synchronize()
     rdx, rdw, mag = oracle.rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], rstd)
@@ -153,7 +154,7 @@ def test_rms_backward_forced_waves_per_row(knobs, wpr):
 @pytest.mark.parametrize("M,N", [(16384, 7168), (4096, 4096), (600, 6152), (301, 1000)])
 def test_fused_backward(M, N):
     inp = synth.add_rmsnorm_fwd_inputs(M, N, H, seed=M, r_std=0.5)
-    _, h, rstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    _, h, rstd = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     dy = synth.store(synth.normal(M, "dy", (M, N)), H)
     dres = synth.store(synth.normal(M + 1, "dy", (M, N)), H)
     dh, dw = ar.add_rmsnorm_bwd(dy.to(DEV), dres.to(DEV), h.to(DEV), inp["w"].to(DEV),
@@ -172,13 +173,13 @@ def test_layernorm(M, N):
     g = lambda t: t.to(DEV)
     y, res, mean, rstd = ar.add_layernorm_fwd(g(x), g(r), g(w), g(b), 1e-5, return_stats=True)
     torch.cuda.synchronize()
-    ry, rres, rmean, rrstd = oracle.add_layernorm_fwd(x, r, w, b, 1e-5)
+    ry, rres, rmean, rrstd = by_rows(oracle.add_layernorm_fwd, x, r, w, b, 1e-5)
     assert_bits_equal(res.cpu(), rres, "LayerNorm residual_out")
     assert_close(y.cpu(), ry, "LayerNorm y")
     assert_close(mean.cpu(), rmean, "mean", atol=1e-6, rtol=1e-5)
     assert_close(rstd.cpu(), rrstd, "rstd", atol=0, rtol=1e-5)
     dy = synth.store(synth.normal(6, "dy", (M, N)), H)
-    _, lmean, lrstd = oracle.layernorm_fwd(x, w, b, 1e-5)
+    _, lmean, lrstd = by_rows(oracle.layernorm_fwd, x, w, b, 1e-5)
     dx, dw, db = ar.layernorm_bwd(g(dy), g(x), g(w), g(lmean), g(lrstd))
     torch.cuda.synchronize()
     rdx, rdw, rdb, mw, mb = oracle.layernorm_bwd(dy, x, w, lmean, lrstd)
@@ -222,7 +223,7 @@ def test_autograd():
     y, res = ag.add_rms_norm(x, r, w, 1e-6)
     torch.autograd.backward([y, res], [gy.to(DEV), gres.to(DEV)])
     torch.cuda.synchronize()
-    ry, rres, rrstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    ry, rres, rrstd = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     assert_close(y.detach().cpu(), ry, "y")
     rdh, rdw, mag = oracle.add_rmsnorm_bwd(gy, gres, rres, inp["w"], rrstd)
     assert_close(x.grad.cpu(), rdh, "x.grad")

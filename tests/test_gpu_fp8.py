@@ -21,6 +21,7 @@ import torch
 
 import add_rmsnorm_amd as ar
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal, assert_close
 
@@ -89,14 +90,14 @@ def run(x, r, w, eps, what, group=None, rows=None):
     xs, rs_ = pick(x), None if r is None else pick(r)
     if r is None:
         q, s = ar.rmsnorm_fwd_fp8(g(x), g(w), eps, group=group)
-        qr, sr, _ = oracle.rmsnorm_fwd_fp8(xs, w, eps, group=group or 0)
-        y64, _ = oracle.rmsnorm_fwd(xs, w, eps, y_dtype=torch.float64)
+        qr, sr, _ = by_rows(oracle.rmsnorm_fwd_fp8, xs, w, eps, group=group or 0)
+        y64, _ = by_rows(oracle.rmsnorm_fwd, xs, w, eps, y_dtype=torch.float64)
     else:
         q, s, res = ar.add_rmsnorm_fwd_fp8(g(x), g(r), g(w), eps, group=group)
-        qr, sr, rres, _ = oracle.rmsnorm_fwd_fp8(xs, w, eps, residual=rs_, group=group or 0)
+        qr, sr, rres, _ = by_rows(oracle.rmsnorm_fwd_fp8, xs, w, eps, residual=rs_, group=group or 0)
         torch.cuda.synchronize()
         assert_bits_equal(pick(res).cpu(), rres, f"residual_out {what}")
-        y64, _ = oracle.rmsnorm_fwd(rres, w, eps, y_dtype=torch.float64)
+        y64, _ = by_rows(oracle.rmsnorm_fwd, rres, w, eps, y_dtype=torch.float64)
     torch.cuda.synchronize()
     # index the codes as bytes (float8 tensors need not support indexing)
     q, s = pick(q.view(torch.uint8)).view(q.dtype), pick(s)
@@ -159,7 +160,7 @@ def test_fp8_special_rows():
     assert (int(qb[2, amax]) & 0x7F) == 0x7E
     # dequantisation in torch agrees with the scale convention
     deq = q.float().cpu()[3] * s[3].cpu()
-    y, _ = oracle.rmsnorm_fwd(x[3:4], inp["w"], 1e-6, y_dtype=torch.float32)
+    y, _ = by_rows(oracle.rmsnorm_fwd, x[3:4], inp["w"], 1e-6, y_dtype=torch.float32)
     assert_close(deq, y[0], "dequantised row", atol=float(s[3]) * 2.0 ** -9, rtol=0.07)
 
 
@@ -179,7 +180,7 @@ def test_fp8_infinite_rows(fused):
     else:
         q, s = ar.rmsnorm_fwd_fp8(x.to(DEV), inp["w"].to(DEV), 1e-6)
     torch.cuda.synchronize()
-    qr, sr = oracle.rmsnorm_fwd_fp8(x, inp["w"], 1e-6)[:2]
+    qr, sr = by_rows(oracle.rmsnorm_fwd_fp8, x, inp["w"], 1e-6)[:2]
     assert torch.equal(s.cpu(), sr) and torch.all(sr == 1.0)
     qb = q.view(torch.uint8).cpu().numpy() & 0x7F
     rb = qr.view(torch.uint8).numpy() & 0x7F

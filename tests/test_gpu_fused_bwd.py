@@ -8,6 +8,7 @@ import torch
 import add_rmsnorm_amd as ar
 import add_rmsnorm_amd.autograd as ag
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_close, assert_dw_close
 
@@ -25,7 +26,7 @@ def _announce(request):
 
 def fused_case(M, N, dtype, wdtype=None, seed=0):
     inp = synth.add_rmsnorm_fwd_inputs(M, N, dtype, wdtype, seed=seed, r_std=0.5)
-    _, h, rstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    _, h, rstd = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     dy = synth.store(synth.normal(seed, "dy", (M, N)), dtype)
     dres = synth.store(synth.normal(seed + 1, "dy", (M, N)), dtype)
     return dy, dres, h, inp["w"], rstd
@@ -158,7 +159,7 @@ def test_add_rms_norm_autograd(dtype, wdtype):
     y, res = ag.add_rms_norm(x, r, w, 1e-6)
     torch.autograd.backward([y, res], [gy.to(DEV), gres.to(DEV)])
     torch.cuda.synchronize()
-    ry, rres, rrstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    ry, rres, rrstd = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     assert_close(y.detach().cpu(), ry, "y")
     rdh, rdw, mag = oracle.add_rmsnorm_bwd(gy, gres, rres, inp["w"], rrstd)
     assert_close(x.grad.cpu(), rdh, "x.grad")
@@ -175,7 +176,7 @@ def test_rms_norm_autograd_and_modules():
     y = ag.rms_norm(x, w, 1e-6)
     y.backward(inp["dy"].to(DEV))
     torch.cuda.synchronize()
-    ry, rrstd = oracle.rmsnorm_fwd(inp["x"], inp["w"], 1e-6)
+    ry, rrstd = by_rows(oracle.rmsnorm_fwd, inp["x"], inp["w"], 1e-6)
     rdx, rdw, mag = oracle.rmsnorm_bwd(inp["dy"], inp["x"], inp["w"], rrstd)
     assert_close(y.detach().cpu(), ry, "y")
     assert_close(x.grad.cpu(), rdx, "x.grad")
@@ -263,9 +264,9 @@ def test_dh_is_rounded_once_16384x7168():
     from parity import assert_correctly_rounded
     M, N = 16384, 7168
     inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=41, r_std=0.5)
-    h = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)[1]
+    h = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)[1]
     w = inp["w"]
-    rstd = oracle.rmsnorm_fwd(h, w, 1e-6)[1]
+    rstd = by_rows(oracle.rmsnorm_fwd, h, w, 1e-6)[1]
     dy = synth.store(synth.normal(41, "dy", (M, N)), torch.bfloat16)
     dres = synth.store(synth.normal(42, "dy", (M, N)), torch.bfloat16)
     dh, _ = ar.add_rmsnorm_bwd(dy.to(DEV), dres.to(DEV), h.to(DEV), w.to(DEV), rstd.to(DEV))

@@ -11,6 +11,7 @@ import torch
 
 import add_rmsnorm_amd as ar
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal, assert_close, assert_correctly_rounded
 
@@ -40,7 +41,7 @@ def gpu_plain(x, w, eps):
 
 def check_fused(x, r, w, eps, what=""):
     y, res, rstd = gpu_fused(x, r, w, eps)
-    ry, rres, rrstd = oracle.add_rmsnorm_fwd(x, r, w, eps)
+    ry, rres, rrstd = by_rows(oracle.add_rmsnorm_fwd, x, r, w, eps)
     assert_bits_equal(res, rres, f"residual_out {what}")
     assert_close(y, ry, f"y {what}")
     assert_close(rstd, rrstd, f"rstd {what}", atol=0, rtol=1e-5)
@@ -49,7 +50,7 @@ def check_fused(x, r, w, eps, what=""):
 
 def check_plain(x, w, eps, what=""):
     y, rstd = gpu_plain(x, w, eps)
-    ry, rrstd = oracle.rmsnorm_fwd(x, w, eps)
+    ry, rrstd = by_rows(oracle.rmsnorm_fwd, x, w, eps)
     assert_close(y, ry, f"y {what}")
     assert_close(rstd, rrstd, f"rstd {what}", atol=0, rtol=1e-5)
     return y, rstd
@@ -140,7 +141,7 @@ def test_three_dim_input_and_no_rstd():
     inp = synth.add_rmsnorm_fwd_inputs(6 * 5, 1024, torch.bfloat16, seed=3)
     x, r = inp["x"].view(6, 5, 1024), inp["r"].view(6, 5, 1024)
     y, res = ar.add_rmsnorm_fwd(x.to(DEV), r.to(DEV), inp["w"].to(DEV), 1e-6)
-    ry, rres, _ = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    ry, rres, _ = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     assert_bits_equal(res.cpu().view(30, 1024), rres, "residual_out")
     assert_close(y.cpu().view(30, 1024), ry, "y")
 
@@ -158,7 +159,7 @@ def test_unaligned_views_take_elementwise_path(offset):
     r.copy_(inp["r"].to(DEV))
     out = big[2, offset:offset + M * N].view(M, N)
     y, res = ar.add_rmsnorm_fwd(x, r, inp["w"].to(DEV), 1e-6, residual_out=out)
-    ry, rres, _ = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    ry, rres, _ = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     assert_bits_equal(res.cpu(), rres, "residual_out")
     assert_close(y.cpu(), ry, "y")
 
@@ -168,7 +169,7 @@ def test_in_place(knobs, force_elem):
     knobs.setenv("ADDRMS_FORCE_ELEM", force_elem)
     M, N = 257, 4096
     inp = synth.add_rmsnorm_fwd_inputs(M, N, torch.bfloat16, seed=11)
-    ry, rres, _ = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], 1e-6)
+    ry, rres, _ = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], 1e-6)
     # residual_out written over r, y over x (the usual in-place residual update)
     x, r, w = inp["x"].to(DEV), inp["r"].to(DEV), inp["w"].to(DEV)
     y, res = ar.add_rmsnorm_fwd(x, r, w, 1e-6, y=x, residual_out=r)
@@ -181,7 +182,7 @@ def test_in_place(knobs, force_elem):
     assert_bits_equal(x.cpu(), rres, "residual_out in x")
     assert_close(r.cpu(), ry, "y in r")
     # plain op in place
-    py, _ = oracle.rmsnorm_fwd(inp["x"], inp["w"], 1e-6)
+    py, _ = by_rows(oracle.rmsnorm_fwd, inp["x"], inp["w"], 1e-6)
     x = inp["x"].to(DEV)
     ar.rmsnorm_fwd(x, w, 1e-6, y=x)
     assert_close(x.cpu(), py, "rmsnorm in place")
@@ -250,7 +251,7 @@ def test_residual_add_exhaustive_sweep():
     r = torch.from_numpy(np.repeat(rs, xs.size).view(np.int16)).view(torch.bfloat16).view(-1, N)
     w = torch.ones(N, dtype=torch.bfloat16)
     _, res, _ = gpu_fused(x, r, w, 1e-6)
-    _, rres, _ = oracle.add_rmsnorm_fwd(x, r, w, 1e-6)
+    _, rres, _ = by_rows(oracle.add_rmsnorm_fwd, x, r, w, 1e-6)
     assert_bits_equal(res, rres, "residual sweep")
 
 
@@ -265,8 +266,8 @@ def test_fused_y_is_rounded_once(name, M):
     inp = synth.workload_inputs(name, M=M)
     eps = synth.WORKLOADS[name]["eps"]
     y, _, _ = gpu_fused(inp["x"], inp["r"], inp["w"], eps)
-    y64 = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], eps, y_dtype=torch.float64)[0]
+    y64 = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], eps, y_dtype=torch.float64)[0]
     assert_correctly_rounded(y, y64, None, f"y {name}")
     yp, _ = gpu_plain(inp["x"], inp["w"], eps)
-    yp64 = oracle.rmsnorm_fwd(inp["x"], inp["w"], eps, y_dtype=torch.float64)[0]
+    yp64 = by_rows(oracle.rmsnorm_fwd, inp["x"], inp["w"], eps, y_dtype=torch.float64)[0]
     assert_correctly_rounded(yp, yp64, None, f"plain y {name}")

@@ -18,6 +18,7 @@ import torch
 
 import add_rmsnorm_amd as ar
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal, assert_close, assert_dw_close
 
@@ -37,7 +38,7 @@ def _fused_rms(inp, eps, what):
     g = lambda t: t.to(DEV)
     y, res, rstd = ar.add_rmsnorm_fwd(g(inp["x"]), g(inp["r"]), g(inp["w"]), eps, return_rstd=True)
     torch.cuda.synchronize()
-    ry, rres, rrstd = oracle.add_rmsnorm_fwd(inp["x"], inp["r"], inp["w"], eps)
+    ry, rres, rrstd = by_rows(oracle.add_rmsnorm_fwd, inp["x"], inp["r"], inp["w"], eps)
     assert_bits_equal(res.cpu(), rres, f"residual_out {what}")
     assert_close(y.cpu(), ry, f"y {what}")
     assert_close(rstd.cpu(), rrstd, f"rstd {what}", atol=0, rtol=1e-5)
@@ -49,7 +50,7 @@ def _fused_ln(inp, eps, what):
     y, res, mean, rstd = ar.add_layernorm_fwd(g(inp["x"]), g(inp["r"]), g(inp["w"]), g(b), eps,
                                               return_stats=True)
     torch.cuda.synchronize()
-    ry, rres, rmean, rrstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], b, eps)
+    ry, rres, rmean, rrstd = by_rows(oracle.add_layernorm_fwd, inp["x"], inp["r"], inp["w"], b, eps)
     assert_bits_equal(res.cpu(), rres, f"residual_out {what}")
     assert_close(y.cpu(), ry, f"y {what}")
     assert_close(mean.cpu(), rmean, f"mean {what}", atol=1e-6, rtol=1e-5)
@@ -114,7 +115,7 @@ def test_backward_few_partial_rows(knobs, cap, M, N):
     knobs.setenv("ADDRMS_MAX_PARTIALS", cap)
     inp = synth.rmsnorm_bwd_inputs(M, N, torch.bfloat16, seed=cap + N)
     dy, x, w = inp["dy"], inp["x"], inp["w"]
-    rstd = oracle.rmsnorm_fwd(x, w, 1e-6)[1]
+    rstd = by_rows(oracle.rmsnorm_fwd, x, w, 1e-6)[1]
     what = f"cap={cap} {M}x{N}"
     # RMS backward
     dx, dw = ar.rmsnorm_bwd(dy.to(DEV), x.to(DEV), w.to(DEV), rstd.to(DEV))
@@ -130,7 +131,7 @@ def test_backward_few_partial_rows(knobs, cap, M, N):
     assert_close(dh.cpu(), rdh, f"dh {what}")
     assert_dw_close(dw.cpu(), rdw, mag, f"fused dw {what}")
     # LayerNorm backward (dw and db partials side by side in the workspace)
-    _, mean, lrstd = oracle.layernorm_fwd(x, w, None, 1e-5)
+    _, mean, lrstd = by_rows(oracle.layernorm_fwd, x, w, None, 1e-5)
     dx, dw, db = ar.layernorm_bwd(dy.to(DEV), x.to(DEV), w.to(DEV), mean.to(DEV), lrstd.to(DEV))
     torch.cuda.synchronize()
     rdx, rdw, rdb, mw, mb = oracle.layernorm_bwd(dy, x, w, mean, lrstd)

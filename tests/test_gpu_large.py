@@ -19,6 +19,7 @@ import torch
 
 import add_rmsnorm_amd as ar
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal, assert_close, assert_dw_close
 
@@ -69,7 +70,7 @@ def test_fused_forward_past_2_31_elements():
     idx = torch.tensor(rows, device=DEV)
     xs = torch.stack([bx[i % BX] for i in rows])
     rs_ = torch.stack([br[i % BR] for i in rows])
-    ry, rres, rrstd = oracle.add_rmsnorm_fwd(xs, rs_, w, 1e-6)
+    ry, rres, rrstd = by_rows(oracle.add_rmsnorm_fwd, xs, rs_, w, 1e-6)
     assert_bits_equal(res[idx].cpu(), rres, "residual_out, sampled rows")
     assert_close(y[idx].cpu(), ry, "y, sampled rows")
     assert_close(rstd[idx].cpu(), rrstd, "rstd, sampled rows", atol=0, rtol=1e-5)
@@ -92,7 +93,7 @@ def test_fused_layernorm_forward_past_2_31_elements():
     idx = torch.tensor(rows, device=DEV)
     xs = torch.stack([bx[i % BX] for i in rows])
     rs_ = torch.stack([br[i % BR] for i in rows])
-    ry, rres, rmean, rrstd = oracle.add_layernorm_fwd(xs, rs_, w, b, 1e-5)
+    ry, rres, rmean, rrstd = by_rows(oracle.add_layernorm_fwd, xs, rs_, w, b, 1e-5)
     assert_bits_equal(res[idx].cpu(), rres, "residual_out, sampled rows")
     assert_close(y[idx].cpu(), ry, "y, sampled rows")
     assert_close(mean[idx].cpu(), rmean, "mean, sampled rows", atol=1e-6, rtol=1e-5)
@@ -102,7 +103,7 @@ def test_fused_layernorm_forward_past_2_31_elements():
 def test_backward_past_2_31_elements():
     bx, _, w = _blocks(torch.bfloat16)
     bdy = synth.store(synth.normal(34, "dy", (BD, N)), torch.bfloat16)
-    brstd = oracle.rmsnorm_fwd(bx, w, 1e-6)[1]           # rstd of each x block row
+    brstd = by_rows(oracle.rmsnorm_fwd, bx, w, 1e-6)[1]           # rstd of each x block row
     x, dy = _tile(bx), _tile(bdy)
     rstd = _tile(brstd.view(BX, 1)).view(M)
     dx, dw = ar.rmsnorm_bwd(dy, x, w.to(DEV), rstd)
@@ -138,9 +139,9 @@ def test_fp8_output_past_2_31_elements(group):
     idx = torch.tensor(rows, device=DEV)
     xs = torch.stack([bx[i % BX] for i in rows])
     rs_ = torch.stack([br[i % BR] for i in rows])
-    qr, sr, rres, _ = oracle.rmsnorm_fwd_fp8(xs, w, 1e-6, residual=rs_, group=group or 0)
+    qr, sr, rres, _ = by_rows(oracle.rmsnorm_fwd_fp8, xs, w, 1e-6, residual=rs_, group=group or 0)
     assert_bits_equal(res[idx].cpu(), rres, "residual_out, sampled rows")
-    y64, _ = oracle.rmsnorm_fwd(rres, w, 1e-6, y_dtype=torch.float64)
+    y64, _ = by_rows(oracle.rmsnorm_fwd, rres, w, 1e-6, y_dtype=torch.float64)
     # index the codes as bytes (float8 tensors need not support indexing)
     check_codes(q.view(torch.uint8)[idx], s[idx], qr, sr, y64, f"E4M3 group {group}, sampled rows",
                 group)
@@ -157,9 +158,9 @@ def test_mxfp4_output_past_2_31_elements():
     idx = torch.tensor(rows, device=DEV)
     xs = torch.stack([bx[i % BX] for i in rows])
     rs_ = torch.stack([br[i % BR] for i in rows])
-    qr, sr, rres, _ = oracle.rmsnorm_fwd_mxfp4(xs, w, 1e-6, residual=rs_)
+    qr, sr, rres, _ = by_rows(oracle.rmsnorm_fwd_mxfp4, xs, w, 1e-6, residual=rs_)
     assert_bits_equal(res[idx].cpu(), rres, "residual_out, sampled rows")
-    y64, _ = oracle.rmsnorm_fwd(rres, w, 1e-6, y_dtype=torch.float64)
+    y64, _ = by_rows(oracle.rmsnorm_fwd, rres, w, 1e-6, y_dtype=torch.float64)
     qs = q.view(torch.uint8)[idx].view(q.dtype)
     ss = s.view(torch.uint8)[idx].view(s.dtype)
     check_mx(qs, ss, qr, sr, y64, "MXFP4, sampled rows")

@@ -9,6 +9,7 @@ import torch
 
 import add_rmsnorm_amd as ar
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal, assert_close, assert_dw_close
 
@@ -39,11 +40,11 @@ def check_fwd(inp, fused, what=""):
     if fused:
         y, res, mean, rstd = ar.add_layernorm_fwd(g(x), g(inp["r"]), g(w), g(b), EPS,
                                                   return_stats=True)
-        ry, rres, rmean, rrstd = oracle.add_layernorm_fwd(x, inp["r"], w, b, EPS)
+        ry, rres, rmean, rrstd = by_rows(oracle.add_layernorm_fwd, x, inp["r"], w, b, EPS)
         assert_bits_equal(res.cpu(), rres, f"residual_out {what}")
     else:
         y, mean, rstd = ar.layernorm_fwd(g(x), g(w), g(b), EPS, return_stats=True)
-        ry, rmean, rrstd = oracle.layernorm_fwd(x, w, b, EPS)
+        ry, rmean, rrstd = by_rows(oracle.layernorm_fwd, x, w, b, EPS)
     torch.cuda.synchronize()
     assert_close(y.cpu(), ry, f"y {what}")
     assert_close(mean.cpu(), rmean, f"mean {what}", atol=1e-6, rtol=1e-5)
@@ -54,7 +55,7 @@ def check_bwd(inp, what="", with_db=True):
     x, w = inp["x"], inp["w"]
     M, N = x.shape
     dy = synth.store(synth.normal(7, "dy", (M, N)), x.dtype)
-    _, mean, rstd = oracle.layernorm_fwd(x, w, inp["b"], EPS)
+    _, mean, rstd = by_rows(oracle.layernorm_fwd, x, w, inp["b"], EPS)
     dx, dw, db = ar.layernorm_bwd(dy.to(DEV), x.to(DEV), w.to(DEV), mean.to(DEV), rstd.to(DEV),
                                   with_db=with_db)
     torch.cuda.synchronize()
@@ -110,7 +111,7 @@ def test_forward_elementwise(knobs, M, N):
 
 def test_forward_in_place_and_empty():
     inp = inputs(200, 4096, torch.bfloat16, seed=13)
-    ry, rres, _, _ = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
+    ry, rres, _, _ = by_rows(oracle.add_layernorm_fwd, inp["x"], inp["r"], inp["w"], inp["b"], EPS)
     x, r = inp["x"].to(DEV), inp["r"].to(DEV)
     ar.add_layernorm_fwd(x, r, inp["w"].to(DEV), inp["b"].to(DEV), EPS, y=x, residual_out=r)
     torch.cuda.synchronize()
@@ -191,7 +192,7 @@ def test_backward_in_place_and_empty(knobs, prefetch):
     inp = inputs(300, 4096, torch.bfloat16, seed=19)
     x, w = inp["x"], inp["w"]
     dy = synth.store(synth.normal(19, "dy", (300, 4096)), torch.bfloat16)
-    _, mean, rstd = oracle.layernorm_fwd(x, w, None, EPS)
+    _, mean, rstd = by_rows(oracle.layernorm_fwd, x, w, None, EPS)
     rdx, rdw, rdb, mw, mb = oracle.layernorm_bwd(dy, x, w, mean, rstd)
     d = dy.to(DEV)
     dx, dw, db = ar.layernorm_bwd(d, x.to(DEV), w.to(DEV), mean.to(DEV), rstd.to(DEV), dx=d)
@@ -254,7 +255,7 @@ def test_fused_backward_prefetch(knobs, M, N, dtype, wdtype, force):
 
 def _fused_backward_case(M, N, dtype, wdtype=None):
     inp = inputs(M, N, dtype, wdtype, seed=29)
-    _, h, mean, rstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
+    _, h, mean, rstd = by_rows(oracle.add_layernorm_fwd, inp["x"], inp["r"], inp["w"], inp["b"], EPS)
     dy = synth.store(synth.normal(29, "dy", (M, N)), dtype)
     dres = synth.store(synth.normal(30, "dy", (M, N)), dtype)
     g = lambda t: t.to(DEV)
@@ -276,7 +277,7 @@ def test_layer_norm_autograd():
     y, res = ag.add_layer_norm(x, r, w, b, EPS)
     torch.autograd.backward([y, res], [gy.to(DEV), gres.to(DEV)])
     torch.cuda.synchronize()
-    ry, rres, rmean, rrstd = oracle.add_layernorm_fwd(inp["x"], inp["r"], inp["w"], inp["b"], EPS)
+    ry, rres, rmean, rrstd = by_rows(oracle.add_layernorm_fwd, inp["x"], inp["r"], inp["w"], inp["b"], EPS)
     assert_close(y.detach().cpu(), ry, "y")
     rdh, rdw, rdb, mw, mb = oracle.add_layernorm_bwd(gy, gres, rres, inp["w"], rmean, rrstd)
     assert_close(x.grad.cpu(), rdh, "x.grad")
@@ -287,7 +288,7 @@ def test_layer_norm_autograd():
     x2 = inp["x"].to(DEV).requires_grad_(True)
     y2 = ag.layer_norm(x2, w.detach(), None, EPS)
     y2.backward(gy.to(DEV))
-    _, m2, s2 = oracle.layernorm_fwd(inp["x"], inp["w"], None, EPS)
+    _, m2, s2 = by_rows(oracle.layernorm_fwd, inp["x"], inp["w"], None, EPS)
     rdx, _, _, _, _ = oracle.layernorm_bwd(gy, inp["x"], inp["w"], m2, s2)
     assert_close(x2.grad.cpu(), rdx, "x2.grad")
     mod = ag.AddLayerNorm(N, dtype=torch.bfloat16, device=DEV)
@@ -310,7 +311,7 @@ def test_rounded_once_full_size():
     g = lambda t: t.to(DEV)
     y, res = ar.add_layernorm_fwd(g(x), g(r), g(w), g(b), EPS)
     torch.cuda.synchronize()
-    y64, h, mean, rstd = oracle.add_layernorm_fwd(x, r, w, b, EPS, y_dtype=torch.float64,
+    y64, h, mean, rstd = by_rows(oracle.add_layernorm_fwd, x, r, w, b, EPS, y_dtype=torch.float64,
                                                   stat_dtype=torch.float64)
     hd, mu, rs = h.double(), mean.double()[:, None], rstd.double()[:, None]
     mag = rs * w.double().abs() * ((hd - mu).abs() + mu.abs()) + b.double().abs()
@@ -320,7 +321,7 @@ def test_rounded_once_full_size():
     x, w = inp["x"], inp["w"]
     M, N = x.shape
     dy = synth.store(synth.normal(53, "dy", (M, N)), x.dtype)
-    _, mean, rstd = oracle.layernorm_fwd(x, w, inp["b"], EPS)
+    _, mean, rstd = by_rows(oracle.layernorm_fwd, x, w, inp["b"], EPS)
     dx, _, _ = ar.layernorm_bwd(g(dy), g(x), g(w), g(mean), g(rstd))
     torch.cuda.synchronize()
     dx64 = oracle.layernorm_bwd(dy, x, w, mean, rstd, dx_dtype=torch.float64)[0]

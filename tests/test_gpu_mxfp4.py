@@ -21,6 +21,7 @@ import torch
 
 import add_rmsnorm_amd as ar
 import oracle
+from oracle_rows import by_rows
 import synth
 from parity import assert_bits_equal
 
@@ -99,14 +100,14 @@ def run(x, r, w, eps, what, rows=None):
     xs, rs_ = pick(x), None if r is None else pick(r)
     if r is None:
         q, s = ar.rmsnorm_fwd_mxfp4(g(x), g(w), eps)
-        qr, sr, _ = oracle.rmsnorm_fwd_mxfp4(xs, w, eps)
-        y64, _ = oracle.rmsnorm_fwd(xs, w, eps, y_dtype=torch.float64)
+        qr, sr, _ = by_rows(oracle.rmsnorm_fwd_mxfp4, xs, w, eps)
+        y64, _ = by_rows(oracle.rmsnorm_fwd, xs, w, eps, y_dtype=torch.float64)
     else:
         q, s, res = ar.add_rmsnorm_fwd_mxfp4(g(x), g(r), g(w), eps)
-        qr, sr, rres, _ = oracle.rmsnorm_fwd_mxfp4(xs, w, eps, residual=rs_)
+        qr, sr, rres, _ = by_rows(oracle.rmsnorm_fwd_mxfp4, xs, w, eps, residual=rs_)
         torch.cuda.synchronize()
         assert_bits_equal(pick(res).cpu(), rres, f"residual_out {what}")
-        y64, _ = oracle.rmsnorm_fwd(rres, w, eps, y_dtype=torch.float64)
+        y64, _ = by_rows(oracle.rmsnorm_fwd, rres, w, eps, y_dtype=torch.float64)
     torch.cuda.synchronize()
     # index the codes and scales as bytes (4- and 8-bit float tensors need
     # not support indexing)
@@ -232,10 +233,10 @@ def test_e2m1_ties_exact(knobs, dtype, force_elem, fused):
     if fused:
         r = torch.zeros_like(x)
         q, s, res = ar.add_rmsnorm_fwd_mxfp4(x.to(DEV), r.to(DEV), w.to(DEV), eps)
-        qr, sr, _, _ = oracle.rmsnorm_fwd_mxfp4(x, w, eps, residual=r)
+        qr, sr, _, _ = by_rows(oracle.rmsnorm_fwd_mxfp4, x, w, eps, residual=r)
     else:
         q, s = ar.rmsnorm_fwd_mxfp4(x.to(DEV), w.to(DEV), eps)
-        qr, sr, _ = oracle.rmsnorm_fwd_mxfp4(x, w, eps)
+        qr, sr, _ = by_rows(oracle.rmsnorm_fwd_mxfp4, x, w, eps)
     torch.cuda.synchronize()
     sb = s.view(torch.uint8).cpu()
     assert torch.equal(sb, sr), (sb[:, :4], sr[:, :4])
